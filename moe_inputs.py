@@ -1,0 +1,109 @@
+"""Seeded synthetic inputs for the MoE W4A16 layer (shared by the product, the tests and the oracle).
+
+This module holds input generation only: it draws random numbers and packs them into the storage
+formats the layer consumes. It contains none of the layer's arithmetic (no decoding, no routing, no
+matmul), so the CPU oracle and the HIP path can both use it without sharing any computation.
+
+Workloads stand in for the shapes the pages name: the Qwen3-Next shape of 800 tokens over 256 experts
+(page "告别Python堆栈：Atlas用纯Rust重写LLM推理，在GB10上跑赢vLLM", section "编译时内核选择和W4A16
+Grouped GEMM"), a Qwen3-MoE-like 128-expert top-8 decode shape and a Mixtral-like 8-expert top-2
+shape (page "AMD ATOM推理引擎…", model table). No model weights are used.
+
+Draw order with ``numpy.random.default_rng(seed)``:
+  1. x       = standard_normal((T, H), float32), rounded to bf16 (round-to-nearest-even)
+  2. logits  = standard_normal((T, E), float32)   (+ a per-expert Zipf-like bias for the skewed workload)
+  3. w13_q   = integers(0, 256, (E, 2I, H/2), uint8)   two E2M1 codes per byte, even K index in the low nibble
+  4. w13_s   = uniform(0.005, 0.02, (E, 2I, H/32)) -> float32 -> bf16 (RNE)
+  5. w2_q    = integers(0, 256, (E, H, I/2), uint8)
+  6. w2_s    = uniform(0.005, 0.02, (E, H, I/32)) -> float32 -> bf16 (RNE)
+bf16 values are carried as uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+GROUP = 32  # K elements per bf16 scale
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int
+    E: int
+    k: int
+    H: int
+    I: int
+    skew: bool = False
+    seed: int = 0
+
+
+# The workloads: tiny parity case, decode batches, the 800-token/256-expert prefill shape,
+# the large-expert prefill shape and the skewed-routing shape.
+WORKLOADS = {
+    "tiny": Workload("tiny", 16, 8, 2, 256, 128),
+    "dec1": Workload("dec1", 1, 128, 8, 2048, 768),
+    "dec8": Workload("dec8", 8, 128, 8, 2048, 768),
+    "dec32": Workload("dec32", 32, 128, 8, 2048, 768),
+    "dec64": Workload("dec64", 64, 128, 8, 2048, 768),
+    "pre800": Workload("pre800", 800, 256, 8, 2048, 512),
+    "big4096": Workload("big4096", 4096, 8, 2, 4096, 14336),
+    "skew8192": Workload("skew8192", 8192, 512, 10, 2048, 512, skew=True),
+}
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even); return the uint16 bit patterns."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to float32 exactly."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def skew_bias(E: int) -> np.ndarray:
+    """Per-expert Zipf-like logit bias b_e = 2*ln(1/rank_e^1.2), rank_e = e+1, float64 then float32."""
+    rank = np.arange(1, E + 1, dtype=np.float64)
+    return (2.0 * np.log(1.0 / rank ** 1.2)).astype(np.float32)
+
+
+@dataclasses.dataclass
+class MoEInputs:
+    wl: Workload
+    x: np.ndarray        # uint16 [T, H]      bf16 bits
+    logits: np.ndarray   # float32 [T, E]
+    w13_q: np.ndarray    # uint8  [E, 2I, H/2]
+    w13_s: np.ndarray    # uint16 [E, 2I, H/32] bf16 bits
+    w2_q: np.ndarray     # uint8  [E, H, I/2]
+    w2_s: np.ndarray     # uint16 [E, H, I/32]  bf16 bits
+
+
+def make_inputs(wl: Workload, seed: int | None = None) -> MoEInputs:
+    """Draw one workload's inputs in the documented order."""
+    T, E, H, I = wl.T, wl.E, wl.H, wl.I
+    if H % GROUP or I % GROUP:
+        raise ValueError("H and I must be multiples of 32")
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    x = f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    logits = rng.standard_normal((T, E), dtype=np.float32)
+    if wl.skew:
+        logits = (logits + skew_bias(E)[None, :]).astype(np.float32)
+    w13_q = rng.integers(0, 256, (E, 2 * I, H // 2), dtype=np.uint8)
+    w13_s = f32_to_bf16_bits(rng.uniform(0.005, 0.02, (E, 2 * I, H // GROUP)).astype(np.float32))
+    w2_q = rng.integers(0, 256, (E, H, I // 2), dtype=np.uint8)
+    w2_s = f32_to_bf16_bits(rng.uniform(0.005, 0.02, (E, H, I // GROUP)).astype(np.float32))
+    return MoEInputs(wl, x, logits, w13_q, w13_s, w2_q, w2_s)
+
+
+def custom(name: str, T: int, E: int, k: int, H: int, I: int, skew: bool = False, seed: int = 0) -> Workload:
+    return Workload(name, T, E, k, H, I, skew, seed)
+
+
+def weight_bytes_per_expert(H: int, I: int) -> int:
+    """Packed 4-bit codes plus bf16 group scales of one expert's gate_up and down weights."""
+    return 2 * I * H // 2 + 2 * I * (H // GROUP) * 2 + H * I // 2 + H * (I // GROUP) * 2

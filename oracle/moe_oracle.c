@@ -1,0 +1,272 @@
+/*
+ * CPU oracle for the MoE W4A16 layer — TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, obviously-correct C: fp64 arithmetic throughout, loops in the order of the
+ * definitions, no blocking or fusion.  Only the test-suite, the smoke check and the CPU-baseline
+ * leg of the benchmark may load this file's library; the product path never does.  It shares no
+ * code, header, table or helper with the HIP implementation.
+ *
+ * Sources (pages), cited by title and section:
+ *   [Atlas]  "告别Python堆栈：Atlas用纯Rust重写LLM推理，在GB10上跑赢vLLM"
+ *            section "编译时内核选择和W4A16 Grouped GEMM": per-expert gate_up and down projections over
+ *            packed FP4 weights that are dequantized to BF16 before the matmul; a launch grid sized by
+ *            max_m_tiles.  Section "KV Cache量化、MTP推测解码和调试工具链": names E2M1 as the FP4
+ *            element format, and the single-precision reference-oracle debugging method.
+ *   [ATOM]   "AMD ATOM推理引擎：如何用分页KV缓存和分段编译实现大模型推理性能翻倍"
+ *            section "8.1 MoE 路径：路由、专家并行与 MORI 通信": routing, top-k selection, expert compute
+ *            and the final combine.  Section "6.1 Linear：按量化类型分派 GEMM": per-1x32 MXFP4 (one scale
+ *            per 32 weights along K).
+ *   [RustDL] "Rust 实现深度学习推理引擎：从计算图到异构硬件加速"
+ *            section "四、算子融合：性能翻倍的关键": SiLU as the activation fused after the matmul.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *   - E2M1 follows the OCP microscaling element definition: 1 sign, 2 exponent bits (bias 1),
+ *     1 mantissa bit, exponent field 0 is subnormal (0 or 0.5).  Code 8 is -0.0.
+ *   - Two codes per byte, the even K index in the low nibble; one bf16 scale per 32 K elements.
+ *   - Gate rows are [0, I) of the gate_up weight, up rows are [I, 2I); h = silu(gate) * up.
+ *   - Routing: softmax over all E logits, keep the k largest, renormalise over the kept k.  Softmax
+ *     is strictly increasing in the logit, so the kept set is the k largest logits; equal logits are
+ *     broken toward the lower expert id, and slot 0 holds the largest.  The comparison is made on
+ *     the fp32 logits themselves.
+ *   - Permutation: a stable counting sort of the flat slot index f = t*k + s by expert id.
+ *   - Combine: y[t] = sum over slots s (ascending) of w[t,s] * o[t,s].
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_GROUP 32
+
+/* ---- element decode ---------------------------------------------------------------------- */
+
+/* E2M1 code -> value.  Bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa.
+ * Exponent field 0: subnormal, value = 0.5 * m.  Otherwise 2^(e-1) * (1 + m/2). */
+double oracle_e2m1_value(int code)
+{
+    int s = (code >> 3) & 1;
+    int e = (code >> 1) & 3;
+    int m = code & 1;
+    double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -mag : mag;
+}
+
+/* bf16 bit pattern -> value (the upper 16 bits of an IEEE binary32). */
+double oracle_bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Dequantized weight W[n, kk] of a row-major [N, K] matrix stored as codes q [N, K/2] and scales
+ * s [N, K/32]: value(code) * scale, computed in fp32 (the product of a <=2-bit and an 8-bit
+ * significand is exact in fp32) and returned widened to fp64. */
+static double weight_at(const uint8_t *q, const uint16_t *s, int64_t K, int64_t n, int64_t kk)
+{
+    uint8_t byte = q[n * (K / 2) + kk / 2];
+    int code = (kk % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+    float v = (float)oracle_e2m1_value(code);
+    float sc = (float)oracle_bf16_value(s[n * (K / ORACLE_GROUP) + kk / ORACLE_GROUP]);
+    return (double)(v * sc);
+}
+
+/* Dense dequantization of one [N, K] weight matrix into out [N, K] (fp64). */
+void oracle_dequant(const uint8_t *q, const uint16_t *s, int64_t N, int64_t K, double *out)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t kk = 0; kk < K; ++kk)
+            out[n * K + kk] = weight_at(q, s, K, n, kk);
+}
+
+/* ---- routing ------------------------------------------------------------------------------ */
+
+/* "a ranks before b" for top-k selection: larger logit first, then lower expert id. */
+static int ranks_before(float la, int a, float lb, int b)
+{
+    if (la != lb) return la > lb;
+    return a < b;
+}
+
+/* Top-k routing of T tokens over E experts: ids [T, k] (slot 0 = best), weights [T, k] in fp64.
+ * Softmax over all experts, keep k, renormalise over the kept k. */
+void oracle_route(const float *logits, int64_t T, int64_t E, int64_t k, int32_t *ids, double *w)
+{
+    double *p = (double *)malloc(sizeof(double) * (size_t)E);
+    unsigned char *taken = (unsigned char *)malloc((size_t)E);
+    for (int64_t t = 0; t < T; ++t) {
+        const float *l = logits + t * E;
+        /* softmax over all E, in fp64 */
+        double mx = -INFINITY;
+        for (int64_t e = 0; e < E; ++e) if ((double)l[e] > mx) mx = (double)l[e];
+        double z = 0.0;
+        for (int64_t e = 0; e < E; ++e) { p[e] = exp((double)l[e] - mx); z += p[e]; }
+        for (int64_t e = 0; e < E; ++e) p[e] /= z;
+        /* k rounds of selection of the best remaining expert */
+        memset(taken, 0, (size_t)E);
+        for (int64_t s = 0; s < k; ++s) {
+            int best = -1;
+            for (int64_t e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || ranks_before(l[e], (int)e, l[best], best)) best = (int)e;
+            }
+            taken[best] = 1;
+            ids[t * k + s] = best;
+        }
+        /* renormalise the kept probabilities */
+        double sum = 0.0;
+        for (int64_t s = 0; s < k; ++s) sum += p[ids[t * k + s]];
+        for (int64_t s = 0; s < k; ++s) w[t * k + s] = p[ids[t * k + s]] / sum;
+    }
+    free(p);
+    free(taken);
+}
+
+/* ---- token -> expert permutation ------------------------------------------------------------ */
+
+/* Stable counting sort of the R = T*k flat slots by expert id.
+ *   counts[E]       rows routed to each expert
+ *   offsets[E+1]    exclusive prefix sum of counts (offsets[E] = R)
+ *   sorted_ids[R]   flat slot f = t*k+s held at permuted row r (ascending f within an expert)
+ *   inv_perm[R]     permuted row of flat slot f
+ *   tiles[*,3]      (expert, first row, rows) for every block of up to block_m rows of one expert,
+ *                   experts ascending, rows ascending
+ * Returns the number of tiles.  The maximum number of row tiles of any one expert is
+ * written to *max_m_tiles. */
+int64_t oracle_align(const int32_t *ids, int64_t T, int64_t k, int64_t E, int64_t block_m,
+                     int32_t *counts, int32_t *offsets, int32_t *sorted_ids, int32_t *inv_perm,
+                     int32_t *tiles, int32_t *max_m_tiles)
+{
+    int64_t R = T * k;
+    for (int64_t e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t f = 0; f < R; ++f) counts[ids[f]] += 1;
+    offsets[0] = 0;
+    for (int64_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int32_t *next = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+    for (int64_t e = 0; e < E; ++e) next[e] = offsets[e];
+    for (int64_t f = 0; f < R; ++f) {           /* ascending f keeps the sort stable */
+        int32_t r = next[ids[f]]++;
+        sorted_ids[r] = (int32_t)f;
+        inv_perm[f] = r;
+    }
+    free(next);
+    int64_t nt = 0;
+    int32_t mmt = 0;
+    for (int64_t e = 0; e < E; ++e) {
+        int32_t m_tiles = 0;
+        for (int64_t r0 = offsets[e]; r0 < offsets[e + 1]; r0 += block_m) {
+            int64_t rows = offsets[e + 1] - r0;
+            if (rows > block_m) rows = block_m;
+            if (tiles) {
+                tiles[nt * 3 + 0] = (int32_t)e;
+                tiles[nt * 3 + 1] = (int32_t)r0;
+                tiles[nt * 3 + 2] = (int32_t)rows;
+            }
+            ++nt;
+            ++m_tiles;
+        }
+        if (m_tiles > mmt) mmt = m_tiles;
+    }
+    if (max_m_tiles) *max_m_tiles = mmt;
+    return nt;
+}
+
+/* ---- expert projections ---------------------------------------------------------------------- */
+
+static double silu(double g) { return g / (1.0 + exp(-g)); }
+
+/* One expert's W4 matrix [N, K] times one activation row a [K] (fp64): out[n] = sum_kk a[kk] W[n,kk],
+ * sums in ascending kk. */
+static void expert_matvec(const uint8_t *q, const uint16_t *s, int64_t N, int64_t K,
+                          const double *a, double *out)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        double acc = 0.0;
+        for (int64_t kk = 0; kk < K; ++kk) acc += a[kk] * weight_at(q, s, K, n, kk);
+        out[n] = acc;
+    }
+}
+
+/* Full layer for a subset of tokens (tok == NULL: tokens 0..n_tok-1).
+ *   x [T, H] bf16 bits, logits [T, E] fp32, w13_q [E, 2I, H/2], w13_s [E, 2I, H/32] bf16 bits,
+ *   w2_q [E, H, I/2], w2_s [E, H, I/32] bf16 bits.
+ *   y [n_tok, H] fp64.  Optional diagnostics (may be NULL): h [n_tok, k, I], o [n_tok, k, H].
+ * Per token: route, then for each slot s the expert's gate_up projection, h = silu(gate) * up,
+ * the down projection o = W2 h, and finally y = sum_s w_s o_s. */
+void oracle_moe_ffn(const uint16_t *x, const float *logits, int64_t T, int64_t H, int64_t I,
+                    int64_t E, int64_t k, const uint8_t *w13_q, const uint16_t *w13_s,
+                    const uint8_t *w2_q, const uint16_t *w2_s, const int64_t *tok, int64_t n_tok,
+                    double *y, double *h_out, double *o_out)
+{
+    (void)T;
+    const int64_t sz13_q = 2 * I * (H / 2), sz13_s = 2 * I * (H / ORACLE_GROUP);
+    const int64_t sz2_q = H * (I / 2), sz2_s = H * (I / ORACLE_GROUP);
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t j = 0; j < n_tok; ++j) {
+        int64_t t = tok ? tok[j] : j;
+        int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+        double *w = (double *)malloc(sizeof(double) * (size_t)k);
+        double *xa = (double *)malloc(sizeof(double) * (size_t)H);
+        double *g = (double *)malloc(sizeof(double) * (size_t)(2 * I));
+        double *h = (double *)malloc(sizeof(double) * (size_t)I);
+        double *o = (double *)malloc(sizeof(double) * (size_t)H);
+        oracle_route(logits + t * E, 1, E, k, ids, w);
+        for (int64_t c = 0; c < H; ++c) xa[c] = oracle_bf16_value(x[t * H + c]);
+        for (int64_t c = 0; c < H; ++c) y[j * H + c] = 0.0;
+        for (int64_t s = 0; s < k; ++s) {
+            int64_t e = ids[s];
+            expert_matvec(w13_q + e * sz13_q, w13_s + e * sz13_s, 2 * I, H, xa, g);
+            for (int64_t i = 0; i < I; ++i) h[i] = silu(g[i]) * g[I + i];
+            expert_matvec(w2_q + e * sz2_q, w2_s + e * sz2_s, H, I, h, o);
+            for (int64_t c = 0; c < H; ++c) y[j * H + c] += w[s] * o[c];
+            if (h_out) memcpy(h_out + (j * k + s) * I, h, sizeof(double) * (size_t)I);
+            if (o_out) memcpy(o_out + (j * k + s) * H, o, sizeof(double) * (size_t)H);
+        }
+        free(ids); free(w); free(xa); free(g); free(h); free(o);
+    }
+}
+
+/* Grouped projection over permuted rows, the operation of one grouped-GEMM launch:
+ * for each permuted row r of expert e (offsets[e] <= r < offsets[e+1]) with activation row
+ * a_row = (a_row_of ? a_row_of[r] / a_row_div : r):
+ *   C[r, n] = sum_kk A[a_row, kk] * W_e[n, kk]           (n < N),
+ * A bf16 bits [*, K], Wq [E, N, K/2], Ws [E, N, K/32].  With silu_mul != 0 the output is
+ *   C[r, j] = silu(G[r, j]) * G[r, N/2 + j]             (j < N/2).
+ * With row_scale != NULL every output of row r is multiplied by row_scale[r].  C is fp64. */
+void oracle_grouped_proj(const uint16_t *A, const int32_t *a_row_of, int64_t a_row_div,
+                         const uint8_t *Wq, const uint16_t *Ws, int64_t E, int64_t N, int64_t K,
+                         const int32_t *offsets, int silu_mul, const double *row_scale, double *C)
+{
+    const int64_t szq = N * (K / 2), szs = N * (K / ORACLE_GROUP);
+    const int64_t nout = silu_mul ? N / 2 : N;
+    for (int64_t e = 0; e < E; ++e) {
+        #pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t r = offsets[e]; r < offsets[e + 1]; ++r) {
+            int64_t arow = a_row_of ? a_row_of[r] / a_row_div : r;
+            double *a = (double *)malloc(sizeof(double) * (size_t)K);
+            double *g = (double *)malloc(sizeof(double) * (size_t)N);
+            for (int64_t c = 0; c < K; ++c) a[c] = oracle_bf16_value(A[arow * K + c]);
+            expert_matvec(Wq + e * szq, Ws + e * szs, N, K, a, g);
+            for (int64_t n = 0; n < nout; ++n) {
+                double v = silu_mul ? silu(g[n]) * g[N / 2 + n] : g[n];
+                if (row_scale) v *= row_scale[r];
+                C[r * nout + n] = v;
+            }
+            free(a); free(g);
+        }
+    }
+}
+
+/* Routing-weighted scatter-reduce: y[t, c] = sum_{s<k} w[t, s] * O[inv_perm[t*k+s], c]
+ * (O given as fp64 [R, H]). */
+void oracle_combine(const double *O, const int32_t *inv_perm, const double *w, int64_t T, int64_t k,
+                    int64_t H, double *y)
+{
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t c = 0; c < H; ++c) {
+            double acc = 0.0;
+            for (int64_t s = 0; s < k; ++s) acc += w[t * k + s] * O[(int64_t)inv_perm[t * k + s] * H + c];
+            y[t * H + c] = acc;
+        }
+}

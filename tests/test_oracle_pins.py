@@ -1,0 +1,255 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each pin is chosen so that a plausible mistake in the oracle (a dropped term, a wrong sign, a
+transposed operand, a swapped nibble, an off-by-one in a scale index, an unstable sort) fails it:
+  * the E2M1 table of the published OCP MX element format (golden fixture),
+  * exhaustive exactness of dequantisation (fp32 product == fp64 product),
+  * hand-worked routing example (golden fixture) and brute-force routing by a full sort,
+  * brute-force permutation by Python's sorted(),
+  * the whole layer against a dense formulation (all experts on all tokens, a dense [T, E] routing
+    matrix with zeros off the top-k) written with numpy matmul in float64,
+  * special cases: E = k = 1 is the textbook SwiGLU FFN; unit codes and unit scales give row sums;
+    zero input gives zero output.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _e2m1_table():
+    vals = {}
+    with open(os.path.join(GOLDEN, "e2m1_ocp_mx.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            c, v = line.split()
+            vals[int(c)] = float(v)
+    return np.array([vals[c] for c in range(16)])
+
+
+TABLE = _e2m1_table()
+
+
+def _np_dequant(q, s):
+    """Independent numpy dequantisation from the golden table (low nibble = even K index)."""
+    N, K = q.shape[0], q.shape[1] * 2
+    c = np.empty((N, K))
+    c[:, 0::2] = TABLE[q & 15]
+    c[:, 1::2] = TABLE[q >> 4]
+    sc = mi.bf16_bits_to_f32(s).astype(np.float64)
+    return c * np.repeat(sc, 32, axis=1)
+
+
+def test_e2m1_matches_ocp_table():
+    for code in range(16):
+        v = oracle.e2m1_value(code)
+        assert v == TABLE[code], (code, v)
+        assert math.copysign(1.0, v) == math.copysign(1.0, TABLE[code])  # code 8 is -0.0
+    assert oracle.e2m1_value(2) == 1.0 and oracle.e2m1_value(7) == 6.0 and oracle.e2m1_value(15) == -6.0
+
+
+def test_bf16_decode_matches_numpy_widening():
+    bits = np.arange(0, 65536, 257, dtype=np.uint16)
+    ref = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    got = np.array([oracle.bf16_value(int(b)) for b in bits])
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+
+
+def test_dequant_exhaustive_exact():
+    # every finite bf16 scale (one per row) times every code (each code twice per 32-element group)
+    scales = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    scales = scales[(scales & 0x7F80) != 0x7F80]  # drop Inf/NaN patterns
+    sf = mi.bf16_bits_to_f32(scales).astype(np.float64)
+    scales = scales[np.abs(sf) * 6.0 < np.finfo(np.float32).max]  # products stay finite in fp32
+    codes = np.arange(32) % 16
+    q = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    qm = np.tile(q, (len(scales), 1))
+    got = oracle.dequant(qm, scales[:, None])
+    ref = TABLE[codes][None, :] * mi.bf16_bits_to_f32(scales).astype(np.float64)[:, None]
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_dequant_layout_nibble_and_group_index():
+    rng = np.random.default_rng(5)
+    q = rng.integers(0, 256, (7, 96 // 2), dtype=np.uint8)
+    s = mi.f32_to_bf16_bits(rng.uniform(0.5, 2.0, (7, 96 // 32)).astype(np.float32))
+    np.testing.assert_array_equal(oracle.dequant(q, s), _np_dequant(q, s))
+
+
+def _golden_route():
+    with open(os.path.join(GOLDEN, "route_worked_example.txt")) as f:
+        rows = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    logits = np.array([float(v) for v in rows[0][1:]], np.float32)[None, :]
+    return logits, {int(r[0][1:]): [int(v) for v in r[1:]] for r in rows[1:]}
+
+
+def test_route_worked_example():
+    logits, expect = _golden_route()
+    ids, w = oracle.route(logits, 2)
+    assert ids[0].tolist() == expect[2]
+    np.testing.assert_allclose(w[0], [0.5, 0.5], rtol=0, atol=1e-15)
+    ids, w = oracle.route(logits, 3)
+    assert ids[0].tolist() == expect[3]
+    a = 1.0 / (2.0 + math.exp(-1.0))
+    np.testing.assert_allclose(w[0], [a, a, math.exp(-1.0) * a], rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("T,E,k,skew", [(16, 8, 2, False), (64, 128, 8, False), (200, 512, 10, True)])
+def test_route_brute_force_and_invariants(T, E, k, skew):
+    rng = np.random.default_rng(T + E)
+    logits = rng.standard_normal((T, E), dtype=np.float32)
+    if skew:
+        logits = (logits + mi.skew_bias(E)[None, :]).astype(np.float32)
+    logits[0, :4] = 1.25  # plant ties
+    ids, w = oracle.route(logits, k)
+    for t in range(T):
+        full = np.exp(logits[t].astype(np.float64) - logits[t].max())
+        p = full / full.sum()
+        order = sorted(range(E), key=lambda e: (-p[e], e))[:k]
+        assert ids[t].tolist() == order
+        assert len(set(ids[t].tolist())) == k
+        ref_w = p[order] / p[order].sum()
+        np.testing.assert_allclose(w[t], ref_w, rtol=1e-12, atol=1e-15)
+        assert abs(w[t].sum() - 1.0) <= 1e-12
+        assert np.all(np.diff(w[t]) <= 0)
+
+
+@pytest.mark.parametrize("T,E,k,bm", [(16, 8, 2, 4), (1, 128, 8, 16), (300, 64, 6, 32), (64, 512, 10, 128)])
+def test_align_brute_force(T, E, k, bm):
+    rng = np.random.default_rng(T * 7 + E)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    a = oracle.align(ids, E, bm)
+    flat = ids.reshape(-1).tolist()
+    R = T * k
+    order = sorted(range(R), key=lambda f: (flat[f], f))
+    assert a["sorted_ids"].tolist() == order
+    inv = [0] * R
+    for r, f in enumerate(order):
+        inv[f] = r
+    assert a["inv_perm"].tolist() == inv
+    assert a["counts"].tolist() == [flat.count(e) for e in range(E)]
+    assert a["offsets"][0] == 0 and a["offsets"][-1] == R
+    assert np.all(np.diff(a["offsets"]) == a["counts"])
+    tiles = []
+    for e in range(E):
+        rows = [r for r in range(R) if flat[order[r]] == e]
+        for j in range(0, len(rows), bm):
+            tiles.append([e, rows[j], len(rows[j:j + bm])])
+    assert a["tiles"].tolist() == tiles and a["num_tiles"] == len(tiles)
+    assert a["max_m_tiles"] == max(-(-flat.count(e) // bm) for e in range(E))
+
+
+def _dense_layer(inp):
+    """Y = sum_e diag(Rw[:, e]) FFN_e(X): every expert on every token, dense routing matrix."""
+    wl = inp.wl
+    T, E, k, H, I = wl.T, wl.E, wl.k, wl.H, wl.I
+    X = mi.bf16_bits_to_f32(inp.x).astype(np.float64)
+    L = inp.logits.astype(np.float64)
+    P = np.exp(L - L.max(1, keepdims=True))
+    P /= P.sum(1, keepdims=True)
+    Rw = np.zeros((T, E))
+    for t in range(T):
+        top = sorted(range(E), key=lambda e: (-inp.logits[t, e], e))[:k]
+        Rw[t, top] = P[t, top] / P[t, top].sum()
+    Y = np.zeros((T, H))
+    for e in range(E):
+        W13 = _np_dequant(inp.w13_q[e], inp.w13_s[e])
+        W2 = _np_dequant(inp.w2_q[e], inp.w2_s[e])
+        G = np.matmul(X, W13.T)
+        Hh = G[:, :I] / (1.0 + np.exp(-G[:, :I])) * G[:, I:]
+        Y += Rw[:, e:e + 1] * np.matmul(Hh, W2.T)
+    return Y
+
+
+@pytest.mark.parametrize("wl", [mi.WORKLOADS["tiny"], mi.custom("odd", 9, 6, 3, 128, 64, seed=3),
+                                mi.custom("skewed", 24, 16, 4, 64, 96, skew=True, seed=4)])
+def test_full_layer_vs_dense_brute_force(wl):
+    inp = mi.make_inputs(wl)
+    y = oracle.moe_ffn(inp)
+    ref = _dense_layer(inp)
+    scale = np.sqrt((ref ** 2).mean())
+    assert np.abs(y - ref).max() <= 1e-12 * scale
+
+
+def test_token_subset_matches_full():
+    inp = mi.make_inputs(mi.WORKLOADS["tiny"])
+    y = oracle.moe_ffn(inp)
+    sub = np.array([15, 0, 7])
+    np.testing.assert_array_equal(oracle.moe_ffn(inp, tokens=sub), y[sub])
+
+
+def test_single_expert_is_textbook_swiglu():
+    inp = mi.make_inputs(mi.custom("one", 5, 1, 1, 64, 32, seed=9))
+    X = mi.bf16_bits_to_f32(inp.x).astype(np.float64)
+    W = _np_dequant(inp.w13_q[0], inp.w13_s[0])
+    W1, W3 = W[:32], W[32:]
+    W2 = _np_dequant(inp.w2_q[0], inp.w2_s[0])
+    a = X @ W1.T
+    ref = (a * (1.0 / (1.0 + np.exp(-a))) * (X @ W3.T)) @ W2.T
+    y = oracle.moe_ffn(inp)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_unit_codes_give_row_sums():
+    # every code 2 (= 1.0), every scale 1.0: each gate/up output is the row sum of x
+    wl = mi.custom("ones", 4, 2, 1, 64, 32, seed=2)
+    inp = mi.make_inputs(wl)
+    inp.w13_q[:] = 0x22
+    inp.w13_s[:] = mi.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    y, h, o = oracle.moe_ffn(inp, diagnostics=True)
+    g = mi.bf16_bits_to_f32(inp.x).astype(np.float64).sum(1)
+    expect_h = g / (1.0 + np.exp(-g)) * g
+    np.testing.assert_allclose(h[:, 0, :], np.repeat(expect_h[:, None], 32, 1), rtol=1e-13)
+
+
+def test_zero_input_gives_zero():
+    inp = mi.make_inputs(mi.WORKLOADS["tiny"])
+    inp.x[:] = 0
+    assert np.all(oracle.moe_ffn(inp) == 0.0)
+
+
+def test_grouped_proj_and_combine_match_per_expert_numpy():
+    inp = mi.make_inputs(mi.WORKLOADS["tiny"])
+    wl = inp.wl
+    ids, w = oracle.route(inp.logits, wl.k)
+    a = oracle.align(ids, wl.E, 8)
+    G = oracle.grouped_proj(inp.x, a["sorted_ids"], wl.k, inp.w13_q, inp.w13_s, a["offsets"], silu_mul=True)
+    X = mi.bf16_bits_to_f32(inp.x).astype(np.float64)
+    for r in range(wl.T * wl.k):
+        f = a["sorted_ids"][r]
+        e = ids.reshape(-1)[f]
+        W = _np_dequant(inp.w13_q[e], inp.w13_s[e])
+        g = W @ X[f // wl.k]
+        np.testing.assert_allclose(G[r], g[:wl.I] / (1 + np.exp(-g[:wl.I])) * g[wl.I:], rtol=1e-12, atol=1e-13)
+    # combine: a permuted O gathers back to token order with slot weights
+    O = np.random.default_rng(1).standard_normal((wl.T * wl.k, wl.H))
+    y = oracle.combine(O, a["inv_perm"], w, wl.T, wl.k)
+    ref = np.zeros((wl.T, wl.H))
+    for t in range(wl.T):
+        for s in range(wl.k):
+            ref[t] += w[t, s] * O[a["inv_perm"][t * wl.k + s]]
+    np.testing.assert_allclose(y, ref, rtol=1e-14, atol=1e-14)
+    # row scale multiplies each permuted row
+    rs = np.linspace(0.5, 1.5, wl.T * wl.k)
+    G2 = oracle.grouped_proj(inp.x, a["sorted_ids"], wl.k, inp.w13_q, inp.w13_s, a["offsets"], silu_mul=True,
+                             row_scale=rs)
+    np.testing.assert_allclose(G2, G * rs[:, None], rtol=1e-15, atol=0)
+
+
+def test_page_byte_figures():
+    # Atlas page, section "编译时内核选择和W4A16 Grouped GEMM": 1611 MB for BF16 expert weights and
+    # 302 MB for W4A16 at the 256-expert shape (hidden 2048, intermediate 512).
+    E, H, I = 256, 2048, 512
+    assert E * 3 * H * I * 2 == 1_610_612_736
+    gate_up_4bit = E * (2 * I * H // 2 + 2 * I * (H // 32) * 2)
+    assert gate_up_4bit == 301_989_888
+    assert E * mi.weight_bytes_per_expert(H, I) == 452_984_832
