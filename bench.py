@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE W4A16 layer on one MI355X.
+
+One step = the whole layer (route -> permute -> gate_up grouped GEMM with SiLU*mul -> down grouped
+GEMM -> combine) over one batch of seeded synthetic inputs already resident in HBM.  The default
+workload is the 800-token / 256-expert prefill shape (top-8, hidden 2048, intermediate 512, E2M1
+group-32 bf16 scales).  Weights are rotated over L distinct copies (L * weight bytes >= 1 GiB) so
+that no step finds its weights in L2 or the Infinity Cache.
+
+Prints ONE JSON line on stdout; progress and the per-kernel table go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import moe_inputs as mi
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+RIDGE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+PAGES_US_800 = 5580.0  # Atlas page, GB10: W4A16 grouped-GEMM MoE layer at 800 tokens / 256 experts
+METRIC = "MoE layer µs, TFLOP/s and weight GB/s (% roofline) at 800 tok/256 experts"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def cpu_baseline(inp, target_s: float):
+    """Time the CPU oracle (as it stands) on a bounded token sample; scale to one whole layer."""
+    import oracle
+
+    wl = inp.wl
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(1)
+    n = min(wl.T, cores)
+    tok = np.sort(rng.choice(wl.T, n, replace=False))
+    t0 = time.perf_counter()
+    oracle.moe_ffn(inp, tokens=tok)
+    dt = time.perf_counter() - t0
+    if dt < target_s / 2 and n < wl.T:
+        n2 = int(min(wl.T, max(n, n * (target_s / max(dt, 1e-3)))))
+        tok = np.sort(rng.choice(wl.T, n2, replace=False))
+        t0 = time.perf_counter()
+        oracle.moe_ffn(inp, tokens=tok)
+        dt = time.perf_counter() - t0
+        n = n2
+    us_layer = dt / n * wl.T * 1e6
+    return {"value": round(us_layer, 1), "unit": "us/layer", "cores": min(cores, n), "kind": "oracle",
+            "sample": f"{n} of {wl.T} tokens of the same workload ({dt:.1f} s wall), scaled to {wl.T} tokens"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="pre800", choices=sorted(mi.WORKLOADS))
+    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = enough for 1 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import moe_w4a16_grouped_amd as moe
+
+    wl = mi.WORKLOADS[args.workload]
+    T, E, k, H, I = wl.T, wl.E, wl.k, wl.H, wl.I
+    R = T * k
+    log(f"bench: workload {wl.name} T={T} E={E} k={k} H={H} I={I}; generating inputs")
+    inp = mi.make_inputs(wl)
+    wbytes_all = E * mi.weight_bytes_per_expert(H, I)
+    L = args.copies or max(1, math.ceil((1 << 30) / wbytes_all))
+    x, logits = dev_bf16(inp.x), dev(inp.logits)
+    w13_q0, w13_s0 = dev(inp.w13_q), dev(inp.w13_s.view(np.int16))
+    w2_q0, w2_s0 = dev(inp.w2_q), dev(inp.w2_s.view(np.int16))
+    copies = [(w13_q0, w13_s0, w2_q0, w2_s0)] + [
+        (w13_q0.clone(), w13_s0.clone(), w2_q0.clone(), w2_s0.clone()) for _ in range(L - 1)]
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_ffn_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device="cuda")
+    log(f"bench: {L} weight copies of {wbytes_all / 1e6:.1f} MB; warmup {args.warmup}, timed steps {args.steps}")
+
+    def step(i):
+        q13, s13, q2, s2 = copies[i % L]
+        moe.moe_ffn_forward(x, logits, q13, s13, q2, s2, k, y=y, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"bench: whole layer {ms_per_step * 1e3:.1f} us/step (host wall {t_wall / args.steps * 1e6:.1f} us/step)")
+
+    # Per-kernel pass: the same layer through the individual entry points, HIP events between the
+    # launches on the stream they run on (torch's current stream).
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    bm = moe.moe_ffn_block_m(T, E, k)
+    h = torch.empty((R, I), dtype=torch.bfloat16, device="cuda")
+    O = torch.empty((R, H), dtype=torch.float32, device="cuda")
+    names = ["route", "align", "gate_up", "down", "combine"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    al = None
+    for i in range(args.warmup + args.steps):
+        q13, s13, q2, s2 = copies[i % L]
+        e = evs[i - args.warmup] if i >= args.warmup else None
+        if e: e[0].record()
+        moe.moe_route_topk(logits, k, ids, wts)
+        if e: e[1].record()
+        al = moe.moe_align(ids, E, bm)
+        if e: e[2].record()
+        moe.moe_grouped_gemm_w4a16(x, al["sorted_ids"], k, q13, s13, al["tiles"], al["max_tiles"],
+                                   al["num_tiles"], bm, moe.MOE_EPI_SILU_MUL, R, C=h)
+        if e: e[3].record()
+        moe.moe_grouped_gemm_w4a16(h, None, 1, q2, s2, al["tiles"], al["max_tiles"], al["num_tiles"], bm,
+                                   moe.MOE_EPI_NONE, R, moe.MOE_OUT_F32, C=O)
+        if e: e[4].record()
+        moe.moe_combine(O, al["inv_perm"], wts, y=y)
+        if e: e[5].record()
+    torch.cuda.synchronize()
+    kern_us = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in evs]) * 1e3) for j, n in enumerate(names)}
+    touched = int((al["counts"] > 0).sum().item())
+    log("bench: per-kernel us (events): " + ", ".join(f"{n}={v:.1f}" for n, v in kern_us.items()))
+
+    bpe = mi.weight_bytes_per_expert(H, I)
+    g13 = 2 * I * H // 2 + 2 * I * (H // 32) * 2
+    layer_bytes = touched * bpe + T * H * 2 + T * E * 4 + T * H * 2
+    weight_bytes = touched * bpe
+    flops = 6.0 * R * H * I
+    us = ms_per_step * 1e3
+    gu_bytes = touched * g13 + T * H * 2 + R * I * 2
+    gu_flops = 4.0 * R * H * I
+    gu_us = kern_us["gate_up"]
+    bound = "hbm" if gu_flops / gu_bytes < RIDGE else "mfma"
+    if bound == "hbm":
+        achieved, peak, unit = gu_bytes / (gu_us * 1e-6) / 1e9, HBM_PEAK_GBPS, "GB/s"
+    else:
+        achieved, peak, unit = gu_flops / (gu_us * 1e-6) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    result = {
+        "metric": METRIC,
+        "value": round(us, 2),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": round(us / PAGES_US_800, 5) if wl.name == "pre800" else None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; E2M1 codes uniform, bf16 group-32 scales U[0.005,0.02], x and logits N(0,1))",
+        "config": {"workload": f"{wl.name}: {T} tokens, {E} experts top-{k}, hidden {H}, intermediate {I}, "
+                               f"W4 E2M1 group-32 bf16 scales", "tokens": T, "experts": E, "top_k": k,
+                   "hidden": H, "intermediate": I, "weight_copies": L, "touched_experts": touched},
+        "tflops": round(flops / (us * 1e-6) / 1e12, 3),
+        "weight_gbps": round(weight_bytes / (us * 1e-6) / 1e9, 1),
+        "layer_gbps": round(layer_bytes / (us * 1e-6) / 1e9, 1),
+        "layer_roofline_frac": round(max(layer_bytes / (HBM_PEAK_GBPS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+                                     / (us * 1e-6), 4),
+        "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
+        "roofline": {"kernel": "gemm_w4a16_tiled (gate_up + SiLU*mul)", "bound": bound, "achieved": round(achieved, 2),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+                     "algorithmic_bytes": gu_bytes, "algorithmic_flops": gu_flops},
+    }
+    if not args.no_cpu_baseline:
+        log(f"bench: timing the CPU oracle on a token sample (~{args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

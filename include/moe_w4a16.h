@@ -1,0 +1,196 @@
+/*
+ * libmoe_w4a16 — mixture-of-experts FFN layer with 4-bit (E2M1) expert weights and bf16 activations
+ * (W4A16), hand-written HIP for AMD Instinct MI355X (gfx950).
+ *
+ * Pages this interface follows (cited by title and section):
+ *   [Atlas] "告别Python堆栈：Atlas用纯Rust重写LLM推理，在GB10上跑赢vLLM",
+ *           section "编译时内核选择和W4A16 Grouped GEMM": one launch per projection covering all
+ *           experts (gate_up, then down); packed FP4 weights dequantized inside the matmul with no
+ *           bf16 weight write-back; a grid sized by the number of row tiles per expert (max_m_tiles).
+ *           Section "KV Cache量化、MTP推测解码和调试工具链": missing zero-initialisation and a broken
+ *           max_m_tiles heuristic as MoE failure modes (so outputs here never rely on the caller
+ *           zeroing them, and tile counts are computed exactly on the device).
+ *   [ATOM]  "AMD ATOM推理引擎：如何用分页KV缓存和分段编译实现大模型推理性能翻倍",
+ *           section "8.1 MoE 路径：路由、专家并行与 MORI 通信": routing, top-k selection, expert
+ *           compute and the final combine.  Section "8.2 量化并非单一格式，而是一套执行契约": dtype,
+ *           scale shape and layout form the kernel's contract.  Section "6.1 Linear：按量化类型分派
+ *           GEMM": per-1x32 scaling of 4-bit weights.
+ *   [RustDL] "Rust 实现深度学习推理引擎：从计算图到异构硬件加速", section "四、算子融合：性能翻倍的关键":
+ *           the activation (SiLU) fused into the producing matmul.
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers unless stated; bf16 values are passed as their uint16_t bits.
+ *   - Every device pointer must be 16-byte aligned (128-bit loads) unless stated otherwise.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls only enqueue
+ *     work on it and return; there is no host<->device synchronisation.
+ *   - The caller allocates and owns every buffer, workspaces included.  The library allocates
+ *     nothing, frees nothing and keeps no pointer after a call returns.
+ *   - Inputs are read-only.  Outputs are fully overwritten; no zero-initialisation is expected.
+ *   - Arguments are validated on the host before anything is launched; a failing call returns a
+ *     negative status, launches nothing and records a message for moe_last_error().
+ *   - Results are deterministic: identical inputs give identical output bits (no floating-point
+ *     atomics).
+ *   - Calls that share a workspace or output buffer must not overlap in time.
+ *
+ * Weight format (the layer's contract)
+ *   - Element: E2M1 (1 sign, 2 exponent bits with bias 1, 1 mantissa bit; values 0, ±0.5, ±1, ±1.5,
+ *     ±2, ±3, ±4, ±6).  Two codes per byte: byte j of a row holds element 2j in bits 0..3 and element
+ *     2j+1 in bits 4..7.
+ *   - Scale: one bf16 per 32 consecutive K elements of a row.  Weight value = E2M1(code) * scale.
+ *   - gate_up weights: codes w13_q [E, 2I, H/2], scales w13_s [E, 2I, H/32]; rows [0, I) are the
+ *     gate projection, rows [I, 2I) the up projection.
+ *   - down weights: codes w2_q [E, H, I/2], scales w2_s [E, H, I/32].
+ *
+ * Numerics: E2M1 codes are exact in bf16; each 32-element group is reduced by bf16 MFMA into an
+ * fp32 partial that is multiplied by the group's scale in fp32; accumulation is fp32.  h (the
+ * SiLU-mul output) is stored as bf16 (round to nearest even), the down-projection output as fp32,
+ * and the combine sums the k slots in fp32 in slot order before one rounding of y to bf16.
+ */
+#ifndef MOE_W4A16_H
+#define MOE_W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status_t;
+
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1)       /* NULL pointer, negative size, k > E, bad enum */
+#define MOE_ERR_UNSUPPORTED_SHAPE (-2) /* size outside the supported range (see each call) */
+#define MOE_ERR_MISALIGNED (-3)        /* a pointer is not 16-byte aligned */
+#define MOE_ERR_WORKSPACE (-4)         /* workspace or tile buffer smaller than required */
+#define MOE_ERR_HIP (-5)               /* a HIP launch failed */
+
+#define MOE_EPI_NONE 0     /* C[r, n] = sum_k A[row(r), k] * W_e[n, k]                          */
+#define MOE_EPI_SILU_MUL 1 /* C[r, j] = silu(G[r, j]) * G[r, N/2 + j], G the NONE result, j < N/2 */
+
+#define MOE_OUT_BF16 0
+#define MOE_OUT_F32 1
+
+#define MOE_MAX_EXPERTS 1024
+
+/* Version of this interface (incremented on any incompatible change). */
+int32_t moe_abi_version(void);
+
+/* Static text of a status code. */
+const char* moe_status_string(moe_status_t status);
+
+/* Text of the most recent failure on the calling host thread ("" if none).  Valid until the
+ * thread's next call into the library. */
+const char* moe_last_error(void);
+
+/*
+ * Top-k routing [ATOM, 8.1]: for each token t, softmax over the E router logits, keep the k
+ * largest probabilities and renormalise them to sum to 1.
+ *   logits    fp32 [T, E] row-major, finite values.
+ *   topk_ids  int32 [T, k] out: expert ids; slot 0 holds the largest logit.  Equal logits are
+ *             ordered by lower expert id; the ids of one token are distinct.
+ *   topk_w    fp32 [T, k] out: renormalised weights, w_s = exp(l_s - l_0) / sum_j exp(l_j - l_0).
+ * Shapes: T >= 0 (T == 0 launches nothing), 1 <= k <= E <= MOE_MAX_EXPERTS.
+ * Alignment: 4 bytes suffices for all three pointers.
+ */
+moe_status_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids,
+                            float* topk_w, void* stream);
+
+/*
+ * Upper bound on the number of row tiles moe_align can emit: floor(T*k / block_m) + min(E, T*k).
+ * Host-only, pure.  Returns -1 for invalid arguments.
+ */
+int32_t moe_max_tiles(int32_t T, int32_t k, int32_t E, int32_t block_m);
+
+/* Device scratch bytes moe_align needs for these sizes (0 when it runs in one workgroup). */
+size_t moe_align_workspace_bytes(int32_t T, int32_t k, int32_t E);
+
+/*
+ * Token -> expert permutation (moe_align) [Atlas, 编译时内核选择和W4A16 Grouped GEMM: per-expert
+ * row tiles; KV Cache量化…调试工具链: the max_m_tiles failure mode].  A stable counting sort of the
+ * R = T*k flat slots f = t*k + s by expert id topk_ids[f]:
+ *   expert_counts  int32 [E]    out: rows routed to each expert.
+ *   expert_offsets int32 [E+1]  out: exclusive prefix sum of the counts; offsets[E] = R.
+ *   sorted_ids     int32 [R]    out: the flat slot at permuted row r; within an expert the slots
+ *                               appear in ascending f, experts in ascending id.
+ *   inv_perm       int32 [R]    out: permuted row of flat slot f (inverse of sorted_ids).
+ *   tiles          int32 [max_tiles, 3] out: (expert, first permuted row, rows <= block_m) for each
+ *                               block of up to block_m consecutive rows of one expert, experts
+ *                               ascending then rows ascending.  Entries past *num_tiles are unused.
+ *   num_tiles      int32 [1]    out: number of tiles written (stays on the device).
+ *   workspace      device scratch of at least moe_align_workspace_bytes(T, k, E) bytes (may be
+ *                  NULL when that is 0).
+ * Shapes: T >= 0, 1 <= k <= E <= MOE_MAX_EXPERTS, 1 <= block_m <= 4096,
+ *         max_tiles >= moe_max_tiles(T, k, E, block_m), T*k < 2^26.
+ * topk_ids must hold ids in [0, E) with no repeats within a token (as moe_route_topk produces).
+ */
+moe_status_t moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t block_m,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_ids,
+                       int32_t* inv_perm, int32_t* tiles, int32_t max_tiles, int32_t* num_tiles,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Grouped W4A16 GEMM, one launch over all experts [Atlas, 编译时内核选择和W4A16 Grouped GEMM].
+ * For every tile (e, row0, rows) of `tiles` and every permuted row r in [row0, row0+rows):
+ *   a(r) = a_row_of ? a_row_of[r] / a_row_div : r                (activation row)
+ *   G[r, n] = sum_{kk<K} A[a(r), kk] * E2M1(Wq[e, n, kk]) * Ws[e, n, kk/32]      (n < N)
+ *   MOE_EPI_NONE:     C[r, n] = G[r, n]                                  C is [R_out, N]
+ *   MOE_EPI_SILU_MUL: C[r, j] = silu(G[r, j]) * G[r, N/2 + j]            C is [R_out, N/2]
+ * with silu(g) = g / (1 + exp(-g)) [RustDL, 四、算子融合].  Rows of C that no tile covers are not
+ * written.
+ *   A          bf16 [*, K] row-major activations (gate_up: the tokens x, with a_row_of = sorted_ids
+ *              and a_row_div = k; down: h in permuted order with a_row_of = NULL).
+ *   Wq, Ws     [E, N, K/2] codes and [E, N, K/32] bf16 scales (the weight format above).
+ *   tiles, num_tiles  as written by moe_align with the same block_m; max_tiles is the capacity
+ *              passed to moe_align (it sizes the launch; tiles past *num_tiles cost nothing).
+ *   block_m    one of 16, 32, 64, 128.
+ *   out_dtype  MOE_OUT_BF16 (round to nearest even) or MOE_OUT_F32; SILU_MUL requires BF16.
+ * Shapes: 1 <= E <= MOE_MAX_EXPERTS, N >= 1 (N even for SILU_MUL), K % 32 == 0, K >= 32.
+ * Alignment: A, Wq, C 16 bytes; Ws 2 bytes.
+ */
+moe_status_t moe_grouped_gemm_w4a16(const uint16_t* A, const int32_t* a_row_of, int32_t a_row_div,
+                                    const uint8_t* Wq, const uint16_t* Ws, int32_t E, int32_t N,
+                                    int32_t K, const int32_t* tiles, int32_t max_tiles,
+                                    const int32_t* num_tiles, int32_t block_m, int32_t epilogue,
+                                    void* C, int32_t out_dtype, void* stream);
+
+/*
+ * Routing-weighted scatter-reduce (combine) [ATOM, 8.1]:
+ *   y[t, c] = bf16( sum_{s=0}^{k-1} topk_w[t, s] * O[inv_perm[t*k + s], c] )
+ * summed in fp32 in ascending slot order, rounded once to bf16.
+ *   O fp32 [T*k, H] (expert outputs in permuted row order); inv_perm int32 [T*k];
+ *   topk_w fp32 [T, k]; y bf16 [T, H] out.
+ * Shapes: T >= 0, k >= 1, H % 8 == 0.
+ */
+moe_status_t moe_combine(const float* O, const int32_t* inv_perm, const float* topk_w, int32_t T,
+                         int32_t k, int32_t H, uint16_t* y, void* stream);
+
+/* Row-tile height (block_m) moe_ffn_forward uses for these sizes (host-only, pure; -1 on invalid
+ * sizes).  Lets a caller run the same launch configuration through the separate entry points. */
+int32_t moe_ffn_block_m(int32_t T, int32_t E, int32_t k);
+
+/* Workspace bytes moe_ffn_forward needs for these sizes (host-only, pure; 0 on invalid sizes). */
+size_t moe_ffn_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k);
+
+/*
+ * The whole MoE FFN layer [ATOM, 8.1; Atlas, 编译时内核选择和W4A16 Grouped GEMM]:
+ *   route (moe_route_topk) -> permute (moe_align) -> gate_up grouped GEMM with SiLU*mul fused
+ *   -> down grouped GEMM -> combine, all enqueued on `stream`:
+ *   y[t] = sum_s w[t,s] * W2_e(s) ( silu(W1_e(s) x[t]) * (W3_e(s) x[t]) ),  e(s) = topk_ids[t, s].
+ *   x bf16 [T, H]; router_logits fp32 [T, E]; weights in the format above; y bf16 [T, H] out.
+ *   topk_ids_out int32 [T, k], topk_w_out fp32 [T, k]: optional copies of the routing (NULL = skip).
+ *   workspace: device scratch of at least moe_ffn_workspace_bytes(T, H, I, E, k) bytes.
+ * Shapes: T >= 0 (T == 0 launches nothing), 1 <= k <= E <= MOE_MAX_EXPERTS, H % 32 == 0,
+ *         I % 32 == 0, H >= 32, I >= 32, T*k < 2^26.
+ */
+moe_status_t moe_ffn_forward(const uint16_t* x, const float* router_logits, int32_t T, int32_t H,
+                             int32_t I, int32_t E, int32_t k, const uint8_t* w13_q,
+                             const uint16_t* w13_s, const uint8_t* w2_q, const uint16_t* w2_s,
+                             uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4A16_H */

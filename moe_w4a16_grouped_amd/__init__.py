@@ -1,0 +1,13 @@
+"""MI355X-native MoE W4A16 layer: Python binding of libmoe_w4a16 (HIP, gfx950).
+
+The package holds the HIP sources (``csrc/``), their build script (``build.py``) and a ctypes binding
+(``_lib.py``) whose functions carry the names of the C entry points declared in
+``include/moe_w4a16.h``.
+"""
+from ._lib import (MOE_EPI_NONE, MOE_EPI_SILU_MUL, MOE_OUT_BF16, MOE_OUT_F32, EXPORTED, LIB_PATH, MoEError,
+                   load, moe_align, moe_align_workspace_bytes, moe_combine, moe_ffn_block_m, moe_ffn_forward,
+                   moe_ffn_workspace_bytes, moe_grouped_gemm_w4a16, moe_max_tiles, moe_route_topk)
+
+__all__ = ["MOE_EPI_NONE", "MOE_EPI_SILU_MUL", "MOE_OUT_BF16", "MOE_OUT_F32", "EXPORTED", "LIB_PATH",
+           "MoEError", "load", "moe_align", "moe_align_workspace_bytes", "moe_combine", "moe_ffn_block_m", "moe_ffn_forward",
+           "moe_ffn_workspace_bytes", "moe_grouped_gemm_w4a16", "moe_max_tiles", "moe_route_topk"]

@@ -1,0 +1,196 @@
+"""ctypes binding of libmoe_w4a16.so: argument marshalling only.
+
+Each function has the name of the C entry point it calls, takes torch tensors on the GPU, passes
+their data pointers and the current HIP stream, and raises ``MoEError`` on a negative status.  Every
+step of the layer runs in the HIP kernels of the library; there is no fallback of any kind: if the
+library is not built, loading fails with an error that says how to build it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "libmoe_w4a16.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED_SHAPE = -2
+MOE_ERR_MISALIGNED = -3
+MOE_ERR_WORKSPACE = -4
+MOE_ERR_HIP = -5
+MOE_EPI_NONE = 0
+MOE_EPI_SILU_MUL = 1
+MOE_OUT_BF16 = 0
+MOE_OUT_F32 = 1
+
+_lib = None
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m moe_w4a16_grouped_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "moe_abi_version": ([], I32),
+        "moe_status_string": ([I32], ctypes.c_char_p),
+        "moe_last_error": ([], ctypes.c_char_p),
+        "moe_route_topk": ([P, I32, I32, I32, P, P, P], I32),
+        "moe_max_tiles": ([I32, I32, I32, I32], I32),
+        "moe_align_workspace_bytes": ([I32, I32, I32], SZ),
+        "moe_align": ([P, I32, I32, I32, I32, P, P, P, P, P, I32, P, P, SZ, P], I32),
+        "moe_grouped_gemm_w4a16": ([P, P, I32, P, P, I32, I32, I32, P, I32, P, I32, I32, P, I32, P], I32),
+        "moe_combine": ([P, P, P, I32, I32, I32, P, P], I32),
+        "moe_ffn_block_m": ([I32, I32, I32], I32),
+        "moe_ffn_workspace_bytes": ([I32, I32, I32, I32, I32], SZ),
+        "moe_ffn_forward": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, SZ, P], I32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+EXPORTED = ("moe_abi_version", "moe_status_string", "moe_last_error", "moe_route_topk", "moe_max_tiles",
+            "moe_align_workspace_bytes", "moe_align", "moe_grouped_gemm_w4a16", "moe_combine",
+            "moe_ffn_block_m", "moe_ffn_workspace_bytes", "moe_ffn_forward")
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        lib = load()
+        raise MoEError(status, f"{lib.moe_status_string(status).decode()}: {lib.moe_last_error().decode()}")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _req(t, dtype, name):
+    ok = t.element_size() == 2 if dtype == "16bit" else t.dtype == dtype
+    if not ok or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor (got {t.dtype}, {t.device})")
+    return t
+
+
+# ---- entry points ----------------------------------------------------------------------------------
+
+def moe_max_tiles(T: int, k: int, E: int, block_m: int) -> int:
+    return int(load().moe_max_tiles(T, k, E, block_m))
+
+
+def moe_align_workspace_bytes(T: int, k: int, E: int) -> int:
+    return int(load().moe_align_workspace_bytes(T, k, E))
+
+
+def moe_ffn_block_m(T: int, E: int, k: int) -> int:
+    return int(load().moe_ffn_block_m(T, E, k))
+
+
+def moe_ffn_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:
+    return int(load().moe_ffn_workspace_bytes(T, H, I, E, k))
+
+
+def moe_route_topk(logits: torch.Tensor, k: int, topk_ids=None, topk_w=None, stream=None):
+    """logits fp32 [T, E] -> (topk_ids int32 [T, k], topk_w fp32 [T, k])."""
+    _req(logits, torch.float32, "logits")
+    T, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(load().moe_route_topk(_p(logits), T, E, k, _p(topk_ids), _p(topk_w), _stream(stream)))
+    return topk_ids, topk_w
+
+
+def moe_align(topk_ids: torch.Tensor, E: int, block_m: int, stream=None) -> dict:
+    """topk_ids int32 [T, k] -> dict of device tensors (counts, offsets, sorted_ids, inv_perm, tiles,
+    num_tiles) and the tile capacity ``max_tiles``."""
+    _req(topk_ids, torch.int32, "topk_ids")
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    R = T * k
+    max_tiles = moe_max_tiles(T, k, E, block_m)
+    out = dict(
+        counts=torch.empty(E, dtype=torch.int32, device=dev),
+        offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+        sorted_ids=torch.empty(max(R, 1), dtype=torch.int32, device=dev),
+        inv_perm=torch.empty(max(R, 1), dtype=torch.int32, device=dev),
+        tiles=torch.empty((max(max_tiles, 1), 3), dtype=torch.int32, device=dev),
+        num_tiles=torch.empty(1, dtype=torch.int32, device=dev),
+    )
+    wsb = moe_align_workspace_bytes(T, k, E)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev) if wsb else None
+    _check(load().moe_align(_p(topk_ids), T, k, E, block_m, _p(out["counts"]), _p(out["offsets"]),
+                            _p(out["sorted_ids"]), _p(out["inv_perm"]), _p(out["tiles"]), max_tiles,
+                            _p(out["num_tiles"]), _p(ws), wsb, _stream(stream)))
+    out["max_tiles"] = max_tiles
+    out["_workspace"] = ws
+    return out
+
+
+def moe_grouped_gemm_w4a16(A, a_row_of, a_row_div: int, Wq, Ws, tiles, max_tiles: int, num_tiles,
+                           block_m: int, epilogue: int, out_rows: int, out_dtype: int = MOE_OUT_BF16,
+                           C=None, stream=None):
+    """Grouped W4A16 GEMM over the tile list; returns C ([out_rows, N] or [out_rows, N/2])."""
+    _req(A, "16bit", "A")
+    _req(Wq, torch.uint8, "Wq")
+    E, N, K2 = Wq.shape
+    K = 2 * K2
+    ncols = N // 2 if epilogue == MOE_EPI_SILU_MUL else N
+    if C is None:
+        dt = torch.float32 if out_dtype == MOE_OUT_F32 else torch.bfloat16
+        C = torch.empty((out_rows, ncols), dtype=dt, device=A.device)
+    _check(load().moe_grouped_gemm_w4a16(_p(A), _p(a_row_of), a_row_div, _p(Wq), _p(Ws), E, N, K, _p(tiles),
+                                         max_tiles, _p(num_tiles), block_m, epilogue, _p(C), out_dtype,
+                                         _stream(stream)))
+    return C
+
+
+def moe_combine(O, inv_perm, topk_w, y=None, stream=None):
+    """O fp32 [T*k, H], inv_perm int32 [T*k], topk_w fp32 [T, k] -> y bf16 [T, H]."""
+    _req(O, torch.float32, "O")
+    T, k = topk_w.shape
+    H = O.shape[1]
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=O.device)
+    _check(load().moe_combine(_p(O), _p(inv_perm), _p(topk_w), T, k, H, _p(y), _stream(stream)))
+    return y
+
+
+def moe_ffn_forward(x, router_logits, w13_q, w13_s, w2_q, w2_s, k: int, y=None, topk_ids_out=None,
+                    topk_w_out=None, workspace=None, stream=None):
+    """Whole layer: x bf16 [T, H], logits fp32 [T, E], weights in the W4 group-32 format -> y bf16."""
+    T, H = x.shape
+    E, N13, _ = w13_q.shape
+    I = N13 // 2
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    wsb = moe_ffn_workspace_bytes(T, H, I, E, k)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=x.device)
+    _check(load().moe_ffn_forward(_p(x), _p(router_logits), T, H, I, E, k, _p(w13_q), _p(w13_s), _p(w2_q),
+                                  _p(w2_s), _p(y), _p(topk_ids_out), _p(topk_w_out), _p(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y

@@ -1,0 +1,214 @@
+// moe_align: stable counting sort of the R = T*k flat routing slots by expert id, plus the per-expert
+// row-tile list that sizes the grouped GEMM launches.
+//
+// The Atlas page ("告别Python堆栈：Atlas用纯Rust重写LLM推理，在GB10上跑赢vLLM"), section
+// "编译时内核选择和W4A16 Grouped GEMM", launches its grouped GEMM over (N tiles, max_m_tiles, experts);
+// section "KV Cache量化、MTP推测解码和调试工具链" reports a broken max_m_tiles heuristic and a missing
+// zero-init as real bugs.  Here the exact tile list and its length are produced on the device, and
+// every output is written in full (no output relies on prior zeroing).
+//
+// Ranking within a wave: the lanes holding the same expert id ("peers") are found with one ballot
+// per id bit; a lane's rank among its peers is the popcount of the peers below it, so the order is
+// ascending flat index (stable) without atomics.  Across waves and workgroups, per-segment counts
+// are turned into per-segment base offsets by a prefix sum in (segment, expert) order.
+#include "launch.h"
+#include "moe_common.h"
+
+namespace moe {
+
+__device__ __forceinline__ uint64_t peer_mask(int id, bool valid, int nbits) {
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (id >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    m &= bit ? bal : ~bal;
+  }
+  return valid ? m : 0ull;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Exclusive scan of (a, b) over the threads of a 1024-thread block; also returns the totals.
+// scratch: 32 ints of LDS.
+__device__ void block_exclusive_scan2(int a, int b, int& ea, int& eb, int& ta, int& tb, int* scratch) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ia = wave_inclusive_scan(a, lane), ib = wave_inclusive_scan(b, lane);
+  if (lane == 63) { scratch[wave] = ia; scratch[16 + wave] = ib; }
+  __syncthreads();
+  if (wave == 0) {
+    const int va = lane < 16 ? scratch[lane] : 0, vb = lane < 16 ? scratch[16 + lane] : 0;
+    const int sa = wave_inclusive_scan(va, lane), sb = wave_inclusive_scan(vb, lane);
+    if (lane < 16) { scratch[lane] = sa - va; scratch[16 + lane] = sb - vb; }
+    if (lane == 15) { scratch[32] = sa; scratch[33] = sb; }
+  }
+  __syncthreads();
+  ea = scratch[wave] + ia - a;
+  eb = scratch[16 + wave] + ib - b;
+  ta = scratch[32];
+  tb = scratch[33];
+}
+
+// Per-expert epilogue shared by both paths: thread e owns expert e.  seg_cnt holds per-segment
+// counts for expert e at seg_cnt[s * E + e]; they are replaced by absolute base rows.
+__device__ void finish_expert(int e, int E, int nseg, int bm, int32_t* seg_cnt, int32_t* counts,
+                              int32_t* offsets, int32_t* tiles, int max_tiles, int32_t* num_tiles,
+                              int* scratch) {
+  int c = 0;
+  if (e < E) {
+    for (int s = 0; s < nseg; ++s) {
+      const int tmp = seg_cnt[s * E + e];
+      seg_cnt[s * E + e] = c;
+      c += tmp;
+    }
+  }
+  const int nt = (c + bm - 1) / bm;
+  int off, toff, total_c, total_t;
+  block_exclusive_scan2(c, nt, off, toff, total_c, total_t, scratch);
+  if (e < E) {
+    counts[e] = c;
+    offsets[e] = off;
+    for (int s = 0; s < nseg; ++s) seg_cnt[s * E + e] += off;
+    for (int i = 0; i < nt && toff + i < max_tiles; ++i) {
+      int32_t* t = tiles + 3 * (size_t)(toff + i);
+      t[0] = e;
+      t[1] = off + i * bm;
+      t[2] = min(bm, c - i * bm);
+    }
+  }
+  if (threadIdx.x == 0) {
+    offsets[E] = total_c;
+    num_tiles[0] = total_t;
+  }
+}
+
+// Count segment [f0, f1) of one wave into cnt[id].
+__device__ __forceinline__ void wave_count(const int32_t* ids, int f0, int f1, int nbits, int32_t* cnt) {
+  const int lane = threadIdx.x & 63;
+  for (int base = f0; base < f1; base += 64) {
+    const int f = base + lane;
+    const bool v = f < f1;
+    const int id = v ? ids[f] : 0;
+    const uint64_t peers = peer_mask(id, v, nbits);
+    if (v && lane == __ffsll((unsigned long long)peers) - 1) cnt[id] += __popcll(peers);
+  }
+}
+
+// Scatter segment [f0, f1) of one wave; base[id] is the next free permuted row of expert id.
+__device__ __forceinline__ void wave_scatter(const int32_t* ids, int f0, int f1, int nbits, int32_t* base,
+                                             int32_t* sorted_ids, int32_t* inv_perm) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int b0 = f0; b0 < f1; b0 += 64) {
+    const int f = b0 + lane;
+    const bool v = f < f1;
+    const int id = v ? ids[f] : 0;
+    const uint64_t peers = peer_mask(id, v, nbits);
+    const int b = v ? base[id] : 0;
+    if (v) {
+      const int r = b + __popcll(peers & below);
+      sorted_ids[r] = f;
+      inv_perm[f] = r;
+    }
+    // one lane per expert advances its base; every lane of the wave has read it above
+    if (v && lane == __ffsll((unsigned long long)peers) - 1) base[id] = b + __popcll(peers);
+  }
+}
+
+// Whole permutation in one 1024-thread workgroup (R <= kAlignSingleMaxR, E <= kAlignSingleMaxE).
+__global__ __launch_bounds__(1024) void align_single_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                            int bm, int nbits, int32_t* counts,
+                                                            int32_t* offsets, int32_t* sorted_ids,
+                                                            int32_t* inv_perm, int32_t* tiles,
+                                                            int max_tiles, int32_t* num_tiles) {
+  extern __shared__ int32_t smem[];
+  int32_t* cnt = smem;             // [16][E]
+  int* scratch = smem + 16 * E;    // 34 ints
+  const int tid = threadIdx.x, wave = tid >> 6;
+  for (int i = tid; i < 16 * E; i += 1024) cnt[i] = 0;
+  __syncthreads();
+  const int seg = (((R + 15) / 16) + 63) & ~63;
+  const int f0 = min(R, wave * seg), f1 = min(R, f0 + seg);
+  wave_count(ids, f0, f1, nbits, cnt + wave * E);
+  __syncthreads();
+  finish_expert(tid, E, 16, bm, cnt, counts, offsets, tiles, max_tiles, num_tiles, scratch);
+  __syncthreads();
+  wave_scatter(ids, f0, f1, nbits, cnt + wave * E, sorted_ids, inv_perm);
+}
+
+// Multi-workgroup path, step 1: per-(workgroup, wave) counts, kAlignChunk slots per workgroup.
+__global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                         int nbits, int32_t* seg_cnt) {
+  extern __shared__ int32_t cnt[];  // [4][E]
+  const int tid = threadIdx.x, wave = tid >> 6;
+  for (int i = tid; i < 4 * E; i += 256) cnt[i] = 0;
+  __syncthreads();
+  const int f0 = min(R, blockIdx.x * kAlignChunk + wave * (kAlignChunk / 4));
+  const int f1 = min(R, f0 + kAlignChunk / 4);
+  wave_count(ids, f0, f1, nbits, cnt + wave * E);
+  __syncthreads();
+  for (int i = tid; i < 4 * E; i += 256) seg_cnt[(size_t)blockIdx.x * 4 * E + i] = cnt[i];
+}
+
+// Step 2: one 1024-thread workgroup turns segment counts into base rows, writes counts, offsets,
+// tiles and the tile count.
+__global__ __launch_bounds__(1024) void align_scan_kernel(int32_t* seg_cnt, int nseg, int E, int bm,
+                                                          int32_t* counts, int32_t* offsets,
+                                                          int32_t* tiles, int max_tiles,
+                                                          int32_t* num_tiles) {
+  __shared__ int scratch[40];
+  finish_expert(threadIdx.x, E, nseg, bm, seg_cnt, counts, offsets, tiles, max_tiles, num_tiles, scratch);
+}
+
+// Step 3: each wave re-walks its segment and scatters from its base rows.
+__global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                            int nbits, const int32_t* seg_base,
+                                                            int32_t* sorted_ids, int32_t* inv_perm) {
+  extern __shared__ int32_t base[];  // [4][E]
+  const int tid = threadIdx.x, wave = tid >> 6;
+  for (int i = tid; i < 4 * E; i += 256) base[i] = seg_base[(size_t)blockIdx.x * 4 * E + i];
+  __syncthreads();
+  const int f0 = min(R, blockIdx.x * kAlignChunk + wave * (kAlignChunk / 4));
+  const int f1 = min(R, f0 + kAlignChunk / 4);
+  wave_scatter(ids, f0, f1, nbits, base + wave * E, sorted_ids, inv_perm);
+}
+
+static int id_bits(int E) {
+  int b = 0;
+  while ((1 << b) < E) ++b;
+  return b;
+}
+
+size_t align_workspace_bytes(int R, int E) {
+  if (R <= kAlignSingleMaxR && E <= kAlignSingleMaxE) return 0;
+  const size_t nblk = (size_t)(R + kAlignChunk - 1) / kAlignChunk;
+  return nblk * 4 * (size_t)E * sizeof(int32_t);
+}
+
+hipError_t launch_align(const int32_t* ids, int R, int E, int block_m, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted_ids, int32_t* inv_perm, int32_t* tiles,
+                        int max_tiles, int32_t* num_tiles, void* workspace, hipStream_t stream) {
+  const int nbits = id_bits(E);
+  if (R <= kAlignSingleMaxR && E <= kAlignSingleMaxE) {
+    const size_t lds = (16 * (size_t)E + 40) * sizeof(int32_t);
+    align_single_kernel<<<1, 1024, lds, stream>>>(ids, R, E, block_m, nbits, counts, offsets, sorted_ids,
+                                                  inv_perm, tiles, max_tiles, num_tiles);
+    return hipGetLastError();
+  }
+  const int nblk = (R + kAlignChunk - 1) / kAlignChunk;
+  int32_t* seg = static_cast<int32_t*>(workspace);
+  const size_t lds = 4 * (size_t)E * sizeof(int32_t);
+  align_hist_kernel<<<nblk, 256, lds, stream>>>(ids, R, E, nbits, seg);
+  align_scan_kernel<<<1, 1024, 0, stream>>>(seg, nblk * 4, E, block_m, counts, offsets, tiles, max_tiles,
+                                            num_tiles);
+  align_scatter_kernel<<<nblk, 256, lds, stream>>>(ids, R, E, nbits, seg, sorted_ids, inv_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe

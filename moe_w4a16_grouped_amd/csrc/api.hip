@@ -1,0 +1,252 @@
+// C-ABI of libmoe_w4a16: host-side validation, workspace carving and launch sequencing.
+// Every entry point validates its arguments before launching anything, reports failures through a
+// status code plus a thread-local message, and only enqueues work on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "launch.h"
+#include "moe_w4a16.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status_t fail(moe_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe_status_t ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
+
+constexpr int64_t kMaxRows = int64_t(1) << 26;
+
+moe_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+moe_status_t check_routing_shape(int32_t T, int32_t E, int32_t k) {
+  if (T < 0 || E < 1 || k < 1) return fail(MOE_ERR_INVALID_ARG, "need T >= 0, E >= 1, k >= 1 (T=%d E=%d k=%d)", T, E, k);
+  if (k > E) return fail(MOE_ERR_INVALID_ARG, "k=%d exceeds E=%d", k, E);
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E=%d exceeds %d", E, MOE_MAX_EXPERTS);
+  if ((int64_t)T * k >= kMaxRows) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "T*k=%lld must be < 2^26", (long long)T * k);
+  return MOE_OK;
+}
+
+int64_t max_tiles_of(int64_t R, int64_t E, int64_t bm) { return R / bm + std::min<int64_t>(E, R); }
+
+// Row tile height for the grouped GEMMs given the average rows per expert.
+int32_t pick_block_m(int64_t R, int64_t E) {
+  const int64_t avg = (R + E - 1) / E;
+  if (avg <= 16) return 16;
+  if (avg <= 32) return 32;
+  if (avg <= 64) return 64;
+  return 128;
+}
+
+// Workspace carve-up for moe_ffn_forward (each region 256-byte aligned).
+struct FfnLayout {
+  size_t ids, w, counts, offsets, sorted, inv, tiles, ntiles, align_ws, h, o, total;
+  int32_t block_m, max_tiles;
+};
+
+size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+
+FfnLayout ffn_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
+  FfnLayout L{};
+  const int64_t R = T * k;
+  L.block_m = pick_block_m(R, E);
+  L.max_tiles = (int32_t)max_tiles_of(R, E, L.block_m);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += up256(bytes); return at; };
+  L.ids = take(R * 4);
+  L.w = take(R * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.sorted = take(R * 4);
+  L.inv = take(R * 4);
+  L.tiles = take((size_t)std::max(L.max_tiles, 1) * 12);
+  L.ntiles = take(4);
+  L.align_ws = take(moe::align_workspace_bytes((int)R, (int)E));
+  L.h = take((size_t)R * I * 2);
+  L.o = take((size_t)R * H * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return 1; }
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "MOE_ERR_UNSUPPORTED_SHAPE";
+    case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+moe_status_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids,
+                            float* topk_w, void* stream) {
+  if (moe_status_t st = check_routing_shape(T, E, k)) return st;
+  if (T == 0) return ok();
+  if (!logits || !topk_ids || !topk_w) return fail(MOE_ERR_INVALID_ARG, "moe_route_topk: NULL pointer");
+  if (!aligned4(logits) || !aligned4(topk_ids) || !aligned4(topk_w))
+    return fail(MOE_ERR_MISALIGNED, "moe_route_topk: pointers must be 4-byte aligned");
+  return hip_status(moe::launch_route_topk(logits, T, E, k, topk_ids, topk_w, (hipStream_t)stream),
+                    "moe_route_topk launch");
+}
+
+int32_t moe_max_tiles(int32_t T, int32_t k, int32_t E, int32_t block_m) {
+  if (T < 0 || k < 1 || E < 1 || block_m < 1) return -1;
+  const int64_t v = max_tiles_of((int64_t)T * k, E, block_m);
+  return v > INT32_MAX ? -1 : (int32_t)v;
+}
+
+size_t moe_align_workspace_bytes(int32_t T, int32_t k, int32_t E) {
+  if (T < 0 || k < 1 || E < 1 || (int64_t)T * k >= kMaxRows) return 0;
+  return moe::align_workspace_bytes(T * k, E);
+}
+
+moe_status_t moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t block_m,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_ids,
+                       int32_t* inv_perm, int32_t* tiles, int32_t max_tiles, int32_t* num_tiles,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (moe_status_t st = check_routing_shape(T, E, k)) return st;
+  if (block_m < 1 || block_m > 4096) return fail(MOE_ERR_INVALID_ARG, "moe_align: block_m=%d outside [1, 4096]", block_m);
+  const int64_t R = (int64_t)T * k;
+  if (!expert_counts || !expert_offsets || !num_tiles || (R > 0 && (!topk_ids || !sorted_ids || !inv_perm || !tiles)))
+    return fail(MOE_ERR_INVALID_ARG, "moe_align: NULL pointer");
+  for (const void* p : {(const void*)topk_ids, (const void*)expert_counts, (const void*)expert_offsets,
+                        (const void*)sorted_ids, (const void*)inv_perm, (const void*)tiles, (const void*)num_tiles})
+    if (p && !aligned4(p)) return fail(MOE_ERR_MISALIGNED, "moe_align: pointers must be 4-byte aligned");
+  const int64_t need_tiles = max_tiles_of(R, E, block_m);
+  if (max_tiles < need_tiles)
+    return fail(MOE_ERR_WORKSPACE, "moe_align: max_tiles=%d < required %lld", max_tiles, (long long)need_tiles);
+  const size_t need_ws = moe::align_workspace_bytes((int)R, E);
+  if (workspace_bytes < need_ws || (need_ws > 0 && !workspace))
+    return fail(MOE_ERR_WORKSPACE, "moe_align: workspace %zu B < required %zu B", workspace_bytes, need_ws);
+  if (need_ws > 0 && !aligned16(workspace)) return fail(MOE_ERR_MISALIGNED, "moe_align: workspace must be 16-byte aligned");
+  return hip_status(moe::launch_align(topk_ids, (int)R, E, block_m, expert_counts, expert_offsets, sorted_ids,
+                                      inv_perm, tiles, max_tiles, num_tiles, workspace, (hipStream_t)stream),
+                    "moe_align launch");
+}
+
+moe_status_t moe_grouped_gemm_w4a16(const uint16_t* A, const int32_t* a_row_of, int32_t a_row_div,
+                                    const uint8_t* Wq, const uint16_t* Ws, int32_t E, int32_t N,
+                                    int32_t K, const int32_t* tiles, int32_t max_tiles,
+                                    const int32_t* num_tiles, int32_t block_m, int32_t epilogue,
+                                    void* C, int32_t out_dtype, void* stream) {
+  if (E < 1 || N < 1 || K < 1 || max_tiles < 0) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_w4a16: need E, N, K >= 1, max_tiles >= 0");
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E=%d exceeds %d", E, MOE_MAX_EXPERTS);
+  if (K % 32 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "K=%d must be a multiple of 32", K);
+  if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "block_m=%d must be 16, 32, 64 or 128", block_m);
+  if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SILU_MUL) return fail(MOE_ERR_INVALID_ARG, "unknown epilogue %d", epilogue);
+  if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return fail(MOE_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
+  if (epilogue == MOE_EPI_SILU_MUL && (N % 2 != 0 || out_dtype != MOE_OUT_BF16))
+    return fail(MOE_ERR_INVALID_ARG, "SILU_MUL needs an even N and bf16 output");
+  if (a_row_of && a_row_div < 1) return fail(MOE_ERR_INVALID_ARG, "a_row_div must be >= 1");
+  if (max_tiles == 0) return ok();
+  if (!A || !Wq || !Ws || !tiles || !num_tiles || !C) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_w4a16: NULL pointer");
+  if (!aligned16(A) || !aligned16(Wq) || !aligned16(C) || !aligned2(Ws) || !aligned4(tiles) || !aligned4(num_tiles) ||
+      (a_row_of && !aligned4(a_row_of)))
+    return fail(MOE_ERR_MISALIGNED, "moe_grouped_gemm_w4a16: A, Wq, C need 16-byte alignment");
+  if ((int64_t)max_tiles * block_m >= kMaxRows + (int64_t)MOE_MAX_EXPERTS * block_m)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "max_tiles=%d too large", max_tiles);
+  moe::GemmArgs a{A, a_row_of, a_row_div, Wq, Ws, N, K, tiles, num_tiles, max_tiles, C, epilogue,
+                  out_dtype == MOE_OUT_F32};
+  return hip_status(moe::launch_grouped_gemm(a, block_m, (hipStream_t)stream), "moe_grouped_gemm_w4a16 launch");
+}
+
+moe_status_t moe_combine(const float* O, const int32_t* inv_perm, const float* topk_w, int32_t T,
+                         int32_t k, int32_t H, uint16_t* y, void* stream) {
+  if (T < 0 || k < 1 || H < 1) return fail(MOE_ERR_INVALID_ARG, "moe_combine: need T >= 0, k >= 1, H >= 1");
+  if (H % 8 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_combine: H=%d must be a multiple of 8", H);
+  if ((int64_t)T * k >= kMaxRows) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "T*k must be < 2^26");
+  if (T == 0) return ok();
+  if (!O || !inv_perm || !topk_w || !y) return fail(MOE_ERR_INVALID_ARG, "moe_combine: NULL pointer");
+  if (!aligned16(O) || !aligned16(y) || !aligned4(inv_perm) || !aligned4(topk_w))
+    return fail(MOE_ERR_MISALIGNED, "moe_combine: O and y need 16-byte alignment");
+  return hip_status(moe::launch_combine(O, inv_perm, topk_w, T, k, H, y, (hipStream_t)stream), "moe_combine launch");
+}
+
+int32_t moe_ffn_block_m(int32_t T, int32_t E, int32_t k) {
+  if (T < 0 || E < 1 || k < 1 || k > E || (int64_t)T * k >= kMaxRows) return -1;
+  return pick_block_m((int64_t)T * k, E);
+}
+
+size_t moe_ffn_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k) {
+  if (T < 0 || H < 1 || I < 1 || E < 1 || k < 1 || k > E || E > MOE_MAX_EXPERTS || (int64_t)T * k >= kMaxRows) return 0;
+  return ffn_layout(T, H, I, E, k).total;
+}
+
+moe_status_t moe_ffn_forward(const uint16_t* x, const float* router_logits, int32_t T, int32_t H,
+                             int32_t I, int32_t E, int32_t k, const uint8_t* w13_q,
+                             const uint16_t* w13_s, const uint8_t* w2_q, const uint16_t* w2_s,
+                             uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (moe_status_t st = check_routing_shape(T, E, k)) return st;
+  if (H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_ffn_forward: H=%d and I=%d must be positive multiples of 32", H, I);
+  if (T == 0) return ok();
+  if (!x || !router_logits || !w13_q || !w13_s || !w2_q || !w2_s || !y || !workspace)
+    return fail(MOE_ERR_INVALID_ARG, "moe_ffn_forward: NULL pointer");
+  if (!aligned16(x) || !aligned16(w13_q) || !aligned16(w2_q) || !aligned16(y) || !aligned16(workspace) ||
+      !aligned4(router_logits) || !aligned2(w13_s) || !aligned2(w2_s) || (topk_ids_out && !aligned4(topk_ids_out)) ||
+      (topk_w_out && !aligned4(topk_w_out)))
+    return fail(MOE_ERR_MISALIGNED, "moe_ffn_forward: x, weights, y and workspace need 16-byte alignment");
+  const FfnLayout L = ffn_layout(T, H, I, E, k);
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "moe_ffn_forward: workspace %zu B < required %zu B", workspace_bytes, L.total);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
+  int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
+  int32_t* ntiles = reinterpret_cast<int32_t*>(ws + L.ntiles);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
+  float* o = reinterpret_cast<float*>(ws + L.o);
+  hipStream_t s = (hipStream_t)stream;
+  const int R = T * k;
+  hipError_t e = moe::launch_route_topk(router_logits, T, E, k, ids, w, s);
+  if (e != hipSuccess) return hip_status(e, "route launch");
+  e = moe::launch_align(ids, R, E, L.block_m, counts, offsets, sorted, inv, tiles, L.max_tiles, ntiles,
+                        ws + L.align_ws, s);
+  if (e != hipSuccess) return hip_status(e, "align launch");
+  moe::GemmArgs g1{x, sorted, k, w13_q, w13_s, 2 * I, H, tiles, ntiles, L.max_tiles, h, MOE_EPI_SILU_MUL, 0};
+  e = moe::launch_grouped_gemm(g1, L.block_m, s);
+  if (e != hipSuccess) return hip_status(e, "gate_up launch");
+  moe::GemmArgs g2{h, nullptr, 1, w2_q, w2_s, H, I, tiles, ntiles, L.max_tiles, o, MOE_EPI_NONE, 1};
+  e = moe::launch_grouped_gemm(g2, L.block_m, s);
+  if (e != hipSuccess) return hip_status(e, "down launch");
+  e = moe::launch_combine(o, inv, w, T, k, H, y, s);
+  return hip_status(e, "combine launch");
+}
+
+}  // extern "C"

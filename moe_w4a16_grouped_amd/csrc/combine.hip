@@ -1,0 +1,46 @@
+// Routing-weighted scatter-reduce ("combine"): y[t] = sum_s w[t,s] * O[inv_perm[t*k+s]].
+// The ATOM page ("AMD ATOM推理引擎：如何用分页KV缓存和分段编译实现大模型推理性能翻倍"), section
+// "8.1 MoE 路径：路由、专家并行与 MORI 通信", names the final combine that gathers each token's expert
+// outputs back.  Slots are summed in fp32 in ascending order (deterministic, no atomics) and y is
+// rounded to bf16 once; every element of y is written.
+#include "launch.h"
+#include "moe_common.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ O,
+                                                      const int32_t* __restrict__ inv_perm,
+                                                      const float* __restrict__ w, int T, int k, int H,
+                                                      uint16_t* __restrict__ y) {
+  const int t = blockIdx.x;
+  const int nvec = H / 8;
+  for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < k; ++s) {
+      const int r = inv_perm[(size_t)t * k + s];
+      const float ws = w[(size_t)t * k + s];
+      const f32x4* src = reinterpret_cast<const f32x4*>(O + (size_t)r * H) + 2 * v;
+      const f32x4 a = src[0], b = src[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] = fmaf(ws, a[i], acc[i]);
+        acc[4 + i] = fmaf(ws, b[i], acc[4 + i]);
+      }
+    }
+    u32x4 out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      out[i] = (uint32_t)f32_to_bf16_bits(acc[2 * i]) | ((uint32_t)f32_to_bf16_bits(acc[2 * i + 1]) << 16);
+    reinterpret_cast<u32x4*>(y + (size_t)t * H)[v] = out;
+  }
+}
+
+hipError_t launch_combine(const float* O, const int32_t* inv_perm, const float* w, int T, int k, int H,
+                          uint16_t* y, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  const int threads = H / 8 >= 256 ? 256 : ((H / 8 + 63) / 64) * 64;
+  combine_kernel<<<T, threads, 0, stream>>>(O, inv_perm, w, T, k, H, y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

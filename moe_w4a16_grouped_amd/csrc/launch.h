@@ -1,0 +1,43 @@
+// Internal host-side launchers (one per kernel family).  Each enqueues on `stream` and returns the
+// launch status; argument validation happens in the C-ABI layer before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_w4a16.h"
+
+namespace moe {
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                             hipStream_t stream);
+
+// Largest R = T*k and E the single-workgroup permutation handles.
+constexpr int kAlignSingleMaxR = 16384;
+constexpr int kAlignSingleMaxE = 512;
+// Flat slots per workgroup in the multi-workgroup permutation.
+constexpr int kAlignChunk = 4096;
+size_t align_workspace_bytes(int R, int E);
+hipError_t launch_align(const int32_t* ids, int R, int E, int block_m, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted_ids, int32_t* inv_perm, int32_t* tiles,
+                        int max_tiles, int32_t* num_tiles, void* workspace, hipStream_t stream);
+
+struct GemmArgs {
+  const uint16_t* A;       // bf16 activations [*, K]
+  const int32_t* a_row_of; // permuted row -> flat index (NULL = identity)
+  int a_row_div;           // activation row = a_row_of[r] / a_row_div
+  const uint8_t* Wq;       // [E, N, K/2]
+  const uint16_t* Ws;      // [E, N, K/32]
+  int N, K;
+  const int32_t* tiles;    // [max_tiles, 3]
+  const int32_t* num_tiles;
+  int max_tiles;
+  void* C;
+  int epilogue;            // MOE_EPI_*
+  int out_f32;
+};
+hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t stream);
+
+hipError_t launch_combine(const float* O, const int32_t* inv_perm, const float* w, int T, int k,
+                          int H, uint16_t* y, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,64 @@
+// Device-side helpers shared by the kernels of libmoe_w4a16 (gfx950 / CDNA4 only).
+//
+// Weight format (the execution contract of the layer, following the ATOM page
+// "AMD ATOM推理引擎：如何用分页KV缓存和分段编译实现大模型推理性能翻倍", section "8.2 量化并非单一格式，
+// 而是一套执行契约": dtype, scale shape and layout are part of the kernel's contract):
+//   * E2M1 4-bit codes, two per byte, the even K index in the low nibble;
+//   * one bf16 scale per 32 consecutive K elements of a weight row (per-1x32 grouping, ATOM page,
+//     section "6.1 Linear：按量化类型分派 GEMM");
+//   * rows are K-contiguous: gate_up [E, 2I, H] (gate rows [0, I), up rows [I, 2I)), down [E, H, I].
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kGroup = 32;    // K elements per scale
+constexpr int kWave = 64;     // CDNA wavefront
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 h = (__bf16)f;  // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// Eight E2M1 codes (one dword, element 0 in the low nibble) -> eight exact bf16 values.
+// The hardware FP4 converter is used with a unit scale, so every code lands exactly on its E2M1
+// value (0, ±0.5, ±1, ±1.5, ±2, ±3, ±4, ±6); the group scale is applied later in fp32.
+__device__ __forceinline__ bf16x8 e2m1x8_to_bf16(uint32_t w) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// 4x4 transpose of dwords across the four 16-lane quarters of a wave.
+// Before: quarter q, register j holds dword j of K-group q (one 16-byte load per lane).
+// After:  register g, quarter q holds dword q of K-group g, which is the B-operand layout of
+//         v_mfma_f32_16x16x32_bf16 for group g (quarter q supplies K elements 8q..8q+7).
+__device__ __forceinline__ u32x4 quarter_transpose(u32x4 v) {
+  auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  return u32x4{c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
+}  // namespace moe

@@ -1,0 +1,135 @@
+"""Host-side tests of the C-ABI library: it loads, exports every function the public header declares,
+and rejects invalid arguments before anything is launched (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_w4a16_grouped_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_w4a16.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(moe_[a-z0-9_]+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return moe.load()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for required in ("moe_align", "moe_grouped_gemm_w4a16", "moe_ffn_forward", "moe_route_topk", "moe_combine"):
+        assert required in names
+    assert set(names) == set(moe.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings(lib):
+    assert lib.moe_abi_version() == 1
+    assert lib.moe_status_string(0) == b"MOE_OK"
+    for code, name in [(-1, b"MOE_ERR_INVALID_ARG"), (-2, b"MOE_ERR_UNSUPPORTED_SHAPE"), (-3, b"MOE_ERR_MISALIGNED"),
+                       (-4, b"MOE_ERR_WORKSPACE"), (-5, b"MOE_ERR_HIP")]:
+        assert lib.moe_status_string(code) == name
+
+
+def test_pure_size_queries(lib):
+    # floor(R / block_m) + min(E, R)
+    assert moe.moe_max_tiles(800, 8, 256, 32) == 6400 // 32 + 256
+    assert moe.moe_max_tiles(1, 8, 128, 16) == 0 + 8
+    assert moe.moe_max_tiles(0, 8, 128, 16) == 0
+    assert moe.moe_max_tiles(-1, 8, 128, 16) == -1
+    assert moe.moe_align_workspace_bytes(64, 8, 128) == 0          # one workgroup
+    assert moe.moe_align_workspace_bytes(8192, 10, 512) == 20 * 4 * 512 * 4
+    ws = moe.moe_ffn_workspace_bytes(800, 2048, 512, 256, 8)
+    R = 800 * 8
+    assert ws >= R * 512 * 2 + R * 2048 * 4  # h (bf16) and the down output (fp32) at least
+    assert moe.moe_ffn_workspace_bytes(4, 2048, 512, 8, 9) == 0    # k > E
+
+
+FAKE = 1 << 20  # an aligned, never-dereferenced pointer value: validation fails before any launch
+
+
+def _ptr(v):
+    return ctypes.c_void_p(v)
+
+
+@pytest.mark.parametrize("T,E,k,expect", [(4, 8, 9, -1), (-1, 8, 2, -1), (4, 0, 1, -1), (4, 2000, 2, -2),
+                                          (1 << 24, 8, 8, -2)])
+def test_route_rejects_bad_shapes(lib, T, E, k, expect):
+    st = lib.moe_route_topk(_ptr(FAKE), T, E, k, _ptr(FAKE), _ptr(FAKE), None)
+    assert st == expect
+    assert lib.moe_last_error()
+
+
+def test_route_zero_tokens_is_a_noop(lib):
+    assert lib.moe_route_topk(None, 0, 8, 2, None, None, None) == 0
+
+
+def test_route_null_and_misaligned(lib):
+    assert lib.moe_route_topk(None, 4, 8, 2, _ptr(FAKE), _ptr(FAKE), None) == -1
+    assert lib.moe_route_topk(_ptr(FAKE + 2), 4, 8, 2, _ptr(FAKE), _ptr(FAKE), None) == -3
+
+
+def test_align_rejects(lib):
+    f = _ptr(FAKE)
+    # too few tiles
+    mt = moe.moe_max_tiles(16, 2, 8, 16)
+    st = lib.moe_align(f, 16, 2, 8, 16, f, f, f, f, f, mt - 1, f, None, 0, None)
+    assert st == -4 and b"max_tiles" in lib.moe_last_error()
+    # multi-workgroup sizes need a workspace
+    mt = moe.moe_max_tiles(8192, 10, 512, 128)
+    st = lib.moe_align(f, 8192, 10, 512, 128, f, f, f, f, f, mt, f, None, 0, None)
+    assert st == -4
+    assert lib.moe_align(f, 16, 2, 8, 0, f, f, f, f, f, 100, f, None, 0, None) == -1
+    assert lib.moe_align(f, 16, 2, 8, 16, f, f, f, f, None, 100, f, None, 0, None) == -1
+    assert lib.moe_align(_ptr(FAKE + 1), 16, 2, 8, 16, f, f, f, f, f, 100, f, None, 0, None) == -3
+
+
+def test_grouped_gemm_rejects(lib):
+    f = _ptr(FAKE)
+    args = dict(A=f, aro=None, div=1, Wq=f, Ws=f, E=8, N=256, K=256, tiles=f, mt=10, nt=f, bm=16, epi=0, C=f,
+                out=0)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.moe_grouped_gemm_w4a16(a["A"], a["aro"], a["div"], a["Wq"], a["Ws"], a["E"], a["N"], a["K"],
+                                          a["tiles"], a["mt"], a["nt"], a["bm"], a["epi"], a["C"], a["out"], None)
+
+    assert call(K=48) == -2            # K not a multiple of 32
+    assert call(bm=24) == -2           # unsupported tile height
+    assert call(epi=7) == -1
+    assert call(epi=1, out=1) == -1    # SiLU*mul writes bf16 only
+    assert call(epi=1, N=255) == -1    # odd N cannot pair gate and up
+    assert call(A=_ptr(FAKE + 8)) == -3
+    assert call(C=None) == -1
+    assert call(E=0) == -1
+    assert call(mt=0) == 0             # nothing to do: no launch
+
+
+def test_combine_and_forward_reject(lib):
+    f = _ptr(FAKE)
+    assert lib.moe_combine(f, f, f, 4, 2, 12, f, None) == -2        # H % 8
+    assert lib.moe_combine(f, f, f, 0, 2, 16, f, None) == 0         # T == 0
+    assert lib.moe_combine(_ptr(FAKE + 4), f, f, 4, 2, 16, f, None) == -3
+    ws = moe.moe_ffn_workspace_bytes(16, 256, 128, 8, 2)
+    fw = lambda **kw: lib.moe_ffn_forward(kw.get("x", f), f, kw.get("T", 16), kw.get("H", 256), kw.get("I", 128),
+                                          kw.get("E", 8), kw.get("k", 2), f, f, f, f, f, None, None, f,
+                                          kw.get("ws", ws), None)
+    assert fw(H=250) == -2
+    assert fw(I=48) == -2
+    assert fw(k=9) == -1
+    assert fw(ws=ws - 1) == -4
+    assert fw(x=_ptr(FAKE + 2)) == -3
+    assert fw(T=0) == 0

@@ -1,0 +1,277 @@
+"""GPU parity: every entry point of libmoe_w4a16 against the CPU oracle on the same seeded inputs.
+
+Integer results (routing ids, counts, offsets, permutation, tiles) must be bit-exact; routing weights
+within 1e-6; layer outputs within max|gpu-ref| <= 3e-2 * rms(ref) and mean relative error <= 5e-3.
+Full-size workloads are checked on sampled tokens (each token's output is independent) in the same
+launch configuration the benchmark times, plus properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU-only hosts, never run there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import moe_w4a16_grouped_amd as moe  # noqa: E402  (loads the HIP library; fails loudly if missing)
+
+_CACHE = {}
+
+
+def workload_inputs(name_or_wl):
+    wl = mi.WORKLOADS[name_or_wl] if isinstance(name_or_wl, str) else name_or_wl
+    key = (wl.name, wl.T, wl.E, wl.k, wl.H, wl.I, wl.skew, wl.seed)
+    if key not in _CACHE:
+        if len(_CACHE) > 3:
+            _CACHE.clear()
+            torch.cuda.empty_cache()
+        inp = mi.make_inputs(wl)
+        _CACHE[key] = (inp, gu.DeviceInputs(inp))
+    return _CACHE[key]
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------------------------------------------
+# routing
+
+ROUTE_CASES = ["tiny", "dec64", "pre800", "big4096", "skew8192"]
+
+
+@pytest.mark.parametrize("name", ROUTE_CASES)
+def test_route_topk_matches_oracle(name):
+    inp, d = workload_inputs(name)
+    ids, w = moe.moe_route_topk(d.logits, inp.wl.k)
+    torch.cuda.synchronize()
+    rid, rw = oracle.route(inp.logits, inp.wl.k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), rid)
+    assert np.abs(w.cpu().numpy().astype(np.float64) - rw).max() <= gu.ROUTE_W_ATOL
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (7, 65, 65), (33, 1024, 16), (130, 64, 6), (5, 3, 2)])
+def test_route_topk_edges_and_ties(T, E, k):
+    rng = np.random.default_rng(T * 1000 + E)
+    logits = rng.integers(-3, 4, (T, E)).astype(np.float32)  # many equal logits: ties by lower id
+    logits[0, ::2] = -0.0
+    logits[0, 1::2] = 0.0
+    ids, w = moe.moe_route_topk(gu.dev(logits), k)
+    torch.cuda.synchronize()
+    rid, rw = oracle.route(logits, k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), rid)
+    assert np.abs(w.cpu().numpy().astype(np.float64) - rw).max() <= gu.ROUTE_W_ATOL
+
+
+# ---------------------------------------------------------------------------------------------------
+# permutation
+
+ALIGN_CASES = [("tiny", 16), ("dec1", 16), ("dec64", 16), ("pre800", 32), ("pre800", 128), ("big4096", 128),
+               ("skew8192", 128), ("skew8192", 16)]
+
+
+def _check_align(got, ref):
+    for key in ("counts", "offsets"):
+        np.testing.assert_array_equal(got[key].cpu().numpy(), ref[key], err_msg=key)
+    R = int(ref["offsets"][-1])
+    np.testing.assert_array_equal(got["sorted_ids"].cpu().numpy()[:R], ref["sorted_ids"])
+    np.testing.assert_array_equal(got["inv_perm"].cpu().numpy()[:R], ref["inv_perm"])
+    nt = int(got["num_tiles"].item())
+    assert nt == ref["num_tiles"]
+    np.testing.assert_array_equal(got["tiles"].cpu().numpy()[:nt], ref["tiles"])
+
+
+@pytest.mark.parametrize("name,bm", ALIGN_CASES)
+def test_align_matches_oracle(name, bm):
+    inp, d = workload_inputs(name)
+    rid, _ = oracle.route(inp.logits, inp.wl.k)
+    got = moe.moe_align(gu.dev(rid), inp.wl.E, bm)
+    torch.cuda.synchronize()
+    _check_align(got, oracle.align(rid, inp.wl.E, bm))
+
+
+@pytest.mark.parametrize("T,E,k,bm", [(0, 8, 2, 16), (1, 1, 1, 16), (5000, 4, 4, 64), (300, 1024, 8, 32),
+                                      (16385, 2, 1, 128), (3000, 600, 6, 16)])
+def test_align_edges(T, E, k, bm):
+    rng = np.random.default_rng(T + 7 * E)
+    ids = np.empty((T, k), np.int32)
+    for t in range(T):
+        if T > 10 and t < T // 2:  # a hot expert: slot 0 of half the tokens goes to expert 0
+            ids[t] = [0, *rng.choice(np.arange(1, E), k - 1, replace=False)]
+        else:
+            ids[t] = rng.choice(E, k, replace=False)
+    got = moe.moe_align(gu.dev(ids) if T else torch.empty((0, k), dtype=torch.int32, device="cuda"), E, bm)
+    torch.cuda.synchronize()
+    _check_align(got, oracle.align(ids, E, bm))
+
+
+# ---------------------------------------------------------------------------------------------------
+# grouped GEMM entry point on its own
+
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("I,H", [(128, 256), (72, 160), (256, 96)])
+def test_grouped_gemm_gate_up_silu_mul(bm, I, H):
+    wl = mi.custom("gg", 150, 8, 3, H, I, skew=True, seed=11)
+    inp, d = workload_inputs(wl)
+    rid, _ = oracle.route(inp.logits, wl.k)
+    a = moe.moe_align(gu.dev(rid), wl.E, bm)
+    R = wl.T * wl.k
+    C = moe.moe_grouped_gemm_w4a16(d.x, a["sorted_ids"], wl.k, d.w13_q, d.w13_s, a["tiles"], a["max_tiles"],
+                                   a["num_tiles"], bm, moe.MOE_EPI_SILU_MUL, R)
+    torch.cuda.synchronize()
+    ra = oracle.align(rid, wl.E, bm)
+    ref = oracle.grouped_proj(inp.x, ra["sorted_ids"], wl.k, inp.w13_q, inp.w13_s, ra["offsets"], silu_mul=True)
+    gu.assert_within_tolerance(gu.host_bf16_to_f64(C), ref, f"gate_up bm={bm}")
+
+
+@pytest.mark.parametrize("bm", [16, 64, 128])
+@pytest.mark.parametrize("out_dtype", [moe.MOE_OUT_F32, moe.MOE_OUT_BF16])
+@pytest.mark.parametrize("N,K", [(256, 128), (200, 160), (48, 1056)])
+def test_grouped_gemm_plain(bm, out_dtype, N, K):
+    E, T, k = 6, 90, 2
+    rng = np.random.default_rng(N + K + bm)
+    logits = rng.standard_normal((T, E), dtype=np.float32)
+    logits[:, 0] += 3.0  # uneven expert sizes, several tiles for expert 0
+    rid, _ = oracle.route(logits, k)
+    R = T * k
+    A = mi.f32_to_bf16_bits(rng.standard_normal((R, K), dtype=np.float32))
+    Wq = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    Ws = mi.f32_to_bf16_bits(rng.uniform(0.005, 0.02, (E, N, K // 32)).astype(np.float32))
+    a = moe.moe_align(gu.dev(rid), E, bm)
+    C = moe.moe_grouped_gemm_w4a16(gu.dev_bf16(A), None, 1, gu.dev(Wq), gu.dev(Ws.view(np.int16)), a["tiles"],
+                                   a["max_tiles"], a["num_tiles"], bm, moe.MOE_EPI_NONE, R, out_dtype)
+    torch.cuda.synchronize()
+    ra = oracle.align(rid, E, bm)
+    ref = oracle.grouped_proj(A, None, 1, Wq, Ws, ra["offsets"])
+    got = C.cpu().numpy().astype(np.float64) if out_dtype == moe.MOE_OUT_F32 else gu.host_bf16_to_f64(C)
+    if out_dtype == moe.MOE_OUT_F32:
+        # bf16 x E2M1 products are exact in fp32; the only error is fp32 summation: at most
+        # (32 + K/32) roundings along any path, so |err| <= (64 + K/32) * 2^-24 * sum|terms|.
+        ref_abs = oracle.grouped_proj(A & 0x7FFF, None, 1, Wq & 0x77, Ws, ra["offsets"])
+        assert np.all(np.abs(got - ref) <= (64 + K / 32) * 2.0 ** -24 * ref_abs)
+    gu.assert_within_tolerance(got, ref, "plain")
+
+
+def test_combine_matches_oracle():
+    T, k, H = 37, 5, 264
+    rng = np.random.default_rng(3)
+    O = rng.standard_normal((T * k, H)).astype(np.float32)
+    inv = rng.permutation(T * k).astype(np.int32)
+    w = rng.uniform(0, 1, (T, k)).astype(np.float32)
+    y = moe.moe_combine(gu.dev(O), gu.dev(inv), gu.dev(w))
+    torch.cuda.synchronize()
+    ref = oracle.combine(O.astype(np.float64), inv, w.astype(np.float64), T, k)
+    got = gu.host_bf16_to_f64(y)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+
+
+# ---------------------------------------------------------------------------------------------------
+# whole layer
+
+def _forward(d, inp, poison=True):
+    wl = inp.wl
+    y = torch.full((wl.T, wl.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ids = torch.full((wl.T, wl.k), -7, dtype=torch.int32, device="cuda")
+    w = torch.full((wl.T, wl.k), float("nan"), dtype=torch.float32, device="cuda")
+    wsb = moe.moe_ffn_workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.k)
+    ws = torch.full((max(wsb, 256),), 0xFF if poison else 0, dtype=torch.uint8, device="cuda")
+    moe.moe_ffn_forward(d.x, d.logits, d.w13_q, d.w13_s, d.w2_q, d.w2_s, wl.k, y=y, topk_ids_out=ids,
+                        topk_w_out=w, workspace=ws)
+    torch.cuda.synchronize()
+    return y, ids, w
+
+
+def _sample_tokens(wl, n):
+    if wl.T <= n:
+        return np.arange(wl.T)
+    rng = np.random.default_rng(99)
+    head = np.arange(min(8, wl.T))
+    rest = rng.choice(np.arange(8, wl.T), n - len(head), replace=False)
+    return np.sort(np.concatenate([head, rest, [wl.T - 1]]))
+
+
+FULL_CASES = [("tiny", 16), ("dec1", 1), ("dec8", 8), ("dec32", 32), ("dec64", 64), ("pre800", 48),
+              ("big4096", 12), ("skew8192", 48)]
+
+
+@pytest.mark.parametrize("name,nsample", FULL_CASES)
+def test_ffn_forward_matches_oracle(name, nsample):
+    inp, d = workload_inputs(name)
+    wl = inp.wl
+    _log(f"ffn_forward {name}: T={wl.T} E={wl.E} k={wl.k} H={wl.H} I={wl.I}")
+    y, ids, w = _forward(d, inp)
+    rid, rw = oracle.route(inp.logits, wl.k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), rid)
+    assert np.abs(w.cpu().numpy().astype(np.float64) - rw).max() <= gu.ROUTE_W_ATOL
+    yh = gu.host_bf16_to_f64(y)
+    assert np.all(np.isfinite(yh)), "output not fully written"
+    tok = _sample_tokens(wl, nsample)
+    ref = oracle.moe_ffn(inp, tokens=tok)
+    r = gu.assert_within_tolerance(yh[tok], ref, name)
+    _log(f"  {name}: {r}")
+
+
+@pytest.mark.parametrize("wl", [
+    mi.custom("one_expert", 3, 1, 1, 256, 128, seed=5),
+    mi.custom("ragged", 37, 16, 4, 160, 96, seed=6),
+    mi.custom("k_eq_E", 20, 6, 6, 128, 64, seed=7),
+    mi.custom("many_experts", 40, 1024, 8, 128, 64, seed=8),
+    mi.custom("t1_big_k", 1, 64, 32, 256, 256, seed=9),
+])
+def test_ffn_forward_edges(wl):
+    inp, d = workload_inputs(wl)
+    y, ids, _ = _forward(d, inp)
+    np.testing.assert_array_equal(ids.cpu().numpy(), oracle.route(inp.logits, wl.k)[0])
+    gu.assert_within_tolerance(gu.host_bf16_to_f64(y), oracle.moe_ffn(inp), wl.name)
+
+
+def test_ffn_forward_hot_expert():
+    wl = mi.custom("hot", 300, 32, 4, 256, 128, seed=12)
+    inp = mi.make_inputs(wl)
+    inp.logits[:, 0] += 50.0  # every token's slot 0 goes to expert 0: ceil(300/BM) tiles there
+    d = gu.DeviceInputs(inp)
+    y, ids, _ = _forward(d, inp)
+    assert np.all(ids.cpu().numpy()[:, 0] == 0)
+    gu.assert_within_tolerance(gu.host_bf16_to_f64(y), oracle.moe_ffn(inp), "hot")
+
+
+# ---------------------------------------------------------------------------------------------------
+# exact invariants of the GPU path (no oracle needed, hold at any size)
+
+def _bits(y):
+    return y.view(torch.int16).cpu().numpy()
+
+
+def test_deterministic_and_scale_equivariant():
+    wl = mi.custom("inv", 200, 32, 4, 512, 256, seed=13)
+    inp = mi.make_inputs(wl)
+    d = gu.DeviceInputs(inp)
+    y1 = _bits(_forward(d, inp)[0])
+    y2 = _bits(_forward(d, inp, poison=False)[0])
+    np.testing.assert_array_equal(y1, y2)
+    base = gu.host_bf16_to_f64(_forward(d, inp)[0])
+    # doubling every up-projection scale (rows I..2I of gate_up) doubles y exactly
+    s = inp.w13_s.copy()
+    s[:, wl.I:, :] = mi.f32_to_bf16_bits(mi.bf16_bits_to_f32(s[:, wl.I:, :]) * 2)
+    d.w13_s = gu.dev(s.view(np.int16))
+    np.testing.assert_array_equal(gu.host_bf16_to_f64(_forward(d, inp)[0]), 2 * base)
+    d.w13_s = gu.dev(inp.w13_s.view(np.int16))
+    s2 = mi.f32_to_bf16_bits(mi.bf16_bits_to_f32(inp.w2_s) * 2)
+    d.w2_s = gu.dev(s2.view(np.int16))
+    np.testing.assert_array_equal(gu.host_bf16_to_f64(_forward(d, inp)[0]), 2 * base)
+
+
+def test_token_permutation_equivariant():
+    wl = mi.custom("perm", 160, 16, 4, 256, 128, seed=14)
+    inp = mi.make_inputs(wl)
+    d = gu.DeviceInputs(inp)
+    y = _bits(_forward(d, inp)[0])
+    p = np.random.default_rng(0).permutation(wl.T)
+    inp2 = mi.MoEInputs(wl, inp.x[p].copy(), inp.logits[p].copy(), inp.w13_q, inp.w13_s, inp.w2_q, inp.w2_s)
+    d2 = gu.DeviceInputs(inp2)
+    np.testing.assert_array_equal(_bits(_forward(d2, inp2)[0]), y[p])
