@@ -114,7 +114,7 @@ def test_align_edges(T, E, k, bm):
 # grouped GEMM entry point on its own
 
 @pytest.mark.parametrize("bm", [16, 32, 64, 128])
-@pytest.mark.parametrize("I,H", [(128, 256), (72, 160), (256, 96)])
+@pytest.mark.parametrize("I,H", [(128, 256), (96, 160), (256, 96)])
 def test_grouped_gemm_gate_up_silu_mul(bm, I, H):
     wl = mi.custom("gg", 150, 8, 3, H, I, skew=True, seed=11)
     inp, d = workload_inputs(wl)
@@ -126,7 +126,17 @@ def test_grouped_gemm_gate_up_silu_mul(bm, I, H):
     torch.cuda.synchronize()
     ra = oracle.align(rid, wl.E, bm)
     ref = oracle.grouped_proj(inp.x, ra["sorted_ids"], wl.k, inp.w13_q, inp.w13_s, ra["offsets"], silu_mul=True)
-    gu.assert_within_tolerance(gu.host_bf16_to_f64(C), ref, f"gate_up bm={bm}")
+    # Per-element bound from the arithmetic: h is rounded once to bf16 (<= 2^-8 relative); the fp32
+    # gate and up sums carry at most (64 + H/32) * 2^-24 * sum|terms| each, which silu(g)*u propagates
+    # with |d silu/dg| <= 1.1 and |silu(g)| <= |g|.
+    G = oracle.grouped_proj(inp.x, ra["sorted_ids"], wl.k, inp.w13_q, inp.w13_s, ra["offsets"])
+    Gabs = oracle.grouped_proj(inp.x & 0x7FFF, ra["sorted_ids"], wl.k, inp.w13_q & 0x77, inp.w13_s, ra["offsets"])
+    dG = (64 + H / 32) * 2.0 ** -24 * Gabs
+    g, u, dg, du = G[:, :I], G[:, I:], dG[:, :I], dG[:, I:]
+    bound = 2.0 ** -8 * np.abs(ref) + 1.1 * np.abs(u) * dg + np.abs(g) * du + 1e-6 * np.abs(ref)
+    got = gu.host_bf16_to_f64(C)
+    assert np.all(np.abs(got - ref) <= bound), f"gate_up bm={bm}: worst excess {np.max(np.abs(got - ref) - bound)}"
+    assert gu.tolerance_report(got, ref)["mean_rel"] <= gu.MEAN_REL
 
 
 @pytest.mark.parametrize("bm", [16, 64, 128])
