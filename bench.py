@@ -75,6 +75,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = enough for 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--layout", choices=["packed", "canonical"], default="packed",
+                    help="weight layout the timed layer reads (packed = prepacked once, outside the timed region)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
@@ -95,13 +97,24 @@ def main():
     w2_q0, w2_s0 = dev(inp.w2_q), dev(inp.w2_s.view(np.int16))
     copies = [(w13_q0, w13_s0, w2_q0, w2_s0)] + [
         (w13_q0.clone(), w13_s0.clone(), w2_q0.clone(), w2_s0.clone()) for _ in range(L - 1)]
+    layout = moe.MOE_LAYOUT_PACKED if args.layout == "packed" else moe.MOE_LAYOUT_CANONICAL
+    prepack_us = None
+    if layout == moe.MOE_LAYOUT_PACKED:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        packed = []
+        for (q13, s13, q2, s2) in copies:
+            packed.append(moe.moe_w4_prepack(q13, s13) + moe.moe_w4_prepack(q2, s2))
+        torch.cuda.synchronize()
+        prepack_us = (time.perf_counter() - t0) / L * 1e6
+        copies = packed
     y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(moe.moe_ffn_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device="cuda")
     log(f"bench: {L} weight copies of {wbytes_all / 1e6:.1f} MB; warmup {args.warmup}, timed steps {args.steps}")
 
     def step(i):
         q13, s13, q2, s2 = copies[i % L]
-        moe.moe_ffn_forward(x, logits, q13, s13, q2, s2, k, y=y, workspace=ws)
+        moe.moe_ffn_forward(x, logits, q13, s13, q2, s2, k, y=y, workspace=ws, weight_layout=layout)
 
     for i in range(args.warmup):
         step(i)
@@ -136,10 +149,10 @@ def main():
         al = moe.moe_align(ids, E, bm)
         if e: e[2].record()
         moe.moe_grouped_gemm_w4a16(x, al["sorted_ids"], k, q13, s13, al["tiles"], al["max_tiles"],
-                                   al["num_tiles"], bm, moe.MOE_EPI_SILU_MUL, R, C=h)
+                                   al["num_tiles"], bm, moe.MOE_EPI_SILU_MUL, R, C=h, weight_layout=layout)
         if e: e[3].record()
         moe.moe_grouped_gemm_w4a16(h, None, 1, q2, s2, al["tiles"], al["max_tiles"], al["num_tiles"], bm,
-                                   moe.MOE_EPI_NONE, R, moe.MOE_OUT_F32, C=O)
+                                   moe.MOE_EPI_NONE, R, moe.MOE_OUT_F32, C=O, weight_layout=layout)
         if e: e[4].record()
         moe.moe_combine(O, al["inv_perm"], wts, y=y)
         if e: e[5].record()
@@ -177,7 +190,8 @@ def main():
         "data": "synthetic (seeded; E2M1 codes uniform, bf16 group-32 scales U[0.005,0.02], x and logits N(0,1))",
         "config": {"workload": f"{wl.name}: {T} tokens, {E} experts top-{k}, hidden {H}, intermediate {I}, "
                                f"W4 E2M1 group-32 bf16 scales", "tokens": T, "experts": E, "top_k": k,
-                   "hidden": H, "intermediate": I, "weight_copies": L, "touched_experts": touched},
+                   "hidden": H, "intermediate": I, "weight_copies": L, "touched_experts": touched,
+                   "weight_layout": args.layout, "prepack_us_per_copy": None if prepack_us is None else round(prepack_us, 1)},
         "tflops": round(flops / (us * 1e-6) / 1e12, 3),
         "weight_gbps": round(weight_bytes / (us * 1e-6) / 1e9, 1),
         "layer_gbps": round(layer_bytes / (us * 1e-6) / 1e9, 1),

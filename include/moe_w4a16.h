@@ -41,6 +41,13 @@
  *     gate projection, rows [I, 2I) the up projection.
  *   - down weights: codes w2_q [E, H, I/2], scales w2_s [E, H, I/32].
  *
+ * Packed layout (optional, from moe_w4_prepack; same values, same total size): for each block of
+ *   16 consecutive rows and 128 consecutive K elements (blocks ordered expert, row block, K block),
+ *   1024 bytes of codes in the order the kernel's 64 lanes consume them, then separately 128 bytes
+ *   of scales [16 rows][4 groups].  It exists so that each wave-level load is one contiguous block
+ *   (the ATOM page, 8.2, lists weight pre-rearrangement as part of a quantized format's contract).
+ *   Requires N % 16 == 0 and K % 128 == 0.  Results are bit-identical to the canonical layout.
+ *
  * Numerics: E2M1 codes are exact in bf16; each 32-element group is reduced by bf16 MFMA into an
  * fp32 partial that is multiplied by the group's scale in fp32; accumulation is fp32.  h (the
  * SiLU-mul output) is stored as bf16 (round to nearest even), the down-projection output as fp32,
@@ -70,6 +77,9 @@ typedef int32_t moe_status_t;
 
 #define MOE_OUT_BF16 0
 #define MOE_OUT_F32 1
+
+#define MOE_LAYOUT_CANONICAL 0 /* the weight format above */
+#define MOE_LAYOUT_PACKED 1    /* the same codes and scales re-laid out by moe_w4_prepack */
 
 #define MOE_MAX_EXPERTS 1024
 
@@ -130,6 +140,17 @@ moe_status_t moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Re-lay out one weight tensor from the canonical layout into the packed layout (see above).
+ *   w_q [E, N, K/2], w_s [E, N, K/32] (canonical, device) -> packed_q (E*N*K/2 bytes) and packed_s
+ *   (E*N*K/32 bf16), device buffers owned by the caller, not overlapping the inputs.
+ * Shapes: 1 <= E <= MOE_MAX_EXPERTS, N >= 16, N % 16 == 0, K >= 128, K % 128 == 0.
+ * Alignment: w_q, packed_q 16 bytes; w_s, packed_s 2 bytes (packed_s 8 bytes for use by the GEMMs).
+ * Done once per weight tensor (e.g. at load time); every later call can read the packed copy.
+ */
+moe_status_t moe_w4_prepack(const uint8_t* w_q, const uint16_t* w_s, int32_t E, int32_t N, int32_t K,
+                            uint8_t* packed_q, uint16_t* packed_s, void* stream);
+
+/*
  * Grouped W4A16 GEMM, one launch over all experts [Atlas, 编译时内核选择和W4A16 Grouped GEMM].
  * For every tile (e, row0, rows) of `tiles` and every permuted row r in [row0, row0+rows):
  *   a(r) = a_row_of ? a_row_of[r] / a_row_div : r                (activation row)
@@ -140,7 +161,9 @@ moe_status_t moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
  * written.
  *   A          bf16 [*, K] row-major activations (gate_up: the tokens x, with a_row_of = sorted_ids
  *              and a_row_div = k; down: h in permuted order with a_row_of = NULL).
- *   Wq, Ws     [E, N, K/2] codes and [E, N, K/32] bf16 scales (the weight format above).
+ *   Wq, Ws     [E, N, K/2] codes and [E, N, K/32] bf16 scales (the weight format above), in
+ *              weight_layout MOE_LAYOUT_CANONICAL or MOE_LAYOUT_PACKED (then N % 16 == 0,
+ *              K % 128 == 0 and Ws 8-byte aligned).
  *   tiles, num_tiles  as written by moe_align with the same block_m; max_tiles is the capacity
  *              passed to moe_align (it sizes the launch; tiles past *num_tiles cost nothing).
  *   block_m    one of 16, 32, 64, 128.
@@ -149,7 +172,8 @@ moe_status_t moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
  * Alignment: A, Wq, C 16 bytes; Ws 2 bytes.
  */
 moe_status_t moe_grouped_gemm_w4a16(const uint16_t* A, const int32_t* a_row_of, int32_t a_row_div,
-                                    const uint8_t* Wq, const uint16_t* Ws, int32_t E, int32_t N,
+                                    const uint8_t* Wq, const uint16_t* Ws, int32_t weight_layout,
+                                    int32_t E, int32_t N,
                                     int32_t K, const int32_t* tiles, int32_t max_tiles,
                                     const int32_t* num_tiles, int32_t block_m, int32_t epilogue,
                                     void* C, int32_t out_dtype, void* stream);
@@ -177,7 +201,8 @@ size_t moe_ffn_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32
  *   route (moe_route_topk) -> permute (moe_align) -> gate_up grouped GEMM with SiLU*mul fused
  *   -> down grouped GEMM -> combine, all enqueued on `stream`:
  *   y[t] = sum_s w[t,s] * W2_e(s) ( silu(W1_e(s) x[t]) * (W3_e(s) x[t]) ),  e(s) = topk_ids[t, s].
- *   x bf16 [T, H]; router_logits fp32 [T, E]; weights in the format above; y bf16 [T, H] out.
+ *   x bf16 [T, H]; router_logits fp32 [T, E]; weights in the format above, all four tensors in
+ *   weight_layout (MOE_LAYOUT_PACKED needs H % 128 == 0 and I % 128 == 0); y bf16 [T, H] out.
  *   topk_ids_out int32 [T, k], topk_w_out fp32 [T, k]: optional copies of the routing (NULL = skip).
  *   workspace: device scratch of at least moe_ffn_workspace_bytes(T, H, I, E, k) bytes.
  * Shapes: T >= 0 (T == 0 launches nothing), 1 <= k <= E <= MOE_MAX_EXPERTS, H % 32 == 0,
@@ -186,7 +211,7 @@ size_t moe_ffn_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32
 moe_status_t moe_ffn_forward(const uint16_t* x, const float* router_logits, int32_t T, int32_t H,
                              int32_t I, int32_t E, int32_t k, const uint8_t* w13_q,
                              const uint16_t* w13_s, const uint8_t* w2_q, const uint16_t* w2_s,
-                             uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, void* workspace,
+                             int32_t weight_layout, uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus

@@ -4,10 +4,11 @@ The package holds the HIP sources (``csrc/``), their build script (``build.py``)
 (``_lib.py``) whose functions carry the names of the C entry points declared in
 ``include/moe_w4a16.h``.
 """
-from ._lib import (MOE_EPI_NONE, MOE_EPI_SILU_MUL, MOE_OUT_BF16, MOE_OUT_F32, EXPORTED, LIB_PATH, MoEError,
+from ._lib import (MOE_EPI_NONE, MOE_EPI_SILU_MUL, MOE_LAYOUT_CANONICAL, MOE_LAYOUT_PACKED, MOE_OUT_BF16,
+                   MOE_OUT_F32, EXPORTED, LIB_PATH, MoEError,
                    load, moe_align, moe_align_workspace_bytes, moe_combine, moe_ffn_block_m, moe_ffn_forward,
-                   moe_ffn_workspace_bytes, moe_grouped_gemm_w4a16, moe_max_tiles, moe_route_topk)
+                   moe_ffn_workspace_bytes, moe_grouped_gemm_w4a16, moe_max_tiles, moe_route_topk, moe_w4_prepack)
 
-__all__ = ["MOE_EPI_NONE", "MOE_EPI_SILU_MUL", "MOE_OUT_BF16", "MOE_OUT_F32", "EXPORTED", "LIB_PATH",
+__all__ = ["MOE_EPI_NONE", "MOE_EPI_SILU_MUL", "MOE_LAYOUT_CANONICAL", "MOE_LAYOUT_PACKED", "MOE_OUT_BF16", "MOE_OUT_F32", "EXPORTED", "LIB_PATH",
            "MoEError", "load", "moe_align", "moe_align_workspace_bytes", "moe_combine", "moe_ffn_block_m", "moe_ffn_forward",
-           "moe_ffn_workspace_bytes", "moe_grouped_gemm_w4a16", "moe_max_tiles", "moe_route_topk"]
+           "moe_ffn_workspace_bytes", "moe_grouped_gemm_w4a16", "moe_max_tiles", "moe_route_topk", "moe_w4_prepack"]

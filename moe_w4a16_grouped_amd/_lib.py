@@ -25,6 +25,8 @@ MOE_EPI_NONE = 0
 MOE_EPI_SILU_MUL = 1
 MOE_OUT_BF16 = 0
 MOE_OUT_F32 = 1
+MOE_LAYOUT_CANONICAL = 0
+MOE_LAYOUT_PACKED = 1
 
 _lib = None
 
@@ -52,11 +54,12 @@ def load() -> ctypes.CDLL:
         "moe_max_tiles": ([I32, I32, I32, I32], I32),
         "moe_align_workspace_bytes": ([I32, I32, I32], SZ),
         "moe_align": ([P, I32, I32, I32, I32, P, P, P, P, P, I32, P, P, SZ, P], I32),
-        "moe_grouped_gemm_w4a16": ([P, P, I32, P, P, I32, I32, I32, P, I32, P, I32, I32, P, I32, P], I32),
+        "moe_w4_prepack": ([P, P, I32, I32, I32, P, P, P], I32),
+        "moe_grouped_gemm_w4a16": ([P, P, I32, P, P, I32, I32, I32, I32, P, I32, P, I32, I32, P, I32, P], I32),
         "moe_combine": ([P, P, P, I32, I32, I32, P, P], I32),
         "moe_ffn_block_m": ([I32, I32, I32], I32),
         "moe_ffn_workspace_bytes": ([I32, I32, I32, I32, I32], SZ),
-        "moe_ffn_forward": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "moe_ffn_forward": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -67,7 +70,7 @@ def load() -> ctypes.CDLL:
 
 
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_last_error", "moe_route_topk", "moe_max_tiles",
-            "moe_align_workspace_bytes", "moe_align", "moe_grouped_gemm_w4a16", "moe_combine",
+            "moe_align_workspace_bytes", "moe_align", "moe_w4_prepack", "moe_grouped_gemm_w4a16", "moe_combine",
             "moe_ffn_block_m", "moe_ffn_workspace_bytes", "moe_ffn_forward")
 
 
@@ -150,9 +153,23 @@ def moe_align(topk_ids: torch.Tensor, E: int, block_m: int, stream=None) -> dict
     return out
 
 
+def moe_w4_prepack(w_q, w_s, packed_q=None, packed_s=None, stream=None):
+    """Canonical [E, N, K/2] codes + [E, N, K/32] scales -> the same tensors in the packed layout
+    (returned with the canonical shapes, which describe their sizes, not their element order)."""
+    _req(w_q, torch.uint8, "w_q")
+    _req(w_s, "16bit", "w_s")
+    E, N, K2 = w_q.shape
+    if packed_q is None:
+        packed_q = torch.empty_like(w_q)
+    if packed_s is None:
+        packed_s = torch.empty_like(w_s)
+    _check(load().moe_w4_prepack(_p(w_q), _p(w_s), E, N, 2 * K2, _p(packed_q), _p(packed_s), _stream(stream)))
+    return packed_q, packed_s
+
+
 def moe_grouped_gemm_w4a16(A, a_row_of, a_row_div: int, Wq, Ws, tiles, max_tiles: int, num_tiles,
                            block_m: int, epilogue: int, out_rows: int, out_dtype: int = MOE_OUT_BF16,
-                           C=None, stream=None):
+                           C=None, stream=None, weight_layout: int = MOE_LAYOUT_CANONICAL):
     """Grouped W4A16 GEMM over the tile list; returns C ([out_rows, N] or [out_rows, N/2])."""
     _req(A, "16bit", "A")
     _req(Wq, torch.uint8, "Wq")
@@ -162,7 +179,8 @@ def moe_grouped_gemm_w4a16(A, a_row_of, a_row_div: int, Wq, Ws, tiles, max_tiles
     if C is None:
         dt = torch.float32 if out_dtype == MOE_OUT_F32 else torch.bfloat16
         C = torch.empty((out_rows, ncols), dtype=dt, device=A.device)
-    _check(load().moe_grouped_gemm_w4a16(_p(A), _p(a_row_of), a_row_div, _p(Wq), _p(Ws), E, N, K, _p(tiles),
+    _check(load().moe_grouped_gemm_w4a16(_p(A), _p(a_row_of), a_row_div, _p(Wq), _p(Ws), weight_layout, E, N, K,
+                                         _p(tiles),
                                          max_tiles, _p(num_tiles), block_m, epilogue, _p(C), out_dtype,
                                          _stream(stream)))
     return C
@@ -180,7 +198,7 @@ def moe_combine(O, inv_perm, topk_w, y=None, stream=None):
 
 
 def moe_ffn_forward(x, router_logits, w13_q, w13_s, w2_q, w2_s, k: int, y=None, topk_ids_out=None,
-                    topk_w_out=None, workspace=None, stream=None):
+                    topk_w_out=None, workspace=None, stream=None, weight_layout: int = MOE_LAYOUT_CANONICAL):
     """Whole layer: x bf16 [T, H], logits fp32 [T, E], weights in the W4 group-32 format -> y bf16."""
     T, H = x.shape
     E, N13, _ = w13_q.shape
@@ -191,6 +209,6 @@ def moe_ffn_forward(x, router_logits, w13_q, w13_s, w2_q, w2_s, k: int, y=None, 
     if workspace is None:
         workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=x.device)
     _check(load().moe_ffn_forward(_p(x), _p(router_logits), T, H, I, E, k, _p(w13_q), _p(w13_s), _p(w2_q),
-                                  _p(w2_s), _p(y), _p(topk_ids_out), _p(topk_w_out), _p(workspace),
+                                  _p(w2_s), weight_layout, _p(y), _p(topk_ids_out), _p(topk_w_out), _p(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
     return y

@@ -154,8 +154,21 @@ moe_status_t moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                     "moe_align launch");
 }
 
+moe_status_t moe_w4_prepack(const uint8_t* w_q, const uint16_t* w_s, int32_t E, int32_t N, int32_t K,
+                            uint8_t* packed_q, uint16_t* packed_s, void* stream) {
+  if (E < 1 || N < 16 || K < 128) return fail(MOE_ERR_INVALID_ARG, "moe_w4_prepack: need E >= 1, N >= 16, K >= 128");
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E=%d exceeds %d", E, MOE_MAX_EXPERTS);
+  if (N % 16 != 0 || K % 128 != 0)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_w4_prepack: N=%d must be a multiple of 16 and K=%d of 128", N, K);
+  if (!w_q || !w_s || !packed_q || !packed_s) return fail(MOE_ERR_INVALID_ARG, "moe_w4_prepack: NULL pointer");
+  if (!aligned16(w_q) || !aligned16(packed_q) || !aligned2(w_s) || !aligned2(packed_s))
+    return fail(MOE_ERR_MISALIGNED, "moe_w4_prepack: codes need 16-byte, scales 2-byte alignment");
+  return hip_status(moe::launch_prepack(w_q, w_s, E, N, K, packed_q, packed_s, (hipStream_t)stream), "moe_w4_prepack launch");
+}
+
 moe_status_t moe_grouped_gemm_w4a16(const uint16_t* A, const int32_t* a_row_of, int32_t a_row_div,
-                                    const uint8_t* Wq, const uint16_t* Ws, int32_t E, int32_t N,
+                                    const uint8_t* Wq, const uint16_t* Ws, int32_t weight_layout,
+                                    int32_t E, int32_t N,
                                     int32_t K, const int32_t* tiles, int32_t max_tiles,
                                     const int32_t* num_tiles, int32_t block_m, int32_t epilogue,
                                     void* C, int32_t out_dtype, void* stream) {
@@ -169,15 +182,19 @@ moe_status_t moe_grouped_gemm_w4a16(const uint16_t* A, const int32_t* a_row_of, 
   if (epilogue == MOE_EPI_SILU_MUL && (N % 2 != 0 || out_dtype != MOE_OUT_BF16))
     return fail(MOE_ERR_INVALID_ARG, "SILU_MUL needs an even N and bf16 output");
   if (a_row_of && a_row_div < 1) return fail(MOE_ERR_INVALID_ARG, "a_row_div must be >= 1");
+  if (weight_layout != MOE_LAYOUT_CANONICAL && weight_layout != MOE_LAYOUT_PACKED)
+    return fail(MOE_ERR_INVALID_ARG, "unknown weight_layout %d", weight_layout);
+  if (weight_layout == MOE_LAYOUT_PACKED && (N % 16 != 0 || K % 128 != 0))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "packed weights need N %% 16 == 0 and K %% 128 == 0 (N=%d K=%d)", N, K);
   if (max_tiles == 0) return ok();
   if (!A || !Wq || !Ws || !tiles || !num_tiles || !C) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_w4a16: NULL pointer");
   if (!aligned16(A) || !aligned16(Wq) || !aligned16(C) || !aligned2(Ws) || !aligned4(tiles) || !aligned4(num_tiles) ||
-      (a_row_of && !aligned4(a_row_of)))
-    return fail(MOE_ERR_MISALIGNED, "moe_grouped_gemm_w4a16: A, Wq, C need 16-byte alignment");
+      (a_row_of && !aligned4(a_row_of)) || (weight_layout == MOE_LAYOUT_PACKED && (reinterpret_cast<uintptr_t>(Ws) & 7u)))
+    return fail(MOE_ERR_MISALIGNED, "moe_grouped_gemm_w4a16: A, Wq, C need 16-byte alignment (packed Ws 8-byte)");
   if ((int64_t)max_tiles * block_m >= kMaxRows + (int64_t)MOE_MAX_EXPERTS * block_m)
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "max_tiles=%d too large", max_tiles);
   moe::GemmArgs a{A, a_row_of, a_row_div, Wq, Ws, N, K, tiles, num_tiles, max_tiles, C, epilogue,
-                  out_dtype == MOE_OUT_F32};
+                  out_dtype == MOE_OUT_F32, weight_layout == MOE_LAYOUT_PACKED};
   return hip_status(moe::launch_grouped_gemm(a, block_m, (hipStream_t)stream), "moe_grouped_gemm_w4a16 launch");
 }
 
@@ -206,17 +223,22 @@ size_t moe_ffn_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32
 moe_status_t moe_ffn_forward(const uint16_t* x, const float* router_logits, int32_t T, int32_t H,
                              int32_t I, int32_t E, int32_t k, const uint8_t* w13_q,
                              const uint16_t* w13_s, const uint8_t* w2_q, const uint16_t* w2_s,
-                             uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, void* workspace,
+                             int32_t weight_layout, uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, void* workspace,
                              size_t workspace_bytes, void* stream) {
   if (moe_status_t st = check_routing_shape(T, E, k)) return st;
   if (H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0)
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_ffn_forward: H=%d and I=%d must be positive multiples of 32", H, I);
+  if (weight_layout != MOE_LAYOUT_CANONICAL && weight_layout != MOE_LAYOUT_PACKED)
+    return fail(MOE_ERR_INVALID_ARG, "unknown weight_layout %d", weight_layout);
+  if (weight_layout == MOE_LAYOUT_PACKED && (H % 128 != 0 || I % 128 != 0))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "packed weights need H %% 128 == 0 and I %% 128 == 0 (H=%d I=%d)", H, I);
   if (T == 0) return ok();
   if (!x || !router_logits || !w13_q || !w13_s || !w2_q || !w2_s || !y || !workspace)
     return fail(MOE_ERR_INVALID_ARG, "moe_ffn_forward: NULL pointer");
   if (!aligned16(x) || !aligned16(w13_q) || !aligned16(w2_q) || !aligned16(y) || !aligned16(workspace) ||
       !aligned4(router_logits) || !aligned2(w13_s) || !aligned2(w2_s) || (topk_ids_out && !aligned4(topk_ids_out)) ||
-      (topk_w_out && !aligned4(topk_w_out)))
+      (topk_w_out && !aligned4(topk_w_out)) ||
+      (weight_layout == MOE_LAYOUT_PACKED && ((reinterpret_cast<uintptr_t>(w13_s) | reinterpret_cast<uintptr_t>(w2_s)) & 7u)))
     return fail(MOE_ERR_MISALIGNED, "moe_ffn_forward: x, weights, y and workspace need 16-byte alignment");
   const FfnLayout L = ffn_layout(T, H, I, E, k);
   if (workspace_bytes < L.total)
@@ -239,10 +261,11 @@ moe_status_t moe_ffn_forward(const uint16_t* x, const float* router_logits, int3
   e = moe::launch_align(ids, R, E, L.block_m, counts, offsets, sorted, inv, tiles, L.max_tiles, ntiles,
                         ws + L.align_ws, s);
   if (e != hipSuccess) return hip_status(e, "align launch");
-  moe::GemmArgs g1{x, sorted, k, w13_q, w13_s, 2 * I, H, tiles, ntiles, L.max_tiles, h, MOE_EPI_SILU_MUL, 0};
+  const int packed = weight_layout == MOE_LAYOUT_PACKED;
+  moe::GemmArgs g1{x, sorted, k, w13_q, w13_s, 2 * I, H, tiles, ntiles, L.max_tiles, h, MOE_EPI_SILU_MUL, 0, packed};
   e = moe::launch_grouped_gemm(g1, L.block_m, s);
   if (e != hipSuccess) return hip_status(e, "gate_up launch");
-  moe::GemmArgs g2{h, nullptr, 1, w2_q, w2_s, H, I, tiles, ntiles, L.max_tiles, o, MOE_EPI_NONE, 1};
+  moe::GemmArgs g2{h, nullptr, 1, w2_q, w2_s, H, I, tiles, ntiles, L.max_tiles, o, MOE_EPI_NONE, 1, packed};
   e = moe::launch_grouped_gemm(g2, L.block_m, s);
   if (e != hipSuccess) return hip_status(e, "down launch");
   e = moe::launch_combine(o, inv, w, T, k, H, y, s);

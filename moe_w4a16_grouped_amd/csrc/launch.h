@@ -34,8 +34,12 @@ struct GemmArgs {
   void* C;
   int epilogue;            // MOE_EPI_*
   int out_f32;
+  int packed;              // weights in the prepacked kernel layout (prepack.hip)
 };
 hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t stream);
+
+hipError_t launch_prepack(const uint8_t* wq, const uint16_t* ws, int E, int N, int K, uint8_t* pq, uint16_t* ps,
+                          hipStream_t stream);
 
 hipError_t launch_combine(const float* O, const int32_t* inv_perm, const float* w, int T, int k,
                           int H, uint16_t* y, hipStream_t stream);

@@ -99,13 +99,14 @@ def test_align_rejects(lib):
 
 def test_grouped_gemm_rejects(lib):
     f = _ptr(FAKE)
-    args = dict(A=f, aro=None, div=1, Wq=f, Ws=f, E=8, N=256, K=256, tiles=f, mt=10, nt=f, bm=16, epi=0, C=f,
+    args = dict(A=f, aro=None, div=1, Wq=f, Ws=f, lay=0, E=8, N=256, K=256, tiles=f, mt=10, nt=f, bm=16, epi=0, C=f,
                 out=0)
 
     def call(**kw):
         a = dict(args, **kw)
-        return lib.moe_grouped_gemm_w4a16(a["A"], a["aro"], a["div"], a["Wq"], a["Ws"], a["E"], a["N"], a["K"],
-                                          a["tiles"], a["mt"], a["nt"], a["bm"], a["epi"], a["C"], a["out"], None)
+        return lib.moe_grouped_gemm_w4a16(a["A"], a["aro"], a["div"], a["Wq"], a["Ws"], a["lay"], a["E"], a["N"],
+                                          a["K"], a["tiles"], a["mt"], a["nt"], a["bm"], a["epi"], a["C"], a["out"],
+                                          None)
 
     assert call(K=48) == -2            # K not a multiple of 32
     assert call(bm=24) == -2           # unsupported tile height
@@ -116,6 +117,20 @@ def test_grouped_gemm_rejects(lib):
     assert call(C=None) == -1
     assert call(E=0) == -1
     assert call(mt=0) == 0             # nothing to do: no launch
+    assert call(lay=2) == -1           # unknown layout
+    assert call(lay=1, K=96) == -2     # packed needs K % 128 == 0
+    assert call(lay=1, N=200) == -2    # packed needs N % 16 == 0
+    assert call(lay=1, Ws=_ptr(FAKE + 2)) == -3  # packed scales need 8-byte alignment
+
+
+def test_prepack_rejects(lib):
+    f = _ptr(FAKE)
+    assert lib.moe_w4_prepack(f, f, 8, 200, 256, f, f, None) == -2
+    assert lib.moe_w4_prepack(f, f, 8, 256, 96, f, f, None) == -1   # K < 128
+    assert lib.moe_w4_prepack(f, f, 8, 256, 160, f, f, None) == -2
+    assert lib.moe_w4_prepack(f, f, 0, 256, 256, f, f, None) == -1
+    assert lib.moe_w4_prepack(f, None, 8, 256, 256, f, f, None) == -1
+    assert lib.moe_w4_prepack(_ptr(FAKE + 4), f, 8, 256, 256, f, f, None) == -3
 
 
 def test_combine_and_forward_reject(lib):
@@ -125,11 +140,13 @@ def test_combine_and_forward_reject(lib):
     assert lib.moe_combine(_ptr(FAKE + 4), f, f, 4, 2, 16, f, None) == -3
     ws = moe.moe_ffn_workspace_bytes(16, 256, 128, 8, 2)
     fw = lambda **kw: lib.moe_ffn_forward(kw.get("x", f), f, kw.get("T", 16), kw.get("H", 256), kw.get("I", 128),
-                                          kw.get("E", 8), kw.get("k", 2), f, f, f, f, f, None, None, f,
-                                          kw.get("ws", ws), None)
+                                          kw.get("E", 8), kw.get("k", 2), f, f, f, f, kw.get("lay", 0), f, None,
+                                          None, f, kw.get("ws", ws), None)
     assert fw(H=250) == -2
     assert fw(I=48) == -2
     assert fw(k=9) == -1
     assert fw(ws=ws - 1) == -4
     assert fw(x=_ptr(FAKE + 2)) == -3
     assert fw(T=0) == 0
+    assert fw(lay=5) == -1
+    assert fw(lay=1, I=96) == -2       # packed needs I % 128 == 0

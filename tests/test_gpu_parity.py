@@ -285,3 +285,57 @@ def test_token_permutation_equivariant():
     inp2 = mi.MoEInputs(wl, inp.x[p].copy(), inp.logits[p].copy(), inp.w13_q, inp.w13_s, inp.w2_q, inp.w2_s)
     d2 = gu.DeviceInputs(inp2)
     np.testing.assert_array_equal(_bits(_forward(d2, inp2)[0]), y[p])
+
+
+# ---------------------------------------------------------------------------------------------------
+# packed weight layout: same values re-laid out; results must be bit-identical to the canonical path
+
+def _packed(d):
+    q13, s13 = moe.moe_w4_prepack(d.w13_q, d.w13_s)
+    q2, s2 = moe.moe_w4_prepack(d.w2_q, d.w2_s)
+    return q13, s13, q2, s2
+
+
+def test_prepack_is_a_permutation_of_bytes():
+    wl = mi.custom("pk", 4, 3, 1, 256, 128, seed=21)
+    inp, d = workload_inputs(wl)
+    q13, s13 = moe.moe_w4_prepack(d.w13_q, d.w13_s)
+    torch.cuda.synchronize()
+    a = np.sort(d.w13_q.cpu().numpy().ravel())
+    b = np.sort(q13.cpu().numpy().ravel())
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(np.sort(d.w13_s.cpu().numpy().ravel()), np.sort(s13.cpu().numpy().ravel()))
+
+
+@pytest.mark.parametrize("name", ["tiny", "dec1", "dec64", "pre800", "big4096", "skew8192"])
+def test_ffn_forward_packed_matches_canonical_bits(name):
+    inp, d = workload_inputs(name)
+    wl = inp.wl
+    _log(f"packed forward {name}")
+    y_c = _bits(_forward(d, inp)[0])
+    q13, s13, q2, s2 = _packed(d)
+    y = torch.full((wl.T, wl.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.moe_ffn_forward(d.x, d.logits, q13, s13, q2, s2, wl.k, y=y, weight_layout=moe.MOE_LAYOUT_PACKED)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_bits(y), y_c)
+
+
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+def test_grouped_gemm_packed_matches_canonical_bits(bm):
+    wl = mi.custom("gp", 150, 8, 3, 256, 128, skew=True, seed=23)
+    inp, d = workload_inputs(wl)
+    rid, _ = oracle.route(inp.logits, wl.k)
+    a = moe.moe_align(gu.dev(rid), wl.E, bm)
+    R = wl.T * wl.k
+    q13, s13, q2, s2 = _packed(d)
+    for (wq, ws, pq, ps, epi, A, aro, div, od) in [
+            (d.w13_q, d.w13_s, q13, s13, moe.MOE_EPI_SILU_MUL, d.x, a["sorted_ids"], wl.k, moe.MOE_OUT_BF16),
+            (d.w2_q, d.w2_s, q2, s2, moe.MOE_EPI_NONE,
+             gu.dev_bf16(mi.f32_to_bf16_bits(np.random.default_rng(2).standard_normal((R, wl.I), dtype=np.float32))),
+             None, 1, moe.MOE_OUT_F32)]:
+        c1 = moe.moe_grouped_gemm_w4a16(A, aro, div, wq, ws, a["tiles"], a["max_tiles"], a["num_tiles"], bm, epi, R, od)
+        c2 = moe.moe_grouped_gemm_w4a16(A, aro, div, pq, ps, a["tiles"], a["max_tiles"], a["num_tiles"], bm, epi, R, od,
+                                        weight_layout=moe.MOE_LAYOUT_PACKED)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(c1.view(torch.int16 if od == moe.MOE_OUT_BF16 else torch.int32).cpu().numpy(),
+                                      c2.view(torch.int16 if od == moe.MOE_OUT_BF16 else torch.int32).cpu().numpy())
