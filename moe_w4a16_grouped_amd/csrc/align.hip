@@ -62,10 +62,17 @@ __device__ void finish_expert(int e, int E, int nseg, int bm, int32_t* seg_cnt, 
                               int* scratch) {
   int c = 0;
   if (e < E) {
-    for (int s = 0; s < nseg; ++s) {
-      const int tmp = seg_cnt[s * E + e];
-      seg_cnt[s * E + e] = c;
-      c += tmp;
+    // segment counts are read 16 at a time so the loads are in flight together
+    for (int s0 = 0; s0 < nseg; s0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = s0 + j < nseg ? seg_cnt[(s0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (s0 + j < nseg) {
+          seg_cnt[(s0 + j) * E + e] = c;
+          c += v[j];
+        }
     }
   }
   const int nt = (c + bm - 1) / bm;
@@ -88,58 +95,80 @@ __device__ void finish_expert(int e, int E, int nseg, int bm, int32_t* seg_cnt, 
   }
 }
 
-// Count segment [f0, f1) of one wave into cnt[id].
-__device__ __forceinline__ void wave_count(const int32_t* ids, int f0, int f1, int nbits, int32_t* cnt) {
+// Per-wave segments hold at most 64 * kSegRegs slots; their ids are loaded once, in one burst, into
+// registers (lane l holds slots f0 + 64*j + l) and used by both the counting and the scatter pass.
+constexpr int kSegRegs = 16;
+
+__device__ __forceinline__ void load_segment(const int32_t* ids, int f0, int f1, int (&id)[kSegRegs]) {
   const int lane = threadIdx.x & 63;
-  for (int base = f0; base < f1; base += 64) {
-    const int f = base + lane;
-    const bool v = f < f1;
-    const int id = v ? ids[f] : 0;
-    const uint64_t peers = peer_mask(id, v, nbits);
-    if (v && lane == __ffsll((unsigned long long)peers) - 1) cnt[id] += __popcll(peers);
+#pragma unroll
+  for (int j = 0; j < kSegRegs; ++j) {
+    const int f = f0 + 64 * j + lane;
+    id[j] = f < f1 ? ids[f] : -1;
+  }
+}
+
+// Count segment [f0, f1) of one wave into cnt[id].
+__device__ __forceinline__ void wave_count(const int (&id)[kSegRegs], int f0, int f1, int nbits, int32_t* cnt) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < kSegRegs; ++j) {
+    if (f0 + 64 * j >= f1) break;
+    const bool v = id[j] >= 0;
+    const uint64_t peers = peer_mask(v ? id[j] : 0, v, nbits);
+    if (v && lane == __ffsll((unsigned long long)peers) - 1) cnt[id[j]] += __popcll(peers);
   }
 }
 
 // Scatter segment [f0, f1) of one wave; base[id] is the next free permuted row of expert id.
-__device__ __forceinline__ void wave_scatter(const int32_t* ids, int f0, int f1, int nbits, int32_t* base,
+// sorted_ids may point to LDS (staging) or global memory.
+__device__ __forceinline__ void wave_scatter(const int (&id)[kSegRegs], int f0, int f1, int nbits, int32_t* base,
                                              int32_t* sorted_ids, int32_t* inv_perm) {
   const int lane = threadIdx.x & 63;
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int b0 = f0; b0 < f1; b0 += 64) {
-    const int f = b0 + lane;
-    const bool v = f < f1;
-    const int id = v ? ids[f] : 0;
-    const uint64_t peers = peer_mask(id, v, nbits);
-    const int b = v ? base[id] : 0;
+#pragma unroll
+  for (int j = 0; j < kSegRegs; ++j) {
+    if (f0 + 64 * j >= f1) break;
+    const int f = f0 + 64 * j + lane;
+    const bool v = id[j] >= 0;
+    const int e = v ? id[j] : 0;
+    const uint64_t peers = peer_mask(e, v, nbits);
+    const int b = v ? base[e] : 0;
     if (v) {
       const int r = b + __popcll(peers & below);
       sorted_ids[r] = f;
       inv_perm[f] = r;
     }
     // one lane per expert advances its base; every lane of the wave has read it above
-    if (v && lane == __ffsll((unsigned long long)peers) - 1) base[id] = b + __popcll(peers);
+    if (v && lane == __ffsll((unsigned long long)peers) - 1) base[e] = b + __popcll(peers);
   }
 }
 
-// Whole permutation in one 1024-thread workgroup (R <= kAlignSingleMaxR, E <= kAlignSingleMaxE).
+// Whole permutation in one 1024-thread workgroup (align_single_fits(R, E)).  sorted_ids is built in
+// LDS (the scatter is random) and written out with coalesced stores.
 __global__ __launch_bounds__(1024) void align_single_kernel(const int32_t* __restrict__ ids, int R, int E,
                                                             int bm, int nbits, int32_t* counts,
                                                             int32_t* offsets, int32_t* sorted_ids,
                                                             int32_t* inv_perm, int32_t* tiles,
                                                             int max_tiles, int32_t* num_tiles) {
   extern __shared__ int32_t smem[];
-  int32_t* cnt = smem;             // [16][E]
-  int* scratch = smem + 16 * E;    // 34 ints
+  int32_t* cnt = smem;                  // [16][E]
+  int* scratch = smem + 16 * E;         // 64 ints
+  int32_t* sorted_lds = scratch + 64;   // [R]
   const int tid = threadIdx.x, wave = tid >> 6;
   for (int i = tid; i < 16 * E; i += 1024) cnt[i] = 0;
   __syncthreads();
   const int seg = (((R + 15) / 16) + 63) & ~63;
   const int f0 = min(R, wave * seg), f1 = min(R, f0 + seg);
-  wave_count(ids, f0, f1, nbits, cnt + wave * E);
+  int id[kSegRegs];
+  load_segment(ids, f0, f1, id);
+  wave_count(id, f0, f1, nbits, cnt + wave * E);
   __syncthreads();
   finish_expert(tid, E, 16, bm, cnt, counts, offsets, tiles, max_tiles, num_tiles, scratch);
   __syncthreads();
-  wave_scatter(ids, f0, f1, nbits, cnt + wave * E, sorted_ids, inv_perm);
+  wave_scatter(id, f0, f1, nbits, cnt + wave * E, sorted_lds, inv_perm);
+  __syncthreads();
+  for (int r = tid; r < R; r += 1024) sorted_ids[r] = sorted_lds[r];
 }
 
 // Multi-workgroup path, step 1: per-(workgroup, wave) counts, kAlignChunk slots per workgroup.
@@ -151,7 +180,9 @@ __global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restri
   __syncthreads();
   const int f0 = min(R, blockIdx.x * kAlignChunk + wave * (kAlignChunk / 4));
   const int f1 = min(R, f0 + kAlignChunk / 4);
-  wave_count(ids, f0, f1, nbits, cnt + wave * E);
+  int id[kSegRegs];
+  load_segment(ids, f0, f1, id);
+  wave_count(id, f0, f1, nbits, cnt + wave * E);
   __syncthreads();
   for (int i = tid; i < 4 * E; i += 256) seg_cnt[(size_t)blockIdx.x * 4 * E + i] = cnt[i];
 }
@@ -176,7 +207,9 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
   __syncthreads();
   const int f0 = min(R, blockIdx.x * kAlignChunk + wave * (kAlignChunk / 4));
   const int f1 = min(R, f0 + kAlignChunk / 4);
-  wave_scatter(ids, f0, f1, nbits, base + wave * E, sorted_ids, inv_perm);
+  int id[kSegRegs];
+  load_segment(ids, f0, f1, id);
+  wave_scatter(id, f0, f1, nbits, base + wave * E, sorted_ids, inv_perm);
 }
 
 static int id_bits(int E) {
@@ -186,7 +219,7 @@ static int id_bits(int E) {
 }
 
 size_t align_workspace_bytes(int R, int E) {
-  if (R <= kAlignSingleMaxR && E <= kAlignSingleMaxE) return 0;
+  if (align_single_fits(R, E)) return 0;
   const size_t nblk = (size_t)(R + kAlignChunk - 1) / kAlignChunk;
   return nblk * 4 * (size_t)E * sizeof(int32_t);
 }
@@ -195,8 +228,8 @@ hipError_t launch_align(const int32_t* ids, int R, int E, int block_m, int32_t* 
                         int32_t* offsets, int32_t* sorted_ids, int32_t* inv_perm, int32_t* tiles,
                         int max_tiles, int32_t* num_tiles, void* workspace, hipStream_t stream) {
   const int nbits = id_bits(E);
-  if (R <= kAlignSingleMaxR && E <= kAlignSingleMaxE) {
-    const size_t lds = (16 * (size_t)E + 40) * sizeof(int32_t);
+  if (align_single_fits(R, E)) {
+    const size_t lds = (16 * (size_t)E + 64 + (size_t)R) * sizeof(int32_t);
     align_single_kernel<<<1, 1024, lds, stream>>>(ids, R, E, block_m, nbits, counts, offsets, sorted_ids,
                                                   inv_perm, tiles, max_tiles, num_tiles);
     return hipGetLastError();

@@ -451,9 +451,9 @@ static hipError_t by_variant(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t stream) {
   if (a.max_tiles <= 0) return hipSuccess;
   switch (block_m) {
-    case 16: return by_variant<Streaming<16, 32, 3>>(a, stream);
+    case 16: return by_variant<Tiled<16, 128, 1, 3>>(a, stream);
     case 32: return by_variant<Tiled<32, 128, 1, 3>>(a, stream);
-    case 64: return by_variant<Tiled<64, 128, 2, 2>>(a, stream);
+    case 64: return by_variant<Tiled<64, 128, 1, 2>>(a, stream);
     default: return by_variant<Tiled<128, 128, 2, 1>>(a, stream);
   }
 }

@@ -4,7 +4,7 @@
 //
 // One wave64 per token.  Each lane holds ceil(E/64) logits as 64-bit keys
 // (order-preserving fp32 bits << 32 | ~expert_id), so one unsigned max picks the largest logit and,
-// among equal logits, the lower expert id.  k rounds of a wave-wide max (xor-shuffle butterfly)
+// among equal logits, the lower expert id.  k rounds of a wave-wide max (DPP row operations)
 // select the experts in order; the weights exp(l_s - l_0) / sum_j exp(l_j - l_0) are the softmax
 // restricted to the kept experts, which equals softmax-then-renormalise.
 #include "launch.h"
@@ -23,15 +23,27 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
   return __uint_as_float(u);
 }
 
+// Max of a 64-bit key over the wave with DPP row operations (xor 1, xor 2 in quads, half-row and
+// row mirrors, then the row broadcasts 15 and 31), leaving the result in lane 63; read back as a
+// wave-uniform value.  Lanes that a DPP step does not feed keep their own key (max with 0).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROW_MASK, 0xF, false);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > v ? o : v;
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  v = dpp_max_step<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_step<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_step<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_max_step<0x140, 0xF>(v);  // row_mirror
+  v = dpp_max_step<0x142, 0xA>(v);  // row_bcast:15
+  v = dpp_max_step<0x143, 0xC>(v);  // row_bcast:31
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 template <int NJ>
@@ -48,6 +60,10 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     const int e = lane + 64 * j;
     key[j] = e < E ? ((uint64_t)ordered_bits(l[e]) << 32) | (uint32_t)(~(uint32_t)e) : 0ull;
   }
+  // slot s is owned by lane s % 64 (register j = s / 64): id and exp(l_s - l_0)
+  constexpr int MAXK = 16;  // slots kept per lane: k <= 64 * MAXK
+  int my_id[MAXK];
+  float my_p[MAXK];
   float top = 0.f, sum = 0.f;
   for (int s = 0; s < k; ++s) {
     uint64_t best = 0;
@@ -61,13 +77,17 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     if (s == 0) top = v;
     const float p = expf(v - top);
     sum += p;
-    if (lane == 0) {
-      ids[(size_t)t * k + s] = e;
-      w[(size_t)t * k + s] = p;
-    }
+#pragma unroll
+    for (int j = 0; j < MAXK; ++j)
+      if (s == 64 * j + lane) { my_id[j] = e; my_p[j] = p; }
   }
-  if (lane == 0) {
-    for (int s = 0; s < k; ++s) w[(size_t)t * k + s] = w[(size_t)t * k + s] / sum;
+#pragma unroll
+  for (int j = 0; j < MAXK; ++j) {
+    const int s = 64 * j + lane;
+    if (s < k) {
+      ids[(size_t)t * k + s] = my_id[j];
+      w[(size_t)t * k + s] = my_p[j] / sum;
+    }
   }
 }
 
