@@ -214,30 +214,25 @@ __global__ __launch_bounds__(256) void gemm_w4a16_tiled(GemmArgs p) {
     u32x4 bt[NI];
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) bt[ni] = b_operands<LAYOUT>(breg[u][ni]);
-    // Per group: all activation fragments are read first, then the MI x NI MFMAs are issued back to
-    // back into separate partial registers, and only then scaled into the accumulators, so the
-    // MFMAs pipeline and the scale FMAs of one group can overlap the next group's MFMAs.
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      bf16x8 af[MI], bf[NI];
+      bf16x8 bf[NI];
       float sc[NI];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        af[mi] = *reinterpret_cast<const bf16x8*>(&a_lds[(wm * WM + mi * 16 + l16) * LDA + g * 32 + q * 8]);
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         bf[ni] = e2m1x8_to_bf16(bt[ni][g]);
         sc[ni] = scale_of<LAYOUT>(sreg[u][ni], g);
       }
-      f32x4 part[MI][NI];
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < MI; ++mi) {
+        const bf16x8 af =
+            *reinterpret_cast<const bf16x8*>(&a_lds[(wm * WM + mi * 16 + l16) * LDA + g * 32 + q * 8]);
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) part[mi][ni] = mfma16x16x32(af[mi], bf[ni], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] += sc[ni] * part[mi][ni];
+        for (int ni = 0; ni < NI; ++ni) {
+          const f32x4 part = mfma16x16x32(af, bf[ni], f32x4{0.f, 0.f, 0.f, 0.f});
+          acc[mi][ni] += sc[ni] * part;
+        }
+      }
     }
   };
 
