@@ -175,7 +175,7 @@ def main():
     # launches on the stream they run on (torch's current stream).
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    bm = moe.moe_ffn_block_m(T, E, k)
+    bm = moe.moe_ffn_block_m(T, E, k, layout)
     h = torch.empty((R, I), dtype=torch.bfloat16, device="cuda")
     O = torch.empty((R, H), dtype=torch.float32, device="cuda")
     names = ["route", "align", "gate_up", "down", "combine"]

@@ -46,7 +46,9 @@
  *   1024 bytes of codes in the order the kernel's 64 lanes consume them, then separately 128 bytes
  *   of scales [16 rows][4 groups].  It exists so that each wave-level load is one contiguous block
  *   (the ATOM page, 8.2, lists weight pre-rearrangement as part of a quantized format's contract).
- *   Requires N % 16 == 0 and K % 128 == 0.  Results are bit-identical to the canonical layout.
+ *   Requires N % 16 == 0 and K % 128 == 0; a gate_up tensor read with SILU_MUL also needs
+ *   N % 32 == 0, so that its up rows (from N/2) start a block.  Results are bit-identical to the
+ *   canonical layout.
  *
  * Numerics: E2M1 codes are exact in bf16; each 32-element group is reduced by bf16 MFMA into an
  * fp32 partial that is multiplied by the group's scale in fp32; accumulation is fp32.  h (the
@@ -162,8 +164,8 @@ moe_status_t moe_w4_prepack(const uint8_t* w_q, const uint16_t* w_s, int32_t E, 
  *   A          bf16 [*, K] row-major activations (gate_up: the tokens x, with a_row_of = sorted_ids
  *              and a_row_div = k; down: h in permuted order with a_row_of = NULL).
  *   Wq, Ws     [E, N, K/2] codes and [E, N, K/32] bf16 scales (the weight format above), in
- *              weight_layout MOE_LAYOUT_CANONICAL or MOE_LAYOUT_PACKED (then N % 16 == 0,
- *              K % 128 == 0 and Ws 8-byte aligned).
+ *              weight_layout MOE_LAYOUT_CANONICAL or MOE_LAYOUT_PACKED (then N % 16 == 0 -- with
+ *              SILU_MUL N % 32 == 0 --, K % 128 == 0 and Ws 8-byte aligned).
  *   tiles, num_tiles  as written by moe_align with the same block_m; max_tiles is the capacity
  *              passed to moe_align (it sizes the launch; tiles past *num_tiles cost nothing).
  *   block_m    one of 16, 32, 64, 128.
@@ -189,9 +191,10 @@ moe_status_t moe_grouped_gemm_w4a16(const uint16_t* A, const int32_t* a_row_of, 
 moe_status_t moe_combine(const float* O, const int32_t* inv_perm, const float* topk_w, int32_t T,
                          int32_t k, int32_t H, uint16_t* y, void* stream);
 
-/* Row-tile height (block_m) moe_ffn_forward uses for these sizes (host-only, pure; -1 on invalid
- * sizes).  Lets a caller run the same launch configuration through the separate entry points. */
-int32_t moe_ffn_block_m(int32_t T, int32_t E, int32_t k);
+/* Row-tile height (block_m) moe_ffn_forward uses for these sizes and weight layout (host-only,
+ * pure; -1 on invalid sizes or layout).  Lets a caller run the same launch configuration through
+ * the separate entry points.  moe_ffn_workspace_bytes covers every layout's choice. */
+int32_t moe_ffn_block_m(int32_t T, int32_t E, int32_t k, int32_t weight_layout);
 
 /* Workspace bytes moe_ffn_forward needs for these sizes (host-only, pure; 0 on invalid sizes). */
 size_t moe_ffn_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k);

@@ -57,7 +57,7 @@ def load() -> ctypes.CDLL:
         "moe_w4_prepack": ([P, P, I32, I32, I32, P, P, P], I32),
         "moe_grouped_gemm_w4a16": ([P, P, I32, P, P, I32, I32, I32, I32, P, I32, P, I32, I32, P, I32, P], I32),
         "moe_combine": ([P, P, P, I32, I32, I32, P, P], I32),
-        "moe_ffn_block_m": ([I32, I32, I32], I32),
+        "moe_ffn_block_m": ([I32, I32, I32, I32], I32),
         "moe_ffn_workspace_bytes": ([I32, I32, I32, I32, I32], SZ),
         "moe_ffn_forward": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, SZ, P], I32),
     }
@@ -107,8 +107,8 @@ def moe_align_workspace_bytes(T: int, k: int, E: int) -> int:
     return int(load().moe_align_workspace_bytes(T, k, E))
 
 
-def moe_ffn_block_m(T: int, E: int, k: int) -> int:
-    return int(load().moe_ffn_block_m(T, E, k))
+def moe_ffn_block_m(T: int, E: int, k: int, weight_layout: int = 0) -> int:
+    return int(load().moe_ffn_block_m(T, E, k, weight_layout))
 
 
 def moe_ffn_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:

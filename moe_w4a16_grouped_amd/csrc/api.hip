@@ -50,12 +50,13 @@ moe_status_t check_routing_shape(int32_t T, int32_t E, int32_t k) {
 int64_t max_tiles_of(int64_t R, int64_t E, int64_t bm) { return R / bm + std::min<int64_t>(E, R); }
 
 // Row tile height for the grouped GEMMs given the average rows per expert (measured on MI355X:
-// 16 for decode-sized experts, 32 around 25 rows per expert, 64 above; 128-row tiles lose to
-// register pressure).
-int32_t pick_block_m(int64_t R, int64_t E) {
+// 16 for decode-sized experts, 32 around 25 rows per expert, 64 above; with packed weights, experts
+// averaging more than 256 rows go to the 128-row large-tile kernel).
+int32_t pick_block_m(int64_t R, int64_t E, bool packed) {
   const int64_t avg = (R + E - 1) / E;
   if (avg <= 16) return 16;
   if (avg <= 32) return 32;
+  if (packed && avg > 256) return 128;
   return 64;
 }
 
@@ -67,11 +68,14 @@ struct FfnLayout {
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 
-FfnLayout ffn_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
+// The tile list is sized for the canonical-layout tile height, which is never larger than the packed
+// one, so one workspace size serves both layouts.
+FfnLayout ffn_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, bool packed) {
   FfnLayout L{};
   const int64_t R = T * k;
-  L.block_m = pick_block_m(R, E);
+  L.block_m = pick_block_m(R, E, packed);
   L.max_tiles = (int32_t)max_tiles_of(R, E, L.block_m);
+  const int64_t tile_cap = std::max<int64_t>(L.max_tiles, max_tiles_of(R, E, pick_block_m(R, E, false)));
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off += up256(bytes); return at; };
   L.ids = take(R * 4);
@@ -80,7 +84,7 @@ FfnLayout ffn_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   L.offsets = take((E + 1) * 4);
   L.sorted = take(R * 4);
   L.inv = take(R * 4);
-  L.tiles = take((size_t)std::max(L.max_tiles, 1) * 12);
+  L.tiles = take((size_t)std::max<int64_t>(tile_cap, 1) * 12);
   L.ntiles = take(4);
   L.align_ws = take(moe::align_workspace_bytes((int)R, (int)E));
   L.h = take((size_t)R * I * 2);
@@ -187,6 +191,8 @@ moe_status_t moe_grouped_gemm_w4a16(const uint16_t* A, const int32_t* a_row_of, 
     return fail(MOE_ERR_INVALID_ARG, "unknown weight_layout %d", weight_layout);
   if (weight_layout == MOE_LAYOUT_PACKED && (N % 16 != 0 || K % 128 != 0))
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "packed weights need N %% 16 == 0 and K %% 128 == 0 (N=%d K=%d)", N, K);
+  if (weight_layout == MOE_LAYOUT_PACKED && epilogue == MOE_EPI_SILU_MUL && N % 32 != 0)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "packed gate_up weights need N %% 32 == 0 (up rows start a 16-row block; N=%d)", N);
   if (max_tiles == 0) return ok();
   if (!A || !Wq || !Ws || !tiles || !num_tiles || !C) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_w4a16: NULL pointer");
   if (!aligned16(A) || !aligned16(Wq) || !aligned16(C) || !aligned2(Ws) || !aligned4(tiles) || !aligned4(num_tiles) ||
@@ -211,14 +217,15 @@ moe_status_t moe_combine(const float* O, const int32_t* inv_perm, const float* t
   return hip_status(moe::launch_combine(O, inv_perm, topk_w, T, k, H, y, (hipStream_t)stream), "moe_combine launch");
 }
 
-int32_t moe_ffn_block_m(int32_t T, int32_t E, int32_t k) {
+int32_t moe_ffn_block_m(int32_t T, int32_t E, int32_t k, int32_t weight_layout) {
   if (T < 0 || E < 1 || k < 1 || k > E || (int64_t)T * k >= kMaxRows) return -1;
-  return pick_block_m((int64_t)T * k, E);
+  if (weight_layout != MOE_LAYOUT_CANONICAL && weight_layout != MOE_LAYOUT_PACKED) return -1;
+  return pick_block_m((int64_t)T * k, E, weight_layout == MOE_LAYOUT_PACKED);
 }
 
 size_t moe_ffn_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k) {
   if (T < 0 || H < 1 || I < 1 || E < 1 || k < 1 || k > E || E > MOE_MAX_EXPERTS || (int64_t)T * k >= kMaxRows) return 0;
-  return ffn_layout(T, H, I, E, k).total;
+  return ffn_layout(T, H, I, E, k, false).total;
 }
 
 moe_status_t moe_ffn_forward(const uint16_t* x, const float* router_logits, int32_t T, int32_t H,
@@ -241,7 +248,7 @@ moe_status_t moe_ffn_forward(const uint16_t* x, const float* router_logits, int3
       (topk_w_out && !aligned4(topk_w_out)) ||
       (weight_layout == MOE_LAYOUT_PACKED && ((reinterpret_cast<uintptr_t>(w13_s) | reinterpret_cast<uintptr_t>(w2_s)) & 7u)))
     return fail(MOE_ERR_MISALIGNED, "moe_ffn_forward: x, weights, y and workspace need 16-byte alignment");
-  const FfnLayout L = ffn_layout(T, H, I, E, k);
+  const FfnLayout L = ffn_layout(T, H, I, E, k, weight_layout == MOE_LAYOUT_PACKED);
   if (workspace_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "moe_ffn_forward: workspace %zu B < required %zu B", workspace_bytes, L.total);
   char* ws = static_cast<char*>(workspace);

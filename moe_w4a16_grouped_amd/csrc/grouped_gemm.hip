@@ -401,6 +401,199 @@ __global__ __launch_bounds__(256) void gemm_w4a16_sk(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------------------------------
+// Large-tile kernel for MFMA-bound shapes (hundreds of rows per expert), packed weights only.
+// 128 x 256 output tile per 512-thread workgroup: 8 waves (2 along M x 4 along N), 64 x 64 each, so
+// two waves share every SIMD and one's scale FMAs can overlap the other's MFMAs.  Activations (gathered
+// rows) and packed weight codes/scales reach LDS through direct global->LDS 16-byte loads
+// (global_load_lds_dwordx4: lane l of an instruction fills LDS bytes [16l, 16l+16) after a
+// wave-uniform base), so staging costs no registers.  NSTAGE LDS stages, one barrier per K step:
+// the loads of step s+NSTAGE-1 are issued right after the barrier of step s, into the stage computed
+// at step s-1.  Activation rows are 256-byte LDS rows whose 16-byte chunks are XOR-swizzled by
+// (row % 16), which makes the fragment reads conflict-free.
+// Work order is XCD-aware: workgroup b runs on XCD b % 8 (round-robin dispatch); on each XCD the
+// workgroups walk one row tile across that XCD's N blocks before the next tile, so the tile's
+// activations are fetched into that XCD's L2 once and reused by all of its N blocks.
+
+// s_waitcnt: vector-memory counter <= N, others not waited on (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Direct global->LDS 16-byte load (lane l writes LDS bytes [16l, 16l+16) after the wave-uniform
+// base).  Issued through inline assembly so that the compiler does not fence every later LDS read
+// behind it; the kernel orders these loads itself with explicit vmcnt waits and barriers.
+__device__ __forceinline__ void g2lds16(const void* g, void* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
+}
+
+template <int EPI, bool OUT_F32, int NSTAGE>
+__global__ __launch_bounds__(512) void gemm_w4a16_mm(GemmArgs p) {
+  constexpr int BM = 128, BN = 256, MI = 4, NI = 4;
+  constexpr int A_BYTES = BM * 256;          // 128 rows x 128 K x bf16
+  constexpr int B_BYTES = (BN / 16) * 1024;  // 16 packed code blocks
+  constexpr int S_BYTES = (BN / 16) * 128;   // 16 packed scale blocks
+  constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * STAGE];
+  __shared__ int32_t sRow[BM];
+
+  const int N = p.N, K = p.K;
+  const int ncols = EPI == MOE_EPI_SILU_MUL ? N / 2 : N;
+  const int bcols = EPI == MOE_EPI_SILU_MUL ? BN / 2 : BN;
+  const int nbn = (ncols + bcols - 1) / bcols;
+  const int nbx = (nbn + 7) / 8;
+  const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
+  const int tile = j / nbx, nb = xcd + 8 * (j % nbx);
+  if (nb >= nbn || tile >= *p.num_tiles) return;
+  const int e = p.tiles[3 * tile], row0 = p.tiles[3 * tile + 1], rows = p.tiles[3 * tile + 2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int l16 = lane & 15, q = lane >> 4;
+  const int nks = K / kBK;
+  const int NB16 = N / 16;
+
+  for (int i = tid; i < BM; i += 512) {
+    const int r = row0 + (i < rows ? i : 0);
+    sRow[i] = p.a_row_of ? p.a_row_of[r] / p.a_row_div : r;
+  }
+  __syncthreads();
+
+  // global sources of this wave's direct loads
+  const uint16_t* a_src[4];  // activation instructions i = 4*wave + t: rows 4i .. 4i+3
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int r = 4 * (4 * wave + t) + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    a_src[t] = p.A + (size_t)sRow[r] * K + c * 8;
+  }
+  auto block_row = [&](int blk) -> int {  // packed row-block index of LDS block blk (clamped)
+    int rb, first;
+    if (EPI == MOE_EPI_SILU_MUL) {
+      first = nb * (BN / 2) + (blk & 7) * 16;
+      rb = (blk < 8 ? first : N / 2 + first) / 16;
+      if (first >= N / 2) rb = 0;
+    } else {
+      first = nb * BN + blk * 16;
+      rb = first / 16;
+      if (first >= N) rb = 0;
+    }
+    return rb;
+  };
+  const uint8_t* b_src[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    b_src[t] = p.Wq + ((size_t)e * NB16 + block_row(2 * wave + t)) * (size_t)nks * 1024 + lane * 16;
+  const uint8_t* s_src = reinterpret_cast<const uint8_t*>(p.Ws) +
+                         ((size_t)e * NB16 + block_row(8 * (wave & 1) + (lane >> 3))) * (size_t)nks * 128 + (lane & 7) * 16;
+
+  auto issue = [&](int ks, int stage) {
+    uint8_t* st = smem + stage * STAGE;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) g2lds16(a_src[t] + (size_t)ks * kBK, st + (4 * wave + t) * 1024);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) g2lds16(b_src[t] + (size_t)ks * 1024, st + A_BYTES + (2 * wave + t) * 1024);
+    if (wave < 2) g2lds16(s_src + (size_t)ks * 128, st + A_BYTES + B_BYTES + wave * 1024);
+  };
+
+  // LDS blocks of this wave's 4 column blocks
+  int blk[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+    blk[ni] = EPI == MOE_EPI_SILU_MUL ? (ni < 2 ? 2 * wn + ni : 8 + 2 * wn + (ni - 2)) : 4 * wn + ni;
+
+  f32x4 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Software pipeline over the MFMA sequence (g, mi, ni), carried across K steps: the partial of
+  // MFMA (mi, ni) waits in pend[ni] and is scaled into its accumulator four MFMAs later, right after
+  // MFMA (mi + 1, ni) is issued; the scale of a partial from the previous group is in psc.  So an MFMA
+  // result is never read right after it is produced, and the scale FMAs fill the MFMA shadow.  The
+  // accumulators still receive their groups in K order; the pipeline starts with zero partials and
+  // zero scales (adding 0 * 0 to a zero accumulator).
+  f32x4 pend[NI];
+  float psc[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    psc[ni] = 0.f;
+    pend[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto compute = [&](int stage) {
+    const uint8_t* st = smem + stage * STAGE;
+    u32x4 braw[NI];
+    u32x2 sraw[NI];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      braw[ni] = *reinterpret_cast<const u32x4*>(st + A_BYTES + blk[ni] * 1024 + lane * 16);
+      sraw[ni] = *reinterpret_cast<const u32x2*>(st + A_BYTES + B_BYTES + blk[ni] * 128 + l16 * 8);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x8 af[MI], bf[NI];
+      float sc[NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int r = wm * 64 + mi * 16 + l16;  // r % 16 == l16
+        af[mi] = *reinterpret_cast<const bf16x8*>(st + r * 256 + (((g * 4 + q) ^ l16) * 16));
+      }
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        bf[ni] = e2m1x8_to_bf16(braw[ni][g]);
+        sc[ni] = __uint_as_float((g & 1) ? (sraw[ni][g >> 1] & 0xFFFF0000u) : (sraw[ni][g >> 1] << 16));
+      }
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const f32x4 part = mfma16x16x32(af[mi], bf[ni], f32x4{0.f, 0.f, 0.f, 0.f});
+          if (mi == 0) acc[MI - 1][ni] += psc[ni] * pend[ni];
+          else acc[mi - 1][ni] += sc[ni] * pend[ni];
+          pend[ni] = part;
+        }
+#pragma unroll
+      for (int i = 0; i < MI * NI; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // then four VALU instructions
+      }
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) psc[ni] = sc[ni];
+    }
+  };
+
+  // Per-step direct loads of each wave: 6 (waves 2..7) or 7 (waves 0, 1).  Step s lives in stage
+  // s % NSTAGE.  The waits are explicit: a stage is read after this wave's loads for it have landed
+  // (at most the next step's loads still in flight) and after the barrier that publishes everyone's.
+  issue(0, 0);
+  if (nks > 1) issue(1, 1);
+  for (int s = 0; s < nks; ++s) {
+    if (s + 1 < nks) wait_vmcnt<6>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (s + 2 < nks) issue(s + 2, (s + 2) % NSTAGE);
+    compute(s % NSTAGE);
+  }
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) acc[MI - 1][ni] += psc[ni] * pend[ni];
+
+  int ncol[NI];
+  bool nvalid[NI];
+  const int col0 = EPI == MOE_EPI_SILU_MUL ? nb * (BN / 2) + wn * 32 : nb * BN + wn * 64;
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    int n;
+    column_of<EPI, NI>(p, col0, ni, l16, n, ncol[ni], nvalid[ni]);
+  }
+  store_tile<EPI, OUT_F32, MI, NI>(p, acc, wm * 64, row0, rows, q, ncol, nvalid);
+}
+
+// ---------------------------------------------------------------------------------------------------
 // Launch configuration.
 
 static int layout_of(const GemmArgs& a) {
@@ -448,8 +641,24 @@ static hipError_t by_variant(const GemmArgs& a, hipStream_t s) {
   return by_layout<Cfg, MOE_EPI_NONE, false>(a, s);
 }
 
+template <int EPI, bool F32>
+static hipError_t launch_mm(const GemmArgs& a, hipStream_t s) {
+  const int ncols = EPI == MOE_EPI_SILU_MUL ? a.N / 2 : a.N;
+  const int bcols = EPI == MOE_EPI_SILU_MUL ? 128 : 256;
+  const int nbn = (ncols + bcols - 1) / bcols;
+  const unsigned grid = 8u * (unsigned)((nbn + 7) / 8) * (unsigned)a.max_tiles;
+  gemm_w4a16_mm<EPI, F32, 3><<<grid, 512, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t stream) {
   if (a.max_tiles <= 0) return hipSuccess;
+  // (packed SiLU*mul needs N % 32 == 0, checked by the caller: up rows start a 16-row block)
+  if (block_m == 128 && a.packed) {
+    if (a.epilogue == MOE_EPI_SILU_MUL) return launch_mm<MOE_EPI_SILU_MUL, false>(a, stream);
+    if (a.out_f32) return launch_mm<MOE_EPI_NONE, true>(a, stream);
+    return launch_mm<MOE_EPI_NONE, false>(a, stream);
+  }
   switch (block_m) {
     case 16: return by_variant<Tiled<16, 128, 1, 3>>(a, stream);
     case 32: return by_variant<Tiled<32, 128, 1, 3>>(a, stream);

@@ -58,6 +58,21 @@ def test_pure_size_queries(lib):
     assert moe.moe_ffn_workspace_bytes(4, 2048, 512, 8, 9) == 0    # k > E
 
 
+def test_block_m_choice():
+    P, C = moe.MOE_LAYOUT_PACKED, moe.MOE_LAYOUT_CANONICAL
+    assert moe.moe_ffn_block_m(1, 128, 8, P) == 16        # decode: 8 rows over 128 experts
+    assert moe.moe_ffn_block_m(800, 256, 8, P) == 32      # 25 rows per expert
+    assert moe.moe_ffn_block_m(8192, 512, 10, P) == 64    # 160 rows per expert
+    assert moe.moe_ffn_block_m(4096, 8, 2, P) == 128      # 1024 rows per expert: large-tile kernel
+    assert moe.moe_ffn_block_m(4096, 8, 2, C) == 64       # ... which needs packed weights
+    assert moe.moe_ffn_block_m(4096, 8, 2, 7) == -1
+    assert moe.moe_ffn_block_m(4, 8, 9, P) == -1
+    # one workspace size serves both layouts: the tile list is sized for the smaller tile height
+    R, E = 4096 * 2, 8
+    ws = moe.moe_ffn_workspace_bytes(4096, 4096, 14336, E, 2)
+    assert ws >= R * 14336 * 2 + R * 4096 * 4 + moe.moe_max_tiles(4096, 2, E, 64) * 12
+
+
 FAKE = 1 << 20  # an aligned, never-dereferenced pointer value: validation fails before any launch
 
 
@@ -120,6 +135,7 @@ def test_grouped_gemm_rejects(lib):
     assert call(lay=2) == -1           # unknown layout
     assert call(lay=1, K=96) == -2     # packed needs K % 128 == 0
     assert call(lay=1, N=200) == -2    # packed needs N % 16 == 0
+    assert call(lay=1, N=80, epi=1) == -2  # packed SiLU*mul needs N % 32 == 0 (up rows start a block)
     assert call(lay=1, Ws=_ptr(FAKE + 2)) == -3  # packed scales need 8-byte alignment
 
 

@@ -339,3 +339,39 @@ def test_grouped_gemm_packed_matches_canonical_bits(bm):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(c1.view(torch.int16 if od == moe.MOE_OUT_BF16 else torch.int32).cpu().numpy(),
                                       c2.view(torch.int16 if od == moe.MOE_OUT_BF16 else torch.int32).cpu().numpy())
+
+
+# The 128-row large-tile kernel (packed weights, block_m 128) against the canonical 64-row kernel: per
+# output element both accumulate the same group partials in K order, so the bits must agree.  Shapes
+# cover 1..5 K steps (pipeline prologue and tail), a ragged last N block and ragged row tiles.
+@pytest.mark.parametrize("T,E,k,H,I,seed", [
+    (300, 4, 2, 640, 416, 31),   # gate_up: 5 K steps, 416 = 3.25 column blocks; down not packable (I % 128)
+    (260, 3, 2, 640, 384, 32),   # down: 3 K steps, 640 = 2.5 column blocks; gate_up 5 K steps
+    (200, 2, 1, 128, 256, 33),   # gate_up 1 K step; down 2 K steps
+])
+def test_large_tile_gemm_matches_canonical_bits(T, E, k, H, I, seed):
+    wl = mi.custom("mm", T, E, k, H, I, skew=True, seed=seed)
+    inp, d = workload_inputs(wl)
+    rid, _ = oracle.route(inp.logits, wl.k)
+    a64 = moe.moe_align(gu.dev(rid), wl.E, 64)
+    a128 = moe.moe_align(gu.dev(rid), wl.E, 128)
+    R = wl.T * wl.k
+    h = gu.dev_bf16(mi.f32_to_bf16_bits(np.random.default_rng(seed).standard_normal((R, wl.I), dtype=np.float32)))
+    projs = []
+    if wl.H % 128 == 0:
+        projs.append((d.w13_q, d.w13_s, moe.MOE_EPI_SILU_MUL, d.x, "sorted", wl.k, moe.MOE_OUT_BF16))
+    if wl.I % 128 == 0:
+        projs.append((d.w2_q, d.w2_s, moe.MOE_EPI_NONE, h, None, 1, moe.MOE_OUT_F32))
+    assert projs
+    for (wq, ws, epi, A, aro, div, od) in projs:
+        _log(f"large tile T={T} E={E} k={k} H={H} I={I} epi={epi}")
+        pq, ps = moe.moe_w4_prepack(wq, ws)
+        ref = moe.moe_grouped_gemm_w4a16(A, a64["sorted_ids"] if aro else None, div, wq, ws, a64["tiles"],
+                                         a64["max_tiles"], a64["num_tiles"], 64, epi, R, od)
+        out = moe.moe_grouped_gemm_w4a16(A, a128["sorted_ids"] if aro else None, div, pq, ps, a128["tiles"],
+                                         a128["max_tiles"], a128["num_tiles"], 128, epi, R, od,
+                                         weight_layout=moe.MOE_LAYOUT_PACKED)
+        torch.cuda.synchronize()
+        view = torch.int16 if od == moe.MOE_OUT_BF16 else torch.int32
+        np.testing.assert_array_equal(out.view(view).cpu().numpy(), ref.view(view).cpu().numpy())
+
