@@ -127,14 +127,16 @@ def moe_route_topk(logits: torch.Tensor, k: int, topk_ids=None, topk_w=None, str
     return topk_ids, topk_w
 
 
-def moe_align(topk_ids: torch.Tensor, E: int, block_m: int, stream=None) -> dict:
+def moe_align(topk_ids: torch.Tensor, E: int, block_m: int, stream=None, max_tiles: int = None) -> dict:
     """topk_ids int32 [T, k] -> dict of device tensors (counts, offsets, sorted_ids, inv_perm, tiles,
-    num_tiles) and the tile capacity ``max_tiles``."""
+    num_tiles) and the tile capacity ``max_tiles`` (default: moe_max_tiles; a larger capacity may be
+    given)."""
     _req(topk_ids, torch.int32, "topk_ids")
     T, k = topk_ids.shape
     dev = topk_ids.device
     R = T * k
-    max_tiles = moe_max_tiles(T, k, E, block_m)
+    if max_tiles is None:
+        max_tiles = moe_max_tiles(T, k, E, block_m)
     out = dict(
         counts=torch.empty(E, dtype=torch.int32, device=dev),
         offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),

@@ -9,8 +9,9 @@
 // "四、算子融合：性能翻倍的关键", fuses the activation into the matmul.
 //
 // gfx950 design shared by both kernels below:
-//  * Work list instead of a 3D grid: blockIdx.y indexes the device-side tile list written by
-//    moe_align (exact, never a host guess); blockIdx.x is the N block.  Slots past num_tiles exit.
+//  * Work list instead of a 3D grid: each workgroup maps its index to an entry of the device-side
+//    tile list written by moe_align (exact, never a host guess) and an N block; slots past
+//    num_tiles are skipped.
 //  * v_mfma_f32_16x16x32_bf16: one MFMA spans exactly one 32-element scale group.  Codes are
 //    converted to exact bf16 (hardware FP4 converter, unit scale); the MFMA produces the group's
 //    fp32 partial, which is multiplied by the bf16 group scale and added to the fp32 accumulator.
@@ -135,26 +136,41 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x4 (&acc)
   }
 }
 
+// Work order of the tiled kernel.  Workgroup b runs on XCD b % 8 (workgroups are dispatched
+// round-robin over the 8 XCDs, each with its own L2).  XCD x takes the contiguous share
+// [x*n/8, (x+1)*n/8) of the n tiles and runs all N blocks of one tile before the next, so a tile's
+// gathered activation rows are fetched into that XCD's L2 once, and consecutive tiles of one expert
+// find its weights there.  The work list holds 8 * ceil(max_tiles / 8) * nbn slots; slots past the
+// XCD's share are skipped.
+__device__ __forceinline__ bool xcd_tile(long long b, int nbn, int num_tiles, int& tile, int& nb) {
+  const int xcd = (int)(b & 7);
+  const long long j = b >> 3;
+  const int lt = (int)(j / nbn);
+  nb = (int)(j - (long long)lt * nbn);
+  const int t0 = (xcd * num_tiles) >> 3, t1 = ((xcd + 1) * num_tiles) >> 3;
+  tile = t0 + lt;
+  return tile < t1;
+}
+
 // ---------------------------------------------------------------------------------------------------
 // Tiled kernel: BM x BN tile per 256-thread workgroup, waves split it WAVES_M x WAVES_N; the
 // activation tile of each K step is staged once in LDS (double buffer, one barrier per step) and
 // shared by the waves.  PF = K steps in flight ahead of the one computed (ring of PF+1 slots).
+constexpr int kLDA = kBK + 8;  // padded LDS activation row of the tiled kernel (bf16 elements)
+
+// One BM x BN output tile (tile list entry `tile`, N block `nb`) of the tiled kernel.
 template <int BM, int BN, int WAVES_M, int PF, int EPI, bool OUT_F32, int LAYOUT>
-__global__ __launch_bounds__(256) void gemm_w4a16_tiled(GemmArgs p) {
+__device__ __forceinline__ void tiled_tile(const GemmArgs& p, int tile, int nb, uint16_t (&sA)[2][BM * kLDA],
+                                           int32_t (&sRow)[BM]) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int MI = WM / 16, NI = WN / 16;
-  constexpr int LDA = kBK + 8;               // padded LDS row (bf16 elements)
+  constexpr int LDA = kLDA;
   constexpr int ACH = BM * (kBK / 8) / 256;  // 16-byte activation chunks per thread per step
   constexpr int NS = PF + 1;
   static_assert(MI >= 1 && NI >= 1 && ACH >= 1, "tile shape");
   static_assert(EPI != MOE_EPI_SILU_MUL || NI % 2 == 0, "SiLU*mul pairs gate and up blocks");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDA];
-  __shared__ int32_t sRow[BM];
-
-  const int tile = blockIdx.y;
-  if (tile >= *p.num_tiles) return;
   const int e = p.tiles[3 * tile], row0 = p.tiles[3 * tile + 1], rows = p.tiles[3 * tile + 2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -171,7 +187,7 @@ __global__ __launch_bounds__(256) void gemm_w4a16_tiled(GemmArgs p) {
   WRow wr[NI];
   int ncol[NI];
   bool nvalid[NI];
-  const int col0 = EPI == MOE_EPI_SILU_MUL ? blockIdx.x * (BN / 2) + wn * (WN / 2) : blockIdx.x * BN + wn * WN;
+  const int col0 = EPI == MOE_EPI_SILU_MUL ? nb * (BN / 2) + wn * (WN / 2) : nb * BN + wn * WN;
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) {
     int n;
@@ -240,6 +256,9 @@ __global__ __launch_bounds__(256) void gemm_w4a16_tiled(GemmArgs p) {
   // s+PF into the slot freed by step s-1, then compute step s.  Activation chunks past K are zeroed
   // here, which makes the matching partial products exactly zero whatever the clamped codes hold.
   auto step = [&](int s, int u, bool prefetch) {
+    // keep the scheduler from hoisting work on later steps' registers into this step, which would
+    // make this step wait for their loads and shorten the prefetch distance
+    __builtin_amdgcn_sched_barrier(0);
     uint16_t* a_lds = sA[s & 1];
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
@@ -266,138 +285,22 @@ __global__ __launch_bounds__(256) void gemm_w4a16_tiled(GemmArgs p) {
   store_tile<EPI, OUT_F32, MI, NI>(p, acc, wm * WM, row0, rows, q, ncol, nvalid);
 }
 
-// ---------------------------------------------------------------------------------------------------
-// Streaming kernel for tiles of at most 32 rows (decode and few-rows-per-expert prefill), where the
-// weight stream from HBM is the bound.  The four waves split K into contiguous ranges; each wave
-// loads its own activation fragments (16-byte loads, rows gathered through a_row_of; padding rows
-// repeat the tile's first row, which the load coalescer merges) and its weights straight into a
-// PF-deep register ring, so the main loop has no LDS traffic and no barrier.  The four partial sums
-// are reduced through LDS once per tile, in wave order.
-template <int BM, int BN, int PF, int EPI, bool OUT_F32, int LAYOUT>
-__global__ __launch_bounds__(256) void gemm_w4a16_sk(GemmArgs p) {
-  constexpr int MI = BM / 16, NI = BN / 16;
-  static_assert(MI >= 1 && MI <= 2 && NI >= 1, "tile shape");
-  static_assert(EPI != MOE_EPI_SILU_MUL || NI % 2 == 0, "SiLU*mul pairs gate and up blocks");
-  constexpr int NS = PF + 1;
+// Launch grids are 2-D: x holds at most kGridX workgroups (a multiple of 8, so with linear index
+// b = y * gridDim.x + x, b % 8 still names the XCD) and y as many rows as the work list needs.
+constexpr unsigned kGridX = 8u << 16;
 
-  __shared__ __attribute__((aligned(16))) float red[3 * 64 * MI * NI * 4];
+__device__ __forceinline__ long long linear_block() {
+  return (long long)blockIdx.y * gridDim.x + blockIdx.x;
+}
 
-  const int tile = blockIdx.y;
-  if (tile >= *p.num_tiles) return;
-  const int e = p.tiles[3 * tile], row0 = p.tiles[3 * tile + 1], rows = p.tiles[3 * tile + 2];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l16 = lane & 15, q = lane >> 4;
-  const int K = p.K;
-  const int kgroups = K / kGroup;
-  const int nks = (K + kBK - 1) / kBK;
-  const int per = (nks + 3) / 4;  // steps per wave (contiguous K ranges)
-  const int s_begin = min(nks, wk * per), s_end = min(nks, s_begin + per);
-  const bool m1 = MI > 1 && rows > 16;  // second 16-row block present (wave-uniform)
-
-  const uint16_t* arow[MI];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
-    const int i = mi * 16 + l16;
-    const int r = row0 + (i < rows ? i : 0);
-    arow[mi] = p.A + (size_t)(p.a_row_of ? p.a_row_of[r] / p.a_row_div : r) * K + q * 8;
-  }
-  WRow wr[NI];
-  int ncol[NI];
-  bool nvalid[NI];
-  const int col0 = blockIdx.x * (EPI == MOE_EPI_SILU_MUL ? BN / 2 : BN);
-#pragma unroll
-  for (int ni = 0; ni < NI; ++ni) {
-    int n;
-    column_of<EPI, NI>(p, col0, ni, l16, n, ncol[ni], nvalid[ni]);
-    wr[ni] = wrow_of<LAYOUT>(p, e, n, q, lane);
-  }
-
-  f32x4 acc[MI][NI];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 areg[NS][MI][4];
-  u32x4 breg[NS][NI];
-  uint32_t sreg[NS][NI][4];
-
-  auto load_step = [&](int s, int u) {
-    s = min(s, s_end - 1);  // prefetches past this wave's range re-read its last step (unused)
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        areg[u][mi][g] = *reinterpret_cast<const u32x4*>(arow[mi] + min(s * kBK + g * 32, K - 32));
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) load_w<LAYOUT>(wr[ni], s, q, kgroups, breg[u][ni], sreg[u][ni]);
-  };
-
-  auto compute_step = [&](int s, int u) {
-    u32x4 bt[NI];
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) bt[ni] = b_operands<LAYOUT>(breg[u][ni]);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      if (LAYOUT == kCanonGeneric && s * 4 + g >= kgroups) break;  // K tail (wave-uniform)
-      bf16x8 bf[NI];
-      float sc[NI];
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        bf[ni] = e2m1x8_to_bf16(bt[ni][g]);
-        sc[ni] = scale_of<LAYOUT>(sreg[u][ni], g);
-      }
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        if (mi == 1 && !m1) break;
-        const bf16x8 af = __builtin_bit_cast(bf16x8, areg[u][mi][g]);
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const f32x4 part = mfma16x16x32(af, bf[ni], f32x4{0.f, 0.f, 0.f, 0.f});
-          acc[mi][ni] += sc[ni] * part;
-        }
-      }
-    }
-  };
-
-  if (s_end > s_begin) {
-#pragma unroll
-    for (int u = 0; u < PF; ++u) load_step(s_begin + u, u);
-    int s0 = s_begin;
-    for (; s0 + NS <= s_end; s0 += NS) {
-#pragma unroll
-      for (int u = 0; u < NS; ++u) {
-        load_step(s0 + u + PF, (u + PF) % NS);
-        compute_step(s0 + u, u);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < NS - 1; ++u)
-      if (s0 + u < s_end) compute_step(s0 + u, u);
-  }
-
-  // K-slice reduction in wave order: waves 1..3 park their sums, wave 0 adds them.
-  constexpr int PER = MI * NI * 4;
-  if (wk > 0) {
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) red[((wk - 1) * 64 + lane) * PER + (mi * NI + ni) * 4 + r] = acc[mi][ni][r];
-  }
-  __syncthreads();
-  if (wk > 0) return;
-#pragma unroll
-  for (int w = 0; w < 3; ++w)
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[mi][ni][r] += red[(w * 64 + lane) * PER + (mi * NI + ni) * 4 + r];
-  store_tile<EPI, OUT_F32, MI, NI>(p, acc, 0, row0, rows, q, ncol, nvalid);
+template <int BM, int BN, int WAVES_M, int PF, int EPI, bool OUT_F32, int LAYOUT>
+__global__ __launch_bounds__(256) void gemm_w4a16_tiled(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kLDA];
+  __shared__ int32_t sRow[BM];
+  const int nbn = EPI == MOE_EPI_SILU_MUL ? (p.N / 2 + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
+  int tile, nb;
+  if (!xcd_tile(linear_block(), nbn, *p.num_tiles, tile, nb)) return;
+  tiled_tile<BM, BN, WAVES_M, PF, EPI, OUT_F32, LAYOUT>(p, tile, nb, sA, sRow);
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -430,24 +333,18 @@ __device__ __forceinline__ void g2lds16(const void* g, void* lds_wave_base) {
   asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
 }
 
+constexpr int kMmBM = 128, kMmBN = 256;
+constexpr int kMmStage = kMmBM * 256 + (kMmBN / 16) * 1024 + (kMmBN / 16) * 128;  // A + codes + scales
+
+// One 128 x 256 output tile (tile list entry `tile`, N block `nb`) of the large-tile kernel.
 template <int EPI, bool OUT_F32, int NSTAGE>
-__global__ __launch_bounds__(512) void gemm_w4a16_mm(GemmArgs p) {
-  constexpr int BM = 128, BN = 256, MI = 4, NI = 4;
+__device__ __forceinline__ void mm_tile(const GemmArgs& p, int tile, int nb, uint8_t (&smem)[NSTAGE * kMmStage],
+                                        int32_t (&sRow)[kMmBM]) {
+  constexpr int BM = kMmBM, BN = kMmBN, MI = 4, NI = 4;
   constexpr int A_BYTES = BM * 256;          // 128 rows x 128 K x bf16
   constexpr int B_BYTES = (BN / 16) * 1024;  // 16 packed code blocks
-  constexpr int S_BYTES = (BN / 16) * 128;   // 16 packed scale blocks
-  constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * STAGE];
-  __shared__ int32_t sRow[BM];
-
+  constexpr int STAGE = kMmStage;
   const int N = p.N, K = p.K;
-  const int ncols = EPI == MOE_EPI_SILU_MUL ? N / 2 : N;
-  const int bcols = EPI == MOE_EPI_SILU_MUL ? BN / 2 : BN;
-  const int nbn = (ncols + bcols - 1) / bcols;
-  const int nbx = (nbn + 7) / 8;
-  const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
-  const int tile = j / nbx, nb = xcd + 8 * (j % nbx);
-  if (nb >= nbn || tile >= *p.num_tiles) return;
   const int e = p.tiles[3 * tile], row0 = p.tiles[3 * tile + 1], rows = p.tiles[3 * tile + 2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -593,6 +490,22 @@ __global__ __launch_bounds__(512) void gemm_w4a16_mm(GemmArgs p) {
   store_tile<EPI, OUT_F32, MI, NI>(p, acc, wm * 64, row0, rows, q, ncol, nvalid);
 }
 
+template <int EPI, bool OUT_F32, int NSTAGE>
+__global__ __launch_bounds__(512) void gemm_w4a16_mm(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * kMmStage];
+  __shared__ int32_t sRow[kMmBM];
+  const int ncols = EPI == MOE_EPI_SILU_MUL ? p.N / 2 : p.N;
+  const int bcols = EPI == MOE_EPI_SILU_MUL ? kMmBN / 2 : kMmBN;
+  const int nbn = (ncols + bcols - 1) / bcols;
+  const int nbx = (nbn + 7) / 8;
+  const long long b = linear_block();
+  const int xcd = (int)(b & 7);
+  const long long j = b >> 3;
+  const int tile = (int)(j / nbx), nb = xcd + 8 * (int)(j % nbx);
+  if (nb >= nbn || tile >= *p.num_tiles) return;
+  mm_tile<EPI, OUT_F32, NSTAGE>(p, tile, nb, smem, sRow);
+}
+
 // ---------------------------------------------------------------------------------------------------
 // Launch configuration.
 
@@ -601,10 +514,16 @@ static int layout_of(const GemmArgs& a) {
   return ((a.K % kBK) == 0 && (reinterpret_cast<uintptr_t>(a.Ws) % 8) == 0) ? kCanonFull : kCanonGeneric;
 }
 
+static dim3 grid2d(long long total) {
+  if (total <= (long long)kGridX) return dim3((unsigned)total, 1);
+  return dim3(kGridX, (unsigned)((total + kGridX - 1) / kGridX));
+}
+
 static dim3 grid_of(const GemmArgs& a, int bn) {
   const int ncols = a.epilogue == MOE_EPI_SILU_MUL ? a.N / 2 : a.N;
   const int bcols = a.epilogue == MOE_EPI_SILU_MUL ? bn / 2 : bn;
-  return dim3((ncols + bcols - 1) / bcols, a.max_tiles);
+  const long long nbn = (ncols + bcols - 1) / bcols;
+  return grid2d(8LL * ((a.max_tiles + 7) / 8) * nbn);
 }
 
 template <int BM, int BN, int WAVES_M, int PF>
@@ -612,15 +531,6 @@ struct Tiled {
   template <int EPI, bool F32, int LAYOUT>
   static hipError_t run(const GemmArgs& a, hipStream_t s) {
     gemm_w4a16_tiled<BM, BN, WAVES_M, PF, EPI, F32, LAYOUT><<<grid_of(a, BN), 256, 0, s>>>(a);
-    return hipGetLastError();
-  }
-};
-
-template <int BM, int BN, int PF>
-struct Streaming {
-  template <int EPI, bool F32, int LAYOUT>
-  static hipError_t run(const GemmArgs& a, hipStream_t s) {
-    gemm_w4a16_sk<BM, BN, PF, EPI, F32, LAYOUT><<<grid_of(a, BN), 256, 0, s>>>(a);
     return hipGetLastError();
   }
 };
@@ -646,8 +556,7 @@ static hipError_t launch_mm(const GemmArgs& a, hipStream_t s) {
   const int ncols = EPI == MOE_EPI_SILU_MUL ? a.N / 2 : a.N;
   const int bcols = EPI == MOE_EPI_SILU_MUL ? 128 : 256;
   const int nbn = (ncols + bcols - 1) / bcols;
-  const unsigned grid = 8u * (unsigned)((nbn + 7) / 8) * (unsigned)a.max_tiles;
-  gemm_w4a16_mm<EPI, F32, 3><<<grid, 512, 0, s>>>(a);
+  gemm_w4a16_mm<EPI, F32, 3><<<grid2d(8LL * ((nbn + 7) / 8) * a.max_tiles), 512, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -375,3 +375,23 @@ def test_large_tile_gemm_matches_canonical_bits(T, E, k, H, I, seed):
         view = torch.int16 if od == moe.MOE_OUT_BF16 else torch.int32
         np.testing.assert_array_equal(out.view(view).cpu().numpy(), ref.view(view).cpu().numpy())
 
+
+
+@pytest.mark.parametrize("bm,layout", [(16, 0), (64, 1), (128, 1)])
+def test_grouped_gemm_large_capacity_grid(bm, layout):
+    # A tile-list capacity far above the tiles used makes the work list longer than one grid row
+    # (2-D launch); unused slots must cost nothing and change no output bit.
+    wl = mi.custom("cap", 64, 8, 2, 256, 128, seed=41)
+    inp, d = workload_inputs(wl)
+    rid, _ = oracle.route(inp.logits, wl.k)
+    R = wl.T * wl.k
+    wq, ws = (d.w13_q, d.w13_s) if layout == 0 else moe.moe_w4_prepack(d.w13_q, d.w13_s)
+    outs = []
+    for cap in (None, 300000):
+        a = moe.moe_align(gu.dev(rid), wl.E, bm, max_tiles=cap)
+        _log(f"capacity grid bm={bm} layout={layout} max_tiles={a['max_tiles']}")
+        outs.append(moe.moe_grouped_gemm_w4a16(d.x, a["sorted_ids"], wl.k, wq, ws, a["tiles"], a["max_tiles"],
+                                               a["num_tiles"], bm, moe.MOE_EPI_SILU_MUL, R, moe.MOE_OUT_BF16,
+                                               weight_layout=layout))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(outs[1].view(torch.int16).cpu().numpy(), outs[0].view(torch.int16).cpu().numpy())
