@@ -7,23 +7,26 @@
 // zero-init as real bugs.  Here the exact tile list and its length are produced on the device, and
 // every output is written in full (no output relies on prior zeroing).
 //
-// Ranking within a wave: the lanes holding the same expert id ("peers") are found with one ballot
-// per id bit; a lane's rank among its peers is the popcount of the peers below it, so the order is
-// ascending flat index (stable) without atomics.  Across waves and workgroups, per-segment counts
-// are turned into per-segment base offsets by a prefix sum in (segment, expert) order.
+// Counting uses LDS atomic adds (order-independent).  Ranking within a wave: the lanes holding the
+// same expert id ("peers") are found through a per-wave LDS table: each lane clears its id's entry,
+// ORs in its own lane bit and reads the entry back, which yields the exact peer set whatever order
+// the OR operations land in.  A lane's rank among its peers is the popcount of the peers below it,
+// so the order is ascending flat index (stable) and deterministic.  Across waves and workgroups,
+// per-segment counts are turned into per-segment base offsets by a prefix sum in (segment, expert)
+// order.
 #include "launch.h"
 #include "moe_common.h"
 
 namespace moe {
 
-__device__ __forceinline__ uint64_t peer_mask(int id, bool valid, int nbits) {
-  uint64_t m = __ballot(valid);
-  for (int b = 0; b < nbits; ++b) {
-    const bool bit = (id >> b) & 1;
-    const uint64_t bal = __ballot(bit);
-    m &= bit ? bal : ~bal;
-  }
-  return valid ? m : 0ull;
+// Peer set of each lane: lanes of this wave holding the same expert id.  tbl is this wave's table of
+// E 64-bit entries; a wave's LDS operations complete in issue order, so the clear, the ORs and the
+// read-back of one call are ordered, and only entries of ids present in the call are touched.
+__device__ __forceinline__ uint64_t lds_peers(uint64_t* tbl, int id, bool valid) {
+  const int lane = threadIdx.x & 63;
+  if (valid) tbl[id] = 0ull;
+  if (valid) atomicOr(reinterpret_cast<unsigned long long*>(tbl + id), 1ull << lane);
+  return valid ? tbl[id] : 0ull;
 }
 
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
@@ -108,21 +111,18 @@ __device__ __forceinline__ void load_segment(const int32_t* ids, int f0, int f1,
   }
 }
 
-// Count segment [f0, f1) of one wave into cnt[id].
-__device__ __forceinline__ void wave_count(const int (&id)[kSegRegs], int f0, int f1, int nbits, int32_t* cnt) {
-  const int lane = threadIdx.x & 63;
+// Count segment [f0, f1) of one wave into cnt[id] (LDS atomic adds).
+__device__ __forceinline__ void wave_count(const int (&id)[kSegRegs], int f0, int f1, int32_t* cnt) {
 #pragma unroll
   for (int j = 0; j < kSegRegs; ++j) {
     if (f0 + 64 * j >= f1) break;
-    const bool v = id[j] >= 0;
-    const uint64_t peers = peer_mask(v ? id[j] : 0, v, nbits);
-    if (v && lane == __ffsll((unsigned long long)peers) - 1) cnt[id[j]] += __popcll(peers);
+    if (id[j] >= 0) atomicAdd(cnt + id[j], 1);
   }
 }
 
-// Scatter segment [f0, f1) of one wave; base[id] is the next free permuted row of expert id.
-// sorted_ids may point to LDS (staging) or global memory.
-__device__ __forceinline__ void wave_scatter(const int (&id)[kSegRegs], int f0, int f1, int nbits, int32_t* base,
+// Scatter segment [f0, f1) of one wave; base[id] is the next free permuted row of expert id, tbl this
+// wave's peer table.  sorted_ids may point to LDS (staging) or global memory.
+__device__ __forceinline__ void wave_scatter(const int (&id)[kSegRegs], int f0, int f1, int32_t* base, uint64_t* tbl,
                                              int32_t* sorted_ids, int32_t* inv_perm) {
   const int lane = threadIdx.x & 63;
   const uint64_t below = (1ull << lane) - 1ull;
@@ -132,48 +132,47 @@ __device__ __forceinline__ void wave_scatter(const int (&id)[kSegRegs], int f0, 
     const int f = f0 + 64 * j + lane;
     const bool v = id[j] >= 0;
     const int e = v ? id[j] : 0;
-    const uint64_t peers = peer_mask(e, v, nbits);
+    const uint64_t peers = lds_peers(tbl, e, v);
     const int b = v ? base[e] : 0;
     if (v) {
       const int r = b + __popcll(peers & below);
       sorted_ids[r] = f;
       inv_perm[f] = r;
     }
-    // one lane per expert advances its base; every lane of the wave has read it above
-    if (v && lane == __ffsll((unsigned long long)peers) - 1) base[e] = b + __popcll(peers);
+    // the highest peer advances the expert's base; every peer has read it above
+    if (v && (peers >> lane) == 1ull) base[e] = b + __popcll(peers);
   }
 }
 
 // Whole permutation in one 1024-thread workgroup (align_single_fits(R, E)).  sorted_ids is built in
 // LDS (the scatter is random) and written out with coalesced stores.
 __global__ __launch_bounds__(1024) void align_single_kernel(const int32_t* __restrict__ ids, int R, int E,
-                                                            int bm, int nbits, int32_t* counts,
-                                                            int32_t* offsets, int32_t* sorted_ids,
-                                                            int32_t* inv_perm, int32_t* tiles,
-                                                            int max_tiles, int32_t* num_tiles) {
-  extern __shared__ int32_t smem[];
-  int32_t* cnt = smem;                  // [16][E]
-  int* scratch = smem + 16 * E;         // 64 ints
-  int32_t* sorted_lds = scratch + 64;   // [R]
+                                                            int bm, int32_t* counts, int32_t* offsets,
+                                                            int32_t* sorted_ids, int32_t* inv_perm,
+                                                            int32_t* tiles, int max_tiles, int32_t* num_tiles) {
+  __shared__ int32_t cnt[16 * kAlignSingleMaxE];
+  __shared__ int scratch[64];
+  __shared__ int32_t sorted_lds[kAlignSingleMaxR];
+  __shared__ uint64_t tbl[16 * kAlignSingleMaxE];
   const int tid = threadIdx.x, wave = tid >> 6;
   for (int i = tid; i < 16 * E; i += 1024) cnt[i] = 0;
-  __syncthreads();
   const int seg = (((R + 15) / 16) + 63) & ~63;
   const int f0 = min(R, wave * seg), f1 = min(R, f0 + seg);
   int id[kSegRegs];
   load_segment(ids, f0, f1, id);
-  wave_count(id, f0, f1, nbits, cnt + wave * E);
+  __syncthreads();
+  wave_count(id, f0, f1, cnt + wave * E);
   __syncthreads();
   finish_expert(tid, E, 16, bm, cnt, counts, offsets, tiles, max_tiles, num_tiles, scratch);
   __syncthreads();
-  wave_scatter(id, f0, f1, nbits, cnt + wave * E, sorted_lds, inv_perm);
+  wave_scatter(id, f0, f1, cnt + wave * E, tbl + wave * E, sorted_lds, inv_perm);
   __syncthreads();
   for (int r = tid; r < R; r += 1024) sorted_ids[r] = sorted_lds[r];
 }
 
 // Multi-workgroup path, step 1: per-(workgroup, wave) counts, kAlignChunk slots per workgroup.
 __global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restrict__ ids, int R, int E,
-                                                         int nbits, int32_t* seg_cnt) {
+                                                         int32_t* seg_cnt) {
   extern __shared__ int32_t cnt[];  // [4][E]
   const int tid = threadIdx.x, wave = tid >> 6;
   for (int i = tid; i < 4 * E; i += 256) cnt[i] = 0;
@@ -182,7 +181,7 @@ __global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restri
   const int f1 = min(R, f0 + kAlignChunk / 4);
   int id[kSegRegs];
   load_segment(ids, f0, f1, id);
-  wave_count(id, f0, f1, nbits, cnt + wave * E);
+  wave_count(id, f0, f1, cnt + wave * E);
   __syncthreads();
   for (int i = tid; i < 4 * E; i += 256) seg_cnt[(size_t)blockIdx.x * 4 * E + i] = cnt[i];
 }
@@ -199,9 +198,11 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(int32_t* seg_cnt, int 
 
 // Step 3: each wave re-walks its segment and scatters from its base rows.
 __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __restrict__ ids, int R, int E,
-                                                            int nbits, const int32_t* seg_base,
-                                                            int32_t* sorted_ids, int32_t* inv_perm) {
-  extern __shared__ int32_t base[];  // [4][E]
+                                                            const int32_t* seg_base, int32_t* sorted_ids,
+                                                            int32_t* inv_perm) {
+  extern __shared__ uint64_t dyn[];  // [4][E] peer tables, then [4][E] base rows
+  uint64_t* tbl = dyn;
+  int32_t* base = reinterpret_cast<int32_t*>(dyn + 4 * E);
   const int tid = threadIdx.x, wave = tid >> 6;
   for (int i = tid; i < 4 * E; i += 256) base[i] = seg_base[(size_t)blockIdx.x * 4 * E + i];
   __syncthreads();
@@ -209,13 +210,7 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
   const int f1 = min(R, f0 + kAlignChunk / 4);
   int id[kSegRegs];
   load_segment(ids, f0, f1, id);
-  wave_scatter(id, f0, f1, nbits, base + wave * E, sorted_ids, inv_perm);
-}
-
-static int id_bits(int E) {
-  int b = 0;
-  while ((1 << b) < E) ++b;
-  return b;
+  wave_scatter(id, f0, f1, base + wave * E, tbl + wave * E, sorted_ids, inv_perm);
 }
 
 size_t align_workspace_bytes(int R, int E) {
@@ -227,20 +222,18 @@ size_t align_workspace_bytes(int R, int E) {
 hipError_t launch_align(const int32_t* ids, int R, int E, int block_m, int32_t* counts,
                         int32_t* offsets, int32_t* sorted_ids, int32_t* inv_perm, int32_t* tiles,
                         int max_tiles, int32_t* num_tiles, void* workspace, hipStream_t stream) {
-  const int nbits = id_bits(E);
   if (align_single_fits(R, E)) {
-    const size_t lds = (16 * (size_t)E + 64 + (size_t)R) * sizeof(int32_t);
-    align_single_kernel<<<1, 1024, lds, stream>>>(ids, R, E, block_m, nbits, counts, offsets, sorted_ids,
-                                                  inv_perm, tiles, max_tiles, num_tiles);
+    align_single_kernel<<<1, 1024, 0, stream>>>(ids, R, E, block_m, counts, offsets, sorted_ids, inv_perm, tiles,
+                                                max_tiles, num_tiles);
     return hipGetLastError();
   }
   const int nblk = (R + kAlignChunk - 1) / kAlignChunk;
   int32_t* seg = static_cast<int32_t*>(workspace);
-  const size_t lds = 4 * (size_t)E * sizeof(int32_t);
-  align_hist_kernel<<<nblk, 256, lds, stream>>>(ids, R, E, nbits, seg);
+  align_hist_kernel<<<nblk, 256, 4 * (size_t)E * sizeof(int32_t), stream>>>(ids, R, E, seg);
   align_scan_kernel<<<1, 1024, 0, stream>>>(seg, nblk * 4, E, block_m, counts, offsets, tiles, max_tiles,
                                             num_tiles);
-  align_scatter_kernel<<<nblk, 256, lds, stream>>>(ids, R, E, nbits, seg, sorted_ids, inv_perm);
+  align_scatter_kernel<<<nblk, 256, 4 * (size_t)E * (sizeof(uint64_t) + sizeof(int32_t)), stream>>>(
+      ids, R, E, seg, sorted_ids, inv_perm);
   return hipGetLastError();
 }
 

@@ -11,11 +11,11 @@ namespace moe {
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              hipStream_t stream);
 
-// Sizes the single-workgroup permutation handles: R = T*k <= 8192 slots and an LDS footprint of
-// 16 per-wave counters per expert plus the R-entry staging of sorted_ids within 60 KB.
+// Single-workgroup permutation: up to kAlignSingleMaxR slots and kAlignSingleMaxE experts (static
+// LDS: 16 per-wave count rows, the staged permutation and 16 per-wave peer tables).
 constexpr int kAlignSingleMaxR = 8192;
-constexpr int kAlignSingleMaxLdsInts = 15360;
-inline bool align_single_fits(int R, int E) { return R <= kAlignSingleMaxR && 16 * E + R + 64 <= kAlignSingleMaxLdsInts; }
+constexpr int kAlignSingleMaxE = 512;
+inline bool align_single_fits(int R, int E) { return R <= kAlignSingleMaxR && E <= kAlignSingleMaxE; }
 // Flat slots per workgroup in the multi-workgroup permutation.
 constexpr int kAlignChunk = 4096;
 size_t align_workspace_bytes(int R, int E);
