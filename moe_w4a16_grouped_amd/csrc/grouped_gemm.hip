@@ -569,9 +569,9 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t strea
     return launch_mm<MOE_EPI_NONE, false>(a, stream);
   }
   switch (block_m) {
-    case 16: return by_variant<Tiled<16, 128, 1, 3>>(a, stream);
-    case 32: return by_variant<Tiled<32, 128, 1, 3>>(a, stream);
-    case 64: return by_variant<Tiled<64, 128, 1, 2>>(a, stream);
+    case 16: return by_variant<Tiled<16, 128, 1, 2>>(a, stream);
+    case 32: return by_variant<Tiled<32, 128, 1, 2>>(a, stream);
+    case 64: return by_variant<Tiled<64, 256, 1, 1>>(a, stream);
     default: return by_variant<Tiled<128, 128, 2, 1>>(a, stream);
   }
 }
