@@ -395,3 +395,38 @@ def test_grouped_gemm_large_capacity_grid(bm, layout):
                                                weight_layout=layout))
     torch.cuda.synchronize()
     np.testing.assert_array_equal(outs[1].view(torch.int16).cpu().numpy(), outs[0].view(torch.int16).cpu().numpy())
+
+
+def test_ffn_forward_graph_replays_match_eager():
+    # The whole layer captured in a HIP graph (no memset or host sync is recorded) and replayed
+    # several times, with eager work and synchronisation in between: every replay must reproduce
+    # the eager output bits.
+    inp, d = workload_inputs("pre800")
+    wl = inp.wl
+    q13, s13, q2, s2 = _packed(d)
+    ws = torch.empty(moe.moe_ffn_workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.k), dtype=torch.uint8, device="cuda")
+    y_ref = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_ffn_forward(d.x, d.logits, q13, s13, q2, s2, wl.k, y=y_ref, workspace=ws,
+                        weight_layout=moe.MOE_LAYOUT_PACKED)
+    torch.cuda.synchronize()
+    ref = _bits(y_ref)
+    y = torch.full((wl.T, wl.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.moe_ffn_forward(d.x, d.logits, q13, s13, q2, s2, wl.k, y=y, workspace=ws,
+                            weight_layout=moe.MOE_LAYOUT_PACKED)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        moe.moe_ffn_forward(d.x, d.logits, q13, s13, q2, s2, wl.k, y=y, workspace=ws,
+                            weight_layout=moe.MOE_LAYOUT_PACKED)
+    for rep in range(3):
+        y.fill_(float("nan"))
+        ws.fill_(0xFF)  # eager work between replays: poison the workspace the replay must rewrite
+        torch.cuda.synchronize()
+        _log(f"graph replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(_bits(y), ref)
