@@ -81,6 +81,42 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}), flush=True)
 
 
+def calibrate():
+    """Measured ceilings of this machine beside the spec peaks: a timed device copy (read + write bytes
+    per second) and a large bf16 GEMM from the vendor library (sustained matrix-core rate)."""
+    out = {}
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    out["copy_gbps"] = round(2 * n * 10 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9, 1)
+    del src, dst
+    m = 8192
+    a = torch.randn((m, m), dtype=torch.bfloat16, device="cuda")
+    b = torch.randn((m, m), dtype=torch.bfloat16, device="cuda")
+    for _ in range(5):
+        c = a @ b
+    torch.cuda.synchronize()
+    reps = 50
+    ev0.record()
+    for _ in range(reps):
+        c = a @ b
+    ev1.record()
+    torch.cuda.synchronize()
+    out["bf16_gemm_tflops"] = round(2.0 * m ** 3 * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e12, 1)
+    out["gemm_shape"] = f"{m}x{m}x{m} bf16, {reps} back-to-back launches"
+    out["spec"] = {"hbm_gbps": HBM_PEAK_GBPS, "bf16_mfma_tflops": MFMA_BF16_PEAK_TFLOPS}
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(inp, target_s: float):
     """Time the CPU oracle (as it stands) on a bounded token sample; scale to one whole layer."""
     import oracle
@@ -118,9 +154,13 @@ def main():
                     help="weight layout the timed layer reads (packed = prepacked once, outside the timed region)")
     ap.add_argument("--copy-probe", action="store_true", help="run only the counter-calibration copy")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
+    ap.add_argument("--calibrate", action="store_true", help="measure copy bandwidth and a vendor bf16 GEMM rate only")
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe()
+        return
+    if args.calibrate:
+        calibrate()
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
