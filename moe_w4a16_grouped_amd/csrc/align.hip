@@ -29,12 +29,21 @@ __device__ __forceinline__ uint64_t lds_peers(uint64_t* tbl, int id, bool valid)
   return valid ? tbl[id] : 0ull;
 }
 
-__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
+// Inclusive prefix sum over the 64 lanes with DPP: shifts by 1, 2, 4, 8 within each row of 16,
+// then the last lane of row 0 is added to row 1 (and of row 2 to row 3), then lane 31 to rows 2, 3.
+// Lanes without a DPP source add 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_add(int v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v = dpp_add<0x111, 0xF>(v);  // row_shr:1
+  v = dpp_add<0x112, 0xF>(v);  // row_shr:2
+  v = dpp_add<0x114, 0xF>(v);  // row_shr:4
+  v = dpp_add<0x118, 0xF>(v);  // row_shr:8
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 
@@ -42,12 +51,12 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 // scratch: 32 ints of LDS.
 __device__ void block_exclusive_scan2(int a, int b, int& ea, int& eb, int& ta, int& tb, int* scratch) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ia = wave_inclusive_scan(a, lane), ib = wave_inclusive_scan(b, lane);
+  const int ia = wave_inclusive_scan(a), ib = wave_inclusive_scan(b);
   if (lane == 63) { scratch[wave] = ia; scratch[16 + wave] = ib; }
   __syncthreads();
   if (wave == 0) {
     const int va = lane < 16 ? scratch[lane] : 0, vb = lane < 16 ? scratch[16 + lane] : 0;
-    const int sa = wave_inclusive_scan(va, lane), sb = wave_inclusive_scan(vb, lane);
+    const int sa = wave_inclusive_scan(va), sb = wave_inclusive_scan(vb);
     if (lane < 16) { scratch[lane] = sa - va; scratch[16 + lane] = sb - vb; }
     if (lane == 15) { scratch[32] = sa; scratch[33] = sb; }
   }
@@ -58,8 +67,9 @@ __device__ void block_exclusive_scan2(int a, int b, int& ea, int& eb, int& ta, i
   tb = scratch[33];
 }
 
-// Per-expert epilogue shared by both paths: thread e owns expert e.  seg_cnt holds per-segment
-// counts for expert e at seg_cnt[s * E + e]; they are replaced by absolute base rows.
+// Multi-workgroup epilogue: thread e owns expert e.  seg_cnt holds per-segment counts for expert e
+// at seg_cnt[s * E + e]; they are replaced by the expert-local exclusive prefix (the permuted row of
+// a segment's first slot of expert e is offsets[e] + seg_cnt[s * E + e]).
 __device__ void finish_expert(int e, int E, int nseg, int bm, int32_t* seg_cnt, int32_t* counts,
                               int32_t* offsets, int32_t* tiles, int max_tiles, int32_t* num_tiles,
                               int* scratch) {
@@ -84,7 +94,42 @@ __device__ void finish_expert(int e, int E, int nseg, int bm, int32_t* seg_cnt, 
   if (e < E) {
     counts[e] = c;
     offsets[e] = off;
-    for (int s = 0; s < nseg; ++s) seg_cnt[s * E + e] += off;
+    for (int i = 0; i < nt && toff + i < max_tiles; ++i) {
+      int32_t* t = tiles + 3 * (size_t)(toff + i);
+      t[0] = e;
+      t[1] = off + i * bm;
+      t[2] = min(bm, c - i * bm);
+    }
+  }
+  if (threadIdx.x == 0) {
+    offsets[E] = total_c;
+    num_tiles[0] = total_t;
+  }
+}
+
+// Single-workgroup epilogue: thread e owns expert e; cnt[w * E + e] (16 waves) holds the counts of
+// wave w and is replaced by the absolute permuted row of wave w's first slot of expert e.
+__device__ void finish_expert_single(int e, int E, int bm, int32_t* cnt, int32_t* counts, int32_t* offsets,
+                                     int32_t* tiles, int max_tiles, int32_t* num_tiles, int* scratch) {
+  int v[16];
+  int c = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    v[w] = e < E ? cnt[w * E + e] : 0;
+    c += v[w];
+  }
+  const int nt = (c + bm - 1) / bm;
+  int off, toff, total_c, total_t;
+  block_exclusive_scan2(c, nt, off, toff, total_c, total_t, scratch);
+  if (e < E) {
+    int run = off;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      cnt[w * E + e] = run;
+      run += v[w];
+    }
+    counts[e] = c;
+    offsets[e] = off;
     for (int i = 0; i < nt && toff + i < max_tiles; ++i) {
       int32_t* t = tiles + 3 * (size_t)(toff + i);
       t[0] = e;
@@ -120,10 +165,12 @@ __device__ __forceinline__ void wave_count(const int (&id)[kSegRegs], int f0, in
   }
 }
 
-// Scatter segment [f0, f1) of one wave; base[id] is the next free permuted row of expert id, tbl this
-// wave's peer table.  sorted_ids may point to LDS (staging) or global memory.
-__device__ __forceinline__ void wave_scatter(const int (&id)[kSegRegs], int f0, int f1, int32_t* base, uint64_t* tbl,
-                                             int32_t* sorted_ids, int32_t* inv_perm) {
+// Scatter segment [f0, f1) of one wave; off[id] + base[id] (base[id] alone when off is NULL) is the
+// next free permuted row of expert id (base is advanced here), tbl this wave's peer table.
+// sorted_ids may point to LDS (staging) or global memory.
+__device__ __forceinline__ void wave_scatter(const int (&id)[kSegRegs], int f0, int f1, int32_t* base,
+                                             const int32_t* off, uint64_t* tbl, int32_t* sorted_ids,
+                                             int32_t* inv_perm) {
   const int lane = threadIdx.x & 63;
   const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
@@ -132,10 +179,11 @@ __device__ __forceinline__ void wave_scatter(const int (&id)[kSegRegs], int f0, 
     const int f = f0 + 64 * j + lane;
     const bool v = id[j] >= 0;
     const int e = v ? id[j] : 0;
-    const uint64_t peers = lds_peers(tbl, e, v);
     const int b = v ? base[e] : 0;
+    const int o = (v && off) ? off[e] : 0;
+    const uint64_t peers = lds_peers(tbl, e, v);
     if (v) {
-      const int r = b + __popcll(peers & below);
+      const int r = o + b + __popcll(peers & below);
       sorted_ids[r] = f;
       inv_perm[f] = r;
     }
@@ -163,9 +211,9 @@ __global__ __launch_bounds__(1024) void align_single_kernel(const int32_t* __res
   __syncthreads();
   wave_count(id, f0, f1, cnt + wave * E);
   __syncthreads();
-  finish_expert(tid, E, 16, bm, cnt, counts, offsets, tiles, max_tiles, num_tiles, scratch);
+  finish_expert_single(tid, E, bm, cnt, counts, offsets, tiles, max_tiles, num_tiles, scratch);
   __syncthreads();
-  wave_scatter(id, f0, f1, cnt + wave * E, tbl + wave * E, sorted_lds, inv_perm);
+  wave_scatter(id, f0, f1, cnt + wave * E, nullptr, tbl + wave * E, sorted_lds, inv_perm);
   __syncthreads();
   for (int r = tid; r < R; r += 1024) sorted_ids[r] = sorted_lds[r];
 }
@@ -186,7 +234,7 @@ __global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restri
   for (int i = tid; i < 4 * E; i += 256) seg_cnt[(size_t)blockIdx.x * 4 * E + i] = cnt[i];
 }
 
-// Step 2: one 1024-thread workgroup turns segment counts into base rows, writes counts, offsets,
+// Step 2: one 1024-thread workgroup turns segment counts into per-expert prefixes, writes counts, offsets,
 // tiles and the tile count.
 __global__ __launch_bounds__(1024) void align_scan_kernel(int32_t* seg_cnt, int nseg, int E, int bm,
                                                           int32_t* counts, int32_t* offsets,
@@ -198,19 +246,21 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(int32_t* seg_cnt, int 
 
 // Step 3: each wave re-walks its segment and scatters from its base rows.
 __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __restrict__ ids, int R, int E,
-                                                            const int32_t* seg_base, int32_t* sorted_ids,
-                                                            int32_t* inv_perm) {
-  extern __shared__ uint64_t dyn[];  // [4][E] peer tables, then [4][E] base rows
+                                                            const int32_t* seg_base, const int32_t* offsets,
+                                                            int32_t* sorted_ids, int32_t* inv_perm) {
+  extern __shared__ uint64_t dyn[];  // [4][E] peer tables, then [4][E] base rows, then [E] offsets
   uint64_t* tbl = dyn;
   int32_t* base = reinterpret_cast<int32_t*>(dyn + 4 * E);
+  int32_t* off = base + 4 * E;
   const int tid = threadIdx.x, wave = tid >> 6;
   for (int i = tid; i < 4 * E; i += 256) base[i] = seg_base[(size_t)blockIdx.x * 4 * E + i];
+  for (int i = tid; i < E; i += 256) off[i] = offsets[i];
   __syncthreads();
   const int f0 = min(R, blockIdx.x * kAlignChunk + wave * (kAlignChunk / 4));
   const int f1 = min(R, f0 + kAlignChunk / 4);
   int id[kSegRegs];
   load_segment(ids, f0, f1, id);
-  wave_scatter(id, f0, f1, base + wave * E, tbl + wave * E, sorted_ids, inv_perm);
+  wave_scatter(id, f0, f1, base + wave * E, off, tbl + wave * E, sorted_ids, inv_perm);
 }
 
 size_t align_workspace_bytes(int R, int E) {
@@ -232,8 +282,8 @@ hipError_t launch_align(const int32_t* ids, int R, int E, int block_m, int32_t* 
   align_hist_kernel<<<nblk, 256, 4 * (size_t)E * sizeof(int32_t), stream>>>(ids, R, E, seg);
   align_scan_kernel<<<1, 1024, 0, stream>>>(seg, nblk * 4, E, block_m, counts, offsets, tiles, max_tiles,
                                             num_tiles);
-  align_scatter_kernel<<<nblk, 256, 4 * (size_t)E * (sizeof(uint64_t) + sizeof(int32_t)), stream>>>(
-      ids, R, E, seg, sorted_ids, inv_perm);
+  align_scatter_kernel<<<nblk, 256, 4 * (size_t)E * (sizeof(uint64_t) + sizeof(int32_t)) + E * sizeof(int32_t),
+                         stream>>>(ids, R, E, seg, offsets, sorted_ids, inv_perm);
   return hipGetLastError();
 }
 
