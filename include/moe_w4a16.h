@@ -168,7 +168,10 @@ moe_status_t moe_w4_prepack(const uint8_t* w_q, const uint16_t* w_s, int32_t E, 
  *              SILU_MUL N % 32 == 0 --, K % 128 == 0 and Ws 8-byte aligned).
  *   tiles, num_tiles  as written by moe_align with the same block_m; max_tiles is the capacity
  *              passed to moe_align (it sizes the launch; tiles past *num_tiles cost nothing).
- *   block_m    one of 16, 32, 64, 128.
+ *   block_m    one of 16, 32, 64, 128.  With block_m 16 and max_tiles <= 32 the four waves of a
+ *              workgroup split K (fp32 partial sums added in wave order), so bits can differ from a
+ *              call with a larger capacity; both stay within the same error bound, and identical
+ *              arguments always give identical bits.
  *   out_dtype  MOE_OUT_BF16 (round to nearest even) or MOE_OUT_F32; SILU_MUL requires BF16.
  * Shapes: 1 <= E <= MOE_MAX_EXPERTS, N >= 1 (N even for SILU_MUL), K % 32 == 0, K >= 32.
  * Alignment: A, Wq, C 16 bytes; Ws 2 bytes.

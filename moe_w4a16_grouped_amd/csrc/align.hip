@@ -16,6 +16,7 @@
 // order.
 #include "launch.h"
 #include "moe_common.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -192,18 +193,14 @@ __device__ __forceinline__ void wave_scatter(const int (&id)[kSegRegs], int f0, 
   }
 }
 
-// Whole permutation in one 1024-thread workgroup (align_single_fits(R, E)).  sorted_ids is built in
-// LDS (the scatter is random) and written out with coalesced stores.
-__global__ __launch_bounds__(1024) void align_single_kernel(const int32_t* __restrict__ ids, int R, int E,
-                                                            int bm, int32_t* counts, int32_t* offsets,
-                                                            int32_t* sorted_ids, int32_t* inv_perm,
-                                                            int32_t* tiles, int max_tiles, int32_t* num_tiles) {
-  __shared__ int32_t cnt[16 * kAlignSingleMaxE];
-  __shared__ int scratch[64];
-  __shared__ int32_t sorted_lds[kAlignSingleMaxR];
-  __shared__ uint64_t tbl[16 * kAlignSingleMaxE];
+// Whole permutation of the R slots ids[0..R) (global or LDS) by one 1024-thread workgroup.  cnt
+// (16 * E ints, zeroed by the caller before a barrier), tbl (16 * E) and sorted_lds (R) are LDS.
+// sorted_ids is staged in LDS (the scatter is random) and written out with coalesced stores.
+__device__ __forceinline__ void align_block(const int32_t* ids, int R, int E, int bm, int32_t* counts,
+                                            int32_t* offsets, int32_t* sorted_ids, int32_t* inv_perm,
+                                            int32_t* tiles, int max_tiles, int32_t* num_tiles, int32_t* cnt,
+                                            int* scratch, int32_t* sorted_lds, uint64_t* tbl) {
   const int tid = threadIdx.x, wave = tid >> 6;
-  for (int i = tid; i < 16 * E; i += 1024) cnt[i] = 0;
   const int seg = (((R + 15) / 16) + 63) & ~63;
   const int f0 = min(R, wave * seg), f1 = min(R, f0 + seg);
   int id[kSegRegs];
@@ -216,6 +213,47 @@ __global__ __launch_bounds__(1024) void align_single_kernel(const int32_t* __res
   wave_scatter(id, f0, f1, cnt + wave * E, nullptr, tbl + wave * E, sorted_lds, inv_perm);
   __syncthreads();
   for (int r = tid; r < R; r += 1024) sorted_ids[r] = sorted_lds[r];
+}
+
+// Whole permutation in one 1024-thread workgroup (align_single_fits(R, E)).
+__global__ __launch_bounds__(1024) void align_single_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                            int bm, int32_t* counts, int32_t* offsets,
+                                                            int32_t* sorted_ids, int32_t* inv_perm,
+                                                            int32_t* tiles, int max_tiles, int32_t* num_tiles) {
+  __shared__ int32_t cnt[16 * kAlignSingleMaxE];
+  __shared__ int scratch[64];
+  __shared__ int32_t sorted_lds[kAlignSingleMaxR];
+  __shared__ uint64_t tbl[16 * kAlignSingleMaxE];
+  for (int i = threadIdx.x; i < 16 * E; i += 1024) cnt[i] = 0;
+  align_block(ids, R, E, bm, counts, offsets, sorted_ids, inv_perm, tiles, max_tiles, num_tiles, cnt, scratch,
+              sorted_lds, tbl);
+}
+
+// Routing and permutation of a small batch in one launch (route_align_fused_fits): wave t routes
+// token t (writing topk ids and weights, and the ids into LDS), then the workgroup builds the
+// permutation from the LDS copy exactly as align_single_kernel does.
+template <int NJ>
+__global__ __launch_bounds__(1024) void route_align_small_kernel(const float* __restrict__ logits, int T, int E,
+                                                                 int k, int bm, int32_t* topk_ids, float* topk_w,
+                                                                 int32_t* counts, int32_t* offsets,
+                                                                 int32_t* sorted_ids, int32_t* inv_perm,
+                                                                 int32_t* tiles, int max_tiles, int32_t* num_tiles) {
+  __shared__ uint64_t rscratch[16 * 2 * kFusedMaxK];
+  __shared__ int32_t ids_lds[kFusedMaxR];
+  __shared__ int32_t cnt[16 * kAlignSingleMaxE];
+  __shared__ int scratch[64];
+  __shared__ int32_t sorted_lds[kFusedMaxR];
+  __shared__ uint64_t tbl[16 * kAlignSingleMaxE];
+  const int wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 16 * E; i += 1024) cnt[i] = 0;
+  if (wave < T) {
+    uint64_t* kept = rscratch + wave * 2 * k;
+    route_token<NJ>(logits + (size_t)wave * E, E, k, kept, kept + k, topk_ids + (size_t)wave * k,
+                    topk_w + (size_t)wave * k, ids_lds + wave * k);
+  }
+  __syncthreads();
+  align_block(ids_lds, T * k, E, bm, counts, offsets, sorted_ids, inv_perm, tiles, max_tiles, num_tiles, cnt,
+              scratch, sorted_lds, tbl);
 }
 
 // Multi-workgroup path, step 1: per-(workgroup, wave) counts, kAlignChunk slots per workgroup.
@@ -267,6 +305,22 @@ size_t align_workspace_bytes(int R, int E) {
   if (align_single_fits(R, E)) return 0;
   const size_t nblk = (size_t)(R + kAlignChunk - 1) / kAlignChunk;
   return nblk * 4 * (size_t)E * sizeof(int32_t);
+}
+
+hipError_t launch_route_align_small(const float* logits, int T, int E, int k, int block_m, int32_t* topk_ids,
+                                   float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
+                                   int32_t* inv_perm, int32_t* tiles, int max_tiles, int32_t* num_tiles,
+                                   hipStream_t stream) {
+  const int nj = (E + 63) / 64;
+#define RA_LAUNCH(NJ_)                                                                                         \
+  route_align_small_kernel<NJ_><<<1, 1024, 0, stream>>>(logits, T, E, k, block_m, topk_ids, topk_w, counts, \
+                                                         offsets, sorted_ids, inv_perm, tiles, max_tiles, num_tiles)
+  if (nj <= 1) RA_LAUNCH(1);
+  else if (nj <= 2) RA_LAUNCH(2);
+  else if (nj <= 4) RA_LAUNCH(4);
+  else RA_LAUNCH(8);
+#undef RA_LAUNCH
+  return hipGetLastError();
 }
 
 hipError_t launch_align(const int32_t* ids, int R, int E, int block_m, int32_t* counts,

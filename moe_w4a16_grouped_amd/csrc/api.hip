@@ -264,11 +264,18 @@ moe_status_t moe_ffn_forward(const uint16_t* x, const float* router_logits, int3
   float* o = reinterpret_cast<float*>(ws + L.o);
   hipStream_t s = (hipStream_t)stream;
   const int R = T * k;
-  hipError_t e = moe::launch_route_topk(router_logits, T, E, k, ids, w, s);
-  if (e != hipSuccess) return hip_status(e, "route launch");
-  e = moe::launch_align(ids, R, E, L.block_m, counts, offsets, sorted, inv, tiles, L.max_tiles, ntiles,
-                        ws + L.align_ws, s);
-  if (e != hipSuccess) return hip_status(e, "align launch");
+  hipError_t e;
+  if (moe::route_align_fused_fits(T, E, k)) {
+    e = moe::launch_route_align_small(router_logits, T, E, k, L.block_m, ids, w, counts, offsets, sorted, inv,
+                                      tiles, L.max_tiles, ntiles, s);
+    if (e != hipSuccess) return hip_status(e, "route+align launch");
+  } else {
+    e = moe::launch_route_topk(router_logits, T, E, k, ids, w, s);
+    if (e != hipSuccess) return hip_status(e, "route launch");
+    e = moe::launch_align(ids, R, E, L.block_m, counts, offsets, sorted, inv, tiles, L.max_tiles, ntiles,
+                          ws + L.align_ws, s);
+    if (e != hipSuccess) return hip_status(e, "align launch");
+  }
   const int packed = weight_layout == MOE_LAYOUT_PACKED;
   moe::GemmArgs g1{x, sorted, k, w13_q, w13_s, 2 * I, H, tiles, ntiles, L.max_tiles, h, MOE_EPI_SILU_MUL, 0, packed};
   e = moe::launch_grouped_gemm(g1, L.block_m, s);

@@ -304,6 +304,143 @@ __global__ __launch_bounds__(256) void gemm_w4a16_tiled(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------------------------------
+// Split-K kernel for a handful of small tiles (single-token decode), where too few workgroups exist
+// to keep the weight stream busy with the tiled kernel.  The four waves split K into contiguous
+// ranges; each wave
+// loads its own activation fragments (16-byte loads, rows gathered through a_row_of; padding rows
+// repeat the tile's first row, which the load coalescer merges) and its weights straight into a
+// PF-deep register ring, so the main loop has no LDS traffic and no barrier.  The four partial sums
+// are reduced through LDS once per tile, in wave order.
+template <int BM, int BN, int PF, int EPI, bool OUT_F32, int LAYOUT>
+__global__ __launch_bounds__(256) void gemm_w4a16_sk(GemmArgs p) {
+  constexpr int MI = BM / 16, NI = BN / 16;
+  static_assert(MI >= 1 && MI <= 2 && NI >= 1, "tile shape");
+  static_assert(EPI != MOE_EPI_SILU_MUL || NI % 2 == 0, "SiLU*mul pairs gate and up blocks");
+  constexpr int NS = PF + 1;
+
+  __shared__ __attribute__((aligned(16))) float red[3 * 64 * MI * NI * 4];
+
+  const int nbn = EPI == MOE_EPI_SILU_MUL ? (p.N / 2 + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
+  int tile, nb;
+  if (!xcd_tile(linear_block(), nbn, *p.num_tiles, tile, nb)) return;
+  const int e = p.tiles[3 * tile], row0 = p.tiles[3 * tile + 1], rows = p.tiles[3 * tile + 2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, q = lane >> 4;
+  const int K = p.K;
+  const int kgroups = K / kGroup;
+  const int nks = (K + kBK - 1) / kBK;
+  const int per = (nks + 3) / 4;  // steps per wave (contiguous K ranges)
+  const int s_begin = min(nks, wk * per), s_end = min(nks, s_begin + per);
+  const bool m1 = MI > 1 && rows > 16;  // second 16-row block present (wave-uniform)
+
+  const uint16_t* arow[MI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int i = mi * 16 + l16;
+    const int r = row0 + (i < rows ? i : 0);
+    arow[mi] = p.A + (size_t)(p.a_row_of ? p.a_row_of[r] / p.a_row_div : r) * K + q * 8;
+  }
+  WRow wr[NI];
+  int ncol[NI];
+  bool nvalid[NI];
+  const int col0 = nb * (EPI == MOE_EPI_SILU_MUL ? BN / 2 : BN);
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    int n;
+    column_of<EPI, NI>(p, col0, ni, l16, n, ncol[ni], nvalid[ni]);
+    wr[ni] = wrow_of<LAYOUT>(p, e, n, q, lane);
+  }
+
+  f32x4 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 areg[NS][MI][4];
+  u32x4 breg[NS][NI];
+  uint32_t sreg[NS][NI][4];
+
+  auto load_step = [&](int s, int u) {
+    s = min(s, s_end - 1);  // prefetches past this wave's range re-read its last step (unused)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        areg[u][mi][g] = *reinterpret_cast<const u32x4*>(arow[mi] + min(s * kBK + g * 32, K - 32));
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) load_w<LAYOUT>(wr[ni], s, q, kgroups, breg[u][ni], sreg[u][ni]);
+  };
+
+  auto compute_step = [&](int s, int u) {
+    u32x4 bt[NI];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) bt[ni] = b_operands<LAYOUT>(breg[u][ni]);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (LAYOUT == kCanonGeneric && s * 4 + g >= kgroups) break;  // K tail (wave-uniform)
+      bf16x8 bf[NI];
+      float sc[NI];
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        bf[ni] = e2m1x8_to_bf16(bt[ni][g]);
+        sc[ni] = scale_of<LAYOUT>(sreg[u][ni], g);
+      }
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        if (mi == 1 && !m1) break;
+        const bf16x8 af = __builtin_bit_cast(bf16x8, areg[u][mi][g]);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const f32x4 part = mfma16x16x32(af, bf[ni], f32x4{0.f, 0.f, 0.f, 0.f});
+          acc[mi][ni] += sc[ni] * part;
+        }
+      }
+    }
+  };
+
+  if (s_end > s_begin) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) load_step(s_begin + u, u);
+    int s0 = s_begin;
+    for (; s0 + NS <= s_end; s0 += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(s0 + u + PF, (u + PF) % NS);
+        compute_step(s0 + u, u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u)
+      if (s0 + u < s_end) compute_step(s0 + u, u);
+  }
+
+  // K-slice reduction in wave order: waves 1..3 park their sums, wave 0 adds them.
+  constexpr int PER = MI * NI * 4;
+  if (wk > 0) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[((wk - 1) * 64 + lane) * PER + (mi * NI + ni) * 4 + r] = acc[mi][ni][r];
+  }
+  __syncthreads();
+  if (wk > 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mi][ni][r] += red[(w * 64 + lane) * PER + (mi * NI + ni) * 4 + r];
+  store_tile<EPI, OUT_F32, MI, NI>(p, acc, 0, row0, rows, q, ncol, nvalid);
+}
+
+// ---------------------------------------------------------------------------------------------------
 // Large-tile kernel for MFMA-bound shapes (hundreds of rows per expert), packed weights only.
 // 128 x 256 output tile per 512-thread workgroup: 8 waves (2 along M x 4 along N), 64 x 64 each, so
 // two waves share every SIMD and one's scale FMAs can overlap the other's MFMAs.  Activations (gathered
@@ -535,6 +672,19 @@ struct Tiled {
   }
 };
 
+template <int BM, int BN, int PF>
+struct SplitK {
+  template <int EPI, bool F32, int LAYOUT>
+  static hipError_t run(const GemmArgs& a, hipStream_t s) {
+    gemm_w4a16_sk<BM, BN, PF, EPI, F32, LAYOUT><<<grid_of(a, BN), 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
+};
+
+// Tile lists of at most this capacity (16-row tiles) use the split-K kernel: measured on MI355X at
+// one token with 128 experts top-8, 8 tiles, its K-split waves stream the weights ~1.5x faster.
+constexpr int kSplitKMaxTiles = 32;
+
 template <class Cfg, int EPI, bool F32>
 static hipError_t by_layout(const GemmArgs& a, hipStream_t s) {
   switch (layout_of(a)) {
@@ -569,7 +719,9 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t strea
     return launch_mm<MOE_EPI_NONE, false>(a, stream);
   }
   switch (block_m) {
-    case 16: return by_variant<Tiled<16, 128, 1, 2>>(a, stream);
+    case 16:
+      if (a.max_tiles <= kSplitKMaxTiles) return by_variant<SplitK<16, 64, 2>>(a, stream);
+      return by_variant<Tiled<16, 128, 1, 2>>(a, stream);
     case 32: return by_variant<Tiled<32, 128, 1, 2>>(a, stream);
     case 64: return by_variant<Tiled<64, 256, 1, 1>>(a, stream);
     default: return by_variant<Tiled<128, 128, 2, 1>>(a, stream);

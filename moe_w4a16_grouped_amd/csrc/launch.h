@@ -16,6 +16,18 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
 constexpr int kAlignSingleMaxR = 8192;
 constexpr int kAlignSingleMaxE = 512;
 inline bool align_single_fits(int R, int E) { return R <= kAlignSingleMaxR && E <= kAlignSingleMaxE; }
+// Routing and permutation of a small batch in one single-workgroup launch: up to 16 tokens (one
+// wave each), k <= kFusedMaxK, T * k <= kFusedMaxR, E <= kAlignSingleMaxE.
+constexpr int kFusedMaxT = 16;
+constexpr int kFusedMaxK = 64;
+constexpr int kFusedMaxR = 1024;
+inline bool route_align_fused_fits(int T, int E, int k) {
+  return T >= 1 && T <= kFusedMaxT && k <= kFusedMaxK && T * k <= kFusedMaxR && E <= kAlignSingleMaxE;
+}
+hipError_t launch_route_align_small(const float* logits, int T, int E, int k, int block_m, int32_t* topk_ids,
+                                   float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
+                                   int32_t* inv_perm, int32_t* tiles, int max_tiles, int32_t* num_tiles,
+                                   hipStream_t stream);
 // Flat slots per workgroup in the multi-workgroup permutation.
 constexpr int kAlignChunk = 4096;
 size_t align_workspace_bytes(int R, int E);

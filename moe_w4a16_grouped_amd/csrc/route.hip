@@ -2,94 +2,22 @@
 // Follows the ATOM page ("AMD ATOM推理引擎：如何用分页KV缓存和分段编译实现大模型推理性能翻倍"),
 // section "8.1 MoE 路径：路由、专家并行与 MORI 通信" (routing and top-k selection).
 //
-// One wave64 per token; lane l holds the logits of experts l, l + 64, ... as order-preserving
-// 32-bit keys.  Selection by radix select: 32 ballot-count rounds find the k-th largest key value
-// T (the largest value with at least k keys >= it); every key above T is kept, and among keys
-// equal to T the lowest expert ids fill the remaining places, which is the (logit desc, id asc)
-// order.  The k kept (key, id) pairs are compacted in LDS, ranked there by that order (slot 0 =
-// largest), and the weights exp(l_s - l_0) / sum_j exp(l_j - l_0) are formed in slot order: the
-// softmax restricted to the kept experts, which equals softmax-then-renormalise.
+// One wave64 per token (the selection itself is in topk.h).
 #include "launch.h"
-#include "moe_common.h"
+#include "topk.h"
 
 namespace moe {
-
-__device__ __forceinline__ uint32_t ordered_bits(float v) {
-  uint32_t u = __float_as_uint(v);
-  if (u == 0x80000000u) u = 0u;  // -0.0 compares equal to +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float from_ordered_bits(uint32_t o) {
-  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
-  return __uint_as_float(u);
-}
 
 template <int NJ>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T, int E,
                                                          int k, int32_t* __restrict__ ids,
                                                          float* __restrict__ w) {
   extern __shared__ uint64_t route_lds[];  // per wave: k compacted pairs, then k ranked pairs
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wv;
   if (t >= T) return;
   uint64_t* kept = route_lds + (size_t)wv * 2 * k;
-  uint64_t* ranked = kept + k;
-  const float* l = logits + (size_t)t * E;
-  uint32_t u[NJ];
-  bool valid[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int e = lane + 64 * j;
-    valid[j] = e < E;
-    u[j] = valid[j] ? ordered_bits(l[e]) : 0u;
-  }
-  // k-th largest key value: the largest p with #{keys >= p} >= k (k <= E, so p = 0 qualifies).
-  // Every candidate is >= 1 and absent experts hold key 0, so they are never counted.
-  uint32_t p = 0;
-#pragma unroll 4
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t c = p | (1u << bit);
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot(u[j] >= c));
-    if (cnt >= k) p = c;
-  }
-  // keep every key above p and, in ascending id order, as many keys equal to p as places remain
-  int need = k;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) need -= __popcll(__ballot(valid[j] && u[j] > p));
-  const uint64_t below = (1ull << lane) - 1ull;
-  int eq_before = 0, kept_before = 0;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const bool eq = valid[j] && u[j] == p;
-    const uint64_t eq_mask = __ballot(eq);
-    const bool keep = valid[j] && (u[j] > p || (eq && eq_before + __popcll(eq_mask & below) < need));
-    eq_before += __popcll(eq_mask);
-    const uint64_t keep_mask = __ballot(keep);
-    if (keep) kept[kept_before + __popcll(keep_mask & below)] = ((uint64_t)u[j] << 32) | (uint32_t)(~(uint32_t)(lane + 64 * j));
-    kept_before += __popcll(keep_mask);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  // rank of each kept pair among the kept pairs (keys are distinct: the low word is ~id)
-  for (int c = lane; c < k; c += 64) {
-    const uint64_t key = kept[c];
-    int rank = 0;
-    for (int c2 = 0; c2 < k; ++c2) rank += kept[c2] > key;
-    ranked[rank] = key;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  const float top = from_ordered_bits((uint32_t)(ranked[0] >> 32));
-  float sum = 0.f;
-  for (int s2 = 0; s2 < k; ++s2) sum += expf(from_ordered_bits((uint32_t)(ranked[s2] >> 32)) - top);
-  for (int s2 = lane; s2 < k; s2 += 64) {
-    const uint64_t key = ranked[s2];
-    ids[(size_t)t * k + s2] = (int)(~(uint32_t)key);
-    w[(size_t)t * k + s2] = expf(from_ordered_bits((uint32_t)(key >> 32)) - top) / sum;
-  }
+  route_token<NJ>(logits + (size_t)t * E, E, k, kept, kept + k, ids + (size_t)t * k, w + (size_t)t * k, nullptr);
 }
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,

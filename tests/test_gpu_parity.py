@@ -139,6 +139,37 @@ def test_grouped_gemm_gate_up_silu_mul(bm, I, H):
     assert gu.tolerance_report(got, ref)["mean_rel"] <= gu.MEAN_REL
 
 
+@pytest.mark.parametrize("I,H", [(128, 256), (96, 160), (256, 384)])
+def test_grouped_gemm_split_k_gate_up(I, H):
+    # 40 tokens top-2 over 8 experts with 16-row tiles: a tile list short enough for the split-K
+    # kernel (four waves each own a quarter of K; partial sums reduced in wave order).
+    wl = mi.custom("sk", 40, 8, 2, H, I, skew=True, seed=17)
+    inp, d = workload_inputs(wl)
+    rid, _ = oracle.route(inp.logits, wl.k)
+    a = moe.moe_align(gu.dev(rid), wl.E, 16)
+    assert a["max_tiles"] <= 32
+    R = wl.T * wl.k
+    C = moe.moe_grouped_gemm_w4a16(d.x, a["sorted_ids"], wl.k, d.w13_q, d.w13_s, a["tiles"], a["max_tiles"],
+                                   a["num_tiles"], 16, moe.MOE_EPI_SILU_MUL, R)
+    torch.cuda.synchronize()
+    ra = oracle.align(rid, wl.E, 16)
+    ref = oracle.grouped_proj(inp.x, ra["sorted_ids"], wl.k, inp.w13_q, inp.w13_s, ra["offsets"], silu_mul=True)
+    G = oracle.grouped_proj(inp.x, ra["sorted_ids"], wl.k, inp.w13_q, inp.w13_s, ra["offsets"])
+    Gabs = oracle.grouped_proj(inp.x & 0x7FFF, ra["sorted_ids"], wl.k, inp.w13_q & 0x77, inp.w13_s, ra["offsets"])
+    dG = (64 + H / 32) * 2.0 ** -24 * Gabs
+    g, u, dg, du = G[:, :I], G[:, I:], dG[:, :I], dG[:, I:]
+    bound = 2.0 ** -8 * np.abs(ref) + 1.1 * np.abs(u) * dg + np.abs(g) * du + 1e-6 * np.abs(ref)
+    got = gu.host_bf16_to_f64(C)
+    assert np.all(np.abs(got - ref) <= bound), f"split-K gate_up: worst excess {np.max(np.abs(got - ref) - bound)}"
+    if H % 128 == 0:
+        pq, ps = moe.moe_w4_prepack(d.w13_q, d.w13_s)
+        Cp = moe.moe_grouped_gemm_w4a16(d.x, a["sorted_ids"], wl.k, pq, ps, a["tiles"], a["max_tiles"],
+                                        a["num_tiles"], 16, moe.MOE_EPI_SILU_MUL, R,
+                                        weight_layout=moe.MOE_LAYOUT_PACKED)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(Cp.view(torch.int16).cpu().numpy(), C.view(torch.int16).cpu().numpy())
+
+
 @pytest.mark.parametrize("bm", [16, 64, 128])
 @pytest.mark.parametrize("out_dtype", [moe.MOE_OUT_F32, moe.MOE_OUT_BF16])
 @pytest.mark.parametrize("N,K", [(256, 128), (200, 160), (48, 1056)])
@@ -380,8 +411,9 @@ def test_large_tile_gemm_matches_canonical_bits(T, E, k, H, I, seed):
 @pytest.mark.parametrize("bm,layout", [(16, 0), (64, 1), (128, 1)])
 def test_grouped_gemm_large_capacity_grid(bm, layout):
     # A tile-list capacity far above the tiles used makes the work list longer than one grid row
-    # (2-D launch); unused slots must cost nothing and change no output bit.
-    wl = mi.custom("cap", 64, 8, 2, 256, 128, seed=41)
+    # (2-D launch); unused slots must cost nothing and change no output bit.  (300 tokens: the
+    # normal capacity is above the split-K limit too, so both calls use the same kernel.)
+    wl = mi.custom("cap", 300, 8, 2, 256, 128, seed=41)
     inp, d = workload_inputs(wl)
     rid, _ = oracle.route(inp.logits, wl.k)
     R = wl.T * wl.k
