@@ -263,6 +263,11 @@ def test_ffn_forward_matches_oracle(name, nsample):
     mi.custom("k_eq_E", 20, 6, 6, 128, 64, seed=7),
     mi.custom("many_experts", 40, 1024, 8, 128, 64, seed=8),
     mi.custom("t1_big_k", 1, 64, 32, 256, 256, seed=9),
+    # the fused small-batch routing + permutation at its limits (16 tokens, k = 64: 1024 slots;
+    # 512 experts) and just past them (17 tokens: separate launches)
+    mi.custom("fused_max", 16, 128, 64, 128, 64, seed=10),
+    mi.custom("fused_e512", 16, 512, 8, 128, 64, seed=15),
+    mi.custom("fused_past", 17, 128, 8, 128, 64, seed=16),
 ])
 def test_ffn_forward_edges(wl):
     inp, d = workload_inputs(wl)
