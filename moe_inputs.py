@@ -17,6 +17,13 @@ Draw order with ``numpy.random.default_rng(seed)``:
   5. w2_q    = integers(0, 256, (E, H, I/2), uint8)
   6. w2_s    = uniform(0.005, 0.02, (E, H, I/32)) -> float32 -> bf16 (RNE)
 bf16 values are carried as uint16 bit patterns.
+
+The router gate and the shared expert (``make_block_inputs``) come from a second generator,
+``default_rng(seed + 1000)``, so the draws above are unchanged; in order:
+  1. w_router = standard_normal((E, H), float32) / sqrt(H), rounded to bf16 (x @ w_router^T is then
+     about N(0, 1), the router-logit distribution of the workloads)
+  2. w13s_q, 3. w13s_s, 4. w2s_q, 5. w2s_s: one expert of intermediate size Is in the same W4 format
+     and distributions as the routed experts.
 """
 from __future__ import annotations
 
@@ -107,3 +114,27 @@ def custom(name: str, T: int, E: int, k: int, H: int, I: int, skew: bool = False
 def weight_bytes_per_expert(H: int, I: int) -> int:
     """Packed 4-bit codes plus bf16 group scales of one expert's gate_up and down weights."""
     return 2 * I * H // 2 + 2 * I * (H // GROUP) * 2 + H * I // 2 + H * (I // GROUP) * 2
+
+
+@dataclasses.dataclass(frozen=True)
+class BlockInputs:
+    """Router gate weight and shared expert for the whole MoE block (routed experts in MoEInputs)."""
+    w_router: np.ndarray  # uint16 [E, H] bf16 bits
+    w13s_q: np.ndarray    # uint8  [2Is, H/2]
+    w13s_s: np.ndarray    # uint16 [2Is, H/32] bf16 bits
+    w2s_q: np.ndarray     # uint8  [H, Is/2]
+    w2s_s: np.ndarray     # uint16 [H, Is/32] bf16 bits
+
+
+def make_block_inputs(wl: Workload, Is: int, seed: int | None = None) -> BlockInputs:
+    """Draw the router gate weight and a shared expert of intermediate size Is (documented order)."""
+    E, H = wl.E, wl.H
+    if Is % GROUP:
+        raise ValueError("Is must be a multiple of 32")
+    rng = np.random.default_rng((wl.seed if seed is None else seed) + 1000)
+    w_router = f32_to_bf16_bits((rng.standard_normal((E, H), dtype=np.float32) / np.float32(np.sqrt(H))))
+    w13s_q = rng.integers(0, 256, (2 * Is, H // 2), dtype=np.uint8)
+    w13s_s = f32_to_bf16_bits(rng.uniform(0.005, 0.02, (2 * Is, H // GROUP)).astype(np.float32))
+    w2s_q = rng.integers(0, 256, (H, Is // 2), dtype=np.uint8)
+    w2s_s = f32_to_bf16_bits(rng.uniform(0.005, 0.02, (H, Is // GROUP)).astype(np.float32))
+    return BlockInputs(w_router, w13s_q, w13s_s, w2s_q, w2s_s)

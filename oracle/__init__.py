@@ -57,6 +57,8 @@ def _load():
             lib.oracle_grouped_proj.argtypes = [P, P, I64, P, P, I64, I64, I64, P, ctypes.c_int, P, P]
             lib.oracle_grouped_proj.restype = None
             lib.oracle_combine.argtypes = [P, P, P, I64, I64, I64, P]
+            lib.oracle_router_logits.argtypes = [P, P, I64, I64, I64, P]
+            lib.oracle_shared_ffn.argtypes = [P, I64, I64, P, P, P, P, P, I64, P]
             lib.oracle_combine.restype = None
             _lib = lib
     return _lib
@@ -164,3 +166,28 @@ def combine(O, inv_perm, w, T: int, k: int):
     y = np.empty((T, H), np.float64)
     _load().oracle_combine(_ptr(O), _ptr(inv_perm), _ptr(w), T, k, H, _ptr(y))
     return y
+
+
+def router_logits(x, w_router):
+    """Gate logits x [T, H] @ w_router [E, H]^T from bf16 bits, fp64 [T, E]."""
+    x = _c(x, np.uint16)
+    wr = _c(w_router, np.uint16)
+    T, H = x.shape
+    E = wr.shape[0]
+    out = np.empty((T, E), np.float64)
+    _load().oracle_router_logits(_ptr(x), _ptr(wr), T, H, E, _ptr(out))
+    return out
+
+
+def shared_ffn(x, w13s_q, w13s_s, w2s_q, w2s_s, tokens=None):
+    """Shared expert (dense SwiGLU in the W4 format) on every token (or a subset); fp64 [n, H]."""
+    x = _c(x, np.uint16)
+    T, H = x.shape
+    Is = w2s_q.shape[1] * 2
+    tok = None if tokens is None else _c(tokens, np.int64)
+    n = T if tok is None else len(tok)
+    out = np.empty((n, H), np.float64)
+    a13q, a13s = _c(w13s_q, np.uint8), _c(w13s_s, np.uint16)
+    a2q, a2s = _c(w2s_q, np.uint8), _c(w2s_s, np.uint16)
+    _load().oracle_shared_ffn(_ptr(x), H, Is, _ptr(a13q), _ptr(a13s), _ptr(a2q), _ptr(a2s), _ptr(tok), n, _ptr(out))
+    return out

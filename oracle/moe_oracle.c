@@ -18,6 +18,8 @@
  *            per 32 weights along K).
  *   [RustDL] "Rust 实现深度学习推理引擎：从计算图到异构硬件加速"
  *            section "四、算子融合：性能翻倍的关键": SiLU as the activation fused after the matmul.
+ *   The Atlas section "KV Cache量化、MTP推测解码和调试工具链" also names, per MoE layer, the gate
+ *   input, the gate logits, the routed-only output and the shared expert output.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - E2M1 follows the OCP microscaling element definition: 1 sign, 2 exponent bits (bias 1),
@@ -30,6 +32,9 @@
  *     the fp32 logits themselves.
  *   - Permutation: a stable counting sort of the flat slot index f = t*k + s by expert id.
  *   - Combine: y[t] = sum over slots s (ascending) of w[t,s] * o[t,s].
+ *   - Gate logits: logits[t, e] = sum_h x[t, h] * w_router[e, h] with bf16 x and w_router.
+ *   - Shared expert: one more SwiGLU FFN with the same W4 format, applied to every token, whose
+ *     output is added to the routed output with weight 1.
  */
 #include <math.h>
 #include <stdint.h>
@@ -269,4 +274,39 @@ void oracle_combine(const double *O, const int32_t *inv_perm, const double *w, i
             for (int64_t s = 0; s < k; ++s) acc += w[t * k + s] * O[(int64_t)inv_perm[t * k + s] * H + c];
             y[t * H + c] = acc;
         }
+}
+
+/* ---- router gate and shared expert --------------------------------------------------------------- */
+
+/* Gate logits: logits[t, e] = sum_h x[t, h] * wr[e, h] (x [T, H] and wr [E, H] as bf16 bits, fp64
+ * sums in ascending h). */
+void oracle_router_logits(const uint16_t *x, const uint16_t *wr, int64_t T, int64_t H, int64_t E, double *logits)
+{
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int64_t h = 0; h < H; ++h) acc += oracle_bf16_value(x[t * H + h]) * oracle_bf16_value(wr[e * H + h]);
+            logits[t * E + e] = acc;
+        }
+}
+
+/* Shared expert for a subset of tokens (tok == NULL: tokens 0..n_tok-1): out[j] = W2s h with
+ * h = silu(W13s[0:Is] x) * W13s[Is:2Is] x, where w13s_q [2Is, H/2], w13s_s [2Is, H/32],
+ * w2s_q [H, Is/2], w2s_s [H, Is/32] (one expert of the routed weight format).  out fp64 [n_tok, H]. */
+void oracle_shared_ffn(const uint16_t *x, int64_t H, int64_t Is, const uint8_t *w13s_q, const uint16_t *w13s_s,
+                       const uint8_t *w2s_q, const uint16_t *w2s_s, const int64_t *tok, int64_t n_tok, double *out)
+{
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t j = 0; j < n_tok; ++j) {
+        int64_t t = tok ? tok[j] : j;
+        double *xa = (double *)malloc(sizeof(double) * (size_t)H);
+        double *g = (double *)malloc(sizeof(double) * (size_t)(2 * Is));
+        double *h = (double *)malloc(sizeof(double) * (size_t)Is);
+        for (int64_t c = 0; c < H; ++c) xa[c] = oracle_bf16_value(x[t * H + c]);
+        expert_matvec(w13s_q, w13s_s, 2 * Is, H, xa, g);
+        for (int64_t i = 0; i < Is; ++i) h[i] = silu(g[i]) * g[Is + i];
+        expert_matvec(w2s_q, w2s_s, H, Is, h, out + j * H);
+        free(xa); free(g); free(h);
+    }
 }

@@ -253,3 +253,53 @@ def test_page_byte_figures():
     gate_up_4bit = E * (2 * I * H // 2 + 2 * I * (H // 32) * 2)
     assert gate_up_4bit == 301_989_888
     assert E * mi.weight_bytes_per_expert(H, I) == 452_984_832
+
+
+# ---------------------------------------------------------------------------------------------------
+# router gate and shared expert (the Atlas debug section names gate logits and a shared expert output)
+
+def test_router_logits_one_hot_gate_selects_inputs():
+    # a gate whose row e is the unit vector at column 3e reads x[t, 3e] exactly
+    T, H, E = 4, 64, 6
+    inp = mi.make_inputs(mi.custom("rl", T, E, 2, H, 32, seed=21))
+    wr = np.zeros((E, H), np.uint16)
+    for e in range(E):
+        wr[e, 3 * e] = 0x3F80  # bf16 1.0
+    lg = oracle.router_logits(inp.x, wr)
+    X = mi.bf16_bits_to_f32(inp.x).astype(np.float64)
+    np.testing.assert_array_equal(lg, X[:, 0:3 * E:3])
+
+
+def test_router_logits_match_dense_matmul_and_scale():
+    wl = mi.custom("rl2", 7, 33, 4, 96, 32, seed=22)
+    inp, blk = mi.make_inputs(wl), mi.make_block_inputs(wl, 32)
+    lg = oracle.router_logits(inp.x, blk.w_router)
+    X = mi.bf16_bits_to_f32(inp.x).astype(np.float64)
+    Wr = mi.bf16_bits_to_f32(blk.w_router).astype(np.float64)
+    np.testing.assert_allclose(lg, X @ Wr.T, rtol=1e-12, atol=1e-12)
+    # doubling every gate weight (exact in bf16) doubles every logit exactly
+    w2 = mi.f32_to_bf16_bits(mi.bf16_bits_to_f32(blk.w_router) * 2)
+    np.testing.assert_array_equal(oracle.router_logits(inp.x, w2), 2 * lg)
+    # the generator's gate gives logits of about unit variance, as the workloads' logits
+    big = mi.custom("rl3", 256, 64, 8, 2048, 32, seed=23)
+    s = oracle.router_logits(mi.make_inputs(big).x, mi.make_block_inputs(big, 32).w_router).std()
+    assert 0.9 < s < 1.1
+
+
+def test_shared_expert_is_textbook_swiglu_and_a_one_expert_layer():
+    wl = mi.custom("sh", 6, 3, 2, 64, 32, seed=24)
+    inp, blk = mi.make_inputs(wl), mi.make_block_inputs(wl, 64)
+    sh = oracle.shared_ffn(inp.x, blk.w13s_q, blk.w13s_s, blk.w2s_q, blk.w2s_s)
+    X = mi.bf16_bits_to_f32(inp.x).astype(np.float64)
+    W = _np_dequant(blk.w13s_q, blk.w13s_s)
+    W1, W3 = W[:64], W[64:]
+    W2 = _np_dequant(blk.w2s_q, blk.w2s_s)
+    a = X @ W1.T
+    ref = (a * (1.0 / (1.0 + np.exp(-a))) * (X @ W3.T)) @ W2.T
+    np.testing.assert_allclose(sh, ref, rtol=1e-12, atol=1e-14)
+    # the same weights as the only expert of a top-1 routed layer (weight 1) give the same output
+    one = mi.MoEInputs(mi.custom("sh1", 6, 1, 1, 64, 64, seed=24), inp.x, np.zeros((6, 1), np.float32),
+                       blk.w13s_q[None], blk.w13s_s[None], blk.w2s_q[None], blk.w2s_s[None])
+    np.testing.assert_array_equal(oracle.moe_ffn(one), sh)
+    np.testing.assert_array_equal(oracle.shared_ffn(inp.x, blk.w13s_q, blk.w13s_s, blk.w2s_q, blk.w2s_s,
+                                                    tokens=np.array([4, 1])), sh[[4, 1]])
