@@ -7,7 +7,8 @@ workload is the 800-token / 256-expert prefill shape (top-8, hidden 2048, interm
 group-32 bf16 scales).  Weights are rotated over L distinct copies (L * weight bytes >= 1 GiB) so
 that no step finds its weights in L2 or the Infinity Cache.  The K timed steps run twice: as eager
 launches and as one replay of a HIP graph holding the same K steps; `value` is the faster of the
-two (both are in `timing`).
+two (both are in `timing`).  `block` adds the whole MoE block around the layer: the router gate
+GEMM from the hidden states and a shared expert (dense W4A16 SwiGLU) added in the combine.
 
 Prints ONE JSON line on stdout; progress and the per-kernel table go to stderr.
 """
@@ -141,6 +142,89 @@ def cpu_baseline(inp, target_s: float):
             "sample": f"{n} of {wl.T} tokens of the same workload ({dt:.1f} s wall), scaled to {wl.T} tokens"}
 
 
+def time_block(moe, wl, inp, x, copies, layout, args):
+    """The whole MoE block from the hidden states: router gate GEMM, shared expert (a dense W4A16
+    SwiGLU of intermediate size I) and the routed layer with the shared output added in the combine.
+    Each weight copy gets its own router and shared-expert weights, rotated with the routed ones.
+    Timed like the layer (HIP graph of K steps), plus per-stage events for the two extra stages."""
+    T, E, k, H, I = wl.T, wl.E, wl.k, wl.H, wl.I
+    Is = I
+    blk = mi.make_block_inputs(wl, Is)
+    wr0 = dev_bf16(blk.w_router)
+    sh0 = (dev(blk.w13s_q), dev(blk.w13s_s.view(np.int16)), dev(blk.w2s_q), dev(blk.w2s_s.view(np.int16)))
+    if layout == moe.MOE_LAYOUT_PACKED:
+        a, b = moe.moe_w4_prepack(sh0[0][None], sh0[1][None])
+        c, d = moe.moe_w4_prepack(sh0[2][None], sh0[3][None])
+        sh0 = (a[0], b[0], c[0], d[0])
+    L = len(copies)
+    extra = [(wr0, sh0)] + [(wr0.clone(), tuple(t.clone() for t in sh0)) for _ in range(L - 1)]
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_ffn_block_workspace_bytes(T, H, I, E, k, Is), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        q13, s13, q2, s2 = copies[i % L]
+        wr, sh = extra[i % L]
+        moe.moe_ffn_block_forward(x, wr, q13, s13, q2, s2, k, shared=sh, y=y, workspace=ws, weight_layout=layout)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    eager_ms = ev0.elapsed_time(ev1) / args.steps
+    graph_ms = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(min(L, args.steps)):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        graph.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        graph_ms = ev0.elapsed_time(ev1) / args.steps
+    # per-stage events for the two stages the block adds
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    so = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    dws = torch.empty(max(moe.moe_dense_ffn_workspace_bytes(T, H, Is), 256), dtype=torch.uint8, device="cuda")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.warmup + args.steps):
+        wr, sh = extra[i % L]
+        e = evs[i - args.warmup] if i >= args.warmup else None
+        if e: e[0].record()
+        moe.moe_router_logits(x, wr, logits=lg)
+        if e: e[1].record()
+        moe.moe_dense_ffn_w4a16(x, *sh, out=so, workspace=dws, weight_layout=layout)
+        if e: e[2].record()
+    torch.cuda.synchronize()
+    router_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e3)
+    shared_us = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e3)
+    best = eager_ms if graph_ms is None else min(eager_ms, graph_ms)
+    router_bytes = T * H * 2 + E * H * 2 + T * E * 4
+    shared_bytes = mi.weight_bytes_per_expert(H, Is) + T * H * 2 + 2 * T * Is * 2 + T * H * 4
+    out = {"us": round(best * 1e3, 2), "eager_us": round(eager_ms * 1e3, 2),
+           "graph_us": None if graph_ms is None else round(graph_ms * 1e3, 2), "shared_intermediate": Is,
+           "router_us": round(router_us, 2), "router_gbps": round(router_bytes / (router_us * 1e-6) / 1e9, 1),
+           "router_tflops": round(2.0 * T * H * E / (router_us * 1e-6) / 1e12, 3),
+           "shared_us": round(shared_us, 2), "shared_gbps": round(shared_bytes / (shared_us * 1e-6) / 1e9, 1),
+           "shared_tflops": round(6.0 * T * H * Is / (shared_us * 1e-6) / 1e12, 3)}
+    log(f"bench: whole block {out['us']:.1f} us (router {router_us:.1f} us, shared expert {shared_us:.1f} us)")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,6 +239,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="run only the counter-calibration copy")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
     ap.add_argument("--calibrate", action="store_true", help="measure copy bandwidth and a vendor bf16 GEMM rate only")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the whole-block timing (router gate + shared expert + routed layer)")
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe()
@@ -317,6 +403,8 @@ def main():
                      "traffic": measured_traffic(wl.name) if args.layout == "packed" else None,
                      "algorithmic_bytes": gu_bytes, "algorithmic_flops": gu_flops},
     }
+    if not args.no_block:
+        result["block"] = time_block(moe, wl, inp, x, copies, layout, args)
     if not args.no_cpu_baseline:
         log(f"bench: timing the CPU oracle on a token sample (~{args.cpu_seconds:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

@@ -185,14 +185,46 @@ moe_status_t moe_grouped_gemm_w4a16(const uint16_t* A, const int32_t* a_row_of, 
 
 /*
  * Routing-weighted scatter-reduce (combine) [ATOM, 8.1]:
- *   y[t, c] = bf16( sum_{s=0}^{k-1} topk_w[t, s] * O[inv_perm[t*k + s], c] )
- * summed in fp32 in ascending slot order, rounded once to bf16.
+ *   y[t, c] = bf16( sum_{s=0}^{k-1} topk_w[t, s] * O[inv_perm[t*k + s], c]  (+ shared[t, c]) )
+ * summed in fp32 in ascending slot order, then the shared term (if any) added, rounded once to bf16.
  *   O fp32 [T*k, H] (expert outputs in permuted row order); inv_perm int32 [T*k];
- *   topk_w fp32 [T, k]; y bf16 [T, H] out.
+ *   topk_w fp32 [T, k]; shared fp32 [T, H] or NULL (the shared-expert output of
+ *   moe_dense_ffn_w4a16, added with weight 1 [Atlas, KV Cache量化、MTP推测解码和调试工具链]);
+ *   y bf16 [T, H] out.
  * Shapes: T >= 0, k >= 1, H % 8 == 0.
  */
-moe_status_t moe_combine(const float* O, const int32_t* inv_perm, const float* topk_w, int32_t T,
-                         int32_t k, int32_t H, uint16_t* y, void* stream);
+moe_status_t moe_combine(const float* O, const int32_t* inv_perm, const float* topk_w, const float* shared,
+                         int32_t T, int32_t k, int32_t H, uint16_t* y, void* stream);
+
+/*
+ * Router gate logits [Atlas, KV Cache量化、MTP推测解码和调试工具链: the gate input and the gate logits
+ * of each MoE layer; ATOM, 8.1: the logits the top-k routing reads]:
+ *   logits[t, e] = sum_h x[t, h] * w_router[e, h], bf16 products accumulated in fp32 (MFMA order,
+ *   so not bit-identical to another summation order).
+ *   x bf16 [T, H]; w_router bf16 [E, H]; logits fp32 [T, E] out (4-byte aligned).
+ * Shapes: 0 <= T < 2^26 (T == 0 launches nothing), 1 <= E <= MOE_MAX_EXPERTS, H % 32 == 0, H >= 32.
+ */
+moe_status_t moe_router_logits(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H, int32_t E,
+                               float* logits, void* stream);
+
+/* Workspace bytes moe_dense_ffn_w4a16 needs (host-only, pure; 0 on invalid sizes). */
+size_t moe_dense_ffn_workspace_bytes(int32_t T, int32_t H, int32_t I);
+
+/*
+ * Dense W4A16 SwiGLU FFN: one expert applied to every token (the shared expert of an MoE block
+ * [Atlas, KV Cache量化、MTP推测解码和调试工具链]), on the same grouped-GEMM kernels with every row in
+ * one group:
+ *   out[t] = W2 ( silu(W1 x[t]) * (W3 x[t]) ), h rounded to bf16 between the projections.
+ *   x bf16 [T, H]; w13_q [2I, H/2], w13_s [2I, H/32], w2_q [H, I/2], w2_s [H, I/32] in the weight
+ *   format above (one expert, E = 1), all in weight_layout; out fp32 [T, H].
+ *   workspace: device scratch of at least moe_dense_ffn_workspace_bytes(T, H, I) bytes (holds h).
+ * Shapes: T >= 0 (T == 0 launches nothing), H and I positive multiples of 32 (of 128 when packed),
+ *         T < 2^26.
+ */
+moe_status_t moe_dense_ffn_w4a16(const uint16_t* x, int32_t T, int32_t H, int32_t I, const uint8_t* w13_q,
+                                 const uint16_t* w13_s, const uint8_t* w2_q, const uint16_t* w2_s,
+                                 int32_t weight_layout, float* out, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /* Row-tile height (block_m) moe_ffn_forward uses for these sizes and weight layout (host-only,
  * pure; -1 on invalid sizes or layout).  Lets a caller run the same launch configuration through
@@ -219,6 +251,29 @@ moe_status_t moe_ffn_forward(const uint16_t* x, const float* router_logits, int3
                              const uint16_t* w13_s, const uint8_t* w2_q, const uint16_t* w2_s,
                              int32_t weight_layout, uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* Workspace bytes moe_ffn_block_forward needs (host-only, pure; 0 on invalid sizes).  Is = 0 means
+ * no shared expert. */
+size_t moe_ffn_block_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t Is);
+
+/*
+ * The whole MoE block from the hidden states [Atlas, KV Cache量化、MTP推测解码和调试工具链: gate input,
+ * gate logits, routed output and shared-expert output of a layer]:
+ *   logits = moe_router_logits(x, w_router); (when Is > 0) s = moe_dense_ffn_w4a16(x, shared weights);
+ *   y = moe_ffn_forward(x, logits, ...) with s added in the combine (weight 1).
+ *   w_router bf16 [E, H]; the routed weights as for moe_ffn_forward; Is = shared-expert intermediate
+ *   size (0 = none, the four shared pointers are then ignored), shared weights w13s_q [2Is, H/2],
+ *   w13s_s [2Is, H/32], w2s_q [H, Is/2], w2s_s [H, Is/32] in weight_layout.
+ *   logits_out fp32 [T, E], topk_ids_out int32 [T, k], topk_w_out fp32 [T, k]: optional copies
+ *   (NULL = skip).  workspace: at least moe_ffn_block_workspace_bytes(T, H, I, E, k, Is) bytes.
+ * Shapes: those of moe_ffn_forward; Is >= 0, and Is > 0 follows the rules for I.
+ */
+moe_status_t moe_ffn_block_forward(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H, int32_t I,
+                                   int32_t E, int32_t k, const uint8_t* w13_q, const uint16_t* w13_s,
+                                   const uint8_t* w2_q, const uint16_t* w2_s, int32_t Is, const uint8_t* w13s_q,
+                                   const uint16_t* w13s_s, const uint8_t* w2s_q, const uint16_t* w2s_s,
+                                   int32_t weight_layout, uint16_t* y, float* logits_out, int32_t* topk_ids_out,
+                                   float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -56,7 +56,13 @@ def load() -> ctypes.CDLL:
         "moe_align": ([P, I32, I32, I32, I32, P, P, P, P, P, I32, P, P, SZ, P], I32),
         "moe_w4_prepack": ([P, P, I32, I32, I32, P, P, P], I32),
         "moe_grouped_gemm_w4a16": ([P, P, I32, P, P, I32, I32, I32, I32, P, I32, P, I32, I32, P, I32, P], I32),
-        "moe_combine": ([P, P, P, I32, I32, I32, P, P], I32),
+        "moe_combine": ([P, P, P, P, I32, I32, I32, P, P], I32),
+        "moe_router_logits": ([P, P, I32, I32, I32, P, P], I32),
+        "moe_dense_ffn_workspace_bytes": ([I32, I32, I32], SZ),
+        "moe_dense_ffn_w4a16": ([P, I32, I32, I32, P, P, P, P, I32, P, P, SZ, P], I32),
+        "moe_ffn_block_workspace_bytes": ([I32, I32, I32, I32, I32, I32], SZ),
+        "moe_ffn_block_forward": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, I32, P, P, P, P, P,
+                                   SZ, P], I32),
         "moe_ffn_block_m": ([I32, I32, I32, I32], I32),
         "moe_ffn_workspace_bytes": ([I32, I32, I32, I32, I32], SZ),
         "moe_ffn_forward": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, SZ, P], I32),
@@ -71,7 +77,9 @@ def load() -> ctypes.CDLL:
 
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_last_error", "moe_route_topk", "moe_max_tiles",
             "moe_align_workspace_bytes", "moe_align", "moe_w4_prepack", "moe_grouped_gemm_w4a16", "moe_combine",
-            "moe_ffn_block_m", "moe_ffn_workspace_bytes", "moe_ffn_forward")
+            "moe_router_logits", "moe_dense_ffn_workspace_bytes", "moe_dense_ffn_w4a16",
+            "moe_ffn_block_m", "moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_block_workspace_bytes",
+            "moe_ffn_block_forward")
 
 
 def _check(status: int):
@@ -188,14 +196,78 @@ def moe_grouped_gemm_w4a16(A, a_row_of, a_row_div: int, Wq, Ws, tiles, max_tiles
     return C
 
 
-def moe_combine(O, inv_perm, topk_w, y=None, stream=None):
-    """O fp32 [T*k, H], inv_perm int32 [T*k], topk_w fp32 [T, k] -> y bf16 [T, H]."""
+def moe_combine(O, inv_perm, topk_w, y=None, stream=None, shared=None):
+    """O fp32 [T*k, H], inv_perm int32 [T*k], topk_w fp32 [T, k] (+ shared fp32 [T, H]) -> y bf16 [T, H]."""
     _req(O, torch.float32, "O")
+    if shared is not None:
+        _req(shared, torch.float32, "shared")
     T, k = topk_w.shape
     H = O.shape[1]
     if y is None:
         y = torch.empty((T, H), dtype=torch.bfloat16, device=O.device)
-    _check(load().moe_combine(_p(O), _p(inv_perm), _p(topk_w), T, k, H, _p(y), _stream(stream)))
+    _check(load().moe_combine(_p(O), _p(inv_perm), _p(topk_w), _p(shared), T, k, H, _p(y), _stream(stream)))
+    return y
+
+
+def moe_router_logits(x, w_router, logits=None, stream=None):
+    """x bf16 [T, H], w_router bf16 [E, H] -> logits fp32 [T, E]."""
+    _req(x, "16bit", "x")
+    _req(w_router, "16bit", "w_router")
+    T, H = x.shape
+    E = w_router.shape[0]
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check(load().moe_router_logits(_p(x), _p(w_router), T, H, E, _p(logits), _stream(stream)))
+    return logits
+
+
+def moe_dense_ffn_workspace_bytes(T: int, H: int, I: int) -> int:
+    return int(load().moe_dense_ffn_workspace_bytes(T, H, I))
+
+
+def moe_dense_ffn_w4a16(x, w13_q, w13_s, w2_q, w2_s, out=None, workspace=None, stream=None,
+                        weight_layout: int = MOE_LAYOUT_CANONICAL):
+    """One dense SwiGLU expert on every token: x bf16 [T, H], w13_q [2I, H/2], w2_q [H, I/2] -> fp32 [T, H]."""
+    _req(x, "16bit", "x")
+    T, H = x.shape
+    I = w13_q.shape[-2] // 2
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    wsb = moe_dense_ffn_workspace_bytes(T, H, I)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=x.device)
+    _check(load().moe_dense_ffn_w4a16(_p(x), T, H, I, _p(w13_q), _p(w13_s), _p(w2_q), _p(w2_s), weight_layout,
+                                      _p(out), _p(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)))
+    return out
+
+
+def moe_ffn_block_workspace_bytes(T: int, H: int, I: int, E: int, k: int, Is: int = 0) -> int:
+    return int(load().moe_ffn_block_workspace_bytes(T, H, I, E, k, Is))
+
+
+def moe_ffn_block_forward(x, w_router, w13_q, w13_s, w2_q, w2_s, k: int, shared=None, y=None, logits_out=None,
+                          topk_ids_out=None, topk_w_out=None, workspace=None, stream=None,
+                          weight_layout: int = MOE_LAYOUT_CANONICAL):
+    """Whole MoE block: router gate, optional shared expert ``shared = (w13s_q, w13s_s, w2s_q, w2s_s)``,
+    routed experts and combine.  x bf16 [T, H], w_router bf16 [E, H] -> y bf16 [T, H]."""
+    _req(x, "16bit", "x")
+    T, H = x.shape
+    E, N13, _ = w13_q.shape
+    I = N13 // 2
+    if shared is None:
+        Is, sh = 0, (None, None, None, None)
+    else:
+        Is, sh = shared[0].shape[-2] // 2, shared
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    wsb = moe_ffn_block_workspace_bytes(T, H, I, E, k, Is)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=x.device)
+    _check(load().moe_ffn_block_forward(_p(x), _p(w_router), T, H, I, E, k, _p(w13_q), _p(w13_s), _p(w2_q),
+                                        _p(w2_s), Is, *(_p(t) for t in sh), weight_layout, _p(y), _p(logits_out),
+                                        _p(topk_ids_out), _p(topk_w_out), _p(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)))
     return y
 
 

@@ -93,6 +93,96 @@ FfnLayout ffn_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, bool
   return L;
 }
 
+// Shape checks shared by the layer entry points (gate_up [E, 2I, H], down [E, H, I]); they apply
+// to an empty batch too.
+moe_status_t check_weight_shape(int32_t H, int32_t I, int32_t weight_layout, const char* who) {
+  if (H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "%s: H=%d and I=%d must be positive multiples of 32", who, H, I);
+  if (weight_layout != MOE_LAYOUT_CANONICAL && weight_layout != MOE_LAYOUT_PACKED)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown weight_layout %d", who, weight_layout);
+  if (weight_layout == MOE_LAYOUT_PACKED && (H % 128 != 0 || I % 128 != 0))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "%s: packed weights need H %% 128 == 0 and I %% 128 == 0 (H=%d I=%d)", who,
+                H, I);
+  return MOE_OK;
+}
+
+moe_status_t check_weight_ptrs(const uint8_t* w13_q, const uint16_t* w13_s, const uint8_t* w2_q, const uint16_t* w2_s,
+                               int32_t weight_layout, const char* who) {
+  if (!w13_q || !w13_s || !w2_q || !w2_s) return fail(MOE_ERR_INVALID_ARG, "%s: NULL weight pointer", who);
+  if (!aligned16(w13_q) || !aligned16(w2_q) || !aligned2(w13_s) || !aligned2(w2_s) ||
+      (weight_layout == MOE_LAYOUT_PACKED && ((reinterpret_cast<uintptr_t>(w13_s) | reinterpret_cast<uintptr_t>(w2_s)) & 7u)))
+    return fail(MOE_ERR_MISALIGNED, "%s: weight codes need 16-byte alignment (packed scales 8-byte)", who);
+  return MOE_OK;
+}
+
+// Pointer checks of the routed layer (called for T > 0).
+moe_status_t check_ffn_ptrs(const uint16_t* x, const uint8_t* w13_q, const uint16_t* w13_s, const uint8_t* w2_q,
+                            const uint16_t* w2_s, int32_t weight_layout, const uint16_t* y,
+                            const int32_t* topk_ids_out, const float* topk_w_out, const void* workspace,
+                            const char* who) {
+  if (moe_status_t st = check_weight_ptrs(w13_q, w13_s, w2_q, w2_s, weight_layout, who)) return st;
+  if (!x || !y || !workspace) return fail(MOE_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (!aligned16(x) || !aligned16(y) || !aligned16(workspace) || (topk_ids_out && !aligned4(topk_ids_out)) ||
+      (topk_w_out && !aligned4(topk_w_out)))
+    return fail(MOE_ERR_MISALIGNED, "%s: x, y and workspace need 16-byte alignment", who);
+  return MOE_OK;
+}
+
+// Dense SwiGLU FFN (one expert applied to every row): gate_up with SiLU*mul into h, then down into
+// out (fp32).  Both projections run the grouped-GEMM kernels in dense mode (no tile list).
+hipError_t run_dense_ffn(const uint16_t* x, int T, int H, int I, const uint8_t* w13_q, const uint16_t* w13_s,
+                         const uint8_t* w2_q, const uint16_t* w2_s, int weight_layout, uint16_t* h, float* out,
+                         hipStream_t s) {
+  const int packed = weight_layout == MOE_LAYOUT_PACKED;
+  const int bm = pick_block_m(T, 1, packed);
+  const int mt = (T + bm - 1) / bm;
+  moe::GemmArgs g1{x, nullptr, 1, w13_q, w13_s, 2 * I, H, nullptr, nullptr, mt, T, h, MOE_EPI_SILU_MUL, 0, packed};
+  hipError_t e = moe::launch_grouped_gemm(g1, bm, s);
+  if (e != hipSuccess) return e;
+  moe::GemmArgs g2{h, nullptr, 1, w2_q, w2_s, H, I, nullptr, nullptr, mt, T, out, MOE_EPI_NONE, 1, packed};
+  return moe::launch_grouped_gemm(g2, bm, s);
+}
+
+// The routed layer after validation: routing and permutation, the two grouped GEMMs and the
+// combine (adding shared_out when given).
+moe_status_t run_ffn(const uint16_t* x, const float* router_logits, int32_t T, int32_t H, int32_t I, int32_t E,
+                     int32_t k, const uint8_t* w13_q, const uint16_t* w13_s, const uint8_t* w2_q, const uint16_t* w2_s,
+                     int32_t weight_layout, uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, char* ws,
+                     const FfnLayout& L, const float* shared_out, hipStream_t s) {
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
+  int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
+  int32_t* ntiles = reinterpret_cast<int32_t*>(ws + L.ntiles);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
+  float* o = reinterpret_cast<float*>(ws + L.o);
+  const int R = T * k;
+  hipError_t e;
+  if (moe::route_align_fused_fits(T, E, k)) {
+    e = moe::launch_route_align_small(router_logits, T, E, k, L.block_m, ids, w, counts, offsets, sorted, inv,
+                                      tiles, L.max_tiles, ntiles, s);
+    if (e != hipSuccess) return hip_status(e, "route+align launch");
+  } else {
+    e = moe::launch_route_topk(router_logits, T, E, k, ids, w, s);
+    if (e != hipSuccess) return hip_status(e, "route launch");
+    e = moe::launch_align(ids, R, E, L.block_m, counts, offsets, sorted, inv, tiles, L.max_tiles, ntiles,
+                          ws + L.align_ws, s);
+    if (e != hipSuccess) return hip_status(e, "align launch");
+  }
+  const int packed = weight_layout == MOE_LAYOUT_PACKED;
+  moe::GemmArgs g1{x, sorted, k, w13_q, w13_s, 2 * I, H, tiles, ntiles, L.max_tiles, 0, h, MOE_EPI_SILU_MUL, 0, packed};
+  e = moe::launch_grouped_gemm(g1, L.block_m, s);
+  if (e != hipSuccess) return hip_status(e, "gate_up launch");
+  moe::GemmArgs g2{h, nullptr, 1, w2_q, w2_s, H, I, tiles, ntiles, L.max_tiles, 0, o, MOE_EPI_NONE, 1, packed};
+  e = moe::launch_grouped_gemm(g2, L.block_m, s);
+  if (e != hipSuccess) return hip_status(e, "down launch");
+  e = moe::launch_combine(o, inv, w, shared_out, T, k, H, y, s);
+  return hip_status(e, "combine launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -200,21 +290,36 @@ moe_status_t moe_grouped_gemm_w4a16(const uint16_t* A, const int32_t* a_row_of, 
     return fail(MOE_ERR_MISALIGNED, "moe_grouped_gemm_w4a16: A, Wq, C need 16-byte alignment (packed Ws 8-byte)");
   if ((int64_t)max_tiles * block_m >= kMaxRows + (int64_t)MOE_MAX_EXPERTS * block_m)
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "max_tiles=%d too large", max_tiles);
-  moe::GemmArgs a{A, a_row_of, a_row_div, Wq, Ws, N, K, tiles, num_tiles, max_tiles, C, epilogue,
+  moe::GemmArgs a{A, a_row_of, a_row_div, Wq, Ws, N, K, tiles, num_tiles, max_tiles, 0, C, epilogue,
                   out_dtype == MOE_OUT_F32, weight_layout == MOE_LAYOUT_PACKED};
   return hip_status(moe::launch_grouped_gemm(a, block_m, (hipStream_t)stream), "moe_grouped_gemm_w4a16 launch");
 }
 
-moe_status_t moe_combine(const float* O, const int32_t* inv_perm, const float* topk_w, int32_t T,
-                         int32_t k, int32_t H, uint16_t* y, void* stream) {
+moe_status_t moe_combine(const float* O, const int32_t* inv_perm, const float* topk_w, const float* shared,
+                         int32_t T, int32_t k, int32_t H, uint16_t* y, void* stream) {
   if (T < 0 || k < 1 || H < 1) return fail(MOE_ERR_INVALID_ARG, "moe_combine: need T >= 0, k >= 1, H >= 1");
   if (H % 8 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_combine: H=%d must be a multiple of 8", H);
   if ((int64_t)T * k >= kMaxRows) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "T*k must be < 2^26");
   if (T == 0) return ok();
   if (!O || !inv_perm || !topk_w || !y) return fail(MOE_ERR_INVALID_ARG, "moe_combine: NULL pointer");
-  if (!aligned16(O) || !aligned16(y) || !aligned4(inv_perm) || !aligned4(topk_w))
-    return fail(MOE_ERR_MISALIGNED, "moe_combine: O and y need 16-byte alignment");
-  return hip_status(moe::launch_combine(O, inv_perm, topk_w, T, k, H, y, (hipStream_t)stream), "moe_combine launch");
+  if (!aligned16(O) || !aligned16(y) || !aligned4(inv_perm) || !aligned4(topk_w) || (shared && !aligned16(shared)))
+    return fail(MOE_ERR_MISALIGNED, "moe_combine: O, shared and y need 16-byte alignment");
+  return hip_status(moe::launch_combine(O, inv_perm, topk_w, shared, T, k, H, y, (hipStream_t)stream),
+                    "moe_combine launch");
+}
+
+moe_status_t moe_router_logits(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H, int32_t E,
+                               float* logits, void* stream) {
+  if (T < 0 || E < 1 || H < 32 || H % 32 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_router_logits: need T >= 0, E >= 1, H a positive multiple of 32");
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E=%d exceeds %d", E, MOE_MAX_EXPERTS);
+  if ((int64_t)T >= kMaxRows) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_router_logits: T=%d must be < 2^26", T);
+  if (T == 0) return ok();
+  if (!x || !w_router || !logits) return fail(MOE_ERR_INVALID_ARG, "moe_router_logits: NULL pointer");
+  if (!aligned16(x) || !aligned16(w_router) || !aligned4(logits))
+    return fail(MOE_ERR_MISALIGNED, "moe_router_logits: x and w_router need 16-byte alignment");
+  return hip_status(moe::launch_router_logits(x, w_router, T, H, E, logits, (hipStream_t)stream),
+                    "moe_router_logits launch");
 }
 
 int32_t moe_ffn_block_m(int32_t T, int32_t E, int32_t k, int32_t weight_layout) {
@@ -234,57 +339,94 @@ moe_status_t moe_ffn_forward(const uint16_t* x, const float* router_logits, int3
                              int32_t weight_layout, uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, void* workspace,
                              size_t workspace_bytes, void* stream) {
   if (moe_status_t st = check_routing_shape(T, E, k)) return st;
-  if (H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0)
-    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_ffn_forward: H=%d and I=%d must be positive multiples of 32", H, I);
-  if (weight_layout != MOE_LAYOUT_CANONICAL && weight_layout != MOE_LAYOUT_PACKED)
-    return fail(MOE_ERR_INVALID_ARG, "unknown weight_layout %d", weight_layout);
-  if (weight_layout == MOE_LAYOUT_PACKED && (H % 128 != 0 || I % 128 != 0))
-    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "packed weights need H %% 128 == 0 and I %% 128 == 0 (H=%d I=%d)", H, I);
+  if (moe_status_t st = check_weight_shape(H, I, weight_layout, "moe_ffn_forward")) return st;
   if (T == 0) return ok();
-  if (!x || !router_logits || !w13_q || !w13_s || !w2_q || !w2_s || !y || !workspace)
-    return fail(MOE_ERR_INVALID_ARG, "moe_ffn_forward: NULL pointer");
-  if (!aligned16(x) || !aligned16(w13_q) || !aligned16(w2_q) || !aligned16(y) || !aligned16(workspace) ||
-      !aligned4(router_logits) || !aligned2(w13_s) || !aligned2(w2_s) || (topk_ids_out && !aligned4(topk_ids_out)) ||
-      (topk_w_out && !aligned4(topk_w_out)) ||
-      (weight_layout == MOE_LAYOUT_PACKED && ((reinterpret_cast<uintptr_t>(w13_s) | reinterpret_cast<uintptr_t>(w2_s)) & 7u)))
-    return fail(MOE_ERR_MISALIGNED, "moe_ffn_forward: x, weights, y and workspace need 16-byte alignment");
+  if (moe_status_t st = check_ffn_ptrs(x, w13_q, w13_s, w2_q, w2_s, weight_layout, y, topk_ids_out, topk_w_out,
+                                       workspace, "moe_ffn_forward"))
+    return st;
+  if (!router_logits) return fail(MOE_ERR_INVALID_ARG, "moe_ffn_forward: NULL router_logits");
+  if (!aligned4(router_logits)) return fail(MOE_ERR_MISALIGNED, "moe_ffn_forward: router_logits need 4-byte alignment");
   const FfnLayout L = ffn_layout(T, H, I, E, k, weight_layout == MOE_LAYOUT_PACKED);
   if (workspace_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "moe_ffn_forward: workspace %zu B < required %zu B", workspace_bytes, L.total);
+  return run_ffn(x, router_logits, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, weight_layout, y, topk_ids_out,
+                 topk_w_out, static_cast<char*>(workspace), L, nullptr, (hipStream_t)stream);
+}
+
+size_t moe_dense_ffn_workspace_bytes(int32_t T, int32_t H, int32_t I) {
+  if (T < 0 || H < 1 || I < 1) return 0;
+  return up256((size_t)T * I * 2);
+}
+
+moe_status_t moe_dense_ffn_w4a16(const uint16_t* x, int32_t T, int32_t H, int32_t I, const uint8_t* w13_q,
+                                 const uint16_t* w13_s, const uint8_t* w2_q, const uint16_t* w2_s,
+                                 int32_t weight_layout, float* out, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (T < 0 || (int64_t)T >= kMaxRows) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_dense_ffn_w4a16: T=%d", T);
+  if (moe_status_t st = check_weight_shape(H, I, weight_layout, "moe_dense_ffn_w4a16")) return st;
+  if (T == 0) return ok();
+  if (moe_status_t st = check_weight_ptrs(w13_q, w13_s, w2_q, w2_s, weight_layout, "moe_dense_ffn_w4a16")) return st;
+  if (!x || !out || !workspace) return fail(MOE_ERR_INVALID_ARG, "moe_dense_ffn_w4a16: NULL pointer");
+  if (!aligned16(x) || !aligned16(out) || !aligned16(workspace))
+    return fail(MOE_ERR_MISALIGNED, "moe_dense_ffn_w4a16: x, out and workspace need 16-byte alignment");
+  if (workspace_bytes < moe_dense_ffn_workspace_bytes(T, H, I))
+    return fail(MOE_ERR_WORKSPACE, "moe_dense_ffn_w4a16: workspace %zu B < required %zu B", workspace_bytes,
+                moe_dense_ffn_workspace_bytes(T, H, I));
+  return hip_status(run_dense_ffn(x, T, H, I, w13_q, w13_s, w2_q, w2_s, weight_layout,
+                                  static_cast<uint16_t*>(workspace), out, (hipStream_t)stream),
+                    "moe_dense_ffn_w4a16 launch");
+}
+
+size_t moe_ffn_block_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t Is) {
+  const size_t base = moe_ffn_workspace_bytes(T, H, I, E, k);
+  if (base == 0 || Is < 0) return 0;
+  size_t total = base + up256((size_t)T * E * 4);
+  if (Is > 0) total += up256((size_t)T * Is * 2) + up256((size_t)T * H * 4);
+  return total;
+}
+
+moe_status_t moe_ffn_block_forward(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H, int32_t I,
+                                   int32_t E, int32_t k, const uint8_t* w13_q, const uint16_t* w13_s,
+                                   const uint8_t* w2_q, const uint16_t* w2_s, int32_t Is, const uint8_t* w13s_q,
+                                   const uint16_t* w13s_s, const uint8_t* w2s_q, const uint16_t* w2s_s,
+                                   int32_t weight_layout, uint16_t* y, float* logits_out, int32_t* topk_ids_out,
+                                   float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (moe_status_t st = check_routing_shape(T, E, k)) return st;
+  if (moe_status_t st = check_weight_shape(H, I, weight_layout, "moe_ffn_block_forward")) return st;
+  if (Is < 0) return fail(MOE_ERR_INVALID_ARG, "moe_ffn_block_forward: Is=%d", Is);
+  if (Is > 0)
+    if (moe_status_t st = check_weight_shape(H, Is, weight_layout, "moe_ffn_block_forward (shared expert)")) return st;
+  if (T == 0) return ok();
+  if (moe_status_t st = check_ffn_ptrs(x, w13_q, w13_s, w2_q, w2_s, weight_layout, y, topk_ids_out, topk_w_out,
+                                       workspace, "moe_ffn_block_forward"))
+    return st;
+  if (Is > 0)
+    if (moe_status_t st = check_weight_ptrs(w13s_q, w13s_s, w2s_q, w2s_s, weight_layout, "moe_ffn_block_forward (shared expert)"))
+      return st;
+  if (!w_router) return fail(MOE_ERR_INVALID_ARG, "moe_ffn_block_forward: NULL w_router");
+  if (!aligned16(w_router) || (logits_out && !aligned4(logits_out)))
+    return fail(MOE_ERR_MISALIGNED, "moe_ffn_block_forward: w_router needs 16-byte alignment");
+  const size_t need = moe_ffn_block_workspace_bytes(T, H, I, E, k, Is);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_ffn_block_forward: workspace %zu B < required %zu B", workspace_bytes, need);
+  const FfnLayout L = ffn_layout(T, H, I, E, k, weight_layout == MOE_LAYOUT_PACKED);
   char* ws = static_cast<char*>(workspace);
-  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
-  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
-  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
-  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
-  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
-  int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
-  int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
-  int32_t* ntiles = reinterpret_cast<int32_t*>(ws + L.ntiles);
-  uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
-  float* o = reinterpret_cast<float*>(ws + L.o);
+  size_t off = moe_ffn_workspace_bytes(T, H, I, E, k);
+  float* logits = logits_out ? logits_out : reinterpret_cast<float*>(ws + off);
+  off += up256((size_t)T * E * 4);
   hipStream_t s = (hipStream_t)stream;
-  const int R = T * k;
-  hipError_t e;
-  if (moe::route_align_fused_fits(T, E, k)) {
-    e = moe::launch_route_align_small(router_logits, T, E, k, L.block_m, ids, w, counts, offsets, sorted, inv,
-                                      tiles, L.max_tiles, ntiles, s);
-    if (e != hipSuccess) return hip_status(e, "route+align launch");
-  } else {
-    e = moe::launch_route_topk(router_logits, T, E, k, ids, w, s);
-    if (e != hipSuccess) return hip_status(e, "route launch");
-    e = moe::launch_align(ids, R, E, L.block_m, counts, offsets, sorted, inv, tiles, L.max_tiles, ntiles,
-                          ws + L.align_ws, s);
-    if (e != hipSuccess) return hip_status(e, "align launch");
+  hipError_t e = moe::launch_router_logits(x, w_router, T, H, E, logits, s);
+  if (e != hipSuccess) return hip_status(e, "router launch");
+  float* shared_out = nullptr;
+  if (Is > 0) {
+    uint16_t* hs = reinterpret_cast<uint16_t*>(ws + off);
+    off += up256((size_t)T * Is * 2);
+    shared_out = reinterpret_cast<float*>(ws + off);
+    e = run_dense_ffn(x, T, H, Is, w13s_q, w13s_s, w2s_q, w2s_s, weight_layout, hs, shared_out, s);
+    if (e != hipSuccess) return hip_status(e, "shared expert launch");
   }
-  const int packed = weight_layout == MOE_LAYOUT_PACKED;
-  moe::GemmArgs g1{x, sorted, k, w13_q, w13_s, 2 * I, H, tiles, ntiles, L.max_tiles, h, MOE_EPI_SILU_MUL, 0, packed};
-  e = moe::launch_grouped_gemm(g1, L.block_m, s);
-  if (e != hipSuccess) return hip_status(e, "gate_up launch");
-  moe::GemmArgs g2{h, nullptr, 1, w2_q, w2_s, H, I, tiles, ntiles, L.max_tiles, o, MOE_EPI_NONE, 1, packed};
-  e = moe::launch_grouped_gemm(g2, L.block_m, s);
-  if (e != hipSuccess) return hip_status(e, "down launch");
-  e = moe::launch_combine(o, inv, w, T, k, H, y, s);
-  return hip_status(e, "combine launch");
+  return run_ffn(x, logits, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, weight_layout, y, topk_ids_out, topk_w_out, ws,
+                 L, shared_out, s);
 }
 
 }  // extern "C"

@@ -152,6 +152,24 @@ __device__ __forceinline__ bool xcd_tile(long long b, int nbn, int num_tiles, in
   return tile < t1;
 }
 
+// Tile list lookups.  In dense mode (no tile list: the shared expert) tile i is rows
+// [i * BM, min((i + 1) * BM, dense_rows)) of expert 0.
+__device__ __forceinline__ int tile_count(const GemmArgs& p, int bm) {
+  return p.tiles ? *p.num_tiles : (p.dense_rows + bm - 1) / bm;
+}
+
+__device__ __forceinline__ void tile_entry(const GemmArgs& p, int tile, int bm, int& e, int& row0, int& rows) {
+  if (p.tiles) {
+    e = p.tiles[3 * tile];
+    row0 = p.tiles[3 * tile + 1];
+    rows = p.tiles[3 * tile + 2];
+  } else {
+    e = 0;
+    row0 = tile * bm;
+    rows = min(bm, p.dense_rows - row0);
+  }
+}
+
 // ---------------------------------------------------------------------------------------------------
 // Tiled kernel: BM x BN tile per 256-thread workgroup, waves split it WAVES_M x WAVES_N; the
 // activation tile of each K step is staged once in LDS (double buffer, one barrier per step) and
@@ -171,7 +189,8 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& p, int tile, int nb, 
   static_assert(MI >= 1 && NI >= 1 && ACH >= 1, "tile shape");
   static_assert(EPI != MOE_EPI_SILU_MUL || NI % 2 == 0, "SiLU*mul pairs gate and up blocks");
 
-  const int e = p.tiles[3 * tile], row0 = p.tiles[3 * tile + 1], rows = p.tiles[3 * tile + 2];
+  int e, row0, rows;
+  tile_entry(p, tile, BM, e, row0, rows);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -299,7 +318,7 @@ __global__ __launch_bounds__(256) void gemm_w4a16_tiled(GemmArgs p) {
   __shared__ int32_t sRow[BM];
   const int nbn = EPI == MOE_EPI_SILU_MUL ? (p.N / 2 + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
   int tile, nb;
-  if (!xcd_tile(linear_block(), nbn, *p.num_tiles, tile, nb)) return;
+  if (!xcd_tile(linear_block(), nbn, tile_count(p, BM), tile, nb)) return;
   tiled_tile<BM, BN, WAVES_M, PF, EPI, OUT_F32, LAYOUT>(p, tile, nb, sA, sRow);
 }
 
@@ -322,8 +341,9 @@ __global__ __launch_bounds__(256) void gemm_w4a16_sk(GemmArgs p) {
 
   const int nbn = EPI == MOE_EPI_SILU_MUL ? (p.N / 2 + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
   int tile, nb;
-  if (!xcd_tile(linear_block(), nbn, *p.num_tiles, tile, nb)) return;
-  const int e = p.tiles[3 * tile], row0 = p.tiles[3 * tile + 1], rows = p.tiles[3 * tile + 2];
+  if (!xcd_tile(linear_block(), nbn, tile_count(p, BM), tile, nb)) return;
+  int e, row0, rows;
+  tile_entry(p, tile, BM, e, row0, rows);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, q = lane >> 4;
@@ -482,7 +502,8 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p, int tile, int nb, uin
   constexpr int B_BYTES = (BN / 16) * 1024;  // 16 packed code blocks
   constexpr int STAGE = kMmStage;
   const int N = p.N, K = p.K;
-  const int e = p.tiles[3 * tile], row0 = p.tiles[3 * tile + 1], rows = p.tiles[3 * tile + 2];
+  int e, row0, rows;
+  tile_entry(p, tile, BM, e, row0, rows);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
@@ -639,7 +660,7 @@ __global__ __launch_bounds__(512) void gemm_w4a16_mm(GemmArgs p) {
   const int xcd = (int)(b & 7);
   const long long j = b >> 3;
   const int tile = (int)(j / nbx), nb = xcd + 8 * (int)(j % nbx);
-  if (nb >= nbn || tile >= *p.num_tiles) return;
+  if (nb >= nbn || tile >= tile_count(p, kMmBM)) return;
   mm_tile<EPI, OUT_F32, NSTAGE>(p, tile, nb, smem, sRow);
 }
 

@@ -8,6 +8,8 @@
 
 namespace moe {
 
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, int T, int H, int E, float* logits,
+                                hipStream_t stream);
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              hipStream_t stream);
 
@@ -42,9 +44,10 @@ struct GemmArgs {
   const uint8_t* Wq;       // [E, N, K/2]
   const uint16_t* Ws;      // [E, N, K/32]
   int N, K;
-  const int32_t* tiles;    // [max_tiles, 3]
+  const int32_t* tiles;    // [max_tiles, 3]; NULL = dense mode (one expert, rows 0..dense_rows)
   const int32_t* num_tiles;
   int max_tiles;
+  int dense_rows;          // dense mode: tile i covers rows [i * BM, min((i + 1) * BM, dense_rows)) of expert 0
   void* C;
   int epilogue;            // MOE_EPI_*
   int out_f32;
@@ -55,7 +58,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t strea
 hipError_t launch_prepack(const uint8_t* wq, const uint16_t* ws, int E, int N, int K, uint8_t* pq, uint16_t* ps,
                           hipStream_t stream);
 
-hipError_t launch_combine(const float* O, const int32_t* inv_perm, const float* w, int T, int k,
-                          int H, uint16_t* y, hipStream_t stream);
+hipError_t launch_combine(const float* O, const int32_t* inv_perm, const float* w, const float* shared, int T,
+                          int k, int H, uint16_t* y, hipStream_t stream);
 
 }  // namespace moe

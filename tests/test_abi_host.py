@@ -151,9 +151,9 @@ def test_prepack_rejects(lib):
 
 def test_combine_and_forward_reject(lib):
     f = _ptr(FAKE)
-    assert lib.moe_combine(f, f, f, 4, 2, 12, f, None) == -2        # H % 8
-    assert lib.moe_combine(f, f, f, 0, 2, 16, f, None) == 0         # T == 0
-    assert lib.moe_combine(_ptr(FAKE + 4), f, f, 4, 2, 16, f, None) == -3
+    assert lib.moe_combine(f, f, f, None, 4, 2, 12, f, None) == -2        # H % 8
+    assert lib.moe_combine(f, f, f, None, 0, 2, 16, f, None) == 0         # T == 0
+    assert lib.moe_combine(_ptr(FAKE + 4), f, f, None, 4, 2, 16, f, None) == -3
     ws = moe.moe_ffn_workspace_bytes(16, 256, 128, 8, 2)
     fw = lambda **kw: lib.moe_ffn_forward(kw.get("x", f), f, kw.get("T", 16), kw.get("H", 256), kw.get("I", 128),
                                           kw.get("E", 8), kw.get("k", 2), f, f, f, f, kw.get("lay", 0), f, None,
@@ -166,3 +166,58 @@ def test_combine_and_forward_reject(lib):
     assert fw(T=0) == 0
     assert fw(lay=5) == -1
     assert fw(lay=1, I=96) == -2       # packed needs I % 128 == 0
+
+
+def test_router_logits_rejects(lib):
+    f = _ptr(FAKE)
+    rl = lambda **kw: lib.moe_router_logits(kw.get("x", f), f, kw.get("T", 8), kw.get("H", 256), kw.get("E", 64),
+                                            kw.get("lg", f), None)
+    assert rl(H=250) == -1            # H % 32
+    assert rl(H=0) == -1
+    assert rl(E=0) == -1
+    assert rl(E=1025) == -2           # above MOE_MAX_EXPERTS
+    assert rl(T=-1) == -1
+    assert rl(T=0) == 0
+    assert rl(x=None) == -1
+    assert rl(x=_ptr(FAKE + 8)) == -3
+    assert rl(lg=_ptr(FAKE + 2)) == -3
+
+
+def test_dense_ffn_rejects(lib):
+    f = _ptr(FAKE)
+    ws = moe.moe_dense_ffn_workspace_bytes(16, 256, 128)
+    assert ws == 16 * 128 * 2
+    df = lambda **kw: lib.moe_dense_ffn_w4a16(kw.get("x", f), kw.get("T", 16), kw.get("H", 256), kw.get("I", 128),
+                                              f, f, kw.get("w2q", f), f, kw.get("lay", 0), f, f, kw.get("ws", ws),
+                                              None)
+    assert df(H=250) == -2
+    assert df(I=40) == -2
+    assert df(lay=1, I=96) == -2
+    assert df(lay=3) == -1
+    assert df(ws=ws - 1) == -4
+    assert df(w2q=None) == -1
+    assert df(x=_ptr(FAKE + 2)) == -3
+    assert df(T=0) == 0
+
+
+def test_block_forward_rejects(lib):
+    f = _ptr(FAKE)
+    T, H, I, E, k = 16, 256, 128, 8, 2
+    base = moe.moe_ffn_workspace_bytes(T, H, I, E, k)
+    ws0 = moe.moe_ffn_block_workspace_bytes(T, H, I, E, k, 0)
+    ws1 = moe.moe_ffn_block_workspace_bytes(T, H, I, E, k, 256)
+    assert ws0 == base + T * E * 4
+    assert ws1 == ws0 + T * 256 * 2 + T * H * 4
+    bf = lambda **kw: lib.moe_ffn_block_forward(
+        f, kw.get("wr", f), kw.get("T", T), H, I, E, k, f, f, f, f, kw.get("Is", 256), kw.get("s1", f), f, f, f,
+        kw.get("lay", 0), f, kw.get("lg", None), None, None, f, kw.get("ws", ws1), None)
+    assert bf(Is=-32) == -1
+    assert bf(Is=48) == -2            # shared expert size follows the rules for I
+    assert bf(Is=96, lay=1) == -2
+    assert bf(s1=None) == -1          # NULL shared weight with Is > 0
+    assert bf(wr=None) == -1
+    assert bf(wr=_ptr(FAKE + 4)) == -3
+    assert bf(lg=_ptr(FAKE + 2)) == -3
+    assert bf(ws=ws1 - 1) == -4
+    assert bf(T=0) == 0
+    assert moe.moe_ffn_block_workspace_bytes(T, H, I, E, k, -1) == 0
