@@ -70,7 +70,9 @@ size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // The tile list is sized for the canonical-layout tile height, which is never larger than the packed
 // one, so one workspace size serves both layouts.
-FfnLayout ffn_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, bool packed) {
+// extra_rows: rows of h and O past the T*k routed rows (the shared expert's, when it runs in the
+// routed launches).
+FfnLayout ffn_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, bool packed, int64_t extra_rows = 0) {
   FfnLayout L{};
   const int64_t R = T * k;
   L.block_m = pick_block_m(R, E, packed);
@@ -87,8 +89,8 @@ FfnLayout ffn_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, bool
   L.tiles = take((size_t)std::max<int64_t>(tile_cap, 1) * 12);
   L.ntiles = take(4);
   L.align_ws = take(moe::align_workspace_bytes((int)R, (int)E));
-  L.h = take((size_t)R * I * 2);
-  L.o = take((size_t)R * H * 4);
+  L.h = take((size_t)(R + extra_rows) * I * 2);
+  L.o = take((size_t)(R + extra_rows) * H * 4);
   L.total = off;
   return L;
 }
@@ -130,25 +132,49 @@ moe_status_t check_ffn_ptrs(const uint16_t* x, const uint8_t* w13_q, const uint1
 
 // Dense SwiGLU FFN (one expert applied to every row): gate_up with SiLU*mul into h, then down into
 // out (fp32).  Both projections run the grouped-GEMM kernels in dense mode (no tile list).
+// Row-tile height of one dense projection with `cols` output columns: the largest tile whose grid
+// alone has a workgroup per CU (256), else 16 (split-K when there are at most 32 row tiles).  The
+// column-block widths are those of the kernels launch_grouped_gemm picks for each height.
+int dense_block_m(int64_t T, int64_t cols, bool silu, bool packed) {
+  for (int bm : {128, 64, 32}) {
+    int64_t bn = bm == 128 ? (packed ? 256 : 128) : bm == 64 ? 256 : 128;
+    if (silu) bn /= 2;  // gate and up columns share a tile
+    if (((T + bm - 1) / bm) * ((cols + bn - 1) / bn) >= 256) return bm;
+  }
+  return 16;
+}
+
 hipError_t run_dense_ffn(const uint16_t* x, int T, int H, int I, const uint8_t* w13_q, const uint16_t* w13_s,
                          const uint8_t* w2_q, const uint16_t* w2_s, int weight_layout, uint16_t* h, float* out,
                          hipStream_t s) {
   const int packed = weight_layout == MOE_LAYOUT_PACKED;
-  const int bm = pick_block_m(T, 1, packed);
-  const int mt = (T + bm - 1) / bm;
-  moe::GemmArgs g1{x, nullptr, 1, w13_q, w13_s, 2 * I, H, nullptr, nullptr, mt, T, h, MOE_EPI_SILU_MUL, 0, packed};
-  hipError_t e = moe::launch_grouped_gemm(g1, bm, s);
+  const int bm1 = dense_block_m(T, I, true, packed), bm2 = dense_block_m(T, H, false, packed);
+  moe::GemmArgs g1{x, nullptr, 1, w13_q, w13_s, 2 * I, H, nullptr, nullptr, (T + bm1 - 1) / bm1, T, h,
+                   MOE_EPI_SILU_MUL, 0, packed};
+  hipError_t e = moe::launch_grouped_gemm(g1, bm1, s);
   if (e != hipSuccess) return e;
-  moe::GemmArgs g2{h, nullptr, 1, w2_q, w2_s, H, I, nullptr, nullptr, mt, T, out, MOE_EPI_NONE, 1, packed};
-  return moe::launch_grouped_gemm(g2, bm, s);
+  moe::GemmArgs g2{h, nullptr, 1, w2_q, w2_s, H, I, nullptr, nullptr, (T + bm2 - 1) / bm2, T, out, MOE_EPI_NONE, 1,
+                   packed};
+  return moe::launch_grouped_gemm(g2, bm2, s);
 }
 
+// Weights of a shared expert that runs inside the routed launches (its intermediate size equals
+// the routed one), or all NULL.
+struct SharedW {
+  const uint8_t* w13_q;
+  const uint16_t* w13_s;
+  const uint8_t* w2_q;
+  const uint16_t* w2_s;
+};
+
 // The routed layer after validation: routing and permutation, the two grouped GEMMs and the
-// combine (adding shared_out when given).
+// combine.  A shared expert is either run in the grouped GEMMs (sw.w13_q set: its tiles follow the
+// routed ones, its rows of h and O follow the T*k routed rows) or was run before (shared_out set);
+// either way its output is added in the combine.
 moe_status_t run_ffn(const uint16_t* x, const float* router_logits, int32_t T, int32_t H, int32_t I, int32_t E,
                      int32_t k, const uint8_t* w13_q, const uint16_t* w13_s, const uint8_t* w2_q, const uint16_t* w2_s,
                      int32_t weight_layout, uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, char* ws,
-                     const FfnLayout& L, const float* shared_out, hipStream_t s) {
+                     const FfnLayout& L, const SharedW& sw, const float* shared_out, hipStream_t s) {
   int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
   float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
@@ -173,13 +199,16 @@ moe_status_t run_ffn(const uint16_t* x, const float* router_logits, int32_t T, i
     if (e != hipSuccess) return hip_status(e, "align launch");
   }
   const int packed = weight_layout == MOE_LAYOUT_PACKED;
-  moe::GemmArgs g1{x, sorted, k, w13_q, w13_s, 2 * I, H, tiles, ntiles, L.max_tiles, 0, h, MOE_EPI_SILU_MUL, 0, packed};
+  const int shared_tiles = sw.w13_q ? (T + L.block_m - 1) / L.block_m : 0;
+  moe::GemmArgs g1{x, sorted, k, w13_q, w13_s, 2 * I, H, tiles, ntiles, L.max_tiles + shared_tiles, 0, h,
+                   MOE_EPI_SILU_MUL, 0, packed, sw.w13_q, sw.w13_s, T, R, 0};
   e = moe::launch_grouped_gemm(g1, L.block_m, s);
   if (e != hipSuccess) return hip_status(e, "gate_up launch");
-  moe::GemmArgs g2{h, nullptr, 1, w2_q, w2_s, H, I, tiles, ntiles, L.max_tiles, 0, o, MOE_EPI_NONE, 1, packed};
+  moe::GemmArgs g2{h, nullptr, 1, w2_q, w2_s, H, I, tiles, ntiles, L.max_tiles + shared_tiles, 0, o, MOE_EPI_NONE, 1,
+                   packed, sw.w2_q, sw.w2_s, T, R, 0};
   e = moe::launch_grouped_gemm(g2, L.block_m, s);
   if (e != hipSuccess) return hip_status(e, "down launch");
-  e = moe::launch_combine(o, inv, w, shared_out, T, k, H, y, s);
+  e = moe::launch_combine(o, inv, w, sw.w13_q ? o + (size_t)R * H : shared_out, T, k, H, y, s);
   return hip_status(e, "combine launch");
 }
 
@@ -350,7 +379,7 @@ moe_status_t moe_ffn_forward(const uint16_t* x, const float* router_logits, int3
   if (workspace_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "moe_ffn_forward: workspace %zu B < required %zu B", workspace_bytes, L.total);
   return run_ffn(x, router_logits, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, weight_layout, y, topk_ids_out,
-                 topk_w_out, static_cast<char*>(workspace), L, nullptr, (hipStream_t)stream);
+                 topk_w_out, static_cast<char*>(workspace), L, SharedW{}, nullptr, (hipStream_t)stream);
 }
 
 size_t moe_dense_ffn_workspace_bytes(int32_t T, int32_t H, int32_t I) {
@@ -409,16 +438,23 @@ moe_status_t moe_ffn_block_forward(const uint16_t* x, const uint16_t* w_router, 
   const size_t need = moe_ffn_block_workspace_bytes(T, H, I, E, k, Is);
   if (workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "moe_ffn_block_forward: workspace %zu B < required %zu B", workspace_bytes, need);
-  const FfnLayout L = ffn_layout(T, H, I, E, k, weight_layout == MOE_LAYOUT_PACKED);
+  // A shared expert of the routed intermediate size runs inside the routed launches; another size
+  // runs as a dense FFN first.
+  const bool fused = Is == I;
+  const bool packed = weight_layout == MOE_LAYOUT_PACKED;
+  const FfnLayout L = ffn_layout(T, H, I, E, k, packed, fused ? T : 0);
   char* ws = static_cast<char*>(workspace);
-  size_t off = moe_ffn_workspace_bytes(T, H, I, E, k);
+  size_t off = L.total;
   float* logits = logits_out ? logits_out : reinterpret_cast<float*>(ws + off);
   off += up256((size_t)T * E * 4);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = moe::launch_router_logits(x, w_router, T, H, E, logits, s);
   if (e != hipSuccess) return hip_status(e, "router launch");
+  SharedW sw{};
   float* shared_out = nullptr;
-  if (Is > 0) {
+  if (fused) {
+    sw = SharedW{w13s_q, w13s_s, w2s_q, w2s_s};
+  } else if (Is > 0) {
     uint16_t* hs = reinterpret_cast<uint16_t*>(ws + off);
     off += up256((size_t)T * Is * 2);
     shared_out = reinterpret_cast<float*>(ws + off);
@@ -426,7 +462,7 @@ moe_status_t moe_ffn_block_forward(const uint16_t* x, const uint16_t* w_router, 
     if (e != hipSuccess) return hip_status(e, "shared expert launch");
   }
   return run_ffn(x, logits, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, weight_layout, y, topk_ids_out, topk_w_out, ws,
-                 L, shared_out, s);
+                 L, sw, shared_out, s);
 }
 
 }  // extern "C"

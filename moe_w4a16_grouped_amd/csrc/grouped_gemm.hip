@@ -154,20 +154,50 @@ __device__ __forceinline__ bool xcd_tile(long long b, int nbn, int num_tiles, in
 
 // Tile list lookups.  In dense mode (no tile list: the shared expert) tile i is rows
 // [i * BM, min((i + 1) * BM, dense_rows)) of expert 0.
-__device__ __forceinline__ int tile_count(const GemmArgs& p, int bm) {
+__device__ __forceinline__ int routed_tile_count(const GemmArgs& p, int bm) {
   return p.tiles ? *p.num_tiles : (p.dense_rows + bm - 1) / bm;
 }
 
-__device__ __forceinline__ void tile_entry(const GemmArgs& p, int tile, int bm, int& e, int& row0, int& rows) {
-  if (p.tiles) {
-    e = p.tiles[3 * tile];
-    row0 = p.tiles[3 * tile + 1];
-    rows = p.tiles[3 * tile + 2];
+// Tiles of one launch: the routed (or dense) tiles, then those of the shared expert.
+__device__ __forceinline__ int tile_count(const GemmArgs& p, int bm) {
+  return routed_tile_count(p, bm) + (p.Wq_sh ? (p.shared_rows + bm - 1) / bm : 0);
+}
+
+// The arguments as seen by one tile, with its expert, first output row and row count.  Routed
+// tiles come from the tile list (dense mode: rows [i * bm, min((i + 1) * bm, dense_rows)) of expert
+// 0).  Shared-expert tiles read the shared weights, and gather no rows: output row r reads
+// activation row r, or token r - shared_row0 when the routed rows are gathered.
+__device__ __forceinline__ GemmArgs tile_view(const GemmArgs& p, int tile, int bm, int& e, int& row0, int& rows) {
+  GemmArgs v = p;
+  const int nr = routed_tile_count(p, bm);
+  if (tile < nr) {
+    if (p.tiles) {
+      e = p.tiles[3 * tile];
+      row0 = p.tiles[3 * tile + 1];
+      rows = p.tiles[3 * tile + 2];
+    } else {
+      e = 0;
+      row0 = tile * bm;
+      rows = min(bm, p.dense_rows - row0);
+    }
   } else {
+    const int j = tile - nr;
     e = 0;
-    row0 = tile * bm;
-    rows = min(bm, p.dense_rows - row0);
+    row0 = p.shared_row0 + j * bm;
+    rows = min(bm, p.shared_rows - j * bm);
+    v.Wq = p.Wq_sh;
+    v.Ws = p.Ws_sh;
+    if (p.a_row_of) {
+      v.a_row_of = nullptr;
+      v.a_row_sub = p.shared_row0;
+    }
   }
+  return v;
+}
+
+// Activation row of output row r.
+__device__ __forceinline__ int a_row(const GemmArgs& p, int r) {
+  return p.a_row_of ? p.a_row_of[r] / p.a_row_div : r - p.a_row_sub;
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -178,7 +208,7 @@ constexpr int kLDA = kBK + 8;  // padded LDS activation row of the tiled kernel 
 
 // One BM x BN output tile (tile list entry `tile`, N block `nb`) of the tiled kernel.
 template <int BM, int BN, int WAVES_M, int PF, int EPI, bool OUT_F32, int LAYOUT>
-__device__ __forceinline__ void tiled_tile(const GemmArgs& p, int tile, int nb, uint16_t (&sA)[2][BM * kLDA],
+__device__ __forceinline__ void tiled_tile(const GemmArgs& p0, int tile, int nb, uint16_t (&sA)[2][BM * kLDA],
                                            int32_t (&sRow)[BM]) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -190,7 +220,7 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& p, int tile, int nb, 
   static_assert(EPI != MOE_EPI_SILU_MUL || NI % 2 == 0, "SiLU*mul pairs gate and up blocks");
 
   int e, row0, rows;
-  tile_entry(p, tile, BM, e, row0, rows);
+  const GemmArgs p = tile_view(p0, tile, BM, e, row0, rows);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -201,7 +231,7 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& p, int tile, int nb, 
 
   for (int i = tid; i < BM; i += 256) {
     const int r = row0 + (i < rows ? i : 0);
-    sRow[i] = p.a_row_of ? p.a_row_of[r] / p.a_row_div : r;
+    sRow[i] = a_row(p, r);
   }
   WRow wr[NI];
   int ncol[NI];
@@ -331,7 +361,7 @@ __global__ __launch_bounds__(256) void gemm_w4a16_tiled(GemmArgs p) {
 // PF-deep register ring, so the main loop has no LDS traffic and no barrier.  The four partial sums
 // are reduced through LDS once per tile, in wave order.
 template <int BM, int BN, int PF, int EPI, bool OUT_F32, int LAYOUT>
-__global__ __launch_bounds__(256) void gemm_w4a16_sk(GemmArgs p) {
+__global__ __launch_bounds__(256) void gemm_w4a16_sk(GemmArgs p0) {
   constexpr int MI = BM / 16, NI = BN / 16;
   static_assert(MI >= 1 && MI <= 2 && NI >= 1, "tile shape");
   static_assert(EPI != MOE_EPI_SILU_MUL || NI % 2 == 0, "SiLU*mul pairs gate and up blocks");
@@ -339,11 +369,11 @@ __global__ __launch_bounds__(256) void gemm_w4a16_sk(GemmArgs p) {
 
   __shared__ __attribute__((aligned(16))) float red[3 * 64 * MI * NI * 4];
 
-  const int nbn = EPI == MOE_EPI_SILU_MUL ? (p.N / 2 + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
+  const int nbn = EPI == MOE_EPI_SILU_MUL ? (p0.N / 2 + BN / 2 - 1) / (BN / 2) : (p0.N + BN - 1) / BN;
   int tile, nb;
-  if (!xcd_tile(linear_block(), nbn, tile_count(p, BM), tile, nb)) return;
+  if (!xcd_tile(linear_block(), nbn, tile_count(p0, BM), tile, nb)) return;
   int e, row0, rows;
-  tile_entry(p, tile, BM, e, row0, rows);
+  const GemmArgs p = tile_view(p0, tile, BM, e, row0, rows);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, q = lane >> 4;
@@ -359,7 +389,7 @@ __global__ __launch_bounds__(256) void gemm_w4a16_sk(GemmArgs p) {
   for (int mi = 0; mi < MI; ++mi) {
     const int i = mi * 16 + l16;
     const int r = row0 + (i < rows ? i : 0);
-    arow[mi] = p.A + (size_t)(p.a_row_of ? p.a_row_of[r] / p.a_row_div : r) * K + q * 8;
+    arow[mi] = p.A + (size_t)a_row(p, r) * K + q * 8;
   }
   WRow wr[NI];
   int ncol[NI];
@@ -495,15 +525,15 @@ constexpr int kMmStage = kMmBM * 256 + (kMmBN / 16) * 1024 + (kMmBN / 16) * 128;
 
 // One 128 x 256 output tile (tile list entry `tile`, N block `nb`) of the large-tile kernel.
 template <int EPI, bool OUT_F32, int NSTAGE>
-__device__ __forceinline__ void mm_tile(const GemmArgs& p, int tile, int nb, uint8_t (&smem)[NSTAGE * kMmStage],
+__device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, uint8_t (&smem)[NSTAGE * kMmStage],
                                         int32_t (&sRow)[kMmBM]) {
   constexpr int BM = kMmBM, BN = kMmBN, MI = 4, NI = 4;
   constexpr int A_BYTES = BM * 256;          // 128 rows x 128 K x bf16
   constexpr int B_BYTES = (BN / 16) * 1024;  // 16 packed code blocks
   constexpr int STAGE = kMmStage;
-  const int N = p.N, K = p.K;
   int e, row0, rows;
-  tile_entry(p, tile, BM, e, row0, rows);
+  const GemmArgs p = tile_view(p0, tile, BM, e, row0, rows);
+  const int N = p.N, K = p.K;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
@@ -513,7 +543,7 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p, int tile, int nb, uin
 
   for (int i = tid; i < BM; i += 512) {
     const int r = row0 + (i < rows ? i : 0);
-    sRow[i] = p.a_row_of ? p.a_row_of[r] / p.a_row_div : r;
+    sRow[i] = a_row(p, r);
   }
   __syncthreads();
 

@@ -52,6 +52,15 @@ struct GemmArgs {
   int epilogue;            // MOE_EPI_*
   int out_f32;
   int packed;              // weights in the prepacked kernel layout (prepack.hip)
+  // Shared expert run in the same launch (NULL = none): one more expert with weights [N, K/2] and
+  // [N, K/32] (same layout as Wq / Ws), applied to shared_rows rows whose output rows start at
+  // shared_row0.  Its tiles follow the routed ones.  Its activation rows are the output rows
+  // themselves when a_row_of is NULL, else the token index (output row - shared_row0).
+  const uint8_t* Wq_sh;
+  const uint16_t* Ws_sh;
+  int shared_rows;
+  int shared_row0;
+  int a_row_sub;           // per-tile view only (set by the kernels; callers leave it 0)
 };
 hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t stream);
 

@@ -109,7 +109,8 @@ def test_router_logits_matches_oracle(name, nsample):
     assert np.all(np.abs(got - ref) <= _logit_bound(inp.x[tok], blk.w_router)), name
 
 
-@pytest.mark.parametrize("T,E,H", [(1, 1, 32), (37, 65, 96), (33, 1024, 64), (100, 200, 160), (31, 63, 2048)])
+@pytest.mark.parametrize("T,E,H", [(1, 1, 32), (37, 65, 96), (33, 1024, 64), (100, 200, 160), (31, 63, 2048),
+                                   (1000, 300, 96), (2051, 129, 256)])
 def test_router_logits_ragged_shapes(T, E, H):
     rng = np.random.default_rng(T + E + H)
     x = mi.f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
@@ -185,8 +186,11 @@ def test_combine_adds_shared_term():
 # ---------------------------------------------------------------------------------------------------
 # the whole block
 
+# Is == I: the shared expert runs inside the routed grouped GEMMs (its tiles after the routed ones);
+# other sizes run it as a dense FFN before the routed layer; Is == 0: no shared expert.
 BLOCK_CASES = [("tiny", 128, 16), ("dec1", 768, 1), ("dec8", 768, 8), ("dec64", 768, 24), ("pre800", 512, 40),
-               ("skew8192", 512, 24), ("tiny", 0, 16), ("pre800", 0, 24)]
+               ("skew8192", 512, 24), ("tiny", 256, 16), ("dec8", 256, 8), ("pre800", 1024, 24), ("tiny", 0, 16),
+               ("pre800", 0, 24)]
 
 
 @pytest.mark.parametrize("name,Is,nsample", BLOCK_CASES)
@@ -214,7 +218,7 @@ def test_block_forward_matches_oracle(name, Is, nsample):
         np.testing.assert_array_equal(_bits(y2), _bits(y))
 
 
-@pytest.mark.parametrize("name,Is", [("dec8", 768), ("pre800", 512)])
+@pytest.mark.parametrize("name,Is", [("dec8", 768), ("pre800", 512), ("pre800", 256)])
 def test_block_forward_packed_matches_canonical_bits(name, Is):
     b = BlockDevice(mi.WORKLOADS[name], Is)
     y0, lg0, _ = b.run()
