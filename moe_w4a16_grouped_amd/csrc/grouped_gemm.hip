@@ -504,22 +504,6 @@ __global__ __launch_bounds__(256) void gemm_w4a16_sk(GemmArgs p0) {
 // workgroups walk one row tile across that XCD's N blocks before the next tile, so the tile's
 // activations are fetched into that XCD's L2 once and reused by all of its N blocks.
 
-// s_waitcnt: vector-memory counter <= N, others not waited on (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-// Direct global->LDS 16-byte load (lane l writes LDS bytes [16l, 16l+16) after the wave-uniform
-// base).  Issued through inline assembly so that the compiler does not fence every later LDS read
-// behind it; the kernel orders these loads itself with explicit vmcnt waits and barriers.
-__device__ __forceinline__ void g2lds16(const void* g, void* lds_wave_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
-  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
-}
-
 constexpr int kMmBM = 128, kMmBN = 256;
 constexpr int kMmStage = kMmBM * 256 + (kMmBN / 16) * 1024 + (kMmBN / 16) * 128;  // A + codes + scales
 

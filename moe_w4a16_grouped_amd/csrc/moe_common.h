@@ -62,4 +62,20 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, 
 // silu(g) = g / (1 + e^-g); the quotient uses the fast reciprocal (the result is rounded to bf16).
 __device__ __forceinline__ float silu_f32(float g) { return __fdividef(g, 1.0f + __expf(-g)); }
 
+// s_waitcnt: vector-memory counter <= N, others not waited on (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Direct global->LDS 16-byte load (lane l writes LDS bytes [16l, 16l+16) after the wave-uniform
+// base).  Issued through inline assembly so that the compiler does not fence every later LDS read
+// behind it; the kernel orders these loads itself with explicit vmcnt waits and barriers.
+__device__ __forceinline__ void g2lds16(const void* g, void* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
+}
+
 }  // namespace moe

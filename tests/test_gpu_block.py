@@ -109,8 +109,12 @@ def test_router_logits_matches_oracle(name, nsample):
     assert np.all(np.abs(got - ref) <= _logit_bound(inp.x[tok], blk.w_router)), name
 
 
+# decode sizes and H % 64 != 0 take the direct-fragment kernel; larger ones the LDS-staged kernel
+# with 32 x 32 tiles and K split 4 ways (H = 192: one group gets no K stage), 64 x 64 tiles (H = 128:
+# fewer K stages than the ring) or 128 x 64 tiles
 @pytest.mark.parametrize("T,E,H", [(1, 1, 32), (37, 65, 96), (33, 1024, 64), (100, 200, 160), (31, 63, 2048),
-                                   (1000, 300, 96), (2051, 129, 256)])
+                                   (1000, 300, 96), (1000, 300, 192), (2051, 129, 256), (4100, 520, 128),
+                                   (4100, 1000, 128)])
 def test_router_logits_ragged_shapes(T, E, H):
     rng = np.random.default_rng(T + E + H)
     x = mi.f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
