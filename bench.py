@@ -4,11 +4,12 @@
 One step = the whole layer (route -> permute -> gate_up grouped GEMM with SiLU*mul -> down grouped
 GEMM -> combine) over one batch of seeded synthetic inputs already resident in HBM.  The default
 workload is the 800-token / 256-expert prefill shape (top-8, hidden 2048, intermediate 512, E2M1
-group-32 bf16 scales).  Weights are rotated over L distinct copies (L * weight bytes >= 1 GiB) so
-that no step finds its weights in L2 or the Infinity Cache.  The K timed steps run twice: as eager
-launches and as one replay of a HIP graph holding the same K steps; `value` is the faster of the
-two (both are in `timing`).  `block` adds the whole MoE block around the layer: the router gate
-GEMM from the hidden states and a shared expert (dense W4A16 SwiGLU) added in the combine.
+group-32 bf16 scales).  Weights are rotated over L distinct copies (L * bytes of the experts the
+routing touches >= 1 GiB) so that no step finds its weights in L2 or the Infinity Cache.  The K
+timed steps run twice: as eager launches and as one replay of a HIP graph holding the same K steps;
+`value` is the faster of the two (both are in `timing`).  `block` adds the whole MoE block around
+the layer: the router gate GEMM from the hidden states and a shared expert (dense W4A16 SwiGLU)
+added in the combine.
 
 Prints ONE JSON line on stdout; progress and the per-kernel table go to stderr.
 """
@@ -261,8 +262,14 @@ def main():
     log(f"bench: workload {wl.name} T={T} E={E} k={k} H={H} I={I}; generating inputs")
     inp = mi.make_inputs(wl)
     wbytes_all = E * mi.weight_bytes_per_expert(H, I)
-    L = args.copies or max(1, math.ceil((1 << 30) / wbytes_all))
     x, logits = dev_bf16(inp.x), dev(inp.logits)
+    # The routing is the same every step, so only the experts it touches are read.  Enough copies
+    # that those bytes, summed over the copies, exceed 1 GiB (four times the 256 MB Infinity Cache):
+    # every step then streams its weights from HBM.  The touched set comes from the library's own
+    # routing of the logits.
+    ids0, _ = moe.moe_route_topk(logits, k)
+    touched0 = int(torch.unique(ids0).numel())
+    L = args.copies or max(1, math.ceil((1 << 30) / (touched0 * mi.weight_bytes_per_expert(H, I))))
     w13_q0, w13_s0 = dev(inp.w13_q), dev(inp.w13_s.view(np.int16))
     w2_q0, w2_s0 = dev(inp.w2_q), dev(inp.w2_s.view(np.int16))
     copies = [(w13_q0, w13_s0, w2_q0, w2_s0)] + [
@@ -280,7 +287,8 @@ def main():
         copies = packed
     y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(moe.moe_ffn_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device="cuda")
-    log(f"bench: {L} weight copies of {wbytes_all / 1e6:.1f} MB; warmup {args.warmup}, timed steps {args.steps}")
+    log(f"bench: {L} weight copies of {wbytes_all / 1e6:.1f} MB ({touched0} of {E} experts touched); "
+        f"warmup {args.warmup}, timed steps {args.steps}")
 
     def step(i):
         q13, s13, q2, s2 = copies[i % L]
