@@ -24,6 +24,11 @@ The router gate and the shared expert (``make_block_inputs``) come from a second
      about N(0, 1), the router-logit distribution of the workloads)
   2. w13s_q, 3. w13s_s, 4. w2s_q, 5. w2s_s: one expert of intermediate size Is in the same W4 format
      and distributions as the routed experts.
+
+The MXFP4 variant (``make_mx_inputs``) draws with ``default_rng(seed)`` in the order above, so x,
+logits and the codes are those of the W4A16 inputs at the same seed; its scales are E8M0 bytes: each
+uniform(0.005, 0.02) draw u becomes 127 + rint(log2(u)) (the nearest power of two in log scale,
+2^-8 .. 2^-6).
 """
 from __future__ import annotations
 
@@ -138,3 +143,42 @@ def make_block_inputs(wl: Workload, Is: int, seed: int | None = None) -> BlockIn
     w2s_q = rng.integers(0, 256, (H, Is // 2), dtype=np.uint8)
     w2s_s = f32_to_bf16_bits(rng.uniform(0.005, 0.02, (H, Is // GROUP)).astype(np.float32))
     return BlockInputs(w_router, w13s_q, w13s_s, w2s_q, w2s_s)
+
+
+@dataclasses.dataclass
+class MXInputs:
+    """Inputs of the MXFP4 (W4A4) variant: same x, logits and codes, E8M0 scale bytes."""
+    wl: Workload
+    x: np.ndarray        # uint16 [T, H] bf16 bits
+    logits: np.ndarray   # float32 [T, E]
+    w13_q: np.ndarray    # uint8  [E, 2I, H/2]
+    w13_e: np.ndarray    # uint8  [E, 2I, H/32] E8M0
+    w2_q: np.ndarray     # uint8  [E, H, I/2]
+    w2_e: np.ndarray     # uint8  [E, H, I/32]  E8M0
+
+
+def e8m0_from_uniform(u: np.ndarray) -> np.ndarray:
+    """Scale draws -> E8M0 bytes of the nearest power of two in log scale."""
+    return (127 + np.rint(np.log2(u))).astype(np.uint8)
+
+
+def make_mx_inputs(wl: Workload, seed: int | None = None) -> MXInputs:
+    """Draw one workload's MXFP4 inputs (the W4A16 draw order, scales as E8M0 bytes)."""
+    T, E, H, I = wl.T, wl.E, wl.H, wl.I
+    if H % GROUP or I % GROUP:
+        raise ValueError("H and I must be multiples of 32")
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    x = f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    logits = rng.standard_normal((T, E), dtype=np.float32)
+    if wl.skew:
+        logits = (logits + skew_bias(E)[None, :]).astype(np.float32)
+    w13_q = rng.integers(0, 256, (E, 2 * I, H // 2), dtype=np.uint8)
+    w13_e = e8m0_from_uniform(rng.uniform(0.005, 0.02, (E, 2 * I, H // GROUP)))
+    w2_q = rng.integers(0, 256, (E, H, I // 2), dtype=np.uint8)
+    w2_e = e8m0_from_uniform(rng.uniform(0.005, 0.02, (E, H, I // GROUP)))
+    return MXInputs(wl, x, logits, w13_q, w13_e, w2_q, w2_e)
+
+
+def mx_weight_bytes_per_expert(H: int, I: int) -> int:
+    """E2M1 codes plus E8M0 scales of one expert's gate_up and down weights."""
+    return 2 * I * H // 2 + 2 * I * (H // GROUP) + H * I // 2 + H * (I // GROUP)

@@ -35,6 +35,14 @@
  *   - Gate logits: logits[t, e] = sum_h x[t, h] * w_router[e, h] with bf16 x and w_router.
  *   - Shared expert: one more SwiGLU FFN with the same W4 format, applied to every token, whose
  *     output is added to the routed output with weight 1.
+ *   - MXFP4 (the ATOM page, section 6.1, lists "per-1x32 MXFP4" with an a4w4 GEMM, and section 8.2
+ *     lists dynamic activation quantization as part of a format's contract): weights are E2M1
+ *     codes with one E8M0 scale (2^(byte - 127)) per 32 K elements; activations are quantized on
+ *     the fly to the same format before each projection (x before gate_up, h before down), by the
+ *     OCP Microscaling (MX) v1.0 conversion: per block of 32, X = 2^(floor(log2(amax)) - 2) (2 = the
+ *     largest E2M1 exponent), clamped to the E8M0 range, an all-zero block taking 2^-127; each
+ *     element becomes the E2M1 value nearest to v / X, ties to the even code, |v / X| > 6 saturating
+ *     to 6.  Each projection's output is exact sums of products of the dequantized operands.
  */
 #include <math.h>
 #include <stdint.h>
@@ -308,5 +316,156 @@ void oracle_shared_ffn(const uint16_t *x, int64_t H, int64_t Is, const uint8_t *
         for (int64_t i = 0; i < Is; ++i) h[i] = silu(g[i]) * g[Is + i];
         expert_matvec(w2s_q, w2s_s, H, Is, h, out + j * H);
         free(xa); free(g); free(h);
+    }
+}
+
+/* ---- MXFP4: E2M1 codes with E8M0 block scales on both operands ----------------------------------- */
+
+/* E8M0 scale byte -> 2^(byte - 127); byte 255 encodes NaN. */
+double oracle_e8m0_value(int byte)
+{
+    if (byte == 255) return NAN;
+    return ldexp(1.0, byte - 127);
+}
+
+/* The E2M1 code nearest to v: magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}, ties to the code whose
+ * mantissa bit is 0, magnitudes above 6 saturate to 6; the sign bit follows v (so -0.0 -> code 8). */
+int oracle_e2m1_nearest(double v)
+{
+    int sign = signbit(v) ? 8 : 0;
+    double a = fabs(v);
+    if (a >= 6.0) return sign | 7;
+    int best = 0;
+    double dbest = a;
+    for (int c = 1; c < 8; ++c) {
+        double d = fabs(a - oracle_e2m1_value(c));
+        if (d < dbest || (d == dbest && (c & 1) == 0)) { best = c; dbest = d; }
+    }
+    return sign | best;
+}
+
+/* MX quantization of a [rows, K] matrix (K % 32 == 0) into codes q [rows, K/2] (even K index in the
+ * low nibble) and scale bytes s [rows, K/32], one block of 32 consecutive K elements at a time. */
+void oracle_mx_quantize(const double *v, int64_t rows, int64_t K, uint8_t *q, uint8_t *s)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < K / ORACLE_GROUP; ++b) {
+            const double *blk = v + r * K + b * ORACLE_GROUP;
+            double amax = 0.0;
+            for (int i = 0; i < ORACLE_GROUP; ++i) if (fabs(blk[i]) > amax) amax = fabs(blk[i]);
+            int e = -127;
+            if (amax > 0.0) {
+                int p;
+                frexp(amax, &p);  /* amax = m * 2^p, 0.5 <= m < 1: floor(log2(amax)) = p - 1 */
+                e = (p - 1) - 2;
+                if (e < -127) e = -127;
+                if (e > 127) e = 127;
+            }
+            s[r * (K / ORACLE_GROUP) + b] = (uint8_t)(e + 127);
+            for (int i = 0; i < ORACLE_GROUP; i += 2) {
+                int c0 = oracle_e2m1_nearest(ldexp(blk[i], -e));
+                int c1 = oracle_e2m1_nearest(ldexp(blk[i + 1], -e));
+                q[r * (K / 2) + (b * ORACLE_GROUP + i) / 2] = (uint8_t)(c0 | (c1 << 4));
+            }
+        }
+}
+
+/* Value of element kk of row n of an MX matrix stored as codes q [*, K/2] and scales s [*, K/32]. */
+static double mx_at(const uint8_t *q, const uint8_t *s, int64_t K, int64_t n, int64_t kk)
+{
+    uint8_t byte = q[n * (K / 2) + kk / 2];
+    int code = (kk % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+    return oracle_e2m1_value(code) * oracle_e8m0_value(s[n * (K / ORACLE_GROUP) + kk / ORACLE_GROUP]);
+}
+
+/* Dense dequantization of an MX matrix [rows, K] into out (fp64). */
+void oracle_mx_dequant(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t K, double *out)
+{
+    for (int64_t n = 0; n < rows; ++n)
+        for (int64_t kk = 0; kk < K; ++kk) out[n * K + kk] = mx_at(q, s, K, n, kk);
+}
+
+/* One expert's MX matrix [N, K] times one (already dequantized) activation row a [K]. */
+static void mx_matvec(const uint8_t *q, const uint8_t *s, int64_t N, int64_t K, const double *a, double *out)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        double acc = 0.0;
+        for (int64_t kk = 0; kk < K; ++kk) acc += a[kk] * mx_at(q, s, K, n, kk);
+        out[n] = acc;
+    }
+}
+
+/* Quantize one activation row to MX and return it dequantized (in place of a). */
+static void mx_roundtrip_row(double *a, int64_t K)
+{
+    uint8_t *q = (uint8_t *)malloc((size_t)(K / 2));
+    uint8_t *sc = (uint8_t *)malloc((size_t)(K / ORACLE_GROUP));
+    oracle_mx_quantize(a, 1, K, q, sc);
+    for (int64_t kk = 0; kk < K; ++kk) a[kk] = mx_at(q, sc, K, 0, kk);
+    free(q);
+    free(sc);
+}
+
+/* Full MXFP4 (W4A4) layer for a subset of tokens (tok == NULL: tokens 0..n_tok-1).
+ *   x [T, H] bf16 bits, logits [T, E] fp32, w13_q [E, 2I, H/2], w13_e [E, 2I, H/32] E8M0,
+ *   w2_q [E, H, I/2], w2_e [E, H, I/32] E8M0; y [n_tok, H] fp64.
+ *   Optional diagnostics (may be NULL): h [n_tok, k, I] (silu(gate) * up before its quantization).
+ * Per token: route; quantize x's row to MX; for each slot s the expert's gate_up projection of the
+ * quantized row, h = silu(gate) * up, h quantized to MX, the down projection, y = sum_s w_s o_s. */
+void oracle_moe_ffn_mx(const uint16_t *x, const float *logits, int64_t T, int64_t H, int64_t I, int64_t E,
+                       int64_t k, const uint8_t *w13_q, const uint8_t *w13_e, const uint8_t *w2_q,
+                       const uint8_t *w2_e, const int64_t *tok, int64_t n_tok, double *y, double *h_out)
+{
+    (void)T;
+    const int64_t sz13_q = 2 * I * (H / 2), sz13_e = 2 * I * (H / ORACLE_GROUP);
+    const int64_t sz2_q = H * (I / 2), sz2_e = H * (I / ORACLE_GROUP);
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t j = 0; j < n_tok; ++j) {
+        int64_t t = tok ? tok[j] : j;
+        int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+        double *w = (double *)malloc(sizeof(double) * (size_t)k);
+        double *xa = (double *)malloc(sizeof(double) * (size_t)H);
+        double *g = (double *)malloc(sizeof(double) * (size_t)(2 * I));
+        double *h = (double *)malloc(sizeof(double) * (size_t)I);
+        double *o = (double *)malloc(sizeof(double) * (size_t)H);
+        oracle_route(logits + t * E, 1, E, k, ids, w);
+        for (int64_t c = 0; c < H; ++c) xa[c] = oracle_bf16_value(x[t * H + c]);
+        mx_roundtrip_row(xa, H);
+        for (int64_t c = 0; c < H; ++c) y[j * H + c] = 0.0;
+        for (int64_t s = 0; s < k; ++s) {
+            int64_t e = ids[s];
+            mx_matvec(w13_q + e * sz13_q, w13_e + e * sz13_e, 2 * I, H, xa, g);
+            for (int64_t i = 0; i < I; ++i) h[i] = silu(g[i]) * g[I + i];
+            if (h_out) memcpy(h_out + (j * k + s) * I, h, sizeof(double) * (size_t)I);
+            mx_roundtrip_row(h, I);
+            mx_matvec(w2_q + e * sz2_q, w2_e + e * sz2_e, H, I, h, o);
+            for (int64_t c = 0; c < H; ++c) y[j * H + c] += w[s] * o[c];
+        }
+        free(ids); free(w); free(xa); free(g); free(h); free(o);
+    }
+}
+
+/* Grouped MX projection over permuted rows (one grouped-GEMM launch of the MXFP4 path): for each
+ * permuted row r of expert e with activation row a_row = (a_row_of ? a_row_of[r] / a_row_div : r),
+ *   C[r, n] = sum_kk A[a_row, kk] * W_e[n, kk],  A given as MX codes Aq [*, K/2] and scales As [*, K/32],
+ * W as Wq [E, N, K/2] and We [E, N, K/32].  With silu_mul != 0, C[r, j] = silu(G[r, j]) * G[r, N/2 + j]
+ * (j < N/2), before any quantization.  C fp64. */
+void oracle_grouped_proj_mx(const uint8_t *Aq, const uint8_t *As, const int32_t *a_row_of, int64_t a_row_div,
+                            const uint8_t *Wq, const uint8_t *We, int64_t E, int64_t N, int64_t K,
+                            const int32_t *offsets, int silu_mul, double *C)
+{
+    const int64_t szq = N * (K / 2), sze = N * (K / ORACLE_GROUP);
+    const int64_t nout = silu_mul ? N / 2 : N;
+    for (int64_t e = 0; e < E; ++e) {
+        #pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t r = offsets[e]; r < offsets[e + 1]; ++r) {
+            int64_t arow = a_row_of ? a_row_of[r] / a_row_div : r;
+            double *a = (double *)malloc(sizeof(double) * (size_t)K);
+            double *g = (double *)malloc(sizeof(double) * (size_t)N);
+            for (int64_t c = 0; c < K; ++c) a[c] = mx_at(Aq, As, K, arow, c);
+            mx_matvec(Wq + e * szq, We + e * sze, N, K, a, g);
+            for (int64_t n = 0; n < nout; ++n) C[r * nout + n] = silu_mul ? silu(g[n]) * g[N / 2 + n] : g[n];
+            free(a); free(g);
+        }
     }
 }

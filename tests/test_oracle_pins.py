@@ -303,3 +303,176 @@ def test_shared_expert_is_textbook_swiglu_and_a_one_expert_layer():
     np.testing.assert_array_equal(oracle.moe_ffn(one), sh)
     np.testing.assert_array_equal(oracle.shared_ffn(inp.x, blk.w13s_q, blk.w13s_s, blk.w2s_q, blk.w2s_s,
                                                     tokens=np.array([4, 1])), sh[[4, 1]])
+
+
+# ---------------------------------------------------------------------------------------------------
+# MXFP4 (W4A4): E8M0 scales, MX quantization, the W4A4 layer
+
+def _golden_mx():
+    blocks = []
+    with open(os.path.join(GOLDEN, "mx_quant_worked_example.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            vals, scale, codes = (part.split() for part in line.split("|"))
+            v = np.zeros(32)
+            v[:len(vals)] = [float(t) for t in vals]
+            c = np.zeros(32, np.int64)
+            c[:len(codes)] = [int(t) for t in codes]
+            blocks.append((v, int(scale[0]), c))
+    return blocks
+
+
+def _codes_of(q):
+    q = np.asarray(q, np.uint8)
+    out = np.empty(q.shape[:-1] + (q.shape[-1] * 2,), np.int64)
+    out[..., 0::2] = q & 0xF
+    out[..., 1::2] = q >> 4
+    return out
+
+
+def _np_mx_dequant(q, s):
+    """Independent numpy dequantisation: golden E2M1 table times 2^(byte - 127)."""
+    table = _e2m1_table()
+    codes = _codes_of(q)
+    scale = np.exp2(np.asarray(s, np.float64) - 127.0)
+    return table[codes] * np.repeat(scale, 32, axis=-1)
+
+
+def test_e8m0_scale_decode():
+    assert oracle.e8m0_value(127) == 1.0
+    assert oracle.e8m0_value(119) == 2.0 ** -8
+    assert oracle.e8m0_value(0) == 2.0 ** -127
+    assert oracle.e8m0_value(254) == 2.0 ** 127
+    assert np.isnan(oracle.e8m0_value(255))
+
+
+def test_mx_quantize_golden_blocks():
+    for v, scale, codes in _golden_mx():
+        q, s = oracle.mx_quantize(v[None])
+        assert int(s[0, 0]) == scale, (v[:8], s)
+        np.testing.assert_array_equal(_codes_of(q)[0], codes)
+
+
+def test_e2m1_nearest_matches_grid_search():
+    # brute force over the eight codes of v's sign: the smallest distance, ties to an even code,
+    # magnitudes at or above 6 saturate
+    table = _e2m1_table()
+    rng = np.random.default_rng(5)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    vals = np.concatenate([rng.uniform(-8, 8, 4000), mids, -mids, np.nextafter(mids, 0), np.nextafter(mids, 9),
+                           [0.0, -0.0, 6.0, -6.0, 7.99, 100.0, 1e-300]])
+    for v in vals:
+        sign = 8 if np.signbit(v) else 0
+        cand = [sign | c for c in range(8)]
+        if abs(v) >= 6:
+            want = sign | 7
+        else:
+            d = [abs(v - table[c]) for c in cand]
+            dmin = min(d)
+            ties = [c for c, dc in zip(cand, d) if dc == dmin]
+            even = [c for c in ties if c % 2 == 0]
+            want = (even or ties)[0]
+        assert oracle.e2m1_nearest(float(v)) == want, v
+
+
+def test_mx_quantize_invariants():
+    rng = np.random.default_rng(6)
+    v = rng.standard_normal((64, 128)) * np.exp2(rng.integers(-20, 20, (64, 1)))
+    v[3, 32:64] = 0.0
+    q, s = oracle.mx_quantize(v)
+    codes = _codes_of(q)
+    # powers of two move only the scale byte
+    for m in (-3, 1, 7):
+        q2, s2 = oracle.mx_quantize(v * 2.0 ** m)
+        np.testing.assert_array_equal(q2, q)
+        nz = s != 0
+        np.testing.assert_array_equal(s2[nz].astype(int), s[nz].astype(int) + m)
+    # negation flips every sign bit
+    qn, sn = oracle.mx_quantize(-v)
+    np.testing.assert_array_equal(_codes_of(qn), codes ^ 8)
+    np.testing.assert_array_equal(sn, s)
+    # the scaled block maximum lands in [4, 8): its code magnitude is 4 or 6
+    X = np.exp2(s.astype(np.float64) - 127)
+    blocks = np.abs(v).reshape(64, 4, 32).max(axis=2)
+    live = blocks > 0
+    assert np.all((blocks[live] / X[live] >= 4) & (blocks[live] / X[live] < 8))
+    # every element is within half the local E2M1 spacing of its value (below saturation)
+    deq = _np_mx_dequant(q, s)
+    scaled = np.abs(v) / np.repeat(X, 32, axis=1)
+    spacing = np.where(scaled < 2, 0.5, np.where(scaled < 4, 1.0, 2.0))
+    ok = (np.abs(deq - v) <= 0.5 * spacing * np.repeat(X, 32, axis=1) * (1 + 1e-12)) | (scaled >= 6)
+    assert np.all(ok)
+    # the all-zero block
+    assert s[3, 1] == 0 and np.all(codes[3, 32:64] == 0)
+
+
+def _mx_layer_dense(inp):
+    """The W4A4 layer written densely in numpy: every expert on every token, a [T, E] routing matrix
+    with the renormalised top-k weights and zeros elsewhere; activations quantized by the oracle's MX
+    quantizer, every MX tensor dequantized by the numpy table above."""
+    wl = inp.wl
+    T, E, k, H, I = wl.T, wl.E, wl.k, wl.H, wl.I
+    ids, w = oracle.route(inp.logits, k)
+    route = np.zeros((T, E))
+    for t in range(T):
+        route[t, ids[t]] = w[t]
+    x = mi.bf16_bits_to_f32(inp.x).astype(np.float64)
+    xq, xs = oracle.mx_quantize(x)
+    xd = _np_mx_dequant(xq, xs)
+    y = np.zeros((T, H))
+    for e in range(E):
+        W13 = _np_mx_dequant(inp.w13_q[e], inp.w13_e[e])
+        W2 = _np_mx_dequant(inp.w2_q[e], inp.w2_e[e])
+        g = xd @ W13.T
+        h = g[:, :I] / (1.0 + np.exp(-g[:, :I])) * g[:, I:]
+        hq, hs = oracle.mx_quantize(h)
+        y += route[:, e:e + 1] * (_np_mx_dequant(hq, hs) @ W2.T)
+    return y
+
+
+@pytest.mark.parametrize("T,E,k,H,I,skew", [(9, 6, 2, 64, 96, False), (5, 4, 4, 128, 64, False),
+                                             (12, 8, 3, 96, 64, True)])
+def test_mx_layer_matches_dense_formulation(T, E, k, H, I, skew):
+    inp = mi.make_mx_inputs(mi.custom("mxdense", T, E, k, H, I, skew=skew, seed=T + E))
+    ref = _mx_layer_dense(inp)
+    y = oracle.moe_ffn_mx(inp)
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.sqrt(np.mean(ref ** 2))
+
+
+def test_mx_single_expert_is_quantized_swiglu():
+    inp = mi.make_mx_inputs(mi.custom("mx1", 7, 1, 1, 64, 64, seed=3))
+    x = mi.bf16_bits_to_f32(inp.x).astype(np.float64)
+    xd = _np_mx_dequant(*oracle.mx_quantize(x))
+    W1 = _np_mx_dequant(inp.w13_q[0, :64], inp.w13_e[0, :64])
+    W3 = _np_mx_dequant(inp.w13_q[0, 64:], inp.w13_e[0, 64:])
+    W2 = _np_mx_dequant(inp.w2_q[0], inp.w2_e[0])
+    a, b = xd @ W1.T, xd @ W3.T
+    h = a * (1 / (1 + np.exp(-a))) * b
+    ref = _np_mx_dequant(*oracle.mx_quantize(h)) @ W2.T
+    np.testing.assert_allclose(oracle.moe_ffn_mx(inp), ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+def test_grouped_proj_mx_matches_rowwise_products():
+    rng = np.random.default_rng(8)
+    E, N, K, R = 3, 48, 96, 20
+    Aq = rng.integers(0, 256, (R, K // 2), dtype=np.uint8)
+    As = rng.integers(120, 130, (R, K // 32), dtype=np.uint8)
+    Wq = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    We = rng.integers(118, 124, (E, N, K // 32), dtype=np.uint8)
+    offsets = np.array([0, 7, 7, R], np.int32)
+    a_row_of = rng.permutation(R).astype(np.int32)
+    C = oracle.grouped_proj_mx(Aq, As, a_row_of, 1, Wq, We, offsets)
+    A = _np_mx_dequant(Aq, As)
+    for e in range(E):
+        W = _np_mx_dequant(Wq[e], We[e])
+        for r in range(offsets[e], offsets[e + 1]):
+            np.testing.assert_allclose(C[r], W @ A[a_row_of[r]], rtol=1e-13, atol=1e-300)
+    Cs = oracle.grouped_proj_mx(Aq, As, None, 1, Wq, We, offsets, silu_mul=True)
+    for e in range(E):
+        W = _np_mx_dequant(Wq[e], We[e])
+        for r in range(offsets[e], offsets[e + 1]):
+            g = W @ A[r]
+            np.testing.assert_allclose(Cs[r], g[:N // 2] / (1 + np.exp(-g[:N // 2])) * g[N // 2:], rtol=1e-12,
+                                       atol=1e-300)
