@@ -275,6 +275,54 @@ moe_status_t moe_ffn_block_forward(const uint16_t* x, const uint16_t* w_router, 
                                    int32_t weight_layout, uint16_t* y, float* logits_out, int32_t* topk_ids_out,
                                    float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * ---- MXFP4 (W4A4) variant ------------------------------------------------------------------------
+ * [ATOM, 6.1: per-1x32 MXFP4 served by an a4w4 GEMM; ATOM, 8.2: dynamic activation quantization is
+ * part of a format's contract.]  Weights and activations are E2M1 codes (as above) with one E8M0
+ * scale byte per 32 consecutive K elements: value = E2M1(code) * 2^(byte - 127) (byte 255 = NaN is
+ * not accepted in weights).  Activations are quantized on the fly, per row and block of 32, by the
+ * OCP MX conversion: X = 2^(floor(log2(max |v|)) - 2) clamped to [2^-127, 2^127] (an all-zero block
+ * takes byte 0), code = nearest E2M1 value of v / X, ties to the even code, saturating at +-6.
+ * Products run on the gfx950 scaled FP4 matrix instruction with fp32 accumulation.
+ */
+
+/* x bf16 [rows, K] -> codes q [rows, K/2] and scale bytes s [rows, K/32] (MX conversion above).
+ * Shapes: 0 <= rows < 2^26, K a positive multiple of 32.  x and q 16-byte aligned. */
+moe_status_t moe_mx_quantize(const uint16_t* x, int32_t rows, int32_t K, uint8_t* q, uint8_t* s, void* stream);
+
+/*
+ * Grouped MXFP4 GEMM over the tile list of moe_align [Atlas, 编译时内核选择和W4A16 Grouped GEMM: one
+ * launch over all experts]: for each permuted row r of expert e, activation row
+ * a = (a_row_of ? a_row_of[r] / a_row_div : r):
+ *   G[r, n] = sum_k A[a, k] * W_e[n, k],  A = (Aq [*, K/2], As [*, K/32]), W = (Wq [E, N, K/2], We [E, N, K/32]).
+ *   epilogue NONE:     C [rows, N] fp32 or bf16 (out_dtype); Cs unused.
+ *   epilogue SILU_MUL: h[r, j] = silu(G[r, j]) * G[r, N/2 + j] in fp32, then quantized per 32 columns:
+ *                      C = codes [rows, N/4], Cs = scale bytes [rows, N/64] (out_dtype ignored).
+ * block_m 16, 32 or 64 (the tile height moe_align used).  K % 32 == 0; SILU_MUL needs N % 64 == 0.
+ */
+moe_status_t moe_grouped_gemm_mxfp4(const uint8_t* Aq, const uint8_t* As, const int32_t* a_row_of, int32_t a_row_div,
+                                    const uint8_t* Wq, const uint8_t* We, int32_t E, int32_t N, int32_t K,
+                                    const int32_t* tiles, int32_t max_tiles, const int32_t* num_tiles, int32_t block_m,
+                                    int32_t epilogue, void* C, uint8_t* Cs, int32_t out_dtype, void* stream);
+
+/* Row-tile height and workspace bytes of moe_ffn_forward_mxfp4 (host-only, pure; -1 / 0 on invalid sizes). */
+int32_t moe_ffn_mxfp4_block_m(int32_t T, int32_t E, int32_t k);
+size_t moe_ffn_mxfp4_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k);
+
+/*
+ * The whole MXFP4 (W4A4) layer [ATOM, 6.1 and 8.1-8.2]: route -> permute -> x quantized -> gate_up
+ * (SiLU*mul, h quantized in the epilogue) -> down (fp32) -> combine, all enqueued on `stream`:
+ *   y[t] = sum_s w[t,s] * W2_e(s) Q( silu(W1_e(s) Q(x[t])) * (W3_e(s) Q(x[t])) ),  Q = MX quantization.
+ *   x bf16 [T, H]; router_logits fp32 [T, E]; w13_q [E, 2I, H/2], w13_e [E, 2I, H/32],
+ *   w2_q [E, H, I/2], w2_e [E, H, I/32]; y bf16 [T, H].  Optional routing copies as for moe_ffn_forward.
+ *   workspace: at least moe_ffn_mxfp4_workspace_bytes(T, H, I, E, k) bytes.
+ * Shapes: as moe_ffn_forward (H, I positive multiples of 32).
+ */
+moe_status_t moe_ffn_forward_mxfp4(const uint16_t* x, const float* router_logits, int32_t T, int32_t H, int32_t I,
+                                   int32_t E, int32_t k, const uint8_t* w13_q, const uint8_t* w13_e,
+                                   const uint8_t* w2_q, const uint8_t* w2_e, uint16_t* y, int32_t* topk_ids_out,
+                                   float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

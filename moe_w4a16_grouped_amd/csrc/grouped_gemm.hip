@@ -136,22 +136,6 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x4 (&acc)
   }
 }
 
-// Work order of the tiled kernel.  Workgroup b runs on XCD b % 8 (workgroups are dispatched
-// round-robin over the 8 XCDs, each with its own L2).  XCD x takes the contiguous share
-// [x*n/8, (x+1)*n/8) of the n tiles and runs all N blocks of one tile before the next, so a tile's
-// gathered activation rows are fetched into that XCD's L2 once, and consecutive tiles of one expert
-// find its weights there.  The work list holds 8 * ceil(max_tiles / 8) * nbn slots; slots past the
-// XCD's share are skipped.
-__device__ __forceinline__ bool xcd_tile(long long b, int nbn, int num_tiles, int& tile, int& nb) {
-  const int xcd = (int)(b & 7);
-  const long long j = b >> 3;
-  const int lt = (int)(j / nbn);
-  nb = (int)(j - (long long)lt * nbn);
-  const int t0 = (xcd * num_tiles) >> 3, t1 = ((xcd + 1) * num_tiles) >> 3;
-  tile = t0 + lt;
-  return tile < t1;
-}
-
 // Tile list lookups.  In dense mode (no tile list: the shared expert) tile i is rows
 // [i * BM, min((i + 1) * BM, dense_rows)) of expert 0.
 __device__ __forceinline__ int routed_tile_count(const GemmArgs& p, int bm) {
@@ -332,14 +316,6 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& p0, int tile, int nb,
     if (s0 + u < nks) step(s0 + u, u, false);
 
   store_tile<EPI, OUT_F32, MI, NI>(p, acc, wm * WM, row0, rows, q, ncol, nvalid);
-}
-
-// Launch grids are 2-D: x holds at most kGridX workgroups (a multiple of 8, so with linear index
-// b = y * gridDim.x + x, b % 8 still names the XCD) and y as many rows as the work list needs.
-constexpr unsigned kGridX = 8u << 16;
-
-__device__ __forceinline__ long long linear_block() {
-  return (long long)blockIdx.y * gridDim.x + blockIdx.x;
 }
 
 template <int BM, int BN, int WAVES_M, int PF, int EPI, bool OUT_F32, int LAYOUT>
@@ -684,11 +660,6 @@ __global__ __launch_bounds__(512) void gemm_w4a16_mm(GemmArgs p) {
 static int layout_of(const GemmArgs& a) {
   if (a.packed) return kPacked;
   return ((a.K % kBK) == 0 && (reinterpret_cast<uintptr_t>(a.Ws) % 8) == 0) ? kCanonFull : kCanonGeneric;
-}
-
-static dim3 grid2d(long long total) {
-  if (total <= (long long)kGridX) return dim3((unsigned)total, 1);
-  return dim3(kGridX, (unsigned)((total + kGridX - 1) / kGridX));
 }
 
 static dim3 grid_of(const GemmArgs& a, int bn) {

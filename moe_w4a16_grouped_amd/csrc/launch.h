@@ -64,6 +64,26 @@ struct GemmArgs {
 };
 hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t stream);
 
+// MXFP4 (W4A4) grouped GEMM: activations and weights as E2M1 codes with E8M0 scale bytes per 32 K.
+struct MxGemmArgs {
+  const uint8_t* Aq;        // activation codes [*, K/2]
+  const uint8_t* As;        // activation scale bytes [*, K/32]
+  const int32_t* a_row_of;  // permuted row -> flat index (NULL = identity)
+  int a_row_div;            // activation row = a_row_of[r] / a_row_div
+  const uint8_t* Wq;        // [E, N, K/2]
+  const uint8_t* We;        // [E, N, K/32]
+  int N, K;
+  const int32_t* tiles;     // [max_tiles, 3]
+  const int32_t* num_tiles;
+  int max_tiles;
+  void* C;                  // NONE: fp32 or bf16 [rows, N]; SILU_MUL: h codes [rows, N/4]
+  uint8_t* Cs;              // SILU_MUL: h scale bytes [rows, N/64]
+  int epilogue;             // MOE_EPI_*
+  int out_f32;
+};
+hipError_t launch_grouped_gemm_mx(const MxGemmArgs& a, int block_m, hipStream_t stream);
+hipError_t launch_mx_quant(const uint16_t* x, long long rows, int K, uint8_t* q, uint8_t* s, hipStream_t stream);
+
 hipError_t launch_prepack(const uint8_t* wq, const uint16_t* ws, int E, int N, int K, uint8_t* pq, uint16_t* ps,
                           hipStream_t stream);
 

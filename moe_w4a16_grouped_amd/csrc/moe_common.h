@@ -78,4 +78,35 @@ __device__ __forceinline__ void g2lds16(const void* g, void* lds_wave_base) {
   asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
 }
 
+
+// Launch grids are 2-D: x holds at most kGridX workgroups (a multiple of 8, so with linear index
+// b = y * gridDim.x + x, b % 8 still names the XCD) and y as many rows as the work list needs.
+constexpr unsigned kGridX = 8u << 16;
+
+__device__ __forceinline__ long long linear_block() {
+  return (long long)blockIdx.y * gridDim.x + blockIdx.x;
+}
+
+// Work order of the grouped GEMMs' tile lists.  Workgroup b runs on XCD b % 8 (workgroups are dispatched
+// round-robin over the 8 XCDs, each with its own L2).  XCD x takes the contiguous share
+// [x*n/8, (x+1)*n/8) of the n tiles and runs all N blocks of one tile before the next, so a tile's
+// gathered activation rows are fetched into that XCD's L2 once, and consecutive tiles of one expert
+// find its weights there.  The work list holds 8 * ceil(max_tiles / 8) * nbn slots; slots past the
+// XCD's share are skipped.
+__device__ __forceinline__ bool xcd_tile(long long b, int nbn, int num_tiles, int& tile, int& nb) {
+  const int xcd = (int)(b & 7);
+  const long long j = b >> 3;
+  const int lt = (int)(j / nbn);
+  nb = (int)(j - (long long)lt * nbn);
+  const int t0 = (xcd * num_tiles) >> 3, t1 = ((xcd + 1) * num_tiles) >> 3;
+  tile = t0 + lt;
+  return tile < t1;
+}
+
+// Host side: the 2-D grid for `total` workgroups.
+static inline dim3 grid2d(long long total) {
+  if (total <= (long long)kGridX) return dim3((unsigned)total, 1);
+  return dim3(kGridX, (unsigned)((total + kGridX - 1) / kGridX));
+}
+
 }  // namespace moe

@@ -1,0 +1,328 @@
+// MXFP4 (W4A4) variant of the layer on gfx950's scaled matrix cores.
+//
+// Format (the ATOM page "AMD ATOM推理引擎：如何用分页KV缓存和分段编译实现大模型推理性能翻倍", section
+// "6.1 Linear：按量化类型分派 GEMM", lists per-1x32 MXFP4 with an a4w4 GEMM; section "8.2 量化并非单一
+// 格式，而是一套执行契约" lists dynamic activation quantization as part of a format's contract): weights
+// and activations are E2M1 codes, two per byte with the even K index in the low nibble, with one
+// E8M0 scale byte (2^(byte - 127)) per 32 consecutive K elements.  Activations are quantized on the
+// fly by the OCP MX conversion: per block, X = 2^(floor(log2(amax)) - 2) clamped to E8M0's range
+// (an all-zero block takes 2^-127), elements rounded to the nearest E2M1 value of v / X, ties to
+// even, saturating at 6.
+//
+// The Atlas page ("告别Python堆栈：Atlas用纯Rust重写LLM推理，在GB10上跑赢vLLM", section "编译时内核选择
+// 和W4A16 Grouped GEMM") runs W4A16 because GB10 has no native FP4 matrix instruction; gfx950 has
+// one: v_mfma_scale_f32_16x16x128_f8f6f4 multiplies 16 x 128 by 128 x 16 E2M1 operands and applies
+// one E8M0 scale per lane and 32-element K block in hardware.  Lane l supplies row l % 16 and the
+// 32 K elements [32 (l / 16), +32) (16 bytes) of each operand plus that block's scale byte; the
+// result has the 16 x 16 fp32 layout of the bf16 instruction (checked exactly on the GPU).  So a K
+// step of 128 is one instruction per 16 x 16 block, with no dequantization and no scale arithmetic
+// in software.
+#include "launch.h"
+#include "moe_common.h"
+
+namespace moe {
+
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+// Shared exponent of a block from its largest magnitude: floor(log2(amax)) - 2, clamped to E8M0's
+// range; zero and subnormal maxima give -127.
+__device__ __forceinline__ int mx_block_exp(float amax) {
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+  if (ef == 0) return -127;
+  return max(-127, min(127, ef - 129));
+}
+
+// Four E2M1 codes of v / 2^e into byte J of w (hardware conversion: nearest, ties to even,
+// saturating; scaling by a power of two is exact).
+template <int J>
+__device__ __forceinline__ uint32_t mx_pack2(uint32_t w, float a, float b, int e) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, ldexpf(a, -e), ldexpf(b, -e), 1.0f, J);
+}
+
+// 32 values -> 16 bytes of codes (given the block exponent).
+__device__ __forceinline__ u32x4 mx_encode32(const float (&v)[32], int e) {
+  u32x4 c;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t w = 0;
+    w = mx_pack2<0>(w, v[8 * d + 0], v[8 * d + 1], e);
+    w = mx_pack2<1>(w, v[8 * d + 2], v[8 * d + 3], e);
+    w = mx_pack2<2>(w, v[8 * d + 4], v[8 * d + 5], e);
+    w = mx_pack2<3>(w, v[8 * d + 6], v[8 * d + 7], e);
+    c[d] = w;
+  }
+  return c;
+}
+
+// ---------------------------------------------------------------------------------------------------
+// Activation quantization: one thread per 32-element block of a row-major bf16 matrix whose rows
+// are whole blocks, so block i sits at element 32 i of x, byte 16 i of the codes and byte i of the
+// scales.  Four 16-byte loads and one 16-byte store per thread.
+__global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restrict__ x, long long nblocks,
+                                                       uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nblocks) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + i * 32);
+  float v[32];
+  float amax = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const u32x4 w = src[d];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * d + 2 * j] = __uint_as_float(w[j] << 16);
+      v[8 * d + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      amax = fmaxf(amax, fmaxf(fabsf(v[8 * d + 2 * j]), fabsf(v[8 * d + 2 * j + 1])));
+    }
+  }
+  const int e = mx_block_exp(amax);
+  *reinterpret_cast<u32x4*>(q + i * 16) = mx_encode32(v, e);
+  s[i] = (uint8_t)(e + 127);
+}
+
+hipError_t launch_mx_quant(const uint16_t* x, long long rows, int K, uint8_t* q, uint8_t* s, hipStream_t stream) {
+  const long long nblocks = rows * (K / 32);
+  if (nblocks <= 0) return hipSuccess;
+  mx_quant_kernel<<<dim3((unsigned)((nblocks + 255) / 256)), 256, 0, stream>>>(x, nblocks, q, s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------------
+// Grouped MX GEMM over the device-side tile list (the same list as the W4A16 path).  A workgroup of
+// four waves computes a BM x BN tile; the waves split K KW ways and N 4/KW ways.  Every wave loads
+// its operand fragments straight into a register ring PF K steps deep (16 bytes of codes and one
+// scale byte per lane and 16-row block, activation rows gathered through a_row_of), so the main
+// loop has no LDS traffic and no barrier; K-split partials are added in LDS in wave order.
+// Epilogues: NONE stores fp32 or bf16 rows; SILU_MUL forms h = silu(gate) * up in fp32 (gate rows
+// [0, N/2), up rows [N/2, N) of the weight), gathers the tile's h in LDS and quantizes each
+// 32-column block of each row to MXFP4 (codes [rows, N/4], scale bytes [rows, N/64]) for the next
+// projection.
+template <int BM, int BN, int KW, int PF, int EPI, bool OUT_F32>
+__global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
+  constexpr int WNS = 4 / KW;             // waves along N
+  constexpr int WN = BN / WNS;            // columns per wave
+  constexpr int MI = BM / 16, NI = WN / 16;
+  constexpr int NS = PF + 1;
+  constexpr int HC = BN / 2;              // h columns of a SILU_MUL tile
+  constexpr int HLD = HC + 4;             // padded LDS row of the h tile (floats)
+  static_assert(KW * WNS == 4 && NI >= 1 && MI >= 1, "tile shape");
+  static_assert(EPI != MOE_EPI_SILU_MUL || (NI % 2 == 0 && HC % 32 == 0), "SiLU*mul tile shape");
+  __shared__ __attribute__((aligned(16))) float red[KW > 1 ? WNS * (KW - 1) * 64 * MI * NI * 4 : 1];
+  __shared__ __attribute__((aligned(16))) float htile[EPI == MOE_EPI_SILU_MUL ? BM * HLD : 1];
+
+  const int N = p.N, K = p.K;
+  const int nbn = EPI == MOE_EPI_SILU_MUL ? (N / 2 + HC - 1) / HC : (N + BN - 1) / BN;
+  int tile, nb;
+  if (!xcd_tile(linear_block(), nbn, *p.num_tiles, tile, nb)) return;
+  const int e = p.tiles[3 * tile], row0 = p.tiles[3 * tile + 1], rows = p.tiles[3 * tile + 2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wk = wave % KW, wn = wave / KW;
+  const int l16 = lane & 15, q = lane >> 4;
+  const int nks = (K + 127) / 128;
+  const int per = (nks + KW - 1) / KW;
+  const int s_begin = min(nks, wk * per), s_end = min(nks, s_begin + per);
+  const int KB = K / 2, KS = K / 32;  // bytes of codes and of scales per row
+
+  // activation fragments: row mi * 16 + l16 of the tile (padding rows read the first row)
+  const uint8_t* aq[MI];
+  const uint8_t* as[MI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int i = mi * 16 + l16;
+    const int r = row0 + (i < rows ? i : 0);
+    const int ar = p.a_row_of ? p.a_row_of[r] / p.a_row_div : r;
+    aq[mi] = p.Aq + (size_t)ar * KB + q * 16;
+    as[mi] = p.As + (size_t)ar * KS + q;
+  }
+  // weight fragments: SILU_MUL pairs gate block j with up block j (rows N/2 + j)
+  const uint8_t* wq[NI];
+  const uint8_t* ws[NI];
+  int ncol[NI];
+  bool nvalid[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    int n;
+    if (EPI == MOE_EPI_SILU_MUL) {
+      const int j = nb * HC + wn * (WN / 2) + (ni % (NI / 2)) * 16 + l16;
+      nvalid[ni] = j < N / 2;
+      ncol[ni] = j;
+      n = ni < NI / 2 ? j : N / 2 + j;
+    } else {
+      n = nb * BN + wn * WN + ni * 16 + l16;
+      nvalid[ni] = n < N;
+      ncol[ni] = n;
+    }
+    if (!nvalid[ni]) n = 0;
+    wq[ni] = p.Wq + ((size_t)e * N + n) * KB + q * 16;
+    ws[ni] = p.We + ((size_t)e * N + n) * KS + q;
+  }
+
+  f32x4 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 areg[NS][MI], breg[NS][NI];
+  uint32_t asc[NS][MI], bsc[NS][NI];
+  auto load_step = [&](int s, int u) {
+    s = min(s, s_end - 1);  // prefetches past this wave's range re-read its last step (unused)
+    // K tail: a quarter past K reads the row's last block and its activation codes are zeroed
+    const bool qv = s * 128 + 32 * q < K;
+    const int cb = qv ? s * 64 : (K - 32 - 32 * q) / 2;  // code byte offset of this lane's block
+    const int sb = qv ? s * 4 : (K / 32 - 1 - q);        // scale byte offset
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      breg[u][ni] = *reinterpret_cast<const u32x4*>(wq[ni] + cb);
+      bsc[u][ni] = ws[ni][sb];
+    }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(aq[mi] + cb);
+      areg[u][mi] = qv ? a : u32x4{0u, 0u, 0u, 0u};
+      asc[u][mi] = as[mi][sb];
+    }
+  };
+  auto compute_step = [&](int u) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const u32x4 a = areg[u][mi];
+      const i32x8 a8 = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const u32x4 b = breg[u][ni];
+        const i32x8 b8 = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[mi][ni], 4, 4, 0, (int)asc[u][mi],
+                                                                        0, (int)bsc[u][ni]);
+      }
+    }
+  };
+
+  if (s_end > s_begin) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) load_step(s_begin + u, u);
+    int s0 = s_begin;
+    for (; s0 + NS <= s_end; s0 += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(s0 + u + PF, (u + PF) % NS);
+        compute_step(u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u)
+      if (s0 + u < s_end) compute_step(u);
+  }
+
+  // K-split partials, added in wave order by the first wave of each N group
+  constexpr int PER = MI * NI * 4;
+  if constexpr (KW > 1) {
+    if (wk > 0) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            red[(((wn * (KW - 1) + wk - 1) * 64) + lane) * PER + (mi * NI + ni) * 4 + r] = acc[mi][ni][r];
+    }
+    __syncthreads();
+    if (wk == 0) {
+#pragma unroll
+      for (int w = 0; w < KW - 1; ++w)
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[mi][ni][r] += red[(((wn * (KW - 1) + w) * 64) + lane) * PER + (mi * NI + ni) * 4 + r];
+    }
+  }
+  const bool owner = KW == 1 || wk == 0;
+
+  if constexpr (EPI == MOE_EPI_SILU_MUL) {
+    if (owner) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int ni = 0; ni < NI / 2; ++ni) {
+            const float g = acc[mi][ni][r], u = acc[mi][ni + NI / 2][r];
+            htile[(mi * 16 + 4 * q + r) * HLD + wn * (WN / 2) + ni * 16 + l16] = silu_f32(g) * u;
+          }
+    }
+    __syncthreads();
+    // one thread per (row, 32-column block) of h
+    constexpr int NB = HC / 32;
+    for (int t = tid; t < BM * NB; t += 256) {
+      const int row = t / NB, blk = t % NB;
+      const int hcol = nb * HC + blk * 32;
+      if (row >= rows || hcol >= N / 2) continue;
+      float v[32];
+      float amax = 0.f;
+      const float4* src = reinterpret_cast<const float4*>(htile + row * HLD + blk * 32);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const float4 f = src[d];
+        v[4 * d] = f.x;
+        v[4 * d + 1] = f.y;
+        v[4 * d + 2] = f.z;
+        v[4 * d + 3] = f.w;
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
+      }
+      const int ex = mx_block_exp(amax);
+      const size_t orow = (size_t)(row0 + row);
+      uint8_t* C = static_cast<uint8_t*>(p.C);
+      *reinterpret_cast<u32x4*>(C + orow * (N / 4) + hcol / 2) = mx_encode32(v, ex);
+      p.Cs[orow * (N / 64) + hcol / 32] = (uint8_t)(ex + 127);
+    }
+  } else {
+    if (!owner) return;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = mi * 16 + 4 * q + r;
+        if (row >= rows) continue;
+        const size_t orow = (size_t)(row0 + row);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          if (!nvalid[ni]) continue;
+          if (OUT_F32) static_cast<float*>(p.C)[orow * N + ncol[ni]] = acc[mi][ni][r];
+          else static_cast<uint16_t*>(p.C)[orow * N + ncol[ni]] = f32_to_bf16_bits(acc[mi][ni][r]);
+        }
+      }
+  }
+}
+
+template <int BM, int BN, int KW, int PF>
+static hipError_t launch_mx_cfg(const MxGemmArgs& a, hipStream_t s) {
+  const int ncols = a.epilogue == MOE_EPI_SILU_MUL ? a.N / 2 : a.N;
+  const int bcols = a.epilogue == MOE_EPI_SILU_MUL ? BN / 2 : BN;
+  const dim3 grid = grid2d(8LL * ((a.max_tiles + 7) / 8) * ((ncols + bcols - 1) / bcols));
+  if (a.epilogue == MOE_EPI_SILU_MUL) gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_SILU_MUL, false><<<grid, 256, 0, s>>>(a);
+  else if (a.out_f32) gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, true><<<grid, 256, 0, s>>>(a);
+  else gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, false><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// Tile lists of at most this capacity (16-row tiles) split K four ways (decode).
+constexpr int kMxSplitKMaxTiles = 32;
+
+hipError_t launch_grouped_gemm_mx(const MxGemmArgs& a, int block_m, hipStream_t stream) {
+  if (a.max_tiles <= 0) return hipSuccess;
+  switch (block_m) {
+    case 16:
+      if (a.max_tiles <= kMxSplitKMaxTiles) return launch_mx_cfg<16, 64, 4, 2>(a, stream);
+      return launch_mx_cfg<16, 128, 1, 2>(a, stream);
+    case 32: return launch_mx_cfg<32, 128, 1, 2>(a, stream);
+    default: return launch_mx_cfg<64, 128, 1, 2>(a, stream);
+  }
+}
+
+}  // namespace moe

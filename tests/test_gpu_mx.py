@@ -1,0 +1,206 @@
+"""GPU parity of the MXFP4 (W4A4) variant against the CPU oracle.
+
+The activation quantizer is bit-exact (the block exponent and every rounding decision are made on
+values that are exact in fp32 and fp64 alike).  Grouped GEMM outputs (fp32) are checked per element
+within the rounding bound of fp32 accumulation.  The fused gate_up epilogue quantizes h = silu(g)*u
+computed in fp32, while the oracle quantizes its fp64 h: codes agree except where h lies within
+fp32 rounding of a rounding boundary, so codes are compared by count and every element is checked to
+be within one E2M1 step.  Layer outputs use the layer tolerance: max|gpu-ref| <= 3e-2 * rms(ref) and
+mean relative error <= 5e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU-only hosts, never run there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import moe_w4a16_grouped_amd as moe  # noqa: E402  (loads the HIP library; fails loudly if missing)
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+_E2M1 = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6])
+
+
+def _codes(q):
+    q = np.asarray(q, np.uint8)
+    out = np.empty(q.shape[:-1] + (q.shape[-1] * 2,), np.int64)
+    out[..., 0::2] = q & 0xF
+    out[..., 1::2] = q >> 4
+    return out
+
+
+def _deq(q, s):
+    return _E2M1[_codes(q)] * np.repeat(np.exp2(np.asarray(s, np.float64) - 127.0), 32, axis=-1)
+
+
+class MXDevice:
+    def __init__(self, inp):
+        self.inp = inp
+        self.x = gu.dev_bf16(inp.x)
+        self.logits = gu.dev(inp.logits)
+        self.w13_q, self.w13_e = gu.dev(inp.w13_q), gu.dev(inp.w13_e)
+        self.w2_q, self.w2_e = gu.dev(inp.w2_q), gu.dev(inp.w2_e)
+
+
+# ---------------------------------------------------------------------------------------------------
+# activation quantization
+
+@pytest.mark.parametrize("rows,K", [(1, 32), (7, 96), (33, 2048), (300, 4096)])
+def test_mx_quantize_bit_exact(rows, K):
+    rng = np.random.default_rng(rows + K)
+    v = rng.standard_normal((rows, K)).astype(np.float32) * np.exp2(rng.integers(-30, 30, (rows, 1))).astype(np.float32)
+    v[0, :32] = 0.0                                    # all-zero block
+    if K >= 64:
+        v[0, 32:64] = [0.25, -0.75, 1.25, 3.5, 5.0, -2.5, 7.0, 0.5] * 4   # ties and saturation at X = 1
+    bits = mi.f32_to_bf16_bits(v)
+    q, s = moe.moe_mx_quantize(gu.dev_bf16(bits))
+    torch.cuda.synchronize()
+    rq, rs = oracle.mx_quantize(mi.bf16_bits_to_f32(bits).astype(np.float64))
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+
+
+# ---------------------------------------------------------------------------------------------------
+# grouped GEMM
+
+def _routing(T, E, k, bm, seed):
+    rng = np.random.default_rng(seed)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    return ids, oracle.align(ids, E, bm)
+
+
+def _mx_operands(rows, N, K, E, seed):
+    rng = np.random.default_rng(seed)
+    Aq = rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+    As = rng.integers(122, 130, (rows, K // 32), dtype=np.uint8)
+    Wq = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    We = rng.integers(118, 123, (E, N, K // 32), dtype=np.uint8)
+    return Aq, As, Wq, We
+
+
+# (T, E, k, bm): few tiles take the K-split kernel, more tiles the N-split one
+GEMM_CASES = [(3, 8, 2, 16), (40, 16, 4, 16), (90, 12, 3, 32), (300, 8, 2, 64)]
+
+
+@pytest.mark.parametrize("T,E,k,bm", GEMM_CASES)
+@pytest.mark.parametrize("N,K", [(256, 2048), (200, 160), (48, 96)])
+def test_grouped_gemm_mxfp4_plain(T, E, k, bm, N, K):
+    ids, al = _routing(T, E, k, bm, seed=T * 7 + N)
+    R = T * k
+    Aq, As, Wq, We = _mx_operands(R, N, K, E, seed=K + bm)
+    tiles = gu.dev(np.ascontiguousarray(al["tiles"].astype(np.int32)))
+    nt = gu.dev(np.array([al["num_tiles"]], np.int32))
+    C = moe.moe_grouped_gemm_mxfp4(gu.dev(Aq), gu.dev(As), None, 1, gu.dev(Wq), gu.dev(We), tiles, al["num_tiles"], nt,
+                                   bm, moe.MOE_EPI_NONE, R)
+    torch.cuda.synchronize()
+    got = C.cpu().numpy().astype(np.float64)
+    ref = oracle.grouped_proj_mx(Aq, As, None, 1, Wq, We, al["offsets"])
+    ref_abs = oracle.grouped_proj_mx(Aq & 0x77, As, None, 1, Wq & 0x77, We, al["offsets"])
+    # fp32 accumulation: at most (64 + K/32) roundings of 2^-24 relative to the sum of |terms|
+    assert np.all(np.abs(got - ref) <= (64 + K / 32) * 2.0 ** -24 * ref_abs + 1e-30)
+
+
+@pytest.mark.parametrize("T,E,k,bm", GEMM_CASES)
+@pytest.mark.parametrize("I,K", [(128, 2048), (96, 160)])
+def test_grouped_gemm_mxfp4_silu_quantized_h(T, E, k, bm, I, K):
+    ids, al = _routing(T, E, k, bm, seed=T + I)
+    R = T * k
+    Aq, _, Wq, We = _mx_operands(T, 2 * I, K, E, seed=I + bm)
+    As = np.random.default_rng(1).integers(124, 128, (T, K // 32), dtype=np.uint8)
+    tiles = gu.dev(np.ascontiguousarray(al["tiles"].astype(np.int32)))
+    nt = gu.dev(np.array([al["num_tiles"]], np.int32))
+    sorted_ids = gu.dev(al["sorted_ids"].astype(np.int32))
+    hq, hs = moe.moe_grouped_gemm_mxfp4(gu.dev(Aq), gu.dev(As), sorted_ids, k, gu.dev(Wq), gu.dev(We), tiles,
+                                        al["num_tiles"], nt, bm, moe.MOE_EPI_SILU_MUL, R)
+    torch.cuda.synchronize()
+    h_ref = oracle.grouped_proj_mx(Aq, As, al["sorted_ids"], k, Wq, We, al["offsets"], silu_mul=True)
+    rq, rs = oracle.mx_quantize(h_ref)
+    gq, gs = hq.cpu().numpy(), hs.cpu().numpy()
+    scale_diff = np.mean(gs != rs)
+    code_diff = np.mean(_codes(gq) != _codes(rq))
+    _log(f"  h codes differing {code_diff:.2e}, scales differing {scale_diff:.2e}")
+    assert scale_diff <= 1e-3 and code_diff <= 1e-3
+    # every element within one E2M1 step (of the larger block scale) of the oracle's
+    step = 2.0 * np.repeat(np.exp2(np.maximum(gs, rs).astype(np.float64) - 127.0), 32, axis=-1)
+    assert np.all(np.abs(_deq(gq, gs) - _deq(rq, rs)) <= step)
+
+
+# ---------------------------------------------------------------------------------------------------
+# whole layer
+
+def _forward(d, wl):
+    y = torch.full((wl.T, wl.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ids = torch.full((wl.T, wl.k), -7, dtype=torch.int32, device="cuda")
+    ws = torch.full((max(moe.moe_ffn_mxfp4_workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.k), 256),), 0xFF,
+                    dtype=torch.uint8, device="cuda")
+    moe.moe_ffn_forward_mxfp4(d.x, d.logits, d.w13_q, d.w13_e, d.w2_q, d.w2_e, wl.k, y=y, topk_ids_out=ids,
+                              workspace=ws)
+    torch.cuda.synchronize()
+    return y, ids
+
+
+def _sample(T, n, seed=99):
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    rest = rng.choice(np.arange(8, T - 1), n - 9, replace=False)
+    return np.sort(np.concatenate([np.arange(8), rest, [T - 1]]))
+
+
+MX_CASES = [("tiny", 16), ("dec1", 1), ("dec8", 8), ("dec64", 24), ("pre800", 40), ("big4096", 12),
+            ("skew8192", 24)]
+
+
+@pytest.mark.parametrize("name,nsample", MX_CASES)
+def test_ffn_forward_mxfp4_matches_oracle(name, nsample):
+    wl = mi.WORKLOADS[name]
+    _log(f"mxfp4 layer {name}: T={wl.T} E={wl.E} k={wl.k} H={wl.H} I={wl.I}")
+    inp = mi.make_mx_inputs(wl)
+    d = MXDevice(inp)
+    y, ids = _forward(d, wl)
+    np.testing.assert_array_equal(ids.cpu().numpy(), oracle.route(inp.logits, wl.k)[0])
+    yh = gu.host_bf16_to_f64(y)
+    assert np.all(np.isfinite(yh)), "output not fully written"
+    tok = _sample(wl.T, nsample)
+    r = gu.assert_within_tolerance(yh[tok], oracle.moe_ffn_mx(inp, tokens=tok), name)
+    _log(f"  {name}: {r}")
+
+
+@pytest.mark.parametrize("wl", [
+    mi.custom("mx_one_expert", 3, 1, 1, 256, 128, seed=5),
+    mi.custom("mx_ragged", 37, 16, 4, 160, 96, seed=6),
+    mi.custom("mx_k_eq_E", 20, 6, 6, 128, 64, seed=7),
+    mi.custom("mx_many_experts", 40, 1024, 8, 128, 64, seed=8),
+    mi.custom("mx_t1_big_k", 1, 64, 32, 256, 256, seed=9),
+    mi.custom("mx_hot", 300, 32, 4, 256, 128, seed=12),
+])
+def test_ffn_forward_mxfp4_edges(wl):
+    inp = mi.make_mx_inputs(wl)
+    if wl.name == "mx_hot":
+        inp.logits[:, 0] += 50.0  # every token's slot 0 on expert 0
+    d = MXDevice(inp)
+    y, ids = _forward(d, wl)
+    np.testing.assert_array_equal(ids.cpu().numpy(), oracle.route(inp.logits, wl.k)[0])
+    gu.assert_within_tolerance(gu.host_bf16_to_f64(y), oracle.moe_ffn_mx(inp), wl.name)
+
+
+def test_ffn_forward_mxfp4_deterministic_and_empty():
+    wl = mi.custom("mx_det", 200, 32, 4, 512, 256, seed=13)
+    d = MXDevice(mi.make_mx_inputs(wl))
+    a = _forward(d, wl)[0].view(torch.int16).cpu().numpy()
+    b = _forward(d, wl)[0].view(torch.int16).cpu().numpy()
+    np.testing.assert_array_equal(a, b)
+    empty = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda")
+    y = moe.moe_ffn_forward_mxfp4(empty, torch.empty((0, 32), dtype=torch.float32, device="cuda"), d.w13_q, d.w13_e,
+                                  d.w2_q, d.w2_e, 4)
+    assert y.shape == (0, 512)
