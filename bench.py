@@ -29,6 +29,7 @@ import moe_inputs as mi
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense fp4 MFMA
 RIDGE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
 PAGES_US_800 = 5580.0  # Atlas page, GB10: W4A16 grouped-GEMM MoE layer at 800 tokens / 256 experts
 METRIC = "MoE layer µs, TFLOP/s and weight GB/s (% roofline) at 800 tok/256 experts"
@@ -226,6 +227,182 @@ def time_block(moe, wl, inp, x, copies, layout, args):
     return out
 
 
+def time_steps(step, L, args):
+    """K steps timed as eager launches and as one replay of a HIP graph of the same K steps."""
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    eager_ms = ev0.elapsed_time(ev1) / args.steps
+    graph_ms = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(min(L, args.steps)):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        graph.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        graph_ms = ev0.elapsed_time(ev1) / args.steps
+    return eager_ms, graph_ms
+
+
+def cpu_baseline_mx(inp, target_s: float):
+    """The MXFP4 oracle timed like cpu_baseline."""
+    import oracle
+
+    wl = inp.wl
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(1)
+    n = min(wl.T, cores)
+    tok = np.sort(rng.choice(wl.T, n, replace=False))
+    t0 = time.perf_counter()
+    oracle.moe_ffn_mx(inp, tokens=tok)
+    dt = time.perf_counter() - t0
+    if dt < target_s / 2 and n < wl.T:
+        n2 = int(min(wl.T, max(n, n * (target_s / max(dt, 1e-3)))))
+        tok = np.sort(rng.choice(wl.T, n2, replace=False))
+        t0 = time.perf_counter()
+        oracle.moe_ffn_mx(inp, tokens=tok)
+        dt = time.perf_counter() - t0
+        n = n2
+    return {"value": round(dt / n * wl.T * 1e6, 1), "unit": "us/layer", "cores": min(cores, n), "kind": "oracle",
+            "sample": f"{n} of {wl.T} tokens of the same workload ({dt:.1f} s wall), scaled to {wl.T} tokens"}
+
+
+def run_mxfp4(args):
+    """The MXFP4 (W4A4) layer: x and h quantized per 1x32 on the fly, E2M1 x E2M1 products on the
+    scaled FP4 matrix instruction.  Same workload shapes, rotation and timing as the W4A16 layer."""
+    import moe_w4a16_grouped_amd as moe
+
+    wl = mi.WORKLOADS[args.workload]
+    T, E, k, H, I = wl.T, wl.E, wl.k, wl.H, wl.I
+    R = T * k
+    log(f"bench: MXFP4 workload {wl.name} T={T} E={E} k={k} H={H} I={I}; generating inputs")
+    inp = mi.make_mx_inputs(wl)
+    x, logits = dev_bf16(inp.x), dev(inp.logits)
+    ids0, _ = moe.moe_route_topk(logits, k)
+    touched = int(torch.unique(ids0).numel())
+    bpe = mi.mx_weight_bytes_per_expert(H, I)
+    L = args.copies or max(1, math.ceil((1 << 30) / (touched * bpe)))
+    w0 = (dev(inp.w13_q), dev(inp.w13_e), dev(inp.w2_q), dev(inp.w2_e))
+    copies = [w0] + [tuple(t.clone() for t in w0) for _ in range(L - 1)]
+    layout = moe.MOE_LAYOUT_PACKED if args.layout == "packed" else moe.MOE_LAYOUT_CANONICAL
+    if layout == moe.MOE_LAYOUT_PACKED:
+        copies = [moe.moe_mx_prepack(a, b) + moe.moe_mx_prepack(c, d) for (a, b, c, d) in copies]
+        torch.cuda.synchronize()
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_ffn_mxfp4_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device="cuda")
+    log(f"bench: {L} weight copies ({touched} of {E} experts touched); warmup {args.warmup}, steps {args.steps}")
+
+    def step(i):
+        q13, e13, q2, e2 = copies[i % L]
+        moe.moe_ffn_forward_mxfp4(x, logits, q13, e13, q2, e2, k, y=y, workspace=ws, weight_layout=layout)
+
+    eager_ms, graph_ms = time_steps(step, L, args)
+    ms = eager_ms if graph_ms is None else min(eager_ms, graph_ms)
+    log(f"bench: MXFP4 layer eager {eager_ms * 1e3:.1f} us, graph {graph_ms * 1e3 if graph_ms else 0:.1f} us")
+
+    # per-kernel pass through the separate entry points
+    bm = moe.moe_ffn_mxfp4_block_m(T, E, k)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    tiled = layout == moe.MOE_LAYOUT_PACKED
+    act = moe.MOE_ACT_TILED if tiled else moe.MOE_ACT_ROWS
+    rows_cap = max(T, R, moe.moe_max_tiles(T, k, E, bm) * bm)
+    xq = torch.empty((rows_cap, H // 2), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((rows_cap, H // 32), dtype=torch.uint8, device="cuda")
+    hq = torch.empty((rows_cap, I // 2), dtype=torch.uint8, device="cuda")
+    hs = torch.empty((rows_cap, I // 32), dtype=torch.uint8, device="cuda")
+    O = torch.empty((R, H), dtype=torch.float32, device="cuda")
+    names = ["route", "align", "quant_x", "gate_up", "down", "combine"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    al = None
+    for i in range(args.warmup + args.steps):
+        q13, e13, q2, e2 = copies[i % L]
+        e = evs[i - args.warmup] if i >= args.warmup else None
+        if e: e[0].record()
+        moe.moe_route_topk(logits, k, ids, wts)
+        if e: e[1].record()
+        al = moe.moe_align(ids, E, bm)
+        if e: e[2].record()
+        if tiled:
+            moe.moe_mx_quantize_tiles(x, al["sorted_ids"], k, al["tiles"], al["max_tiles"], al["num_tiles"], bm, xq, xs)
+        else:
+            moe.moe_mx_quantize(x, xq[:T], xs[:T])
+        if e: e[3].record()
+        moe.moe_grouped_gemm_mxfp4(xq, xs, al["sorted_ids"], k, q13, e13, al["tiles"], al["max_tiles"],
+                                   al["num_tiles"], bm, moe.MOE_EPI_SILU_MUL, R, C=hq, Cs=hs, weight_layout=layout,
+                                   act_layout=act)
+        if e: e[4].record()
+        moe.moe_grouped_gemm_mxfp4(hq, hs, None, 1, q2, e2, al["tiles"], al["max_tiles"], al["num_tiles"], bm,
+                                   moe.MOE_EPI_NONE, R, moe.MOE_OUT_F32, C=O, weight_layout=layout, act_layout=act)
+        if e: e[5].record()
+        moe.moe_combine(O, al["inv_perm"], wts, y=y)
+        if e: e[6].record()
+    torch.cuda.synchronize()
+    kern_us = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in evs]) * 1e3) for j, n in enumerate(names)}
+    log("bench: per-kernel us (events): " + ", ".join(f"{n}={v:.1f}" for n, v in kern_us.items()))
+
+    us = ms * 1e3
+    flops = 6.0 * R * H * I
+    weight_bytes = touched * bpe
+    g13 = 2 * I * H // 2 + 2 * I * (H // 32)
+    gu_bytes = touched * g13 + T * H // 2 + T * H // 32 + R * I // 2 + R * I // 32
+    gu_flops = 4.0 * R * H * I
+    gu_us = kern_us["gate_up"]
+    ridge = MFMA_FP4_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if gu_flops / gu_bytes < ridge:
+        bound, achieved, peak, unit = "hbm", gu_bytes / (gu_us * 1e-6) / 1e9, HBM_PEAK_GBPS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", gu_flops / (gu_us * 1e-6) / 1e12, MFMA_FP4_PEAK_TFLOPS, "TFLOP/s"
+    result = {
+        "metric": METRIC,
+        "value": round(us, 2),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4 (E2M1 x E2M1, E8M0 per-32 scales; fp32 accumulation)",
+        "data": "synthetic (seeded; E2M1 codes uniform, E8M0 scales 2^-8..2^-6, x and logits N(0,1))",
+        "config": {"workload": f"{wl.name} MXFP4 (W4A4): {T} tokens, {E} experts top-{k}, hidden {H}, "
+                               f"intermediate {I}", "method": "mxfp4", "tokens": T, "experts": E, "top_k": k,
+                   "hidden": H, "intermediate": I, "weight_copies": L, "touched_experts": touched,
+                   "weight_layout": args.layout},
+        "tflops": round(flops / (us * 1e-6) / 1e12, 3),
+        "weight_gbps": round(weight_bytes / (us * 1e-6) / 1e9, 1),
+        "timing": {"eager_us": round(eager_ms * 1e3, 2), "graph_us": None if graph_ms is None else round(graph_ms * 1e3, 2),
+                   "value_from": "graph" if graph_ms is not None and graph_ms <= eager_ms else "eager"},
+        "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
+        "roofline": {"kernel": "gemm_mx_kernel (gate_up + SiLU*mul + h quantization)", "bound": bound,
+                     "achieved": round(achieved, 2), "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": None, "algorithmic_bytes": gu_bytes, "algorithmic_flops": gu_flops},
+    }
+    if not args.no_cpu_baseline:
+        log(f"bench: timing the MXFP4 CPU oracle on a token sample (~{args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline_mx(inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +417,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="run only the counter-calibration copy")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
     ap.add_argument("--calibrate", action="store_true", help="measure copy bandwidth and a vendor bf16 GEMM rate only")
+    ap.add_argument("--method", choices=["w4a16", "mxfp4"], default="w4a16",
+                    help="w4a16: bf16 activations, bf16 group scales (the default); mxfp4: W4A4 with E8M0 scales")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the whole-block timing (router gate + shared expert + routed layer)")
     args = ap.parse_args()
@@ -253,6 +432,10 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.method == "mxfp4":
+        run_mxfp4(args)
+        return
 
     import moe_w4a16_grouped_amd as moe
 

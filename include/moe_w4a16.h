@@ -290,6 +290,33 @@ moe_status_t moe_ffn_block_forward(const uint16_t* x, const uint16_t* w_router, 
  * Shapes: 0 <= rows < 2^26, K a positive multiple of 32.  x and q 16-byte aligned. */
 moe_status_t moe_mx_quantize(const uint16_t* x, int32_t rows, int32_t K, uint8_t* q, uint8_t* s, void* stream);
 
+/* Activation layouts of the MXFP4 GEMM. */
+#define MOE_ACT_ROWS 0   /* row-major [*, K/2] codes and [*, K/32] scales, rows gathered through a_row_of */
+#define MOE_ACT_TILED 1  /* tile-blocked: the tile list's rows, tile by tile, in the packed block order */
+
+/*
+ * Packed MXFP4 weight layout (same bytes, MFMA lane order): the [E, N, K] matrix cut into blocks of
+ * 16 rows x 128 K elements ordered (expert, row block, K block), K fastest; per block 1024 bytes of
+ * codes (bytes [16l, 16l+16) = row l % 16, K elements [32 (l / 16), +32)) and, separately, 64 scale
+ * bytes (byte l = the same row and 32-block).  w_q [E, N, K/2], w_e [E, N, K/32] canonical in,
+ * packed_q / packed_e of the same sizes out.  Needs N % 16 == 0, K % 128 == 0 [ATOM, 8.2: weight
+ * pre-rearrangement is part of a quantized format's contract].
+ */
+moe_status_t moe_mx_prepack(const uint8_t* w_q, const uint8_t* w_e, int32_t E, int32_t N, int32_t K, uint8_t* packed_q,
+                            uint8_t* packed_e, void* stream);
+
+/*
+ * x quantized (as moe_mx_quantize) and gathered into the tile-blocked activation layout of a tile
+ * list: tile t's rows r = tiles[t].row0 + i (i < tiles[t].rows), source row a_row_of[r] / a_row_div
+ * (or r), padded to block_m rows; blocks of 16 rows x 128 K ordered (tile, 16-row group, K block) with
+ * K fastest, each 1024 code bytes in the packed lane order plus 64 scale bytes.  Padding rows and
+ * tiles past *num_tiles are left unwritten.  q: max_tiles * block_m * K/2 bytes, s: max_tiles *
+ * block_m * K/32 bytes.  Needs K % 128 == 0, block_m 16, 32 or 64.
+ */
+moe_status_t moe_mx_quantize_tiles(const uint16_t* x, int32_t T, int32_t K, const int32_t* a_row_of,
+                                  int32_t a_row_div, const int32_t* tiles, int32_t max_tiles, const int32_t* num_tiles,
+                                  int32_t block_m, uint8_t* q, uint8_t* s, void* stream);
+
 /*
  * Grouped MXFP4 GEMM over the tile list of moe_align [Atlas, 编译时内核选择和W4A16 Grouped GEMM: one
  * launch over all experts]: for each permuted row r of expert e, activation row
@@ -298,10 +325,16 @@ moe_status_t moe_mx_quantize(const uint16_t* x, int32_t rows, int32_t K, uint8_t
  *   epilogue NONE:     C [rows, N] fp32 or bf16 (out_dtype); Cs unused.
  *   epilogue SILU_MUL: h[r, j] = silu(G[r, j]) * G[r, N/2 + j] in fp32, then quantized per 32 columns:
  *                      C = codes [rows, N/4], Cs = scale bytes [rows, N/64] (out_dtype ignored).
- * block_m 16, 32 or 64 (the tile height moe_align used).  K % 32 == 0; SILU_MUL needs N % 64 == 0.
+ * weight_layout: MOE_LAYOUT_CANONICAL or MOE_LAYOUT_PACKED (moe_mx_prepack; needs N % 16 == 0 and
+ * K % 128 == 0).  act_layout: MOE_ACT_ROWS, or MOE_ACT_TILED (packed weights only; A from
+ * moe_mx_quantize_tiles or a previous SILU_MUL output, a_row_of unused; a SILU_MUL output is then
+ * written tile-blocked too, for K = N/2 of the next projection, which needs N/2 % 128 == 0).
+ * Results are bit-identical across layouts.  block_m 16, 32 or 64 (the tile height moe_align used).
+ * K % 32 == 0; SILU_MUL needs N % 64 == 0.
  */
 moe_status_t moe_grouped_gemm_mxfp4(const uint8_t* Aq, const uint8_t* As, const int32_t* a_row_of, int32_t a_row_div,
-                                    const uint8_t* Wq, const uint8_t* We, int32_t E, int32_t N, int32_t K,
+                                    const uint8_t* Wq, const uint8_t* We, int32_t weight_layout, int32_t act_layout,
+                                    int32_t E, int32_t N, int32_t K,
                                     const int32_t* tiles, int32_t max_tiles, const int32_t* num_tiles, int32_t block_m,
                                     int32_t epilogue, void* C, uint8_t* Cs, int32_t out_dtype, void* stream);
 
@@ -314,14 +347,18 @@ size_t moe_ffn_mxfp4_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E,
  * (SiLU*mul, h quantized in the epilogue) -> down (fp32) -> combine, all enqueued on `stream`:
  *   y[t] = sum_s w[t,s] * W2_e(s) Q( silu(W1_e(s) Q(x[t])) * (W3_e(s) Q(x[t])) ),  Q = MX quantization.
  *   x bf16 [T, H]; router_logits fp32 [T, E]; w13_q [E, 2I, H/2], w13_e [E, 2I, H/32],
- *   w2_q [E, H, I/2], w2_e [E, H, I/32]; y bf16 [T, H].  Optional routing copies as for moe_ffn_forward.
- *   workspace: at least moe_ffn_mxfp4_workspace_bytes(T, H, I, E, k) bytes.
+ *   w2_q [E, H, I/2], w2_e [E, H, I/32], all four in weight_layout (MOE_LAYOUT_PACKED from
+ *   moe_mx_prepack needs H % 128 == 0 and I % 128 == 0; the quantized activations are then kept in
+ *   the same blocked order internally; results are bit-identical to the canonical layout);
+ *   y bf16 [T, H].  Optional routing copies as for moe_ffn_forward.
+ *   workspace: at least moe_ffn_mxfp4_workspace_bytes(T, H, I, E, k) bytes (either layout).
  * Shapes: as moe_ffn_forward (H, I positive multiples of 32).
  */
 moe_status_t moe_ffn_forward_mxfp4(const uint16_t* x, const float* router_logits, int32_t T, int32_t H, int32_t I,
                                    int32_t E, int32_t k, const uint8_t* w13_q, const uint8_t* w13_e,
-                                   const uint8_t* w2_q, const uint8_t* w2_e, uint16_t* y, int32_t* topk_ids_out,
-                                   float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream);
+                                   const uint8_t* w2_q, const uint8_t* w2_e, int32_t weight_layout, uint16_t* y,
+                                   int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 #ifdef __cplusplus
 }

@@ -4,19 +4,19 @@ The package holds the HIP sources (``csrc/``), their build script (``build.py``)
 (``_lib.py``) whose functions carry the names of the C entry points declared in
 ``include/moe_w4a16.h``.
 """
-from ._lib import (MOE_EPI_NONE, MOE_EPI_SILU_MUL, MOE_LAYOUT_CANONICAL, MOE_LAYOUT_PACKED, MOE_OUT_BF16,
+from ._lib import (MOE_ACT_ROWS, MOE_ACT_TILED, MOE_EPI_NONE, MOE_EPI_SILU_MUL, MOE_LAYOUT_CANONICAL, MOE_LAYOUT_PACKED, MOE_OUT_BF16,
                    MOE_OUT_F32, EXPORTED, LIB_PATH, MoEError,
                    load, moe_align, moe_align_workspace_bytes, moe_combine, moe_dense_ffn_w4a16,
                    moe_dense_ffn_workspace_bytes, moe_ffn_block_forward, moe_ffn_block_m,
                    moe_ffn_block_workspace_bytes, moe_ffn_forward, moe_ffn_workspace_bytes, moe_grouped_gemm_w4a16,
-                   moe_max_tiles, moe_route_topk, moe_router_logits, moe_w4_prepack, moe_mx_quantize,
+                   moe_max_tiles, moe_route_topk, moe_router_logits, moe_w4_prepack, moe_mx_quantize, moe_mx_quantize_tiles, moe_mx_prepack,
                    moe_grouped_gemm_mxfp4, moe_ffn_mxfp4_block_m, moe_ffn_mxfp4_workspace_bytes,
                    moe_ffn_forward_mxfp4)
 
-__all__ = ["MOE_EPI_NONE", "MOE_EPI_SILU_MUL", "MOE_LAYOUT_CANONICAL", "MOE_LAYOUT_PACKED", "MOE_OUT_BF16",
+__all__ = ["MOE_ACT_ROWS", "MOE_ACT_TILED", "MOE_EPI_NONE", "MOE_EPI_SILU_MUL", "MOE_LAYOUT_CANONICAL", "MOE_LAYOUT_PACKED", "MOE_OUT_BF16",
            "MOE_OUT_F32", "EXPORTED", "LIB_PATH", "MoEError", "load", "moe_align", "moe_align_workspace_bytes",
            "moe_combine", "moe_dense_ffn_w4a16", "moe_dense_ffn_workspace_bytes", "moe_ffn_block_forward",
            "moe_ffn_block_m", "moe_ffn_block_workspace_bytes", "moe_ffn_forward", "moe_ffn_workspace_bytes",
            "moe_grouped_gemm_w4a16", "moe_max_tiles", "moe_route_topk", "moe_router_logits", "moe_w4_prepack",
-           "moe_mx_quantize", "moe_grouped_gemm_mxfp4", "moe_ffn_mxfp4_block_m", "moe_ffn_mxfp4_workspace_bytes",
+           "moe_mx_quantize", "moe_mx_quantize_tiles", "moe_mx_prepack", "moe_grouped_gemm_mxfp4", "moe_ffn_mxfp4_block_m", "moe_ffn_mxfp4_workspace_bytes",
            "moe_ffn_forward_mxfp4"]

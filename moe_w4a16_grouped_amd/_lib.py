@@ -27,6 +27,8 @@ MOE_OUT_BF16 = 0
 MOE_OUT_F32 = 1
 MOE_LAYOUT_CANONICAL = 0
 MOE_LAYOUT_PACKED = 1
+MOE_ACT_ROWS = 0
+MOE_ACT_TILED = 1
 
 _lib = None
 
@@ -62,10 +64,13 @@ def load() -> ctypes.CDLL:
         "moe_dense_ffn_w4a16": ([P, I32, I32, I32, P, P, P, P, I32, P, P, SZ, P], I32),
         "moe_ffn_block_workspace_bytes": ([I32, I32, I32, I32, I32, I32], SZ),
         "moe_mx_quantize": ([P, I32, I32, P, P, P], I32),
-        "moe_grouped_gemm_mxfp4": ([P, P, P, I32, P, P, I32, I32, I32, P, I32, P, I32, I32, P, P, I32, P], I32),
+        "moe_mx_prepack": ([P, P, I32, I32, I32, P, P, P], I32),
+        "moe_mx_quantize_tiles": ([P, I32, I32, P, I32, P, I32, P, I32, P, P, P], I32),
+        "moe_grouped_gemm_mxfp4": ([P, P, P, I32, P, P, I32, I32, I32, I32, I32, P, I32, P, I32, I32, P, P, I32, P],
+                                   I32),
         "moe_ffn_mxfp4_block_m": ([I32, I32, I32], I32),
         "moe_ffn_mxfp4_workspace_bytes": ([I32, I32, I32, I32, I32], SZ),
-        "moe_ffn_forward_mxfp4": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "moe_ffn_forward_mxfp4": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, SZ, P], I32),
         "moe_ffn_block_forward": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, I32, P, P, P, P, P,
                                    SZ, P], I32),
         "moe_ffn_block_m": ([I32, I32, I32, I32], I32),
@@ -84,7 +89,7 @@ EXPORTED = ("moe_abi_version", "moe_status_string", "moe_last_error", "moe_route
             "moe_align_workspace_bytes", "moe_align", "moe_w4_prepack", "moe_grouped_gemm_w4a16", "moe_combine",
             "moe_router_logits", "moe_dense_ffn_workspace_bytes", "moe_dense_ffn_w4a16",
             "moe_ffn_block_m", "moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_block_workspace_bytes",
-            "moe_ffn_block_forward", "moe_mx_quantize", "moe_grouped_gemm_mxfp4", "moe_ffn_mxfp4_block_m",
+            "moe_ffn_block_forward", "moe_mx_quantize", "moe_mx_quantize_tiles", "moe_mx_prepack", "moe_grouped_gemm_mxfp4", "moe_ffn_mxfp4_block_m",
             "moe_ffn_mxfp4_workspace_bytes", "moe_ffn_forward_mxfp4")
 
 
@@ -309,16 +314,52 @@ def moe_mx_quantize(x, q=None, s=None, stream=None):
     return q, s
 
 
+def moe_mx_prepack(w_q, w_e, packed_q=None, packed_e=None, stream=None):
+    """Canonical MXFP4 weights (codes [E, N, K/2], scale bytes [E, N, K/32]) -> the packed layout
+    (returned with the canonical shapes, which describe sizes, not element order)."""
+    _req(w_q, torch.uint8, "w_q")
+    _req(w_e, torch.uint8, "w_e")
+    E, N, K2 = w_q.shape
+    if packed_q is None:
+        packed_q = torch.empty_like(w_q)
+    if packed_e is None:
+        packed_e = torch.empty_like(w_e)
+    _check(load().moe_mx_prepack(_p(w_q), _p(w_e), E, N, 2 * K2, _p(packed_q), _p(packed_e), _stream(stream)))
+    return packed_q, packed_e
+
+
+def moe_mx_quantize_tiles(x, a_row_of, a_row_div: int, tiles, max_tiles: int, num_tiles, block_m: int, q=None, s=None,
+                          stream=None):
+    """x bf16 [T, K] -> tile-blocked codes (uint8 [max_tiles * block_m, K/2]) and scale bytes
+    (uint8 [max_tiles * block_m, K/32]) of the tile list (shapes give sizes, not element order)."""
+    _req(x, "16bit", "x")
+    T, K = x.shape
+    rows = max(max_tiles, 1) * block_m
+    if q is None:
+        q = torch.empty((rows, K // 2), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+    if q.numel() < rows * (K // 2) or s.numel() < rows * (K // 32):
+        raise ValueError(f"tile-blocked activations need {rows} rows (max_tiles * block_m)")
+    _check(load().moe_mx_quantize_tiles(_p(x), T, K, _p(a_row_of), a_row_div, _p(tiles), max_tiles, _p(num_tiles),
+                                        block_m, _p(q), _p(s), _stream(stream)))
+    return q, s
+
+
 def moe_grouped_gemm_mxfp4(Aq, As, a_row_of, a_row_div: int, Wq, We, tiles, max_tiles: int, num_tiles,
                            block_m: int, epilogue: int, out_rows: int, out_dtype: int = MOE_OUT_F32, C=None,
-                           Cs=None, stream=None):
+                           Cs=None, stream=None, weight_layout: int = MOE_LAYOUT_CANONICAL,
+                           act_layout: int = MOE_ACT_ROWS):
     """Grouped MXFP4 GEMM over the tile list.  NONE: returns C [out_rows, N]; SILU_MUL: returns the
-    quantized h as (codes [out_rows, N/4], scale bytes [out_rows, N/64])."""
+    quantized h as (codes [out_rows, N/4], scale bytes [out_rows, N/64]); with act_layout TILED the
+    h buffers must hold max_tiles * block_m rows (tile-blocked)."""
     _req(Aq, torch.uint8, "Aq")
     _req(Wq, torch.uint8, "Wq")
     E, N, K2 = Wq.shape
     K = 2 * K2
     dev = Aq.device
+    if act_layout == MOE_ACT_TILED and epilogue == MOE_EPI_SILU_MUL:
+        out_rows = max(out_rows, max(max_tiles, 1) * block_m)  # h is written tile-blocked
     if epilogue == MOE_EPI_SILU_MUL:
         if C is None:
             C = torch.empty((out_rows, N // 4), dtype=torch.uint8, device=dev)
@@ -326,7 +367,12 @@ def moe_grouped_gemm_mxfp4(Aq, As, a_row_of, a_row_div: int, Wq, We, tiles, max_
             Cs = torch.empty((out_rows, N // 64), dtype=torch.uint8, device=dev)
     elif C is None:
         C = torch.empty((out_rows, N), dtype=torch.float32 if out_dtype == MOE_OUT_F32 else torch.bfloat16, device=dev)
-    _check(load().moe_grouped_gemm_mxfp4(_p(Aq), _p(As), _p(a_row_of), a_row_div, _p(Wq), _p(We), E, N, K, _p(tiles),
+    if act_layout == MOE_ACT_TILED and epilogue == MOE_EPI_SILU_MUL:
+        need = max(max_tiles, 1) * block_m
+        if C.shape[0] < need or Cs.shape[0] < need:
+            raise ValueError(f"tile-blocked h needs {need} rows (max_tiles * block_m), got {C.shape[0]}")
+    _check(load().moe_grouped_gemm_mxfp4(_p(Aq), _p(As), _p(a_row_of), a_row_div, _p(Wq), _p(We), weight_layout,
+                                         act_layout, E, N, K, _p(tiles),
                                          max_tiles, _p(num_tiles), block_m, epilogue, _p(C), _p(Cs), out_dtype,
                                          _stream(stream)))
     return (C, Cs) if epilogue == MOE_EPI_SILU_MUL else C
@@ -341,7 +387,7 @@ def moe_ffn_mxfp4_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int
 
 
 def moe_ffn_forward_mxfp4(x, router_logits, w13_q, w13_e, w2_q, w2_e, k: int, y=None, topk_ids_out=None,
-                          topk_w_out=None, workspace=None, stream=None):
+                          topk_w_out=None, workspace=None, stream=None, weight_layout: int = MOE_LAYOUT_CANONICAL):
     """Whole MXFP4 (W4A4) layer: x bf16 [T, H], logits fp32 [T, E], MXFP4 weights -> y bf16 [T, H]."""
     _req(x, "16bit", "x")
     T, H = x.shape
@@ -353,6 +399,6 @@ def moe_ffn_forward_mxfp4(x, router_logits, w13_q, w13_e, w2_q, w2_e, k: int, y=
     if workspace is None:
         workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=x.device)
     _check(load().moe_ffn_forward_mxfp4(_p(x), _p(router_logits), T, H, I, E, k, _p(w13_q), _p(w13_e), _p(w2_q),
-                                        _p(w2_e), _p(y), _p(topk_ids_out), _p(topk_w_out), _p(workspace),
+                                        _p(w2_e), weight_layout, _p(y), _p(topk_ids_out), _p(topk_w_out), _p(workspace),
                                         workspace.numel() * workspace.element_size(), _stream(stream)))
     return y

@@ -220,16 +220,21 @@ struct MxLayout {
   size_t xq, xs, hq, hs, o, total;
 };
 
+// The quantized x and h regions hold either row-major rows (T and R of them) or the tile-blocked
+// layout of the tile list (max_tiles * block_m rows), whichever is larger, so one size serves both
+// weight layouts.
 MxLayout mx_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   MxLayout M{};
   M.L = ffn_layout(T, H, I, E, k, false);
   const int64_t R = T * k;
+  const int64_t tiled_rows = (int64_t)M.L.max_tiles * M.L.block_m;
+  const int64_t xr = std::max(T, tiled_rows), hr = std::max(R, tiled_rows);
   size_t off = M.L.h;
   auto take = [&](size_t bytes) { size_t at = off; off += up256(bytes); return at; };
-  M.xq = take((size_t)T * H / 2);
-  M.xs = take((size_t)T * H / 32);
-  M.hq = take((size_t)R * I / 2);
-  M.hs = take((size_t)R * I / 32);
+  M.xq = take((size_t)xr * H / 2);
+  M.xs = take((size_t)xr * H / 32);
+  M.hq = take((size_t)hr * I / 2);
+  M.hs = take((size_t)hr * I / 32);
   M.o = take((size_t)R * H * 4);
   M.total = off;
   return M;
@@ -500,8 +505,39 @@ moe_status_t moe_mx_quantize(const uint16_t* x, int32_t rows, int32_t K, uint8_t
   return hip_status(moe::launch_mx_quant(x, rows, K, q, s, (hipStream_t)stream), "moe_mx_quantize launch");
 }
 
+moe_status_t moe_mx_prepack(const uint8_t* w_q, const uint8_t* w_e, int32_t E, int32_t N, int32_t K, uint8_t* packed_q,
+                            uint8_t* packed_e, void* stream) {
+  if (E < 1 || N < 1 || K < 128) return fail(MOE_ERR_INVALID_ARG, "moe_mx_prepack: need E, N >= 1 and K >= 128");
+  if (N % 16 != 0 || K % 128 != 0)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_mx_prepack: N=%d must be a multiple of 16 and K=%d of 128", N, K);
+  if (!w_q || !w_e || !packed_q || !packed_e) return fail(MOE_ERR_INVALID_ARG, "moe_mx_prepack: NULL pointer");
+  if (!aligned16(w_q) || !aligned16(packed_q)) return fail(MOE_ERR_MISALIGNED, "moe_mx_prepack: codes need 16-byte alignment");
+  return hip_status(moe::launch_mx_prepack(w_q, w_e, E, N, K, packed_q, packed_e, (hipStream_t)stream),
+                    "moe_mx_prepack launch");
+}
+
+moe_status_t moe_mx_quantize_tiles(const uint16_t* x, int32_t T, int32_t K, const int32_t* a_row_of,
+                                  int32_t a_row_div, const int32_t* tiles, int32_t max_tiles, const int32_t* num_tiles,
+                                  int32_t block_m, uint8_t* q, uint8_t* s, void* stream) {
+  if (T < 0 || K < 128 || K % 128 != 0 || max_tiles < 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_mx_quantize_tiles: need T >= 0, K a positive multiple of 128, max_tiles >= 0");
+  if (block_m != 16 && block_m != 32 && block_m != 64)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_mx_quantize_tiles: block_m=%d must be 16, 32 or 64", block_m);
+  if (a_row_of && a_row_div < 1) return fail(MOE_ERR_INVALID_ARG, "a_row_div must be >= 1");
+  if ((int64_t)max_tiles * block_m >= kMaxRows + (int64_t)MOE_MAX_EXPERTS * block_m)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "max_tiles=%d too large", max_tiles);
+  if (T == 0 || max_tiles == 0) return ok();
+  if (!x || !tiles || !num_tiles || !q || !s) return fail(MOE_ERR_INVALID_ARG, "moe_mx_quantize_tiles: NULL pointer");
+  if (!aligned16(x) || !aligned16(q) || !aligned4(tiles) || !aligned4(num_tiles) || (a_row_of && !aligned4(a_row_of)))
+    return fail(MOE_ERR_MISALIGNED, "moe_mx_quantize_tiles: x and q need 16-byte alignment");
+  return hip_status(moe::launch_mx_quant_tiles(x, K, a_row_of, a_row_div, tiles, num_tiles, max_tiles, block_m, q, s,
+                                               (hipStream_t)stream),
+                    "moe_mx_quantize_tiles launch");
+}
+
 moe_status_t moe_grouped_gemm_mxfp4(const uint8_t* Aq, const uint8_t* As, const int32_t* a_row_of, int32_t a_row_div,
-                                    const uint8_t* Wq, const uint8_t* We, int32_t E, int32_t N, int32_t K,
+                                    const uint8_t* Wq, const uint8_t* We, int32_t weight_layout, int32_t act_layout,
+                                    int32_t E, int32_t N, int32_t K,
                                     const int32_t* tiles, int32_t max_tiles, const int32_t* num_tiles, int32_t block_m,
                                     int32_t epilogue, void* C, uint8_t* Cs, int32_t out_dtype, void* stream) {
   if (E < 1 || N < 1 || K < 1 || max_tiles < 0)
@@ -515,6 +551,16 @@ moe_status_t moe_grouped_gemm_mxfp4(const uint8_t* Aq, const uint8_t* As, const 
   if (epilogue == MOE_EPI_SILU_MUL && N % 64 != 0)
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "SILU_MUL output is MXFP4: N/2 = %d must be a multiple of 32", N / 2);
   if (a_row_of && a_row_div < 1) return fail(MOE_ERR_INVALID_ARG, "a_row_div must be >= 1");
+  if (weight_layout != MOE_LAYOUT_CANONICAL && weight_layout != MOE_LAYOUT_PACKED)
+    return fail(MOE_ERR_INVALID_ARG, "unknown weight_layout %d", weight_layout);
+  if (weight_layout == MOE_LAYOUT_PACKED && (N % 16 != 0 || K % 128 != 0))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "packed MXFP4 weights need N %% 16 == 0 and K %% 128 == 0 (N=%d K=%d)", N, K);
+  if (act_layout != MOE_ACT_ROWS && act_layout != MOE_ACT_TILED)
+    return fail(MOE_ERR_INVALID_ARG, "unknown act_layout %d", act_layout);
+  if (act_layout == MOE_ACT_TILED && weight_layout != MOE_LAYOUT_PACKED)
+    return fail(MOE_ERR_INVALID_ARG, "tile-blocked activations need packed weights");
+  if (act_layout == MOE_ACT_TILED && epilogue == MOE_EPI_SILU_MUL && (N / 2) % 128 != 0)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "a tile-blocked h needs N/2 %% 128 == 0 (N=%d)", N);
   if (max_tiles == 0) return ok();
   if (!Aq || !As || !Wq || !We || !tiles || !num_tiles || !C || (epilogue == MOE_EPI_SILU_MUL && !Cs))
     return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_mxfp4: NULL pointer");
@@ -524,7 +570,8 @@ moe_status_t moe_grouped_gemm_mxfp4(const uint8_t* Aq, const uint8_t* As, const 
   if ((int64_t)max_tiles * block_m >= kMaxRows + (int64_t)MOE_MAX_EXPERTS * block_m)
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "max_tiles=%d too large", max_tiles);
   moe::MxGemmArgs a{Aq, As, a_row_of, a_row_div, Wq, We, N, K, tiles, num_tiles, max_tiles, C, Cs, epilogue,
-                    out_dtype == MOE_OUT_F32};
+                    out_dtype == MOE_OUT_F32,
+                    act_layout == MOE_ACT_TILED ? 2 : (weight_layout == MOE_LAYOUT_PACKED ? 1 : 0)};
   return hip_status(moe::launch_grouped_gemm_mx(a, block_m, (hipStream_t)stream), "moe_grouped_gemm_mxfp4 launch");
 }
 
@@ -542,11 +589,16 @@ size_t moe_ffn_mxfp4_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E,
 
 moe_status_t moe_ffn_forward_mxfp4(const uint16_t* x, const float* router_logits, int32_t T, int32_t H, int32_t I,
                                    int32_t E, int32_t k, const uint8_t* w13_q, const uint8_t* w13_e,
-                                   const uint8_t* w2_q, const uint8_t* w2_e, uint16_t* y, int32_t* topk_ids_out,
-                                   float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream) {
+                                   const uint8_t* w2_q, const uint8_t* w2_e, int32_t weight_layout, uint16_t* y,
+                                   int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
   if (moe_status_t st = check_routing_shape(T, E, k)) return st;
   if (H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0)
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_ffn_forward_mxfp4: H=%d and I=%d must be positive multiples of 32", H, I);
+  if (weight_layout != MOE_LAYOUT_CANONICAL && weight_layout != MOE_LAYOUT_PACKED)
+    return fail(MOE_ERR_INVALID_ARG, "moe_ffn_forward_mxfp4: unknown weight_layout %d", weight_layout);
+  if (weight_layout == MOE_LAYOUT_PACKED && (H % 128 != 0 || I % 128 != 0))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "packed MXFP4 weights need H %% 128 == 0 and I %% 128 == 0 (H=%d I=%d)", H, I);
   if (T == 0) return ok();
   if (!x || !router_logits || !w13_q || !w13_e || !w2_q || !w2_e || !y || !workspace)
     return fail(MOE_ERR_INVALID_ARG, "moe_ffn_forward_mxfp4: NULL pointer");
@@ -585,13 +637,17 @@ moe_status_t moe_ffn_forward_mxfp4(const uint16_t* x, const float* router_logits
                           ws + L.align_ws, s);
     if (e != hipSuccess) return hip_status(e, "align launch");
   }
-  e = moe::launch_mx_quant(x, T, H, xq, xs, s);
+  // packed weights: x gathered into the tile-blocked layout, h written in it by the gate_up epilogue
+  const int mode = weight_layout == MOE_LAYOUT_PACKED ? 2 : 0;
+  if (mode == 2) e = moe::launch_mx_quant_tiles(x, H, sorted, k, tiles, ntiles, L.max_tiles, L.block_m, xq, xs, s);
+  else e = moe::launch_mx_quant(x, T, H, xq, xs, s);
   if (e != hipSuccess) return hip_status(e, "x quantization launch");
   moe::MxGemmArgs g1{xq, xs, sorted, k, w13_q, w13_e, 2 * I, H, tiles, ntiles, L.max_tiles, hq, hs,
-                     MOE_EPI_SILU_MUL, 0};
+                     MOE_EPI_SILU_MUL, 0, mode};
   e = moe::launch_grouped_gemm_mx(g1, L.block_m, s);
   if (e != hipSuccess) return hip_status(e, "gate_up launch");
-  moe::MxGemmArgs g2{hq, hs, nullptr, 1, w2_q, w2_e, H, I, tiles, ntiles, L.max_tiles, o, nullptr, MOE_EPI_NONE, 1};
+  moe::MxGemmArgs g2{hq, hs, nullptr, 1, w2_q, w2_e, H, I, tiles, ntiles, L.max_tiles, o, nullptr, MOE_EPI_NONE, 1,
+                     mode};
   e = moe::launch_grouped_gemm_mx(g2, L.block_m, s);
   if (e != hipSuccess) return hip_status(e, "down launch");
   return hip_status(moe::launch_combine(o, inv, w, nullptr, T, k, H, y, s), "combine launch");

@@ -80,9 +80,20 @@ struct MxGemmArgs {
   uint8_t* Cs;              // SILU_MUL: h scale bytes [rows, N/64]
   int epilogue;             // MOE_EPI_*
   int out_f32;
+  // 0: row-major activations (gathered through a_row_of), canonical weights, row-major output;
+  // 1: as 0 with packed weights (moe_mx_prepack);
+  // 2: tile-blocked activations (mx_tiled_* below), packed weights; a SILU_MUL output (h) is
+  //    written tile-blocked for the next projection, a NONE output row-major.  Needs K % 128 == 0.
+  int mode;
 };
 hipError_t launch_grouped_gemm_mx(const MxGemmArgs& a, int block_m, hipStream_t stream);
 hipError_t launch_mx_quant(const uint16_t* x, long long rows, int K, uint8_t* q, uint8_t* s, hipStream_t stream);
+// x rows quantized and gathered into the tile-blocked layout of a tile list (block height bm).
+hipError_t launch_mx_quant_tiles(const uint16_t* x, int K, const int32_t* a_row_of, int a_row_div,
+                                 const int32_t* tiles, const int32_t* num_tiles, int max_tiles, int bm, uint8_t* q,
+                                 uint8_t* s, hipStream_t stream);
+hipError_t launch_mx_prepack(const uint8_t* wq, const uint8_t* we, int E, int N, int K, uint8_t* pq, uint8_t* pe,
+                             hipStream_t stream);
 
 hipError_t launch_prepack(const uint8_t* wq, const uint16_t* ws, int E, int N, int K, uint8_t* pq, uint16_t* ps,
                           hipStream_t stream);

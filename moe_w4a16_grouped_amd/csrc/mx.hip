@@ -88,17 +88,106 @@ hipError_t launch_mx_quant(const uint16_t* x, long long rows, int K, uint8_t* q,
 }
 
 // ---------------------------------------------------------------------------------------------------
+// Operand layouts in MFMA lane order, so that every wave-level load is one contiguous block.
+//  * Packed weights (moe_mx_prepack): the [E, N, K] matrix cut into blocks of 16 rows x 128 K
+//    elements, ordered (expert, row block, K block) with K fastest; a block is 1024 bytes of codes
+//    (bytes [16l, 16l+16) = lane l: row l % 16, K elements [32 (l / 16), +32)) and, in a separate
+//    array, 64 scale bytes (byte l = lane l's block).  Needs N % 16 == 0 and K % 128 == 0.
+//  * Tile-blocked activations: the rows of a tile list, tile by tile, each tile padded to bm rows,
+//    in the same blocks (tile, 16-row group, K block).  Written by the quantizers below and by the
+//    gate_up epilogue, read by the grouped GEMM with no gather.
+__device__ __forceinline__ size_t mx_block(long long group, int s, int nks) { return (size_t)group * nks + s; }
+
+// x rows of a tile list quantized into the tile-blocked layout: one thread per (tile, row, 32-K
+// block); tiles past num_tiles and padding rows are not written (the GEMM never stores them).
+__global__ __launch_bounds__(256) void mx_quant_tiles_kernel(const uint16_t* __restrict__ x, int K,
+                                                             const int32_t* __restrict__ a_row_of, int a_row_div,
+                                                             const int32_t* __restrict__ tiles,
+                                                             const int32_t* __restrict__ num_tiles, int bm,
+                                                             long long total, uint8_t* __restrict__ q,
+                                                             uint8_t* __restrict__ s) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int kb = K / 32;
+  const int b = (int)(idx % kb);
+  const long long rest = idx / kb;
+  const int i = (int)(rest % bm);
+  const int t = (int)(rest / bm);
+  if (t >= *num_tiles || i >= tiles[3 * t + 2]) return;
+  const int r = tiles[3 * t + 1] + i;
+  const int src = a_row_of ? a_row_of[r] / a_row_div : r;
+  const u32x4* in = reinterpret_cast<const u32x4*>(x + (size_t)src * K + 32 * b);
+  float v[32];
+  float amax = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const u32x4 w = in[d];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * d + 2 * j] = __uint_as_float(w[j] << 16);
+      v[8 * d + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      amax = fmaxf(amax, fmaxf(fabsf(v[8 * d + 2 * j]), fabsf(v[8 * d + 2 * j + 1])));
+    }
+  }
+  const int e = mx_block_exp(amax);
+  const int lane = (b & 3) * 16 + (i & 15);
+  const size_t blk = mx_block((long long)t * (bm / 16) + (i >> 4), b >> 2, K / 128);
+  *reinterpret_cast<u32x4*>(q + blk * 1024 + lane * 16) = mx_encode32(v, e);
+  s[blk * 64 + lane] = (uint8_t)(e + 127);
+}
+
+hipError_t launch_mx_quant_tiles(const uint16_t* x, int K, const int32_t* a_row_of, int a_row_div,
+                                 const int32_t* tiles, const int32_t* num_tiles, int max_tiles, int bm, uint8_t* q,
+                                 uint8_t* s, hipStream_t stream) {
+  const long long total = (long long)max_tiles * bm * (K / 32);
+  if (total <= 0) return hipSuccess;
+  mx_quant_tiles_kernel<<<dim3((unsigned)((total + 255) / 256)), 256, 0, stream>>>(x, K, a_row_of, a_row_div, tiles,
+                                                                                  num_tiles, bm, total, q, s);
+  return hipGetLastError();
+}
+
+// Canonical MXFP4 weights -> packed layout: one thread per 16-byte lane slot of a block.
+__global__ __launch_bounds__(256) void mx_prepack_kernel(const uint8_t* __restrict__ wq, const uint8_t* __restrict__ we,
+                                                         int N, int K, long long total, uint8_t* __restrict__ pq,
+                                                         uint8_t* __restrict__ pe) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int nks = K / 128, nbn = N / 16;
+  const int lane = (int)(idx & 63);
+  const long long blk = idx >> 6;
+  const int st = (int)(blk % nks);
+  const long long rb = blk / nks;  // expert * nbn + row block
+  const long long e = rb / nbn;
+  const int n = (int)(rb % nbn) * 16 + (lane & 15), qd = lane >> 4;
+  const size_t row = (size_t)e * N + n;
+  *reinterpret_cast<u32x4*>(pq + idx * 16) =
+      *reinterpret_cast<const u32x4*>(wq + row * (K / 2) + (size_t)st * 64 + qd * 16);
+  pe[idx] = we[row * (K / 32) + st * 4 + qd];
+}
+
+hipError_t launch_mx_prepack(const uint8_t* wq, const uint8_t* we, int E, int N, int K, uint8_t* pq, uint8_t* pe,
+                             hipStream_t stream) {
+  const long long total = (long long)E * (N / 16) * (K / 128) * 64;
+  if (total <= 0) return hipSuccess;
+  mx_prepack_kernel<<<dim3((unsigned)((total + 255) / 256)), 256, 0, stream>>>(wq, we, N, K, total, pq, pe);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------------
 // Grouped MX GEMM over the device-side tile list (the same list as the W4A16 path).  A workgroup of
 // four waves computes a BM x BN tile; the waves split K KW ways and N 4/KW ways.  Every wave loads
 // its operand fragments straight into a register ring PF K steps deep (16 bytes of codes and one
-// scale byte per lane and 16-row block, activation rows gathered through a_row_of), so the main
-// loop has no LDS traffic and no barrier; K-split partials are added in LDS in wave order.
+// scale byte per lane and 16-row block), so the main loop has no LDS traffic and no barrier; K-split
+// partials are added in LDS in wave order.  With row-major activations (gathered through a_row_of)
+// and canonical weights each load touches 16 rows per 16-lane quarter; the packed weights and the
+// tile-blocked activations (MODE 1, 2) turn every wave-level load into one contiguous 1 KB block.
 // Epilogues: NONE stores fp32 or bf16 rows; SILU_MUL forms h = silu(gate) * up in fp32 (gate rows
 // [0, N/2), up rows [N/2, N) of the weight), gathers the tile's h in LDS and quantizes each
 // 32-column block of each row to MXFP4 (codes [rows, N/4], scale bytes [rows, N/64]) for the next
 // projection.
-template <int BM, int BN, int KW, int PF, int EPI, bool OUT_F32>
+template <int BM, int BN, int KW, int PF, int EPI, bool OUT_F32, int MODE>
 __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
+  constexpr bool ATB = MODE == 2, WPK = MODE >= 1;  // tile-blocked activations, packed weights
   constexpr int WNS = 4 / KW;             // waves along N
   constexpr int WN = BN / WNS;            // columns per wave
   constexpr int MI = BM / 16, NI = WN / 16;
@@ -125,16 +214,22 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
   const int s_begin = min(nks, wk * per), s_end = min(nks, s_begin + per);
   const int KB = K / 2, KS = K / 32;  // bytes of codes and of scales per row
 
-  // activation fragments: row mi * 16 + l16 of the tile (padding rows read the first row)
+  // activation fragments: row mi * 16 + l16 of the tile (row-major: padding rows read the first row)
   const uint8_t* aq[MI];
   const uint8_t* as[MI];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
-    const int i = mi * 16 + l16;
-    const int r = row0 + (i < rows ? i : 0);
-    const int ar = p.a_row_of ? p.a_row_of[r] / p.a_row_div : r;
-    aq[mi] = p.Aq + (size_t)ar * KB + q * 16;
-    as[mi] = p.As + (size_t)ar * KS + q;
+    if (ATB) {
+      const size_t blk = mx_block((long long)tile * MI + mi, 0, nks);
+      aq[mi] = p.Aq + blk * 1024 + lane * 16;
+      as[mi] = p.As + blk * 64 + lane;
+    } else {
+      const int i = mi * 16 + l16;
+      const int r = row0 + (i < rows ? i : 0);
+      const int ar = p.a_row_of ? p.a_row_of[r] / p.a_row_div : r;
+      aq[mi] = p.Aq + (size_t)ar * KB + q * 16;
+      as[mi] = p.As + (size_t)ar * KS + q;
+    }
   }
   // weight fragments: SILU_MUL pairs gate block j with up block j (rows N/2 + j)
   const uint8_t* wq[NI];
@@ -155,8 +250,14 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
       ncol[ni] = n;
     }
     if (!nvalid[ni]) n = 0;
-    wq[ni] = p.Wq + ((size_t)e * N + n) * KB + q * 16;
-    ws[ni] = p.We + ((size_t)e * N + n) * KS + q;
+    if (WPK) {
+      const size_t blk = mx_block((long long)e * (N / 16) + (n >> 4), 0, nks);
+      wq[ni] = p.Wq + blk * 1024 + lane * 16;
+      ws[ni] = p.We + blk * 64 + lane;
+    } else {
+      wq[ni] = p.Wq + ((size_t)e * N + n) * KB + q * 16;
+      ws[ni] = p.We + ((size_t)e * N + n) * KS + q;
+    }
   }
 
   f32x4 acc[MI][NI];
@@ -169,20 +270,21 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
   uint32_t asc[NS][MI], bsc[NS][NI];
   auto load_step = [&](int s, int u) {
     s = min(s, s_end - 1);  // prefetches past this wave's range re-read its last step (unused)
-    // K tail: a quarter past K reads the row's last block and its activation codes are zeroed
-    const bool qv = s * 128 + 32 * q < K;
+    // K tail (row-major, canonical): a quarter past K reads the row's last block and its activation
+    // codes are zeroed.  The blocked layouts need K % 128 == 0.
+    const bool qv = WPK || s * 128 + 32 * q < K;
     const int cb = qv ? s * 64 : (K - 32 - 32 * q) / 2;  // code byte offset of this lane's block
     const int sb = qv ? s * 4 : (K / 32 - 1 - q);        // scale byte offset
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
-      breg[u][ni] = *reinterpret_cast<const u32x4*>(wq[ni] + cb);
-      bsc[u][ni] = ws[ni][sb];
+      breg[u][ni] = *reinterpret_cast<const u32x4*>(wq[ni] + (WPK ? (size_t)s * 1024 : (size_t)cb));
+      bsc[u][ni] = ws[ni][WPK ? s * 64 : sb];
     }
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(aq[mi] + cb);
+      const u32x4 a = *reinterpret_cast<const u32x4*>(aq[mi] + (ATB ? (size_t)s * 1024 : (size_t)cb));
       areg[u][mi] = qv ? a : u32x4{0u, 0u, 0u, 0u};
-      asc[u][mi] = as[mi][sb];
+      asc[u][mi] = as[mi][ATB ? s * 64 : sb];
     }
   };
   auto compute_step = [&](int u) {
@@ -276,10 +378,18 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
       }
       const int ex = mx_block_exp(amax);
-      const size_t orow = (size_t)(row0 + row);
       uint8_t* C = static_cast<uint8_t*>(p.C);
-      *reinterpret_cast<u32x4*>(C + orow * (N / 4) + hcol / 2) = mx_encode32(v, ex);
-      p.Cs[orow * (N / 64) + hcol / 32] = (uint8_t)(ex + 127);
+      if (ATB) {
+        // tile-blocked for the next projection (K = N/2 there)
+        const int b = hcol / 32, ln = (b & 3) * 16 + (row & 15);
+        const size_t blk = mx_block((long long)tile * MI + (row >> 4), b >> 2, (N / 2) / 128);
+        *reinterpret_cast<u32x4*>(C + blk * 1024 + ln * 16) = mx_encode32(v, ex);
+        p.Cs[blk * 64 + ln] = (uint8_t)(ex + 127);
+      } else {
+        const size_t orow = (size_t)(row0 + row);
+        *reinterpret_cast<u32x4*>(C + orow * (N / 4) + hcol / 2) = mx_encode32(v, ex);
+        p.Cs[orow * (N / 64) + hcol / 32] = (uint8_t)(ex + 127);
+      }
     }
   } else {
     if (!owner) return;
@@ -300,14 +410,23 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
   }
 }
 
+template <int BM, int BN, int KW, int PF, int MODE>
+static void launch_mx_mode(const MxGemmArgs& a, dim3 grid, hipStream_t s) {
+  if (a.epilogue == MOE_EPI_SILU_MUL) gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_SILU_MUL, false, MODE><<<grid, 256, 0, s>>>(a);
+  else if (a.out_f32) gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, true, MODE><<<grid, 256, 0, s>>>(a);
+  else gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, false, MODE><<<grid, 256, 0, s>>>(a);
+}
+
 template <int BM, int BN, int KW, int PF>
 static hipError_t launch_mx_cfg(const MxGemmArgs& a, hipStream_t s) {
   const int ncols = a.epilogue == MOE_EPI_SILU_MUL ? a.N / 2 : a.N;
   const int bcols = a.epilogue == MOE_EPI_SILU_MUL ? BN / 2 : BN;
   const dim3 grid = grid2d(8LL * ((a.max_tiles + 7) / 8) * ((ncols + bcols - 1) / bcols));
-  if (a.epilogue == MOE_EPI_SILU_MUL) gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_SILU_MUL, false><<<grid, 256, 0, s>>>(a);
-  else if (a.out_f32) gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, true><<<grid, 256, 0, s>>>(a);
-  else gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, false><<<grid, 256, 0, s>>>(a);
+  switch (a.mode) {
+    case 2: launch_mx_mode<BM, BN, KW, PF, 2>(a, grid, s); break;
+    case 1: launch_mx_mode<BM, BN, KW, PF, 1>(a, grid, s); break;
+    default: launch_mx_mode<BM, BN, KW, PF, 0>(a, grid, s); break;
+  }
   return hipGetLastError();
 }
 

@@ -221,3 +221,47 @@ def test_block_forward_rejects(lib):
     assert bf(ws=ws1 - 1) == -4
     assert bf(T=0) == 0
     assert moe.moe_ffn_block_workspace_bytes(T, H, I, E, k, -1) == 0
+
+
+
+def test_mxfp4_entry_points_reject(lib):
+    f = _ptr(FAKE)
+    # quantizer
+    assert lib.moe_mx_quantize(f, 4, 48, f, f, None) == -1         # K % 32
+    assert lib.moe_mx_quantize(f, 0, 64, f, f, None) == 0
+    assert lib.moe_mx_quantize(_ptr(FAKE + 4), 4, 64, f, f, None) == -3
+    # prepack
+    assert lib.moe_mx_prepack(f, f, 2, 40, 256, f, f, None) == -2   # N % 16
+    assert lib.moe_mx_prepack(f, f, 2, 48, 160, f, f, None) == -2   # K % 128
+    assert lib.moe_mx_prepack(f, None, 2, 48, 256, f, f, None) == -1
+    # grouped GEMM
+    g = lambda **kw: lib.moe_grouped_gemm_mxfp4(f, f, None, 1, f, f, kw.get("lay", 0), kw.get("act", 0), 4, kw.get("N", 256),
+                                                kw.get("K", 256), f, 8, f, kw.get("bm", 16), kw.get("epi", 0), f,
+                                                kw.get("cs", f), 1, None)
+    assert g(K=100) == -2
+    assert g(bm=128) == -2                                         # MXFP4 tiles are 16, 32 or 64 rows
+    assert g(epi=1, N=96) == -2                                    # h blocks of 32 need N % 64 == 0
+    assert g(epi=1, cs=None) == -1
+    assert g(lay=1, K=160) == -2
+    assert g(lay=7) == -1
+    assert g(act=1) == -1                                          # tile-blocked activations need packed weights
+    assert g(act=1, lay=1, epi=1, N=192) == -2                     # tile-blocked h needs N/2 % 128 == 0
+    assert g(act=2, lay=1) == -1
+    qt = lambda **kw: lib.moe_mx_quantize_tiles(f, 16, kw.get("K", 256), None, 1, f, 8, f, kw.get("bm", 16), f, f, None)
+    assert qt(K=96) == -1
+    assert qt(bm=128) == -2
+    # layer
+    assert moe.moe_ffn_mxfp4_block_m(800, 256, 8) == 32
+    assert moe.moe_ffn_mxfp4_workspace_bytes(16, 256, 96, 8, 2) > 0
+    assert moe.moe_ffn_mxfp4_workspace_bytes(16, 250, 96, 8, 2) == 0
+    ws = moe.moe_ffn_mxfp4_workspace_bytes(16, 256, 128, 8, 2)
+    fw = lambda **kw: lib.moe_ffn_forward_mxfp4(kw.get("x", f), f, kw.get("T", 16), kw.get("H", 256), kw.get("I", 128),
+                                                8, kw.get("k", 2), f, f, f, f, kw.get("lay", 0), f, None, None, f,
+                                                kw.get("ws", ws), None)
+    assert fw(H=250) == -2
+    assert fw(k=9) == -1
+    assert fw(ws=ws - 1) == -4
+    assert fw(x=_ptr(FAKE + 2)) == -3
+    assert fw(lay=1, I=96) == -2                                   # packed needs I % 128 == 0
+    assert fw(lay=3) == -1
+    assert fw(T=0) == 0

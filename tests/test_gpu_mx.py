@@ -50,6 +50,12 @@ class MXDevice:
         self.logits = gu.dev(inp.logits)
         self.w13_q, self.w13_e = gu.dev(inp.w13_q), gu.dev(inp.w13_e)
         self.w2_q, self.w2_e = gu.dev(inp.w2_q), gu.dev(inp.w2_e)
+        self._packed = None
+
+    def packed(self):
+        if self._packed is None:
+            self._packed = moe.moe_mx_prepack(self.w13_q, self.w13_e) + moe.moe_mx_prepack(self.w2_q, self.w2_e)
+        return self._packed
 
 
 # ---------------------------------------------------------------------------------------------------
@@ -138,13 +144,16 @@ def test_grouped_gemm_mxfp4_silu_quantized_h(T, E, k, bm, I, K):
 # ---------------------------------------------------------------------------------------------------
 # whole layer
 
-def _forward(d, wl):
+def _forward(d, wl, layout=moe.MOE_LAYOUT_CANONICAL):
     y = torch.full((wl.T, wl.H), float("nan"), dtype=torch.bfloat16, device="cuda")
     ids = torch.full((wl.T, wl.k), -7, dtype=torch.int32, device="cuda")
     ws = torch.full((max(moe.moe_ffn_mxfp4_workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.k), 256),), 0xFF,
                     dtype=torch.uint8, device="cuda")
-    moe.moe_ffn_forward_mxfp4(d.x, d.logits, d.w13_q, d.w13_e, d.w2_q, d.w2_e, wl.k, y=y, topk_ids_out=ids,
-                              workspace=ws)
+    if layout == moe.MOE_LAYOUT_PACKED:
+        w = d.packed()
+    else:
+        w = (d.w13_q, d.w13_e, d.w2_q, d.w2_e)
+    moe.moe_ffn_forward_mxfp4(d.x, d.logits, *w, wl.k, y=y, topk_ids_out=ids, workspace=ws, weight_layout=layout)
     torch.cuda.synchronize()
     return y, ids
 
@@ -204,3 +213,97 @@ def test_ffn_forward_mxfp4_deterministic_and_empty():
     y = moe.moe_ffn_forward_mxfp4(empty, torch.empty((0, 32), dtype=torch.float32, device="cuda"), d.w13_q, d.w13_e,
                                   d.w2_q, d.w2_e, 4)
     assert y.shape == (0, 512)
+
+
+# ---------------------------------------------------------------------------------------------------
+# packed weights (and, in the layer, tile-blocked activations): same values, same bits
+
+def test_mx_prepack_is_a_permutation_of_bytes():
+    rng = np.random.default_rng(30)
+    wq = rng.integers(0, 256, (3, 48, 128), dtype=np.uint8)
+    we = rng.integers(100, 140, (3, 48, 8), dtype=np.uint8)
+    pq, pe = moe.moe_mx_prepack(gu.dev(wq), gu.dev(we))
+    torch.cuda.synchronize()
+    pq, pe = pq.cpu().numpy(), pe.cpu().numpy()
+    assert not np.array_equal(pq, wq)
+    np.testing.assert_array_equal(np.sort(pq.ravel()), np.sort(wq.ravel()))
+    np.testing.assert_array_equal(np.sort(pe.ravel()), np.sort(we.ravel()))
+    # block (e, row block, K block), lane l: row 16 rb + l % 16, K elements [128 kb + 32 (l / 16), +32)
+    e, rb, kb, lane = 2, 1, 1, 37
+    blk = (e * 3 + rb) * 2 + kb
+    row, qd = 16 * rb + lane % 16, lane // 16
+    np.testing.assert_array_equal(pq.reshape(-1)[blk * 1024 + 16 * lane: blk * 1024 + 16 * lane + 16],
+                                  wq[e, row, 64 * kb + 16 * qd: 64 * kb + 16 * qd + 16])
+    assert pe.reshape(-1)[blk * 64 + lane] == we[e, row, 4 * kb + qd]
+
+
+@pytest.mark.parametrize("T,E,k,bm", GEMM_CASES)
+def test_grouped_gemm_mxfp4_packed_matches_canonical_bits(T, E, k, bm):
+    ids, al = _routing(T, E, k, bm, seed=T + 5)
+    R, I, K = T * k, 128, 256
+    Aq, As, Wq, We = _mx_operands(T, 2 * I, K, E, seed=bm)
+    tiles = gu.dev(np.ascontiguousarray(al["tiles"].astype(np.int32)))
+    nt = gu.dev(np.array([al["num_tiles"]], np.int32))
+    srt = gu.dev(al["sorted_ids"].astype(np.int32))
+    dWq, dWe = gu.dev(Wq), gu.dev(We)
+    pWq, pWe = moe.moe_mx_prepack(dWq, dWe)
+    outs = []
+    for Wt, Et, lay in ((dWq, dWe, moe.MOE_LAYOUT_CANONICAL), (pWq, pWe, moe.MOE_LAYOUT_PACKED)):
+        h = moe.moe_grouped_gemm_mxfp4(gu.dev(Aq), gu.dev(As), srt, k, Wt, Et, tiles, al["num_tiles"], nt, bm,
+                                       moe.MOE_EPI_SILU_MUL, R, weight_layout=lay)
+        o = moe.moe_grouped_gemm_mxfp4(gu.dev(Aq), gu.dev(As), srt, k, Wt, Et, tiles, al["num_tiles"], nt, bm,
+                                       moe.MOE_EPI_NONE, R, weight_layout=lay)
+        torch.cuda.synchronize()
+        outs.append((h[0].cpu().numpy(), h[1].cpu().numpy(), o.view(torch.int32).cpu().numpy()))
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["tiny", "dec1", "dec64", "pre800", "big4096", "skew8192"])
+def test_ffn_forward_mxfp4_packed_matches_canonical_bits(name):
+    wl = mi.WORKLOADS[name]
+    d = MXDevice(mi.make_mx_inputs(wl))
+    y0, i0 = _forward(d, wl)
+    y1, i1 = _forward(d, wl, moe.MOE_LAYOUT_PACKED)
+    np.testing.assert_array_equal(i0.cpu().numpy(), i1.cpu().numpy())
+    np.testing.assert_array_equal(y0.view(torch.int16).cpu().numpy(), y1.view(torch.int16).cpu().numpy())
+
+
+@pytest.mark.parametrize("wl", [mi.custom("mxp_bm16", 40, 16, 4, 256, 128, seed=21),
+                                mi.custom("mxp_bm32", 90, 12, 3, 384, 256, seed=22),
+                                mi.custom("mxp_bm64", 300, 8, 2, 256, 384, seed=23)])
+def test_ffn_forward_mxfp4_packed_matches_oracle(wl):
+    inp = mi.make_mx_inputs(wl)
+    d = MXDevice(inp)
+    y, ids = _forward(d, wl, moe.MOE_LAYOUT_PACKED)
+    np.testing.assert_array_equal(ids.cpu().numpy(), oracle.route(inp.logits, wl.k)[0])
+    gu.assert_within_tolerance(gu.host_bf16_to_f64(y), oracle.moe_ffn_mx(inp), wl.name)
+
+
+@pytest.mark.parametrize("T,E,k,bm", GEMM_CASES)
+def test_mxfp4_tiled_activation_chain_matches_row_major_bits(T, E, k, bm):
+    # x -> quantize -> gate_up (SiLU*mul, h quantized) -> down, once with row-major activations and
+    # canonical weights, once with tile-blocked activations and packed weights: same O bits
+    ids, al = _routing(T, E, k, bm, seed=T + 11)
+    R, H, I = T * k, 256, 128
+    rng = np.random.default_rng(bm + T)
+    x = gu.dev_bf16(mi.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)))
+    _, _, W13, E13 = _mx_operands(1, 2 * I, H, E, seed=3)
+    _, _, W2, E2 = _mx_operands(1, H, I, E, seed=4)
+    W13, E13, W2, E2 = gu.dev(W13), gu.dev(E13), gu.dev(W2), gu.dev(E2)
+    P13, Q13 = moe.moe_mx_prepack(W13, E13)
+    P2, Q2 = moe.moe_mx_prepack(W2, E2)
+    mt = al["num_tiles"]
+    tiles = gu.dev(np.ascontiguousarray(al["tiles"].astype(np.int32)))
+    nt = gu.dev(np.array([mt], np.int32))
+    srt = gu.dev(al["sorted_ids"].astype(np.int32))
+    xq, xs = moe.moe_mx_quantize(x)
+    hq, hs = moe.moe_grouped_gemm_mxfp4(xq, xs, srt, k, W13, E13, tiles, mt, nt, bm, moe.MOE_EPI_SILU_MUL, R)
+    O1 = moe.moe_grouped_gemm_mxfp4(hq, hs, None, 1, W2, E2, tiles, mt, nt, bm, moe.MOE_EPI_NONE, R)
+    tq, ts = moe.moe_mx_quantize_tiles(x, srt, k, tiles, mt, nt, bm)
+    gq, gs = moe.moe_grouped_gemm_mxfp4(tq, ts, None, 1, P13, Q13, tiles, mt, nt, bm, moe.MOE_EPI_SILU_MUL, R,
+                                        weight_layout=moe.MOE_LAYOUT_PACKED, act_layout=moe.MOE_ACT_TILED)
+    O2 = moe.moe_grouped_gemm_mxfp4(gq, gs, None, 1, P2, Q2, tiles, mt, nt, bm, moe.MOE_EPI_NONE, R,
+                                    weight_layout=moe.MOE_LAYOUT_PACKED, act_layout=moe.MOE_ACT_TILED)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(O1.view(torch.int32).cpu().numpy(), O2.view(torch.int32).cpu().numpy())
