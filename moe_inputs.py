@@ -29,6 +29,15 @@ The MXFP4 variant (``make_mx_inputs``) draws with ``default_rng(seed)`` in the o
 logits and the codes are those of the W4A16 inputs at the same seed; its scales are E8M0 bytes: each
 uniform(0.005, 0.02) draw u becomes 127 + rint(log2(u)) (the nearest power of two in log scale,
 2^-8 .. 2^-6).
+
+The FP8 variant (``make_f8_inputs``) draws with ``default_rng(seed)`` in the same order (x and logits
+are those of the W4A16 inputs at the same seed), with one byte per weight element and one fp32 scale
+per 128 K elements:
+  3. w13_q = integers(0, 256, (E, 2I, H), uint8), the two NaN codes of E4M3 (0x7F, 0xFF) replaced by
+     0x7E / 0xFE (+-448), so every finite E4M3 code occurs (magnitudes 2^-9 .. 448)
+  4. w13_s = uniform(0.005, 0.02, (E, 2I, H/128)) / 32 as float32 (the 2^-5 keeps weights near the
+     W4 layer's rms, about 0.03, while the codes span up to 448)
+  5. w2_q, 6. w2_s likewise for (E, H, I) and (E, H, I/128).
 """
 from __future__ import annotations
 
@@ -182,3 +191,47 @@ def make_mx_inputs(wl: Workload, seed: int | None = None) -> MXInputs:
 def mx_weight_bytes_per_expert(H: int, I: int) -> int:
     """E2M1 codes plus E8M0 scales of one expert's gate_up and down weights."""
     return 2 * I * H // 2 + 2 * I * (H // GROUP) + H * I // 2 + H * (I // GROUP)
+
+
+F8_BLOCK = 128  # K elements per FP8 scale
+
+
+@dataclasses.dataclass
+class F8Inputs:
+    """Inputs of the FP8 (W8A8, per-1x128) variant: same x and logits, E4M3 codes, fp32 scales."""
+    wl: Workload
+    x: np.ndarray        # uint16  [T, H] bf16 bits
+    logits: np.ndarray   # float32 [T, E]
+    w13_q: np.ndarray    # uint8   [E, 2I, H]     E4M3 codes
+    w13_s: np.ndarray    # float32 [E, 2I, H/128]
+    w2_q: np.ndarray     # uint8   [E, H, I]      E4M3 codes
+    w2_s: np.ndarray     # float32 [E, H, I/128]
+
+
+def e4m3_codes(rng, shape) -> np.ndarray:
+    """Uniform bytes with the two E4M3 NaN codes moved to the largest finite magnitude."""
+    q = rng.integers(0, 256, shape, dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] -= 1
+    return q
+
+
+def make_f8_inputs(wl: Workload, seed: int | None = None) -> F8Inputs:
+    """Draw one workload's FP8 inputs (documented order)."""
+    T, E, H, I = wl.T, wl.E, wl.H, wl.I
+    if H % F8_BLOCK or I % F8_BLOCK:
+        raise ValueError("H and I must be multiples of 128 for the FP8 variant")
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    x = f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    logits = rng.standard_normal((T, E), dtype=np.float32)
+    if wl.skew:
+        logits = (logits + skew_bias(E)[None, :]).astype(np.float32)
+    w13_q = e4m3_codes(rng, (E, 2 * I, H))
+    w13_s = (rng.uniform(0.005, 0.02, (E, 2 * I, H // F8_BLOCK)) / 32.0).astype(np.float32)
+    w2_q = e4m3_codes(rng, (E, H, I))
+    w2_s = (rng.uniform(0.005, 0.02, (E, H, I // F8_BLOCK)) / 32.0).astype(np.float32)
+    return F8Inputs(wl, x, logits, w13_q, w13_s, w2_q, w2_s)
+
+
+def f8_weight_bytes_per_expert(H: int, I: int) -> int:
+    """E4M3 codes plus fp32 per-1x128 scales of one expert's gate_up and down weights."""
+    return 2 * I * H + 2 * I * (H // F8_BLOCK) * 4 + H * I + H * (I // F8_BLOCK) * 4

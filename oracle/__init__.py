@@ -68,6 +68,14 @@ def _load():
             lib.oracle_mx_dequant.argtypes = [P, P, I64, I64, P]
             lib.oracle_moe_ffn_mx.argtypes = [P, P, I64, I64, I64, I64, I64, P, P, P, P, P, I64, P, P]
             lib.oracle_grouped_proj_mx.argtypes = [P, P, P, I64, P, P, I64, I64, I64, P, ctypes.c_int, P]
+            lib.oracle_e4m3_value.argtypes = [ctypes.c_int]
+            lib.oracle_e4m3_value.restype = ctypes.c_double
+            lib.oracle_e4m3_nearest.argtypes = [ctypes.c_double]
+            lib.oracle_e4m3_nearest.restype = ctypes.c_int
+            lib.oracle_f8_quantize.argtypes = [P, I64, I64, P, P]
+            lib.oracle_f8_dequant.argtypes = [P, P, I64, I64, P]
+            lib.oracle_moe_ffn_f8.argtypes = [P, P, I64, I64, I64, I64, I64, P, P, P, P, P, I64, P, P]
+            lib.oracle_grouped_proj_f8.argtypes = [P, P, P, I64, P, P, I64, I64, I64, P, ctypes.c_int, P]
             _lib = lib
     return _lib
 
@@ -259,5 +267,68 @@ def grouped_proj_mx(Aq, As, a_row_of, a_row_div: int, Wq, We, offsets, silu_mul:
     C = np.empty((R, nout), np.float64)
     aro = None if a_row_of is None else _c(a_row_of, np.int32)
     _load().oracle_grouped_proj_mx(_ptr(Aq), _ptr(As), _ptr(aro), a_row_div, _ptr(Wq), _ptr(We), E, N, K,
+                                   _ptr(offsets), int(bool(silu_mul)), _ptr(C))
+    return C
+
+
+# ---- FP8 (E4M3 codes, per-1x128 fp32 scales on both operands) -------------------------------------
+
+def e4m3_value(code: int) -> float:
+    return float(_load().oracle_e4m3_value(int(code)))
+
+
+def e4m3_nearest(v: float) -> int:
+    return int(_load().oracle_e4m3_nearest(float(v)))
+
+
+def f8_quantize(v):
+    """Per-1x128 FP8 quantization of values [rows, K] (fp64 in; decisions in fp32) ->
+    (codes uint8 [rows, K], scales float32 [rows, K/128])."""
+    v = _c(v, np.float64)
+    if v.ndim == 1:
+        v = v[None]
+    rows, K = v.shape
+    q = np.empty((rows, K), np.uint8)
+    s = np.empty((rows, K // 128), np.float32)
+    _load().oracle_f8_quantize(_ptr(v), rows, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def f8_dequant(q, s) -> np.ndarray:
+    """FP8 codes [rows, K] + fp32 scales [rows, K/128] -> fp64 [rows, K]."""
+    q, s = _c(q, np.uint8), _c(s, np.float32)
+    rows, K = q.shape
+    out = np.empty((rows, K), np.float64)
+    _load().oracle_f8_dequant(_ptr(q), _ptr(s), rows, K, _ptr(out))
+    return out
+
+
+def moe_ffn_f8(inp, tokens=None, diagnostics: bool = False):
+    """FP8 (W8A8, per-1x128) layer on ``moe_inputs.F8Inputs``; returns y fp64 [n_tok, H] (and h
+    before its quantization, [n_tok, k, I], if asked)."""
+    wl = inp.wl
+    T, E, k, H, I = wl.T, wl.E, wl.k, wl.H, wl.I
+    tok = None if tokens is None else _c(tokens, np.int64)
+    n = T if tok is None else len(tok)
+    y = np.empty((n, H), np.float64)
+    h = np.empty((n, k, I), np.float64) if diagnostics else None
+    _load().oracle_moe_ffn_f8(_ptr(_c(inp.x, np.uint16)), _ptr(_c(inp.logits, np.float32)), T, H, I, E, k,
+                              _ptr(_c(inp.w13_q, np.uint8)), _ptr(_c(inp.w13_s, np.float32)),
+                              _ptr(_c(inp.w2_q, np.uint8)), _ptr(_c(inp.w2_s, np.float32)), _ptr(tok), n, _ptr(y),
+                              _ptr(h))
+    return (y, h) if diagnostics else y
+
+
+def grouped_proj_f8(Aq, As, a_row_of, a_row_div: int, Wq, Ws, offsets, silu_mul: bool = False):
+    """Grouped FP8 projection over permuted rows (see the C function); fp64, before any quantization."""
+    Aq, As = _c(Aq, np.uint8), _c(As, np.float32)
+    Wq, Ws = _c(Wq, np.uint8), _c(Ws, np.float32)
+    offsets = _c(offsets, np.int32)
+    E, N, K = Wq.shape
+    R = int(offsets[-1])
+    nout = N // 2 if silu_mul else N
+    C = np.empty((R, nout), np.float64)
+    aro = None if a_row_of is None else _c(a_row_of, np.int32)
+    _load().oracle_grouped_proj_f8(_ptr(Aq), _ptr(As), _ptr(aro), a_row_div, _ptr(Wq), _ptr(Ws), E, N, K,
                                    _ptr(offsets), int(bool(silu_mul)), _ptr(C))
     return C

@@ -43,6 +43,16 @@
  *     largest E2M1 exponent), clamped to the E8M0 range, an all-zero block taking 2^-127; each
  *     element becomes the E2M1 value nearest to v / X, ties to the even code, |v / X| > 6 saturating
  *     to 6.  Each projection's output is exact sums of products of the dequantized operands.
+ *   - FP8 (the ATOM page, section 6.1, lists "per-1x128 FP8" served by an a8w8 block-scale GEMM, and
+ *     section 8.1 names an FP8 path of its fused MoE): weights and activations are OCP FP8 E4M3 codes
+ *     (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 subnormal; S.1111.111
+ *     is NaN; largest finite 448), one byte per element, with one fp32 scale per row and block of 128
+ *     consecutive K elements on both operands (the literal reading of "per-1x128", applied to both).
+ *     Activations are quantized on the fly before each projection (x before gate_up, h before down):
+ *     per block, the values rounded to fp32, amax = max |v|, s = amax / 448 rounded to fp32, and each
+ *     code the E4M3 value nearest to the fp32 quotient v / s, ties to the even code; s == 0 (an
+ *     all-zero block) gives codes 0.  These decisions are taken in fp32, the precision the GPU takes
+ *     them in, so that both sides reach the same codes from the same fp32 values.
  */
 #include <math.h>
 #include <stdint.h>
@@ -464,6 +474,159 @@ void oracle_grouped_proj_mx(const uint8_t *Aq, const uint8_t *As, const int32_t 
             double *g = (double *)malloc(sizeof(double) * (size_t)N);
             for (int64_t c = 0; c < K; ++c) a[c] = mx_at(Aq, As, K, arow, c);
             mx_matvec(Wq + e * szq, We + e * sze, N, K, a, g);
+            for (int64_t n = 0; n < nout; ++n) C[r * nout + n] = silu_mul ? silu(g[n]) * g[N / 2 + n] : g[n];
+            free(a); free(g);
+        }
+    }
+}
+
+/* ---- FP8: E4M3 codes with per-1x128 fp32 scales on both operands --------------------------------- */
+
+#define ORACLE_F8_BLOCK 128
+
+/* OCP FP8 E4M3 code -> value.  Bit 7 sign, bits 6..3 exponent (bias 7), bits 2..0 mantissa.
+ * Exponent field 0: subnormal, value = (m/8) * 2^-6.  Otherwise 2^(e-7) * (1 + m/8), except that
+ * exponent 15 with mantissa 7 encodes NaN (the format has no infinities). */
+double oracle_e4m3_value(int code)
+{
+    int s = (code >> 7) & 1;
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    double mag = (e == 0) ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* The E4M3 code nearest to v among the finite codes (so magnitudes beyond 448 saturate to 448),
+ * ties to the code whose mantissa bit 0 is clear; the sign bit follows v (-0.0 -> code 0x80). */
+int oracle_e4m3_nearest(double v)
+{
+    int sign = signbit(v) ? 0x80 : 0;
+    double a = fabs(v);
+    int best = 0;
+    double dbest = a;
+    for (int c = 1; c < 0x7F; ++c) {
+        double d = fabs(a - oracle_e4m3_value(c));
+        if (d < dbest || (d == dbest && (c & 1) == 0)) { best = c; dbest = d; }
+    }
+    return sign | best;
+}
+
+/* Per-1x128 FP8 quantization of a [rows, K] matrix (K % 128 == 0) into codes q [rows, K] and fp32
+ * scales s [rows, K/128].  Per block: values rounded to fp32, amax = max |v|, s = amax / 448 (fp32
+ * division), code = nearest E4M3 value of the fp32 quotient v / s; s == 0 gives codes 0. */
+void oracle_f8_quantize(const double *v, int64_t rows, int64_t K, uint8_t *q, float *s)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < K / ORACLE_F8_BLOCK; ++b) {
+            const double *blk = v + r * K + b * ORACLE_F8_BLOCK;
+            float amax = 0.0f;
+            for (int i = 0; i < ORACLE_F8_BLOCK; ++i) {
+                float f = fabsf((float)blk[i]);
+                if (f > amax) amax = f;
+            }
+            float sc = amax / 448.0f;
+            s[r * (K / ORACLE_F8_BLOCK) + b] = sc;
+            for (int i = 0; i < ORACLE_F8_BLOCK; ++i) {
+                float quot = (sc == 0.0f) ? 0.0f : (float)blk[i] / sc;
+                q[r * K + b * ORACLE_F8_BLOCK + i] = (sc == 0.0f) ? 0 : (uint8_t)oracle_e4m3_nearest((double)quot);
+            }
+        }
+}
+
+/* Value of element kk of row n of an FP8 matrix stored as codes q [*, K] and scales s [*, K/128]
+ * (fp64 product: exact). */
+static double f8_at(const uint8_t *q, const float *s, int64_t K, int64_t n, int64_t kk)
+{
+    return oracle_e4m3_value(q[n * K + kk]) * (double)s[n * (K / ORACLE_F8_BLOCK) + kk / ORACLE_F8_BLOCK];
+}
+
+/* Dense dequantization of an FP8 matrix [rows, K] into out (fp64). */
+void oracle_f8_dequant(const uint8_t *q, const float *s, int64_t rows, int64_t K, double *out)
+{
+    for (int64_t n = 0; n < rows; ++n)
+        for (int64_t kk = 0; kk < K; ++kk) out[n * K + kk] = f8_at(q, s, K, n, kk);
+}
+
+/* One expert's FP8 matrix [N, K] times one (already dequantized) activation row a [K]. */
+static void f8_matvec(const uint8_t *q, const float *s, int64_t N, int64_t K, const double *a, double *out)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        double acc = 0.0;
+        for (int64_t kk = 0; kk < K; ++kk) acc += a[kk] * f8_at(q, s, K, n, kk);
+        out[n] = acc;
+    }
+}
+
+/* Quantize one activation row to FP8 and return it dequantized (in place of a). */
+static void f8_roundtrip_row(double *a, int64_t K)
+{
+    uint8_t *q = (uint8_t *)malloc((size_t)K);
+    float *sc = (float *)malloc(sizeof(float) * (size_t)(K / ORACLE_F8_BLOCK));
+    oracle_f8_quantize(a, 1, K, q, sc);
+    for (int64_t kk = 0; kk < K; ++kk) a[kk] = f8_at(q, sc, K, 0, kk);
+    free(q);
+    free(sc);
+}
+
+/* Full FP8 (W8A8, per-1x128) layer for a subset of tokens (tok == NULL: tokens 0..n_tok-1).
+ *   x [T, H] bf16 bits, logits [T, E] fp32, w13_q [E, 2I, H] E4M3, w13_s [E, 2I, H/128] fp32,
+ *   w2_q [E, H, I], w2_s [E, H, I/128] fp32; y [n_tok, H] fp64.
+ *   Optional diagnostics (may be NULL): h [n_tok, k, I] (silu(gate) * up before its quantization).
+ * Per token: route; quantize x's row; for each slot s the expert's gate_up projection of the
+ * quantized row, h = silu(gate) * up, h quantized, the down projection, y = sum_s w_s o_s. */
+void oracle_moe_ffn_f8(const uint16_t *x, const float *logits, int64_t T, int64_t H, int64_t I, int64_t E,
+                       int64_t k, const uint8_t *w13_q, const float *w13_s, const uint8_t *w2_q,
+                       const float *w2_s, const int64_t *tok, int64_t n_tok, double *y, double *h_out)
+{
+    (void)T;
+    const int64_t sz13_q = 2 * I * H, sz13_s = 2 * I * (H / ORACLE_F8_BLOCK);
+    const int64_t sz2_q = H * I, sz2_s = H * (I / ORACLE_F8_BLOCK);
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t j = 0; j < n_tok; ++j) {
+        int64_t t = tok ? tok[j] : j;
+        int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+        double *w = (double *)malloc(sizeof(double) * (size_t)k);
+        double *xa = (double *)malloc(sizeof(double) * (size_t)H);
+        double *g = (double *)malloc(sizeof(double) * (size_t)(2 * I));
+        double *h = (double *)malloc(sizeof(double) * (size_t)I);
+        double *o = (double *)malloc(sizeof(double) * (size_t)H);
+        oracle_route(logits + t * E, 1, E, k, ids, w);
+        for (int64_t c = 0; c < H; ++c) xa[c] = oracle_bf16_value(x[t * H + c]);
+        f8_roundtrip_row(xa, H);
+        for (int64_t c = 0; c < H; ++c) y[j * H + c] = 0.0;
+        for (int64_t s = 0; s < k; ++s) {
+            int64_t e = ids[s];
+            f8_matvec(w13_q + e * sz13_q, w13_s + e * sz13_s, 2 * I, H, xa, g);
+            for (int64_t i = 0; i < I; ++i) h[i] = silu(g[i]) * g[I + i];
+            if (h_out) memcpy(h_out + (j * k + s) * I, h, sizeof(double) * (size_t)I);
+            f8_roundtrip_row(h, I);
+            f8_matvec(w2_q + e * sz2_q, w2_s + e * sz2_s, H, I, h, o);
+            for (int64_t c = 0; c < H; ++c) y[j * H + c] += w[s] * o[c];
+        }
+        free(ids); free(w); free(xa); free(g); free(h); free(o);
+    }
+}
+
+/* Grouped FP8 projection over permuted rows (one grouped-GEMM launch of the FP8 path): for each
+ * permuted row r of expert e with activation row a_row = (a_row_of ? a_row_of[r] / a_row_div : r),
+ *   C[r, n] = sum_kk A[a_row, kk] * W_e[n, kk],  A as codes Aq [*, K] and scales As [*, K/128],
+ * W as Wq [E, N, K] and Ws [E, N, K/128].  With silu_mul != 0, C[r, j] = silu(G[r, j]) * G[r, N/2 + j]
+ * (j < N/2), before any quantization.  C fp64. */
+void oracle_grouped_proj_f8(const uint8_t *Aq, const float *As, const int32_t *a_row_of, int64_t a_row_div,
+                            const uint8_t *Wq, const float *Ws, int64_t E, int64_t N, int64_t K,
+                            const int32_t *offsets, int silu_mul, double *C)
+{
+    const int64_t szq = N * K, szs = N * (K / ORACLE_F8_BLOCK);
+    const int64_t nout = silu_mul ? N / 2 : N;
+    for (int64_t e = 0; e < E; ++e) {
+        #pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t r = offsets[e]; r < offsets[e + 1]; ++r) {
+            int64_t arow = a_row_of ? a_row_of[r] / a_row_div : r;
+            double *a = (double *)malloc(sizeof(double) * (size_t)K);
+            double *g = (double *)malloc(sizeof(double) * (size_t)N);
+            for (int64_t c = 0; c < K; ++c) a[c] = f8_at(Aq, As, K, arow, c);
+            f8_matvec(Wq + e * szq, Ws + e * szs, N, K, a, g);
             for (int64_t n = 0; n < nout; ++n) C[r * nout + n] = silu_mul ? silu(g[n]) * g[N / 2 + n] : g[n];
             free(a); free(g);
         }

@@ -476,3 +476,188 @@ def test_grouped_proj_mx_matches_rowwise_products():
             g = W @ A[r]
             np.testing.assert_allclose(Cs[r], g[:N // 2] / (1 + np.exp(-g[:N // 2])) * g[N // 2:], rtol=1e-12,
                                        atol=1e-300)
+
+
+# ---------------------------------------------------------------------------------------------------
+# FP8 (E4M3 codes, per-1x128 fp32 scales)
+
+def _golden_e4m3():
+    out = {}
+    with open(os.path.join(GOLDEN, "e4m3_ocp_fp8.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            c, v = line.split()
+            out[int(c, 16)] = float(v)
+    return out
+
+
+def _torch_e4m3_table():
+    """The 256 E4M3 values decoded by torch's float8_e4m3fn (an independent implementation)."""
+    import torch
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _np_f8_dequant(q, s):
+    return _torch_e4m3_table()[np.asarray(q, np.int64)] * np.repeat(np.asarray(s, np.float64), 128, axis=-1)
+
+
+def test_e4m3_decode_golden_and_library():
+    for c, v in _golden_e4m3().items():
+        got = oracle.e4m3_value(c)
+        if math.isnan(v):
+            assert math.isnan(got), c
+        else:
+            assert got == v and math.copysign(1, got) == math.copysign(1, v), (hex(c), got, v)
+    table = _torch_e4m3_table()
+    for c in range(256):
+        got = oracle.e4m3_value(c)
+        assert (math.isnan(got) and math.isnan(table[c])) or got == table[c], hex(c)
+
+
+def test_e4m3_nearest_matches_library_rounding():
+    # torch's float8_e4m3fn cast rounds to nearest, ties to even, for |v| <= 464 (beyond, it gives NaN
+    # where the quantizer saturates): every midpoint between adjacent codes, its neighbours and
+    # random values across the exponent range
+    import torch
+    table = _torch_e4m3_table()
+    # (values are float32, the precision the quantizer's quotients have; torch narrows wider values
+    # to float32 before the cast)
+    mags = np.sort(table[:0x7F]).astype(np.float32)
+    mids = (mags[1:] + mags[:-1]) / np.float32(2)
+    rng = np.random.default_rng(11)
+    vals = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9)), mags,
+                           (rng.uniform(-1, 1, 3000) * np.exp2(rng.integers(-12, 9, 3000))).astype(np.float32),
+                           np.array([464.0, 2.0 ** -10], np.float32)])
+    vals = np.concatenate([vals, -vals])
+    vals = vals[np.abs(vals) <= 464]
+    want = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_nearest(float(v)) for v in vals])
+    np.testing.assert_array_equal(got, want)
+    # saturation (closed form): anything beyond 448 maps to +-448
+    for v in (465.0, 1e6, 1e300):
+        assert oracle.e4m3_nearest(v) == 0x7E and oracle.e4m3_nearest(-v) == 0xFE
+
+
+def _golden_f8():
+    out = []
+    with open(os.path.join(GOLDEN, "f8_quant_worked_example.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            vals, sbits, codes = line.split("|")
+            v = np.zeros(128)
+            vv = [float(t) for t in vals.split()]
+            v[:len(vv)] = vv
+            c = np.zeros(128, np.uint8)
+            cc = [int(t, 16) for t in codes.split()]
+            c[:len(cc)] = cc
+            out.append((v, int(sbits.strip(), 16), c))
+    return out
+
+
+def test_f8_quantize_golden_blocks():
+    for v, sbits, codes in _golden_f8():
+        q, s = oracle.f8_quantize(v[None])
+        assert int(s.view(np.uint32)[0, 0]) == sbits, (v[:4], hex(int(s.view(np.uint32)[0, 0])))
+        np.testing.assert_array_equal(q[0], codes)
+
+
+def test_f8_quantize_invariants():
+    rng = np.random.default_rng(12)
+    v = (rng.standard_normal((48, 512)) * np.exp2(rng.integers(-20, 20, (48, 1)))).astype(np.float32).astype(np.float64)
+    v[5, 128:256] = 0.0
+    q, s = oracle.f8_quantize(v)
+    # a power of two moves only the scale
+    for m in (-4, 3):
+        q2, s2 = oracle.f8_quantize(v * 2.0 ** m)
+        np.testing.assert_array_equal(q2, q)
+        np.testing.assert_array_equal(s2, (s * np.float32(2.0 ** m)).astype(np.float32))
+    # negation flips every sign bit of a non-zero block
+    qn, sn = oracle.f8_quantize(-v)
+    live = np.repeat(s > 0, 128, axis=1)
+    np.testing.assert_array_equal(qn[live], q[live] ^ 0x80)
+    np.testing.assert_array_equal(sn, s)
+    # the block maximum maps to +-448; every element within half the local E4M3 spacing (relative
+    # 2^-4 of a normal value, 2^-10 absolute below 2^-6) times s, up to the two fp32 roundings
+    blk = np.abs(v).reshape(48, 4, 128)
+    arg = blk.argmax(axis=2)
+    qb = q.reshape(48, 4, 128)
+    for r in range(48):
+        for b in range(4):
+            if s[r, b] > 0:
+                assert qb[r, b, arg[r, b]] & 0x7F == 0x7E
+    deq = _np_f8_dequant(q, s)
+    S = np.repeat(s.astype(np.float64), 128, axis=1)
+    scaled = np.abs(v) / np.where(S > 0, S, 1)
+    half = np.where(scaled >= 2.0 ** -6, scaled * 2.0 ** -4, 2.0 ** -10)
+    assert np.all(np.abs(deq - v) <= (half * (1 + 1e-6) + scaled * 2e-7) * S)
+    assert s[5, 1] == 0 and np.all(q[5, 128:256] == 0)
+
+
+def _f8_layer_dense(inp):
+    """The W8A8 layer written densely in numpy: every expert on every token, a [T, E] routing matrix
+    with the renormalised top-k weights and zeros elsewhere; activations quantized by the oracle's FP8
+    quantizer, every FP8 tensor dequantized through torch's E4M3 decode."""
+    wl = inp.wl
+    T, E, k, H, I = wl.T, wl.E, wl.k, wl.H, wl.I
+    ids, w = oracle.route(inp.logits, k)
+    route = np.zeros((T, E))
+    for t in range(T):
+        route[t, ids[t]] = w[t]
+    x = mi.bf16_bits_to_f32(inp.x).astype(np.float64)
+    xd = _np_f8_dequant(*oracle.f8_quantize(x))
+    y = np.zeros((T, H))
+    for e in range(E):
+        W13 = _np_f8_dequant(inp.w13_q[e], inp.w13_s[e])
+        W2 = _np_f8_dequant(inp.w2_q[e], inp.w2_s[e])
+        g = xd @ W13.T
+        h = g[:, :I] / (1.0 + np.exp(-g[:, :I])) * g[:, I:]
+        y += route[:, e:e + 1] * (_np_f8_dequant(*oracle.f8_quantize(h)) @ W2.T)
+    return y
+
+
+@pytest.mark.parametrize("T,E,k,H,I,skew", [(9, 6, 2, 128, 256, False), (5, 4, 4, 256, 128, False),
+                                             (12, 8, 3, 128, 128, True)])
+def test_f8_layer_matches_dense_formulation(T, E, k, H, I, skew):
+    inp = mi.make_f8_inputs(mi.custom("f8dense", T, E, k, H, I, skew=skew, seed=T + E))
+    ref = _f8_layer_dense(inp)
+    y = oracle.moe_ffn_f8(inp)
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.sqrt(np.mean(ref ** 2))
+
+
+def test_f8_single_expert_is_quantized_swiglu():
+    inp = mi.make_f8_inputs(mi.custom("f81", 7, 1, 1, 128, 128, seed=3))
+    x = mi.bf16_bits_to_f32(inp.x).astype(np.float64)
+    xd = _np_f8_dequant(*oracle.f8_quantize(x))
+    W1 = _np_f8_dequant(inp.w13_q[0, :128], inp.w13_s[0, :128])
+    W3 = _np_f8_dequant(inp.w13_q[0, 128:], inp.w13_s[0, 128:])
+    W2 = _np_f8_dequant(inp.w2_q[0], inp.w2_s[0])
+    a, b = xd @ W1.T, xd @ W3.T
+    h = a * (1 / (1 + np.exp(-a))) * b
+    ref = _np_f8_dequant(*oracle.f8_quantize(h)) @ W2.T
+    np.testing.assert_allclose(oracle.moe_ffn_f8(inp), ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+def test_grouped_proj_f8_matches_rowwise_products():
+    rng = np.random.default_rng(9)
+    E, N, K, R = 3, 48, 256, 20
+    Aq = mi.e4m3_codes(rng, (R, K))
+    As = rng.uniform(0.5, 2.0, (R, K // 128)).astype(np.float32)
+    Wq = mi.e4m3_codes(rng, (E, N, K))
+    Ws = rng.uniform(1e-4, 1e-3, (E, N, K // 128)).astype(np.float32)
+    offsets = np.array([0, 7, 7, R], np.int32)
+    a_row_of = rng.permutation(R).astype(np.int32)
+    C = oracle.grouped_proj_f8(Aq, As, a_row_of, 1, Wq, Ws, offsets)
+    A = _np_f8_dequant(Aq, As)
+    for e in range(E):
+        W = _np_f8_dequant(Wq[e], Ws[e])
+        for r in range(offsets[e], offsets[e + 1]):
+            np.testing.assert_allclose(C[r], W @ A[a_row_of[r]], rtol=1e-13, atol=1e-300)
+    Cs = oracle.grouped_proj_f8(Aq, As, None, 1, Wq, Ws, offsets, silu_mul=True)
+    for e in range(E):
+        W = _np_f8_dequant(Wq[e], Ws[e])
+        for r in range(offsets[e], offsets[e + 1]):
+            g = W @ A[r]
+            np.testing.assert_allclose(Cs[r], g[:N // 2] / (1 + np.exp(-g[:N // 2])) * g[N // 2:], rtol=1e-12,
+                                       atol=1e-300)
