@@ -360,6 +360,65 @@ moe_status_t moe_ffn_forward_mxfp4(const uint16_t* x, const float* router_logits
                                    int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes,
                                    void* stream);
 
+/*
+ * ---- FP8 (W8A8, per-1x128) variant ----------------------------------------------------------------
+ * [ATOM, 6.1: per-1x128 FP8 served by an a8w8 block-scale GEMM; ATOM, 8.1: the FP8 path of the fused
+ * MoE; ATOM, 8.2: dynamic activation quantization is part of a format's contract.]  Weights and
+ * activations are OCP FP8 E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent
+ * field 0 subnormal; largest finite 448; the NaN codes 0x7F / 0xFF are not accepted in weights), one
+ * byte per element, rows K-contiguous, with one fp32 scale per row and block of 128 consecutive K
+ * elements: value = E4M3(code) * scale.  Activations are quantized on the fly, per row and block:
+ * s = max |v| / 448 (fp32 division), code = the E4M3 value nearest to the fp32 quotient v / s, ties to
+ * the even code; an all-zero block gets s = 0 and codes 0.  Products run on the gfx950 FP8 matrix
+ * instruction, one 128-element K block per instruction, whose fp32 partial is multiplied by the two
+ * block scales in fp32; accumulation is fp32.
+ */
+#define MOE_IN_BF16 0
+#define MOE_IN_F32 1
+
+/* x [rows, K] (bf16 bits, or fp32 with in_dtype MOE_IN_F32) -> codes q [rows, K] and fp32 scales
+ * s [rows, K/128] (the conversion above).  Shapes: 0 <= rows < 2^26, K a positive multiple of 128.
+ * Alignment: x and q 16 bytes, s 4 bytes. */
+moe_status_t moe_f8_quantize(const void* x, int32_t in_dtype, int32_t rows, int32_t K, uint8_t* q, float* s,
+                             void* stream);
+
+/*
+ * Grouped FP8 GEMM over the tile list of moe_align [Atlas, 编译时内核选择和W4A16 Grouped GEMM: one
+ * launch over all experts]: for each permuted row r of expert e, activation row
+ * a = (a_row_of ? a_row_of[r] / a_row_div : r):
+ *   G[r, n] = sum_k A[a, k] * W_e[n, k],  A = (Aq [*, K], As [*, K/128]), W = (Wq [E, N, K], Ws [E, N, K/128]).
+ *   epilogue NONE:     C [rows, N], fp32 or bf16 (out_dtype).
+ *   epilogue SILU_MUL: C [rows, N/2] fp32, h[r, j] = silu(G[r, j]) * G[r, N/2 + j] (out_dtype must be
+ *                      MOE_OUT_F32; moe_f8_quantize then quantizes h for the next projection).
+ * Rows of C that no tile covers are not written.  block_m 16, 32 or 64 (the tile height moe_align
+ * used); with 16 and max_tiles <= 32 the four waves of a workgroup split K (fp32 partials added in
+ * wave order).
+ * Shapes: 1 <= E <= MOE_MAX_EXPERTS, N >= 1 (N even for SILU_MUL), K a positive multiple of 128,
+ *         K <= 32768.  Alignment: Aq, Wq, C 16 bytes; As, Ws 4 bytes.
+ */
+moe_status_t moe_grouped_gemm_f8(const uint8_t* Aq, const float* As, const int32_t* a_row_of, int32_t a_row_div,
+                                 const uint8_t* Wq, const float* Ws, int32_t E, int32_t N, int32_t K,
+                                 const int32_t* tiles, int32_t max_tiles, const int32_t* num_tiles, int32_t block_m,
+                                 int32_t epilogue, void* C, int32_t out_dtype, void* stream);
+
+/* Row-tile height and workspace bytes of moe_ffn_forward_f8 (host-only, pure; -1 / 0 on invalid sizes). */
+int32_t moe_ffn_f8_block_m(int32_t T, int32_t E, int32_t k);
+size_t moe_ffn_f8_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k);
+
+/*
+ * The whole FP8 (W8A8, per-1x128) layer [ATOM, 6.1 and 8.1-8.2]: route -> permute -> x quantized ->
+ * gate_up (SiLU*mul, h in fp32) -> h quantized -> down (fp32) -> combine, all enqueued on `stream`:
+ *   y[t] = sum_s w[t,s] * W2_e(s) Q( silu(W1_e(s) Q(x[t])) * (W3_e(s) Q(x[t])) ),  Q = FP8 quantization.
+ *   x bf16 [T, H]; router_logits fp32 [T, E]; w13_q [E, 2I, H], w13_s [E, 2I, H/128] fp32,
+ *   w2_q [E, H, I], w2_s [E, H, I/128] fp32; y bf16 [T, H].  Optional routing copies as for
+ *   moe_ffn_forward.  workspace: at least moe_ffn_f8_workspace_bytes(T, H, I, E, k) bytes.
+ * Shapes: as moe_ffn_forward, with H and I positive multiples of 128, H and I <= 32768.
+ */
+moe_status_t moe_ffn_forward_f8(const uint16_t* x, const float* router_logits, int32_t T, int32_t H, int32_t I,
+                                int32_t E, int32_t k, const uint8_t* w13_q, const float* w13_s, const uint8_t* w2_q,
+                                const float* w2_s, uint16_t* y, int32_t* topk_ids_out, float* topk_w_out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

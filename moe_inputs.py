@@ -33,10 +33,12 @@ uniform(0.005, 0.02) draw u becomes 127 + rint(log2(u)) (the nearest power of tw
 The FP8 variant (``make_f8_inputs``) draws with ``default_rng(seed)`` in the same order (x and logits
 are those of the W4A16 inputs at the same seed), with one byte per weight element and one fp32 scale
 per 128 K elements:
-  3. w13_q = integers(0, 256, (E, 2I, H), uint8), the two NaN codes of E4M3 (0x7F, 0xFF) replaced by
-     0x7E / 0xFE (+-448), so every finite E4M3 code occurs (magnitudes 2^-9 .. 448)
-  4. w13_s = uniform(0.005, 0.02, (E, 2I, H/128)) / 32 as float32 (the 2^-5 keeps weights near the
-     W4 layer's rms, about 0.03, while the codes span up to 448)
+  3. w13_q [E, 2I, H]: E4M3 codes drawn field by field, in this order: sign bits integers(0, 2),
+     exponent field 15 - min(geometric(0.5) - 1, 15) (half the codes in the top binade, a quarter in
+     the next, ..., the shape of amax-scaled near-Gaussian weights rather than a log-uniform spread),
+     mantissa integers(0, 8); the NaN pattern (exponent 15, mantissa 7) becomes mantissa 6 (448)
+  4. w13_s = uniform(0.005, 0.02, (E, 2I, H/128)) / 128 as float32 (the 2^-7 keeps weights near the
+     W4 layer's rms, about 0.03, while the codes reach 448)
   5. w2_q, 6. w2_s likewise for (E, H, I) and (E, H, I/128).
 """
 from __future__ import annotations
@@ -209,7 +211,19 @@ class F8Inputs:
 
 
 def e4m3_codes(rng, shape) -> np.ndarray:
-    """Uniform bytes with the two E4M3 NaN codes moved to the largest finite magnitude."""
+    """E4M3 codes: uniform sign, exponent field 15 - min(geometric(1/2) - 1, 15), uniform mantissa;
+    the NaN pattern (exponent 15, mantissa 7) moved to the largest finite magnitude."""
+    sign = rng.integers(0, 2, shape, dtype=np.uint8)
+    expo = (15 - np.minimum(rng.geometric(0.5, shape) - 1, 15)).astype(np.uint8)
+    mant = rng.integers(0, 8, shape, dtype=np.uint8)
+    q = (sign << 7) | (expo << 3) | mant
+    q[(q & 0x7F) == 0x7F] -= 1
+    return q
+
+
+def e4m3_codes_uniform(rng, shape) -> np.ndarray:
+    """Every finite E4M3 code equally likely (log-uniform magnitudes 2^-9 .. 448): uniform bytes with
+    the two NaN codes moved to the largest finite magnitude.  For tests of the full code range."""
     q = rng.integers(0, 256, shape, dtype=np.uint8)
     q[(q & 0x7F) == 0x7F] -= 1
     return q
@@ -226,9 +240,9 @@ def make_f8_inputs(wl: Workload, seed: int | None = None) -> F8Inputs:
     if wl.skew:
         logits = (logits + skew_bias(E)[None, :]).astype(np.float32)
     w13_q = e4m3_codes(rng, (E, 2 * I, H))
-    w13_s = (rng.uniform(0.005, 0.02, (E, 2 * I, H // F8_BLOCK)) / 32.0).astype(np.float32)
+    w13_s = (rng.uniform(0.005, 0.02, (E, 2 * I, H // F8_BLOCK)) / 128.0).astype(np.float32)
     w2_q = e4m3_codes(rng, (E, H, I))
-    w2_s = (rng.uniform(0.005, 0.02, (E, H, I // F8_BLOCK)) / 32.0).astype(np.float32)
+    w2_s = (rng.uniform(0.005, 0.02, (E, H, I // F8_BLOCK)) / 128.0).astype(np.float32)
     return F8Inputs(wl, x, logits, w13_q, w13_s, w2_q, w2_s)
 
 

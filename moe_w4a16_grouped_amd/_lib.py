@@ -29,6 +29,8 @@ MOE_LAYOUT_CANONICAL = 0
 MOE_LAYOUT_PACKED = 1
 MOE_ACT_ROWS = 0
 MOE_ACT_TILED = 1
+MOE_IN_BF16 = 0
+MOE_IN_F32 = 1
 
 _lib = None
 
@@ -73,6 +75,11 @@ def load() -> ctypes.CDLL:
         "moe_ffn_forward_mxfp4": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, SZ, P], I32),
         "moe_ffn_block_forward": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, I32, P, P, P, P, P,
                                    SZ, P], I32),
+        "moe_f8_quantize": ([P, I32, I32, I32, P, P, P], I32),
+        "moe_grouped_gemm_f8": ([P, P, P, I32, P, P, I32, I32, I32, P, I32, P, I32, I32, P, I32, P], I32),
+        "moe_ffn_f8_block_m": ([I32, I32, I32], I32),
+        "moe_ffn_f8_workspace_bytes": ([I32, I32, I32, I32, I32], SZ),
+        "moe_ffn_forward_f8": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, SZ, P], I32),
         "moe_ffn_block_m": ([I32, I32, I32, I32], I32),
         "moe_ffn_workspace_bytes": ([I32, I32, I32, I32, I32], SZ),
         "moe_ffn_forward": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, SZ, P], I32),
@@ -90,7 +97,8 @@ EXPORTED = ("moe_abi_version", "moe_status_string", "moe_last_error", "moe_route
             "moe_router_logits", "moe_dense_ffn_workspace_bytes", "moe_dense_ffn_w4a16",
             "moe_ffn_block_m", "moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_block_workspace_bytes",
             "moe_ffn_block_forward", "moe_mx_quantize", "moe_mx_quantize_tiles", "moe_mx_prepack", "moe_grouped_gemm_mxfp4", "moe_ffn_mxfp4_block_m",
-            "moe_ffn_mxfp4_workspace_bytes", "moe_ffn_forward_mxfp4")
+            "moe_ffn_mxfp4_workspace_bytes", "moe_ffn_forward_mxfp4", "moe_f8_quantize", "moe_grouped_gemm_f8",
+            "moe_ffn_f8_block_m", "moe_ffn_f8_workspace_bytes", "moe_ffn_forward_f8")
 
 
 def _check(status: int):
@@ -402,3 +410,67 @@ def moe_ffn_forward_mxfp4(x, router_logits, w13_q, w13_e, w2_q, w2_e, k: int, y=
                                         _p(w2_e), weight_layout, _p(y), _p(topk_ids_out), _p(topk_w_out), _p(workspace),
                                         workspace.numel() * workspace.element_size(), _stream(stream)))
     return y
+
+
+# ---- FP8 (W8A8, per-1x128) -------------------------------------------------------------------------
+
+def moe_f8_quantize(x, q=None, s=None, stream=None):
+    """x bf16 or fp32 [rows, K] -> (E4M3 codes uint8 [rows, K], fp32 scales [rows, K/128])."""
+    if x.dtype == torch.float32:
+        in_dtype = MOE_IN_F32
+    else:
+        _req(x, "16bit", "x")
+        in_dtype = MOE_IN_BF16
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous CUDA tensor")
+    rows, K = x.shape
+    if q is None:
+        q = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((rows, K // 128), dtype=torch.float32, device=x.device)
+    _check(load().moe_f8_quantize(_p(x), in_dtype, rows, K, _p(q), _p(s), _stream(stream)))
+    return q, s
+
+
+def moe_grouped_gemm_f8(Aq, As, a_row_of, a_row_div: int, Wq, Ws, tiles, max_tiles: int, num_tiles, block_m: int,
+                        epilogue: int, out_rows: int, out_dtype: int = MOE_OUT_F32, C=None, stream=None):
+    """Grouped FP8 GEMM over the tile list.  NONE: returns C [out_rows, N] (fp32 or bf16); SILU_MUL:
+    returns h fp32 [out_rows, N/2]."""
+    _req(Aq, torch.uint8, "Aq")
+    _req(Wq, torch.uint8, "Wq")
+    E, N, K = Wq.shape
+    if C is None:
+        cols = N // 2 if epilogue == MOE_EPI_SILU_MUL else N
+        dt = torch.float32 if out_dtype == MOE_OUT_F32 else torch.bfloat16
+        C = torch.empty((out_rows, cols), dtype=dt, device=Aq.device)
+    _check(load().moe_grouped_gemm_f8(_p(Aq), _p(As), _p(a_row_of), a_row_div, _p(Wq), _p(Ws), E, N, K, _p(tiles),
+                                      max_tiles, _p(num_tiles), block_m, epilogue, _p(C), out_dtype, _stream(stream)))
+    return C
+
+
+def moe_ffn_f8_block_m(T: int, E: int, k: int) -> int:
+    return int(load().moe_ffn_f8_block_m(T, E, k))
+
+
+def moe_ffn_f8_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:
+    return int(load().moe_ffn_f8_workspace_bytes(T, H, I, E, k))
+
+
+def moe_ffn_forward_f8(x, router_logits, w13_q, w13_s, w2_q, w2_s, k: int, y=None, topk_ids_out=None,
+                       topk_w_out=None, workspace=None, stream=None):
+    """Whole FP8 (W8A8, per-1x128) layer: x bf16 [T, H], logits fp32 [T, E], E4M3 weights with fp32
+    scales -> y bf16 [T, H]."""
+    _req(x, "16bit", "x")
+    T, H = x.shape
+    E, N13, _ = w13_q.shape
+    I = N13 // 2
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    wsb = moe_ffn_f8_workspace_bytes(T, H, I, E, k)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=x.device)
+    _check(load().moe_ffn_forward_f8(_p(x), _p(router_logits), T, H, I, E, k, _p(w13_q), _p(w13_s), _p(w2_q),
+                                     _p(w2_s), _p(y), _p(topk_ids_out), _p(topk_w_out), _p(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y
+

@@ -240,6 +240,36 @@ MxLayout mx_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   return M;
 }
 
+// Workspace of the FP8 layer: the routing regions of ffn_layout (canonical tile heights), then
+// x quantized (codes [T, H], scales [T, H/128]), h in fp32 [R, I], h quantized (codes [R, I],
+// scales [R, I/128]) and O fp32 [R, H].
+struct F8Layout {
+  FfnLayout L;
+  size_t xq, xs, hf, hq, hs, o, total;
+};
+
+F8Layout f8_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
+  F8Layout M{};
+  M.L = ffn_layout(T, H, I, E, k, false);
+  const int64_t R = T * k;
+  size_t off = M.L.h;
+  auto take = [&](size_t bytes) { size_t at = off; off += up256(bytes); return at; };
+  M.xq = take((size_t)T * H);
+  M.xs = take((size_t)T * (H / 128) * 4);
+  M.hf = take((size_t)R * I * 4);
+  M.hq = take((size_t)R * I);
+  M.hs = take((size_t)R * (I / 128) * 4);
+  M.o = take((size_t)R * H * 4);
+  M.total = off;
+  return M;
+}
+
+constexpr int32_t kF8MaxK = 32768;  // the GEMM stages a tile's activation scales (64 rows x K/128) in LDS
+
+bool f8_dims_ok(int32_t H, int32_t I) {
+  return H >= 128 && I >= 128 && H % 128 == 0 && I % 128 == 0 && H <= kF8MaxK && I <= kF8MaxK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -649,6 +679,122 @@ moe_status_t moe_ffn_forward_mxfp4(const uint16_t* x, const float* router_logits
   moe::MxGemmArgs g2{hq, hs, nullptr, 1, w2_q, w2_e, H, I, tiles, ntiles, L.max_tiles, o, nullptr, MOE_EPI_NONE, 1,
                      mode};
   e = moe::launch_grouped_gemm_mx(g2, L.block_m, s);
+  if (e != hipSuccess) return hip_status(e, "down launch");
+  return hip_status(moe::launch_combine(o, inv, w, nullptr, T, k, H, y, s), "combine launch");
+}
+
+// ---- FP8 (W8A8, per-1x128) variant ------------------------------------------------------------------
+
+moe_status_t moe_f8_quantize(const void* x, int32_t in_dtype, int32_t rows, int32_t K, uint8_t* q, float* s,
+                             void* stream) {
+  if (rows < 0 || K < 128 || K % 128 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_f8_quantize: need rows >= 0 and K a positive multiple of 128");
+  if (in_dtype != MOE_IN_BF16 && in_dtype != MOE_IN_F32)
+    return fail(MOE_ERR_INVALID_ARG, "moe_f8_quantize: unknown in_dtype %d", in_dtype);
+  if ((int64_t)rows >= kMaxRows) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_f8_quantize: rows=%d must be < 2^26", rows);
+  if (rows == 0) return ok();
+  if (!x || !q || !s) return fail(MOE_ERR_INVALID_ARG, "moe_f8_quantize: NULL pointer");
+  if (!aligned16(x) || !aligned16(q) || !aligned4(s))
+    return fail(MOE_ERR_MISALIGNED, "moe_f8_quantize: x and q need 16-byte alignment, s 4-byte");
+  return hip_status(moe::launch_f8_quant(x, in_dtype == MOE_IN_F32, rows, K, q, s, (hipStream_t)stream),
+                    "moe_f8_quantize launch");
+}
+
+moe_status_t moe_grouped_gemm_f8(const uint8_t* Aq, const float* As, const int32_t* a_row_of, int32_t a_row_div,
+                                 const uint8_t* Wq, const float* Ws, int32_t E, int32_t N, int32_t K,
+                                 const int32_t* tiles, int32_t max_tiles, const int32_t* num_tiles, int32_t block_m,
+                                 int32_t epilogue, void* C, int32_t out_dtype, void* stream) {
+  if (E < 1 || N < 1 || K < 1 || max_tiles < 0 || a_row_div < 1)
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_f8: need E, N, K, a_row_div >= 1, max_tiles >= 0");
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_grouped_gemm_f8: E=%d exceeds %d", E, MOE_MAX_EXPERTS);
+  if (K % 128 != 0 || K > kF8MaxK)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_grouped_gemm_f8: K=%d must be a multiple of 128 and <= %d", K, kF8MaxK);
+  if (block_m != 16 && block_m != 32 && block_m != 64)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_grouped_gemm_f8: block_m=%d must be 16, 32 or 64", block_m);
+  if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SILU_MUL)
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_f8: unknown epilogue %d", epilogue);
+  if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32)
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_f8: unknown out_dtype %d", out_dtype);
+  if (epilogue == MOE_EPI_SILU_MUL && (N % 2 != 0 || out_dtype != MOE_OUT_F32))
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_f8: SILU_MUL needs an even N and out_dtype F32");
+  if (max_tiles == 0) return ok();
+  if (!Aq || !As || !Wq || !Ws || !tiles || !num_tiles || !C)
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_f8: NULL pointer");
+  if (!aligned16(Aq) || !aligned16(Wq) || !aligned16(C) || !aligned4(As) || !aligned4(Ws) || !aligned4(tiles))
+    return fail(MOE_ERR_MISALIGNED, "moe_grouped_gemm_f8: Aq, Wq, C need 16-byte alignment, As, Ws 4-byte");
+  moe::F8GemmArgs a{Aq, As, a_row_of, a_row_div, Wq, Ws, N, K, tiles, num_tiles, max_tiles, C, epilogue,
+                    out_dtype == MOE_OUT_F32};
+  return hip_status(moe::launch_grouped_gemm_f8(a, block_m, (hipStream_t)stream), "moe_grouped_gemm_f8 launch");
+}
+
+int32_t moe_ffn_f8_block_m(int32_t T, int32_t E, int32_t k) {
+  if (T < 0 || E < 1 || k < 1 || k > E || (int64_t)T * k >= kMaxRows) return -1;
+  return pick_block_m((int64_t)T * k, E, false);
+}
+
+size_t moe_ffn_f8_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k) {
+  if (T < 0 || !f8_dims_ok(H, I) || E < 1 || k < 1 || k > E || E > MOE_MAX_EXPERTS || (int64_t)T * k >= kMaxRows)
+    return 0;
+  return f8_layout(T, H, I, E, k).total;
+}
+
+moe_status_t moe_ffn_forward_f8(const uint16_t* x, const float* router_logits, int32_t T, int32_t H, int32_t I,
+                                int32_t E, int32_t k, const uint8_t* w13_q, const float* w13_s, const uint8_t* w2_q,
+                                const float* w2_s, uint16_t* y, int32_t* topk_ids_out, float* topk_w_out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (moe_status_t st = check_routing_shape(T, E, k)) return st;
+  if (!f8_dims_ok(H, I))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_ffn_forward_f8: H=%d and I=%d must be positive multiples of 128, <= %d",
+                H, I, kF8MaxK);
+  if (T == 0) return ok();
+  if (!x || !router_logits || !w13_q || !w13_s || !w2_q || !w2_s || !y || !workspace)
+    return fail(MOE_ERR_INVALID_ARG, "moe_ffn_forward_f8: NULL pointer");
+  if (!aligned16(x) || !aligned16(w13_q) || !aligned16(w2_q) || !aligned16(y) || !aligned16(workspace) ||
+      !aligned4(w13_s) || !aligned4(w2_s) || !aligned4(router_logits) || (topk_ids_out && !aligned4(topk_ids_out)) ||
+      (topk_w_out && !aligned4(topk_w_out)))
+    return fail(MOE_ERR_MISALIGNED, "moe_ffn_forward_f8: x, weight codes, y and workspace need 16-byte alignment");
+  const F8Layout M = f8_layout(T, H, I, E, k);
+  if (workspace_bytes < M.total)
+    return fail(MOE_ERR_WORKSPACE, "moe_ffn_forward_f8: workspace %zu B < required %zu B", workspace_bytes, M.total);
+  const FfnLayout& L = M.L;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
+  int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
+  int32_t* ntiles = reinterpret_cast<int32_t*>(ws + L.ntiles);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(ws + M.xq);
+  float* xs = reinterpret_cast<float*>(ws + M.xs);
+  float* hf = reinterpret_cast<float*>(ws + M.hf);
+  uint8_t* hq = reinterpret_cast<uint8_t*>(ws + M.hq);
+  float* hs = reinterpret_cast<float*>(ws + M.hs);
+  float* o = reinterpret_cast<float*>(ws + M.o);
+  const int R = T * k;
+  hipError_t e;
+  if (moe::route_align_fused_fits(T, E, k)) {
+    e = moe::launch_route_align_small(router_logits, T, E, k, L.block_m, ids, w, counts, offsets, sorted, inv,
+                                      tiles, L.max_tiles, ntiles, s);
+    if (e != hipSuccess) return hip_status(e, "route+align launch");
+  } else {
+    e = moe::launch_route_topk(router_logits, T, E, k, ids, w, s);
+    if (e != hipSuccess) return hip_status(e, "route launch");
+    e = moe::launch_align(ids, R, E, L.block_m, counts, offsets, sorted, inv, tiles, L.max_tiles, ntiles,
+                          ws + L.align_ws, s);
+    if (e != hipSuccess) return hip_status(e, "align launch");
+  }
+  e = moe::launch_f8_quant(x, false, T, H, xq, xs, s);
+  if (e != hipSuccess) return hip_status(e, "x quantization launch");
+  moe::F8GemmArgs g1{xq, xs, sorted, k, w13_q, w13_s, 2 * I, H, tiles, ntiles, L.max_tiles, hf, MOE_EPI_SILU_MUL, 1};
+  e = moe::launch_grouped_gemm_f8(g1, L.block_m, s);
+  if (e != hipSuccess) return hip_status(e, "gate_up launch");
+  e = moe::launch_f8_quant(hf, true, R, I, hq, hs, s);
+  if (e != hipSuccess) return hip_status(e, "h quantization launch");
+  moe::F8GemmArgs g2{hq, hs, nullptr, 1, w2_q, w2_s, H, I, tiles, ntiles, L.max_tiles, o, MOE_EPI_NONE, 1};
+  e = moe::launch_grouped_gemm_f8(g2, L.block_m, s);
   if (e != hipSuccess) return hip_status(e, "down launch");
   return hip_status(moe::launch_combine(o, inv, w, nullptr, T, k, H, y, s), "combine launch");
 }

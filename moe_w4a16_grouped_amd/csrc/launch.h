@@ -95,6 +95,27 @@ hipError_t launch_mx_quant_tiles(const uint16_t* x, int K, const int32_t* a_row_
 hipError_t launch_mx_prepack(const uint8_t* wq, const uint8_t* we, int E, int N, int K, uint8_t* pq, uint8_t* pe,
                              hipStream_t stream);
 
+// FP8 (W8A8, per-1x128) grouped GEMM: E4M3 codes with one fp32 scale per row and 128 K elements.
+struct F8GemmArgs {
+  const uint8_t* Aq;        // activation codes [*, K]
+  const float* As;          // activation scales [*, K/128]
+  const int32_t* a_row_of;  // permuted row -> flat index (NULL = identity)
+  int a_row_div;            // activation row = a_row_of[r] / a_row_div
+  const uint8_t* Wq;        // [E, N, K]
+  const float* Ws;          // [E, N, K/128]
+  int N, K;
+  const int32_t* tiles;     // [max_tiles, 3]
+  const int32_t* num_tiles;
+  int max_tiles;
+  void* C;                  // NONE: fp32 or bf16 [rows, N]; SILU_MUL: fp32 h [rows, N/2]
+  int epilogue;             // MOE_EPI_*
+  int out_f32;
+};
+hipError_t launch_grouped_gemm_f8(const F8GemmArgs& a, int block_m, hipStream_t stream);
+// x (bf16, or fp32 when in_f32) [rows, K] -> codes [rows, K] and scales [rows, K/128].
+hipError_t launch_f8_quant(const void* x, bool in_f32, long long rows, int K, uint8_t* q, float* s,
+                           hipStream_t stream);
+
 hipError_t launch_prepack(const uint8_t* wq, const uint16_t* ws, int E, int N, int K, uint8_t* pq, uint16_t* ps,
                           hipStream_t stream);
 

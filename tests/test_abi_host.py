@@ -265,3 +265,44 @@ def test_mxfp4_entry_points_reject(lib):
     assert fw(lay=1, I=96) == -2                                   # packed needs I % 128 == 0
     assert fw(lay=3) == -1
     assert fw(T=0) == 0
+
+
+def test_f8_entry_points_reject(lib):
+    f = _ptr(FAKE)
+    # quantizer
+    assert lib.moe_f8_quantize(f, 0, 4, 96, f, f, None) == -1      # K % 128
+    assert lib.moe_f8_quantize(f, 2, 4, 128, f, f, None) == -1     # unknown input dtype
+    assert lib.moe_f8_quantize(f, 0, 0, 128, f, f, None) == 0
+    assert lib.moe_f8_quantize(_ptr(FAKE + 4), 1, 4, 128, f, f, None) == -3
+    assert lib.moe_f8_quantize(f, 0, 4, 128, f, None, None) == -1
+    # grouped GEMM
+    g = lambda **kw: lib.moe_grouped_gemm_f8(f, f, None, 1, f, f, 4, kw.get("N", 256), kw.get("K", 256), f,
+                                             kw.get("mt", 8), f, kw.get("bm", 16), kw.get("epi", 0), kw.get("C", f),
+                                             kw.get("od", 1), None)
+    assert g(K=160) == -2
+    assert g(K=32768 + 128) == -2                                  # activation scales of a tile staged in LDS
+    assert g(bm=128) == -2
+    assert g(epi=1, N=255) == -1                                   # SiLU*mul pairs gate and up rows
+    assert g(epi=1, od=0) == -1                                    # h is written in fp32
+    assert g(epi=5) == -1
+    assert g(C=None) == -1
+    assert g(C=_ptr(FAKE + 8)) == -3
+    assert g(mt=0, C=None) == 0                                    # no tiles: nothing to launch
+    # layer
+    assert moe.moe_ffn_f8_block_m(800, 256, 8) == 32
+    assert moe.moe_ffn_f8_workspace_bytes(16, 256, 128, 8, 2) > 0
+    assert moe.moe_ffn_f8_workspace_bytes(16, 256, 96, 8, 2) == 0  # I % 128
+    T, H, I, E, k = 16, 256, 128, 8, 2
+    ws = moe.moe_ffn_f8_workspace_bytes(T, H, I, E, k)
+    R = T * k
+    assert ws >= T * H + R * I * 4 + R * I + R * H * 4            # x codes, h fp32, h codes, down output
+    fw = lambda **kw: lib.moe_ffn_forward_f8(kw.get("x", f), f, kw.get("T", T), kw.get("H", H), kw.get("I", I), E,
+                                             kw.get("k", k), f, kw.get("ws13", f), f, f, f, None, None, f,
+                                             kw.get("ws", ws), None)
+    assert fw(H=192) == -2
+    assert fw(k=9) == -1
+    assert fw(ws=ws - 1) == -4
+    assert fw(x=_ptr(FAKE + 2)) == -3
+    assert fw(ws13=_ptr(FAKE + 2)) == -3                           # fp32 scales need 4-byte alignment
+    assert fw(ws13=None) == -1
+    assert fw(T=0) == 0
