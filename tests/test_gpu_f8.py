@@ -282,8 +282,8 @@ def _near_midpoint(h, q, s):
 
 
 def _flip_allowance(inp, tok):
-    """Per output of the sampled tokens: sum over slots of w * |W2_e| @ (step of every h element that
-    is near a rounding midpoint), from oracle quantities only."""
+    """Per output of the sampled tokens: sum over slots of w * |W2_e| @ (how far each h element near a
+    rounding midpoint can move), from oracle quantities only."""
     wl = inp.wl
     y, h = oracle.moe_ffn_f8(inp, tokens=tok, diagnostics=True)
     ids, w = oracle.route(inp.logits, wl.k)
