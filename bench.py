@@ -30,6 +30,7 @@ import moe_inputs as mi
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense fp4 MFMA
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 RIDGE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
 PAGES_US_800 = 5580.0  # Atlas page, GB10: W4A16 grouped-GEMM MoE layer at 800 tokens / 256 experts
 METRIC = "MoE layer µs, TFLOP/s and weight GB/s (% roofline) at 800 tok/256 experts"
@@ -262,23 +263,24 @@ def time_steps(step, L, args):
     return eager_ms, graph_ms
 
 
-def cpu_baseline_mx(inp, target_s: float):
-    """The MXFP4 oracle timed like cpu_baseline."""
+def cpu_baseline_mx(inp, target_s: float, fn=None):
+    """The MXFP4 oracle (or another variant's oracle function fn) timed like cpu_baseline."""
     import oracle
 
+    fn = fn or oracle.moe_ffn_mx
     wl = inp.wl
     cores = len(os.sched_getaffinity(0))
     rng = np.random.default_rng(1)
     n = min(wl.T, cores)
     tok = np.sort(rng.choice(wl.T, n, replace=False))
     t0 = time.perf_counter()
-    oracle.moe_ffn_mx(inp, tokens=tok)
+    fn(inp, tokens=tok)
     dt = time.perf_counter() - t0
     if dt < target_s / 2 and n < wl.T:
         n2 = int(min(wl.T, max(n, n * (target_s / max(dt, 1e-3)))))
         tok = np.sort(rng.choice(wl.T, n2, replace=False))
         t0 = time.perf_counter()
-        oracle.moe_ffn_mx(inp, tokens=tok)
+        fn(inp, tokens=tok)
         dt = time.perf_counter() - t0
         n = n2
     return {"value": round(dt / n * wl.T * 1e6, 1), "unit": "us/layer", "cores": min(cores, n), "kind": "oracle",
@@ -403,6 +405,116 @@ def run_mxfp4(args):
     print(json.dumps(result), flush=True)
 
 
+def run_f8(args):
+    """The FP8 (W8A8, per-1x128) layer: x and h quantized per 1x128 on the fly, E4M3 x E4M3 products
+    on the FP8 matrix instruction.  Same workload shapes, rotation and timing as the W4A16 layer."""
+    import oracle
+    import moe_w4a16_grouped_amd as moe
+
+    wl = mi.WORKLOADS[args.workload]
+    T, E, k, H, I = wl.T, wl.E, wl.k, wl.H, wl.I
+    R = T * k
+    log(f"bench: FP8 workload {wl.name} T={T} E={E} k={k} H={H} I={I}; generating inputs")
+    inp = mi.make_f8_inputs(wl)
+    x, logits = dev_bf16(inp.x), dev(inp.logits)
+    ids0, _ = moe.moe_route_topk(logits, k)
+    touched = int(torch.unique(ids0).numel())
+    bpe = mi.f8_weight_bytes_per_expert(H, I)
+    L = args.copies or max(1, math.ceil((1 << 30) / (touched * bpe)))
+    w0 = (dev(inp.w13_q), dev(inp.w13_s), dev(inp.w2_q), dev(inp.w2_s))
+    copies = [w0] + [tuple(t.clone() for t in w0) for _ in range(L - 1)]
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_ffn_f8_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device="cuda")
+    log(f"bench: {L} weight copies ({touched} of {E} experts touched); warmup {args.warmup}, steps {args.steps}")
+
+    def step(i):
+        q13, s13, q2, s2 = copies[i % L]
+        moe.moe_ffn_forward_f8(x, logits, q13, s13, q2, s2, k, y=y, workspace=ws)
+
+    eager_ms, graph_ms = time_steps(step, L, args)
+    ms = eager_ms if graph_ms is None else min(eager_ms, graph_ms)
+    log(f"bench: FP8 layer eager {eager_ms * 1e3:.1f} us, graph {graph_ms * 1e3 if graph_ms else 0:.1f} us")
+
+    # per-kernel pass through the separate entry points
+    bm = moe.moe_ffn_f8_block_m(T, E, k)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    xq = torch.empty((T, H), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((T, H // 128), dtype=torch.float32, device="cuda")
+    hf = torch.empty((R, I), dtype=torch.float32, device="cuda")
+    hq = torch.empty((R, I), dtype=torch.uint8, device="cuda")
+    hs = torch.empty((R, I // 128), dtype=torch.float32, device="cuda")
+    O = torch.empty((R, H), dtype=torch.float32, device="cuda")
+    names = ["route", "align", "quant_x", "gate_up", "quant_h", "down", "combine"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    for i in range(args.warmup + args.steps):
+        q13, s13, q2, s2 = copies[i % L]
+        e = evs[i - args.warmup] if i >= args.warmup else None
+        if e: e[0].record()
+        moe.moe_route_topk(logits, k, ids, wts)
+        if e: e[1].record()
+        al = moe.moe_align(ids, E, bm)
+        if e: e[2].record()
+        moe.moe_f8_quantize(x, xq, xs)
+        if e: e[3].record()
+        moe.moe_grouped_gemm_f8(xq, xs, al["sorted_ids"], k, q13, s13, al["tiles"], al["max_tiles"], al["num_tiles"],
+                                bm, moe.MOE_EPI_SILU_MUL, R, C=hf)
+        if e: e[4].record()
+        moe.moe_f8_quantize(hf, hq, hs)
+        if e: e[5].record()
+        moe.moe_grouped_gemm_f8(hq, hs, None, 1, q2, s2, al["tiles"], al["max_tiles"], al["num_tiles"], bm,
+                                moe.MOE_EPI_NONE, R, moe.MOE_OUT_F32, C=O)
+        if e: e[6].record()
+        moe.moe_combine(O, al["inv_perm"], wts, y=y)
+        if e: e[7].record()
+    torch.cuda.synchronize()
+    kern_us = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in evs]) * 1e3) for j, n in enumerate(names)}
+    log("bench: per-kernel us (events): " + ", ".join(f"{n}={v:.1f}" for n, v in kern_us.items()))
+
+    us = ms * 1e3
+    flops = 6.0 * R * H * I
+    weight_bytes = touched * bpe
+    g13 = 2 * I * H + 2 * I * (H // 128) * 4
+    gu_bytes = touched * g13 + T * H + T * (H // 128) * 4 + R * I * 4
+    gu_flops = 4.0 * R * H * I
+    gu_us = kern_us["gate_up"]
+    ridge = MFMA_FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if gu_flops / gu_bytes < ridge:
+        bound, achieved, peak, unit = "hbm", gu_bytes / (gu_us * 1e-6) / 1e9, HBM_PEAK_GBPS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", gu_flops / (gu_us * 1e-6) / 1e12, MFMA_FP8_PEAK_TFLOPS, "TFLOP/s"
+    result = {
+        "metric": METRIC,
+        "value": round(us, 2),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8 (E4M3 x E4M3, fp32 per-1x128 scales; fp32 accumulation)",
+        "data": "synthetic (seeded; E4M3 weight codes with a geometric exponent field, fp32 scales, "
+                "x and logits N(0,1))",
+        "config": {"workload": f"{wl.name} FP8 (W8A8, per-1x128): {T} tokens, {E} experts top-{k}, hidden {H}, "
+                               f"intermediate {I}", "method": "f8", "tokens": T, "experts": E, "top_k": k,
+                   "hidden": H, "intermediate": I, "weight_copies": L, "touched_experts": touched},
+        "tflops": round(flops / (us * 1e-6) / 1e12, 3),
+        "weight_gbps": round(weight_bytes / (us * 1e-6) / 1e9, 1),
+        "timing": {"eager_us": round(eager_ms * 1e3, 2), "graph_us": None if graph_ms is None else round(graph_ms * 1e3, 2),
+                   "value_from": "graph" if graph_ms is not None and graph_ms <= eager_ms else "eager"},
+        "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
+        "roofline": {"kernel": "gemm_f8_kernel (gate_up + SiLU*mul, fp32 h)", "bound": bound,
+                     "achieved": round(achieved, 2), "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": None, "algorithmic_bytes": gu_bytes, "algorithmic_flops": gu_flops},
+    }
+    if not args.no_cpu_baseline:
+        log(f"bench: timing the FP8 CPU oracle on a token sample (~{args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline_mx(inp, args.cpu_seconds, oracle.moe_ffn_f8)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -417,8 +529,9 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="run only the counter-calibration copy")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
     ap.add_argument("--calibrate", action="store_true", help="measure copy bandwidth and a vendor bf16 GEMM rate only")
-    ap.add_argument("--method", choices=["w4a16", "mxfp4"], default="w4a16",
-                    help="w4a16: bf16 activations, bf16 group scales (the default); mxfp4: W4A4 with E8M0 scales")
+    ap.add_argument("--method", choices=["w4a16", "mxfp4", "f8"], default="w4a16",
+                    help="w4a16: bf16 activations, bf16 group scales (the default); mxfp4: W4A4 with E8M0 scales; "
+                         "f8: W8A8 E4M3 with per-1x128 fp32 scales")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the whole-block timing (router gate + shared expert + routed layer)")
     args = ap.parse_args()
@@ -435,6 +548,9 @@ def main():
 
     if args.method == "mxfp4":
         run_mxfp4(args)
+        return
+    if args.method == "f8":
+        run_f8(args)
         return
 
     import moe_w4a16_grouped_amd as moe
