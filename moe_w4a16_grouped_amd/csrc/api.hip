@@ -248,10 +248,21 @@ struct F8Layout {
   size_t xq, xs, hf, hq, hs, o, total;
 };
 
+// Row-tile height of the FP8 layer: as the canonical W4A16 choice, but experts averaging more than
+// 128 rows take the 128 x 256 LDS-staged kernel (its tile list is never longer than the 64-row one,
+// so the canonical tile capacity of ffn_layout covers it).
+int32_t pick_f8_block_m(int64_t R, int64_t E) {
+  const int64_t avg = (R + E - 1) / E;
+  if (avg > 128) return 128;
+  return pick_block_m(R, E, false);
+}
+
 F8Layout f8_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   F8Layout M{};
   M.L = ffn_layout(T, H, I, E, k, false);
   const int64_t R = T * k;
+  M.L.block_m = pick_f8_block_m(R, E);
+  M.L.max_tiles = (int32_t)max_tiles_of(R, E, M.L.block_m);
   size_t off = M.L.h;
   auto take = [&](size_t bytes) { size_t at = off; off += up256(bytes); return at; };
   M.xq = take((size_t)T * H);
@@ -709,8 +720,8 @@ moe_status_t moe_grouped_gemm_f8(const uint8_t* Aq, const float* As, const int32
   if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_grouped_gemm_f8: E=%d exceeds %d", E, MOE_MAX_EXPERTS);
   if (K % 128 != 0 || K > kF8MaxK)
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_grouped_gemm_f8: K=%d must be a multiple of 128 and <= %d", K, kF8MaxK);
-  if (block_m != 16 && block_m != 32 && block_m != 64)
-    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_grouped_gemm_f8: block_m=%d must be 16, 32 or 64", block_m);
+  if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_grouped_gemm_f8: block_m=%d must be 16, 32, 64 or 128", block_m);
   if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SILU_MUL)
     return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_f8: unknown epilogue %d", epilogue);
   if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32)
@@ -729,7 +740,7 @@ moe_status_t moe_grouped_gemm_f8(const uint8_t* Aq, const float* As, const int32
 
 int32_t moe_ffn_f8_block_m(int32_t T, int32_t E, int32_t k) {
   if (T < 0 || E < 1 || k < 1 || k > E || (int64_t)T * k >= kMaxRows) return -1;
-  return pick_block_m((int64_t)T * k, E, false);
+  return pick_f8_block_m((int64_t)T * k, E);
 }
 
 size_t moe_ffn_f8_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k) {

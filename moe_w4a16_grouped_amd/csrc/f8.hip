@@ -288,6 +288,194 @@ __global__ __launch_bounds__(256) void gemm_f8_kernel(F8GemmArgs p) {
     }
 }
 
+// ---------------------------------------------------------------------------------------------------
+// Large-tile FP8 kernel for MFMA-bound shapes (hundreds of rows per expert).  A 128 x 256 output tile
+// per 512-thread workgroup: 8 waves (2 along M x 4 along N), 64 x 64 each, two waves per SIMD so one's
+// scale arithmetic can overlap the other's matrix instructions.  Per K step the tile's activation
+// codes (128 rows x 128 B, gathered rows), weight codes (256 rows x 128 B) and both operands' row
+// scales reach LDS by direct global->LDS loads, through three stages with one barrier per step.  Code
+// rows are 128 B with their 16-byte chunks XOR-swizzled by (row / 2) % 8, so the sixteen rows a
+// fragment read touches fall in sixteen distinct bank groups.  Same products, scale arithmetic and K
+// order as gemm_f8_kernel, so the results are bit-identical to it.
+constexpr int kF8MmBM = 128, kF8MmBN = 256;
+constexpr int kF8MmA = kF8MmBM * 128, kF8MmB = kF8MmBN * 128;  // code bytes per stage
+constexpr int kF8MmStage = kF8MmA + kF8MmB + (kF8MmBM + kF8MmBN) * 4;
+
+// Direct global->LDS 4-byte load (lane l writes LDS bytes [4l, 4l+4) after the wave-uniform base).
+__device__ __forceinline__ void g2lds4(const void* g, void* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
+  asm volatile("global_load_lds_dword %0, off" : : "v"(g), "{m0}"(lds) : "memory");
+}
+
+__device__ __forceinline__ int f8_swz(int row) { return (row >> 1) & 7; }
+
+template <int EPI, bool OUT_F32, int NSTAGE>
+__global__ __launch_bounds__(512) void gemm_f8_mm(F8GemmArgs p) {
+  constexpr int MI = 4, NI = 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * kF8MmStage];
+  __shared__ int32_t sRow[kF8MmBM];
+  const int N = p.N, K = p.K;
+  const int ncols = EPI == MOE_EPI_SILU_MUL ? N / 2 : N;
+  const int bcols = EPI == MOE_EPI_SILU_MUL ? kF8MmBN / 2 : kF8MmBN;
+  const int nbn = (ncols + bcols - 1) / bcols;
+  const int nbx = (nbn + 7) / 8;
+  const long long b = linear_block();
+  const int xcd = (int)(b & 7);
+  const long long jb = b >> 3;
+  const int tile = (int)(jb / nbx), nb = xcd + 8 * (int)(jb % nbx);
+  if (nb >= nbn || tile >= *p.num_tiles) return;
+  const int e = p.tiles[3 * tile], row0 = p.tiles[3 * tile + 1], rows = p.tiles[3 * tile + 2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int l16 = lane & 15, q = lane >> 4;
+  const int nks = K / kF8Block;
+
+  for (int i = tid; i < kF8MmBM; i += 512) {
+    const int r = row0 + (i < rows ? i : 0);
+    sRow[i] = p.a_row_of ? p.a_row_of[r] / p.a_row_div : r;
+  }
+  __syncthreads();
+
+  // weight row of tile column nt (0..255): SILU_MUL puts the 128 gate rows first, then their up rows
+  auto wrow = [&](int nt) -> int {
+    int n;
+    if (EPI == MOE_EPI_SILU_MUL) {
+      const int j = nb * (kF8MmBN / 2) + (nt & 127);
+      n = j < N / 2 ? (nt < 128 ? j : N / 2 + j) : 0;
+    } else {
+      n = nb * kF8MmBN + nt;
+      if (n >= N) n = 0;
+    }
+    return n;
+  };
+  // sources of this wave's direct loads: code instructions cover 8 rows each (lane l: row l / 8,
+  // LDS chunk l % 8, which holds the row's global chunk (l % 8) ^ swizzle)
+  const uint8_t* a_src[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r = 8 * (2 * wave + t) + (lane >> 3);
+    a_src[t] = p.Aq + (size_t)sRow[r] * K + 16 * ((lane & 7) ^ f8_swz(r));
+  }
+  const uint8_t* b_src[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int nt = 8 * (4 * wave + t) + (lane >> 3);
+    b_src[t] = p.Wq + ((size_t)e * N + wrow(nt)) * K + 16 * ((lane & 7) ^ f8_swz(nt));
+  }
+  // scales: waves 0, 1 the 128 activation rows, waves 2..5 the 256 weight rows (one float per lane)
+  const float* s_src = nullptr;
+  if (wave < 2) s_src = p.As + (size_t)sRow[64 * wave + lane] * nks;
+  else if (wave < 6) s_src = p.Ws + ((size_t)e * N + wrow(64 * (wave - 2) + lane)) * nks;
+
+  auto issue = [&](int ks, int stage) {
+    uint8_t* st = smem + stage * kF8MmStage;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) g2lds16(a_src[t] + (size_t)ks * 128, st + (2 * wave + t) * 1024);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) g2lds16(b_src[t] + (size_t)ks * 128, st + kF8MmA + (4 * wave + t) * 1024);
+    if (wave < 2) g2lds4(s_src + ks, st + kF8MmA + kF8MmB + wave * 256);
+    else if (wave < 6) g2lds4(s_src + ks, st + kF8MmA + kF8MmB + kF8MmBM * 4 + (wave - 2) * 256);
+  };
+
+  // tile columns of this wave's four 16-column blocks
+  int ntile[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+    ntile[ni] = EPI == MOE_EPI_SILU_MUL ? (ni < 2 ? wn * 32 + ni * 16 : 128 + wn * 32 + (ni - 2) * 16) + l16
+                                        : wn * 64 + ni * 16 + l16;
+
+  f32x4 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto frag = [&](const uint8_t* base, int row) -> i32x8 {
+    const int sw = f8_swz(row);
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + row * 128 + 16 * (q ^ sw));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + row * 128 + 16 * ((4 + q) ^ sw));
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+
+  auto compute = [&](int stage) {
+    const uint8_t* st = smem + stage * kF8MmStage;
+    const float* sa = reinterpret_cast<const float*>(st + kF8MmA + kF8MmB);
+    const float* sb = sa + kF8MmBM;
+    i32x8 bf[NI];
+    float sw[NI];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      bf[ni] = frag(st + kF8MmA, ntile[ni]);
+      sw[ni] = sb[ntile[ni]];
+    }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int r = wm * 64 + mi * 16;
+      const i32x8 af = frag(st, r + l16);
+      const f32x4 sa4 = *reinterpret_cast<const f32x4*>(&sa[r + 4 * q]);
+      f32x4 part[NI];
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        part[ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[ni], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                                     127, 0, 127);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc[mi][ni][rr] = fmaf(sa4[rr] * sw[ni], part[ni][rr], acc[mi][ni][rr]);
+    }
+  };
+
+  // Per-step direct loads of each wave: 7 (waves 0..5) or 6 (waves 6, 7).  Step s lives in stage
+  // s % NSTAGE.  A stage is read after this wave's loads for it have landed (at most the next step's
+  // loads still in flight) and after the barrier that publishes everyone's.
+  issue(0, 0);
+  if (nks > 1) issue(1, 1);
+  for (int s = 0; s < nks; ++s) {
+    if (s + 1 < nks) wait_vmcnt<6>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (s + 2 < nks) issue(s + 2, (s + 2) % NSTAGE);
+    compute(s % NSTAGE);
+  }
+
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = wm * 64 + mi * 16 + 4 * q + rr;
+      if (row >= rows) continue;
+      const size_t orow = (size_t)(row0 + row);
+      if constexpr (EPI == MOE_EPI_SILU_MUL) {
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const int j = nb * (kF8MmBN / 2) + wn * 32 + ni * 16 + l16;
+          if (j >= N / 2) continue;
+          static_cast<float*>(p.C)[orow * (N / 2) + j] = silu_f32(acc[mi][ni][rr]) * acc[mi][ni + 2][rr];
+        }
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int n = nb * kF8MmBN + wn * 64 + ni * 16 + l16;
+          if (n >= N) continue;
+          if (OUT_F32) static_cast<float*>(p.C)[orow * N + n] = acc[mi][ni][rr];
+          else static_cast<uint16_t*>(p.C)[orow * N + n] = f32_to_bf16_bits(acc[mi][ni][rr]);
+        }
+      }
+    }
+}
+
+template <int EPI, bool F32>
+static hipError_t launch_f8_mm(const F8GemmArgs& a, hipStream_t s) {
+  const int ncols = EPI == MOE_EPI_SILU_MUL ? a.N / 2 : a.N;
+  const int bcols = EPI == MOE_EPI_SILU_MUL ? kF8MmBN / 2 : kF8MmBN;
+  const int nbn = (ncols + bcols - 1) / bcols;
+  gemm_f8_mm<EPI, F32, 3><<<grid2d(8LL * ((nbn + 7) / 8) * a.max_tiles), 512, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int KW, int PF>
 static hipError_t launch_f8_cfg(const F8GemmArgs& a, hipStream_t s) {
   const int ncols = a.epilogue == MOE_EPI_SILU_MUL ? a.N / 2 : a.N;
@@ -305,6 +493,11 @@ constexpr int kF8SplitKMaxTiles = 32;
 
 hipError_t launch_grouped_gemm_f8(const F8GemmArgs& a, int block_m, hipStream_t stream) {
   if (a.max_tiles <= 0) return hipSuccess;
+  if (block_m == 128) {
+    if (a.epilogue == MOE_EPI_SILU_MUL) return launch_f8_mm<MOE_EPI_SILU_MUL, true>(a, stream);
+    if (a.out_f32) return launch_f8_mm<MOE_EPI_NONE, true>(a, stream);
+    return launch_f8_mm<MOE_EPI_NONE, false>(a, stream);
+  }
   switch (block_m) {
     case 16:
       if (a.max_tiles <= kF8SplitKMaxTiles) return launch_f8_cfg<16, 64, 4, 2>(a, stream);

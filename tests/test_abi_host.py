@@ -281,7 +281,7 @@ def test_f8_entry_points_reject(lib):
                                              kw.get("od", 1), None)
     assert g(K=160) == -2
     assert g(K=32768 + 128) == -2                                  # activation scales of a tile staged in LDS
-    assert g(bm=128) == -2
+    assert g(bm=256) == -2
     assert g(epi=1, N=255) == -1                                   # SiLU*mul pairs gate and up rows
     assert g(epi=1, od=0) == -1                                    # h is written in fp32
     assert g(epi=5) == -1
@@ -290,6 +290,7 @@ def test_f8_entry_points_reject(lib):
     assert g(mt=0, C=None) == 0                                    # no tiles: nothing to launch
     # layer
     assert moe.moe_ffn_f8_block_m(800, 256, 8) == 32
+    assert moe.moe_ffn_f8_block_m(4096, 8, 2) == 128               # large experts: the LDS-staged kernel
     assert moe.moe_ffn_f8_workspace_bytes(16, 256, 128, 8, 2) > 0
     assert moe.moe_ffn_f8_workspace_bytes(16, 256, 96, 8, 2) == 0  # I % 128
     T, H, I, E, k = 16, 256, 128, 8, 2

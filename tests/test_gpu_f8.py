@@ -145,7 +145,7 @@ def _truncation_bound(Aq, As, a_rows, Wq, Ws, offsets):
 
 
 # (T, E, k, bm): few tiles take the K-split kernel, more tiles the N-split ones
-GEMM_CASES = [(3, 8, 2, 16), (40, 16, 4, 16), (90, 12, 3, 32), (300, 8, 2, 64)]
+GEMM_CASES = [(3, 8, 2, 16), (40, 16, 4, 16), (90, 12, 3, 32), (300, 8, 2, 64), (600, 4, 2, 128)]
 
 
 @pytest.mark.parametrize("T,E,k,bm", GEMM_CASES)
@@ -316,6 +316,27 @@ def _assert_layer(yh, inp, tok, label):
     assert np.all(excess <= 0), f"{label}: worst excess over tolerance + allowance {excess.max() / rms:.3e} rms"
     assert r["mean_rel"] <= gu.MEAN_REL, f"{label}: {r}"
     return r
+
+
+@pytest.mark.parametrize("epi", [0, 1])
+def test_grouped_gemm_f8_large_tile_matches_register_kernel_bits(epi):
+    # the 128-row LDS-staged kernel and the 64-row register kernel take the same products, scale
+    # arithmetic and K order per row: identical bits on the same routing
+    T, E, k, N, K = 500, 6, 2, 384, 1024
+    ids, al64 = _routing(T, E, k, 64, seed=41)
+    al128 = oracle.align(ids, E, 128)
+    R = T * k
+    Aq, As, Wq, Ws = _f8_operands(T if epi else R, N, K, E, seed=42, full_range=True)
+    outs = []
+    for bm, al in ((64, al64), (128, al128)):
+        tiles = gu.dev(np.ascontiguousarray(al["tiles"].astype(np.int32)))
+        nt = gu.dev(np.array([al["num_tiles"]], np.int32))
+        aro = gu.dev(al["sorted_ids"].astype(np.int32)) if epi else None
+        C = moe.moe_grouped_gemm_f8(gu.dev(Aq), gu.dev(As), aro, k if epi else 1, gu.dev(Wq), gu.dev(Ws), tiles,
+                                    al["num_tiles"], nt, bm, moe.MOE_EPI_SILU_MUL if epi else moe.MOE_EPI_NONE, R)
+        torch.cuda.synchronize()
+        outs.append(C.view(torch.int32).cpu().numpy())
+    np.testing.assert_array_equal(outs[0], outs[1])
 
 
 # ---------------------------------------------------------------------------------------------------
