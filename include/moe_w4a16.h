@@ -391,8 +391,10 @@ moe_status_t moe_f8_quantize(const void* x, int32_t in_dtype, int32_t rows, int3
  *   epilogue SILU_MUL: C [rows, N/2] fp32, h[r, j] = silu(G[r, j]) * G[r, N/2 + j] (out_dtype must be
  *                      MOE_OUT_F32; moe_f8_quantize then quantizes h for the next projection).
  * Rows of C that no tile covers are not written.  block_m 16, 32, 64 or 128 (the tile height
- * moe_align used); with 16 and max_tiles <= 32 the four waves of a workgroup split K (fp32 partials
- * added in wave order); 128 runs a 128 x 256 LDS-staged kernel (bit-identical to the others).
+ * moe_align used).  With block_m 16 or 32 the waves of a workgroup split K (four ways when block_m
+ * is 16 and max_tiles <= 32, else two) and add their fp32 partials in wave order, so bits can
+ * differ between tile heights and capacities; identical arguments always give identical bits.
+ * 128 runs a 128 x 256 LDS-staged kernel, bit-identical to the 64-row one.
  * Shapes: 1 <= E <= MOE_MAX_EXPERTS, N >= 1 (N even for SILU_MUL), K a positive multiple of 128,
  *         K <= 32768.  Alignment: Aq, Wq, C 16 bytes; As, Ws 4 bytes.
  */

@@ -498,12 +498,18 @@ hipError_t launch_grouped_gemm_f8(const F8GemmArgs& a, int block_m, hipStream_t 
     if (a.out_f32) return launch_f8_mm<MOE_EPI_NONE, true>(a, stream);
     return launch_f8_mm<MOE_EPI_NONE, false>(a, stream);
   }
+  // Configurations from sweeps on MI355X (HIP events, weights streamed from HBM): with 128 experts
+  // top-8 at 8 and 64 tokens, gate_up takes 36 / 86 us with <16,64,KW2> against 43 / 90 us for
+  // <16,128,KW1>, down 21 / 44 us with <16,256,KW2> against 21 / 52 us; at 800 tokens and 256
+  // experts <32,128,KW2> takes 151 / 85 us (gate_up / down) against 174 / 91 us for <32,128,KW1>;
+  // 64-row tiles run 148 us with 256 columns against 182 us with 128.
   switch (block_m) {
     case 16:
       if (a.max_tiles <= kF8SplitKMaxTiles) return launch_f8_cfg<16, 64, 4, 2>(a, stream);
-      return launch_f8_cfg<16, 128, 1, 2>(a, stream);
-    case 32: return launch_f8_cfg<32, 128, 1, 2>(a, stream);
-    default: return launch_f8_cfg<64, 128, 1, 1>(a, stream);
+      if (a.epilogue == MOE_EPI_SILU_MUL) return launch_f8_cfg<16, 64, 2, 2>(a, stream);
+      return launch_f8_cfg<16, 256, 2, 1>(a, stream);
+    case 32: return launch_f8_cfg<32, 128, 2, 2>(a, stream);
+    default: return launch_f8_cfg<64, 256, 1, 1>(a, stream);
   }
 }
 
