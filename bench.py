@@ -321,10 +321,10 @@ def run_mxfp4(args):
     log(f"bench: MXFP4 layer eager {eager_ms * 1e3:.1f} us, graph {graph_ms * 1e3 if graph_ms else 0:.1f} us")
 
     # per-kernel pass through the separate entry points
-    bm = moe.moe_ffn_mxfp4_block_m(T, E, k)
+    bm = moe.moe_ffn_mxfp4_block_m(T, H, I, E, k)
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    tiled = layout == moe.MOE_LAYOUT_PACKED
+    tiled = layout == moe.MOE_LAYOUT_PACKED and bm != 128  # the 128-row kernel reads row-major activations
     act = moe.MOE_ACT_TILED if tiled else moe.MOE_ACT_ROWS
     rows_cap = max(T, R, moe.moe_max_tiles(T, k, E, bm) * bm)
     xq = torch.empty((rows_cap, H // 2), dtype=torch.uint8, device="cuda")

@@ -329,8 +329,9 @@ moe_status_t moe_mx_quantize_tiles(const uint16_t* x, int32_t T, int32_t K, cons
  * K % 128 == 0).  act_layout: MOE_ACT_ROWS, or MOE_ACT_TILED (packed weights only; A from
  * moe_mx_quantize_tiles or a previous SILU_MUL output, a_row_of unused; a SILU_MUL output is then
  * written tile-blocked too, for K = N/2 of the next projection, which needs N/2 % 128 == 0).
- * Results are bit-identical across layouts.  block_m 16, 32 or 64 (the tile height moe_align used).
- * K % 32 == 0; SILU_MUL needs N % 64 == 0.
+ * Results are bit-identical across layouts.  block_m 16, 32, 64 or 128 (the tile height moe_align
+ * used); 128 runs a 128 x 256 LDS-staged kernel (bit-identical to the others) that needs
+ * K % 128 == 0, MOE_ACT_ROWS and 4-byte aligned As and We.  K % 32 == 0; SILU_MUL needs N % 64 == 0.
  */
 moe_status_t moe_grouped_gemm_mxfp4(const uint8_t* Aq, const uint8_t* As, const int32_t* a_row_of, int32_t a_row_div,
                                     const uint8_t* Wq, const uint8_t* We, int32_t weight_layout, int32_t act_layout,
@@ -339,7 +340,7 @@ moe_status_t moe_grouped_gemm_mxfp4(const uint8_t* Aq, const uint8_t* As, const 
                                     int32_t epilogue, void* C, uint8_t* Cs, int32_t out_dtype, void* stream);
 
 /* Row-tile height and workspace bytes of moe_ffn_forward_mxfp4 (host-only, pure; -1 / 0 on invalid sizes). */
-int32_t moe_ffn_mxfp4_block_m(int32_t T, int32_t E, int32_t k);
+int32_t moe_ffn_mxfp4_block_m(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k);
 size_t moe_ffn_mxfp4_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k);
 
 /*
@@ -350,7 +351,9 @@ size_t moe_ffn_mxfp4_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E,
  *   w2_q [E, H, I/2], w2_e [E, H, I/32], all four in weight_layout (MOE_LAYOUT_PACKED from
  *   moe_mx_prepack needs H % 128 == 0 and I % 128 == 0; the quantized activations are then kept in
  *   the same blocked order internally; results are bit-identical to the canonical layout);
- *   y bf16 [T, H].  Optional routing copies as for moe_ffn_forward.
+ *   y bf16 [T, H].  Optional routing copies as for moe_ffn_forward.  With experts of more than 128
+ *   rows on average (and H, I multiples of 128) the 128-row kernel runs, on row-major activations,
+ *   and the scale arrays need 4-byte alignment.
  *   workspace: at least moe_ffn_mxfp4_workspace_bytes(T, H, I, E, k) bytes (either layout).
  * Shapes: as moe_ffn_forward (H, I positive multiples of 32).
  */

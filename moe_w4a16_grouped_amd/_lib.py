@@ -70,7 +70,7 @@ def load() -> ctypes.CDLL:
         "moe_mx_quantize_tiles": ([P, I32, I32, P, I32, P, I32, P, I32, P, P, P], I32),
         "moe_grouped_gemm_mxfp4": ([P, P, P, I32, P, P, I32, I32, I32, I32, I32, P, I32, P, I32, I32, P, P, I32, P],
                                    I32),
-        "moe_ffn_mxfp4_block_m": ([I32, I32, I32], I32),
+        "moe_ffn_mxfp4_block_m": ([I32, I32, I32, I32, I32], I32),
         "moe_ffn_mxfp4_workspace_bytes": ([I32, I32, I32, I32, I32], SZ),
         "moe_ffn_forward_mxfp4": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, SZ, P], I32),
         "moe_ffn_block_forward": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, I32, P, P, P, P, P,
@@ -386,8 +386,8 @@ def moe_grouped_gemm_mxfp4(Aq, As, a_row_of, a_row_div: int, Wq, We, tiles, max_
     return (C, Cs) if epilogue == MOE_EPI_SILU_MUL else C
 
 
-def moe_ffn_mxfp4_block_m(T: int, E: int, k: int) -> int:
-    return int(load().moe_ffn_mxfp4_block_m(T, E, k))
+def moe_ffn_mxfp4_block_m(T: int, H: int, I: int, E: int, k: int) -> int:
+    return int(load().moe_ffn_mxfp4_block_m(T, H, I, E, k))
 
 
 def moe_ffn_mxfp4_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:

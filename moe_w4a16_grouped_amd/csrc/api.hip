@@ -223,10 +223,21 @@ struct MxLayout {
 // The quantized x and h regions hold either row-major rows (T and R of them) or the tile-blocked
 // layout of the tile list (max_tiles * block_m rows), whichever is larger, so one size serves both
 // weight layouts.
+// Row-tile height of the MXFP4 layer: the canonical W4A16 choice, but experts averaging more than 128
+// rows take the 128 x 256 LDS-staged kernel when both K dimensions are multiples of 128 (its tile list
+// is never longer than the 64-row one, so the canonical tile capacity of ffn_layout covers it).
+int32_t pick_mx_block_m(int64_t R, int64_t E, int64_t H, int64_t I) {
+  const int64_t avg = (R + E - 1) / E;
+  if (avg > 128 && H % 128 == 0 && I % 128 == 0) return 128;
+  return pick_block_m(R, E, false);
+}
+
 MxLayout mx_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   MxLayout M{};
   M.L = ffn_layout(T, H, I, E, k, false);
   const int64_t R = T * k;
+  M.L.block_m = pick_mx_block_m(R, E, H, I);
+  M.L.max_tiles = (int32_t)max_tiles_of(R, E, M.L.block_m);
   const int64_t tiled_rows = (int64_t)M.L.max_tiles * M.L.block_m;
   const int64_t xr = std::max(T, tiled_rows), hr = std::max(R, tiled_rows);
   size_t off = M.L.h;
@@ -585,8 +596,11 @@ moe_status_t moe_grouped_gemm_mxfp4(const uint8_t* Aq, const uint8_t* As, const 
     return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_mxfp4: need E, N, K >= 1, max_tiles >= 0");
   if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E=%d exceeds %d", E, MOE_MAX_EXPERTS);
   if (K % 32 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "K=%d must be a multiple of 32", K);
-  if (block_m != 16 && block_m != 32 && block_m != 64)
-    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_grouped_gemm_mxfp4: block_m=%d must be 16, 32 or 64", block_m);
+  if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_grouped_gemm_mxfp4: block_m=%d must be 16, 32, 64 or 128", block_m);
+  if (block_m == 128 && (K % 128 != 0 || act_layout != MOE_ACT_ROWS))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE,
+                "moe_grouped_gemm_mxfp4: block_m 128 needs K %% 128 == 0 and row-major activations (K=%d)", K);
   if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SILU_MUL) return fail(MOE_ERR_INVALID_ARG, "unknown epilogue %d", epilogue);
   if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return fail(MOE_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
   if (epilogue == MOE_EPI_SILU_MUL && N % 64 != 0)
@@ -608,6 +622,8 @@ moe_status_t moe_grouped_gemm_mxfp4(const uint8_t* Aq, const uint8_t* As, const 
   if (!aligned16(Aq) || !aligned16(Wq) || !aligned16(C) || !aligned4(tiles) || !aligned4(num_tiles) ||
       (a_row_of && !aligned4(a_row_of)))
     return fail(MOE_ERR_MISALIGNED, "moe_grouped_gemm_mxfp4: Aq, Wq, C need 16-byte alignment");
+  if (block_m == 128 && (!aligned4(As) || !aligned4(We)))
+    return fail(MOE_ERR_MISALIGNED, "moe_grouped_gemm_mxfp4: block_m 128 needs 4-byte aligned scale arrays");
   if ((int64_t)max_tiles * block_m >= kMaxRows + (int64_t)MOE_MAX_EXPERTS * block_m)
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "max_tiles=%d too large", max_tiles);
   moe::MxGemmArgs a{Aq, As, a_row_of, a_row_div, Wq, We, N, K, tiles, num_tiles, max_tiles, C, Cs, epilogue,
@@ -616,9 +632,9 @@ moe_status_t moe_grouped_gemm_mxfp4(const uint8_t* Aq, const uint8_t* As, const 
   return hip_status(moe::launch_grouped_gemm_mx(a, block_m, (hipStream_t)stream), "moe_grouped_gemm_mxfp4 launch");
 }
 
-int32_t moe_ffn_mxfp4_block_m(int32_t T, int32_t E, int32_t k) {
-  if (T < 0 || E < 1 || k < 1 || k > E || (int64_t)T * k >= kMaxRows) return -1;
-  return pick_block_m((int64_t)T * k, E, false);
+int32_t moe_ffn_mxfp4_block_m(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k) {
+  if (T < 0 || E < 1 || k < 1 || k > E || (int64_t)T * k >= kMaxRows || H < 32 || I < 32) return -1;
+  return pick_mx_block_m((int64_t)T * k, E, H, I);
 }
 
 size_t moe_ffn_mxfp4_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k) {
@@ -679,7 +695,11 @@ moe_status_t moe_ffn_forward_mxfp4(const uint16_t* x, const float* router_logits
     if (e != hipSuccess) return hip_status(e, "align launch");
   }
   // packed weights: x gathered into the tile-blocked layout, h written in it by the gate_up epilogue
-  const int mode = weight_layout == MOE_LAYOUT_PACKED ? 2 : 0;
+  // (the 128-row kernel reads row-major activations with either weight layout)
+  const int packed = weight_layout == MOE_LAYOUT_PACKED;
+  const int mode = L.block_m == 128 ? packed : (packed ? 2 : 0);
+  if (L.block_m == 128 && (!aligned4(w13_e) || !aligned4(w2_e)))
+    return fail(MOE_ERR_MISALIGNED, "moe_ffn_forward_mxfp4: scale arrays need 4-byte alignment");
   if (mode == 2) e = moe::launch_mx_quant_tiles(x, H, sorted, k, tiles, ntiles, L.max_tiles, L.block_m, xq, xs, s);
   else e = moe::launch_mx_quant(x, T, H, xq, xs, s);
   if (e != hipSuccess) return hip_status(e, "x quantization launch");

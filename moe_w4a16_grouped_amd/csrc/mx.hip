@@ -410,6 +410,250 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------------
+// Large-tile MXFP4 kernel for MFMA-bound shapes (hundreds of rows per expert), row-major activations
+// (gathered rows) with canonical (MODE 0) or packed (MODE 1) weights, K % 128 == 0.  A 128 x 256
+// output tile per 512-thread workgroup: 8 waves (2 along M x 4 along N), 64 x 64 each.  Per K step of
+// 128 the tile's activation codes (128 rows x 64 B), weight codes (256 rows x 64 B) and both operands'
+// E8M0 scale bytes reach LDS by direct global->LDS loads, through NSTAGE stages with one barrier per
+// step.  Code rows are 64 B with their 16-byte chunks XOR-swizzled by (row / 4) % 4, so the sixteen rows
+// a fragment read touches fall in sixteen distinct bank groups.  The scaled instruction applies both
+// scales and accumulates into the fp32 accumulators itself, so the loop holds no vector ALU work.
+// Same instruction sequence per output as gemm_mx_kernel (one K step after another into the same
+// accumulator), so the results are bit-identical to it.  SILU_MUL stages h in LDS and one thread per
+// (row, 32-column block) quantizes it into row-major codes and scale bytes.
+constexpr int kMxMmBM = 128, kMxMmBN = 256;
+constexpr int kMxMmA = kMxMmBM * 64, kMxMmB = kMxMmBN * 64;  // code bytes per stage
+constexpr int kMxMmStage = kMxMmA + kMxMmB + (kMxMmBM + kMxMmBN) * 4;
+constexpr int kMxMmHLD = kMxMmBN / 2 + 4;                     // padded LDS row of the h tile (floats)
+
+// Direct global->LDS 4-byte load (lane l writes LDS bytes [4l, 4l+4) after the wave-uniform base).
+__device__ __forceinline__ void g2lds4_mx(const void* g, void* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
+  asm volatile("global_load_lds_dword %0, off" : : "v"(g), "{m0}"(lds) : "memory");
+}
+
+__device__ __forceinline__ int mx_swz(int row) { return (row >> 2) & 3; }
+
+// s_waitcnt vmcnt(n) for a run-time n in [0, 8].
+__device__ __forceinline__ void wait_vmcnt_upto8(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    default: wait_vmcnt<8>(); break;
+  }
+}
+
+template <int EPI, bool OUT_F32, int MODE, int NSTAGE>
+__global__ __launch_bounds__(512) void gemm_mx_mm(MxGemmArgs p) {
+  constexpr int MI = 4, NI = 4;
+  constexpr bool WPK = MODE == 1;
+  static_assert(NSTAGE >= 3 && NSTAGE * kMxMmStage >= kMxMmBM * kMxMmHLD * 4, "stages also hold the h tile");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * kMxMmStage];
+  __shared__ int32_t sRow[kMxMmBM];
+  const int N = p.N, K = p.K;
+  const int ncols = EPI == MOE_EPI_SILU_MUL ? N / 2 : N;
+  const int bcols = EPI == MOE_EPI_SILU_MUL ? kMxMmBN / 2 : kMxMmBN;
+  const int nbn = (ncols + bcols - 1) / bcols;
+  const int nbx = (nbn + 7) / 8;
+  const long long b = linear_block();
+  const int xcd = (int)(b & 7);
+  const long long jb = b >> 3;
+  const int tile = (int)(jb / nbx), nb = xcd + 8 * (int)(jb % nbx);
+  if (nb >= nbn || tile >= *p.num_tiles) return;
+  const int e = p.tiles[3 * tile], row0 = p.tiles[3 * tile + 1], rows = p.tiles[3 * tile + 2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int l16 = lane & 15, q = lane >> 4;
+  const int nks = K / 128;
+  const int KB = K / 2, KS = K / 32;  // code and scale bytes per row
+
+  for (int i = tid; i < kMxMmBM; i += 512) {
+    const int r = row0 + (i < rows ? i : 0);
+    sRow[i] = p.a_row_of ? p.a_row_of[r] / p.a_row_div : r;
+  }
+  __syncthreads();
+
+  // weight row of tile column nt (0..255): SILU_MUL puts the 128 gate rows first, then their up rows
+  auto wrow = [&](int nt) -> int {
+    int n;
+    if (EPI == MOE_EPI_SILU_MUL) {
+      const int j = nb * (kMxMmBN / 2) + (nt & 127);
+      n = j < N / 2 ? (nt < 128 ? j : N / 2 + j) : 0;
+    } else {
+      n = nb * kMxMmBN + nt;
+      if (n >= N) n = 0;
+    }
+    return n;
+  };
+  // code sources: one instruction covers 16 rows (lane l: row l / 4, LDS chunk l % 4, which holds the
+  // row's global chunk (l % 4) ^ swizzle, i.e. K elements [32 c, 32 c + 32) of the step)
+  const uint8_t* a_src;
+  {
+    const int r = 16 * wave + (lane >> 2);
+    a_src = p.Aq + (size_t)sRow[r] * KB + 16 * ((lane & 3) ^ mx_swz(r));
+  }
+  const uint8_t* b_src[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int nt = 16 * (2 * wave + t) + (lane >> 2);
+    const int c = (lane & 3) ^ mx_swz(nt);
+    const int n = wrow(nt);
+    if (WPK) b_src[t] = p.Wq + ((size_t)e * (N / 16) + n / 16) * (size_t)nks * 1024 + 16 * (c * 16 + n % 16);
+    else b_src[t] = p.Wq + ((size_t)e * N + n) * KB + 16 * c;
+  }
+  // scale sources: waves 0, 1 the 128 activation rows (4 bytes = the step's four blocks of a row);
+  // waves 2..5 the weights: canonical 4 bytes per row, packed the 64-byte scale blocks of 16 rows
+  const uint8_t* s_src = nullptr;
+  if (wave < 2) {
+    s_src = p.As + (size_t)sRow[64 * wave + lane] * KS;
+  } else if (wave < 6) {
+    if (WPK) {
+      const int rb = 4 * (wave - 2) + (lane >> 4);
+      const int n0 = wrow(16 * rb);
+      s_src = p.We + ((size_t)e * (N / 16) + n0 / 16) * (size_t)nks * 64 + 4 * (lane & 15);
+    } else {
+      s_src = p.We + ((size_t)e * N + wrow(64 * (wave - 2) + lane)) * KS;
+    }
+  }
+
+  auto issue = [&](int ks, int stage) {
+    uint8_t* st = smem + stage * kMxMmStage;
+    g2lds16(a_src + (size_t)ks * 64, st + wave * 1024);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      g2lds16(b_src[t] + (size_t)ks * (WPK ? 1024 : 64), st + kMxMmA + (2 * wave + t) * 1024);
+    if (wave < 2) g2lds4_mx(s_src + (size_t)ks * 4, st + kMxMmA + kMxMmB + wave * 256);
+    else if (wave < 6)
+      g2lds4_mx(s_src + (size_t)ks * (WPK ? 64 : 4), st + kMxMmA + kMxMmB + kMxMmBM * 4 + (wave - 2) * 256);
+  };
+
+  int ntile[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+    ntile[ni] = EPI == MOE_EPI_SILU_MUL ? (ni < 2 ? wn * 32 + ni * 16 : 128 + wn * 32 + (ni - 2) * 16) + l16
+                                        : wn * 64 + ni * 16 + l16;
+
+  f32x4 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto frag = [&](const uint8_t* base, int row) -> i32x8 {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(base + row * 64 + 16 * (q ^ mx_swz(row)));
+    return i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+  };
+
+  auto compute = [&](int stage) {
+    const uint8_t* st = smem + stage * kMxMmStage;
+    const uint8_t* sa = st + kMxMmA + kMxMmB;
+    const uint8_t* sb = sa + kMxMmBM * 4;
+    i32x8 bf[NI];
+    int bs[NI];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int nt = ntile[ni];
+      bf[ni] = frag(st + kMxMmA, nt);
+      bs[ni] = WPK ? sb[(nt >> 4) * 64 + 16 * q + (nt & 15)] : sb[nt * 4 + q];
+    }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int r = wm * 64 + mi * 16 + l16;
+      const i32x8 af = frag(st, r);
+      const int as = sa[r * 4 + q];
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[ni], acc[mi][ni], 4, 4, 0, as, 0, bs[ni]);
+    }
+  };
+
+  // Per-step direct loads of each wave: 4 (waves 0..5) or 3 (waves 6, 7).  Step s lives in stage
+  // s % NSTAGE; before reading it a wave waits until only the loads of the steps after s that it has
+  // already issued are outstanding, then the barrier publishes everyone's.
+  const int per_step = wave < 6 ? 4 : 3;
+#pragma unroll
+  for (int u = 0; u < NSTAGE - 1; ++u)
+    if (u < nks) issue(u, u);
+  for (int s = 0; s < nks; ++s) {
+    wait_vmcnt_upto8(min(nks - 1 - s, NSTAGE - 2) * per_step);
+    __syncthreads();
+    if (s + NSTAGE - 1 < nks) issue(s + NSTAGE - 1, (s + NSTAGE - 1) % NSTAGE);
+    compute(s % NSTAGE);
+  }
+
+  if constexpr (EPI == MOE_EPI_SILU_MUL) {
+    float* htile = reinterpret_cast<float*>(smem);
+    __syncthreads();  // every wave is done with the stages
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          htile[(wm * 64 + mi * 16 + 4 * q + rr) * kMxMmHLD + wn * 32 + ni * 16 + l16] =
+              silu_f32(acc[mi][ni][rr]) * acc[mi][ni + 2][rr];
+    __syncthreads();
+    const int row = tid >> 2, blk = tid & 3;
+    const int hcol = nb * (kMxMmBN / 2) + blk * 32;
+    if (row < rows && hcol < N / 2) {
+      float v[32];
+      float amax = 0.f;
+      const float4* src = reinterpret_cast<const float4*>(htile + row * kMxMmHLD + blk * 32);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const float4 f = src[d];
+        v[4 * d] = f.x;
+        v[4 * d + 1] = f.y;
+        v[4 * d + 2] = f.z;
+        v[4 * d + 3] = f.w;
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
+      }
+      const int ex = mx_block_exp(amax);
+      const size_t orow = (size_t)(row0 + row);
+      *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(p.C) + orow * (N / 4) + hcol / 2) = mx_encode32(v, ex);
+      p.Cs[orow * (N / 64) + hcol / 32] = (uint8_t)(ex + 127);
+    }
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = wm * 64 + mi * 16 + 4 * q + rr;
+        if (row >= rows) continue;
+        const size_t orow = (size_t)(row0 + row);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int n = nb * kMxMmBN + wn * 64 + ni * 16 + l16;
+          if (n >= N) continue;
+          if (OUT_F32) static_cast<float*>(p.C)[orow * N + n] = acc[mi][ni][rr];
+          else static_cast<uint16_t*>(p.C)[orow * N + n] = f32_to_bf16_bits(acc[mi][ni][rr]);
+        }
+      }
+  }
+}
+
+template <int MODE>
+static hipError_t launch_mx_mm(const MxGemmArgs& a, hipStream_t s) {
+  const int ncols = a.epilogue == MOE_EPI_SILU_MUL ? a.N / 2 : a.N;
+  const int bcols = a.epilogue == MOE_EPI_SILU_MUL ? kMxMmBN / 2 : kMxMmBN;
+  const int nbn = (ncols + bcols - 1) / bcols;
+  const dim3 grid = grid2d(8LL * ((nbn + 7) / 8) * a.max_tiles);
+  if (a.epilogue == MOE_EPI_SILU_MUL) gemm_mx_mm<MOE_EPI_SILU_MUL, false, MODE, 3><<<grid, 512, 0, s>>>(a);
+  else if (a.out_f32) gemm_mx_mm<MOE_EPI_NONE, true, MODE, 3><<<grid, 512, 0, s>>>(a);
+  else gemm_mx_mm<MOE_EPI_NONE, false, MODE, 3><<<grid, 512, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int KW, int PF, int MODE>
 static void launch_mx_mode(const MxGemmArgs& a, dim3 grid, hipStream_t s) {
   if (a.epilogue == MOE_EPI_SILU_MUL) gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_SILU_MUL, false, MODE><<<grid, 256, 0, s>>>(a);
@@ -435,6 +679,7 @@ constexpr int kMxSplitKMaxTiles = 32;
 
 hipError_t launch_grouped_gemm_mx(const MxGemmArgs& a, int block_m, hipStream_t stream) {
   if (a.max_tiles <= 0) return hipSuccess;
+  if (block_m == 128) return a.mode == 1 ? launch_mx_mm<1>(a, stream) : launch_mx_mm<0>(a, stream);
   switch (block_m) {
     case 16:
       if (a.max_tiles <= kMxSplitKMaxTiles) return launch_mx_cfg<16, 64, 4, 2>(a, stream);

@@ -239,7 +239,9 @@ def test_mxfp4_entry_points_reject(lib):
                                                 kw.get("K", 256), f, 8, f, kw.get("bm", 16), kw.get("epi", 0), f,
                                                 kw.get("cs", f), 1, None)
     assert g(K=100) == -2
-    assert g(bm=128) == -2                                         # MXFP4 tiles are 16, 32 or 64 rows
+    assert g(bm=256) == -2                                         # MXFP4 tiles are 16, 32, 64 or 128 rows
+    assert g(bm=128, K=160) == -2                                  # the 128-row kernel steps K by 128
+    assert g(bm=128, act=1, lay=1) == -2                           # ... and reads row-major activations
     assert g(epi=1, N=96) == -2                                    # h blocks of 32 need N % 64 == 0
     assert g(epi=1, cs=None) == -1
     assert g(lay=1, K=160) == -2
@@ -251,7 +253,9 @@ def test_mxfp4_entry_points_reject(lib):
     assert qt(K=96) == -1
     assert qt(bm=128) == -2
     # layer
-    assert moe.moe_ffn_mxfp4_block_m(800, 256, 8) == 32
+    assert moe.moe_ffn_mxfp4_block_m(800, 2048, 512, 256, 8) == 32
+    assert moe.moe_ffn_mxfp4_block_m(4096, 4096, 14336, 8, 2) == 128  # large experts: the LDS-staged kernel
+    assert moe.moe_ffn_mxfp4_block_m(4096, 4096, 14336 + 32, 8, 2) == 64  # ... which needs K % 128 == 0
     assert moe.moe_ffn_mxfp4_workspace_bytes(16, 256, 96, 8, 2) > 0
     assert moe.moe_ffn_mxfp4_workspace_bytes(16, 250, 96, 8, 2) == 0
     ws = moe.moe_ffn_mxfp4_workspace_bytes(16, 256, 128, 8, 2)

@@ -96,6 +96,8 @@ def _mx_operands(rows, N, K, E, seed):
 
 # (T, E, k, bm): few tiles take the K-split kernel, more tiles the N-split one
 GEMM_CASES = [(3, 8, 2, 16), (40, 16, 4, 16), (90, 12, 3, 32), (300, 8, 2, 64)]
+# the 128-row LDS-staged kernel needs K % 128 == 0
+MM_CASES = [(600, 4, 2, 128), (700, 6, 3, 128)]
 
 
 @pytest.mark.parametrize("T,E,k,bm", GEMM_CASES)
@@ -116,9 +118,62 @@ def test_grouped_gemm_mxfp4_plain(T, E, k, bm, N, K):
     assert np.all(np.abs(got - ref) <= (64 + K / 32) * 2.0 ** -24 * ref_abs + 1e-30)
 
 
-@pytest.mark.parametrize("T,E,k,bm", GEMM_CASES)
+@pytest.mark.parametrize("T,E,k,bm", MM_CASES)
+@pytest.mark.parametrize("N,K", [(512, 2048), (200, 384)])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_grouped_gemm_mxfp4_large_tile(T, E, k, bm, N, K, layout):
+    ids, al = _routing(T, E, k, bm, seed=T * 3 + N)
+    R = T * k
+    if layout == 1 and N % 16:
+        N = 208
+    Aq, As, Wq, We = _mx_operands(R, N, K, E, seed=K + N)
+    tiles = gu.dev(np.ascontiguousarray(al["tiles"].astype(np.int32)))
+    nt = gu.dev(np.array([al["num_tiles"]], np.int32))
+    dWq, dWe = gu.dev(Wq), gu.dev(We)
+    if layout == 1:
+        dWq, dWe = moe.moe_mx_prepack(dWq, dWe)
+    C = moe.moe_grouped_gemm_mxfp4(gu.dev(Aq), gu.dev(As), None, 1, dWq, dWe, tiles, al["num_tiles"], nt, bm,
+                                   moe.MOE_EPI_NONE, R, weight_layout=layout)
+    torch.cuda.synchronize()
+    got = C.cpu().numpy().astype(np.float64)
+    ref = oracle.grouped_proj_mx(Aq, As, None, 1, Wq, We, al["offsets"])
+    ref_abs = oracle.grouped_proj_mx(Aq & 0x77, As, None, 1, Wq & 0x77, We, al["offsets"])
+    assert np.all(np.abs(got - ref) <= (64 + K / 32) * 2.0 ** -24 * ref_abs + 1e-30)
+
+
+@pytest.mark.parametrize("epi", [0, 1])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_grouped_gemm_mxfp4_large_tile_matches_register_kernel_bits(epi, layout):
+    # the 128-row LDS-staged kernel issues the same scaled instructions per output as the 64-row
+    # register kernel: identical bits (fp32 output, or h codes and scale bytes) on the same routing
+    T, E, k, N, K = 500, 6, 2, 512, 1024
+    rng = np.random.default_rng(51)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    R = T * k
+    Aq, As, Wq, We = _mx_operands(T if epi else R, N, K, E, seed=52)
+    dWq, dWe = gu.dev(Wq), gu.dev(We)
+    if layout == 1:
+        dWq, dWe = moe.moe_mx_prepack(dWq, dWe)
+    outs = []
+    for bm in (64, 128):
+        al = oracle.align(ids, E, bm)
+        tiles = gu.dev(np.ascontiguousarray(al["tiles"].astype(np.int32)))
+        nt = gu.dev(np.array([al["num_tiles"]], np.int32))
+        aro = gu.dev(al["sorted_ids"].astype(np.int32)) if epi else None
+        out = moe.moe_grouped_gemm_mxfp4(gu.dev(Aq), gu.dev(As), aro, k if epi else 1, dWq, dWe, tiles,
+                                         al["num_tiles"], nt, bm, moe.MOE_EPI_SILU_MUL if epi else moe.MOE_EPI_NONE,
+                                         R, weight_layout=layout)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy() for t in out] if epi else [out.view(torch.int32).cpu().numpy()])
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("T,E,k,bm", GEMM_CASES + MM_CASES[:1])
 @pytest.mark.parametrize("I,K", [(128, 2048), (96, 160)])
 def test_grouped_gemm_mxfp4_silu_quantized_h(T, E, k, bm, I, K):
+    if bm == 128 and K % 128:
+        pytest.skip("the 128-row kernel steps K by 128")
     ids, al = _routing(T, E, k, bm, seed=T + I)
     R = T * k
     Aq, _, Wq, We = _mx_operands(T, 2 * I, K, E, seed=I + bm)
