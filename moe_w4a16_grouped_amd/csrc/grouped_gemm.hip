@@ -689,7 +689,9 @@ struct SplitK {
 
 // Tile lists of at most this capacity (16-row tiles) use the split-K kernel: measured on MI355X at
 // one token with 128 experts top-8, 8 tiles (weights streamed from HBM), gate_up takes 6.5 us with
-// K split 8 ways against 9.1 us for the tiled kernel, down 4.1 us against 5.1 us.
+// K split 8 ways against 9.1 us for the tiled kernel, down 4.1 us against 5.1 us.  Swept again with
+// HIP events at 1 and 3 tokens: 32-column blocks with K split 4 ways take 9.1 / 14.8 us for gate_up
+// against 10.4 / 19.7 us for 64-column blocks split 8 ways.
 constexpr int kSplitKMaxTiles = 32;
 
 template <class Cfg, int EPI, bool F32>
@@ -728,8 +730,6 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t strea
   switch (block_m) {
     case 16:
       if (a.max_tiles <= kSplitKMaxTiles) {
-        // gate_up (K = hidden): K split 8 ways; down (K = intermediate, shorter): 32-column blocks
-        if (a.epilogue == MOE_EPI_SILU_MUL) return by_variant<SplitK<16, 64, 2, 8>>(a, stream);
         return by_variant<SplitK<16, 32, 2, 4>>(a, stream);
       }
       // 256-column blocks once the grid holds three workgroups per CU (768) with them: measured on
