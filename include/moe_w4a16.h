@@ -378,6 +378,7 @@ moe_status_t moe_ffn_forward_mxfp4(const uint16_t* x, const float* router_logits
  */
 #define MOE_IN_BF16 0
 #define MOE_IN_F32 1
+#define MOE_OUT_F8 2  /* SILU_MUL output of moe_grouped_gemm_f8 quantized per 1x128 (codes + fp32 scales) */
 
 /* x [rows, K] (bf16 bits, or fp32 with in_dtype MOE_IN_F32) -> codes q [rows, K] and fp32 scales
  * s [rows, K/128] (the conversion above).  Shapes: 0 <= rows < 2^26, K a positive multiple of 128.
@@ -391,8 +392,11 @@ moe_status_t moe_f8_quantize(const void* x, int32_t in_dtype, int32_t rows, int3
  * a = (a_row_of ? a_row_of[r] / a_row_div : r):
  *   G[r, n] = sum_k A[a, k] * W_e[n, k],  A = (Aq [*, K], As [*, K/128]), W = (Wq [E, N, K], Ws [E, N, K/128]).
  *   epilogue NONE:     C [rows, N], fp32 or bf16 (out_dtype).
- *   epilogue SILU_MUL: C [rows, N/2] fp32, h[r, j] = silu(G[r, j]) * G[r, N/2 + j] (out_dtype must be
- *                      MOE_OUT_F32; moe_f8_quantize then quantizes h for the next projection).
+ *   epilogue SILU_MUL: h[r, j] = silu(G[r, j]) * G[r, N/2 + j] in fp32, stored as
+ *                      out_dtype MOE_OUT_F32: C [rows, N/2] fp32 (moe_f8_quantize then quantizes it), or
+ *                      out_dtype MOE_OUT_F8: quantized in the epilogue exactly as moe_f8_quantize would,
+ *                      C = codes [rows, N/2], Cs = fp32 scales [rows, N/256]; needs block_m 128 and
+ *                      N/2 % 128 == 0.  Cs is unused (may be NULL) for the other output types.
  * Rows of C that no tile covers are not written.  block_m 16, 32, 64 or 128 (the tile height
  * moe_align used).  With block_m 16 or 32 the waves of a workgroup split K (four ways when block_m
  * is 16 and max_tiles <= 32, else two) and add their fp32 partials in wave order, so bits can
@@ -404,7 +408,7 @@ moe_status_t moe_f8_quantize(const void* x, int32_t in_dtype, int32_t rows, int3
 moe_status_t moe_grouped_gemm_f8(const uint8_t* Aq, const float* As, const int32_t* a_row_of, int32_t a_row_div,
                                  const uint8_t* Wq, const float* Ws, int32_t E, int32_t N, int32_t K,
                                  const int32_t* tiles, int32_t max_tiles, const int32_t* num_tiles, int32_t block_m,
-                                 int32_t epilogue, void* C, int32_t out_dtype, void* stream);
+                                 int32_t epilogue, void* C, float* Cs, int32_t out_dtype, void* stream);
 
 /* Row-tile height and workspace bytes of moe_ffn_forward_f8 (host-only, pure; -1 / 0 on invalid sizes). */
 int32_t moe_ffn_f8_block_m(int32_t T, int32_t E, int32_t k);
@@ -412,7 +416,8 @@ size_t moe_ffn_f8_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, in
 
 /*
  * The whole FP8 (W8A8, per-1x128) layer [ATOM, 6.1 and 8.1-8.2]: route -> permute -> x quantized ->
- * gate_up (SiLU*mul, h in fp32) -> h quantized -> down (fp32) -> combine, all enqueued on `stream`:
+ * gate_up (SiLU*mul, h in fp32) -> h quantized (in the gate_up epilogue with 128-row tiles) -> down
+ * (fp32) -> combine, all enqueued on `stream`:
  *   y[t] = sum_s w[t,s] * W2_e(s) Q( silu(W1_e(s) Q(x[t])) * (W3_e(s) Q(x[t])) ),  Q = FP8 quantization.
  *   x bf16 [T, H]; router_logits fp32 [T, E]; w13_q [E, 2I, H], w13_s [E, 2I, H/128] fp32,
  *   w2_q [E, H, I], w2_s [E, H, I/128] fp32; y bf16 [T, H].  Optional routing copies as for

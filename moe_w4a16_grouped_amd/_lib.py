@@ -31,6 +31,7 @@ MOE_ACT_ROWS = 0
 MOE_ACT_TILED = 1
 MOE_IN_BF16 = 0
 MOE_IN_F32 = 1
+MOE_OUT_F8 = 2
 
 _lib = None
 
@@ -76,7 +77,7 @@ def load() -> ctypes.CDLL:
         "moe_ffn_block_forward": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, I32, P, P, P, P, P,
                                    SZ, P], I32),
         "moe_f8_quantize": ([P, I32, I32, I32, P, P, P], I32),
-        "moe_grouped_gemm_f8": ([P, P, P, I32, P, P, I32, I32, I32, P, I32, P, I32, I32, P, I32, P], I32),
+        "moe_grouped_gemm_f8": ([P, P, P, I32, P, P, I32, I32, I32, P, I32, P, I32, I32, P, P, I32, P], I32),
         "moe_ffn_f8_block_m": ([I32, I32, I32], I32),
         "moe_ffn_f8_workspace_bytes": ([I32, I32, I32, I32, I32], SZ),
         "moe_ffn_forward_f8": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, SZ, P], I32),
@@ -433,19 +434,26 @@ def moe_f8_quantize(x, q=None, s=None, stream=None):
 
 
 def moe_grouped_gemm_f8(Aq, As, a_row_of, a_row_div: int, Wq, Ws, tiles, max_tiles: int, num_tiles, block_m: int,
-                        epilogue: int, out_rows: int, out_dtype: int = MOE_OUT_F32, C=None, stream=None):
+                        epilogue: int, out_rows: int, out_dtype: int = MOE_OUT_F32, C=None, Cs=None, stream=None):
     """Grouped FP8 GEMM over the tile list.  NONE: returns C [out_rows, N] (fp32 or bf16); SILU_MUL:
-    returns h fp32 [out_rows, N/2]."""
+    returns h fp32 [out_rows, N/2], or with out_dtype MOE_OUT_F8 the quantized h as (codes uint8
+    [out_rows, N/2], scales fp32 [out_rows, N/256])."""
     _req(Aq, torch.uint8, "Aq")
     _req(Wq, torch.uint8, "Wq")
     E, N, K = Wq.shape
-    if C is None:
+    if out_dtype == MOE_OUT_F8:
+        if C is None:
+            C = torch.empty((out_rows, N // 2), dtype=torch.uint8, device=Aq.device)
+        if Cs is None:
+            Cs = torch.empty((out_rows, max(N // 256, 1)), dtype=torch.float32, device=Aq.device)
+    elif C is None:
         cols = N // 2 if epilogue == MOE_EPI_SILU_MUL else N
         dt = torch.float32 if out_dtype == MOE_OUT_F32 else torch.bfloat16
         C = torch.empty((out_rows, cols), dtype=dt, device=Aq.device)
     _check(load().moe_grouped_gemm_f8(_p(Aq), _p(As), _p(a_row_of), a_row_div, _p(Wq), _p(Ws), E, N, K, _p(tiles),
-                                      max_tiles, _p(num_tiles), block_m, epilogue, _p(C), out_dtype, _stream(stream)))
-    return C
+                                      max_tiles, _p(num_tiles), block_m, epilogue, _p(C), _p(Cs), out_dtype,
+                                      _stream(stream)))
+    return (C, Cs) if out_dtype == MOE_OUT_F8 else C
 
 
 def moe_ffn_f8_block_m(T: int, E: int, k: int) -> int:

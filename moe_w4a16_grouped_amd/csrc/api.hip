@@ -734,7 +734,7 @@ moe_status_t moe_f8_quantize(const void* x, int32_t in_dtype, int32_t rows, int3
 moe_status_t moe_grouped_gemm_f8(const uint8_t* Aq, const float* As, const int32_t* a_row_of, int32_t a_row_div,
                                  const uint8_t* Wq, const float* Ws, int32_t E, int32_t N, int32_t K,
                                  const int32_t* tiles, int32_t max_tiles, const int32_t* num_tiles, int32_t block_m,
-                                 int32_t epilogue, void* C, int32_t out_dtype, void* stream) {
+                                 int32_t epilogue, void* C, float* Cs, int32_t out_dtype, void* stream) {
   if (E < 1 || N < 1 || K < 1 || max_tiles < 0 || a_row_div < 1)
     return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_f8: need E, N, K, a_row_div >= 1, max_tiles >= 0");
   if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_grouped_gemm_f8: E=%d exceeds %d", E, MOE_MAX_EXPERTS);
@@ -744,17 +744,21 @@ moe_status_t moe_grouped_gemm_f8(const uint8_t* Aq, const float* As, const int32
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_grouped_gemm_f8: block_m=%d must be 16, 32, 64 or 128", block_m);
   if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SILU_MUL)
     return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_f8: unknown epilogue %d", epilogue);
-  if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32)
+  if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32 && out_dtype != MOE_OUT_F8)
     return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_f8: unknown out_dtype %d", out_dtype);
-  if (epilogue == MOE_EPI_SILU_MUL && (N % 2 != 0 || out_dtype != MOE_OUT_F32))
-    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_f8: SILU_MUL needs an even N and out_dtype F32");
+  if (epilogue == MOE_EPI_SILU_MUL && (N % 2 != 0 || out_dtype == MOE_OUT_BF16))
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_f8: SILU_MUL needs an even N and out_dtype F32 or F8");
+  if (out_dtype == MOE_OUT_F8 && (epilogue != MOE_EPI_SILU_MUL || block_m != 128 || (N / 2) % 128 != 0))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE,
+                "moe_grouped_gemm_f8: out_dtype F8 needs SILU_MUL, block_m 128 and N/2 %% 128 == 0 (N=%d)", N);
   if (max_tiles == 0) return ok();
-  if (!Aq || !As || !Wq || !Ws || !tiles || !num_tiles || !C)
+  if (!Aq || !As || !Wq || !Ws || !tiles || !num_tiles || !C || (out_dtype == MOE_OUT_F8 && !Cs))
     return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_f8: NULL pointer");
-  if (!aligned16(Aq) || !aligned16(Wq) || !aligned16(C) || !aligned4(As) || !aligned4(Ws) || !aligned4(tiles))
-    return fail(MOE_ERR_MISALIGNED, "moe_grouped_gemm_f8: Aq, Wq, C need 16-byte alignment, As, Ws 4-byte");
+  if (!aligned16(Aq) || !aligned16(Wq) || !aligned16(C) || !aligned4(As) || !aligned4(Ws) || !aligned4(tiles) ||
+      (Cs && !aligned4(Cs)))
+    return fail(MOE_ERR_MISALIGNED, "moe_grouped_gemm_f8: Aq, Wq, C need 16-byte alignment, As, Ws, Cs 4-byte");
   moe::F8GemmArgs a{Aq, As, a_row_of, a_row_div, Wq, Ws, N, K, tiles, num_tiles, max_tiles, C, epilogue,
-                    out_dtype == MOE_OUT_F32};
+                    out_dtype == MOE_OUT_F8 ? 2 : (out_dtype == MOE_OUT_F32 ? 1 : 0), Cs};
   return hip_status(moe::launch_grouped_gemm_f8(a, block_m, (hipStream_t)stream), "moe_grouped_gemm_f8 launch");
 }
 
@@ -819,11 +823,17 @@ moe_status_t moe_ffn_forward_f8(const uint16_t* x, const float* router_logits, i
   }
   e = moe::launch_f8_quant(x, false, T, H, xq, xs, s);
   if (e != hipSuccess) return hip_status(e, "x quantization launch");
-  moe::F8GemmArgs g1{xq, xs, sorted, k, w13_q, w13_s, 2 * I, H, tiles, ntiles, L.max_tiles, hf, MOE_EPI_SILU_MUL, 1};
+  // the 128-row kernel quantizes h in its epilogue (one 1x128 block per row and workgroup)
+  const bool fused_h = L.block_m == 128 && I % 128 == 0;
+  moe::F8GemmArgs g1{xq, xs, sorted, k, w13_q, w13_s, 2 * I, H, tiles, ntiles, L.max_tiles,
+                     fused_h ? static_cast<void*>(hq) : static_cast<void*>(hf), MOE_EPI_SILU_MUL, fused_h ? 2 : 1,
+                     fused_h ? hs : nullptr};
   e = moe::launch_grouped_gemm_f8(g1, L.block_m, s);
   if (e != hipSuccess) return hip_status(e, "gate_up launch");
-  e = moe::launch_f8_quant(hf, true, R, I, hq, hs, s);
-  if (e != hipSuccess) return hip_status(e, "h quantization launch");
+  if (!fused_h) {
+    e = moe::launch_f8_quant(hf, true, R, I, hq, hs, s);
+    if (e != hipSuccess) return hip_status(e, "h quantization launch");
+  }
   moe::F8GemmArgs g2{hq, hs, nullptr, 1, w2_q, w2_s, H, I, tiles, ntiles, L.max_tiles, o, MOE_EPI_NONE, 1};
   e = moe::launch_grouped_gemm_f8(g2, L.block_m, s);
   if (e != hipSuccess) return hip_status(e, "down launch");

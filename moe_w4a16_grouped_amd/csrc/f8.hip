@@ -297,7 +297,12 @@ __global__ __launch_bounds__(256) void gemm_f8_kernel(F8GemmArgs p) {
 // rows are 128 B with their 16-byte chunks XOR-swizzled by (row / 2) % 8, so the sixteen rows a
 // fragment read touches fall in sixteen distinct bank groups.  Same products, scale arithmetic and K
 // order as gemm_f8_kernel, so the results are bit-identical to it.
+// SILU_MUL with OUT == 2 quantizes h in the epilogue: a workgroup holds 128 h columns of each of its
+// rows, exactly one 1x128 block, so h goes through LDS once and one DPP row of 16 lanes per row takes
+// the block maximum and writes the E4M3 codes and the scale, with the arithmetic of f8_quant_kernel
+// (bit-identical to storing fp32 h and quantizing it there).
 constexpr int kF8MmBM = 128, kF8MmBN = 256;
+constexpr int kF8MmHLD = kF8MmBN / 2 + 4;  // padded LDS row of the h tile (floats)
 constexpr int kF8MmA = kF8MmBM * 128, kF8MmB = kF8MmBN * 128;  // code bytes per stage
 constexpr int kF8MmStage = kF8MmA + kF8MmB + (kF8MmBM + kF8MmBN) * 4;
 
@@ -310,9 +315,12 @@ __device__ __forceinline__ void g2lds4(const void* g, void* lds_wave_base) {
 
 __device__ __forceinline__ int f8_swz(int row) { return (row >> 1) & 7; }
 
-template <int EPI, bool OUT_F32, int NSTAGE>
+template <int EPI, int OUT, int NSTAGE>
 __global__ __launch_bounds__(512) void gemm_f8_mm(F8GemmArgs p) {
   constexpr int MI = 4, NI = 4;
+  constexpr bool OUT_F32 = OUT == 1;
+  static_assert(OUT != 2 || EPI == MOE_EPI_SILU_MUL, "quantized output is h");
+  static_assert(NSTAGE * kF8MmStage >= kF8MmBM * kF8MmHLD * 4, "stages also hold the h tile");
   __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * kF8MmStage];
   __shared__ int32_t sRow[kF8MmBM];
   const int N = p.N, K = p.K;
@@ -441,6 +449,49 @@ __global__ __launch_bounds__(512) void gemm_f8_mm(F8GemmArgs p) {
     compute(s % NSTAGE);
   }
 
+  if constexpr (OUT == 2) {
+    // h tile in LDS (the stages are free once every wave has passed this barrier)
+    float* htile = reinterpret_cast<float*>(smem);
+    __syncthreads();
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          htile[(wm * 64 + mi * 16 + 4 * q + rr) * kF8MmHLD + wn * 32 + ni * 16 + l16] =
+              silu_f32(acc[mi][ni][rr]) * acc[mi][ni + 2][rr];
+    __syncthreads();
+    // one DPP row (16 lanes, 8 columns each) per h row: 32 rows per pass over the 512 threads
+    const int hcol = nb * (kF8MmBN / 2);
+    const int part = lane & 15;
+#pragma unroll
+    for (int pass = 0; pass < kF8MmBM / 32; ++pass) {
+      const int row = pass * 32 + (tid >> 4);  // wave-uniform per 16-lane row
+      const float* src = htile + row * kF8MmHLD + part * 8;
+      float v[8];
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        v[j] = src[j];
+        amax = fmaxf(amax, fabsf(v[j]));
+      }
+      amax = row16_max(amax);
+      const float sc = amax / kE4M3Max;
+      u32x2 out = {0u, 0u};
+      if (sc != 0.f) {
+        out[0] = f8_encode4(v, sc);
+        out[1] = f8_encode4(v + 4, sc);
+      }
+      if (row < rows && hcol < N / 2) {
+        const size_t orow = (size_t)(row0 + row);
+        *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(p.C) + orow * (N / 2) + hcol + part * 8) = out;
+        if (part == 0) p.Cs[orow * (N / 256) + nb] = sc;
+      }
+    }
+    return;
+  }
+
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -467,12 +518,12 @@ __global__ __launch_bounds__(512) void gemm_f8_mm(F8GemmArgs p) {
     }
 }
 
-template <int EPI, bool F32>
+template <int EPI, int OUT>
 static hipError_t launch_f8_mm(const F8GemmArgs& a, hipStream_t s) {
   const int ncols = EPI == MOE_EPI_SILU_MUL ? a.N / 2 : a.N;
   const int bcols = EPI == MOE_EPI_SILU_MUL ? kF8MmBN / 2 : kF8MmBN;
   const int nbn = (ncols + bcols - 1) / bcols;
-  gemm_f8_mm<EPI, F32, 3><<<grid2d(8LL * ((nbn + 7) / 8) * a.max_tiles), 512, 0, s>>>(a);
+  gemm_f8_mm<EPI, OUT, 3><<<grid2d(8LL * ((nbn + 7) / 8) * a.max_tiles), 512, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -494,9 +545,10 @@ constexpr int kF8SplitKMaxTiles = 32;
 hipError_t launch_grouped_gemm_f8(const F8GemmArgs& a, int block_m, hipStream_t stream) {
   if (a.max_tiles <= 0) return hipSuccess;
   if (block_m == 128) {
-    if (a.epilogue == MOE_EPI_SILU_MUL) return launch_f8_mm<MOE_EPI_SILU_MUL, true>(a, stream);
-    if (a.out_f32) return launch_f8_mm<MOE_EPI_NONE, true>(a, stream);
-    return launch_f8_mm<MOE_EPI_NONE, false>(a, stream);
+    if (a.epilogue == MOE_EPI_SILU_MUL)
+      return a.out_f32 == 2 ? launch_f8_mm<MOE_EPI_SILU_MUL, 2>(a, stream) : launch_f8_mm<MOE_EPI_SILU_MUL, 1>(a, stream);
+    if (a.out_f32) return launch_f8_mm<MOE_EPI_NONE, 1>(a, stream);
+    return launch_f8_mm<MOE_EPI_NONE, 0>(a, stream);
   }
   // Configurations from sweeps on MI355X (HIP events, weights streamed from HBM): with 128 experts
   // top-8 at 8 and 64 tokens, gate_up takes 36 / 86 us with <16,64,KW2> against 43 / 90 us for

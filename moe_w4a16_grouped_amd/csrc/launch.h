@@ -107,9 +107,10 @@ struct F8GemmArgs {
   const int32_t* tiles;     // [max_tiles, 3]
   const int32_t* num_tiles;
   int max_tiles;
-  void* C;                  // NONE: fp32 or bf16 [rows, N]; SILU_MUL: fp32 h [rows, N/2]
+  void* C;                  // NONE: fp32 or bf16 [rows, N]; SILU_MUL: fp32 h [rows, N/2] or h codes
   int epilogue;             // MOE_EPI_*
-  int out_f32;
+  int out_f32;              // 0 bf16, 1 fp32, 2 (SILU_MUL, 128-row tiles) h quantized per 1x128
+  float* Cs;                // out_f32 == 2: h scales [rows, N/256]
 };
 hipError_t launch_grouped_gemm_f8(const F8GemmArgs& a, int block_m, hipStream_t stream);
 // x (bf16, or fp32 when in_f32) [rows, K] -> codes [rows, K] and scales [rows, K/128].

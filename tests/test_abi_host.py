@@ -282,7 +282,7 @@ def test_f8_entry_points_reject(lib):
     # grouped GEMM
     g = lambda **kw: lib.moe_grouped_gemm_f8(f, f, None, 1, f, f, 4, kw.get("N", 256), kw.get("K", 256), f,
                                              kw.get("mt", 8), f, kw.get("bm", 16), kw.get("epi", 0), kw.get("C", f),
-                                             kw.get("od", 1), None)
+                                             kw.get("cs", None), kw.get("od", 1), None)
     assert g(K=160) == -2
     assert g(K=32768 + 128) == -2                                  # activation scales of a tile staged in LDS
     assert g(bm=256) == -2
@@ -292,6 +292,11 @@ def test_f8_entry_points_reject(lib):
     assert g(C=None) == -1
     assert g(C=_ptr(FAKE + 8)) == -3
     assert g(mt=0, C=None) == 0                                    # no tiles: nothing to launch
+    assert g(epi=1, od=2, bm=64, cs=f) == -2                       # fused h quantization: 128-row tiles
+    assert g(epi=1, od=2, bm=128, N=384, cs=f) == -2               # ... and whole 1x128 blocks of h
+    assert g(epi=0, od=2, bm=128, cs=f) == -2                      # ... of the SiLU*mul output
+    assert g(epi=1, od=2, bm=128, N=512) == -1                     # ... into a scale array
+    assert g(epi=1, od=2, bm=128, N=512, cs=_ptr(FAKE + 2)) == -3
     # layer
     assert moe.moe_ffn_f8_block_m(800, 256, 8) == 32
     assert moe.moe_ffn_f8_block_m(4096, 8, 2) == 128               # large experts: the LDS-staged kernel

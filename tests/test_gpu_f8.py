@@ -339,6 +339,27 @@ def test_grouped_gemm_f8_large_tile_matches_register_kernel_bits(epi):
     np.testing.assert_array_equal(outs[0], outs[1])
 
 
+def test_grouped_gemm_f8_fused_h_quantization_matches_separate_quantizer_bits():
+    # SILU_MUL with out_dtype F8 (128-row kernel): the epilogue quantizes h exactly as moe_f8_quantize
+    # does on the fp32 h of the same kernel
+    T, E, k, I, K = 600, 5, 2, 384, 1024
+    ids, al = _routing(T, E, k, 128, seed=61)
+    R = T * k
+    Aq, As, Wq, Ws = _f8_operands(T, 2 * I, K, E, seed=62, full_range=True)
+    tiles = gu.dev(np.ascontiguousarray(al["tiles"].astype(np.int32)))
+    nt = gu.dev(np.array([al["num_tiles"]], np.int32))
+    srt = gu.dev(al["sorted_ids"].astype(np.int32))
+    args = (gu.dev(Aq), gu.dev(As), srt, k, gu.dev(Wq), gu.dev(Ws), tiles, al["num_tiles"], nt, 128, moe.MOE_EPI_SILU_MUL, R)
+    h = moe.moe_grouped_gemm_f8(*args)
+    q0, s0 = moe.moe_f8_quantize(h)
+    q1 = torch.full((R, I), 0x7F, dtype=torch.uint8, device="cuda")
+    s1 = torch.full((R, I // 128), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_grouped_gemm_f8(*args, out_dtype=moe.MOE_OUT_F8, C=q1, Cs=s1)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q1.cpu().numpy(), q0.cpu().numpy())
+    np.testing.assert_array_equal(s1.cpu().numpy().view(np.uint32), s0.cpu().numpy().view(np.uint32))
+
+
 # ---------------------------------------------------------------------------------------------------
 # whole layer
 
