@@ -327,12 +327,8 @@ __global__ __launch_bounds__(512) void gemm_f8_mm(F8GemmArgs p) {
   const int ncols = EPI == MOE_EPI_SILU_MUL ? N / 2 : N;
   const int bcols = EPI == MOE_EPI_SILU_MUL ? kF8MmBN / 2 : kF8MmBN;
   const int nbn = (ncols + bcols - 1) / bcols;
-  const int nbx = (nbn + 7) / 8;
-  const long long b = linear_block();
-  const int xcd = (int)(b & 7);
-  const long long jb = b >> 3;
-  const int tile = (int)(jb / nbx), nb = xcd + 8 * (int)(jb % nbx);
-  if (nb >= nbn || tile >= *p.num_tiles) return;
+  int tile, nb;
+  if (!mm_work(linear_block(), nbn, *p.num_tiles, tile, nb)) return;
   const int e = p.tiles[3 * tile], row0 = p.tiles[3 * tile + 1], rows = p.tiles[3 * tile + 2];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -523,7 +519,7 @@ static hipError_t launch_f8_mm(const F8GemmArgs& a, hipStream_t s) {
   const int ncols = EPI == MOE_EPI_SILU_MUL ? a.N / 2 : a.N;
   const int bcols = EPI == MOE_EPI_SILU_MUL ? kF8MmBN / 2 : kF8MmBN;
   const int nbn = (ncols + bcols - 1) / bcols;
-  gemm_f8_mm<EPI, OUT, 3><<<grid2d(8LL * ((nbn + 7) / 8) * a.max_tiles), 512, 0, s>>>(a);
+  gemm_f8_mm<EPI, OUT, 3><<<mm_grid(nbn, a.max_tiles), 512, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -476,9 +476,10 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a16_sk(GemmArgs p0) {
 // the loads of step s+NSTAGE-1 are issued right after the barrier of step s, into the stage computed
 // at step s-1.  Activation rows are 256-byte LDS rows whose 16-byte chunks are XOR-swizzled by
 // (row % 16), which makes the fragment reads conflict-free.
-// Work order is XCD-aware: workgroup b runs on XCD b % 8 (round-robin dispatch); on each XCD the
-// workgroups walk one row tile across that XCD's N blocks before the next tile, so the tile's
-// activations are fetched into that XCD's L2 once and reused by all of its N blocks.
+// Work order is XCD-aware (mm_work): workgroup b runs on XCD b % 8 (round-robin dispatch); with at
+// least 8 N blocks each XCD walks one row tile across its N blocks before the next tile, so the tile's
+// activations are fetched into that XCD's L2 once and reused by all of its N blocks; with fewer N
+// blocks the XCDs take contiguous shares of the tile list instead, so that none idles.
 
 constexpr int kMmBM = 128, kMmBN = 256;
 constexpr int kMmStage = kMmBM * 256 + (kMmBN / 16) * 1024 + (kMmBN / 16) * 128;  // A + codes + scales
@@ -645,12 +646,8 @@ __global__ __launch_bounds__(512) void gemm_w4a16_mm(GemmArgs p) {
   const int ncols = EPI == MOE_EPI_SILU_MUL ? p.N / 2 : p.N;
   const int bcols = EPI == MOE_EPI_SILU_MUL ? kMmBN / 2 : kMmBN;
   const int nbn = (ncols + bcols - 1) / bcols;
-  const int nbx = (nbn + 7) / 8;
-  const long long b = linear_block();
-  const int xcd = (int)(b & 7);
-  const long long j = b >> 3;
-  const int tile = (int)(j / nbx), nb = xcd + 8 * (int)(j % nbx);
-  if (nb >= nbn || tile >= tile_count(p, kMmBM)) return;
+  int tile, nb;
+  if (!mm_work(linear_block(), nbn, tile_count(p, kMmBM), tile, nb)) return;
   mm_tile<EPI, OUT_F32, NSTAGE>(p, tile, nb, smem, sRow);
 }
 
@@ -715,7 +712,7 @@ static hipError_t launch_mm(const GemmArgs& a, hipStream_t s) {
   const int ncols = EPI == MOE_EPI_SILU_MUL ? a.N / 2 : a.N;
   const int bcols = EPI == MOE_EPI_SILU_MUL ? 128 : 256;
   const int nbn = (ncols + bcols - 1) / bcols;
-  gemm_w4a16_mm<EPI, F32, 3><<<grid2d(8LL * ((nbn + 7) / 8) * a.max_tiles), 512, 0, s>>>(a);
+  gemm_w4a16_mm<EPI, F32, 3><<<mm_grid(nbn, a.max_tiles), 512, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -109,4 +109,25 @@ static inline dim3 grid2d(long long total) {
   return dim3(kGridX, (unsigned)((total + kGridX - 1) / kGridX));
 }
 
+// Work order of the large-tile (LDS-staged) kernels.  With at least 8 N blocks, XCD x takes the N
+// blocks nb = x, x + 8, ... of every tile, tile after tile: a tile's activations are fetched once
+// per XCD and each XCD's L2 keeps its own share of an expert's weight columns across the expert's
+// tiles.  With fewer N blocks that order would leave XCDs idle, so the XCDs take contiguous shares of
+// the tile list instead (xcd_tile).  The grid comes from mm_grid.
+__device__ __forceinline__ bool mm_work(long long b, int nbn, int num_tiles, int& tile, int& nb) {
+  if (nbn >= 8) {
+    const int nbx = (nbn + 7) / 8;
+    const long long j = b >> 3;
+    tile = (int)(j / nbx);
+    nb = (int)(b & 7) + 8 * (int)(j % nbx);
+    return nb < nbn && tile < num_tiles;
+  }
+  return xcd_tile(b, nbn, num_tiles, tile, nb);
+}
+
+static inline dim3 mm_grid(int nbn, int max_tiles) {
+  if (nbn >= 8) return grid2d(8LL * ((nbn + 7) / 8) * max_tiles);
+  return grid2d(8LL * ((max_tiles + 7) / 8) * nbn);
+}
+
 }  // namespace moe

@@ -462,12 +462,8 @@ __global__ __launch_bounds__(512) void gemm_mx_mm(MxGemmArgs p) {
   const int ncols = EPI == MOE_EPI_SILU_MUL ? N / 2 : N;
   const int bcols = EPI == MOE_EPI_SILU_MUL ? kMxMmBN / 2 : kMxMmBN;
   const int nbn = (ncols + bcols - 1) / bcols;
-  const int nbx = (nbn + 7) / 8;
-  const long long b = linear_block();
-  const int xcd = (int)(b & 7);
-  const long long jb = b >> 3;
-  const int tile = (int)(jb / nbx), nb = xcd + 8 * (int)(jb % nbx);
-  if (nb >= nbn || tile >= *p.num_tiles) return;
+  int tile, nb;
+  if (!mm_work(linear_block(), nbn, *p.num_tiles, tile, nb)) return;
   const int e = p.tiles[3 * tile], row0 = p.tiles[3 * tile + 1], rows = p.tiles[3 * tile + 2];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -647,7 +643,7 @@ static hipError_t launch_mx_mm(const MxGemmArgs& a, hipStream_t s) {
   const int ncols = a.epilogue == MOE_EPI_SILU_MUL ? a.N / 2 : a.N;
   const int bcols = a.epilogue == MOE_EPI_SILU_MUL ? kMxMmBN / 2 : kMxMmBN;
   const int nbn = (ncols + bcols - 1) / bcols;
-  const dim3 grid = grid2d(8LL * ((nbn + 7) / 8) * a.max_tiles);
+  const dim3 grid = mm_grid(nbn, a.max_tiles);
   if (a.epilogue == MOE_EPI_SILU_MUL) gemm_mx_mm<MOE_EPI_SILU_MUL, false, MODE, 3><<<grid, 512, 0, s>>>(a);
   else if (a.out_f32) gemm_mx_mm<MOE_EPI_NONE, true, MODE, 3><<<grid, 512, 0, s>>>(a);
   else gemm_mx_mm<MOE_EPI_NONE, false, MODE, 3><<<grid, 512, 0, s>>>(a);
