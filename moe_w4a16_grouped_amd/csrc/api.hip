@@ -186,8 +186,24 @@ moe_status_t run_ffn(const uint16_t* x, const float* router_logits, int32_t T, i
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
   float* o = reinterpret_cast<float*>(ws + L.o);
   const int R = T * k;
+  const int packed = weight_layout == MOE_LAYOUT_PACKED;
+  const int shared_tiles = sw.w13_q ? (T + L.block_m - 1) / L.block_m : 0;
   hipError_t e;
-  if (moe::route_align_fused_fits(T, E, k)) {
+  moe::GemmArgs g1{x, sorted, k, w13_q, w13_s, 2 * I, H, tiles, ntiles, L.max_tiles + shared_tiles, 0, h,
+                   MOE_EPI_SILU_MUL, 0, packed, sw.w13_q, sw.w13_s, T, R, 0};
+  if (moe::route_prologue_fits(T, E, k) && L.block_m == 16) {
+    // small batch: the gate_up launch routes and permutes in its own prologue
+    g1.route_logits = router_logits;
+    g1.route_T = T;
+    g1.route_E = E;
+    g1.route_k = k;
+    g1.route_ids = ids;
+    g1.route_w = w;
+    g1.route_tiles = tiles;
+    g1.route_num_tiles = ntiles;
+    g1.route_sorted = sorted;
+    g1.route_inv = inv;
+  } else if (moe::route_align_fused_fits(T, E, k)) {
     e = moe::launch_route_align_small(router_logits, T, E, k, L.block_m, ids, w, counts, offsets, sorted, inv,
                                       tiles, L.max_tiles, ntiles, s);
     if (e != hipSuccess) return hip_status(e, "route+align launch");
@@ -198,10 +214,6 @@ moe_status_t run_ffn(const uint16_t* x, const float* router_logits, int32_t T, i
                           ws + L.align_ws, s);
     if (e != hipSuccess) return hip_status(e, "align launch");
   }
-  const int packed = weight_layout == MOE_LAYOUT_PACKED;
-  const int shared_tiles = sw.w13_q ? (T + L.block_m - 1) / L.block_m : 0;
-  moe::GemmArgs g1{x, sorted, k, w13_q, w13_s, 2 * I, H, tiles, ntiles, L.max_tiles + shared_tiles, 0, h,
-                   MOE_EPI_SILU_MUL, 0, packed, sw.w13_q, sw.w13_s, T, R, 0};
   e = moe::launch_grouped_gemm(g1, L.block_m, s);
   if (e != hipSuccess) return hip_status(e, "gate_up launch");
   moe::GemmArgs g2{h, nullptr, 1, w2_q, w2_s, H, I, tiles, ntiles, L.max_tiles + shared_tiles, 0, o, MOE_EPI_NONE, 1,

@@ -24,6 +24,7 @@
 //    neutralised where it is consumed, so each step waits only for its own loads.
 #include "launch.h"
 #include "moe_common.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -185,15 +186,129 @@ __device__ __forceinline__ int a_row(const GemmArgs& p, int r) {
 }
 
 // ---------------------------------------------------------------------------------------------------
+// Routing prologue of the gate_up launch for small batches (GemmArgs::route_logits).  The ATOM page
+// ("AMD ATOM推理引擎：如何用分页KV缓存和分段编译实现大模型推理性能翻倍", section "8.1 MoE 路径：路由、
+// 专家并行与 MORI 通信") routes each token to its top-k experts and groups the slots by expert; at a
+// few tokens those steps are a chain of dependent memory round trips, so instead of a launch of
+// their own every workgroup of this launch repeats them in LDS (a few hundred slots at most) and
+// derives its own tile.  The result is the permutation moe_align builds: experts in ascending order,
+// each expert's slots in ascending flat order (token * k + slot), one 16-row tile per touched expert
+// (a batch of at most 16 tokens gives every expert at most 16 rows), tile j = j-th touched expert.
+// Workgroup 0 writes the routing and the tile count, the workgroup with N block 0 of each tile writes
+// that tile's list entry and its part of the permutation, for the launches that follow.
+struct __attribute__((aligned(16))) RouteLds {
+  uint64_t kept[4][2 * kRouteMaxK];
+  uint64_t pairs[4][128];  // rank-counting selection (E <= 128)
+  int32_t ids[kRouteMaxT * kRouteMaxK];
+  int32_t cnt[kAlignSingleMaxE];
+  int32_t wsum[4];
+  int32_t wmatch[4];
+  int32_t tile_e, tile_row0, tile_rows;
+  int32_t tok[16];  // token of each row of this workgroup's tile
+};
+
+// Runs the routing prologue in a 256-thread workgroup and maps the workgroup (linear index b) to its
+// tile and N block as xcd_tile does over the routed tiles plus `shared_tiles`.  Returns false when the
+// workgroup has no tile.  For a routed tile (tile < nr) sets e, row0 (first permuted row), rows and
+// L.tok; shared tiles are left to the caller.
+template <int NJ>
+__device__ bool route_prologue(const GemmArgs& p, RouteLds& L, int nbn, int shared_tiles, int& tile, int& nb,
+                               int& nr, int& e, int& row0, int& rows) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = p.route_T, E = p.route_E, k = p.route_k, R = T * k;
+  const long long b = linear_block();
+  const bool writer = b == 0;
+  for (int i = tid; i < E; i += 256) L.cnt[i] = 0;
+  for (int t = wave; t < T; t += 4) {
+    const float* lg = p.route_logits + (size_t)t * E;
+    int32_t* io = writer ? p.route_ids + (size_t)t * k : nullptr;
+    float* wo = writer ? p.route_w + (size_t)t * k : nullptr;
+    if constexpr (NJ <= 2) route_token_rank(lg, E, k, L.pairs[wave], L.kept[wave], io, wo, L.ids + t * k);
+    else route_token<NJ>(lg, E, k, L.kept[wave], L.kept[wave] + k, io, wo, L.ids + t * k);
+  }
+  __syncthreads();
+  for (int i = tid; i < R; i += 256) atomicAdd(&L.cnt[L.ids[i]], 1);
+  __syncthreads();
+  // Exclusive scan over experts of (rows << 16 | touched): thread tid owns experts 2 tid, 2 tid + 1
+  // (R <= 256 rows and E <= 512 experts both fit 16 bits).
+  const int e0 = 2 * tid, e1 = e0 + 1;
+  const int c0 = e0 < E ? L.cnt[e0] : 0, c1 = e1 < E ? L.cnt[e1] : 0;
+  const int v = ((c0 + c1) << 16) | ((c0 > 0) + (c1 > 0));
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) L.wsum[wave] = incl;
+  __syncthreads();
+  int excl = incl - v;
+  for (int w = 0; w < wave; ++w) excl += L.wsum[w];
+  nr = (L.wsum[0] + L.wsum[1] + L.wsum[2] + L.wsum[3]) & 0xFFFF;
+  if (writer && tid == 0) *p.route_num_tiles = nr;
+  if (!xcd_tile(b, nbn, nr + shared_tiles, tile, nb)) return false;
+  if (tile >= nr) return true;
+  const int j0 = excl & 0xFFFF, r0 = excl >> 16;
+  int te = -1, trow = 0, trows = 0;
+  if (c0 > 0 && j0 == tile) te = e0, trow = r0, trows = c0;
+  if (c1 > 0 && j0 + (c0 > 0) == tile) te = e1, trow = r0 + c0, trows = c1;
+  if (te >= 0) {
+    L.tile_e = te;
+    L.tile_row0 = trow;
+    L.tile_rows = trows;
+    if (nb == 0) {
+      p.route_tiles[3 * tile] = te;
+      p.route_tiles[3 * tile + 1] = trow;
+      p.route_tiles[3 * tile + 2] = trows;
+    }
+  }
+  __syncthreads();
+  e = L.tile_e;
+  row0 = L.tile_row0;
+  rows = L.tile_rows;
+  // rows of the tile: slot i (thread i, R <= 256) ranks among the slots routed to e
+  const bool m = tid < R && L.ids[tid] == e;
+  const uint64_t bal = __ballot(m);
+  if (lane == 0) L.wmatch[wave] = __popcll(bal);
+  __syncthreads();
+  int rank = __popcll(bal & ((1ull << lane) - 1ull));
+  for (int w = 0; w < wave; ++w) rank += L.wmatch[w];
+  if (m) {
+    L.tok[rank] = tid / k;
+    if (nb == 0) {
+      p.route_sorted[row0 + rank] = tid;
+      p.route_inv[tid] = row0 + rank;
+    }
+  }
+  __syncthreads();
+  return true;
+}
+
+// The view of a shared-expert tile (tile index j past the routed ones), as tile_view gives it.
+__device__ __forceinline__ GemmArgs shared_view(const GemmArgs& p, int j, int bm, int& e, int& row0, int& rows) {
+  GemmArgs v = p;
+  e = 0;
+  row0 = p.shared_row0 + j * bm;
+  rows = min(bm, p.shared_rows - j * bm);
+  v.Wq = p.Wq_sh;
+  v.Ws = p.Ws_sh;
+  v.a_row_of = nullptr;
+  v.a_row_sub = p.shared_row0;
+  return v;
+}
+
+// ---------------------------------------------------------------------------------------------------
 // Tiled kernel: BM x BN tile per 256-thread workgroup, waves split it WAVES_M x WAVES_N; the
 // activation tile of each K step is staged once in LDS (double buffer, one barrier per step) and
 // shared by the waves.  PF = K steps in flight ahead of the one computed (ring of PF+1 slots).
 constexpr int kLDA = kBK + 8;  // padded LDS activation row of the tiled kernel (bf16 elements)
 
-// One BM x BN output tile (tile list entry `tile`, N block `nb`) of the tiled kernel.
+// One BM x BN output tile (expert e, permuted rows [row0, row0 + rows), N block nb) of the tiled
+// kernel; p is the tile's view of the arguments and sRow already holds the activation row of each
+// tile row (padding rows repeat row 0); it is published by the barrier before the first K step.
 template <int BM, int BN, int WAVES_M, int PF, int EPI, bool OUT_F32, int LAYOUT>
-__device__ __forceinline__ void tiled_tile(const GemmArgs& p0, int tile, int nb, uint16_t (&sA)[2][BM * kLDA],
-                                           int32_t (&sRow)[BM]) {
+__device__ __forceinline__ void tiled_tile(const GemmArgs& p, int e, int row0, int rows, int nb,
+                                           uint16_t (&sA)[2][BM * kLDA], const int32_t (&sRow)[BM]) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int MI = WM / 16, NI = WN / 16;
@@ -203,8 +318,6 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& p0, int tile, int nb,
   static_assert(MI >= 1 && NI >= 1 && ACH >= 1, "tile shape");
   static_assert(EPI != MOE_EPI_SILU_MUL || NI % 2 == 0, "SiLU*mul pairs gate and up blocks");
 
-  int e, row0, rows;
-  const GemmArgs p = tile_view(p0, tile, BM, e, row0, rows);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -213,10 +326,6 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& p0, int tile, int nb,
   const int kgroups = K / kGroup;
   const int nks = (K + kBK - 1) / kBK;
 
-  for (int i = tid; i < BM; i += 256) {
-    const int r = row0 + (i < rows ? i : 0);
-    sRow[i] = a_row(p, r);
-  }
   WRow wr[NI];
   int ncol[NI];
   bool nvalid[NI];
@@ -318,14 +427,33 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& p0, int tile, int nb,
   store_tile<EPI, OUT_F32, MI, NI>(p, acc, wm * WM, row0, rows, q, ncol, nvalid);
 }
 
-template <int BM, int BN, int WAVES_M, int PF, int EPI, bool OUT_F32, int LAYOUT>
-__global__ __launch_bounds__(256) void gemm_w4a16_tiled(GemmArgs p) {
+// RNJ > 0: the launch runs the routing prologue (route_token over 64 * RNJ experts per lane group).
+template <int BM, int BN, int WAVES_M, int PF, int EPI, bool OUT_F32, int LAYOUT, int RNJ = 0>
+__global__ __launch_bounds__(256) void gemm_w4a16_tiled(GemmArgs p0) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kLDA];
   __shared__ int32_t sRow[BM];
-  const int nbn = EPI == MOE_EPI_SILU_MUL ? (p.N / 2 + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
-  int tile, nb;
-  if (!xcd_tile(linear_block(), nbn, tile_count(p, BM), tile, nb)) return;
-  tiled_tile<BM, BN, WAVES_M, PF, EPI, OUT_F32, LAYOUT>(p, tile, nb, sA, sRow);
+  const int nbn = EPI == MOE_EPI_SILU_MUL ? (p0.N / 2 + BN / 2 - 1) / (BN / 2) : (p0.N + BN - 1) / BN;
+  int tile, nb, e, row0, rows;
+  GemmArgs p;
+  if constexpr (RNJ > 0) {
+    static_assert(BM == 16, "the routing prologue builds 16-row tiles");
+    __shared__ RouteLds rl;
+    int nr;
+    const int sh = p0.Wq_sh ? (p0.shared_rows + BM - 1) / BM : 0;
+    if (!route_prologue<RNJ>(p0, rl, nbn, sh, tile, nb, nr, e, row0, rows)) return;
+    if (tile < nr) {
+      p = p0;
+      for (int i = threadIdx.x; i < BM; i += 256) sRow[i] = rl.tok[i < rows ? i : 0];
+    } else {
+      p = shared_view(p0, tile - nr, BM, e, row0, rows);
+      for (int i = threadIdx.x; i < BM; i += 256) sRow[i] = a_row(p, row0 + (i < rows ? i : 0));
+    }
+  } else {
+    if (!xcd_tile(linear_block(), nbn, tile_count(p0, BM), tile, nb)) return;
+    p = tile_view(p0, tile, BM, e, row0, rows);
+    for (int i = threadIdx.x; i < BM; i += 256) sRow[i] = a_row(p, row0 + (i < rows ? i : 0));
+  }
+  tiled_tile<BM, BN, WAVES_M, PF, EPI, OUT_F32, LAYOUT>(p, e, row0, rows, nb, sA, sRow);
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -336,7 +464,7 @@ __global__ __launch_bounds__(256) void gemm_w4a16_tiled(GemmArgs p) {
 // (16-byte loads, rows gathered through a_row_of; padding rows repeat the tile's first row, which
 // the load coalescer merges), so the main loop has no LDS traffic and no barrier.  The KW partial
 // sums are reduced through LDS once per tile, in wave order.
-template <int BM, int BN, int PF, int EPI, bool OUT_F32, int LAYOUT, int KW = 4>
+template <int BM, int BN, int PF, int EPI, bool OUT_F32, int LAYOUT, int KW = 4, int RNJ = 0>
 __global__ __launch_bounds__(64 * KW) void gemm_w4a16_sk(GemmArgs p0) {
   constexpr int MI = BM / 16, NI = BN / 16;
   static_assert(MI >= 1 && MI <= 2 && NI >= 1, "tile shape");
@@ -346,13 +474,34 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a16_sk(GemmArgs p0) {
   __shared__ __attribute__((aligned(16))) float red[(KW - 1) * 64 * MI * NI * 4];
 
   const int nbn = EPI == MOE_EPI_SILU_MUL ? (p0.N / 2 + BN / 2 - 1) / (BN / 2) : (p0.N + BN - 1) / BN;
-  int tile, nb;
-  if (!xcd_tile(linear_block(), nbn, tile_count(p0, BM), tile, nb)) return;
-  int e, row0, rows;
-  const GemmArgs p = tile_view(p0, tile, BM, e, row0, rows);
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, q = lane >> 4;
+  int tile, nb, e, row0, rows;
+  GemmArgs p;
+  int arow_of[MI];  // activation row of each of this lane's tile rows (padding rows repeat row 0)
+  if constexpr (RNJ > 0) {
+    static_assert(BM == 16 && KW == 4, "the routing prologue builds 16-row tiles in 256-thread workgroups");
+    __shared__ RouteLds rl;
+    int nr;
+    const int sh = p0.Wq_sh ? (p0.shared_rows + BM - 1) / BM : 0;
+    if (!route_prologue<RNJ>(p0, rl, nbn, sh, tile, nb, nr, e, row0, rows)) return;
+    if (tile < nr) {
+      p = p0;
+      arow_of[0] = rl.tok[l16 < rows ? l16 : 0];
+    } else {
+      p = shared_view(p0, tile - nr, BM, e, row0, rows);
+      arow_of[0] = a_row(p, row0 + (l16 < rows ? l16 : 0));
+    }
+  } else {
+    if (!xcd_tile(linear_block(), nbn, tile_count(p0, BM), tile, nb)) return;
+    p = tile_view(p0, tile, BM, e, row0, rows);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int i = mi * 16 + l16;
+      arow_of[mi] = a_row(p, row0 + (i < rows ? i : 0));
+    }
+  }
+  const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = p.K;
   const int kgroups = K / kGroup;
   const int nks = (K + kBK - 1) / kBK;
@@ -362,11 +511,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a16_sk(GemmArgs p0) {
 
   const uint16_t* arow[MI];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
-    const int i = mi * 16 + l16;
-    const int r = row0 + (i < rows ? i : 0);
-    arow[mi] = p.A + (size_t)a_row(p, r) * K + q * 8;
-  }
+  for (int mi = 0; mi < MI; ++mi) arow[mi] = p.A + (size_t)arow_of[mi] * K + q * 8;
   WRow wr[NI];
   int ncol[NI];
   bool nvalid[NI];
@@ -668,18 +813,18 @@ static dim3 grid_of(const GemmArgs& a, int bn) {
 
 template <int BM, int BN, int WAVES_M, int PF>
 struct Tiled {
-  template <int EPI, bool F32, int LAYOUT>
+  template <int EPI, bool F32, int LAYOUT, int RNJ = 0>
   static hipError_t run(const GemmArgs& a, hipStream_t s) {
-    gemm_w4a16_tiled<BM, BN, WAVES_M, PF, EPI, F32, LAYOUT><<<grid_of(a, BN), 256, 0, s>>>(a);
+    gemm_w4a16_tiled<BM, BN, WAVES_M, PF, EPI, F32, LAYOUT, RNJ><<<grid_of(a, BN), 256, 0, s>>>(a);
     return hipGetLastError();
   }
 };
 
 template <int BM, int BN, int PF, int KW = 4>
 struct SplitK {
-  template <int EPI, bool F32, int LAYOUT>
+  template <int EPI, bool F32, int LAYOUT, int RNJ = 0>
   static hipError_t run(const GemmArgs& a, hipStream_t s) {
-    gemm_w4a16_sk<BM, BN, PF, EPI, F32, LAYOUT, KW><<<grid_of(a, BN), 64 * KW, 0, s>>>(a);
+    gemm_w4a16_sk<BM, BN, PF, EPI, F32, LAYOUT, KW, RNJ><<<grid_of(a, BN), 64 * KW, 0, s>>>(a);
     return hipGetLastError();
   }
 };
@@ -697,6 +842,23 @@ static hipError_t by_layout(const GemmArgs& a, hipStream_t s) {
     case kPacked: return Cfg::template run<EPI, F32, kPacked>(a, s);
     case kCanonFull: return Cfg::template run<EPI, F32, kCanonFull>(a, s);
     default: return Cfg::template run<EPI, F32, kCanonGeneric>(a, s);
+  }
+}
+
+// The SiLU*mul launch with the routing prologue (16-row tiles): experts per lane group 128 or 512.
+template <class Cfg>
+static hipError_t routed(const GemmArgs& a, hipStream_t s) {
+  constexpr int EPI = MOE_EPI_SILU_MUL;
+  const bool small = a.route_E <= 128;
+  switch (layout_of(a)) {
+    case kPacked:
+      return small ? Cfg::template run<EPI, false, kPacked, 2>(a, s) : Cfg::template run<EPI, false, kPacked, 8>(a, s);
+    case kCanonFull:
+      return small ? Cfg::template run<EPI, false, kCanonFull, 2>(a, s)
+                   : Cfg::template run<EPI, false, kCanonFull, 8>(a, s);
+    default:
+      return small ? Cfg::template run<EPI, false, kCanonGeneric, 2>(a, s)
+                   : Cfg::template run<EPI, false, kCanonGeneric, 8>(a, s);
   }
 }
 
@@ -726,15 +888,20 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t strea
   }
   switch (block_m) {
     case 16:
+      // (the routing prologue, a.route_logits, comes with the SiLU*mul epilogue and 16-row tiles only)
       if (a.max_tiles <= kSplitKMaxTiles) {
+        if (a.route_logits) return routed<SplitK<16, 32, 2, 4>>(a, stream);
         return by_variant<SplitK<16, 32, 2, 4>>(a, stream);
       }
       // 256-column blocks once the grid holds three workgroups per CU (768) with them: measured on
       // MI355X with 128 experts top-8, 32 and 64 tokens: gate_up 39.6 / 41.5 us against 40.0 / 44.5 us
       // for 128-column blocks; at 8 tokens (408 workgroups) 128-column blocks stay faster
       if (8LL * ((a.max_tiles + 7) / 8) * (a.epilogue == MOE_EPI_SILU_MUL ? (a.N / 2 + 127) / 128 : (a.N + 255) / 256) >=
-          768)
+          768) {
+        if (a.route_logits) return routed<Tiled<16, 256, 1, 1>>(a, stream);
         return by_variant<Tiled<16, 256, 1, 1>>(a, stream);
+      }
+      if (a.route_logits) return routed<Tiled<16, 128, 1, 2>>(a, stream);
       return by_variant<Tiled<16, 128, 1, 2>>(a, stream);
     case 32: return by_variant<Tiled<32, 128, 1, 2>>(a, stream);
     case 64: return by_variant<Tiled<64, 256, 1, 1>>(a, stream);

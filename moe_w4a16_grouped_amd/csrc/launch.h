@@ -61,7 +61,26 @@ struct GemmArgs {
   int shared_rows;
   int shared_row0;
   int a_row_sub;           // per-tile view only (set by the kernels; callers leave it 0)
+  // Routing prologue (SiLU*mul launch with 16-row tiles, route_prologue_fits; route_logits NULL = off):
+  // every workgroup routes the batch from the router logits and builds its own tile list entry and
+  // row gather in LDS instead of reading tiles / num_tiles / a_row_of; it writes what the later
+  // launches read: the tile list and its length, the permutation (sorted_ids, inv_perm) and the
+  // routing (ids, weights).  Expert counts and offsets are not written.
+  const float* route_logits;  // [T, E]
+  int route_T, route_E, route_k;
+  int32_t* route_ids;         // [T, k]
+  float* route_w;             // [T, k]
+  int32_t* route_tiles;       // [max_tiles, 3]
+  int32_t* route_num_tiles;
+  int32_t* route_sorted;      // [T * k]
+  int32_t* route_inv;         // [T * k]
 };
+// Batches the routing prologue serves: at most 16 tokens (so every expert fits one 16-row tile),
+// k <= 16, E <= 512.
+constexpr int kRouteMaxT = 16, kRouteMaxK = 16;
+inline bool route_prologue_fits(int T, int E, int k) {
+  return T >= 1 && T <= kRouteMaxT && k <= kRouteMaxK && E <= kAlignSingleMaxE;
+}
 hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t stream);
 
 // MXFP4 (W4A4) grouped GEMM: activations and weights as E2M1 codes with E8M0 scale bytes per 32 K.

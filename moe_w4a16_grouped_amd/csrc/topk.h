@@ -26,7 +26,8 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
 }
 
 // Top-k of one token by one wave.  kept and ranked are this wave's LDS scratch (k entries each);
-// ids_out / w_out receive the token's k slots; ids_lds (may be NULL) receives a copy of the ids.
+// ids_out / w_out (NULL: not written) receive the token's k slots; ids_lds (may be NULL) receives a
+// copy of the ids.
 template <int NJ>
 __device__ __forceinline__ void route_token(const float* __restrict__ l, int E, int k, uint64_t* kept,
                                             uint64_t* ranked, int32_t* __restrict__ ids_out,
@@ -84,9 +85,69 @@ __device__ __forceinline__ void route_token(const float* __restrict__ l, int E, 
   for (int s2 = lane; s2 < k; s2 += 64) {
     const uint64_t key = ranked[s2];
     const int e = (int)(~(uint32_t)key);
-    ids_out[s2] = e;
-    w_out[s2] = expf(from_ordered_bits((uint32_t)(key >> 32)) - top) / sum;
+    if (ids_out) {
+      ids_out[s2] = e;
+      w_out[s2] = expf(from_ordered_bits((uint32_t)(key >> 32)) - top) / sum;
+    }
     if (ids_lds) ids_lds[s2] = e;
+  }
+}
+
+// Top-k of one token by one wave for E <= 128 by counting ranks.  Each expert's (key, id) pair is
+// one 64-bit value (key << 32 | ~id) whose unsigned order is the (logit desc, id asc) order; lane l
+// places the pairs of experts l and l + 64 in LDS (pairs, 128 entries; absent experts hold 0, below
+// every pair) and counts, for each of its two experts, the pairs above it: that count is the slot,
+// kept when below k.  The same selection and slot order as route_token, without its serial rounds.
+// ids_lds receives the ids by slot.  With ids_out set, the kept pairs are placed in ranked (k
+// entries) and the weights formed as route_token forms them (same operations in the same order, so
+// the same bits); otherwise no weights are formed.
+__device__ __forceinline__ void route_token_rank(const float* __restrict__ l, int E, int k, uint64_t* pairs,
+                                                 uint64_t* ranked, int32_t* __restrict__ ids_out,
+                                                 float* __restrict__ w_out, int32_t* ids_lds) {
+  const int lane = threadIdx.x & 63;
+  uint64_t me[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = lane + 64 * j;
+    me[j] = e < E ? ((uint64_t)ordered_bits(l[e]) << 32) | (uint32_t)(~(uint32_t)e) : 0ull;
+    pairs[e] = me[j];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  int rank[2] = {0, 0};
+#pragma unroll 1
+  for (int i0 = 0; i0 < 128; i0 += 16) {
+    uint64_t kv[16];
+#pragma unroll
+    for (int c = 0; c < 16; c += 2) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(pairs + i0 + c);
+      kv[c] = ((uint64_t)v[1] << 32) | v[0];
+      kv[c + 1] = ((uint64_t)v[3] << 32) | v[2];
+    }
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      rank[0] += kv[c] > me[0] ? 1 : 0;
+      rank[1] += kv[c] > me[1] ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = lane + 64 * j;
+    if (e < E && rank[j] < k) {
+      ids_lds[rank[j]] = e;
+      if (ids_out) ranked[rank[j]] = me[j];
+    }
+  }
+  if (!ids_out) return;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const float top = from_ordered_bits((uint32_t)(ranked[0] >> 32));
+  float sum = 0.f;
+  for (int s2 = 0; s2 < k; ++s2) sum += expf(from_ordered_bits((uint32_t)(ranked[s2] >> 32)) - top);
+  for (int s2 = lane; s2 < k; s2 += 64) {
+    const uint64_t key = ranked[s2];
+    ids_out[s2] = (int)(~(uint32_t)key);
+    w_out[s2] = expf(from_ordered_bits((uint32_t)(key >> 32)) - top) / sum;
   }
 }
 

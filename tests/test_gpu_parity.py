@@ -268,6 +268,13 @@ def test_ffn_forward_matches_oracle(name, nsample):
     mi.custom("fused_max", 16, 128, 64, 128, 64, seed=10),
     mi.custom("fused_e512", 16, 512, 8, 128, 64, seed=15),
     mi.custom("fused_past", 17, 128, 8, 128, 64, seed=16),
+    # the gate_up launch's routing prologue (at most 16 tokens, k <= 16) at its limits: 512 experts
+    # with k = 16, 129 experts (the wider selection), k = E, one token; k = 17 falls back
+    mi.custom("prologue_max", 16, 512, 16, 128, 64, seed=17),
+    mi.custom("prologue_e129", 5, 129, 16, 160, 96, seed=18),
+    mi.custom("prologue_k_eq_E", 3, 4, 4, 128, 64, seed=19),
+    mi.custom("prologue_t1", 1, 256, 8, 256, 128, seed=20),
+    mi.custom("prologue_past_k", 4, 64, 17, 128, 64, seed=24),
 ])
 def test_ffn_forward_edges(wl):
     inp, d = workload_inputs(wl)
@@ -356,6 +363,49 @@ def test_ffn_forward_packed_matches_canonical_bits(name):
     np.testing.assert_array_equal(_bits(y), y_c)
 
 
+def _layer_from_entry_points(d, inp, packed):
+    """The layer composed from the separate entry points, ending with the stand-alone combine."""
+    wl = inp.wl
+    layout = moe.MOE_LAYOUT_PACKED if packed else moe.MOE_LAYOUT_CANONICAL
+    q13, s13, q2, s2 = _packed(d) if packed else (d.w13_q, d.w13_s, d.w2_q, d.w2_s)
+    ids, w = moe.moe_route_topk(d.logits, wl.k)
+    bm = moe.moe_ffn_block_m(wl.T, wl.E, wl.k, layout)
+    al = moe.moe_align(ids, wl.E, bm)
+    R = wl.T * wl.k
+    h = moe.moe_grouped_gemm_w4a16(d.x, al["sorted_ids"], wl.k, q13, s13, al["tiles"], al["max_tiles"],
+                                   al["num_tiles"], bm, moe.MOE_EPI_SILU_MUL, R, weight_layout=layout)
+    O = moe.moe_grouped_gemm_w4a16(h, None, 1, q2, s2, al["tiles"], al["max_tiles"], al["num_tiles"], bm,
+                                   moe.MOE_EPI_NONE, R, out_dtype=moe.MOE_OUT_F32, weight_layout=layout)
+    y = moe.moe_combine(O, al["inv_perm"], w)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("name,packed", [("tiny", False), ("dec1", True), ("dec8", True), ("dec8", False),
+                                         ("dec64", True),
+                                         ("pre800", True), ("pre800", False), ("skew8192", True),
+                                         ("big4096", True)])
+def test_ffn_forward_matches_entry_point_chain_bits(name, packed):
+    """The layer entry point must give, bit for bit, what the chain of the separate entry points gives
+    (routing, permutation, both grouped GEMMs, combine) with the same tile heights; the workspace,
+    including every routing region, starts poisoned."""
+    inp, d = workload_inputs(name)
+    wl = inp.wl
+    _log(f"layer vs entry-point chain {name} packed={packed}")
+    y_ref = _bits(_layer_from_entry_points(d, inp, packed))
+    if packed:
+        q13, s13, q2, s2 = _packed(d)
+        y = torch.full((wl.T, wl.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+        wsb = moe.moe_ffn_workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.k)
+        ws = torch.full((max(wsb, 256),), 0xFF, dtype=torch.uint8, device="cuda")
+        moe.moe_ffn_forward(d.x, d.logits, q13, s13, q2, s2, wl.k, y=y, workspace=ws,
+                            weight_layout=moe.MOE_LAYOUT_PACKED)
+        torch.cuda.synchronize()
+    else:
+        y = _forward(d, inp)[0]
+    np.testing.assert_array_equal(_bits(y), y_ref)
+
+
 @pytest.mark.parametrize("bm", [16, 32, 64, 128])
 def test_grouped_gemm_packed_matches_canonical_bits(bm):
     wl = mi.custom("gp", 150, 8, 3, 256, 128, skew=True, seed=23)
@@ -434,11 +484,12 @@ def test_grouped_gemm_large_capacity_grid(bm, layout):
     np.testing.assert_array_equal(outs[1].view(torch.int16).cpu().numpy(), outs[0].view(torch.int16).cpu().numpy())
 
 
-def test_ffn_forward_graph_replays_match_eager():
+@pytest.mark.parametrize("name", ["pre800", "dec1"])
+def test_ffn_forward_graph_replays_match_eager(name):
     # The whole layer captured in a HIP graph (no memset or host sync is recorded) and replayed
     # several times, with eager work and synchronisation in between: every replay must reproduce
     # the eager output bits.
-    inp, d = workload_inputs("pre800")
+    inp, d = workload_inputs(name)
     wl = inp.wl
     q13, s13, q2, s2 = _packed(d)
     ws = torch.empty(moe.moe_ffn_workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.k), dtype=torch.uint8, device="cuda")
