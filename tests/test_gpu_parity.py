@@ -382,6 +382,11 @@ def _layer_from_entry_points(d, inp, packed):
 
 
 @pytest.mark.parametrize("name,packed", [("tiny", False), ("dec1", True), ("dec8", True), ("dec8", False),
+                                         # decode batches with a K tail (I = 96): down rows reduced as
+                                         # the split-K kernel (<= 32 tiles) and as the tiled kernel
+                                         (mi.custom("tail_split", 2, 16, 4, 160, 96, seed=25), False),
+                                         (mi.custom("tail_tiled", 12, 64, 4, 160, 96, seed=26), False),
+                                         (mi.custom("k16_tiled", 9, 32, 16, 256, 128, seed=27), False),
                                          ("dec64", True),
                                          ("pre800", True), ("pre800", False), ("skew8192", True),
                                          ("big4096", True)])
@@ -391,7 +396,7 @@ def test_ffn_forward_matches_entry_point_chain_bits(name, packed):
     including every routing region, starts poisoned."""
     inp, d = workload_inputs(name)
     wl = inp.wl
-    _log(f"layer vs entry-point chain {name} packed={packed}")
+    _log(f"layer vs entry-point chain {wl.name} packed={packed}")
     y_ref = _bits(_layer_from_entry_points(d, inp, packed))
     if packed:
         q13, s13, q2, s2 = _packed(d)
