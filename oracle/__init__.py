@@ -76,6 +76,10 @@ def _load():
             lib.oracle_f8_dequant.argtypes = [P, P, I64, I64, P]
             lib.oracle_moe_ffn_f8.argtypes = [P, P, I64, I64, I64, I64, I64, P, P, P, P, P, I64, P, P]
             lib.oracle_grouped_proj_f8.argtypes = [P, P, P, I64, P, P, I64, I64, I64, P, ctypes.c_int, P]
+            lib.oracle_mx8_quantize.argtypes = [P, I64, I64, P, P]
+            lib.oracle_mx8_dequant.argtypes = [P, P, I64, I64, P]
+            lib.oracle_moe_ffn_w4a8.argtypes = [P, P, I64, I64, I64, I64, I64, P, P, P, P, P, I64, P, P]
+            lib.oracle_grouped_proj_w4a8.argtypes = [P, P, P, I64, P, P, I64, I64, I64, P, ctypes.c_int, P]
             _lib = lib
     return _lib
 
@@ -331,4 +335,58 @@ def grouped_proj_f8(Aq, As, a_row_of, a_row_div: int, Wq, Ws, offsets, silu_mul:
     aro = None if a_row_of is None else _c(a_row_of, np.int32)
     _load().oracle_grouped_proj_f8(_ptr(Aq), _ptr(As), _ptr(aro), a_row_div, _ptr(Wq), _ptr(Ws), E, N, K,
                                    _ptr(offsets), int(bool(silu_mul)), _ptr(C))
+    return C
+
+
+# ---- W4A8 (MXFP8 activations: E4M3 codes + E8M0 per 32; MXFP4 weights) --------------------------------
+
+def mx8_quantize(v):
+    """MXFP8 quantization of fp64 values [rows, K] -> (codes uint8 [rows, K], scale bytes uint8 [rows, K/32])."""
+    v = _c(v, np.float64)
+    if v.ndim == 1:
+        v = v[None]
+    rows, K = v.shape
+    q = np.empty((rows, K), np.uint8)
+    s = np.empty((rows, K // 32), np.uint8)
+    _load().oracle_mx8_quantize(_ptr(v), rows, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def mx8_dequant(q, s) -> np.ndarray:
+    """MXFP8 codes [rows, K] + scale bytes [rows, K/32] -> fp64 [rows, K]."""
+    q, s = _c(q, np.uint8), _c(s, np.uint8)
+    rows, K = q.shape
+    out = np.empty((rows, K), np.float64)
+    _load().oracle_mx8_dequant(_ptr(q), _ptr(s), rows, K, _ptr(out))
+    return out
+
+
+def moe_ffn_w4a8(inp, tokens=None, diagnostics: bool = False):
+    """W4A8 layer on ``moe_inputs.MXInputs`` (the MXFP4 weights); returns y fp64 [n_tok, H] (and h
+    before its quantization, [n_tok, k, I], if asked)."""
+    wl = inp.wl
+    T, E, k, H, I = wl.T, wl.E, wl.k, wl.H, wl.I
+    tok = None if tokens is None else _c(tokens, np.int64)
+    n = T if tok is None else len(tok)
+    y = np.empty((n, H), np.float64)
+    h = np.empty((n, k, I), np.float64) if diagnostics else None
+    _load().oracle_moe_ffn_w4a8(_ptr(_c(inp.x, np.uint16)), _ptr(_c(inp.logits, np.float32)), T, H, I, E, k,
+                                _ptr(_c(inp.w13_q, np.uint8)), _ptr(_c(inp.w13_e, np.uint8)),
+                                _ptr(_c(inp.w2_q, np.uint8)), _ptr(_c(inp.w2_e, np.uint8)), _ptr(tok), n, _ptr(y),
+                                _ptr(h))
+    return (y, h) if diagnostics else y
+
+
+def grouped_proj_w4a8(Aq, As, a_row_of, a_row_div: int, Wq, We, offsets, silu_mul: bool = False):
+    """Grouped W4A8 projection over permuted rows (see the C function); fp64, before any quantization."""
+    Aq, As = _c(Aq, np.uint8), _c(As, np.uint8)
+    Wq, We = _c(Wq, np.uint8), _c(We, np.uint8)
+    offsets = _c(offsets, np.int32)
+    E, N, K = Wq.shape[0], Wq.shape[1], Wq.shape[2] * 2
+    R = int(offsets[-1])
+    nout = N // 2 if silu_mul else N
+    C = np.empty((R, nout), np.float64)
+    aro = None if a_row_of is None else _c(a_row_of, np.int32)
+    _load().oracle_grouped_proj_w4a8(_ptr(Aq), _ptr(As), _ptr(aro), a_row_div, _ptr(Wq), _ptr(We), E, N, K,
+                                     _ptr(offsets), int(bool(silu_mul)), _ptr(C))
     return C

@@ -53,6 +53,12 @@
  *     code the E4M3 value nearest to the fp32 quotient v / s, ties to the even code; s == 0 (an
  *     all-zero block) gives codes 0.  These decisions are taken in fp32, the precision the GPU takes
  *     them in, so that both sides reach the same codes from the same fp32 values.
+ *   - W4A8 (the scaled-instruction path with 8-bit activations beside the a4w4 one): weights as in
+ *     the MXFP4 layer; activations quantized on the fly to MXFP8, the OCP MX format with E4M3
+ *     elements: per block of 32 K elements X = 2^(floor(log2(amax)) - 8) (8 = the largest E4M3
+ *     exponent), clamped to the E8M0 range, an all-zero block taking 2^-127; each element becomes the
+ *     E4M3 value nearest to v / X, ties to the even code, magnitudes beyond 448 saturating to 448.
+ *     v / X is exact, so every decision is taken on exact values.
  */
 #include <math.h>
 #include <stdint.h>
@@ -627,6 +633,116 @@ void oracle_grouped_proj_f8(const uint8_t *Aq, const float *As, const int32_t *a
             double *g = (double *)malloc(sizeof(double) * (size_t)N);
             for (int64_t c = 0; c < K; ++c) a[c] = f8_at(Aq, As, K, arow, c);
             f8_matvec(Wq + e * szq, Ws + e * szs, N, K, a, g);
+            for (int64_t n = 0; n < nout; ++n) C[r * nout + n] = silu_mul ? silu(g[n]) * g[N / 2 + n] : g[n];
+            free(a); free(g);
+        }
+    }
+}
+
+/* ---- W4A8: MXFP8 (E4M3 + E8M0 per 32) activations, MXFP4 weights ----------------------------------- */
+
+/* MXFP8 quantization of a [rows, K] matrix (K % 32 == 0) into codes q [rows, K] (one byte per
+ * element) and scale bytes s [rows, K/32]: per block of 32, X = 2^e with e = floor(log2(amax)) - 8
+ * clamped to [-127, 127] (-127 for an all-zero block), code = nearest E4M3 value of v / X. */
+void oracle_mx8_quantize(const double *v, int64_t rows, int64_t K, uint8_t *q, uint8_t *s)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < K / ORACLE_GROUP; ++b) {
+            const double *blk = v + r * K + b * ORACLE_GROUP;
+            double amax = 0.0;
+            for (int i = 0; i < ORACLE_GROUP; ++i) if (fabs(blk[i]) > amax) amax = fabs(blk[i]);
+            int e = -127;
+            if (amax > 0.0) {
+                int p;
+                frexp(amax, &p);  /* amax = m * 2^p, 0.5 <= m < 1: floor(log2(amax)) = p - 1 */
+                e = (p - 1) - 8;
+                if (e < -127) e = -127;
+                if (e > 127) e = 127;
+            }
+            s[r * (K / ORACLE_GROUP) + b] = (uint8_t)(e + 127);
+            for (int i = 0; i < ORACLE_GROUP; ++i)
+                q[r * K + b * ORACLE_GROUP + i] = (uint8_t)oracle_e4m3_nearest(ldexp(blk[i], -e));
+        }
+}
+
+/* Value of element kk of row n of an MXFP8 matrix stored as codes q [*, K] and scales s [*, K/32]. */
+static double mx8_at(const uint8_t *q, const uint8_t *s, int64_t K, int64_t n, int64_t kk)
+{
+    return oracle_e4m3_value(q[n * K + kk]) * oracle_e8m0_value(s[n * (K / ORACLE_GROUP) + kk / ORACLE_GROUP]);
+}
+
+/* Dense dequantization of an MXFP8 matrix [rows, K] into out (fp64). */
+void oracle_mx8_dequant(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t K, double *out)
+{
+    for (int64_t n = 0; n < rows; ++n)
+        for (int64_t kk = 0; kk < K; ++kk) out[n * K + kk] = mx8_at(q, s, K, n, kk);
+}
+
+/* Quantize one activation row to MXFP8 and return it dequantized (in place of a). */
+static void mx8_roundtrip_row(double *a, int64_t K)
+{
+    uint8_t *q = (uint8_t *)malloc((size_t)K);
+    uint8_t *sc = (uint8_t *)malloc((size_t)(K / ORACLE_GROUP));
+    oracle_mx8_quantize(a, 1, K, q, sc);
+    for (int64_t kk = 0; kk < K; ++kk) a[kk] = mx8_at(q, sc, K, 0, kk);
+    free(q);
+    free(sc);
+}
+
+/* Full W4A8 layer for a subset of tokens (tok == NULL: tokens 0..n_tok-1); arguments as for
+ * oracle_moe_ffn_mx (the same MXFP4 weights).  Per token: route; quantize x's row to MXFP8; for each
+ * slot the expert's gate_up projection of the quantized row, h = silu(gate) * up, h quantized to
+ * MXFP8, the down projection, y = sum_s w_s o_s.  Optional h_out: h before its quantization. */
+void oracle_moe_ffn_w4a8(const uint16_t *x, const float *logits, int64_t T, int64_t H, int64_t I, int64_t E,
+                         int64_t k, const uint8_t *w13_q, const uint8_t *w13_e, const uint8_t *w2_q,
+                         const uint8_t *w2_e, const int64_t *tok, int64_t n_tok, double *y, double *h_out)
+{
+    (void)T;
+    const int64_t sz13_q = 2 * I * (H / 2), sz13_e = 2 * I * (H / ORACLE_GROUP);
+    const int64_t sz2_q = H * (I / 2), sz2_e = H * (I / ORACLE_GROUP);
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t j = 0; j < n_tok; ++j) {
+        int64_t t = tok ? tok[j] : j;
+        int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+        double *w = (double *)malloc(sizeof(double) * (size_t)k);
+        double *xa = (double *)malloc(sizeof(double) * (size_t)H);
+        double *g = (double *)malloc(sizeof(double) * (size_t)(2 * I));
+        double *h = (double *)malloc(sizeof(double) * (size_t)I);
+        double *o = (double *)malloc(sizeof(double) * (size_t)H);
+        oracle_route(logits + t * E, 1, E, k, ids, w);
+        for (int64_t c = 0; c < H; ++c) xa[c] = oracle_bf16_value(x[t * H + c]);
+        mx8_roundtrip_row(xa, H);
+        for (int64_t c = 0; c < H; ++c) y[j * H + c] = 0.0;
+        for (int64_t s = 0; s < k; ++s) {
+            int64_t e = ids[s];
+            mx_matvec(w13_q + e * sz13_q, w13_e + e * sz13_e, 2 * I, H, xa, g);
+            for (int64_t i = 0; i < I; ++i) h[i] = silu(g[i]) * g[I + i];
+            if (h_out) memcpy(h_out + (j * k + s) * I, h, sizeof(double) * (size_t)I);
+            mx8_roundtrip_row(h, I);
+            mx_matvec(w2_q + e * sz2_q, w2_e + e * sz2_e, H, I, h, o);
+            for (int64_t c = 0; c < H; ++c) y[j * H + c] += w[s] * o[c];
+        }
+        free(ids); free(w); free(xa); free(g); free(h); free(o);
+    }
+}
+
+/* Grouped W4A8 projection over permuted rows (one grouped-GEMM launch of the W4A8 path): as
+ * oracle_grouped_proj_mx with the activations given as MXFP8 codes Aq [*, K] and scale bytes
+ * As [*, K/32].  C fp64, before any quantization. */
+void oracle_grouped_proj_w4a8(const uint8_t *Aq, const uint8_t *As, const int32_t *a_row_of, int64_t a_row_div,
+                              const uint8_t *Wq, const uint8_t *We, int64_t E, int64_t N, int64_t K,
+                              const int32_t *offsets, int silu_mul, double *C)
+{
+    const int64_t szq = N * (K / 2), sze = N * (K / ORACLE_GROUP);
+    const int64_t nout = silu_mul ? N / 2 : N;
+    for (int64_t e = 0; e < E; ++e) {
+        #pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t r = offsets[e]; r < offsets[e + 1]; ++r) {
+            int64_t arow = a_row_of ? a_row_of[r] / a_row_div : r;
+            double *a = (double *)malloc(sizeof(double) * (size_t)K);
+            double *g = (double *)malloc(sizeof(double) * (size_t)N);
+            for (int64_t c = 0; c < K; ++c) a[c] = mx8_at(Aq, As, K, arow, c);
+            mx_matvec(Wq + e * szq, We + e * sze, N, K, a, g);
             for (int64_t n = 0; n < nout; ++n) C[r * nout + n] = silu_mul ? silu(g[n]) * g[N / 2 + n] : g[n];
             free(a); free(g);
         }

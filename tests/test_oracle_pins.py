@@ -665,3 +665,159 @@ def test_grouped_proj_f8_matches_rowwise_products():
             want = g[:N // 2] / (1 + np.exp(-g[:N // 2])) * g[N // 2:]
             slack = 1e-12 * (np.abs(want) + ga[:N // 2] * np.abs(g[N // 2:]) + np.abs(g[:N // 2]) * ga[N // 2:])
             assert np.all(np.abs(Cs[r] - want) <= slack)
+
+
+# ---------------------------------------------------------------------------------------------------
+# W4A8: MXFP8 activation quantization (E4M3 elements, E8M0 per 32) and the W4A8 layer
+
+def _golden_mx8():
+    blocks = []
+    with open(os.path.join(GOLDEN, "mx8_quant_worked_example.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            vals, scale, codes = (part.split() for part in line.split("|"))
+            v = np.zeros(32)
+            v[:len(vals)] = [float(t) for t in vals]
+            c = np.zeros(32, np.int64)
+            c[:len(codes)] = [int(t) for t in codes]
+            blocks.append((v, int(scale[0]), c))
+    return blocks
+
+
+def _np_mx8_dequant(q, s):
+    """Independent dequantisation: torch's E4M3 decode times 2^(byte - 127)."""
+    table = _torch_e4m3_table()
+    scale = np.exp2(np.asarray(s, np.float64) - 127.0)
+    return table[np.asarray(q, np.int64)] * np.repeat(scale, 32, axis=-1)
+
+
+def test_mx8_quantize_golden_blocks():
+    for v, scale, codes in _golden_mx8():
+        q, s = oracle.mx8_quantize(v[None])
+        assert int(s[0, 0]) == scale, (v[:8], s)
+        np.testing.assert_array_equal(q[0].astype(np.int64), codes)
+
+
+def test_mx8_quantize_invariants():
+    rng = np.random.default_rng(31)
+    v = rng.standard_normal((64, 128)) * np.exp2(rng.integers(-20, 20, (64, 1)))
+    v[5, 64:96] = 0.0
+    q, s = oracle.mx8_quantize(v)
+    # powers of two move only the scale byte
+    for m in (-4, 1, 9):
+        q2, s2 = oracle.mx8_quantize(v * 2.0 ** m)
+        np.testing.assert_array_equal(q2, q)
+        nz = s != 0
+        np.testing.assert_array_equal(s2[nz].astype(int), s[nz].astype(int) + m)
+    # negation flips every sign bit
+    qn, sn = oracle.mx8_quantize(-v)
+    np.testing.assert_array_equal(qn, q ^ 0x80)
+    np.testing.assert_array_equal(sn, s)
+    # the scaled block maximum lies in [256, 512): its code is one of 256 .. 448 (codes 120 .. 126)
+    X = np.exp2(s.astype(np.float64) - 127)
+    blocks = np.abs(v).reshape(64, 4, 32)
+    bmax = blocks.max(axis=2)
+    live = bmax > 0
+    assert np.all((bmax[live] / X[live] >= 256) & (bmax[live] / X[live] < 512))
+    arg = blocks.argmax(axis=2)
+    qmax = np.take_along_axis(q.reshape(64, 4, 32), arg[..., None], axis=2)[..., 0] & 0x7F
+    assert np.all((qmax[live] >= 120) & (qmax[live] <= 126))
+    # every element is within half the local E4M3 spacing of its value, or saturated at 448
+    deq = _np_mx8_dequant(q, s)
+    Xr = np.repeat(X, 32, axis=1)
+    scaled = np.abs(v) / Xr
+    spacing = np.where(scaled < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(scaled, 2.0 ** -6))) - 3))
+    ok = (np.abs(deq - v) <= 0.5 * spacing * Xr * (1 + 1e-12)) | ((scaled > 448) & (np.abs(deq) == 448 * Xr))
+    assert np.all(ok)
+    # the all-zero block
+    assert s[5, 2] == 0 and np.all(q[5, 64:96] == 0)
+
+
+def _w4a8_layer_dense(inp):
+    """The W4A8 layer written densely in numpy: every expert on every token, a [T, E] routing matrix
+    with the renormalised top-k weights and zeros elsewhere; activations quantized by the oracle's MXFP8
+    quantizer and decoded with torch's E4M3 table, weights decoded with the numpy E2M1 table."""
+    wl = inp.wl
+    T, E, k, H, I = wl.T, wl.E, wl.k, wl.H, wl.I
+    ids, w = oracle.route(inp.logits, k)
+    route = np.zeros((T, E))
+    for t in range(T):
+        route[t, ids[t]] = w[t]
+    x = mi.bf16_bits_to_f32(inp.x).astype(np.float64)
+    xd = _np_mx8_dequant(*oracle.mx8_quantize(x))
+    y = np.zeros((T, H))
+    for e in range(E):
+        W13 = _np_mx_dequant(inp.w13_q[e], inp.w13_e[e])
+        W2 = _np_mx_dequant(inp.w2_q[e], inp.w2_e[e])
+        g = xd @ W13.T
+        h = g[:, :I] / (1.0 + np.exp(-g[:, :I])) * g[:, I:]
+        y += route[:, e:e + 1] * (_np_mx8_dequant(*oracle.mx8_quantize(h)) @ W2.T)
+    return y
+
+
+@pytest.mark.parametrize("T,E,k,H,I,skew", [(9, 6, 2, 64, 96, False), (5, 4, 4, 128, 64, False),
+                                             (12, 8, 3, 96, 64, True)])
+def test_w4a8_layer_matches_dense_formulation(T, E, k, H, I, skew):
+    inp = mi.make_mx_inputs(mi.custom("w4a8dense", T, E, k, H, I, skew=skew, seed=T + E + 1))
+    ref = _w4a8_layer_dense(inp)
+    y = oracle.moe_ffn_w4a8(inp)
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.sqrt(np.mean(ref ** 2))
+
+
+def test_w4a8_single_expert_is_quantized_swiglu():
+    inp = mi.make_mx_inputs(mi.custom("w4a8one", 7, 1, 1, 64, 64, seed=33))
+    x = mi.bf16_bits_to_f32(inp.x).astype(np.float64)
+    xd = _np_mx8_dequant(*oracle.mx8_quantize(x))
+    W1 = _np_mx_dequant(inp.w13_q[0, :64], inp.w13_e[0, :64])
+    W3 = _np_mx_dequant(inp.w13_q[0, 64:], inp.w13_e[0, 64:])
+    W2 = _np_mx_dequant(inp.w2_q[0], inp.w2_e[0])
+    a, b = xd @ W1.T, xd @ W3.T
+    h = a * (1 / (1 + np.exp(-a))) * b
+    ref = _np_mx8_dequant(*oracle.mx8_quantize(h)) @ W2.T
+    np.testing.assert_allclose(oracle.moe_ffn_w4a8(inp), ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+def test_w4a8_activations_differ_from_w4a4_only_by_the_element_format():
+    # same weights and routing: the W4A8 layer is closer to the unquantized-activation layer than
+    # the W4A4 one (E4M3 keeps 3 mantissa bits, E2M1 one)
+    inp = mi.make_mx_inputs(mi.custom("w4a8cmp", 12, 8, 2, 128, 64, seed=34))
+    x = mi.bf16_bits_to_f32(inp.x).astype(np.float64)
+    ids, w = oracle.route(inp.logits, 2)
+    exact = np.zeros((12, 128))
+    for t in range(12):
+        for s_ in range(2):
+            e = ids[t, s_]
+            g = _np_mx_dequant(inp.w13_q[e], inp.w13_e[e]) @ x[t]
+            h = g[:64] / (1 + np.exp(-g[:64])) * g[64:]
+            exact[t] += w[t, s_] * (_np_mx_dequant(inp.w2_q[e], inp.w2_e[e]) @ h)
+    err8 = np.linalg.norm(oracle.moe_ffn_w4a8(inp) - exact)
+    err4 = np.linalg.norm(oracle.moe_ffn_mx(inp) - exact)
+    assert err8 < 0.25 * err4
+
+
+def test_grouped_proj_w4a8_matches_rowwise_products():
+    rng = np.random.default_rng(35)
+    E, N, K, R = 3, 48, 96, 20
+    Aq = rng.integers(0, 256, (R, K), dtype=np.uint8)
+    Aq[(Aq & 0x7F) == 0x7F] = 0x7E  # no NaN codes
+    As = rng.integers(108, 114, (R, K // 32), dtype=np.uint8)  # E4M3 magnitudes up to 448: keep silu finite
+    Wq = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    We = rng.integers(118, 124, (E, N, K // 32), dtype=np.uint8)
+    offsets = np.array([0, 7, 7, R], np.int32)
+    a_row_of = rng.permutation(R).astype(np.int32)
+    C = oracle.grouped_proj_w4a8(Aq, As, a_row_of, 1, Wq, We, offsets)
+    A = _np_mx8_dequant(Aq, As)
+    for e in range(E):
+        W = _np_mx_dequant(Wq[e], We[e])
+        for r in range(offsets[e], offsets[e + 1]):
+            terms = np.abs(W) @ np.abs(A[a_row_of[r]])
+            assert np.all(np.abs(C[r] - W @ A[a_row_of[r]]) <= 1e-13 * terms + 1e-300)
+    Cs = oracle.grouped_proj_w4a8(Aq, As, None, 1, Wq, We, offsets, silu_mul=True)
+    for e in range(E):
+        W = _np_mx_dequant(Wq[e], We[e])
+        for r in range(offsets[e], offsets[e + 1]):
+            g = W @ A[r]
+            np.testing.assert_allclose(Cs[r], g[:N // 2] / (1 + np.exp(-g[:N // 2])) * g[N // 2:], rtol=1e-10,
+                                       atol=1e-9 * np.abs(g).max())
