@@ -364,6 +364,59 @@ moe_status_t moe_ffn_forward_mxfp4(const uint16_t* x, const float* router_logits
                                    void* stream);
 
 /*
+ * ---- W4A8 variant (MXFP8 activations on the MXFP4 weights) -----------------------------------------
+ * [ATOM, 6.1: the MX formats served by the scaled-instruction GEMMs; ATOM, 8.2: dynamic activation
+ * quantization is part of a format's contract.]  Weights exactly as the MXFP4 variant (either layout,
+ * the same moe_mx_prepack).  Activations are MXFP8: OCP FP8 E4M3 codes (one byte per element; 1 sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits, largest finite 448) with one E8M0 scale byte per 32
+ * consecutive K elements: value = E4M3(code) * 2^(byte - 127).  Quantization per row and block of 32:
+ * X = 2^(floor(log2(max |v|)) - 8) clamped to [2^-127, 2^127] (an all-zero block takes byte 0), code =
+ * nearest E4M3 value of v / X, ties to the even code, saturating at +-448.  Products run on the gfx950
+ * scaled matrix instruction with E4M3 x E2M1 operands and fp32 accumulation.
+ */
+
+/* x bf16 [rows, K] -> codes q [rows, K] and scale bytes s [rows, K/32] (MXFP8 conversion above).
+ * Shapes: 0 <= rows < 2^26, K a positive multiple of 32.  x and q 16-byte aligned. */
+moe_status_t moe_mx8_quantize(const uint16_t* x, int32_t rows, int32_t K, uint8_t* q, uint8_t* s, void* stream);
+
+/*
+ * Grouped W4A8 GEMM over the tile list of moe_align (as moe_grouped_gemm_mxfp4 with row-major
+ * activations): for each permuted row r of expert e, activation row a = (a_row_of ? a_row_of[r] /
+ * a_row_div : r):
+ *   G[r, n] = sum_k A[a, k] * W_e[n, k],  A = (Aq [*, K] E4M3 codes, As [*, K/32]), W = (Wq [E, N, K/2], We [E, N, K/32]).
+ *   epilogue NONE:     C [rows, N] fp32 or bf16 (out_dtype); Cs unused.
+ *   epilogue SILU_MUL: h[r, j] = silu(G[r, j]) * G[r, N/2 + j] in fp32, then quantized to MXFP8 per 32
+ *                      columns: C = codes [rows, N/2], Cs = scale bytes [rows, N/64] (out_dtype ignored).
+ * weight_layout: MOE_LAYOUT_CANONICAL or MOE_LAYOUT_PACKED (moe_mx_prepack; needs N % 16 == 0 and
+ * K % 128 == 0); results are bit-identical across layouts.  block_m 16, 32 or 64.  K % 32 == 0;
+ * SILU_MUL needs N % 64 == 0.  Aq, Wq and C 16-byte aligned.
+ */
+moe_status_t moe_grouped_gemm_w4a8(const uint8_t* Aq, const uint8_t* As, const int32_t* a_row_of, int32_t a_row_div,
+                                   const uint8_t* Wq, const uint8_t* We, int32_t weight_layout, int32_t E, int32_t N,
+                                   int32_t K, const int32_t* tiles, int32_t max_tiles, const int32_t* num_tiles,
+                                   int32_t block_m, int32_t epilogue, void* C, uint8_t* Cs, int32_t out_dtype,
+                                   void* stream);
+
+/* Row-tile height and workspace bytes of moe_ffn_forward_w4a8 (host-only, pure; -1 / 0 on invalid sizes). */
+int32_t moe_ffn_w4a8_block_m(int32_t T, int32_t E, int32_t k);
+size_t moe_ffn_w4a8_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k);
+
+/*
+ * The whole W4A8 layer [ATOM, 6.1 and 8.1-8.2]: route -> permute -> x quantized to MXFP8 -> gate_up
+ * (SiLU*mul, h quantized to MXFP8 in the epilogue) -> down (fp32) -> combine, all enqueued on `stream`:
+ *   y[t] = sum_s w[t,s] * W2_e(s) Q8( silu(W1_e(s) Q8(x[t])) * (W3_e(s) Q8(x[t])) ),  Q8 = MXFP8 quantization.
+ *   Arguments as moe_ffn_forward_mxfp4 (the same MXFP4 weights in either layout; packed needs
+ *   H % 128 == 0 and I % 128 == 0, results bit-identical to the canonical layout); y bf16 [T, H].
+ *   workspace: at least moe_ffn_w4a8_workspace_bytes(T, H, I, E, k) bytes.
+ * Shapes: as moe_ffn_forward (H, I positive multiples of 32).
+ */
+moe_status_t moe_ffn_forward_w4a8(const uint16_t* x, const float* router_logits, int32_t T, int32_t H, int32_t I,
+                                  int32_t E, int32_t k, const uint8_t* w13_q, const uint8_t* w13_e,
+                                  const uint8_t* w2_q, const uint8_t* w2_e, int32_t weight_layout, uint16_t* y,
+                                  int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
  * ---- FP8 (W8A8, per-1x128) variant ----------------------------------------------------------------
  * [ATOM, 6.1: per-1x128 FP8 served by an a8w8 block-scale GEMM; ATOM, 8.1: the FP8 path of the fused
  * MoE; ATOM, 8.2: dynamic activation quantization is part of a format's contract.]  Weights and

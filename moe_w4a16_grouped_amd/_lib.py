@@ -74,6 +74,11 @@ def load() -> ctypes.CDLL:
         "moe_ffn_mxfp4_block_m": ([I32, I32, I32, I32, I32], I32),
         "moe_ffn_mxfp4_workspace_bytes": ([I32, I32, I32, I32, I32], SZ),
         "moe_ffn_forward_mxfp4": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, SZ, P], I32),
+        "moe_mx8_quantize": ([P, I32, I32, P, P, P], I32),
+        "moe_grouped_gemm_w4a8": ([P, P, P, I32, P, P, I32, I32, I32, I32, P, I32, P, I32, I32, P, P, I32, P], I32),
+        "moe_ffn_w4a8_block_m": ([I32, I32, I32], I32),
+        "moe_ffn_w4a8_workspace_bytes": ([I32, I32, I32, I32, I32], SZ),
+        "moe_ffn_forward_w4a8": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, SZ, P], I32),
         "moe_ffn_block_forward": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, I32, P, P, P, P, P,
                                    SZ, P], I32),
         "moe_f8_quantize": ([P, I32, I32, I32, P, P, P], I32),
@@ -99,7 +104,8 @@ EXPORTED = ("moe_abi_version", "moe_status_string", "moe_last_error", "moe_route
             "moe_ffn_block_m", "moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_block_workspace_bytes",
             "moe_ffn_block_forward", "moe_mx_quantize", "moe_mx_quantize_tiles", "moe_mx_prepack", "moe_grouped_gemm_mxfp4", "moe_ffn_mxfp4_block_m",
             "moe_ffn_mxfp4_workspace_bytes", "moe_ffn_forward_mxfp4", "moe_f8_quantize", "moe_grouped_gemm_f8",
-            "moe_ffn_f8_block_m", "moe_ffn_f8_workspace_bytes", "moe_ffn_forward_f8")
+            "moe_ffn_f8_block_m", "moe_ffn_f8_workspace_bytes", "moe_ffn_forward_f8", "moe_mx8_quantize",
+            "moe_grouped_gemm_w4a8", "moe_ffn_w4a8_block_m", "moe_ffn_w4a8_workspace_bytes", "moe_ffn_forward_w4a8")
 
 
 def _check(status: int):
@@ -410,6 +416,69 @@ def moe_ffn_forward_mxfp4(x, router_logits, w13_q, w13_e, w2_q, w2_e, k: int, y=
     _check(load().moe_ffn_forward_mxfp4(_p(x), _p(router_logits), T, H, I, E, k, _p(w13_q), _p(w13_e), _p(w2_q),
                                         _p(w2_e), weight_layout, _p(y), _p(topk_ids_out), _p(topk_w_out), _p(workspace),
                                         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y
+
+
+# ---- W4A8 (MXFP8 activations on MXFP4 weights) ------------------------------------------------------
+
+def moe_mx8_quantize(x, q=None, s=None, stream=None):
+    """x bf16 [rows, K] -> MXFP8 (codes uint8 [rows, K], scale bytes uint8 [rows, K/32])."""
+    _req(x, "16bit", "x")
+    rows, K = x.shape
+    if q is None:
+        q = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+    _check(load().moe_mx8_quantize(_p(x), rows, K, _p(q), _p(s), _stream(stream)))
+    return q, s
+
+
+def moe_grouped_gemm_w4a8(Aq, As, a_row_of, a_row_div: int, Wq, We, tiles, max_tiles: int, num_tiles,
+                          block_m: int, epilogue: int, out_rows: int, out_dtype: int = MOE_OUT_F32, C=None,
+                          Cs=None, stream=None, weight_layout: int = MOE_LAYOUT_CANONICAL):
+    """Grouped W4A8 GEMM over the tile list (MXFP8 activations, row-major).  NONE: returns C
+    [out_rows, N]; SILU_MUL: returns the MXFP8 h as (codes [out_rows, N/2], scale bytes [out_rows, N/64])."""
+    _req(Aq, torch.uint8, "Aq")
+    _req(Wq, torch.uint8, "Wq")
+    E, N, K2 = Wq.shape
+    K = 2 * K2
+    dev = Aq.device
+    if epilogue == MOE_EPI_SILU_MUL:
+        if C is None:
+            C = torch.empty((out_rows, N // 2), dtype=torch.uint8, device=dev)
+        if Cs is None:
+            Cs = torch.empty((out_rows, N // 64), dtype=torch.uint8, device=dev)
+    elif C is None:
+        C = torch.empty((out_rows, N), dtype=torch.float32 if out_dtype == MOE_OUT_F32 else torch.bfloat16, device=dev)
+    _check(load().moe_grouped_gemm_w4a8(_p(Aq), _p(As), _p(a_row_of), a_row_div, _p(Wq), _p(We), weight_layout,
+                                        E, N, K, _p(tiles), max_tiles, _p(num_tiles), block_m, epilogue, _p(C),
+                                        _p(Cs), out_dtype, _stream(stream)))
+    return (C, Cs) if epilogue == MOE_EPI_SILU_MUL else C
+
+
+def moe_ffn_w4a8_block_m(T: int, E: int, k: int) -> int:
+    return int(load().moe_ffn_w4a8_block_m(T, E, k))
+
+
+def moe_ffn_w4a8_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:
+    return int(load().moe_ffn_w4a8_workspace_bytes(T, H, I, E, k))
+
+
+def moe_ffn_forward_w4a8(x, router_logits, w13_q, w13_e, w2_q, w2_e, k: int, y=None, topk_ids_out=None,
+                         topk_w_out=None, workspace=None, stream=None, weight_layout: int = MOE_LAYOUT_CANONICAL):
+    """Whole W4A8 layer: x bf16 [T, H], logits fp32 [T, E], MXFP4 weights -> y bf16 [T, H]."""
+    _req(x, "16bit", "x")
+    T, H = x.shape
+    E, N13, _ = w13_q.shape
+    I = N13 // 2
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    wsb = moe_ffn_w4a8_workspace_bytes(T, H, I, E, k)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=x.device)
+    _check(load().moe_ffn_forward_w4a8(_p(x), _p(router_logits), T, H, I, E, k, _p(w13_q), _p(w13_e), _p(w2_q),
+                                       _p(w2_e), weight_layout, _p(y), _p(topk_ids_out), _p(topk_w_out), _p(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)))
     return y
 
 

@@ -726,6 +726,154 @@ moe_status_t moe_ffn_forward_mxfp4(const uint16_t* x, const float* router_logits
   return hip_status(moe::launch_combine(o, inv, w, nullptr, T, k, H, y, s), "combine launch");
 }
 
+// ---- W4A8 variant (MXFP8 activations on MXFP4 weights) ---------------------------------------------
+
+namespace {
+
+// Workspace of the W4A8 layer: the routing regions of ffn_layout (canonical tile heights), then x
+// quantized (codes [T, H], scale bytes [T, H/32]), h quantized (codes [R, I], scale bytes [R, I/32])
+// and O fp32 [R, H].
+struct W4a8Layout {
+  FfnLayout L;
+  size_t xq, xs, hq, hs, o, total;
+};
+
+W4a8Layout w4a8_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
+  W4a8Layout M{};
+  M.L = ffn_layout(T, H, I, E, k, false);
+  const int64_t R = T * k;
+  size_t off = M.L.h;
+  auto take = [&](size_t bytes) { size_t at = off; off += up256(bytes); return at; };
+  M.xq = take((size_t)T * H);
+  M.xs = take((size_t)T * H / 32);
+  M.hq = take((size_t)R * I);
+  M.hs = take((size_t)R * I / 32);
+  M.o = take((size_t)R * H * 4);
+  M.total = off;
+  return M;
+}
+
+}  // namespace
+
+moe_status_t moe_mx8_quantize(const uint16_t* x, int32_t rows, int32_t K, uint8_t* q, uint8_t* s, void* stream) {
+  if (rows < 0 || K < 32 || K % 32 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_mx8_quantize: need rows >= 0 and K a positive multiple of 32");
+  if ((int64_t)rows >= kMaxRows) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_mx8_quantize: rows=%d must be < 2^26", rows);
+  if (rows == 0) return ok();
+  if (!x || !q || !s) return fail(MOE_ERR_INVALID_ARG, "moe_mx8_quantize: NULL pointer");
+  if (!aligned16(x) || !aligned16(q)) return fail(MOE_ERR_MISALIGNED, "moe_mx8_quantize: x and q need 16-byte alignment");
+  return hip_status(moe::launch_mx8_quant(x, rows, K, q, s, (hipStream_t)stream), "moe_mx8_quantize launch");
+}
+
+moe_status_t moe_grouped_gemm_w4a8(const uint8_t* Aq, const uint8_t* As, const int32_t* a_row_of, int32_t a_row_div,
+                                   const uint8_t* Wq, const uint8_t* We, int32_t weight_layout, int32_t E, int32_t N,
+                                   int32_t K, const int32_t* tiles, int32_t max_tiles, const int32_t* num_tiles,
+                                   int32_t block_m, int32_t epilogue, void* C, uint8_t* Cs, int32_t out_dtype,
+                                   void* stream) {
+  if (E < 1 || N < 1 || K < 1 || max_tiles < 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_w4a8: need E, N, K >= 1, max_tiles >= 0");
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E=%d exceeds %d", E, MOE_MAX_EXPERTS);
+  if (K % 32 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "K=%d must be a multiple of 32", K);
+  if (block_m != 16 && block_m != 32 && block_m != 64)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_grouped_gemm_w4a8: block_m=%d must be 16, 32 or 64", block_m);
+  if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SILU_MUL) return fail(MOE_ERR_INVALID_ARG, "unknown epilogue %d", epilogue);
+  if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return fail(MOE_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
+  if (epilogue == MOE_EPI_SILU_MUL && N % 64 != 0)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "SILU_MUL output is MXFP8: N/2 = %d must be a multiple of 32", N / 2);
+  if (a_row_of && a_row_div < 1) return fail(MOE_ERR_INVALID_ARG, "a_row_div must be >= 1");
+  if (weight_layout != MOE_LAYOUT_CANONICAL && weight_layout != MOE_LAYOUT_PACKED)
+    return fail(MOE_ERR_INVALID_ARG, "unknown weight_layout %d", weight_layout);
+  if (weight_layout == MOE_LAYOUT_PACKED && (N % 16 != 0 || K % 128 != 0))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "packed MXFP4 weights need N %% 16 == 0 and K %% 128 == 0 (N=%d K=%d)", N, K);
+  if (max_tiles == 0) return ok();
+  if (!Aq || !As || !Wq || !We || !tiles || !num_tiles || !C || (epilogue == MOE_EPI_SILU_MUL && !Cs))
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_w4a8: NULL pointer");
+  if (!aligned16(Aq) || !aligned16(Wq) || !aligned16(C) || !aligned4(tiles) || !aligned4(num_tiles) ||
+      (a_row_of && !aligned4(a_row_of)))
+    return fail(MOE_ERR_MISALIGNED, "moe_grouped_gemm_w4a8: Aq, Wq, C need 16-byte alignment");
+  if ((int64_t)max_tiles * block_m >= kMaxRows + (int64_t)MOE_MAX_EXPERTS * block_m)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "max_tiles=%d too large", max_tiles);
+  moe::MxGemmArgs a{Aq, As, a_row_of, a_row_div, Wq, We, N, K, tiles, num_tiles, max_tiles, C, Cs, epilogue,
+                    out_dtype == MOE_OUT_F32, weight_layout == MOE_LAYOUT_PACKED ? 1 : 0, 1};
+  return hip_status(moe::launch_grouped_gemm_mx(a, block_m, (hipStream_t)stream), "moe_grouped_gemm_w4a8 launch");
+}
+
+int32_t moe_ffn_w4a8_block_m(int32_t T, int32_t E, int32_t k) {
+  if (T < 0 || E < 1 || k < 1 || k > E || (int64_t)T * k >= kMaxRows) return -1;
+  return pick_block_m((int64_t)T * k, E, false);
+}
+
+size_t moe_ffn_w4a8_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k) {
+  if (T < 0 || H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0 || E < 1 || k < 1 || k > E || E > MOE_MAX_EXPERTS ||
+      (int64_t)T * k >= kMaxRows)
+    return 0;
+  return w4a8_layout(T, H, I, E, k).total;
+}
+
+moe_status_t moe_ffn_forward_w4a8(const uint16_t* x, const float* router_logits, int32_t T, int32_t H, int32_t I,
+                                  int32_t E, int32_t k, const uint8_t* w13_q, const uint8_t* w13_e,
+                                  const uint8_t* w2_q, const uint8_t* w2_e, int32_t weight_layout, uint16_t* y,
+                                  int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (moe_status_t st = check_routing_shape(T, E, k)) return st;
+  if (H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_ffn_forward_w4a8: H=%d and I=%d must be positive multiples of 32", H, I);
+  if (weight_layout != MOE_LAYOUT_CANONICAL && weight_layout != MOE_LAYOUT_PACKED)
+    return fail(MOE_ERR_INVALID_ARG, "moe_ffn_forward_w4a8: unknown weight_layout %d", weight_layout);
+  if (weight_layout == MOE_LAYOUT_PACKED && (H % 128 != 0 || I % 128 != 0))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "packed MXFP4 weights need H %% 128 == 0 and I %% 128 == 0 (H=%d I=%d)", H, I);
+  if (T == 0) return ok();
+  if (!x || !router_logits || !w13_q || !w13_e || !w2_q || !w2_e || !y || !workspace)
+    return fail(MOE_ERR_INVALID_ARG, "moe_ffn_forward_w4a8: NULL pointer");
+  if (!aligned16(x) || !aligned16(w13_q) || !aligned16(w2_q) || !aligned16(y) || !aligned16(workspace) ||
+      !aligned4(router_logits) || (topk_ids_out && !aligned4(topk_ids_out)) || (topk_w_out && !aligned4(topk_w_out)))
+    return fail(MOE_ERR_MISALIGNED, "moe_ffn_forward_w4a8: x, weight codes, y and workspace need 16-byte alignment");
+  const W4a8Layout M = w4a8_layout(T, H, I, E, k);
+  if (workspace_bytes < M.total)
+    return fail(MOE_ERR_WORKSPACE, "moe_ffn_forward_w4a8: workspace %zu B < required %zu B", workspace_bytes, M.total);
+  const FfnLayout& L = M.L;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
+  int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
+  int32_t* ntiles = reinterpret_cast<int32_t*>(ws + L.ntiles);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(ws + M.xq);
+  uint8_t* xs = reinterpret_cast<uint8_t*>(ws + M.xs);
+  uint8_t* hq = reinterpret_cast<uint8_t*>(ws + M.hq);
+  uint8_t* hs = reinterpret_cast<uint8_t*>(ws + M.hs);
+  float* o = reinterpret_cast<float*>(ws + M.o);
+  const int R = T * k;
+  hipError_t e;
+  if (moe::route_align_fused_fits(T, E, k)) {
+    e = moe::launch_route_align_small(router_logits, T, E, k, L.block_m, ids, w, counts, offsets, sorted, inv,
+                                      tiles, L.max_tiles, ntiles, s);
+    if (e != hipSuccess) return hip_status(e, "route+align launch");
+  } else {
+    e = moe::launch_route_topk(router_logits, T, E, k, ids, w, s);
+    if (e != hipSuccess) return hip_status(e, "route launch");
+    e = moe::launch_align(ids, R, E, L.block_m, counts, offsets, sorted, inv, tiles, L.max_tiles, ntiles,
+                          ws + L.align_ws, s);
+    if (e != hipSuccess) return hip_status(e, "align launch");
+  }
+  e = moe::launch_mx8_quant(x, T, H, xq, xs, s);
+  if (e != hipSuccess) return hip_status(e, "x quantization launch");
+  const int mode = weight_layout == MOE_LAYOUT_PACKED ? 1 : 0;
+  moe::MxGemmArgs g1{xq, xs, sorted, k, w13_q, w13_e, 2 * I, H, tiles, ntiles, L.max_tiles, hq, hs,
+                     MOE_EPI_SILU_MUL, 0, mode, 1};
+  e = moe::launch_grouped_gemm_mx(g1, L.block_m, s);
+  if (e != hipSuccess) return hip_status(e, "gate_up launch");
+  moe::MxGemmArgs g2{hq, hs, nullptr, 1, w2_q, w2_e, H, I, tiles, ntiles, L.max_tiles, o, nullptr, MOE_EPI_NONE, 1,
+                     mode, 1};
+  e = moe::launch_grouped_gemm_mx(g2, L.block_m, s);
+  if (e != hipSuccess) return hip_status(e, "down launch");
+  return hip_status(moe::launch_combine(o, inv, w, nullptr, T, k, H, y, s), "combine launch");
+}
+
 // ---- FP8 (W8A8, per-1x128) variant ------------------------------------------------------------------
 
 moe_status_t moe_f8_quantize(const void* x, int32_t in_dtype, int32_t rows, int32_t K, uint8_t* q, float* s,

@@ -17,6 +17,15 @@
 // result has the 16 x 16 fp32 layout of the bf16 instruction (checked exactly on the GPU).  So a K
 // step of 128 is one instruction per 16 x 16 block, with no dequantization and no scale arithmetic
 // in software.
+//
+// W4A8: the same instruction takes E4M3 activations (format 0) against the E2M1 weights.  Activations
+// are then MXFP8: E4M3 codes, one byte per element, with one E8M0 scale per 32 K elements, X =
+// 2^(floor(log2(amax)) - 8) (8 = the largest E4M3 exponent) and elements rounded to the nearest E4M3
+// value of v / X, ties to even, saturating at 448.  An 8-bit operand is laid out differently from a
+// 4-bit one: lane l supplies 32 bytes, K elements [16 (l / 16), +16) in its first four dwords and
+// [64 + 16 (l / 16), +16) in the last four (measured with one-hot operands on the GPU), while its
+// scale byte still belongs to the 32-element block [32 (l / 16), +32), as for the E2M1 operand.  h
+// leaves the gate_up epilogue as MXFP8.
 #include "launch.h"
 #include "moe_common.h"
 
@@ -54,6 +63,31 @@ __device__ __forceinline__ u32x4 mx_encode32(const float (&v)[32], int e) {
   return c;
 }
 
+// MXFP8 (W4A8 activations): shared exponent floor(log2(amax)) - 8, clamped to E8M0's range; zero and
+// subnormal maxima give -127.
+__device__ __forceinline__ int mx8_block_exp(float amax) {
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+  if (ef == 0) return -127;
+  return max(-127, min(127, ef - 135));
+}
+
+// 32 values -> 32 E4M3 codes of v / 2^e (exact power-of-two scaling, clamped to +-448, then the
+// hardware conversion: nearest, ties to even), element j at byte j.
+__device__ __forceinline__ void mx8_encode32(const float (&v)[32], int e, u32x4& c0, u32x4& c1) {
+  uint32_t w[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    float a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = fminf(fmaxf(ldexpf(v[4 * d + j], -e), -448.0f), 448.0f);
+    int t = __builtin_amdgcn_cvt_pk_fp8_f32(a[0], a[1], 0, false);
+    t = __builtin_amdgcn_cvt_pk_fp8_f32(a[2], a[3], t, true);
+    w[d] = (uint32_t)t;
+  }
+  c0 = u32x4{w[0], w[1], w[2], w[3]};
+  c1 = u32x4{w[4], w[5], w[6], w[7]};
+}
+
 // ---------------------------------------------------------------------------------------------------
 // Activation quantization: one thread per 32-element block of a row-major bf16 matrix whose rows
 // are whole blocks, so block i sits at element 32 i of x, byte 16 i of the codes and byte i of the
@@ -78,6 +112,40 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restric
   const int e = mx_block_exp(amax);
   *reinterpret_cast<u32x4*>(q + i * 16) = mx_encode32(v, e);
   s[i] = (uint8_t)(e + 127);
+}
+
+// MXFP8 quantization, same decomposition: 32 code bytes (two 16-byte stores) and one scale byte per
+// thread.
+__global__ __launch_bounds__(256) void mx8_quant_kernel(const uint16_t* __restrict__ x, long long nblocks,
+                                                        uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nblocks) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + i * 32);
+  float v[32];
+  float amax = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const u32x4 w = src[d];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * d + 2 * j] = __uint_as_float(w[j] << 16);
+      v[8 * d + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      amax = fmaxf(amax, fmaxf(fabsf(v[8 * d + 2 * j]), fabsf(v[8 * d + 2 * j + 1])));
+    }
+  }
+  const int e = mx8_block_exp(amax);
+  u32x4 c0, c1;
+  mx8_encode32(v, e, c0, c1);
+  *reinterpret_cast<u32x4*>(q + i * 32) = c0;
+  *reinterpret_cast<u32x4*>(q + i * 32 + 16) = c1;
+  s[i] = (uint8_t)(e + 127);
+}
+
+hipError_t launch_mx8_quant(const uint16_t* x, long long rows, int K, uint8_t* q, uint8_t* s, hipStream_t stream) {
+  const long long nblocks = rows * (K / 32);
+  if (nblocks <= 0) return hipSuccess;
+  mx8_quant_kernel<<<dim3((unsigned)((nblocks + 255) / 256)), 256, 0, stream>>>(x, nblocks, q, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_mx_quant(const uint16_t* x, long long rows, int K, uint8_t* q, uint8_t* s, hipStream_t stream) {
@@ -184,10 +252,15 @@ hipError_t launch_mx_prepack(const uint8_t* wq, const uint8_t* we, int E, int N,
 // Epilogues: NONE stores fp32 or bf16 rows; SILU_MUL forms h = silu(gate) * up in fp32 (gate rows
 // [0, N/2), up rows [N/2, N) of the weight), gathers the tile's h in LDS and quantizes each
 // 32-column block of each row to MXFP4 (codes [rows, N/4], scale bytes [rows, N/64]) for the next
-// projection.
-template <int BM, int BN, int KW, int PF, int EPI, bool OUT_F32, int MODE>
+// projection.  AF = 0 (W4A8): MXFP8 activations (32 code bytes per lane and K step in the 8-bit operand
+// layout above, row-major only), the instruction's A format E4M3, and h quantized to MXFP8 (codes
+// [rows, N/2], scale bytes [rows, N/64]).
+template <int BM, int BN, int KW, int PF, int EPI, bool OUT_F32, int MODE, int AF = 4>
 __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
   constexpr bool ATB = MODE == 2, WPK = MODE >= 1;  // tile-blocked activations, packed weights
+  constexpr bool A8 = AF == 0;                       // E4M3 activations
+  static_assert(AF == 0 || AF == 4, "activation format");
+  static_assert(!A8 || !ATB, "MXFP8 activations are row-major");
   constexpr int WNS = 4 / KW;             // waves along N
   constexpr int WN = BN / WNS;            // columns per wave
   constexpr int MI = BM / 16, NI = WN / 16;
@@ -213,6 +286,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
   const int per = (nks + KW - 1) / KW;
   const int s_begin = min(nks, wk * per), s_end = min(nks, s_begin + per);
   const int KB = K / 2, KS = K / 32;  // bytes of codes and of scales per row
+  const int KBA = A8 ? K : KB;        // bytes of activation codes per row
 
   // activation fragments: row mi * 16 + l16 of the tile (row-major: padding rows read the first row)
   const uint8_t* aq[MI];
@@ -227,7 +301,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
       const int i = mi * 16 + l16;
       const int r = row0 + (i < rows ? i : 0);
       const int ar = p.a_row_of ? p.a_row_of[r] / p.a_row_div : r;
-      aq[mi] = p.Aq + (size_t)ar * KB + q * 16;
+      aq[mi] = p.Aq + (size_t)ar * KBA + (A8 ? 0 : q * 16);
       as[mi] = p.As + (size_t)ar * KS + q;
     }
   }
@@ -266,7 +340,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 areg[NS][MI], breg[NS][NI];
+  u32x4 areg[NS][MI], areg2[NS][MI], breg[NS][NI];  // areg2: second half of an E4M3 fragment
   uint32_t asc[NS][MI], bsc[NS][NI];
   auto load_step = [&](int s, int u) {
     s = min(s, s_end - 1);  // prefetches past this wave's range re-read its last step (unused)
@@ -275,6 +349,10 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
     const bool qv = WPK || s * 128 + 32 * q < K;
     const int cb = qv ? s * 64 : (K - 32 - 32 * q) / 2;  // code byte offset of this lane's block
     const int sb = qv ? s * 4 : (K / 32 - 1 - q);        // scale byte offset
+    // E4M3 activations: this lane's two 16-byte halves lie in blocks q / 2 and 2 + q / 2 of the step;
+    // a half past K reads the row's first bytes and is zeroed
+    const bool v0 = WPK || s * 4 + (q >> 1) < K / 32, v1 = WPK || s * 4 + 2 + (q >> 1) < K / 32;
+    const int o0 = v0 ? s * 128 + 16 * q : 0, o1 = v1 ? s * 128 + 64 + 16 * q : 0;
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       breg[u][ni] = *reinterpret_cast<const u32x4*>(wq[ni] + (WPK ? (size_t)s * 1024 : (size_t)cb));
@@ -282,8 +360,15 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
     }
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(aq[mi] + (ATB ? (size_t)s * 1024 : (size_t)cb));
-      areg[u][mi] = qv ? a : u32x4{0u, 0u, 0u, 0u};
+      if (A8) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(aq[mi] + o0);
+        const u32x4 a2 = *reinterpret_cast<const u32x4*>(aq[mi] + o1);
+        areg[u][mi] = v0 ? a : u32x4{0u, 0u, 0u, 0u};
+        areg2[u][mi] = v1 ? a2 : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(aq[mi] + (ATB ? (size_t)s * 1024 : (size_t)cb));
+        areg[u][mi] = qv ? a : u32x4{0u, 0u, 0u, 0u};
+      }
       asc[u][mi] = as[mi][ATB ? s * 64 : sb];
     }
   };
@@ -291,12 +376,13 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       const u32x4 a = areg[u][mi];
-      const i32x8 a8 = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+      const u32x4 a2 = A8 ? areg2[u][mi] : u32x4{0u, 0u, 0u, 0u};
+      const i32x8 a8 = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)a2[0], (int)a2[1], (int)a2[2], (int)a2[3]};
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         const u32x4 b = breg[u][ni];
         const i32x8 b8 = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
-        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[mi][ni], 4, 4, 0, (int)asc[u][mi],
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[mi][ni], AF, 4, 0, (int)asc[u][mi],
                                                                         0, (int)bsc[u][ni]);
       }
     }
@@ -377,8 +463,20 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
         v[4 * d + 3] = f.w;
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
       }
-      const int ex = mx_block_exp(amax);
       uint8_t* C = static_cast<uint8_t*>(p.C);
+      if (A8) {
+        // MXFP8 h, row-major (codes [rows, N/2], scale bytes [rows, N/64])
+        const int ex = mx8_block_exp(amax);
+        u32x4 c0, c1;
+        mx8_encode32(v, ex, c0, c1);
+        const size_t orow = (size_t)(row0 + row);
+        uint8_t* dst = C + orow * (N / 2) + hcol;
+        *reinterpret_cast<u32x4*>(dst) = c0;
+        *reinterpret_cast<u32x4*>(dst + 16) = c1;
+        p.Cs[orow * (N / 64) + hcol / 32] = (uint8_t)(ex + 127);
+        continue;
+      }
+      const int ex = mx_block_exp(amax);
       if (ATB) {
         // tile-blocked for the next projection (K = N/2 there)
         const int b = hcol / 32, ln = (b & 3) * 16 + (row & 15);
@@ -650,11 +748,12 @@ static hipError_t launch_mx_mm(const MxGemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int KW, int PF, int MODE>
+template <int BM, int BN, int KW, int PF, int MODE, int AF = 4>
 static void launch_mx_mode(const MxGemmArgs& a, dim3 grid, hipStream_t s) {
-  if (a.epilogue == MOE_EPI_SILU_MUL) gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_SILU_MUL, false, MODE><<<grid, 256, 0, s>>>(a);
-  else if (a.out_f32) gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, true, MODE><<<grid, 256, 0, s>>>(a);
-  else gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, false, MODE><<<grid, 256, 0, s>>>(a);
+  if (a.epilogue == MOE_EPI_SILU_MUL)
+    gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_SILU_MUL, false, MODE, AF><<<grid, 256, 0, s>>>(a);
+  else if (a.out_f32) gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, true, MODE, AF><<<grid, 256, 0, s>>>(a);
+  else gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, false, MODE, AF><<<grid, 256, 0, s>>>(a);
 }
 
 template <int BM, int BN, int KW, int PF>
@@ -662,6 +761,11 @@ static hipError_t launch_mx_cfg(const MxGemmArgs& a, hipStream_t s) {
   const int ncols = a.epilogue == MOE_EPI_SILU_MUL ? a.N / 2 : a.N;
   const int bcols = a.epilogue == MOE_EPI_SILU_MUL ? BN / 2 : BN;
   const dim3 grid = grid2d(8LL * ((a.max_tiles + 7) / 8) * ((ncols + bcols - 1) / bcols));
+  if (a.act_e4m3) {  // W4A8 (row-major activations; the caller rejects mode 2)
+    if (a.mode == 1) launch_mx_mode<BM, BN, KW, PF, 1, 0>(a, grid, s);
+    else launch_mx_mode<BM, BN, KW, PF, 0, 0>(a, grid, s);
+    return hipGetLastError();
+  }
   switch (a.mode) {
     case 2: launch_mx_mode<BM, BN, KW, PF, 2>(a, grid, s); break;
     case 1: launch_mx_mode<BM, BN, KW, PF, 1>(a, grid, s); break;
@@ -675,6 +779,7 @@ constexpr int kMxSplitKMaxTiles = 32;
 
 hipError_t launch_grouped_gemm_mx(const MxGemmArgs& a, int block_m, hipStream_t stream) {
   if (a.max_tiles <= 0) return hipSuccess;
+  // (W4A8 runs the register kernel only; the caller never passes 128-row tiles with it)
   if (block_m == 128) return a.mode == 1 ? launch_mx_mm<1>(a, stream) : launch_mx_mm<0>(a, stream);
   // Configurations from sweeps on MI355X (HIP events, weights streamed from HBM, packed weights and
   // tile-blocked activations), 128 experts top-8: gate_up at 1 / 8 / 64 tokens takes 7.7 / 18.8 /

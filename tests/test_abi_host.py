@@ -316,3 +316,43 @@ def test_f8_entry_points_reject(lib):
     assert fw(ws13=_ptr(FAKE + 2)) == -3                           # fp32 scales need 4-byte alignment
     assert fw(ws13=None) == -1
     assert fw(T=0) == 0
+
+
+def test_w4a8_entry_points_reject(lib):
+    f = _ptr(FAKE)
+    # quantizer
+    assert lib.moe_mx8_quantize(f, 4, 48, f, f, None) == -1          # K % 32
+    assert lib.moe_mx8_quantize(f, 0, 64, f, f, None) == 0
+    assert lib.moe_mx8_quantize(_ptr(FAKE + 8), 4, 64, f, f, None) == -3
+    assert lib.moe_mx8_quantize(f, 4, 64, f, None, None) == -1
+    # grouped GEMM (MXFP8 activations, row-major)
+    g = lambda **kw: lib.moe_grouped_gemm_w4a8(f, f, None, 1, f, f, kw.get("wl", 0), 4, kw.get("N", 256),
+                                               kw.get("K", 256), f, kw.get("mt", 8), f, kw.get("bm", 16),
+                                               kw.get("epi", 0), kw.get("C", f), kw.get("cs", f), kw.get("od", 1), None)
+    assert g(K=48) == -2
+    assert g(bm=128) == -2                                          # register kernel only
+    assert g(epi=1, N=96) == -2                                     # h blocks of 32 columns
+    assert g(epi=5) == -1
+    assert g(od=7) == -1
+    assert g(wl=1, K=96) == -2                                      # packed weights: K % 128
+    assert g(epi=1, cs=None) == -1                                  # h scale bytes
+    assert g(C=_ptr(FAKE + 4)) == -3
+    assert g(mt=0, C=None) == 0                                     # no tiles: nothing to launch
+    # layer
+    assert moe.moe_ffn_w4a8_block_m(800, 256, 8) == 32
+    assert moe.moe_ffn_w4a8_block_m(4096, 8, 2) == 64              # never the 128-row tiles
+    assert moe.moe_ffn_w4a8_block_m(4, 8, 9) == -1
+    T, H, I, E, k = 16, 256, 128, 8, 2
+    ws = moe.moe_ffn_w4a8_workspace_bytes(T, H, I, E, k)
+    R = T * k
+    assert ws >= T * H + R * I + R * H * 4                          # x codes, h codes, down output
+    assert moe.moe_ffn_w4a8_workspace_bytes(T, H, 96, E, 10) == 0   # k > E
+    fw = lambda **kw: lib.moe_ffn_forward_w4a8(kw.get("x", f), f, kw.get("T", T), kw.get("H", H), kw.get("I", I), E,
+                                               kw.get("k", k), f, f, f, f, kw.get("wl", 0), f, None, None, f,
+                                               kw.get("ws", ws), None)
+    assert fw(H=200) == -2
+    assert fw(wl=1, I=96) == -2                                     # packed weights: I % 128
+    assert fw(k=9) == -1
+    assert fw(ws=ws - 1) == -4
+    assert fw(x=_ptr(FAKE + 2)) == -3
+    assert fw(T=0) == 0
