@@ -405,6 +405,120 @@ def run_mxfp4(args):
     print(json.dumps(result), flush=True)
 
 
+def run_w4a8(args):
+    """The W4A8 layer: x and h quantized to MXFP8 (E4M3, E8M0 per 32) on the fly, E4M3 x E2M1 products on
+    the scaled matrix instruction against the MXFP4 weights.  Same workload shapes, rotation and timing
+    as the W4A16 layer."""
+    import moe_w4a16_grouped_amd as moe
+
+    wl = mi.WORKLOADS[args.workload]
+    T, E, k, H, I = wl.T, wl.E, wl.k, wl.H, wl.I
+    R = T * k
+    log(f"bench: W4A8 workload {wl.name} T={T} E={E} k={k} H={H} I={I}; generating inputs")
+    inp = mi.make_mx_inputs(wl)
+    x, logits = dev_bf16(inp.x), dev(inp.logits)
+    ids0, _ = moe.moe_route_topk(logits, k)
+    touched = int(torch.unique(ids0).numel())
+    bpe = mi.mx_weight_bytes_per_expert(H, I)
+    L = args.copies or max(1, math.ceil((1 << 30) / (touched * bpe)))
+    w0 = (dev(inp.w13_q), dev(inp.w13_e), dev(inp.w2_q), dev(inp.w2_e))
+    copies = [w0] + [tuple(t.clone() for t in w0) for _ in range(L - 1)]
+    layout = moe.MOE_LAYOUT_PACKED if args.layout == "packed" else moe.MOE_LAYOUT_CANONICAL
+    if layout == moe.MOE_LAYOUT_PACKED:
+        copies = [moe.moe_mx_prepack(a, b) + moe.moe_mx_prepack(c, d) for (a, b, c, d) in copies]
+        torch.cuda.synchronize()
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_ffn_w4a8_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device="cuda")
+    log(f"bench: {L} weight copies ({touched} of {E} experts touched); warmup {args.warmup}, steps {args.steps}")
+
+    def step(i):
+        q13, e13, q2, e2 = copies[i % L]
+        moe.moe_ffn_forward_w4a8(x, logits, q13, e13, q2, e2, k, y=y, workspace=ws, weight_layout=layout)
+
+    eager_ms, graph_ms = time_steps(step, L, args)
+    ms = eager_ms if graph_ms is None else min(eager_ms, graph_ms)
+    log(f"bench: W4A8 layer eager {eager_ms * 1e3:.1f} us, graph {graph_ms * 1e3 if graph_ms else 0:.1f} us")
+
+    # per-kernel pass through the separate entry points
+    bm = moe.moe_ffn_w4a8_block_m(T, E, k)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    xq = torch.empty((T, H), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((T, H // 32), dtype=torch.uint8, device="cuda")
+    hq = torch.empty((R, I), dtype=torch.uint8, device="cuda")
+    hs = torch.empty((R, I // 32), dtype=torch.uint8, device="cuda")
+    O = torch.empty((R, H), dtype=torch.float32, device="cuda")
+    names = ["route", "align", "quant_x", "gate_up", "down", "combine"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    for i in range(args.warmup + args.steps):
+        q13, e13, q2, e2 = copies[i % L]
+        e = evs[i - args.warmup] if i >= args.warmup else None
+        if e: e[0].record()
+        moe.moe_route_topk(logits, k, ids, wts)
+        if e: e[1].record()
+        al = moe.moe_align(ids, E, bm)
+        if e: e[2].record()
+        moe.moe_mx8_quantize(x, xq, xs)
+        if e: e[3].record()
+        moe.moe_grouped_gemm_w4a8(xq, xs, al["sorted_ids"], k, q13, e13, al["tiles"], al["max_tiles"],
+                                  al["num_tiles"], bm, moe.MOE_EPI_SILU_MUL, R, C=hq, Cs=hs, weight_layout=layout)
+        if e: e[4].record()
+        moe.moe_grouped_gemm_w4a8(hq, hs, None, 1, q2, e2, al["tiles"], al["max_tiles"], al["num_tiles"], bm,
+                                  moe.MOE_EPI_NONE, R, moe.MOE_OUT_F32, C=O, weight_layout=layout)
+        if e: e[5].record()
+        moe.moe_combine(O, al["inv_perm"], wts, y=y)
+        if e: e[6].record()
+    torch.cuda.synchronize()
+    kern_us = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in evs]) * 1e3) for j, n in enumerate(names)}
+    log("bench: per-kernel us (events): " + ", ".join(f"{n}={v:.1f}" for n, v in kern_us.items()))
+
+    us = ms * 1e3
+    flops = 6.0 * R * H * I
+    weight_bytes = touched * bpe
+    g13 = 2 * I * H // 2 + 2 * I * (H // 32)
+    gu_bytes = touched * g13 + T * H + T * H // 32 + R * I + R * I // 32
+    gu_flops = 4.0 * R * H * I
+    gu_us = kern_us["gate_up"]
+    # an 8-bit operand runs the scaled instruction at the fp8 rate
+    ridge = MFMA_FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if gu_flops / gu_bytes < ridge:
+        bound, achieved, peak, unit = "hbm", gu_bytes / (gu_us * 1e-6) / 1e9, HBM_PEAK_GBPS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", gu_flops / (gu_us * 1e-6) / 1e12, MFMA_FP8_PEAK_TFLOPS, "TFLOP/s"
+    result = {
+        "metric": METRIC,
+        "value": round(us, 2),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8 x fp4 (E4M3 x E2M1, E8M0 per-32 scales; fp32 accumulation)",
+        "data": "synthetic (seeded; E2M1 codes uniform, E8M0 scales 2^-8..2^-6, x and logits N(0,1))",
+        "config": {"workload": f"{wl.name} W4A8 (MXFP8 activations): {T} tokens, {E} experts top-{k}, hidden {H}, "
+                               f"intermediate {I}", "method": "w4a8", "tokens": T, "experts": E, "top_k": k,
+                   "hidden": H, "intermediate": I, "weight_copies": L, "touched_experts": touched,
+                   "weight_layout": args.layout},
+        "tflops": round(flops / (us * 1e-6) / 1e12, 3),
+        "weight_gbps": round(weight_bytes / (us * 1e-6) / 1e9, 1),
+        "timing": {"eager_us": round(eager_ms * 1e3, 2), "graph_us": None if graph_ms is None else round(graph_ms * 1e3, 2),
+                   "value_from": "graph" if graph_ms is not None and graph_ms <= eager_ms else "eager"},
+        "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
+        "roofline": {"kernel": "gemm_mx_kernel, E4M3 activations (gate_up + SiLU*mul + h quantization)", "bound": bound,
+                     "achieved": round(achieved, 2), "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": None, "algorithmic_bytes": gu_bytes, "algorithmic_flops": gu_flops},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        log(f"bench: timing the W4A8 CPU oracle on a token sample (~{args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline_mx(inp, args.cpu_seconds, oracle.moe_ffn_w4a8)
+    print(json.dumps(result), flush=True)
+
+
 def run_f8(args):
     """The FP8 (W8A8, per-1x128) layer: x and h quantized per 1x128 on the fly, E4M3 x E4M3 products
     on the FP8 matrix instruction.  Same workload shapes, rotation and timing as the W4A16 layer."""
@@ -536,9 +650,9 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="run only the counter-calibration copy")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
     ap.add_argument("--calibrate", action="store_true", help="measure copy bandwidth and a vendor bf16 GEMM rate only")
-    ap.add_argument("--method", choices=["w4a16", "mxfp4", "f8"], default="w4a16",
+    ap.add_argument("--method", choices=["w4a16", "mxfp4", "w4a8", "f8"], default="w4a16",
                     help="w4a16: bf16 activations, bf16 group scales (the default); mxfp4: W4A4 with E8M0 scales; "
-                         "f8: W8A8 E4M3 with per-1x128 fp32 scales")
+                         "w4a8: MXFP8 activations on the MXFP4 weights; f8: W8A8 E4M3 with per-1x128 fp32 scales")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the whole-block timing (router gate + shared expert + routed layer)")
     args = ap.parse_args()
@@ -558,6 +672,9 @@ def main():
         return
     if args.method == "f8":
         run_f8(args)
+        return
+    if args.method == "w4a8":
+        run_w4a8(args)
         return
 
     import moe_w4a16_grouped_amd as moe
