@@ -440,7 +440,7 @@ def run_w4a8(args):
     log(f"bench: W4A8 layer eager {eager_ms * 1e3:.1f} us, graph {graph_ms * 1e3 if graph_ms else 0:.1f} us")
 
     # per-kernel pass through the separate entry points
-    bm = moe.moe_ffn_w4a8_block_m(T, E, k)
+    bm = moe.moe_ffn_w4a8_block_m(T, H, I, E, k)
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
     xq = torch.empty((T, H), dtype=torch.uint8, device="cuda")

@@ -388,8 +388,10 @@ moe_status_t moe_mx8_quantize(const uint16_t* x, int32_t rows, int32_t K, uint8_
  *   epilogue SILU_MUL: h[r, j] = silu(G[r, j]) * G[r, N/2 + j] in fp32, then quantized to MXFP8 per 32
  *                      columns: C = codes [rows, N/2], Cs = scale bytes [rows, N/64] (out_dtype ignored).
  * weight_layout: MOE_LAYOUT_CANONICAL or MOE_LAYOUT_PACKED (moe_mx_prepack; needs N % 16 == 0 and
- * K % 128 == 0); results are bit-identical across layouts.  block_m 16, 32 or 64.  K % 32 == 0;
- * SILU_MUL needs N % 64 == 0.  Aq, Wq and C 16-byte aligned.
+ * K % 128 == 0); results are bit-identical across layouts.  block_m 16, 32, 64 or 128 (the tile height
+ * moe_align used); 128 runs a 128 x 256 LDS-staged kernel (bit-identical to the others) that needs
+ * K % 128 == 0 and 4-byte aligned As and We.  K % 32 == 0; SILU_MUL needs N % 64 == 0.  Aq, Wq and C
+ * 16-byte aligned.
  */
 moe_status_t moe_grouped_gemm_w4a8(const uint8_t* Aq, const uint8_t* As, const int32_t* a_row_of, int32_t a_row_div,
                                    const uint8_t* Wq, const uint8_t* We, int32_t weight_layout, int32_t E, int32_t N,
@@ -397,8 +399,9 @@ moe_status_t moe_grouped_gemm_w4a8(const uint8_t* Aq, const uint8_t* As, const i
                                    int32_t block_m, int32_t epilogue, void* C, uint8_t* Cs, int32_t out_dtype,
                                    void* stream);
 
-/* Row-tile height and workspace bytes of moe_ffn_forward_w4a8 (host-only, pure; -1 / 0 on invalid sizes). */
-int32_t moe_ffn_w4a8_block_m(int32_t T, int32_t E, int32_t k);
+/* Row-tile height and workspace bytes of moe_ffn_forward_w4a8 (host-only, pure; -1 / 0 on invalid sizes):
+ * the MXFP4 layer's choice (128 for experts averaging more than 128 rows with H, I multiples of 128). */
+int32_t moe_ffn_w4a8_block_m(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k);
 size_t moe_ffn_w4a8_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k);
 
 /*
@@ -407,6 +410,8 @@ size_t moe_ffn_w4a8_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, 
  *   y[t] = sum_s w[t,s] * W2_e(s) Q8( silu(W1_e(s) Q8(x[t])) * (W3_e(s) Q8(x[t])) ),  Q8 = MXFP8 quantization.
  *   Arguments as moe_ffn_forward_mxfp4 (the same MXFP4 weights in either layout; packed needs
  *   H % 128 == 0 and I % 128 == 0, results bit-identical to the canonical layout); y bf16 [T, H].
+ *   With experts of more than 128 rows on average (and H, I multiples of 128) the 128-row kernel
+ *   runs and the scale arrays need 4-byte alignment.
  *   workspace: at least moe_ffn_w4a8_workspace_bytes(T, H, I, E, k) bytes.
  * Shapes: as moe_ffn_forward (H, I positive multiples of 32).
  */

@@ -76,7 +76,7 @@ def load() -> ctypes.CDLL:
         "moe_ffn_forward_mxfp4": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, SZ, P], I32),
         "moe_mx8_quantize": ([P, I32, I32, P, P, P], I32),
         "moe_grouped_gemm_w4a8": ([P, P, P, I32, P, P, I32, I32, I32, I32, P, I32, P, I32, I32, P, P, I32, P], I32),
-        "moe_ffn_w4a8_block_m": ([I32, I32, I32], I32),
+        "moe_ffn_w4a8_block_m": ([I32, I32, I32, I32, I32], I32),
         "moe_ffn_w4a8_workspace_bytes": ([I32, I32, I32, I32, I32], SZ),
         "moe_ffn_forward_w4a8": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, SZ, P], I32),
         "moe_ffn_block_forward": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, I32, P, P, P, P, P,
@@ -456,8 +456,8 @@ def moe_grouped_gemm_w4a8(Aq, As, a_row_of, a_row_div: int, Wq, We, tiles, max_t
     return (C, Cs) if epilogue == MOE_EPI_SILU_MUL else C
 
 
-def moe_ffn_w4a8_block_m(T: int, E: int, k: int) -> int:
-    return int(load().moe_ffn_w4a8_block_m(T, E, k))
+def moe_ffn_w4a8_block_m(T: int, H: int, I: int, E: int, k: int) -> int:
+    return int(load().moe_ffn_w4a8_block_m(T, H, I, E, k))
 
 
 def moe_ffn_w4a8_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:

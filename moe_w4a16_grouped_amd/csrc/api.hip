@@ -738,10 +738,14 @@ struct W4a8Layout {
   size_t xq, xs, hq, hs, o, total;
 };
 
+// Tile heights as the MXFP4 layer: experts averaging more than 128 rows (H, I multiples of 128) take the
+// 128 x 256 LDS-staged kernel; the canonical tile capacity of ffn_layout covers its shorter list.
 W4a8Layout w4a8_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   W4a8Layout M{};
   M.L = ffn_layout(T, H, I, E, k, false);
   const int64_t R = T * k;
+  M.L.block_m = pick_mx_block_m(R, E, H, I);
+  M.L.max_tiles = (int32_t)max_tiles_of(R, E, M.L.block_m);
   size_t off = M.L.h;
   auto take = [&](size_t bytes) { size_t at = off; off += up256(bytes); return at; };
   M.xq = take((size_t)T * H);
@@ -774,8 +778,10 @@ moe_status_t moe_grouped_gemm_w4a8(const uint8_t* Aq, const uint8_t* As, const i
     return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_w4a8: need E, N, K >= 1, max_tiles >= 0");
   if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E=%d exceeds %d", E, MOE_MAX_EXPERTS);
   if (K % 32 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "K=%d must be a multiple of 32", K);
-  if (block_m != 16 && block_m != 32 && block_m != 64)
-    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_grouped_gemm_w4a8: block_m=%d must be 16, 32 or 64", block_m);
+  if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_grouped_gemm_w4a8: block_m=%d must be 16, 32, 64 or 128", block_m);
+  if (block_m == 128 && K % 128 != 0)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_grouped_gemm_w4a8: block_m 128 needs K %% 128 == 0 (K=%d)", K);
   if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SILU_MUL) return fail(MOE_ERR_INVALID_ARG, "unknown epilogue %d", epilogue);
   if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return fail(MOE_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
   if (epilogue == MOE_EPI_SILU_MUL && N % 64 != 0)
@@ -791,6 +797,8 @@ moe_status_t moe_grouped_gemm_w4a8(const uint8_t* Aq, const uint8_t* As, const i
   if (!aligned16(Aq) || !aligned16(Wq) || !aligned16(C) || !aligned4(tiles) || !aligned4(num_tiles) ||
       (a_row_of && !aligned4(a_row_of)))
     return fail(MOE_ERR_MISALIGNED, "moe_grouped_gemm_w4a8: Aq, Wq, C need 16-byte alignment");
+  if (block_m == 128 && (!aligned4(As) || !aligned4(We)))
+    return fail(MOE_ERR_MISALIGNED, "moe_grouped_gemm_w4a8: block_m 128 needs 4-byte aligned scale arrays");
   if ((int64_t)max_tiles * block_m >= kMaxRows + (int64_t)MOE_MAX_EXPERTS * block_m)
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "max_tiles=%d too large", max_tiles);
   moe::MxGemmArgs a{Aq, As, a_row_of, a_row_div, Wq, We, N, K, tiles, num_tiles, max_tiles, C, Cs, epilogue,
@@ -798,9 +806,9 @@ moe_status_t moe_grouped_gemm_w4a8(const uint8_t* Aq, const uint8_t* As, const i
   return hip_status(moe::launch_grouped_gemm_mx(a, block_m, (hipStream_t)stream), "moe_grouped_gemm_w4a8 launch");
 }
 
-int32_t moe_ffn_w4a8_block_m(int32_t T, int32_t E, int32_t k) {
-  if (T < 0 || E < 1 || k < 1 || k > E || (int64_t)T * k >= kMaxRows) return -1;
-  return pick_block_m((int64_t)T * k, E, false);
+int32_t moe_ffn_w4a8_block_m(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k) {
+  if (T < 0 || E < 1 || k < 1 || k > E || (int64_t)T * k >= kMaxRows || H < 32 || I < 32) return -1;
+  return pick_mx_block_m((int64_t)T * k, E, H, I);
 }
 
 size_t moe_ffn_w4a8_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k) {
@@ -860,6 +868,8 @@ moe_status_t moe_ffn_forward_w4a8(const uint16_t* x, const float* router_logits,
                           ws + L.align_ws, s);
     if (e != hipSuccess) return hip_status(e, "align launch");
   }
+  if (L.block_m == 128 && (!aligned4(w13_e) || !aligned4(w2_e)))
+    return fail(MOE_ERR_MISALIGNED, "moe_ffn_forward_w4a8: scale arrays need 4-byte alignment");
   e = moe::launch_mx8_quant(x, T, H, xq, xs, s);
   if (e != hipSuccess) return hip_status(e, "x quantization launch");
   const int mode = weight_layout == MOE_LAYOUT_PACKED ? 1 : 0;

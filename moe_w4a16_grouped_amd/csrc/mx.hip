@@ -522,7 +522,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
 // (row, 32-column block) quantizes it into row-major codes and scale bytes.
 constexpr int kMxMmBM = 128, kMxMmBN = 256;
 constexpr int kMxMmA = kMxMmBM * 64, kMxMmB = kMxMmBN * 64;  // code bytes per stage
-constexpr int kMxMmStage = kMxMmA + kMxMmB + (kMxMmBM + kMxMmBN) * 4;
+constexpr int kMxMmA8 = kMxMmBM * 128;                        // E4M3 activation bytes per stage (W4A8)
 constexpr int kMxMmHLD = kMxMmBN / 2 + 4;                     // padded LDS row of the h tile (floats)
 
 // Direct global->LDS 4-byte load (lane l writes LDS bytes [4l, 4l+4) after the wave-uniform base).
@@ -533,6 +533,8 @@ __device__ __forceinline__ void g2lds4_mx(const void* g, void* lds_wave_base) {
 }
 
 __device__ __forceinline__ int mx_swz(int row) { return (row >> 2) & 3; }
+// E4M3 activation rows (128 bytes per K step): chunks swizzled by (row / 2) % 8.
+__device__ __forceinline__ int mx8_swz(int row) { return (row >> 1) & 7; }
 
 // s_waitcnt vmcnt(n) for a run-time n in [0, 8].
 __device__ __forceinline__ void wait_vmcnt_upto8(int n) {
@@ -549,12 +551,17 @@ __device__ __forceinline__ void wait_vmcnt_upto8(int n) {
   }
 }
 
-template <int EPI, bool OUT_F32, int MODE, int NSTAGE>
+// AF = 0 (W4A8): E4M3 activations, 128-byte code rows per K step copied by two direct loads per wave
+// and read in the 8-bit operand layout (two 16-byte halves per lane); h leaves as MXFP8.
+template <int EPI, bool OUT_F32, int MODE, int NSTAGE, int AF = 4>
 __global__ __launch_bounds__(512) void gemm_mx_mm(MxGemmArgs p) {
   constexpr int MI = 4, NI = 4;
   constexpr bool WPK = MODE == 1;
-  static_assert(NSTAGE >= 3 && NSTAGE * kMxMmStage >= kMxMmBM * kMxMmHLD * 4, "stages also hold the h tile");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * kMxMmStage];
+  constexpr bool A8 = AF == 0;
+  constexpr int ABYTES = A8 ? kMxMmA8 : kMxMmA;                      // activation code bytes per stage
+  constexpr int STAGE = ABYTES + kMxMmB + (kMxMmBM + kMxMmBN) * 4;
+  static_assert(NSTAGE >= 3 && NSTAGE * STAGE >= kMxMmBM * kMxMmHLD * 4, "stages also hold the h tile");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * STAGE];
   __shared__ int32_t sRow[kMxMmBM];
   const int N = p.N, K = p.K;
   const int ncols = EPI == MOE_EPI_SILU_MUL ? N / 2 : N;
@@ -570,6 +577,7 @@ __global__ __launch_bounds__(512) void gemm_mx_mm(MxGemmArgs p) {
   const int l16 = lane & 15, q = lane >> 4;
   const int nks = K / 128;
   const int KB = K / 2, KS = K / 32;  // code and scale bytes per row
+  const int KBA = A8 ? K : KB;        // activation code bytes per row
 
   for (int i = tid; i < kMxMmBM; i += 512) {
     const int r = row0 + (i < rows ? i : 0);
@@ -591,10 +599,18 @@ __global__ __launch_bounds__(512) void gemm_mx_mm(MxGemmArgs p) {
   };
   // code sources: one instruction covers 16 rows (lane l: row l / 4, LDS chunk l % 4, which holds the
   // row's global chunk (l % 4) ^ swizzle, i.e. K elements [32 c, 32 c + 32) of the step)
-  const uint8_t* a_src;
-  {
+  // (E4M3: two instructions of 8 rows each, lane l: row l / 8, LDS chunk l % 8 holding the row's
+  // global chunk (l % 8) ^ swizzle)
+  const uint8_t* a_src[A8 ? 2 : 1];
+  if (A8) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r = 16 * wave + 8 * t + (lane >> 3);
+      a_src[t] = p.Aq + (size_t)sRow[r] * KBA + 16 * ((lane & 7) ^ mx8_swz(r));
+    }
+  } else {
     const int r = 16 * wave + (lane >> 2);
-    a_src = p.Aq + (size_t)sRow[r] * KB + 16 * ((lane & 3) ^ mx_swz(r));
+    a_src[0] = p.Aq + (size_t)sRow[r] * KB + 16 * ((lane & 3) ^ mx_swz(r));
   }
   const uint8_t* b_src[2];
 #pragma unroll
@@ -621,14 +637,19 @@ __global__ __launch_bounds__(512) void gemm_mx_mm(MxGemmArgs p) {
   }
 
   auto issue = [&](int ks, int stage) {
-    uint8_t* st = smem + stage * kMxMmStage;
-    g2lds16(a_src + (size_t)ks * 64, st + wave * 1024);
+    uint8_t* st = smem + stage * STAGE;
+    if (A8) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) g2lds16(a_src[t] + (size_t)ks * 128, st + wave * 2048 + t * 1024);
+    } else {
+      g2lds16(a_src[0] + (size_t)ks * 64, st + wave * 1024);
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
-      g2lds16(b_src[t] + (size_t)ks * (WPK ? 1024 : 64), st + kMxMmA + (2 * wave + t) * 1024);
-    if (wave < 2) g2lds4_mx(s_src + (size_t)ks * 4, st + kMxMmA + kMxMmB + wave * 256);
+      g2lds16(b_src[t] + (size_t)ks * (WPK ? 1024 : 64), st + ABYTES + (2 * wave + t) * 1024);
+    if (wave < 2) g2lds4_mx(s_src + (size_t)ks * 4, st + ABYTES + kMxMmB + wave * 256);
     else if (wave < 6)
-      g2lds4_mx(s_src + (size_t)ks * (WPK ? 64 : 4), st + kMxMmA + kMxMmB + kMxMmBM * 4 + (wave - 2) * 256);
+      g2lds4_mx(s_src + (size_t)ks * (WPK ? 64 : 4), st + ABYTES + kMxMmB + kMxMmBM * 4 + (wave - 2) * 256);
   };
 
   int ntile[NI];
@@ -648,33 +669,42 @@ __global__ __launch_bounds__(512) void gemm_mx_mm(MxGemmArgs p) {
     return i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
   };
 
+  // E4M3 fragment of LDS row `row`: K bytes [16q, +16) and [64 + 16q, +16) of the step
+  auto frag8 = [&](const uint8_t* base, int row) -> i32x8 {
+    const int sw = mx8_swz(row);
+    const u32x4 v0 = *reinterpret_cast<const u32x4*>(base + row * 128 + 16 * (q ^ sw));
+    const u32x4 v1 = *reinterpret_cast<const u32x4*>(base + row * 128 + 16 * ((4 + q) ^ sw));
+    return i32x8{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3], (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
+  };
+
   auto compute = [&](int stage) {
-    const uint8_t* st = smem + stage * kMxMmStage;
-    const uint8_t* sa = st + kMxMmA + kMxMmB;
+    const uint8_t* st = smem + stage * STAGE;
+    const uint8_t* sa = st + ABYTES + kMxMmB;
     const uint8_t* sb = sa + kMxMmBM * 4;
     i32x8 bf[NI];
     int bs[NI];
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       const int nt = ntile[ni];
-      bf[ni] = frag(st + kMxMmA, nt);
+      bf[ni] = frag(st + ABYTES, nt);
       bs[ni] = WPK ? sb[(nt >> 4) * 64 + 16 * q + (nt & 15)] : sb[nt * 4 + q];
     }
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       const int r = wm * 64 + mi * 16 + l16;
-      const i32x8 af = frag(st, r);
+      const i32x8 af = A8 ? frag8(st, r) : frag(st, r);
       const int as = sa[r * 4 + q];
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[ni], acc[mi][ni], 4, 4, 0, as, 0, bs[ni]);
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[ni], acc[mi][ni], AF, 4, 0, as, 0, bs[ni]);
     }
   };
 
-  // Per-step direct loads of each wave: 4 (waves 0..5) or 3 (waves 6, 7).  Step s lives in stage
-  // s % NSTAGE; before reading it a wave waits until only the loads of the steps after s that it has
-  // already issued are outstanding, then the barrier publishes everyone's.
-  const int per_step = wave < 6 ? 4 : 3;
+  // Per-step direct loads of each wave: 4 (waves 0..5) or 3 (waves 6, 7), one more with E4M3
+  // activations.  Step s lives in stage s % NSTAGE; before reading it a wave waits until only the
+  // loads of the steps after s that it has already issued are outstanding, then the barrier publishes
+  // everyone's.
+  const int per_step = (wave < 6 ? 4 : 3) + (A8 ? 1 : 0);
 #pragma unroll
   for (int u = 0; u < NSTAGE - 1; ++u)
     if (u < nks) issue(u, u);
@@ -712,10 +742,20 @@ __global__ __launch_bounds__(512) void gemm_mx_mm(MxGemmArgs p) {
         v[4 * d + 3] = f.w;
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
       }
-      const int ex = mx_block_exp(amax);
       const size_t orow = (size_t)(row0 + row);
-      *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(p.C) + orow * (N / 4) + hcol / 2) = mx_encode32(v, ex);
-      p.Cs[orow * (N / 64) + hcol / 32] = (uint8_t)(ex + 127);
+      if (A8) {  // MXFP8 h, row-major
+        const int ex = mx8_block_exp(amax);
+        u32x4 c0, c1;
+        mx8_encode32(v, ex, c0, c1);
+        uint8_t* dst = static_cast<uint8_t*>(p.C) + orow * (N / 2) + hcol;
+        *reinterpret_cast<u32x4*>(dst) = c0;
+        *reinterpret_cast<u32x4*>(dst + 16) = c1;
+        p.Cs[orow * (N / 64) + hcol / 32] = (uint8_t)(ex + 127);
+      } else {
+        const int ex = mx_block_exp(amax);
+        *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(p.C) + orow * (N / 4) + hcol / 2) = mx_encode32(v, ex);
+        p.Cs[orow * (N / 64) + hcol / 32] = (uint8_t)(ex + 127);
+      }
     }
   } else {
 #pragma unroll
@@ -736,15 +776,15 @@ __global__ __launch_bounds__(512) void gemm_mx_mm(MxGemmArgs p) {
   }
 }
 
-template <int MODE>
+template <int MODE, int AF = 4>
 static hipError_t launch_mx_mm(const MxGemmArgs& a, hipStream_t s) {
   const int ncols = a.epilogue == MOE_EPI_SILU_MUL ? a.N / 2 : a.N;
   const int bcols = a.epilogue == MOE_EPI_SILU_MUL ? kMxMmBN / 2 : kMxMmBN;
   const int nbn = (ncols + bcols - 1) / bcols;
   const dim3 grid = mm_grid(nbn, a.max_tiles);
-  if (a.epilogue == MOE_EPI_SILU_MUL) gemm_mx_mm<MOE_EPI_SILU_MUL, false, MODE, 3><<<grid, 512, 0, s>>>(a);
-  else if (a.out_f32) gemm_mx_mm<MOE_EPI_NONE, true, MODE, 3><<<grid, 512, 0, s>>>(a);
-  else gemm_mx_mm<MOE_EPI_NONE, false, MODE, 3><<<grid, 512, 0, s>>>(a);
+  if (a.epilogue == MOE_EPI_SILU_MUL) gemm_mx_mm<MOE_EPI_SILU_MUL, false, MODE, 3, AF><<<grid, 512, 0, s>>>(a);
+  else if (a.out_f32) gemm_mx_mm<MOE_EPI_NONE, true, MODE, 3, AF><<<grid, 512, 0, s>>>(a);
+  else gemm_mx_mm<MOE_EPI_NONE, false, MODE, 3, AF><<<grid, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -779,8 +819,10 @@ constexpr int kMxSplitKMaxTiles = 32;
 
 hipError_t launch_grouped_gemm_mx(const MxGemmArgs& a, int block_m, hipStream_t stream) {
   if (a.max_tiles <= 0) return hipSuccess;
-  // (W4A8 runs the register kernel only; the caller never passes 128-row tiles with it)
-  if (block_m == 128) return a.mode == 1 ? launch_mx_mm<1>(a, stream) : launch_mx_mm<0>(a, stream);
+  if (block_m == 128) {
+    if (a.act_e4m3) return a.mode == 1 ? launch_mx_mm<1, 0>(a, stream) : launch_mx_mm<0, 0>(a, stream);
+    return a.mode == 1 ? launch_mx_mm<1>(a, stream) : launch_mx_mm<0>(a, stream);
+  }
   // Configurations from sweeps on MI355X (HIP events, weights streamed from HBM, packed weights and
   // tile-blocked activations), 128 experts top-8: gate_up at 1 / 8 / 64 tokens takes 7.7 / 18.8 /
   // 38.9 us as <16,64,KW2> against 10.3 / 21.3 / 39.7 us before; down at 8 tokens 10.3 us with a

@@ -330,7 +330,10 @@ def test_w4a8_entry_points_reject(lib):
                                                kw.get("K", 256), f, kw.get("mt", 8), f, kw.get("bm", 16),
                                                kw.get("epi", 0), kw.get("C", f), kw.get("cs", f), kw.get("od", 1), None)
     assert g(K=48) == -2
-    assert g(bm=128) == -2                                          # register kernel only
+    assert g(bm=256) == -2
+    assert g(bm=128, K=160) == -2                                   # the 128-row kernel steps K by 128
+    assert lib.moe_grouped_gemm_w4a8(f, _ptr(FAKE + 1), None, 1, f, f, 0, 4, 256, 256, f, 8, f, 128, 0, f, None, 1,
+                                     None) == -3                    # the 128-row kernel loads scales 4 bytes wide
     assert g(epi=1, N=96) == -2                                     # h blocks of 32 columns
     assert g(epi=5) == -1
     assert g(od=7) == -1
@@ -339,9 +342,10 @@ def test_w4a8_entry_points_reject(lib):
     assert g(C=_ptr(FAKE + 4)) == -3
     assert g(mt=0, C=None) == 0                                     # no tiles: nothing to launch
     # layer
-    assert moe.moe_ffn_w4a8_block_m(800, 256, 8) == 32
-    assert moe.moe_ffn_w4a8_block_m(4096, 8, 2) == 64              # never the 128-row tiles
-    assert moe.moe_ffn_w4a8_block_m(4, 8, 9) == -1
+    assert moe.moe_ffn_w4a8_block_m(800, 2048, 512, 256, 8) == 32
+    assert moe.moe_ffn_w4a8_block_m(4096, 4096, 14336, 8, 2) == 128  # large experts: the LDS-staged kernel
+    assert moe.moe_ffn_w4a8_block_m(4096, 4096, 14336 - 32, 8, 2) == 64  # ... which steps K by 128
+    assert moe.moe_ffn_w4a8_block_m(4, 256, 128, 8, 9) == -1
     T, H, I, E, k = 16, 256, 128, 8, 2
     ws = moe.moe_ffn_w4a8_workspace_bytes(T, H, I, E, k)
     R = T * k

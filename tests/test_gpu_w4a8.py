@@ -190,15 +190,74 @@ def test_grouped_gemm_w4a8_plain(T, E, k, bm, N, K, narrow):
     assert np.all(err <= bound)
 
 
+# the 128-row LDS-staged kernel (K % 128 == 0)
+MM_CASES = [(600, 4, 2, 128), (700, 6, 3, 128)]
+
+
+@pytest.mark.parametrize("T,E,k,bm", MM_CASES)
+@pytest.mark.parametrize("N,K", [(512, 2048), (200, 384)])
+@pytest.mark.parametrize("narrow", [True, False])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_grouped_gemm_w4a8_large_tile(T, E, k, bm, N, K, narrow, layout):
+    ids, al = _routing(T, E, k, bm, seed=T * 3 + N)
+    R = T * k
+    Aq, As, Wq, We = _operands(R, N, K, E, seed=K + narrow, narrow=narrow)
+    tiles = gu.dev(np.ascontiguousarray(al["tiles"].astype(np.int32)))
+    nt = gu.dev(np.array([al["num_tiles"]], np.int32))
+    dWq, dWe = gu.dev(Wq), gu.dev(We)
+    if layout == moe.MOE_LAYOUT_PACKED:
+        if N % 16:
+            pytest.skip("packed weights need N % 16 == 0")
+        dWq, dWe = moe.moe_mx_prepack(dWq, dWe)
+    C = moe.moe_grouped_gemm_w4a8(gu.dev(Aq), gu.dev(As), None, 1, dWq, dWe, tiles, al["num_tiles"], nt, bm,
+                                  moe.MOE_EPI_NONE, R, weight_layout=layout)
+    torch.cuda.synchronize()
+    got = C.cpu().numpy().astype(np.float64)
+    ref = oracle.grouped_proj_w4a8(Aq, As, None, 1, Wq, We, al["offsets"])
+    tsum, smax = _bounds(Aq, As, np.arange(R), Wq, We, _row_experts(al, R), K)
+    bound = (64 + K / 32) * 2.0 ** -24 * tsum + 1e-30
+    if not narrow:
+        bound = bound + 2.0 ** -5 * smax
+    err = np.abs(got - ref)
+    _log(f"  max err / bound {np.max(err / bound):.3f}")
+    assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("epi", [0, 1])
+def test_grouped_gemm_w4a8_large_tile_matches_register_kernel_bits(epi):
+    # the same rows in 128-row tiles (LDS-staged kernel) and in 64-row tiles (register kernel): each
+    # output is the same instruction sequence, so the bits agree
+    T, E, k, N, K = 700, 6, 3, 512, 1024
+    rng = np.random.default_rng(41)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    a128, a64 = oracle.align(ids, E, 128), oracle.align(ids, E, 64)
+    np.testing.assert_array_equal(a128["sorted_ids"], a64["sorted_ids"])
+    R = T * k
+    Aq, As, Wq, We = _operands(T, N, K, E, seed=42)
+    out = []
+    for al, bm in ((a128, 128), (a64, 64)):
+        tiles = gu.dev(np.ascontiguousarray(al["tiles"].astype(np.int32)))
+        nt = gu.dev(np.array([al["num_tiles"]], np.int32))
+        srt = gu.dev(al["sorted_ids"].astype(np.int32))
+        r = moe.moe_grouped_gemm_w4a8(gu.dev(Aq), gu.dev(As), srt, k, gu.dev(Wq), gu.dev(We), tiles, al["num_tiles"],
+                                      nt, bm, epi, R)
+        torch.cuda.synchronize()
+        out.append([t.cpu().numpy() for t in r] if epi else [r.cpu().numpy()])
+    for a, b in zip(*out):
+        np.testing.assert_array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
 def _e4m3_step(mag):
     """Spacing of the E4M3 grid at quotient magnitude mag (subnormal spacing 2^-9 below 2^-6)."""
     mag = np.maximum(mag, 2.0 ** -6)
     return np.exp2(np.floor(np.log2(mag)) - 3)
 
 
-@pytest.mark.parametrize("T,E,k,bm", GEMM_CASES)
+@pytest.mark.parametrize("T,E,k,bm", GEMM_CASES + MM_CASES[:1])
 @pytest.mark.parametrize("I,K", [(128, 2048), (96, 160)])
 def test_grouped_gemm_w4a8_silu_quantized_h(T, E, k, bm, I, K):
+    if bm == 128 and K % 128:
+        pytest.skip("the 128-row kernel steps K by 128")
     ids, al = _routing(T, E, k, bm, seed=T + I + 1)
     R = T * k
     Aq, As, Wq, We = _operands(T, 2 * I, K, E, seed=I + bm + 1)
