@@ -443,10 +443,13 @@ def run_w4a8(args):
     bm = moe.moe_ffn_w4a8_block_m(T, H, I, E, k)
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    xq = torch.empty((T, H), dtype=torch.uint8, device="cuda")
-    xs = torch.empty((T, H // 32), dtype=torch.uint8, device="cuda")
-    hq = torch.empty((R, I), dtype=torch.uint8, device="cuda")
-    hs = torch.empty((R, I // 32), dtype=torch.uint8, device="cuda")
+    tiled = layout == moe.MOE_LAYOUT_PACKED and bm != 128  # the 128-row kernel reads row-major activations
+    act = moe.MOE_ACT_TILED if tiled else moe.MOE_ACT_ROWS
+    rows_cap = max(T, R, moe.moe_max_tiles(T, k, E, bm) * bm)
+    xq = torch.empty((rows_cap, H), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((rows_cap, H // 32), dtype=torch.uint8, device="cuda")
+    hq = torch.empty((rows_cap, I), dtype=torch.uint8, device="cuda")
+    hs = torch.empty((rows_cap, I // 32), dtype=torch.uint8, device="cuda")
     O = torch.empty((R, H), dtype=torch.float32, device="cuda")
     names = ["route", "align", "quant_x", "gate_up", "down", "combine"]
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
@@ -458,13 +461,18 @@ def run_w4a8(args):
         if e: e[1].record()
         al = moe.moe_align(ids, E, bm)
         if e: e[2].record()
-        moe.moe_mx8_quantize(x, xq, xs)
+        if tiled:
+            moe.moe_mx8_quantize_tiles(x, al["sorted_ids"], k, al["tiles"], al["max_tiles"], al["num_tiles"], bm, xq,
+                                       xs)
+        else:
+            moe.moe_mx8_quantize(x, xq[:T], xs[:T])
         if e: e[3].record()
         moe.moe_grouped_gemm_w4a8(xq, xs, al["sorted_ids"], k, q13, e13, al["tiles"], al["max_tiles"],
-                                  al["num_tiles"], bm, moe.MOE_EPI_SILU_MUL, R, C=hq, Cs=hs, weight_layout=layout)
+                                  al["num_tiles"], bm, moe.MOE_EPI_SILU_MUL, R, C=hq, Cs=hs, weight_layout=layout,
+                                  act_layout=act)
         if e: e[4].record()
         moe.moe_grouped_gemm_w4a8(hq, hs, None, 1, q2, e2, al["tiles"], al["max_tiles"], al["num_tiles"], bm,
-                                  moe.MOE_EPI_NONE, R, moe.MOE_OUT_F32, C=O, weight_layout=layout)
+                                  moe.MOE_EPI_NONE, R, moe.MOE_OUT_F32, C=O, weight_layout=layout, act_layout=act)
         if e: e[5].record()
         moe.moe_combine(O, al["inv_perm"], wts, y=y)
         if e: e[6].record()

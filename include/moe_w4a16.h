@@ -380,24 +380,38 @@ moe_status_t moe_ffn_forward_mxfp4(const uint16_t* x, const float* router_logits
 moe_status_t moe_mx8_quantize(const uint16_t* x, int32_t rows, int32_t K, uint8_t* q, uint8_t* s, void* stream);
 
 /*
- * Grouped W4A8 GEMM over the tile list of moe_align (as moe_grouped_gemm_mxfp4 with row-major
- * activations): for each permuted row r of expert e, activation row a = (a_row_of ? a_row_of[r] /
- * a_row_div : r):
+ * x quantized to MXFP8 (as moe_mx8_quantize) and gathered into the tile-blocked layout of a tile list
+ * (rows as for moe_mx_quantize_tiles): blocks of 16 rows x 128 K ordered (tile, 16-row group, K block),
+ * K fastest, each 2048 code bytes in the instruction's 8-bit lane order with the halves apart: bytes
+ * [16l, 16l+16) = row l % 16, K [16 (l / 16), +16) of the block; bytes [1024 + 16l, +16) = the same row,
+ * K [64 + 16 (l / 16), +16); and, separately, 64 scale bytes (byte l = row l % 16, 32-block l / 16).
+ * Padding rows and tiles past *num_tiles are left unwritten.  q: max_tiles * block_m * K bytes, s:
+ * max_tiles * block_m * K/32 bytes.  Needs K % 128 == 0, block_m 16, 32 or 64.
+ */
+moe_status_t moe_mx8_quantize_tiles(const uint16_t* x, int32_t T, int32_t K, const int32_t* a_row_of,
+                                   int32_t a_row_div, const int32_t* tiles, int32_t max_tiles, const int32_t* num_tiles,
+                                   int32_t block_m, uint8_t* q, uint8_t* s, void* stream);
+
+/*
+ * Grouped W4A8 GEMM over the tile list of moe_align (as moe_grouped_gemm_mxfp4): for each permuted
+ * row r of expert e, activation row a = (a_row_of ? a_row_of[r] / a_row_div : r):
  *   G[r, n] = sum_k A[a, k] * W_e[n, k],  A = (Aq [*, K] E4M3 codes, As [*, K/32]), W = (Wq [E, N, K/2], We [E, N, K/32]).
  *   epilogue NONE:     C [rows, N] fp32 or bf16 (out_dtype); Cs unused.
  *   epilogue SILU_MUL: h[r, j] = silu(G[r, j]) * G[r, N/2 + j] in fp32, then quantized to MXFP8 per 32
  *                      columns: C = codes [rows, N/2], Cs = scale bytes [rows, N/64] (out_dtype ignored).
  * weight_layout: MOE_LAYOUT_CANONICAL or MOE_LAYOUT_PACKED (moe_mx_prepack; needs N % 16 == 0 and
- * K % 128 == 0); results are bit-identical across layouts.  block_m 16, 32, 64 or 128 (the tile height
- * moe_align used); 128 runs a 128 x 256 LDS-staged kernel (bit-identical to the others) that needs
- * K % 128 == 0 and 4-byte aligned As and We.  K % 32 == 0; SILU_MUL needs N % 64 == 0.  Aq, Wq and C
- * 16-byte aligned.
+ * K % 128 == 0).  act_layout: MOE_ACT_ROWS, or MOE_ACT_TILED (packed weights and block_m <= 64; A from
+ * moe_mx8_quantize_tiles or a previous SILU_MUL output, a_row_of unused; a SILU_MUL output is then
+ * written tile-blocked too, which needs N/2 % 128 == 0).  Results are bit-identical across layouts.
+ * block_m 16, 32, 64 or 128 (the tile height moe_align used); 128 runs a 128 x 256 LDS-staged kernel
+ * (bit-identical to the others) that needs K % 128 == 0, MOE_ACT_ROWS and 4-byte aligned As and We.
+ * K % 32 == 0; SILU_MUL needs N % 64 == 0.  Aq, Wq and C 16-byte aligned.
  */
 moe_status_t moe_grouped_gemm_w4a8(const uint8_t* Aq, const uint8_t* As, const int32_t* a_row_of, int32_t a_row_div,
-                                   const uint8_t* Wq, const uint8_t* We, int32_t weight_layout, int32_t E, int32_t N,
-                                   int32_t K, const int32_t* tiles, int32_t max_tiles, const int32_t* num_tiles,
-                                   int32_t block_m, int32_t epilogue, void* C, uint8_t* Cs, int32_t out_dtype,
-                                   void* stream);
+                                   const uint8_t* Wq, const uint8_t* We, int32_t weight_layout, int32_t act_layout,
+                                   int32_t E, int32_t N, int32_t K, const int32_t* tiles, int32_t max_tiles,
+                                   const int32_t* num_tiles, int32_t block_m, int32_t epilogue, void* C, uint8_t* Cs,
+                                   int32_t out_dtype, void* stream);
 
 /* Row-tile height and workspace bytes of moe_ffn_forward_w4a8 (host-only, pure; -1 / 0 on invalid sizes):
  * the MXFP4 layer's choice (128 for experts averaging more than 128 rows with H, I multiples of 128). */
@@ -410,8 +424,9 @@ size_t moe_ffn_w4a8_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, 
  *   y[t] = sum_s w[t,s] * W2_e(s) Q8( silu(W1_e(s) Q8(x[t])) * (W3_e(s) Q8(x[t])) ),  Q8 = MXFP8 quantization.
  *   Arguments as moe_ffn_forward_mxfp4 (the same MXFP4 weights in either layout; packed needs
  *   H % 128 == 0 and I % 128 == 0, results bit-identical to the canonical layout); y bf16 [T, H].
- *   With experts of more than 128 rows on average (and H, I multiples of 128) the 128-row kernel
- *   runs and the scale arrays need 4-byte alignment.
+ *   With packed weights the quantized activations are kept tile-blocked internally.  With experts of
+ *   more than 128 rows on average (and H, I multiples of 128) the 128-row kernel runs, on row-major
+ *   activations, and the scale arrays need 4-byte alignment.
  *   workspace: at least moe_ffn_w4a8_workspace_bytes(T, H, I, E, k) bytes.
  * Shapes: as moe_ffn_forward (H, I positive multiples of 32).
  */

@@ -75,7 +75,9 @@ def load() -> ctypes.CDLL:
         "moe_ffn_mxfp4_workspace_bytes": ([I32, I32, I32, I32, I32], SZ),
         "moe_ffn_forward_mxfp4": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, SZ, P], I32),
         "moe_mx8_quantize": ([P, I32, I32, P, P, P], I32),
-        "moe_grouped_gemm_w4a8": ([P, P, P, I32, P, P, I32, I32, I32, I32, P, I32, P, I32, I32, P, P, I32, P], I32),
+        "moe_mx8_quantize_tiles": ([P, I32, I32, P, I32, P, I32, P, I32, P, P, P], I32),
+        "moe_grouped_gemm_w4a8": ([P, P, P, I32, P, P, I32, I32, I32, I32, I32, P, I32, P, I32, I32, P, P, I32, P],
+                                  I32),
         "moe_ffn_w4a8_block_m": ([I32, I32, I32, I32, I32], I32),
         "moe_ffn_w4a8_workspace_bytes": ([I32, I32, I32, I32, I32], SZ),
         "moe_ffn_forward_w4a8": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, SZ, P], I32),
@@ -105,7 +107,8 @@ EXPORTED = ("moe_abi_version", "moe_status_string", "moe_last_error", "moe_route
             "moe_ffn_block_forward", "moe_mx_quantize", "moe_mx_quantize_tiles", "moe_mx_prepack", "moe_grouped_gemm_mxfp4", "moe_ffn_mxfp4_block_m",
             "moe_ffn_mxfp4_workspace_bytes", "moe_ffn_forward_mxfp4", "moe_f8_quantize", "moe_grouped_gemm_f8",
             "moe_ffn_f8_block_m", "moe_ffn_f8_workspace_bytes", "moe_ffn_forward_f8", "moe_mx8_quantize",
-            "moe_grouped_gemm_w4a8", "moe_ffn_w4a8_block_m", "moe_ffn_w4a8_workspace_bytes", "moe_ffn_forward_w4a8")
+            "moe_mx8_quantize_tiles", "moe_grouped_gemm_w4a8", "moe_ffn_w4a8_block_m", "moe_ffn_w4a8_workspace_bytes",
+            "moe_ffn_forward_w4a8")
 
 
 def _check(status: int):
@@ -433,16 +436,35 @@ def moe_mx8_quantize(x, q=None, s=None, stream=None):
     return q, s
 
 
+def moe_mx8_quantize_tiles(x, a_row_of, a_row_div: int, tiles, max_tiles: int, num_tiles, block_m: int, q=None,
+                           s=None, stream=None):
+    """x bf16 [T, K] -> tile-blocked MXFP8 codes [max_tiles * block_m, K] and scale bytes [.., K/32]."""
+    _req(x, "16bit", "x")
+    T, K = x.shape
+    rows = max(max_tiles, 1) * block_m
+    if q is None:
+        q = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+    _check(load().moe_mx8_quantize_tiles(_p(x), T, K, _p(a_row_of), a_row_div, _p(tiles), max_tiles, _p(num_tiles),
+                                         block_m, _p(q), _p(s), _stream(stream)))
+    return q, s
+
+
 def moe_grouped_gemm_w4a8(Aq, As, a_row_of, a_row_div: int, Wq, We, tiles, max_tiles: int, num_tiles,
                           block_m: int, epilogue: int, out_rows: int, out_dtype: int = MOE_OUT_F32, C=None,
-                          Cs=None, stream=None, weight_layout: int = MOE_LAYOUT_CANONICAL):
-    """Grouped W4A8 GEMM over the tile list (MXFP8 activations, row-major).  NONE: returns C
-    [out_rows, N]; SILU_MUL: returns the MXFP8 h as (codes [out_rows, N/2], scale bytes [out_rows, N/64])."""
+                          Cs=None, stream=None, weight_layout: int = MOE_LAYOUT_CANONICAL,
+                          act_layout: int = MOE_ACT_ROWS):
+    """Grouped W4A8 GEMM over the tile list (MXFP8 activations).  NONE: returns C [out_rows, N];
+    SILU_MUL: returns the MXFP8 h as (codes [out_rows, N/2], scale bytes [out_rows, N/64]); with
+    act_layout TILED the h buffers hold max_tiles * block_m rows (tile-blocked)."""
     _req(Aq, torch.uint8, "Aq")
     _req(Wq, torch.uint8, "Wq")
     E, N, K2 = Wq.shape
     K = 2 * K2
     dev = Aq.device
+    if act_layout == MOE_ACT_TILED and epilogue == MOE_EPI_SILU_MUL:
+        out_rows = max(out_rows, max(max_tiles, 1) * block_m)  # h is written tile-blocked
     if epilogue == MOE_EPI_SILU_MUL:
         if C is None:
             C = torch.empty((out_rows, N // 2), dtype=torch.uint8, device=dev)
@@ -451,8 +473,8 @@ def moe_grouped_gemm_w4a8(Aq, As, a_row_of, a_row_div: int, Wq, We, tiles, max_t
     elif C is None:
         C = torch.empty((out_rows, N), dtype=torch.float32 if out_dtype == MOE_OUT_F32 else torch.bfloat16, device=dev)
     _check(load().moe_grouped_gemm_w4a8(_p(Aq), _p(As), _p(a_row_of), a_row_div, _p(Wq), _p(We), weight_layout,
-                                        E, N, K, _p(tiles), max_tiles, _p(num_tiles), block_m, epilogue, _p(C),
-                                        _p(Cs), out_dtype, _stream(stream)))
+                                        act_layout, E, N, K, _p(tiles), max_tiles, _p(num_tiles), block_m, epilogue,
+                                        _p(C), _p(Cs), out_dtype, _stream(stream)))
     return (C, Cs) if epilogue == MOE_EPI_SILU_MUL else C
 
 

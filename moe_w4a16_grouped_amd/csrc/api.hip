@@ -746,12 +746,15 @@ W4a8Layout w4a8_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   const int64_t R = T * k;
   M.L.block_m = pick_mx_block_m(R, E, H, I);
   M.L.max_tiles = (int32_t)max_tiles_of(R, E, M.L.block_m);
+  // row-major rows or the tile-blocked rows of the tile list, whichever is larger
+  const int64_t tiled_rows = (int64_t)M.L.max_tiles * M.L.block_m;
+  const int64_t xr = std::max(T, tiled_rows), hr = std::max(R, tiled_rows);
   size_t off = M.L.h;
   auto take = [&](size_t bytes) { size_t at = off; off += up256(bytes); return at; };
-  M.xq = take((size_t)T * H);
-  M.xs = take((size_t)T * H / 32);
-  M.hq = take((size_t)R * I);
-  M.hs = take((size_t)R * I / 32);
+  M.xq = take((size_t)xr * H);
+  M.xs = take((size_t)xr * H / 32);
+  M.hq = take((size_t)hr * I);
+  M.hs = take((size_t)hr * I / 32);
   M.o = take((size_t)R * H * 4);
   M.total = off;
   return M;
@@ -769,11 +772,30 @@ moe_status_t moe_mx8_quantize(const uint16_t* x, int32_t rows, int32_t K, uint8_
   return hip_status(moe::launch_mx8_quant(x, rows, K, q, s, (hipStream_t)stream), "moe_mx8_quantize launch");
 }
 
+moe_status_t moe_mx8_quantize_tiles(const uint16_t* x, int32_t T, int32_t K, const int32_t* a_row_of,
+                                   int32_t a_row_div, const int32_t* tiles, int32_t max_tiles, const int32_t* num_tiles,
+                                   int32_t block_m, uint8_t* q, uint8_t* s, void* stream) {
+  if (T < 0 || K < 128 || K % 128 != 0 || max_tiles < 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_mx8_quantize_tiles: need T >= 0, K a positive multiple of 128, max_tiles >= 0");
+  if (block_m != 16 && block_m != 32 && block_m != 64)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_mx8_quantize_tiles: block_m=%d must be 16, 32 or 64", block_m);
+  if (a_row_of && a_row_div < 1) return fail(MOE_ERR_INVALID_ARG, "a_row_div must be >= 1");
+  if ((int64_t)max_tiles * block_m >= kMaxRows + (int64_t)MOE_MAX_EXPERTS * block_m)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "max_tiles=%d too large", max_tiles);
+  if (T == 0 || max_tiles == 0) return ok();
+  if (!x || !tiles || !num_tiles || !q || !s) return fail(MOE_ERR_INVALID_ARG, "moe_mx8_quantize_tiles: NULL pointer");
+  if (!aligned16(x) || !aligned16(q) || !aligned4(tiles) || !aligned4(num_tiles) || (a_row_of && !aligned4(a_row_of)))
+    return fail(MOE_ERR_MISALIGNED, "moe_mx8_quantize_tiles: x and q need 16-byte alignment");
+  return hip_status(moe::launch_mx8_quant_tiles(x, K, a_row_of, a_row_div, tiles, num_tiles, max_tiles, block_m, q, s,
+                                                (hipStream_t)stream),
+                    "moe_mx8_quantize_tiles launch");
+}
+
 moe_status_t moe_grouped_gemm_w4a8(const uint8_t* Aq, const uint8_t* As, const int32_t* a_row_of, int32_t a_row_div,
-                                   const uint8_t* Wq, const uint8_t* We, int32_t weight_layout, int32_t E, int32_t N,
-                                   int32_t K, const int32_t* tiles, int32_t max_tiles, const int32_t* num_tiles,
-                                   int32_t block_m, int32_t epilogue, void* C, uint8_t* Cs, int32_t out_dtype,
-                                   void* stream) {
+                                   const uint8_t* Wq, const uint8_t* We, int32_t weight_layout, int32_t act_layout,
+                                   int32_t E, int32_t N, int32_t K, const int32_t* tiles, int32_t max_tiles,
+                                   const int32_t* num_tiles, int32_t block_m, int32_t epilogue, void* C, uint8_t* Cs,
+                                   int32_t out_dtype, void* stream) {
   if (E < 1 || N < 1 || K < 1 || max_tiles < 0)
     return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_w4a8: need E, N, K >= 1, max_tiles >= 0");
   if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E=%d exceeds %d", E, MOE_MAX_EXPERTS);
@@ -791,6 +813,12 @@ moe_status_t moe_grouped_gemm_w4a8(const uint8_t* Aq, const uint8_t* As, const i
     return fail(MOE_ERR_INVALID_ARG, "unknown weight_layout %d", weight_layout);
   if (weight_layout == MOE_LAYOUT_PACKED && (N % 16 != 0 || K % 128 != 0))
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "packed MXFP4 weights need N %% 16 == 0 and K %% 128 == 0 (N=%d K=%d)", N, K);
+  if (act_layout != MOE_ACT_ROWS && act_layout != MOE_ACT_TILED)
+    return fail(MOE_ERR_INVALID_ARG, "unknown act_layout %d", act_layout);
+  if (act_layout == MOE_ACT_TILED && (weight_layout != MOE_LAYOUT_PACKED || block_m == 128))
+    return fail(MOE_ERR_INVALID_ARG, "tile-blocked activations need packed weights and tiles of at most 64 rows");
+  if (act_layout == MOE_ACT_TILED && epilogue == MOE_EPI_SILU_MUL && (N / 2) % 128 != 0)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "a tile-blocked h needs N/2 %% 128 == 0 (N=%d)", N);
   if (max_tiles == 0) return ok();
   if (!Aq || !As || !Wq || !We || !tiles || !num_tiles || !C || (epilogue == MOE_EPI_SILU_MUL && !Cs))
     return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_w4a8: NULL pointer");
@@ -802,7 +830,8 @@ moe_status_t moe_grouped_gemm_w4a8(const uint8_t* Aq, const uint8_t* As, const i
   if ((int64_t)max_tiles * block_m >= kMaxRows + (int64_t)MOE_MAX_EXPERTS * block_m)
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "max_tiles=%d too large", max_tiles);
   moe::MxGemmArgs a{Aq, As, a_row_of, a_row_div, Wq, We, N, K, tiles, num_tiles, max_tiles, C, Cs, epilogue,
-                    out_dtype == MOE_OUT_F32, weight_layout == MOE_LAYOUT_PACKED ? 1 : 0, 1};
+                    out_dtype == MOE_OUT_F32,
+                    act_layout == MOE_ACT_TILED ? 2 : (weight_layout == MOE_LAYOUT_PACKED ? 1 : 0), 1};
   return hip_status(moe::launch_grouped_gemm_mx(a, block_m, (hipStream_t)stream), "moe_grouped_gemm_w4a8 launch");
 }
 
@@ -870,9 +899,13 @@ moe_status_t moe_ffn_forward_w4a8(const uint16_t* x, const float* router_logits,
   }
   if (L.block_m == 128 && (!aligned4(w13_e) || !aligned4(w2_e)))
     return fail(MOE_ERR_MISALIGNED, "moe_ffn_forward_w4a8: scale arrays need 4-byte alignment");
-  e = moe::launch_mx8_quant(x, T, H, xq, xs, s);
+  // packed weights: x gathered into the tile-blocked layout, h written in it by the gate_up epilogue
+  // (the 128-row kernel reads row-major activations with either weight layout)
+  const int packed = weight_layout == MOE_LAYOUT_PACKED;
+  const int mode = L.block_m == 128 ? packed : (packed ? 2 : 0);
+  if (mode == 2) e = moe::launch_mx8_quant_tiles(x, H, sorted, k, tiles, ntiles, L.max_tiles, L.block_m, xq, xs, s);
+  else e = moe::launch_mx8_quant(x, T, H, xq, xs, s);
   if (e != hipSuccess) return hip_status(e, "x quantization launch");
-  const int mode = weight_layout == MOE_LAYOUT_PACKED ? 1 : 0;
   moe::MxGemmArgs g1{xq, xs, sorted, k, w13_q, w13_e, 2 * I, H, tiles, ntiles, L.max_tiles, hq, hs,
                      MOE_EPI_SILU_MUL, 0, mode, 1};
   e = moe::launch_grouped_gemm_mx(g1, L.block_m, s);

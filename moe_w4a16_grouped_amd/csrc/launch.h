@@ -104,15 +104,20 @@ struct MxGemmArgs {
   // 2: tile-blocked activations (mx_tiled_* below), packed weights; a SILU_MUL output (h) is
   //    written tile-blocked for the next projection, a NONE output row-major.  Needs K % 128 == 0.
   int mode;
-  // W4A8 (nonzero): activations are MXFP8 (E4M3 codes [*, K], one byte per element, scale bytes
-  // [*, K/32]), row-major (mode 0 or 1), tiles of at most 64 rows; a SILU_MUL output is MXFP8 h
-  // (codes [rows, N/2], scale bytes [rows, N/64]).
+  // W4A8 (nonzero): activations are MXFP8 (E4M3 codes, one byte per element, and scale bytes):
+  // row-major [*, K] and [*, K/32] (mode 0 or 1, or 128-row tiles) or tile-blocked (mode 2, blocks of
+  // 2048 code bytes and 64 scale bytes, see mx8_quant_tiles_kernel); a SILU_MUL output is MXFP8 h in the
+  // same arrangement (row-major codes [rows, N/2], scale bytes [rows, N/64]).
   int act_e4m3;
 };
 hipError_t launch_grouped_gemm_mx(const MxGemmArgs& a, int block_m, hipStream_t stream);
 hipError_t launch_mx_quant(const uint16_t* x, long long rows, int K, uint8_t* q, uint8_t* s, hipStream_t stream);
 // bf16 x [rows, K] -> MXFP8 codes [rows, K] and scale bytes [rows, K/32].
 hipError_t launch_mx8_quant(const uint16_t* x, long long rows, int K, uint8_t* q, uint8_t* s, hipStream_t stream);
+// x rows quantized to MXFP8 and gathered into the tile-blocked layout of a tile list (block height bm).
+hipError_t launch_mx8_quant_tiles(const uint16_t* x, int K, const int32_t* a_row_of, int a_row_div,
+                                  const int32_t* tiles, const int32_t* num_tiles, int max_tiles, int bm, uint8_t* q,
+                                  uint8_t* s, hipStream_t stream);
 // x rows quantized and gathered into the tile-blocked layout of a tile list (block height bm).
 hipError_t launch_mx_quant_tiles(const uint16_t* x, int K, const int32_t* a_row_of, int a_row_div,
                                  const int32_t* tiles, const int32_t* num_tiles, int max_tiles, int bm, uint8_t* q,

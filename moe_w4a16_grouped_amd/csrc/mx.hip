@@ -214,6 +214,68 @@ hipError_t launch_mx_quant_tiles(const uint16_t* x, int K, const int32_t* a_row_
   return hipGetLastError();
 }
 
+// Tile-blocked MXFP8 activations (W4A8 with packed weights): blocks of 16 rows x 128 K ordered (tile,
+// 16-row group, K block) as above, each 2048 code bytes in the 8-bit lane layout, halves first: bytes
+// [16l, 16l+16) = lane l's first half (row l % 16, K [16 (l / 16), +16) of the step), bytes
+// [1024 + 16l, +16) = its second half (K [64 + 16 (l / 16), +16)); so each half is one contiguous 1 KB
+// wave load.  64 scale bytes per block as for MXFP4 (byte l: row l % 16, 32-block l / 16).
+// Byte position of the 16 codes at K offset o (a multiple of 16 within the step) of tile row i.
+__device__ __forceinline__ size_t mx8_tiled_pos(size_t blk, int o, int i) {
+  const int half = o >= 64, qq = (o - 64 * half) >> 4;
+  return blk * 2048 + half * 1024 + (size_t)(qq * 16 + (i & 15)) * 16;
+}
+
+// x rows of a tile list quantized to MXFP8 in the tile-blocked layout: one thread per (tile, row,
+// 32-K block); tiles past num_tiles and padding rows are not written.
+__global__ __launch_bounds__(256) void mx8_quant_tiles_kernel(const uint16_t* __restrict__ x, int K,
+                                                              const int32_t* __restrict__ a_row_of, int a_row_div,
+                                                              const int32_t* __restrict__ tiles,
+                                                              const int32_t* __restrict__ num_tiles, int bm,
+                                                              long long total, uint8_t* __restrict__ q,
+                                                              uint8_t* __restrict__ s) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int kb = K / 32;
+  const int b = (int)(idx % kb);
+  const long long rest = idx / kb;
+  const int i = (int)(rest % bm);
+  const int t = (int)(rest / bm);
+  if (t >= *num_tiles || i >= tiles[3 * t + 2]) return;
+  const int r = tiles[3 * t + 1] + i;
+  const int src = a_row_of ? a_row_of[r] / a_row_div : r;
+  const u32x4* in = reinterpret_cast<const u32x4*>(x + (size_t)src * K + 32 * b);
+  float v[32];
+  float amax = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const u32x4 w = in[d];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * d + 2 * j] = __uint_as_float(w[j] << 16);
+      v[8 * d + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      amax = fmaxf(amax, fmaxf(fabsf(v[8 * d + 2 * j]), fabsf(v[8 * d + 2 * j + 1])));
+    }
+  }
+  const int e = mx8_block_exp(amax);
+  u32x4 c0, c1;
+  mx8_encode32(v, e, c0, c1);
+  const size_t blk = mx_block((long long)t * (bm / 16) + (i >> 4), b >> 2, K / 128);
+  const int o = 32 * (b & 3);
+  *reinterpret_cast<u32x4*>(q + mx8_tiled_pos(blk, o, i)) = c0;
+  *reinterpret_cast<u32x4*>(q + mx8_tiled_pos(blk, o + 16, i)) = c1;
+  s[blk * 64 + (b & 3) * 16 + (i & 15)] = (uint8_t)(e + 127);
+}
+
+hipError_t launch_mx8_quant_tiles(const uint16_t* x, int K, const int32_t* a_row_of, int a_row_div,
+                                  const int32_t* tiles, const int32_t* num_tiles, int max_tiles, int bm, uint8_t* q,
+                                  uint8_t* s, hipStream_t stream) {
+  const long long total = (long long)max_tiles * bm * (K / 32);
+  if (total <= 0) return hipSuccess;
+  mx8_quant_tiles_kernel<<<dim3((unsigned)((total + 255) / 256)), 256, 0, stream>>>(x, K, a_row_of, a_row_div, tiles,
+                                                                                   num_tiles, bm, total, q, s);
+  return hipGetLastError();
+}
+
 // Canonical MXFP4 weights -> packed layout: one thread per 16-byte lane slot of a block.
 __global__ __launch_bounds__(256) void mx_prepack_kernel(const uint8_t* __restrict__ wq, const uint8_t* __restrict__ we,
                                                          int N, int K, long long total, uint8_t* __restrict__ pq,
@@ -253,14 +315,14 @@ hipError_t launch_mx_prepack(const uint8_t* wq, const uint8_t* we, int E, int N,
 // [0, N/2), up rows [N/2, N) of the weight), gathers the tile's h in LDS and quantizes each
 // 32-column block of each row to MXFP4 (codes [rows, N/4], scale bytes [rows, N/64]) for the next
 // projection.  AF = 0 (W4A8): MXFP8 activations (32 code bytes per lane and K step in the 8-bit operand
-// layout above, row-major only), the instruction's A format E4M3, and h quantized to MXFP8 (codes
-// [rows, N/2], scale bytes [rows, N/64]).
+// layout above; MODE 2: the tile-blocked MXFP8 layout, two contiguous 1 KB loads per wave), the
+// instruction's A format E4M3, and h quantized to MXFP8 (row-major: codes [rows, N/2], scale bytes
+// [rows, N/64]; MODE 2: tile-blocked).
 template <int BM, int BN, int KW, int PF, int EPI, bool OUT_F32, int MODE, int AF = 4>
 __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
   constexpr bool ATB = MODE == 2, WPK = MODE >= 1;  // tile-blocked activations, packed weights
   constexpr bool A8 = AF == 0;                       // E4M3 activations
   static_assert(AF == 0 || AF == 4, "activation format");
-  static_assert(!A8 || !ATB, "MXFP8 activations are row-major");
   constexpr int WNS = 4 / KW;             // waves along N
   constexpr int WN = BN / WNS;            // columns per wave
   constexpr int MI = BM / 16, NI = WN / 16;
@@ -295,7 +357,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
   for (int mi = 0; mi < MI; ++mi) {
     if (ATB) {
       const size_t blk = mx_block((long long)tile * MI + mi, 0, nks);
-      aq[mi] = p.Aq + blk * 1024 + lane * 16;
+      aq[mi] = p.Aq + blk * (A8 ? 2048 : 1024) + lane * 16;
       as[mi] = p.As + blk * 64 + lane;
     } else {
       const int i = mi * 16 + l16;
@@ -361,8 +423,8 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       if (A8) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(aq[mi] + o0);
-        const u32x4 a2 = *reinterpret_cast<const u32x4*>(aq[mi] + o1);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(aq[mi] + (ATB ? (size_t)s * 2048 : (size_t)o0));
+        const u32x4 a2 = *reinterpret_cast<const u32x4*>(aq[mi] + (ATB ? (size_t)s * 2048 + 1024 : (size_t)o1));
         areg[u][mi] = v0 ? a : u32x4{0u, 0u, 0u, 0u};
         areg2[u][mi] = v1 ? a2 : u32x4{0u, 0u, 0u, 0u};
       } else {
@@ -464,6 +526,18 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
       }
       uint8_t* C = static_cast<uint8_t*>(p.C);
+      if (A8 && ATB) {
+        // MXFP8 h, tile-blocked for the next projection (K = N/2 there)
+        const int ex = mx8_block_exp(amax);
+        u32x4 c0, c1;
+        mx8_encode32(v, ex, c0, c1);
+        const int b = hcol / 32;
+        const size_t blk = mx_block((long long)tile * MI + (row >> 4), b >> 2, (N / 2) / 128);
+        *reinterpret_cast<u32x4*>(C + mx8_tiled_pos(blk, 32 * (b & 3), row)) = c0;
+        *reinterpret_cast<u32x4*>(C + mx8_tiled_pos(blk, 32 * (b & 3) + 16, row)) = c1;
+        p.Cs[blk * 64 + (b & 3) * 16 + (row & 15)] = (uint8_t)(ex + 127);
+        continue;
+      }
       if (A8) {
         // MXFP8 h, row-major (codes [rows, N/2], scale bytes [rows, N/64])
         const int ex = mx8_block_exp(amax);
@@ -801,9 +875,12 @@ static hipError_t launch_mx_cfg(const MxGemmArgs& a, hipStream_t s) {
   const int ncols = a.epilogue == MOE_EPI_SILU_MUL ? a.N / 2 : a.N;
   const int bcols = a.epilogue == MOE_EPI_SILU_MUL ? BN / 2 : BN;
   const dim3 grid = grid2d(8LL * ((a.max_tiles + 7) / 8) * ((ncols + bcols - 1) / bcols));
-  if (a.act_e4m3) {  // W4A8 (row-major activations; the caller rejects mode 2)
-    if (a.mode == 1) launch_mx_mode<BM, BN, KW, PF, 1, 0>(a, grid, s);
-    else launch_mx_mode<BM, BN, KW, PF, 0, 0>(a, grid, s);
+  if (a.act_e4m3) {  // W4A8
+    switch (a.mode) {
+      case 2: launch_mx_mode<BM, BN, KW, PF, 2, 0>(a, grid, s); break;
+      case 1: launch_mx_mode<BM, BN, KW, PF, 1, 0>(a, grid, s); break;
+      default: launch_mx_mode<BM, BN, KW, PF, 0, 0>(a, grid, s); break;
+    }
     return hipGetLastError();
   }
   switch (a.mode) {

@@ -326,14 +326,23 @@ def test_w4a8_entry_points_reject(lib):
     assert lib.moe_mx8_quantize(_ptr(FAKE + 8), 4, 64, f, f, None) == -3
     assert lib.moe_mx8_quantize(f, 4, 64, f, None, None) == -1
     # grouped GEMM (MXFP8 activations, row-major)
-    g = lambda **kw: lib.moe_grouped_gemm_w4a8(f, f, None, 1, f, f, kw.get("wl", 0), 4, kw.get("N", 256),
-                                               kw.get("K", 256), f, kw.get("mt", 8), f, kw.get("bm", 16),
-                                               kw.get("epi", 0), kw.get("C", f), kw.get("cs", f), kw.get("od", 1), None)
+    g = lambda **kw: lib.moe_grouped_gemm_w4a8(f, f, None, 1, f, f, kw.get("wl", 0), kw.get("al", 0), 4,
+                                               kw.get("N", 256), kw.get("K", 256), f, kw.get("mt", 8), f,
+                                               kw.get("bm", 16), kw.get("epi", 0), kw.get("C", f), kw.get("cs", f),
+                                               kw.get("od", 1), None)
     assert g(K=48) == -2
     assert g(bm=256) == -2
     assert g(bm=128, K=160) == -2                                   # the 128-row kernel steps K by 128
-    assert lib.moe_grouped_gemm_w4a8(f, _ptr(FAKE + 1), None, 1, f, f, 0, 4, 256, 256, f, 8, f, 128, 0, f, None, 1,
-                                     None) == -3                    # the 128-row kernel loads scales 4 bytes wide
+    assert lib.moe_grouped_gemm_w4a8(f, _ptr(FAKE + 1), None, 1, f, f, 0, 0, 4, 256, 256, f, 8, f, 128, 0, f, None,
+                                     1, None) == -3                 # the 128-row kernel loads scales 4 bytes wide
+    assert g(al=1) == -1                                            # tile-blocked activations: packed weights
+    assert g(al=1, wl=1, bm=128) == -1                              # ... and tiles of at most 64 rows
+    assert g(al=1, wl=1, epi=1, N=320) == -2                        # a tile-blocked h needs N/2 % 128 == 0
+    assert g(al=3) == -1
+    q8 = lambda **kw: lib.moe_mx8_quantize_tiles(f, 4, kw.get("K", 256), None, 1, f, 8, f, kw.get("bm", 16), f, f,
+                                                 None)
+    assert q8(K=96) == -1
+    assert q8(bm=128) == -2
     assert g(epi=1, N=96) == -2                                     # h blocks of 32 columns
     assert g(epi=5) == -1
     assert g(od=7) == -1

@@ -316,6 +316,65 @@ def test_grouped_gemm_w4a8_packed_matches_canonical_bits(bm):
             np.testing.assert_array_equal(a[1].cpu().numpy(), b[1].cpu().numpy())
 
 
+@pytest.mark.parametrize("T,E,k,bm", [(3, 8, 2, 16), (40, 16, 4, 16), (90, 12, 3, 32), (300, 8, 2, 64)])
+def test_w4a8_tiled_activation_chain_matches_row_major_bits(T, E, k, bm):
+    # x -> quantize -> gate_up (SiLU*mul, h quantized) -> down, once with row-major activations and
+    # canonical weights, once with tile-blocked MXFP8 activations and packed weights: same O bits
+    ids, al = _routing(T, E, k, bm, seed=T + 13)
+    R, H, I = T * k, 256, 128
+    rng = np.random.default_rng(bm + T + 1)
+    x = gu.dev_bf16(mi.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)))
+    _, _, W13, E13 = _operands(1, 2 * I, H, E, seed=5)
+    _, _, W2, E2 = _operands(1, H, I, E, seed=6)
+    W13, E13, W2, E2 = gu.dev(W13), gu.dev(E13), gu.dev(W2), gu.dev(E2)
+    P13, Q13 = moe.moe_mx_prepack(W13, E13)
+    P2, Q2 = moe.moe_mx_prepack(W2, E2)
+    mt = al["num_tiles"]
+    tiles = gu.dev(np.ascontiguousarray(al["tiles"].astype(np.int32)))
+    nt = gu.dev(np.array([mt], np.int32))
+    srt = gu.dev(al["sorted_ids"].astype(np.int32))
+    xq, xs = moe.moe_mx8_quantize(x)
+    hq, hs = moe.moe_grouped_gemm_w4a8(xq, xs, srt, k, W13, E13, tiles, mt, nt, bm, moe.MOE_EPI_SILU_MUL, R)
+    O1 = moe.moe_grouped_gemm_w4a8(hq, hs, None, 1, W2, E2, tiles, mt, nt, bm, moe.MOE_EPI_NONE, R)
+    tq, ts = moe.moe_mx8_quantize_tiles(x, srt, k, tiles, mt, nt, bm)
+    gq, gs = moe.moe_grouped_gemm_w4a8(tq, ts, None, 1, P13, Q13, tiles, mt, nt, bm, moe.MOE_EPI_SILU_MUL, R,
+                                       weight_layout=moe.MOE_LAYOUT_PACKED, act_layout=moe.MOE_ACT_TILED)
+    O2 = moe.moe_grouped_gemm_w4a8(gq, gs, None, 1, P2, Q2, tiles, mt, nt, bm, moe.MOE_EPI_NONE, R,
+                                   weight_layout=moe.MOE_LAYOUT_PACKED, act_layout=moe.MOE_ACT_TILED)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(O1.view(torch.int32).cpu().numpy(), O2.view(torch.int32).cpu().numpy())
+
+
+def test_mx8_quantize_tiles_is_the_row_major_quantization_rearranged():
+    T, E, k, bm, K = 37, 8, 3, 16, 384
+    ids, al = _routing(T, E, k, bm, seed=7)
+    rng = np.random.default_rng(8)
+    bits = mi.f32_to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32) * 3)
+    x = gu.dev_bf16(bits)
+    mt = al["num_tiles"]
+    tiles = gu.dev(np.ascontiguousarray(al["tiles"].astype(np.int32)))
+    nt = gu.dev(np.array([mt], np.int32))
+    srt = gu.dev(al["sorted_ids"].astype(np.int32))
+    tq, ts = moe.moe_mx8_quantize_tiles(x, srt, k, tiles, mt, nt, bm)
+    torch.cuda.synchronize()
+    rq, rs = oracle.mx8_quantize(mi.bf16_bits_to_f32(bits).astype(np.float64))
+    tq, ts = tq.cpu().numpy().reshape(-1), ts.cpu().numpy().reshape(-1)
+    nks = K // 128
+    for t in range(mt):
+        e, row0, rows = al["tiles"][t]
+        for i in range(rows):
+            src = al["sorted_ids"][row0 + i] // k
+            for s_ in range(nks):
+                blk = (t * (bm // 16) + i // 16) * nks + s_
+                for qq in range(4):
+                    lane = qq * 16 + (i % 16)
+                    a = tq[blk * 2048 + lane * 16: blk * 2048 + lane * 16 + 16]
+                    b = tq[blk * 2048 + 1024 + lane * 16: blk * 2048 + 1024 + lane * 16 + 16]
+                    np.testing.assert_array_equal(a, rq[src, s_ * 128 + 16 * qq: s_ * 128 + 16 * qq + 16])
+                    np.testing.assert_array_equal(b, rq[src, s_ * 128 + 64 + 16 * qq: s_ * 128 + 80 + 16 * qq])
+                    assert ts[blk * 64 + lane] == rs[src, s_ * 4 + qq]
+
+
 # ---------------------------------------------------------------------------------------------------
 # whole layer
 
