@@ -268,6 +268,10 @@ def test_ffn_forward_matches_oracle(name, nsample):
     mi.custom("fused_max", 16, 128, 64, 128, 64, seed=10),
     mi.custom("fused_e512", 16, 512, 8, 128, 64, seed=15),
     mi.custom("fused_past", 17, 128, 8, 128, 64, seed=16),
+    # a few dozen tokens: k = 16 with 1024 slots, 256 experts, 65 tokens
+    mi.custom("t64_k16", 64, 128, 16, 128, 64, seed=21),
+    mi.custom("t40_e256", 40, 256, 8, 128, 64, seed=22),
+    mi.custom("t65", 65, 64, 4, 128, 64, seed=23),
     # the gate_up launch's routing prologue (at most 16 tokens, k <= 16) at its limits: 512 experts
     # with k = 16, 129 experts (the wider selection), k = E, one token; k = 17 falls back
     mi.custom("prologue_max", 16, 512, 16, 128, 64, seed=17),
