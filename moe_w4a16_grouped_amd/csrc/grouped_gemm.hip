@@ -219,12 +219,27 @@ __device__ bool route_prologue(const GemmArgs& p, RouteLds& L, int nbn, int shar
   const long long b = linear_block();
   const bool writer = b == 0;
   for (int i = tid; i < E; i += 256) L.cnt[i] = 0;
-  for (int t = wave; t < T; t += 4) {
-    const float* lg = p.route_logits + (size_t)t * E;
-    int32_t* io = writer ? p.route_ids + (size_t)t * k : nullptr;
-    float* wo = writer ? p.route_w + (size_t)t * k : nullptr;
-    if constexpr (NJ <= 2) route_token_rank(lg, E, k, L.pairs[wave], L.kept[wave], io, wo, L.ids + t * k);
-    else route_token<NJ>(lg, E, k, L.kept[wave], L.kept[wave] + k, io, wo, L.ids + t * k);
+  if constexpr (NJ <= 2) {
+    // every logits load of this wave's tokens (at most 4) first, so that they share one round trip
+    constexpr int TPW = kRouteMaxT / 4;
+    uint64_t me[TPW][2];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+      if (wave + 4 * j < T) rank_pairs_load(p.route_logits + (size_t)(wave + 4 * j) * E, E, me[j]);
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int t = wave + 4 * j;
+      if (t >= T) break;
+      route_token_rank_pairs(me[j], E, k, L.pairs[wave], L.kept[wave], writer ? p.route_ids + (size_t)t * k : nullptr,
+                             writer ? p.route_w + (size_t)t * k : nullptr, L.ids + t * k);
+    }
+  } else {
+    for (int t = wave; t < T; t += 4) {
+      const float* lg = p.route_logits + (size_t)t * E;
+      int32_t* io = writer ? p.route_ids + (size_t)t * k : nullptr;
+      float* wo = writer ? p.route_w + (size_t)t * k : nullptr;
+      route_token<NJ>(lg, E, k, L.kept[wave], L.kept[wave] + k, io, wo, L.ids + t * k);
+    }
   }
   __syncthreads();
   for (int i = tid; i < R; i += 256) atomicAdd(&L.cnt[L.ids[i]], 1);

@@ -93,6 +93,17 @@ __device__ __forceinline__ void route_token(const float* __restrict__ l, int E, 
   }
 }
 
+// The (key, ~id) pairs of lane l's experts l and l + 64 (0 for absent experts), loaded ahead of
+// route_token_rank_pairs so that a wave routing several tokens issues all its loads at once.
+__device__ __forceinline__ void rank_pairs_load(const float* __restrict__ l, int E, uint64_t (&me)[2]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = lane + 64 * j;
+    me[j] = e < E ? ((uint64_t)ordered_bits(l[e]) << 32) | (uint32_t)(~(uint32_t)e) : 0ull;
+  }
+}
+
 // Top-k of one token by one wave for E <= 128 by counting ranks.  Each expert's (key, id) pair is
 // one 64-bit value (key << 32 | ~id) whose unsigned order is the (logit desc, id asc) order; lane l
 // places the pairs of experts l and l + 64 in LDS (pairs, 128 entries; absent experts hold 0, below
@@ -101,17 +112,12 @@ __device__ __forceinline__ void route_token(const float* __restrict__ l, int E, 
 // ids_lds receives the ids by slot.  With ids_out set, the kept pairs are placed in ranked (k
 // entries) and the weights formed as route_token forms them (same operations in the same order, so
 // the same bits); otherwise no weights are formed.
-__device__ __forceinline__ void route_token_rank(const float* __restrict__ l, int E, int k, uint64_t* pairs,
-                                                 uint64_t* ranked, int32_t* __restrict__ ids_out,
-                                                 float* __restrict__ w_out, int32_t* ids_lds) {
+__device__ __forceinline__ void route_token_rank_pairs(const uint64_t (&me)[2], int E, int k, uint64_t* pairs,
+                                                       uint64_t* ranked, int32_t* __restrict__ ids_out,
+                                                       float* __restrict__ w_out, int32_t* ids_lds) {
   const int lane = threadIdx.x & 63;
-  uint64_t me[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int e = lane + 64 * j;
-    me[j] = e < E ? ((uint64_t)ordered_bits(l[e]) << 32) | (uint32_t)(~(uint32_t)e) : 0ull;
-    pairs[e] = me[j];
-  }
+  for (int j = 0; j < 2; ++j) pairs[lane + 64 * j] = me[j];
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   int rank[2] = {0, 0};
@@ -149,6 +155,15 @@ __device__ __forceinline__ void route_token_rank(const float* __restrict__ l, in
     ids_out[s2] = (int)(~(uint32_t)key);
     w_out[s2] = expf(from_ordered_bits((uint32_t)(key >> 32)) - top) / sum;
   }
+}
+
+// route_token_rank_pairs with its own loads.
+__device__ __forceinline__ void route_token_rank(const float* __restrict__ l, int E, int k, uint64_t* pairs,
+                                                 uint64_t* ranked, int32_t* __restrict__ ids_out,
+                                                 float* __restrict__ w_out, int32_t* ids_lds) {
+  uint64_t me[2];
+  rank_pairs_load(l, E, me);
+  route_token_rank_pairs(me, E, k, pairs, ranked, ids_out, w_out, ids_lds);
 }
 
 }  // namespace moe
