@@ -671,7 +671,7 @@ def main():
         calibrate()
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
 
