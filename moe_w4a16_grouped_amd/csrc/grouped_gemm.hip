@@ -198,7 +198,6 @@ __device__ __forceinline__ int a_row(const GemmArgs& p, int r) {
 // that tile's list entry and its part of the permutation, for the launches that follow.
 struct __attribute__((aligned(16))) RouteLds {
   uint64_t kept[4][2 * kRouteMaxK];
-  uint64_t pairs[4][128];  // rank-counting selection (E <= 128)
   int32_t ids[kRouteMaxT * kRouteMaxK];
   int32_t cnt[kAlignSingleMaxE];
   int32_t wsum[4];
@@ -222,16 +221,16 @@ __device__ bool route_prologue(const GemmArgs& p, RouteLds& L, int nbn, int shar
   if constexpr (NJ <= 2) {
     // every logits load of this wave's tokens (at most 4) first, so that they share one round trip
     constexpr int TPW = kRouteMaxT / 4;
-    uint64_t me[TPW][2];
+    uint32_t u[TPW][NJ];
 #pragma unroll
     for (int j = 0; j < TPW; ++j)
-      if (wave + 4 * j < T) rank_pairs_load(p.route_logits + (size_t)(wave + 4 * j) * E, E, me[j]);
+      if (wave + 4 * j < T) route_keys_load<NJ>(p.route_logits + (size_t)(wave + 4 * j) * E, E, u[j]);
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
       const int t = wave + 4 * j;
       if (t >= T) break;
-      route_token_rank_pairs(me[j], E, k, L.pairs[wave], L.kept[wave], writer ? p.route_ids + (size_t)t * k : nullptr,
-                             writer ? p.route_w + (size_t)t * k : nullptr, L.ids + t * k);
+      route_token_keys<NJ>(u[j], E, k, L.kept[wave], L.kept[wave] + k, writer ? p.route_ids + (size_t)t * k : nullptr,
+                           writer ? p.route_w + (size_t)t * k : nullptr, L.ids + t * k);
     }
   } else {
     for (int t = wave; t < T; t += 4) {

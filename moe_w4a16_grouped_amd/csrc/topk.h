@@ -3,12 +3,12 @@
 // section "8.1 MoE 路径：路由、专家并行与 MORI 通信" (routing and top-k selection).
 //
 // Lane l holds the logits of experts l, l + 64, ... as order-preserving 32-bit keys.  Selection by
-// radix select: 32 ballot-count rounds find the k-th largest key value T (the largest value with
-// at least k keys >= it); every key above T is kept, and among keys equal to T the lowest expert
-// ids fill the remaining places, which is the (logit desc, id asc) order.  The k kept (key, id)
-// pairs are compacted in LDS, ranked there by that order (slot 0 = largest), and the weights
-// exp(l_s - l_0) / sum_j exp(l_j - l_0) are formed in slot order: the softmax restricted to the
-// kept experts, which equals softmax-then-renormalise.
+// radix select: up to 32 ballot-count rounds find the k-th largest key value T (the largest value
+// with at least k keys >= it), stopping early once a prefix separates exactly k keys; every key
+// above T is kept, and among keys equal to T the lowest expert ids fill the remaining places, which
+// is the (logit desc, id asc) order.  The k kept (key, id) pairs are compacted in LDS, ranked there
+// by that order (slot 0 = largest), and the weights exp(l_s - l_0) / sum_j exp(l_j - l_0) are formed
+// in slot order: the softmax restricted to the kept experts, which equals softmax-then-renormalise.
 #pragma once
 #include "moe_common.h"
 
@@ -25,24 +25,33 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
   return __uint_as_float(u);
 }
 
-// Top-k of one token by one wave.  kept and ranked are this wave's LDS scratch (k entries each);
-// ids_out / w_out (NULL: not written) receive the token's k slots; ids_lds (may be NULL) receives a
-// copy of the ids.
+// The keys of lane l's experts l, l + 64, ... (0 for absent experts).
 template <int NJ>
-__device__ __forceinline__ void route_token(const float* __restrict__ l, int E, int k, uint64_t* kept,
-                                            uint64_t* ranked, int32_t* __restrict__ ids_out,
-                                            float* __restrict__ w_out, int32_t* ids_lds) {
+__device__ __forceinline__ void route_keys_load(const float* __restrict__ l, int E, uint32_t (&u)[NJ]) {
   const int lane = threadIdx.x & 63;
-  uint32_t u[NJ];
-  bool valid[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
-    valid[j] = e < E;
-    u[j] = valid[j] ? ordered_bits(l[e]) : 0u;
+    u[j] = e < E ? ordered_bits(l[e]) : 0u;
   }
+}
+
+// Top-k of one token by one wave from its keys (route_keys_load).  kept and ranked are this wave's
+// LDS scratch (k entries each); ids_out / w_out (NULL: not written, and no weights are formed)
+// receive the token's k slots; ids_lds (may be NULL) receives a copy of the ids.
+template <int NJ>
+__device__ __forceinline__ void route_token_keys(const uint32_t (&u)[NJ], int E, int k, uint64_t* kept,
+                                                 uint64_t* ranked, int32_t* __restrict__ ids_out,
+                                                 float* __restrict__ w_out, int32_t* ids_lds) {
+  const int lane = threadIdx.x & 63;
+  bool valid[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) valid[j] = lane + 64 * j < E;
   // k-th largest key value: the largest p with #{keys >= p} >= k (k <= E, so p = 0 qualifies).
-  // Every candidate is >= 1 and absent experts hold key 0, so they are never counted.
+  // Every candidate is >= 1 and absent experts hold key 0, so they are never counted.  Once exactly
+  // k keys are >= the accepted prefix, those k keys are the selection whatever the lower bits hold,
+  // so the rounds stop there (p then stays below the k-th largest key, and the tie rule below keeps
+  // all k: need equals the number of keys equal to p).
   uint32_t p = 0;
 #pragma unroll 4
   for (int bit = 31; bit >= 0; --bit) {
@@ -50,7 +59,10 @@ __device__ __forceinline__ void route_token(const float* __restrict__ l, int E, 
     int cnt = 0;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot(u[j] >= c));
-    if (cnt >= k) p = c;
+    if (cnt >= k) {
+      p = c;
+      if (cnt == k) break;
+    }
   }
   // keep every key above p and, in ascending id order, as many keys equal to p as places remain
   int need = k;
@@ -79,91 +91,30 @@ __device__ __forceinline__ void route_token(const float* __restrict__ l, int E, 
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
+  if (!ids_out) {
+    for (int s2 = lane; s2 < k; s2 += 64) ids_lds[s2] = (int)(~(uint32_t)ranked[s2]);
+    return;
+  }
   const float top = from_ordered_bits((uint32_t)(ranked[0] >> 32));
   float sum = 0.f;
   for (int s2 = 0; s2 < k; ++s2) sum += expf(from_ordered_bits((uint32_t)(ranked[s2] >> 32)) - top);
   for (int s2 = lane; s2 < k; s2 += 64) {
     const uint64_t key = ranked[s2];
     const int e = (int)(~(uint32_t)key);
-    if (ids_out) {
-      ids_out[s2] = e;
-      w_out[s2] = expf(from_ordered_bits((uint32_t)(key >> 32)) - top) / sum;
-    }
+    ids_out[s2] = e;
+    w_out[s2] = expf(from_ordered_bits((uint32_t)(key >> 32)) - top) / sum;
     if (ids_lds) ids_lds[s2] = e;
   }
 }
 
-// The (key, ~id) pairs of lane l's experts l and l + 64 (0 for absent experts), loaded ahead of
-// route_token_rank_pairs so that a wave routing several tokens issues all its loads at once.
-__device__ __forceinline__ void rank_pairs_load(const float* __restrict__ l, int E, uint64_t (&me)[2]) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int e = lane + 64 * j;
-    me[j] = e < E ? ((uint64_t)ordered_bits(l[e]) << 32) | (uint32_t)(~(uint32_t)e) : 0ull;
-  }
-}
-
-// Top-k of one token by one wave for E <= 128 by counting ranks.  Each expert's (key, id) pair is
-// one 64-bit value (key << 32 | ~id) whose unsigned order is the (logit desc, id asc) order; lane l
-// places the pairs of experts l and l + 64 in LDS (pairs, 128 entries; absent experts hold 0, below
-// every pair) and counts, for each of its two experts, the pairs above it: that count is the slot,
-// kept when below k.  The same selection and slot order as route_token, without its serial rounds.
-// ids_lds receives the ids by slot.  With ids_out set, the kept pairs are placed in ranked (k
-// entries) and the weights formed as route_token forms them (same operations in the same order, so
-// the same bits); otherwise no weights are formed.
-__device__ __forceinline__ void route_token_rank_pairs(const uint64_t (&me)[2], int E, int k, uint64_t* pairs,
-                                                       uint64_t* ranked, int32_t* __restrict__ ids_out,
-                                                       float* __restrict__ w_out, int32_t* ids_lds) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) pairs[lane + 64 * j] = me[j];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  int rank[2] = {0, 0};
-#pragma unroll 1
-  for (int i0 = 0; i0 < 128; i0 += 16) {
-    uint64_t kv[16];
-#pragma unroll
-    for (int c = 0; c < 16; c += 2) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(pairs + i0 + c);
-      kv[c] = ((uint64_t)v[1] << 32) | v[0];
-      kv[c + 1] = ((uint64_t)v[3] << 32) | v[2];
-    }
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      rank[0] += kv[c] > me[0] ? 1 : 0;
-      rank[1] += kv[c] > me[1] ? 1 : 0;
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int e = lane + 64 * j;
-    if (e < E && rank[j] < k) {
-      ids_lds[rank[j]] = e;
-      if (ids_out) ranked[rank[j]] = me[j];
-    }
-  }
-  if (!ids_out) return;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  const float top = from_ordered_bits((uint32_t)(ranked[0] >> 32));
-  float sum = 0.f;
-  for (int s2 = 0; s2 < k; ++s2) sum += expf(from_ordered_bits((uint32_t)(ranked[s2] >> 32)) - top);
-  for (int s2 = lane; s2 < k; s2 += 64) {
-    const uint64_t key = ranked[s2];
-    ids_out[s2] = (int)(~(uint32_t)key);
-    w_out[s2] = expf(from_ordered_bits((uint32_t)(key >> 32)) - top) / sum;
-  }
-}
-
-// route_token_rank_pairs with its own loads.
-__device__ __forceinline__ void route_token_rank(const float* __restrict__ l, int E, int k, uint64_t* pairs,
-                                                 uint64_t* ranked, int32_t* __restrict__ ids_out,
-                                                 float* __restrict__ w_out, int32_t* ids_lds) {
-  uint64_t me[2];
-  rank_pairs_load(l, E, me);
-  route_token_rank_pairs(me, E, k, pairs, ranked, ids_out, w_out, ids_lds);
+// route_token_keys with its own loads.
+template <int NJ>
+__device__ __forceinline__ void route_token(const float* __restrict__ l, int E, int k, uint64_t* kept,
+                                            uint64_t* ranked, int32_t* __restrict__ ids_out,
+                                            float* __restrict__ w_out, int32_t* ids_lds) {
+  uint32_t u[NJ];
+  route_keys_load<NJ>(l, E, u);
+  route_token_keys<NJ>(u, E, k, kept, ranked, ids_out, w_out, ids_lds);
 }
 
 }  // namespace moe
