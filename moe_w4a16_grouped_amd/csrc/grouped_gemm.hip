@@ -907,12 +907,13 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t strea
         if (a.route_logits) return routed<SplitK<16, 32, 2, 4>>(a, stream);
         return by_variant<SplitK<16, 32, 2, 4>>(a, stream);
       }
-      // 256-column blocks once the grid holds three workgroups per CU (768) with them: measured on
-      // MI355X with 128 experts top-8, 32 and 64 tokens: gate_up 39.6 / 41.5 us against 40.0 / 44.5 us
-      // for 128-column blocks; at 8 tokens (408 workgroups) 128-column blocks stay faster, and with one
-      // K step in flight rather than two (gate_up 22.0 against 23.5 us, down 11.9 against 12.4 us)
-      if (8LL * ((a.max_tiles + 7) / 8) * (a.epilogue == MOE_EPI_SILU_MUL ? (a.N / 2 + 127) / 128 : (a.N + 255) / 256) >=
-          768) {
+      // SiLU*mul: 256-column blocks once the grid holds three workgroups per CU (768) with them:
+      // measured on MI355X with 128 experts top-8, 32 and 64 tokens: gate_up 39.8 / 41.3 us against
+      // 40.4 / 44.0 us for 128-column blocks; at 8 tokens (408 workgroups) 128-column blocks are
+      // faster, and with one K step in flight rather than two (22.0 against 23.5 us).  The down
+      // projection (K = 768) is fastest with 128-column blocks one step ahead at 8, 32 and 64 tokens:
+      // 11.6 / 23.5 / 25.0 us against 13.2 / 24.1 / 26.7 us with 256-column blocks.
+      if (a.epilogue == MOE_EPI_SILU_MUL && 8LL * ((a.max_tiles + 7) / 8) * ((a.N / 2 + 127) / 128) >= 768) {
         if (a.route_logits) return routed<Tiled<16, 256, 1, 1>>(a, stream);
         return by_variant<Tiled<16, 256, 1, 1>>(a, stream);
       }
