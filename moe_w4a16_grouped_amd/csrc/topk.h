@@ -92,7 +92,8 @@ __device__ __forceinline__ void route_token_keys(const uint32_t (&u)[NJ], int E,
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   if (!ids_out) {
-    for (int s2 = lane; s2 < k; s2 += 64) ids_lds[s2] = (int)(~(uint32_t)ranked[s2]);
+    if (ids_lds)
+      for (int s2 = lane; s2 < k; s2 += 64) ids_lds[s2] = (int)(~(uint32_t)ranked[s2]);
     return;
   }
   const float top = from_ordered_bits((uint32_t)(ranked[0] >> 32));
