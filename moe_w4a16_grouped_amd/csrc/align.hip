@@ -76,13 +76,15 @@ __device__ void finish_expert(int e, int E, int nseg, int bm, int32_t* seg_cnt, 
                               int* scratch) {
   int c = 0;
   if (e < E) {
-    // segment counts are read 16 at a time so the loads are in flight together
-    for (int s0 = 0; s0 < nseg; s0 += 16) {
-      int v[16];
+    // segment counts are read 32 at a time so the loads are in flight together (80 segments of the
+    // 81920-slot skewed batch: three round trips)
+    constexpr int kBatch = 32;
+    for (int s0 = 0; s0 < nseg; s0 += kBatch) {
+      int v[kBatch];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = s0 + j < nseg ? seg_cnt[(s0 + j) * E + e] : 0;
+      for (int j = 0; j < kBatch; ++j) v[j] = s0 + j < nseg ? seg_cnt[(s0 + j) * E + e] : 0;
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
+      for (int j = 0; j < kBatch; ++j)
         if (s0 + j < nseg) {
           seg_cnt[(s0 + j) * E + e] = c;
           c += v[j];
