@@ -68,6 +68,63 @@ def test_route_topk_edges_and_ties(T, E, k):
     assert np.abs(w.cpu().numpy().astype(np.float64) - rw).max() <= gu.ROUTE_W_ATOL
 
 
+def _threshold_logits(T, E, k, seed):
+    """Logits whose selection boundary sits at different depths of the radix select: token t % 3 == 0
+    has its k-th and (k+1)-th largest logits one float apart (every bit decides), t % 3 == 1 has exactly
+    k positive logits (the sign bit decides), t % 3 == 2 has the k-th and (k+1)-th largest equal (a tie
+    at the boundary, resolved by the lower expert id).  Needs 1 <= k < E."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((T, E), np.float32)
+    for t in range(T):
+        vals = np.sort(rng.standard_normal(E).astype(np.float32))[::-1].copy()
+        mode = t % 3
+        if mode == 0:
+            vals[k] = np.nextafter(vals[k - 1], np.float32(-np.inf))
+            vals[k + 1:] = np.minimum(vals[k + 1:], np.nextafter(vals[k], np.float32(-np.inf)))
+        elif mode == 1:
+            vals = np.abs(vals) + np.float32(0.25)
+            vals[k:] = -vals[k:]
+        else:
+            vals[k] = vals[k - 1]
+        out[t, rng.permutation(E)] = vals
+    return out
+
+
+@pytest.mark.parametrize("E,k", [(64, 8), (128, 8), (128, 1), (256, 8), (512, 10), (1000, 16), (33, 32)])
+def test_route_topk_boundary_depths(E, k):
+    """The selection stops once a key prefix separates exactly k logits; boundaries decided by the
+    sign bit, by the last mantissa bit, and by a tie must all give the oracle's routing."""
+    logits = _threshold_logits(9, E, k, seed=E + k)
+    ids, w = moe.moe_route_topk(gu.dev(logits), k)
+    torch.cuda.synchronize()
+    rid, rw = oracle.route(logits, k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), rid)
+    assert np.abs(w.cpu().numpy().astype(np.float64) - rw).max() <= gu.ROUTE_W_ATOL
+
+
+@pytest.mark.parametrize("E", [128, 256])
+def test_ffn_forward_prologue_boundary_depths(E):
+    """At 12 tokens the gate_up launch routes in its prologue; with the boundary logits above its
+    routing, permutation and output must equal, bit for bit, those of the separate entry points."""
+    wl = mi.custom("boundary", 12, E, 8, 256, 128, seed=31)
+    inp = mi.make_inputs(wl)
+    inp.logits = _threshold_logits(wl.T, E, wl.k, seed=31 + E)
+    rid, _ = oracle.route(inp.logits, wl.k)
+    d = gu.DeviceInputs(inp)
+    _log(f"prologue boundary logits E={E}")
+    y_ref = _bits(_layer_from_entry_points(d, inp, True))
+    q13, s13, q2, s2 = _packed(d)
+    y = torch.full((wl.T, wl.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    wsb = moe.moe_ffn_workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.k)
+    ws = torch.full((max(wsb, 256),), 0xFF, dtype=torch.uint8, device="cuda")
+    ids = torch.full((wl.T, wl.k), -1, dtype=torch.int32, device="cuda")
+    moe.moe_ffn_forward(d.x, d.logits, q13, s13, q2, s2, wl.k, y=y, workspace=ws,
+                        weight_layout=moe.MOE_LAYOUT_PACKED, topk_ids_out=ids)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids.cpu().numpy(), rid)
+    np.testing.assert_array_equal(_bits(y), y_ref)
+
+
 # ---------------------------------------------------------------------------------------------------
 # permutation
 
