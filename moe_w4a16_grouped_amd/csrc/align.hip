@@ -68,12 +68,13 @@ __device__ void block_exclusive_scan2(int a, int b, int& ea, int& eb, int& ta, i
   tb = scratch[33];
 }
 
-// Multi-workgroup epilogue: thread e owns expert e.  seg_cnt holds per-segment counts for expert e
-// at seg_cnt[s * E + e]; they are replaced by the expert-local exclusive prefix (the permuted row of
-// a segment's first slot of expert e is offsets[e] + seg_cnt[s * E + e]).
+// Multi-workgroup epilogue: thread e owns expert e (s_toff, s_off, s_cnt: E + 1, E, E ints of LDS).
+// seg_cnt holds per-segment counts for expert e at seg_cnt[s * E + e]; they are replaced by the
+// expert-local exclusive prefix (the permuted row of a segment's first slot of expert e is
+// offsets[e] + seg_cnt[s * E + e]).
 __device__ void finish_expert(int e, int E, int nseg, int bm, int32_t* seg_cnt, int32_t* counts,
                               int32_t* offsets, int32_t* tiles, int max_tiles, int32_t* num_tiles,
-                              int* scratch) {
+                              int* scratch, int32_t* s_toff, int32_t* s_off, int32_t* s_cnt) {
   int c = 0;
   if (e < E) {
     // segment counts are read 32 at a time so the loads are in flight together (80 segments of the
@@ -97,16 +98,31 @@ __device__ void finish_expert(int e, int E, int nseg, int bm, int32_t* seg_cnt, 
   if (e < E) {
     counts[e] = c;
     offsets[e] = off;
-    for (int i = 0; i < nt && toff + i < max_tiles; ++i) {
-      int32_t* t = tiles + 3 * (size_t)(toff + i);
-      t[0] = e;
-      t[1] = off + i * bm;
-      t[2] = min(bm, c - i * bm);
-    }
+    s_toff[e] = toff;
+    s_off[e] = off;
+    s_cnt[e] = c;
   }
   if (threadIdx.x == 0) {
     offsets[E] = total_c;
     num_tiles[0] = total_t;
+    s_toff[E] = total_t;
+  }
+  __syncthreads();
+  // tile i belongs to the expert e with s_toff[e] <= i < s_toff[e + 1] (the last such e: experts without
+  // rows have no tiles), so the whole workgroup writes the list, a hot expert's tiles included
+  const int nw = min(total_t, max_tiles);
+  for (int i = threadIdx.x; i < nw; i += blockDim.x) {
+    int lo = 0, hi = E;  // s_toff[lo] <= i < s_toff[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_toff[mid] <= i) lo = mid;
+      else hi = mid;
+    }
+    const int j = i - s_toff[lo];
+    int32_t* t = tiles + 3 * (size_t)i;
+    t[0] = lo;
+    t[1] = s_off[lo] + j * bm;
+    t[2] = min(bm, s_cnt[lo] - j * bm);
   }
 }
 
@@ -281,7 +297,9 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(int32_t* seg_cnt, int 
                                                           int32_t* tiles, int max_tiles,
                                                           int32_t* num_tiles) {
   __shared__ int scratch[40];
-  finish_expert(threadIdx.x, E, nseg, bm, seg_cnt, counts, offsets, tiles, max_tiles, num_tiles, scratch);
+  __shared__ int32_t s_toff[1025], s_off[1024], s_cnt[1024];  // E <= 1024: one expert per thread
+  finish_expert(threadIdx.x, E, nseg, bm, seg_cnt, counts, offsets, tiles, max_tiles, num_tiles, scratch, s_toff,
+                s_off, s_cnt);
 }
 
 // Step 3: each wave re-walks its segment and scatters from its base rows.
