@@ -19,7 +19,34 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int nvec = H / 8;
   for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < k; ++s) {
+    // whole chunks of 8 slots: every row index and weight of the chunk, then every row, are loaded
+    // before its first FMA, so a chunk costs two dependent round trips instead of two per slot; the
+    // remaining slots one by one.  The FMAs run in ascending slot order either way.
+    int s = 0;
+    for (; s + 8 <= k; s += 8) {
+      int r[8];
+      float ws[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        r[j] = inv_perm[(size_t)t * k + s + j];
+        ws[j] = w[(size_t)t * k + s + j];
+      }
+      f32x4 a[8], b[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(O + (size_t)r[j] * H) + 2 * v;
+        a[j] = src[0];
+        b[j] = src[1];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[i] = fmaf(ws[j], a[j][i], acc[i]);
+          acc[4 + i] = fmaf(ws[j], b[j][i], acc[4 + i]);
+        }
+    }
+    for (; s < k; ++s) {
       const int r = inv_perm[(size_t)t * k + s];
       const float ws = w[(size_t)t * k + s];
       const f32x4* src = reinterpret_cast<const f32x4*>(O + (size_t)r * H) + 2 * v;
