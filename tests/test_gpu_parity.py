@@ -255,17 +255,28 @@ def test_grouped_gemm_plain(bm, out_dtype, N, K):
     gu.assert_within_tolerance(got, ref, "plain")
 
 
-def test_combine_matches_oracle():
-    T, k, H = 37, 5, 264
-    rng = np.random.default_rng(3)
+@pytest.mark.parametrize("k", [5, 8, 10, 16])
+@pytest.mark.parametrize("with_shared", [False, True])
+def test_combine_matches_oracle(k, with_shared):
+    """k = 5: the slot-by-slot tail only; 8: one whole chunk of 8 slots; 10: a chunk and a tail;
+    16: two chunks.  fp32 sums of at most k + 1 terms (each rounding at most 2^-24 of the running
+    sum, itself at most sum|terms|), then one bf16 rounding (2^-8 relative); the bound below doubles
+    the summation term to cover the rounding of the rounded sum."""
+    T, H = 37, 264
+    rng = np.random.default_rng(3 + k)
     O = rng.standard_normal((T * k, H)).astype(np.float32)
     inv = rng.permutation(T * k).astype(np.int32)
     w = rng.uniform(0, 1, (T, k)).astype(np.float32)
-    y = moe.moe_combine(gu.dev(O), gu.dev(inv), gu.dev(w))
+    S = rng.standard_normal((T, H)).astype(np.float32) if with_shared else None
+    y = moe.moe_combine(gu.dev(O), gu.dev(inv), gu.dev(w), shared=None if S is None else gu.dev(S))
     torch.cuda.synchronize()
     ref = oracle.combine(O.astype(np.float64), inv, w.astype(np.float64), T, k)
+    terms = oracle.combine(np.abs(O.astype(np.float64)), inv, w.astype(np.float64), T, k)
+    if S is not None:
+        ref = ref + S
+        terms = terms + np.abs(S)
     got = gu.host_bf16_to_f64(y)
-    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + (k + 2) * 2.0 ** -23 * terms)
 
 
 # ---------------------------------------------------------------------------------------------------

@@ -245,6 +245,131 @@ def test_grouped_proj_and_combine_match_per_expert_numpy():
     np.testing.assert_allclose(G2, G * rs[:, None], rtol=1e-15, atol=0)
 
 
+def _golden_combine():
+    rows = {}
+    with open(os.path.join(GOLDEN, "combine_worked_example.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            key, *vals = line.split()
+            rows[key] = vals
+    return rows
+
+
+def test_combine_worked_example():
+    """Hand-worked scatter-reduce (golden fixture): y[t] = sum_s w[t,s] O[inv_perm[t*k+s]]."""
+    g = _golden_combine()
+    T, k, H = 2, 2, 3
+    ids = np.array(g["ids"], np.int32).reshape(T, k)
+    a = oracle.align(ids, 2, 4)
+    np.testing.assert_array_equal(a["sorted_ids"], np.array(g["sorted_ids"], np.int32))
+    np.testing.assert_array_equal(a["inv_perm"], np.array(g["inv_perm"], np.int32))
+    O = np.array(g["O"], np.float64).reshape(T * k, H)
+    w = np.array(g["w"], np.float64).reshape(T, k)
+    y = oracle.combine(O, a["inv_perm"], w, T, k)
+    np.testing.assert_array_equal(y, np.array(g["y"], np.float64).reshape(T, H))
+
+
+@pytest.mark.parametrize("K,N,bm", [(64, 48, 4), (160, 96, 8), (256, 32, 16)])
+def test_grouped_proj_plain_matches_rowwise_numpy(K, N, bm):
+    """The plain (no SiLU) projection: identity rows (a_row_of = None) and gathered rows with a
+    divisor, each row against its expert's dequantized matrix times the row (numpy, float64)."""
+    rng = np.random.default_rng(K + N)
+    T, E, k = 23, 5, 2
+    logits = rng.standard_normal((T, E), dtype=np.float32)
+    logits[:, 1] += 2.0  # uneven expert sizes, one expert with several tiles
+    ids, _ = oracle.route(logits, k)
+    a = oracle.align(ids, E, bm)
+    R = T * k
+    Wq = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    Ws = mi.f32_to_bf16_bits(rng.uniform(0.005, 0.02, (E, N, K // 32)).astype(np.float32))
+    W = [_np_dequant(Wq[e], Ws[e]) for e in range(E)]
+    expert_of_row = np.repeat(np.arange(E), a["counts"])
+    # identity rows: permuted row r reads A[r]
+    A = mi.f32_to_bf16_bits(rng.standard_normal((R, K), dtype=np.float32))
+    Af = mi.bf16_bits_to_f32(A).astype(np.float64)
+    C = oracle.grouped_proj(A, None, 1, Wq, Ws, a["offsets"])
+    assert C.shape == (R, N)
+    for r in range(R):
+        np.testing.assert_allclose(C[r], W[expert_of_row[r]] @ Af[r], rtol=1e-12, atol=1e-13)
+    # gathered rows: permuted row r reads token sorted_ids[r] // k of X [T, K]
+    X = mi.f32_to_bf16_bits(rng.standard_normal((T, K), dtype=np.float32))
+    Xf = mi.bf16_bits_to_f32(X).astype(np.float64)
+    Cg = oracle.grouped_proj(X, a["sorted_ids"], k, Wq, Ws, a["offsets"])
+    for r in range(R):
+        t = a["sorted_ids"][r] // k
+        assert ids[t].tolist()[a["sorted_ids"][r] % k] == expert_of_row[r]
+        np.testing.assert_allclose(Cg[r], W[expert_of_row[r]] @ Xf[t], rtol=1e-12, atol=1e-13)
+
+
+def _bf16_round_f64(v):
+    return mi.bf16_bits_to_f32(mi.f32_to_bf16_bits(v.astype(np.float32))).astype(np.float64)
+
+
+@pytest.mark.parametrize("wl", [mi.WORKLOADS["tiny"], mi.custom("odd", 9, 6, 3, 128, 64, seed=3),
+                                mi.custom("skewed", 24, 16, 4, 64, 96, skew=True, seed=4)])
+@pytest.mark.parametrize("bm", [4, 16])
+def test_chain_of_steps_matches_layer_and_dense(wl, bm):
+    """The layer as the GPU runs it, step by step through the oracle: route -> align -> gathered
+    gate_up with SiLU*mul -> plain down on identity rows -> combine.  Pinned two ways:
+      * gate_up's permuted rows equal the per-token layer's h (its diagnostics) and the dense
+        formulation's h (every expert on every token, numpy float64), within 1e-12;
+      * with h rounded to bf16 between the projections (the boundary's h is bf16), y equals the
+        dense formulation fed the same bf16 h, within 1e-12 * rms, and differs from the fp64-h layer
+        by no more than that rounding can move it (2^-8 relative per h element, through |W2| and w)."""
+    inp = mi.make_inputs(wl)
+    T, E, k, H, I = wl.T, wl.E, wl.k, wl.H, wl.I
+    ids, w = oracle.route(inp.logits, k)
+    a = oracle.align(ids, E, bm)
+    R = T * k
+    Hp = oracle.grouped_proj(inp.x, a["sorted_ids"], k, inp.w13_q, inp.w13_s, a["offsets"], silu_mul=True)
+    y_layer, h_diag, _ = oracle.moe_ffn(inp, diagnostics=True)
+    f = a["sorted_ids"]
+    h_tok = h_diag.reshape(R, I)[f]  # the layer's h of slot f, in permuted order
+    hs = np.sqrt((h_tok ** 2).mean())
+    assert np.abs(Hp - h_tok).max() <= 1e-12 * hs
+    # dense h: every expert on every token
+    X = mi.bf16_bits_to_f32(inp.x).astype(np.float64)
+    flat = ids.reshape(-1)
+    for e in range(E):
+        G = X @ _np_dequant(inp.w13_q[e], inp.w13_s[e]).T
+        Hd = G[:, :I] / (1.0 + np.exp(-G[:, :I])) * G[:, I:]
+        rows = np.nonzero(flat[f] == e)[0]
+        assert np.abs(Hp[rows] - Hd[f[rows] // k]).max(initial=0.0) <= 1e-12 * hs
+    # down on identity rows, then combine
+    hb = mi.f32_to_bf16_bits(Hp.astype(np.float32))
+    O = oracle.grouped_proj(hb, None, 1, inp.w2_q, inp.w2_s, a["offsets"])
+    y = oracle.combine(O, a["inv_perm"], w, T, k)
+    # dense down + combine fed the same bf16 h: Y = sum_e diag(Rw[:, e]) (Hb_e W2_e^T)
+    Hbf = mi.bf16_bits_to_f32(hb).astype(np.float64)
+    L = inp.logits.astype(np.float64)
+    P = np.exp(L - L.max(1, keepdims=True))
+    P /= P.sum(1, keepdims=True)
+    Y = np.zeros((T, H))
+    W2abs = []
+    for e in range(E):
+        Hb_e = np.zeros((T, I))
+        rows = np.nonzero(flat[f] == e)[0]
+        Hb_e[f[rows] // k] = Hbf[rows]
+        W2 = _np_dequant(inp.w2_q[e], inp.w2_s[e])
+        W2abs.append(np.abs(W2))
+        Rw = np.zeros(T)
+        for t in range(T):
+            top = sorted(range(E), key=lambda j: (-inp.logits[t, j], j))[:k]
+            if e in top:
+                Rw[t] = P[t, e] / P[t, top].sum()
+        Y += Rw[:, None] * (Hb_e @ W2.T)
+    rms = np.sqrt((Y ** 2).mean())
+    assert np.abs(y - Y).max() <= 1e-12 * rms
+    # against the per-token fp64-h layer: only h's bf16 rounding separates them
+    bound = np.zeros((T, H))
+    for r in range(R):
+        t, s = divmod(int(f[r]), k)
+        bound[t] += w[t, s] * (W2abs[flat[f[r]]] @ (2.0 ** -8 * np.abs(Hp[r])))
+    assert np.all(np.abs(y - y_layer) <= bound + 1e-12 * rms)
+    assert np.abs(y - y_layer).max() > 0  # the rounding is visible, so the bound is not vacuous
+
+
 def test_page_byte_figures():
     # Atlas page, section "编译时内核选择和W4A16 Grouped GEMM": 1611 MB for BF16 expert weights and
     # 302 MB for W4A16 at the 256-expert shape (hidden 2048, intermediate 512).
