@@ -206,13 +206,27 @@ int64_t oracle_align(const int32_t *ids, int64_t T, int64_t k, int64_t E, int64_
 static double silu(double g) { return g / (1.0 + exp(-g)); }
 
 /* One expert's W4 matrix [N, K] times one activation row a [K] (fp64): out[n] = sum_kk a[kk] W[n,kk],
- * sums in ascending kk. */
+ * sums in ascending kk.  Each weight is the value weight_at gives (the code's E2M1 value times the
+ * group's bf16 scale, in fp32); the 16 code values are looked up in a table filled from
+ * oracle_e2m1_value and each group's scale is decoded once, which changes no product. */
 static void expert_matvec(const uint8_t *q, const uint16_t *s, int64_t N, int64_t K,
                           const double *a, double *out)
 {
+    float tab[16];
+    for (int c = 0; c < 16; ++c) tab[c] = (float)oracle_e2m1_value(c);
     for (int64_t n = 0; n < N; ++n) {
+        const uint8_t *qr = q + n * (K / 2);
+        const uint16_t *sr = s + n * (K / ORACLE_GROUP);
         double acc = 0.0;
-        for (int64_t kk = 0; kk < K; ++kk) acc += a[kk] * weight_at(q, s, K, n, kk);
+        for (int64_t g = 0; g < K / ORACLE_GROUP; ++g) {
+            const float sc = (float)oracle_bf16_value(sr[g]);
+            for (int64_t i = 0; i < ORACLE_GROUP; ++i) {
+                const int64_t kk = g * ORACLE_GROUP + i;
+                const uint8_t byte = qr[kk / 2];
+                const int code = (kk % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+                acc += a[kk] * (double)(tab[code] * sc);
+            }
+        }
         out[n] = acc;
     }
 }
@@ -401,12 +415,26 @@ void oracle_mx_dequant(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t
         for (int64_t kk = 0; kk < K; ++kk) out[n * K + kk] = mx_at(q, s, K, n, kk);
 }
 
-/* One expert's MX matrix [N, K] times one (already dequantized) activation row a [K]. */
+/* One expert's MX matrix [N, K] times one (already dequantized) activation row a [K].  Each weight
+ * is the value mx_at gives (E2M1 value times the E8M0 scale, exact in fp64); the code values come
+ * from a table filled from oracle_e2m1_value and each block's scale is decoded once. */
 static void mx_matvec(const uint8_t *q, const uint8_t *s, int64_t N, int64_t K, const double *a, double *out)
 {
+    double tab[16];
+    for (int c = 0; c < 16; ++c) tab[c] = oracle_e2m1_value(c);
     for (int64_t n = 0; n < N; ++n) {
+        const uint8_t *qr = q + n * (K / 2);
+        const uint8_t *sr = s + n * (K / ORACLE_GROUP);
         double acc = 0.0;
-        for (int64_t kk = 0; kk < K; ++kk) acc += a[kk] * mx_at(q, s, K, n, kk);
+        for (int64_t g = 0; g < K / ORACLE_GROUP; ++g) {
+            const double sc = oracle_e8m0_value(sr[g]);
+            for (int64_t i = 0; i < ORACLE_GROUP; ++i) {
+                const int64_t kk = g * ORACLE_GROUP + i;
+                const uint8_t byte = qr[kk / 2];
+                const int code = (kk % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+                acc += a[kk] * (tab[code] * sc);
+            }
+        }
         out[n] = acc;
     }
 }
@@ -554,12 +582,22 @@ void oracle_f8_dequant(const uint8_t *q, const float *s, int64_t rows, int64_t K
         for (int64_t kk = 0; kk < K; ++kk) out[n * K + kk] = f8_at(q, s, K, n, kk);
 }
 
-/* One expert's FP8 matrix [N, K] times one (already dequantized) activation row a [K]. */
+/* One expert's FP8 matrix [N, K] times one (already dequantized) activation row a [K].  Each weight
+ * is the value f8_at gives (E4M3 value times the block's fp32 scale, exact in fp64); the 256 code
+ * values come from a table filled from oracle_e4m3_value. */
 static void f8_matvec(const uint8_t *q, const float *s, int64_t N, int64_t K, const double *a, double *out)
 {
+    double tab[256];
+    for (int c = 0; c < 256; ++c) tab[c] = oracle_e4m3_value(c);
     for (int64_t n = 0; n < N; ++n) {
         double acc = 0.0;
-        for (int64_t kk = 0; kk < K; ++kk) acc += a[kk] * f8_at(q, s, K, n, kk);
+        for (int64_t b = 0; b < K / ORACLE_F8_BLOCK; ++b) {
+            const double sc = (double)s[n * (K / ORACLE_F8_BLOCK) + b];
+            for (int64_t i = 0; i < ORACLE_F8_BLOCK; ++i) {
+                const int64_t kk = b * ORACLE_F8_BLOCK + i;
+                acc += a[kk] * (tab[q[n * K + kk]] * sc);
+            }
+        }
         out[n] = acc;
     }
 }
