@@ -48,3 +48,25 @@ def assert_within_tolerance(y: np.ndarray, ref: np.ndarray, label: str = ""):
     r = tolerance_report(y, ref)
     assert r["max_over_rms"] <= MAX_ABS_OVER_RMS and r["mean_rel"] <= MEAN_REL, f"{label}: {r}"
     return r
+
+
+def sample_tokens(T: int, n: int, ids=None, per_expert: int = 2, seed: int = 99) -> np.ndarray:
+    """Token indices to check against the oracle at full size (each token's output is independent):
+    the first 8 and the last token, up to `per_expert` tokens routed to each touched expert (when the
+    routing ids [T, k] are given, so that every touched expert's rows appear, the rarely chosen ones
+    included), then random tokens up to n in all.  All tokens when T <= n."""
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    chosen = set(range(min(8, T))) | {T - 1}
+    if ids is not None:
+        flat_t = np.repeat(np.arange(T), ids.shape[1])
+        flat_e = ids.reshape(-1)
+        for e in np.unique(flat_e):
+            toks = np.unique(flat_t[flat_e == e])
+            chosen.update(rng.choice(toks, min(per_expert, len(toks)), replace=False).tolist())
+    rest = np.setdiff1d(np.arange(T), np.fromiter(chosen, np.int64))
+    extra = max(0, n - len(chosen))
+    if extra:
+        chosen.update(rng.choice(rest, min(extra, len(rest)), replace=False).tolist())
+    return np.array(sorted(chosen), np.int64)

@@ -373,16 +373,8 @@ def _forward(d, wl):
     return y, ids
 
 
-def _sample(T, n, seed=99):
-    if T <= n:
-        return np.arange(T)
-    rng = np.random.default_rng(seed)
-    rest = rng.choice(np.arange(8, T - 1), n - 9, replace=False)
-    return np.sort(np.concatenate([np.arange(8), rest, [T - 1]]))
-
-
-F8_CASES = [("tiny", 16), ("dec1", 1), ("dec8", 8), ("dec64", 24), ("pre800", 40), ("big4096", 12),
-            ("skew8192", 24)]
+F8_CASES = [("tiny", 16), ("dec1", 1), ("dec8", 8), ("dec32", 32), ("dec64", 64), ("pre800", 200),
+            ("big4096", 512), ("skew8192", 1024)]
 
 
 @pytest.mark.parametrize("name,nsample", F8_CASES)
@@ -392,10 +384,11 @@ def test_ffn_forward_f8_matches_oracle(name, nsample):
     inp = mi.make_f8_inputs(wl)
     d = F8Device(inp)
     y, ids = _forward(d, wl)
-    np.testing.assert_array_equal(ids.cpu().numpy(), oracle.route(inp.logits, wl.k)[0])
+    rid = oracle.route(inp.logits, wl.k)[0]
+    np.testing.assert_array_equal(ids.cpu().numpy(), rid)
     yh = gu.host_bf16_to_f64(y)
     assert np.all(np.isfinite(yh)), "output not fully written"
-    tok = _sample(wl.T, nsample)
+    tok = gu.sample_tokens(wl.T, nsample, rid)
     _assert_layer(yh[tok], inp, tok, name)
 
 
