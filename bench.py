@@ -6,10 +6,12 @@ GEMM -> combine) over one batch of seeded synthetic inputs already resident in H
 workload is the 800-token / 256-expert prefill shape (top-8, hidden 2048, intermediate 512, E2M1
 group-32 bf16 scales).  Weights are rotated over L distinct copies (L * bytes of the experts the
 routing touches >= 1 GiB) so that no step finds its weights in L2 or the Infinity Cache.  The K
-timed steps run twice: as eager launches and as one replay of a HIP graph holding the same K steps;
-`value` is the faster of the two (both are in `timing`).  `block` adds the whole MoE block around
-the layer: the router gate GEMM from the hidden states and a shared expert (dense W4A16 SwiGLU)
-added in the combine.
+timed steps run as eager launches with a HIP event between consecutive steps; `value` is the median
+per-step time (p10, p90, the mean and a median from one-layer HIP graphs are under `timing`).  The
+dominant kernel's roofline uses its mean HIP-event launch time from a per-kernel pass.  `workloads`
+times the decode, 4096-token and skewed shapes the same way (timing only); `block` adds the whole MoE
+block around the layer (router gate GEMM, shared expert); `cpu_baseline` times the CPU oracle on the
+host cores (all of them, and one thread) on token samples and compares the GPU output on them.
 
 Prints ONE JSON line on stdout; progress and the per-kernel table go to stderr.
 """
@@ -121,35 +123,12 @@ def calibrate():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(inp, target_s: float):
-    """Time the CPU oracle (as it stands) on a bounded token sample; scale to one whole layer."""
-    import oracle
-
-    wl = inp.wl
-    cores = len(os.sched_getaffinity(0))
-    rng = np.random.default_rng(1)
-    n = min(wl.T, cores)
-    tok = np.sort(rng.choice(wl.T, n, replace=False))
-    t0 = time.perf_counter()
-    oracle.moe_ffn(inp, tokens=tok)
-    dt = time.perf_counter() - t0
-    if dt < target_s / 2 and n < wl.T:
-        n2 = int(min(wl.T, max(n, n * (target_s / max(dt, 1e-3)))))
-        tok = np.sort(rng.choice(wl.T, n2, replace=False))
-        t0 = time.perf_counter()
-        oracle.moe_ffn(inp, tokens=tok)
-        dt = time.perf_counter() - t0
-        n = n2
-    us_layer = dt / n * wl.T * 1e6
-    return {"value": round(us_layer, 1), "unit": "us/layer", "cores": min(cores, n), "kind": "oracle",
-            "sample": f"{n} of {wl.T} tokens of the same workload ({dt:.1f} s wall), scaled to {wl.T} tokens"}
-
-
 def time_block(moe, wl, inp, x, copies, layout, args):
     """The whole MoE block from the hidden states: router gate GEMM, shared expert (a dense W4A16
     SwiGLU of intermediate size I) and the routed layer with the shared output added in the combine.
     Each weight copy gets its own router and shared-expert weights, rotated with the routed ones.
-    Timed like the layer (HIP graph of K steps), plus per-stage events for the two extra stages."""
+    Timed like the layer (median of per-step eager times, and from one-step graphs), plus per-stage
+    events for the two extra stages."""
     T, E, k, H, I = wl.T, wl.E, wl.k, wl.H, wl.I
     Is = I
     blk = mi.make_block_inputs(wl, Is)
@@ -169,36 +148,8 @@ def time_block(moe, wl, inp, x, copies, layout, args):
         wr, sh = extra[i % L]
         moe.moe_ffn_block_forward(x, wr, q13, s13, q2, s2, k, shared=sh, y=y, workspace=ws, weight_layout=layout)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for i in range(args.steps):
-        step(i)
-    ev1.record()
-    torch.cuda.synchronize()
-    eager_ms = ev0.elapsed_time(ev1) / args.steps
-    graph_ms = None
-    if not args.no_graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for i in range(min(L, args.steps)):
-                step(i)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(args.steps):
-                step(i)
-        graph.replay()
-        torch.cuda.synchronize()
-        ev0.record()
-        graph.replay()
-        ev1.record()
-        torch.cuda.synchronize()
-        graph_ms = ev0.elapsed_time(ev1) / args.steps
+    eager_ms = pctl(per_step_times(step, args.steps, args.warmup)[0])[0]
+    graph_ms = None if args.no_graph else pctl(per_step_graph_times(step, L, args.steps, args.warmup))[0]
     # per-stage events for the two stages the block adds
     lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
     so = torch.empty((T, H), dtype=torch.float32, device="cuda")
@@ -215,10 +166,9 @@ def time_block(moe, wl, inp, x, copies, layout, args):
     torch.cuda.synchronize()
     router_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e3)
     shared_us = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e3)
-    best = eager_ms if graph_ms is None else min(eager_ms, graph_ms)
     router_bytes = T * H * 2 + E * H * 2 + T * E * 4
     shared_bytes = mi.weight_bytes_per_expert(H, Is) + T * H * 2 + 2 * T * Is * 2 + T * H * 4
-    out = {"us": round(best * 1e3, 2), "eager_us": round(eager_ms * 1e3, 2),
+    out = {"us": round(eager_ms * 1e3, 2), "timing": "median of per-step eager times; graph_us from one-layer graphs",
            "graph_us": None if graph_ms is None else round(graph_ms * 1e3, 2), "shared_intermediate": Is,
            "router_us": round(router_us, 2), "router_gbps": round(router_bytes / (router_us * 1e-6) / 1e9, 1),
            "router_tflops": round(2.0 * T * H * E / (router_us * 1e-6) / 1e12, 3),
@@ -229,37 +179,9 @@ def time_block(moe, wl, inp, x, copies, layout, args):
 
 
 def time_steps(step, L, args):
-    """K steps timed as eager launches and as one replay of a HIP graph of the same K steps."""
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for i in range(args.steps):
-        step(i)
-    ev1.record()
-    torch.cuda.synchronize()
-    eager_ms = ev0.elapsed_time(ev1) / args.steps
-    graph_ms = None
-    if not args.no_graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for i in range(min(L, args.steps)):
-                step(i)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(args.steps):
-                step(i)
-        graph.replay()
-        torch.cuda.synchronize()
-        ev0.record()
-        graph.replay()
-        ev1.record()
-        torch.cuda.synchronize()
-        graph_ms = ev0.elapsed_time(ev1) / args.steps
+    """K steps: the median per-step eager time, and the median from one-layer HIP graphs (ms)."""
+    eager_ms = pctl(per_step_times(step, args.steps, args.warmup)[0])[0]
+    graph_ms = None if args.no_graph else pctl(per_step_graph_times(step, L, args.steps, args.warmup))[0]
     return eager_ms, graph_ms
 
 
@@ -317,7 +239,7 @@ def run_mxfp4(args):
         moe.moe_ffn_forward_mxfp4(x, logits, q13, e13, q2, e2, k, y=y, workspace=ws, weight_layout=layout)
 
     eager_ms, graph_ms = time_steps(step, L, args)
-    ms = eager_ms if graph_ms is None else min(eager_ms, graph_ms)
+    ms = eager_ms  # the value: median per-step eager time
     log(f"bench: MXFP4 layer eager {eager_ms * 1e3:.1f} us, graph {graph_ms * 1e3 if graph_ms else 0:.1f} us")
 
     # per-kernel pass through the separate entry points
@@ -392,8 +314,9 @@ def run_mxfp4(args):
                    "weight_layout": args.layout},
         "tflops": round(flops / (us * 1e-6) / 1e12, 3),
         "weight_gbps": round(weight_bytes / (us * 1e-6) / 1e9, 1),
-        "timing": {"eager_us": round(eager_ms * 1e3, 2), "graph_us": None if graph_ms is None else round(graph_ms * 1e3, 2),
-                   "value_from": "graph" if graph_ms is not None and graph_ms <= eager_ms else "eager"},
+        "timing": {"method": "median of per-step eager times (HIP event between consecutive steps)",
+                   "eager_us": round(eager_ms * 1e3, 2),
+                   "graph_median_us": None if graph_ms is None else round(graph_ms * 1e3, 2)},
         "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
         "roofline": {"kernel": "gemm_mx_kernel (gate_up + SiLU*mul + h quantization)", "bound": bound,
                      "achieved": round(achieved, 2), "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
@@ -436,7 +359,7 @@ def run_w4a8(args):
         moe.moe_ffn_forward_w4a8(x, logits, q13, e13, q2, e2, k, y=y, workspace=ws, weight_layout=layout)
 
     eager_ms, graph_ms = time_steps(step, L, args)
-    ms = eager_ms if graph_ms is None else min(eager_ms, graph_ms)
+    ms = eager_ms  # the value: median per-step eager time
     log(f"bench: W4A8 layer eager {eager_ms * 1e3:.1f} us, graph {graph_ms * 1e3 if graph_ms else 0:.1f} us")
 
     # per-kernel pass through the separate entry points
@@ -512,8 +435,9 @@ def run_w4a8(args):
                    "weight_layout": args.layout},
         "tflops": round(flops / (us * 1e-6) / 1e12, 3),
         "weight_gbps": round(weight_bytes / (us * 1e-6) / 1e9, 1),
-        "timing": {"eager_us": round(eager_ms * 1e3, 2), "graph_us": None if graph_ms is None else round(graph_ms * 1e3, 2),
-                   "value_from": "graph" if graph_ms is not None and graph_ms <= eager_ms else "eager"},
+        "timing": {"method": "median of per-step eager times (HIP event between consecutive steps)",
+                   "eager_us": round(eager_ms * 1e3, 2),
+                   "graph_median_us": None if graph_ms is None else round(graph_ms * 1e3, 2)},
         "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
         "roofline": {"kernel": "gemm_mx_kernel, E4M3 activations (gate_up + SiLU*mul + h quantization)", "bound": bound,
                      "achieved": round(achieved, 2), "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
@@ -554,7 +478,7 @@ def run_f8(args):
         moe.moe_ffn_forward_f8(x, logits, q13, s13, q2, s2, k, y=y, workspace=ws)
 
     eager_ms, graph_ms = time_steps(step, L, args)
-    ms = eager_ms if graph_ms is None else min(eager_ms, graph_ms)
+    ms = eager_ms  # the value: median per-step eager time
     log(f"bench: FP8 layer eager {eager_ms * 1e3:.1f} us, graph {graph_ms * 1e3 if graph_ms else 0:.1f} us")
 
     # per-kernel pass through the separate entry points
@@ -630,8 +554,9 @@ def run_f8(args):
                    "hidden": H, "intermediate": I, "weight_copies": L, "touched_experts": touched},
         "tflops": round(flops / (us * 1e-6) / 1e12, 3),
         "weight_gbps": round(weight_bytes / (us * 1e-6) / 1e9, 1),
-        "timing": {"eager_us": round(eager_ms * 1e3, 2), "graph_us": None if graph_ms is None else round(graph_ms * 1e3, 2),
-                   "value_from": "graph" if graph_ms is not None and graph_ms <= eager_ms else "eager"},
+        "timing": {"method": "median of per-step eager times (HIP event between consecutive steps)",
+                   "eager_us": round(eager_ms * 1e3, 2),
+                   "graph_median_us": None if graph_ms is None else round(graph_ms * 1e3, 2)},
         "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
         "roofline": {"kernel": ("gemm_f8_mm (gate_up + SiLU*mul + h quantization)" if fused_h
                                 else "gemm_f8_kernel (gate_up + SiLU*mul, fp32 h)"), "bound": bound,
@@ -644,78 +569,235 @@ def run_f8(args):
     print(json.dumps(result), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="pre800", choices=sorted(mi.WORKLOADS))
-    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = enough for 1 GiB)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--layout", choices=["packed", "canonical"], default="packed",
-                    help="weight layout the timed layer reads (packed = prepacked once, outside the timed region)")
-    ap.add_argument("--copy-probe", action="store_true", help="run only the counter-calibration copy")
-    ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
-    ap.add_argument("--calibrate", action="store_true", help="measure copy bandwidth and a vendor bf16 GEMM rate only")
-    ap.add_argument("--method", choices=["w4a16", "mxfp4", "w4a8", "f8"], default="w4a16",
-                    help="w4a16: bf16 activations, bf16 group scales (the default); mxfp4: W4A4 with E8M0 scales; "
-                         "w4a8: MXFP8 activations on the MXFP4 weights; f8: W8A8 E4M3 with per-1x128 fp32 scales")
-    ap.add_argument("--no-block", action="store_true",
-                    help="skip the whole-block timing (router gate + shared expert + routed layer)")
-    args = ap.parse_args()
-    if args.copy_probe:
-        copy_probe()
-        return
-    if args.calibrate:
-        calibrate()
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer has no multi-GPU path",
-              file=sys.stderr)
-        sys.exit(2)
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    if args.method == "mxfp4":
-        run_mxfp4(args)
-        return
-    if args.method == "f8":
-        run_f8(args)
-        return
-    if args.method == "w4a8":
-        run_w4a8(args)
-        return
 
+def _omp_set_threads(n: int) -> bool:
+    """Thread count of the oracle's OpenMP runtime (the process-wide libgomp it links)."""
+    import ctypes
+
+    try:
+        ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+        return True
+    except OSError:
+        return False
+
+
+def cpu_baseline_w4a16(inp, y_gpu: np.ndarray, target_s: float, fn=None):
+    """The CPU oracle as it stands, timed on the host cores on bounded token samples of the same
+    workload and scaled to one whole layer: once with every core the process may use, once with one
+    thread.  The all-core sample's outputs are also compared with the GPU's y on those tokens."""
+    import oracle
+
+    fn = fn or oracle.moe_ffn
+    wl = inp.wl
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(1)
+
+    def timed(n_target, seconds):
+        n = min(wl.T, n_target)
+        tok = np.sort(rng.choice(wl.T, n, replace=False))
+        t0 = time.perf_counter()
+        ref = fn(inp, tokens=tok)
+        dt = time.perf_counter() - t0
+        if dt < seconds / 2 and n < wl.T:
+            n = int(min(wl.T, max(n, n * (seconds / max(dt, 1e-3)))))
+            tok = np.sort(rng.choice(wl.T, n, replace=False))
+            t0 = time.perf_counter()
+            ref = fn(inp, tokens=tok)
+            dt = time.perf_counter() - t0
+        return tok, ref, dt
+
+    _omp_set_threads(cores)
+    tok, ref, dt = timed(cores, target_s)
+    out = {"value": round(dt / len(tok) * wl.T * 1e6, 1), "unit": "us/layer", "cores": min(cores, len(tok)),
+           "kind": "oracle", "cpu_model": cpu_model(),
+           "sample": f"{len(tok)} of {wl.T} tokens of the same workload ({dt:.1f} s wall, {cores} threads), "
+                     f"scaled to {wl.T} tokens"}
+    if y_gpu is not None:
+        d = np.abs(y_gpu[tok] - ref)
+        rms = float(np.sqrt(np.mean(ref ** 2)))
+        out["parity"] = {"tokens": int(len(tok)), "max_over_rms": round(float(d.max() / rms), 5),
+                         "mean_rel": round(float(d.sum() / np.abs(ref).sum()), 6),
+                         "bound": {"max_over_rms": 3e-2, "mean_rel": 5e-3}}
+    if _omp_set_threads(1):
+        tok1, _, dt1 = timed(1, target_s / 2)
+        out["one_thread"] = {"value": round(dt1 / len(tok1) * wl.T * 1e6, 1), "unit": "us/layer", "cores": 1,
+                             "sample": f"{len(tok1)} of {wl.T} tokens ({dt1:.1f} s wall, 1 thread), scaled to "
+                                       f"{wl.T} tokens"}
+        _omp_set_threads(cores)
+    return out
+
+
+def pctl(xs):
+    a = np.asarray(xs, np.float64)
+    return float(np.median(a)), float(np.percentile(a, 10)), float(np.percentile(a, 90))
+
+
+def per_step_times(step, K: int, W: int):
+    """W untimed steps, then K steps with a HIP event between consecutive steps on the stream the
+    layer runs on (torch's current stream), bracketed by device synchronisation.  Returns the K
+    per-step durations (ms) and the host wall time of the K steps (s)."""
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(K):
+        step(i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [evs[i].elapsed_time(evs[i + 1]) for i in range(K)], wall
+
+
+def per_step_graph_times(step, L: int, K: int, W: int):
+    """The same steps replayed from HIP graphs: one graph per weight copy, each holding one layer,
+    replayed in rotation with a HIP event between consecutive replays.  Returns per-step ms."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(L):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(L):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i)
+        graphs.append(g)
+    for i in range(W):
+        graphs[i % L].replay()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    evs[0].record()
+    for i in range(K):
+        graphs[i % L].replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    return [evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
+
+
+def measured_hbm(n_bytes: int = 1 << 30):
+    """This box's measured bandwidth beside the 8 TB/s spec: a device copy (read + write bytes per
+    second) and a read-only reduction of n_bytes."""
+    src = torch.ones(n_bytes // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    out["copy_gbps"] = round(2 * n_bytes * 10 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9, 1)
+    v = src.view(torch.int64)
+    for _ in range(3):
+        r = v.sum()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(10):
+        r = v.sum()
+    ev1.record()
+    torch.cuda.synchronize()
+    out["read_gbps"] = round(n_bytes * 10 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9, 1)
+    del src, dst, v, r
+    torch.cuda.empty_cache()
+    return out
+
+
+def layer_roofline(wl, touched: int):
+    """Algorithmic bytes and flops of one layer (touched experts' packed weights and scales once, x,
+    logits and y; intermediates excluded) and the roofline time, bound and floor."""
+    T, E, k, H, I = wl.T, wl.E, wl.k, wl.H, wl.I
+    nbytes = touched * mi.weight_bytes_per_expert(H, I) + T * H * 2 + T * E * 4 + T * H * 2
+    flops = 6.0 * T * k * H * I
+    t_hbm = nbytes / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    return nbytes, flops, ("hbm" if t_hbm >= t_mfma else "mfma"), max(t_hbm, t_mfma)
+
+
+def setup_w4a16(moe, wl, layout, copies_arg=0, log_prefix="bench"):
+    """Seeded inputs on the device, the touched expert count and L weight copies (prepacked when
+    the layout asks), so that L x touched bytes >= 1 GiB and every step streams its weights."""
+    inp = mi.make_inputs(wl)
+    x, logits = dev_bf16(inp.x), dev(inp.logits)
+    ids0, _ = moe.moe_route_topk(logits, wl.k)
+    touched = int(torch.unique(ids0).numel())
+    L = copies_arg or max(1, math.ceil((1 << 30) / (touched * mi.weight_bytes_per_expert(wl.H, wl.I))))
+    w0 = (dev(inp.w13_q), dev(inp.w13_s.view(np.int16)), dev(inp.w2_q), dev(inp.w2_s.view(np.int16)))
+    copies = [w0] + [tuple(t.clone() for t in w0) for _ in range(L - 1)]
+    prepack_us = None
+    if layout == moe.MOE_LAYOUT_PACKED:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        copies = [moe.moe_w4_prepack(a, b) + moe.moe_w4_prepack(c, d) for (a, b, c, d) in copies]
+        torch.cuda.synchronize()
+        prepack_us = (time.perf_counter() - t0) / L * 1e6
+    return inp, x, logits, touched, L, copies, prepack_us
+
+
+def time_workloads(moe, names, layout, args):
+    """Timing only (no oracle) of further workloads, each in the default line's launch configuration:
+    median, p10 and p90 of per-step eager times, the layer roofline and its fraction."""
+    out = {}
+    K = max(20, args.steps)
+    for name in names:
+        wl = mi.WORKLOADS[name]
+        lay = layout if (wl.H % 128 == 0 and wl.I % 128 == 0) else moe.MOE_LAYOUT_CANONICAL
+        inp, x, logits, touched, L, copies, _ = setup_w4a16(moe, wl, lay)
+        y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(max(moe.moe_ffn_workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.k), 256), dtype=torch.uint8,
+                         device="cuda")
+
+        def step(i):
+            q13, s13, q2, s2 = copies[i % L]
+            moe.moe_ffn_forward(x, logits, q13, s13, q2, s2, wl.k, y=y, workspace=ws, weight_layout=lay)
+
+        per, _ = per_step_times(step, K, args.warmup)
+        med, p10, p90 = pctl(per)
+        gmed = None
+        if not args.no_graph:
+            gmed = pctl(per_step_graph_times(step, L, K, args.warmup))[0]
+        nbytes, flops, bound, t_min = layer_roofline(wl, touched)
+        out[name] = {"us": round(med * 1e3, 2), "p10_us": round(p10 * 1e3, 2), "p90_us": round(p90 * 1e3, 2),
+                     "graph_us": None if gmed is None else round(gmed * 1e3, 2),
+                     "bound": bound, "roofline_us": round(t_min * 1e6, 2), "frac": round(t_min / (med * 1e-3), 4),
+                     "tflops": round(flops / (med * 1e-3) / 1e12, 2),
+                     "gbps": round(nbytes / (med * 1e-3) / 1e9, 1), "algorithmic_bytes": nbytes,
+                     "algorithmic_flops": flops, "touched_experts": touched, "weight_copies": L,
+                     "block_m": moe.moe_ffn_block_m(wl.T, wl.E, wl.k, lay)}
+        log(f"bench: workload {name}: {out[name]['us']:.1f} us/layer (p10 {out[name]['p10_us']:.1f}, "
+            f"p90 {out[name]['p90_us']:.1f}; graph {out[name]['graph_us']}), {bound} roofline frac {out[name]['frac']}")
+        del inp, x, logits, copies, y, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+def run_w4a16(args):
+    """The W4A16 layer (the default line)."""
     import moe_w4a16_grouped_amd as moe
 
     wl = mi.WORKLOADS[args.workload]
     T, E, k, H, I = wl.T, wl.E, wl.k, wl.H, wl.I
     R = T * k
-    log(f"bench: workload {wl.name} T={T} E={E} k={k} H={H} I={I}; generating inputs")
-    inp = mi.make_inputs(wl)
-    wbytes_all = E * mi.weight_bytes_per_expert(H, I)
-    x, logits = dev_bf16(inp.x), dev(inp.logits)
-    # The routing is the same every step, so only the experts it touches are read.  Enough copies
-    # that those bytes, summed over the copies, exceed 1 GiB (four times the 256 MB Infinity Cache):
-    # every step then streams its weights from HBM.  The touched set comes from the library's own
-    # routing of the logits.
-    ids0, _ = moe.moe_route_topk(logits, k)
-    touched0 = int(torch.unique(ids0).numel())
-    L = args.copies or max(1, math.ceil((1 << 30) / (touched0 * mi.weight_bytes_per_expert(H, I))))
-    w13_q0, w13_s0 = dev(inp.w13_q), dev(inp.w13_s.view(np.int16))
-    w2_q0, w2_s0 = dev(inp.w2_q), dev(inp.w2_s.view(np.int16))
-    copies = [(w13_q0, w13_s0, w2_q0, w2_s0)] + [
-        (w13_q0.clone(), w13_s0.clone(), w2_q0.clone(), w2_s0.clone()) for _ in range(L - 1)]
     layout = moe.MOE_LAYOUT_PACKED if args.layout == "packed" else moe.MOE_LAYOUT_CANONICAL
-    prepack_us = None
-    if layout == moe.MOE_LAYOUT_PACKED:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        packed = []
-        for (q13, s13, q2, s2) in copies:
-            packed.append(moe.moe_w4_prepack(q13, s13) + moe.moe_w4_prepack(q2, s2))
-        torch.cuda.synchronize()
-        prepack_us = (time.perf_counter() - t0) / L * 1e6
-        copies = packed
+    log(f"bench: workload {wl.name} T={T} E={E} k={k} H={H} I={I}; generating inputs")
+    inp, x, logits, touched0, L, copies, prepack_us = setup_w4a16(moe, wl, layout, args.copies)
+    wbytes_all = E * mi.weight_bytes_per_expert(H, I)
     y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(moe.moe_ffn_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device="cuda")
     log(f"bench: {L} weight copies of {wbytes_all / 1e6:.1f} MB ({touched0} of {E} experts touched); "
@@ -725,49 +807,20 @@ def main():
         q13, s13, q2, s2 = copies[i % L]
         moe.moe_ffn_forward(x, logits, q13, s13, q2, s2, k, y=y, workspace=ws, weight_layout=layout)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    ev0.record()
-    for i in range(args.steps):
-        step(i)
-    ev1.record()
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"bench: whole layer {ms_per_step * 1e3:.1f} us/step (host wall {t_wall / args.steps * 1e6:.1f} us/step)")
-    eager_ms = ms_per_step
-
-    # The same K steps replayed from a HIP graph: K consecutive layers (weight copies rotated as
-    # above) captured once, then replayed once untimed and once timed, so the launches need no host
-    # work.  The library records no memset and no host synchronisation, so the layer is capturable.
-    graph_ms = None
+    # The timed region: K eager steps, a HIP event between consecutive steps; value = the median.
+    per, wall = per_step_times(step, args.steps, args.warmup)
+    med, p10, p90 = pctl(per)
+    mean_ms = float(np.sum(per)) / args.steps
+    log(f"bench: whole layer median {med * 1e3:.1f} us/step (p10 {p10 * 1e3:.1f}, p90 {p90 * 1e3:.1f}, "
+        f"mean {mean_ms * 1e3:.1f}; host wall {wall / args.steps * 1e6:.1f} us/step)")
+    y_host = mi.bf16_bits_to_f32(y.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    graph_med = None
     if not args.no_graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for i in range(min(L, args.steps)):
-                step(i)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(args.steps):
-                step(i)
-        graph.replay()
-        torch.cuda.synchronize()
-        ev0.record()
-        graph.replay()
-        ev1.record()
-        torch.cuda.synchronize()
-        graph_ms = ev0.elapsed_time(ev1) / args.steps
-        log(f"bench: whole layer from a HIP graph {graph_ms * 1e3:.1f} us/step ({args.steps} captured steps)")
-        ms_per_step = min(ms_per_step, graph_ms)
+        graph_med = pctl(per_step_graph_times(step, L, args.steps, args.warmup))[0]
+        log(f"bench: whole layer from HIP graphs (one layer per graph) median {graph_med * 1e3:.1f} us/step")
 
     # Per-kernel pass: the same layer through the individual entry points, HIP events between the
-    # launches on the stream they run on (torch's current stream).
+    # launches on the stream they run on (torch's current stream), K steps after W warmup steps.
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
     bm = moe.moe_ffn_block_m(T, E, k, layout)
@@ -797,13 +850,12 @@ def main():
     touched = int((al["counts"] > 0).sum().item())
     log("bench: per-kernel us (events): " + ", ".join(f"{n}={v:.1f}" for n, v in kern_us.items()))
 
-    bpe = mi.weight_bytes_per_expert(H, I)
+    us = med * 1e3
+    layer_bytes, flops, layer_bound, t_min = layer_roofline(wl, touched)
+    weight_bytes = touched * mi.weight_bytes_per_expert(H, I)
     g13 = 2 * I * H // 2 + 2 * I * (H // 32) * 2
-    layer_bytes = touched * bpe + T * H * 2 + T * E * 4 + T * H * 2
-    weight_bytes = touched * bpe
-    flops = 6.0 * R * H * I
-    us = ms_per_step * 1e3
-    gu_bytes = touched * g13 + T * H * 2 + R * I * 2
+    # the dominant kernel (gate_up): its touched experts' weights and x, once (h excluded, an intermediate)
+    gu_bytes = touched * g13 + T * H * 2
     gu_flops = 4.0 * R * H * I
     gu_us = kern_us["gate_up"]
     bound = "hbm" if gu_flops / gu_bytes < RIDGE else "mfma"
@@ -811,6 +863,8 @@ def main():
         achieved, peak, unit = gu_bytes / (gu_us * 1e-6) / 1e9, HBM_PEAK_GBPS, "GB/s"
     else:
         achieved, peak, unit = gu_flops / (gu_us * 1e-6) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    hbm = measured_hbm()
+    log(f"bench: measured copy {hbm['copy_gbps']} GB/s (read + write), read {hbm['read_gbps']} GB/s")
     result = {
         "metric": METRIC,
         "value": round(us, 2),
@@ -818,7 +872,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(med, 5),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": round(us / PAGES_US_800, 5) if wl.name == "pre800" else None,
@@ -827,27 +881,89 @@ def main():
         "config": {"workload": f"{wl.name}: {T} tokens, {E} experts top-{k}, hidden {H}, intermediate {I}, "
                                f"W4 E2M1 group-32 bf16 scales", "tokens": T, "experts": E, "top_k": k,
                    "hidden": H, "intermediate": I, "weight_copies": L, "touched_experts": touched,
-                   "weight_layout": args.layout, "prepack_us_per_copy": None if prepack_us is None else round(prepack_us, 1)},
+                   "weight_layout": args.layout, "block_m": bm,
+                   "prepack_us_per_copy": None if prepack_us is None else round(prepack_us, 1)},
         "tflops": round(flops / (us * 1e-6) / 1e12, 3),
         "weight_gbps": round(weight_bytes / (us * 1e-6) / 1e9, 1),
         "layer_gbps": round(layer_bytes / (us * 1e-6) / 1e9, 1),
-        "layer_roofline_frac": round(max(layer_bytes / (HBM_PEAK_GBPS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
-                                     / (us * 1e-6), 4),
-        "timing": {"eager_us": round(eager_ms * 1e3, 2), "graph_us": None if graph_ms is None else round(graph_ms * 1e3, 2),
-                   "value_from": "graph" if graph_ms is not None and graph_ms <= eager_ms else "eager"},
+        "layer_roofline": {"bound": layer_bound, "algorithmic_bytes": layer_bytes, "algorithmic_flops": flops,
+                           "roofline_us": round(t_min * 1e6, 2), "frac": round(t_min / (us * 1e-6), 4)},
+        "timing": {"method": "median of per-step eager times (HIP event between consecutive steps)",
+                   "median_us": round(us, 2), "p10_us": round(p10 * 1e3, 2), "p90_us": round(p90 * 1e3, 2),
+                   "mean_us": round(mean_ms * 1e3, 2),
+                   "graph_median_us": None if graph_med is None else round(graph_med * 1e3, 2)},
         "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
         "roofline": {"kernel": ("gemm_w4a16_mm" if bm == 128 and layout == moe.MOE_LAYOUT_PACKED else "gemm_w4a16_tiled")
                                + " (gate_up + SiLU*mul)", "bound": bound, "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(wl.name) if args.layout == "packed" else None,
-                     "algorithmic_bytes": gu_bytes, "algorithmic_flops": gu_flops},
+                     "algorithmic_bytes": gu_bytes, "algorithmic_flops": gu_flops,
+                     "duration_us": round(gu_us, 2),
+                     "duration_from": "mean of K HIP-event launch durations in the per-kernel pass",
+                     "measured_peak": {"read_gbps": hbm["read_gbps"], "copy_gbps": hbm["copy_gbps"],
+                                       "frac_of_read": round(achieved / hbm["read_gbps"], 4) if bound == "hbm" else None}},
     }
     if not args.no_block:
         result["block"] = time_block(moe, wl, inp, x, copies, layout, args)
+    del copies
+    torch.cuda.empty_cache()
+    if not args.no_workloads:
+        others = [n for n in ("dec1", "dec8", "dec32", "dec64", "big4096", "skew8192") if n != wl.name]
+        result["workloads"] = time_workloads(moe, others, layout, args)
     if not args.no_cpu_baseline:
-        log(f"bench: timing the CPU oracle on a token sample (~{args.cpu_seconds:.0f} s)")
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        log(f"bench: timing the CPU oracle on token samples (~{args.cpu_seconds:.0f} s + 1 thread)")
+        result["cpu_baseline"] = cpu_baseline_w4a16(inp, y_host, args.cpu_seconds)
+        pr = result["cpu_baseline"].get("parity")
+        if pr:
+            log(f"bench: GPU y vs oracle on {pr['tokens']} tokens: max/rms {pr['max_over_rms']}, "
+                f"mean rel {pr['mean_rel']}")
     print(json.dumps(result), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="pre800", choices=sorted(mi.WORKLOADS))
+    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = enough for 1 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--layout", choices=["packed", "canonical"], default="packed",
+                    help="weight layout the timed layer reads (packed = prepacked once, outside the timed region)")
+    ap.add_argument("--copy-probe", action="store_true", help="run only the counter-calibration copy")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
+    ap.add_argument("--calibrate", action="store_true", help="measure copy bandwidth and a vendor bf16 GEMM rate only")
+    ap.add_argument("--method", choices=["w4a16", "mxfp4", "w4a8", "f8"], default="w4a16",
+                    help="w4a16: bf16 activations, bf16 group scales (the default); mxfp4: W4A4 with E8M0 scales; "
+                         "w4a8: MXFP8 activations on the MXFP4 weights; f8: W8A8 E4M3 with per-1x128 fp32 scales")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the timing-only lines of the other workloads (decode, 4096-token, skewed)")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the whole-block timing (router gate + shared expert + routed layer)")
+    args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe()
+        return
+    if args.calibrate:
+        calibrate()
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+
+    if args.method == "mxfp4":
+        run_mxfp4(args)
+        return
+    if args.method == "f8":
+        run_f8(args)
+        return
+    if args.method == "w4a8":
+        run_w4a8(args)
+        return
+
+    run_w4a16(args)
 
 
 if __name__ == "__main__":
