@@ -252,6 +252,30 @@ moe_status_t moe_ffn_forward(const uint16_t* x, const float* router_logits, int3
                              int32_t weight_layout, uint16_t* y, int32_t* topk_ids_out, float* topk_w_out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Bytes of the static device scratch array that moe_ffn_forward_noalloc works in (64 MiB). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+size_t moe_ffn_noalloc_scratch_bytes(void);
+
+/*
+ * moe_ffn_forward for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments, layouts, results and
+ * errors as moe_ffn_forward minus the workspace: the intermediate buffers (routing, permutation,
+ * tile list, h, O) live in one static device array of MOE_NOALLOC_SCRATCH_BYTES inside the library.
+ * The call allocates nothing (no hipMalloc, no allocating library routine) and launches exactly the
+ * kernels moe_ffn_forward launches, so its outputs are bit-identical to moe_ffn_forward's.
+ *   - Limit: sizes whose moe_ffn_workspace_bytes exceeds MOE_NOALLOC_SCRATCH_BYTES are rejected with
+ *     MOE_ERR_WORKSPACE before anything touches the device (the 800-token, 256-expert, H = 2048,
+ *     I = 512 layer needs about 59 MB; every decode batch of a few hundred tokens fits).
+ *   - Each GPU holds its own copy of the array from the first call on that device (the calling
+ *     thread's current device, which `stream` must belong to) until the process ends.
+ *   - All calls on one GPU share that GPU's array: calls that overlap in time on one GPU (two streams,
+ *     two host threads) race and must be serialised by the caller.
+ */
+moe_status_t moe_ffn_forward_noalloc(const uint16_t* x, const float* router_logits, int32_t T, int32_t H, int32_t I,
+                                     int32_t E, int32_t k, const uint8_t* w13_q, const uint16_t* w13_s,
+                                     const uint8_t* w2_q, const uint16_t* w2_s, int32_t weight_layout, uint16_t* y,
+                                     int32_t* topk_ids_out, float* topk_w_out, void* stream);
+
 /* Workspace bytes moe_ffn_block_forward needs (host-only, pure; 0 on invalid sizes).  Is = 0 means
  * no shared expert. */
 size_t moe_ffn_block_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t Is);

@@ -91,6 +91,8 @@ def load() -> ctypes.CDLL:
         "moe_ffn_block_m": ([I32, I32, I32, I32], I32),
         "moe_ffn_workspace_bytes": ([I32, I32, I32, I32, I32], SZ),
         "moe_ffn_forward": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, SZ, P], I32),
+        "moe_ffn_noalloc_scratch_bytes": ([], SZ),
+        "moe_ffn_forward_noalloc": ([P, P, I32, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -108,7 +110,7 @@ EXPORTED = ("moe_abi_version", "moe_status_string", "moe_last_error", "moe_route
             "moe_ffn_mxfp4_workspace_bytes", "moe_ffn_forward_mxfp4", "moe_f8_quantize", "moe_grouped_gemm_f8",
             "moe_ffn_f8_block_m", "moe_ffn_f8_workspace_bytes", "moe_ffn_forward_f8", "moe_mx8_quantize",
             "moe_mx8_quantize_tiles", "moe_grouped_gemm_w4a8", "moe_ffn_w4a8_block_m", "moe_ffn_w4a8_workspace_bytes",
-            "moe_ffn_forward_w4a8")
+            "moe_ffn_forward_w4a8", "moe_ffn_noalloc_scratch_bytes", "moe_ffn_forward_noalloc")
 
 
 def _check(status: int):
@@ -316,6 +318,24 @@ def moe_ffn_forward(x, router_logits, w13_q, w13_s, w2_q, w2_s, k: int, y=None, 
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
     return y
 
+
+def moe_ffn_noalloc_scratch_bytes() -> int:
+    return int(load().moe_ffn_noalloc_scratch_bytes())
+
+
+def moe_ffn_forward_noalloc(x, router_logits, w13_q, w13_s, w2_q, w2_s, k: int, y=None, topk_ids_out=None,
+                            topk_w_out=None, stream=None, weight_layout: int = MOE_LAYOUT_CANONICAL):
+    """moe_ffn_forward working in the library's static device scratch (the C call allocates nothing;
+    y is allocated here only when the caller passes none)."""
+    T, H = x.shape
+    E, N13, _ = w13_q.shape
+    I = N13 // 2
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _check(load().moe_ffn_forward_noalloc(_p(x), _p(router_logits), T, H, I, E, k, _p(w13_q), _p(w13_s), _p(w2_q),
+                                          _p(w2_s), weight_layout, _p(y), _p(topk_ids_out), _p(topk_w_out),
+                                          _stream(stream)))
+    return y
 
 
 # ---- MXFP4 (W4A4) ----------------------------------------------------------------------------------

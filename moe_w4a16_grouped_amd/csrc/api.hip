@@ -7,9 +7,13 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "launch.h"
 #include "moe_w4a16.h"
+
+// The static scratch array of moe_ffn_forward_noalloc (see scratch_of_current_device below).
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -118,14 +122,15 @@ moe_status_t check_weight_ptrs(const uint8_t* w13_q, const uint16_t* w13_s, cons
 }
 
 // Pointer checks of the routed layer (called for T > 0).
+// (workspace_needed = false: the call brings no workspace, as in the entry point without allocation.)
 moe_status_t check_ffn_ptrs(const uint16_t* x, const uint8_t* w13_q, const uint16_t* w13_s, const uint8_t* w2_q,
                             const uint16_t* w2_s, int32_t weight_layout, const uint16_t* y,
                             const int32_t* topk_ids_out, const float* topk_w_out, const void* workspace,
-                            const char* who) {
+                            const char* who, bool workspace_needed = true) {
   if (moe_status_t st = check_weight_ptrs(w13_q, w13_s, w2_q, w2_s, weight_layout, who)) return st;
-  if (!x || !y || !workspace) return fail(MOE_ERR_INVALID_ARG, "%s: NULL pointer", who);
-  if (!aligned16(x) || !aligned16(y) || !aligned16(workspace) || (topk_ids_out && !aligned4(topk_ids_out)) ||
-      (topk_w_out && !aligned4(topk_w_out)))
+  if (!x || !y || (workspace_needed && !workspace)) return fail(MOE_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (!aligned16(x) || !aligned16(y) || (workspace_needed && !aligned16(workspace)) ||
+      (topk_ids_out && !aligned4(topk_ids_out)) || (topk_w_out && !aligned4(topk_w_out)))
     return fail(MOE_ERR_MISALIGNED, "%s: x, y and workspace need 16-byte alignment", who);
   return MOE_OK;
 }
@@ -222,6 +227,38 @@ moe_status_t run_ffn(const uint16_t* x, const float* router_logits, int32_t T, i
   if (e != hipSuccess) return hip_status(e, "down launch");
   e = moe::launch_combine(o, inv, w, sw.w13_q ? o + (size_t)R * H : shared_out, T, k, H, y, s);
   return hip_status(e, "combine launch");
+}
+
+// Scratch of the layer entry point that allocates nothing: a static device array of fixed size.
+// Each GPU the library runs on holds its own copy (allocated when the code object is loaded on that
+// device) until the process ends.  Host code never passes the array's name to a kernel or a copy:
+// that name is a host-side stand-in, not a device address.  The device address is looked up once
+// per device, with that device current, and kept.  Every call on one GPU shares that GPU's array
+// and it keeps the last call's contents; no kernel of the layer needs it cleared (every region is
+// written before it is read), and calls that overlap in time on one GPU race.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+size_t scratch_capacity() { return sizeof(scratch); }
+
+moe_status_t scratch_of_current_device(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "moe_ffn_forward_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_ffn_forward_noalloc: device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "moe_ffn_forward_noalloc: hipGetSymbolAddress(scratch)");
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u))
+      return fail(MOE_ERR_HIP, "moe_ffn_forward_noalloc: scratch address %p is not 256-byte aligned", p);
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 // Workspace of the MXFP4 layer: the routing regions of ffn_layout (canonical tile heights), then
@@ -472,6 +509,35 @@ moe_status_t moe_ffn_forward(const uint16_t* x, const float* router_logits, int3
     return fail(MOE_ERR_WORKSPACE, "moe_ffn_forward: workspace %zu B < required %zu B", workspace_bytes, L.total);
   return run_ffn(x, router_logits, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, weight_layout, y, topk_ids_out,
                  topk_w_out, static_cast<char*>(workspace), L, SharedW{}, nullptr, (hipStream_t)stream);
+}
+
+size_t moe_ffn_noalloc_scratch_bytes(void) { return scratch_capacity(); }
+
+moe_status_t moe_ffn_forward_noalloc(const uint16_t* x, const float* router_logits, int32_t T, int32_t H, int32_t I,
+                                     int32_t E, int32_t k, const uint8_t* w13_q, const uint16_t* w13_s,
+                                     const uint8_t* w2_q, const uint16_t* w2_s, int32_t weight_layout, uint16_t* y,
+                                     int32_t* topk_ids_out, float* topk_w_out, void* stream) {
+  if (moe_status_t st = check_routing_shape(T, E, k)) return st;
+  if (moe_status_t st = check_weight_shape(H, I, weight_layout, "moe_ffn_forward_noalloc")) return st;
+  // The size limit is checked before anything touches the device, so an oversized call fails the
+  // same way on any host.
+  const FfnLayout L = ffn_layout(T, H, I, E, k, weight_layout == MOE_LAYOUT_PACKED);
+  if (L.total > scratch_capacity())
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_ffn_forward_noalloc: these sizes need %zu B of scratch, above the library's static %zu B "
+                "(use moe_ffn_forward with a caller workspace)",
+                L.total, scratch_capacity());
+  if (T == 0) return ok();
+  if (moe_status_t st = check_ffn_ptrs(x, w13_q, w13_s, w2_q, w2_s, weight_layout, y, topk_ids_out, topk_w_out,
+                                       nullptr, "moe_ffn_forward_noalloc", false))
+    return st;
+  if (!router_logits) return fail(MOE_ERR_INVALID_ARG, "moe_ffn_forward_noalloc: NULL router_logits");
+  if (!aligned4(router_logits))
+    return fail(MOE_ERR_MISALIGNED, "moe_ffn_forward_noalloc: router_logits need 4-byte alignment");
+  char* ws = nullptr;
+  if (moe_status_t st = scratch_of_current_device(&ws)) return st;
+  return run_ffn(x, router_logits, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, weight_layout, y, topk_ids_out,
+                 topk_w_out, ws, L, SharedW{}, nullptr, (hipStream_t)stream);
 }
 
 size_t moe_dense_ffn_workspace_bytes(int32_t T, int32_t H, int32_t I) {

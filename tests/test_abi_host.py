@@ -369,3 +369,21 @@ def test_w4a8_entry_points_reject(lib):
     assert fw(ws=ws - 1) == -4
     assert fw(x=_ptr(FAKE + 2)) == -3
     assert fw(T=0) == 0
+
+
+def test_noalloc_entry_point_rejects_sizes_beyond_its_scratch(lib):
+    """The entry point without allocation checks its fixed scratch size on the host, before any
+    device call, so an oversized layer fails the same way with or without a GPU."""
+    assert moe.moe_ffn_noalloc_scratch_bytes() == 64 << 20
+    # the 800-token, 256-expert layer fits; the 4096-token, 8-expert one (about 215 MB) does not
+    assert moe.moe_ffn_workspace_bytes(800, 2048, 512, 256, 8) <= moe.moe_ffn_noalloc_scratch_bytes()
+    assert moe.moe_ffn_workspace_bytes(4096, 4096, 14336, 8, 2) > moe.moe_ffn_noalloc_scratch_bytes()
+    P = _ptr(FAKE)
+    st = lib.moe_ffn_forward_noalloc(P, P, 4096, 4096, 14336, 8, 2, P, P, P, P, moe.MOE_LAYOUT_PACKED, P, None,
+                                     None, None)
+    assert st == -4 and b"static" in lib.moe_last_error()
+    # shape errors come first, as in moe_ffn_forward
+    st = lib.moe_ffn_forward_noalloc(P, P, 4, 2048, 512, 8, 9, P, P, P, P, 0, P, None, None, None)
+    assert st == -1
+    # an empty batch is a valid no-op that needs no device
+    assert lib.moe_ffn_forward_noalloc(P, P, 0, 2048, 512, 8, 2, P, P, P, P, 0, P, None, None, None) == 0
