@@ -32,6 +32,7 @@ MOE_ACT_TILED = 1
 MOE_IN_BF16 = 0
 MOE_IN_F32 = 1
 MOE_OUT_F8 = 2
+MOE_OUT_F16E = 3
 
 _lib = None
 
@@ -60,8 +61,8 @@ def load() -> ctypes.CDLL:
         "moe_align_workspace_bytes": ([I32, I32, I32], SZ),
         "moe_align": ([P, I32, I32, I32, I32, P, P, P, P, P, I32, P, P, SZ, P], I32),
         "moe_w4_prepack": ([P, P, I32, I32, I32, P, P, P], I32),
-        "moe_grouped_gemm_w4a16": ([P, P, I32, P, P, I32, I32, I32, I32, P, I32, P, I32, I32, P, I32, P], I32),
-        "moe_combine": ([P, P, P, P, I32, I32, I32, P, P], I32),
+        "moe_grouped_gemm_w4a16": ([P, P, I32, P, P, I32, I32, I32, I32, P, I32, P, I32, I32, P, I32, P, P], I32),
+        "moe_combine": ([P, I32, P, P, P, P, I32, I32, I32, P, P], I32),
         "moe_router_logits": ([P, P, I32, I32, I32, P, P], I32),
         "moe_dense_ffn_workspace_bytes": ([I32, I32, I32], SZ),
         "moe_dense_ffn_w4a16": ([P, I32, I32, I32, P, P, P, P, I32, P, P, SZ, P], I32),
@@ -210,33 +211,45 @@ def moe_w4_prepack(w_q, w_s, packed_q=None, packed_s=None, stream=None):
 
 def moe_grouped_gemm_w4a16(A, a_row_of, a_row_div: int, Wq, Ws, tiles, max_tiles: int, num_tiles,
                            block_m: int, epilogue: int, out_rows: int, out_dtype: int = MOE_OUT_BF16,
-                           C=None, stream=None, weight_layout: int = MOE_LAYOUT_CANONICAL):
-    """Grouped W4A16 GEMM over the tile list; returns C ([out_rows, N] or [out_rows, N/2])."""
+                           C=None, stream=None, weight_layout: int = MOE_LAYOUT_CANONICAL, C_exp=None):
+    """Grouped W4A16 GEMM over the tile list; returns C ([out_rows, N] or [out_rows, N/2]), or
+    (C fp16, C_exp uint8 [out_rows, ceil(N/16)]) for MOE_OUT_F16E."""
     _req(A, "16bit", "A")
     _req(Wq, torch.uint8, "Wq")
     E, N, K2 = Wq.shape
     K = 2 * K2
     ncols = N // 2 if epilogue == MOE_EPI_SILU_MUL else N
     if C is None:
-        dt = torch.float32 if out_dtype == MOE_OUT_F32 else torch.bfloat16
+        dt = {MOE_OUT_F32: torch.float32, MOE_OUT_F16E: torch.float16}.get(out_dtype, torch.bfloat16)
         C = torch.empty((out_rows, ncols), dtype=dt, device=A.device)
+    if out_dtype == MOE_OUT_F16E and C_exp is None:
+        C_exp = torch.empty((out_rows, (ncols + 15) // 16), dtype=torch.uint8, device=A.device)
     _check(load().moe_grouped_gemm_w4a16(_p(A), _p(a_row_of), a_row_div, _p(Wq), _p(Ws), weight_layout, E, N, K,
                                          _p(tiles),
-                                         max_tiles, _p(num_tiles), block_m, epilogue, _p(C), out_dtype,
+                                         max_tiles, _p(num_tiles), block_m, epilogue, _p(C), out_dtype, _p(C_exp),
                                          _stream(stream)))
-    return C
+    return (C, C_exp) if out_dtype == MOE_OUT_F16E else C
 
 
-def moe_combine(O, inv_perm, topk_w, y=None, stream=None, shared=None):
-    """O fp32 [T*k, H], inv_perm int32 [T*k], topk_w fp32 [T, k] (+ shared fp32 [T, H]) -> y bf16 [T, H]."""
-    _req(O, torch.float32, "O")
+def moe_combine(O, inv_perm, topk_w, y=None, stream=None, shared=None, O_exp=None):
+    """O fp32 [T*k, H], or fp16 [T*k, H] with exponent bytes O_exp [T*k, H/16] (MOE_OUT_F16E),
+    inv_perm int32 [T*k], topk_w fp32 [T, k] (+ shared fp32 [T, H]) -> y bf16 [T, H]."""
+    if O.dtype == torch.float16:
+        if O_exp is None:
+            raise ValueError("fp16 O needs its exponent bytes O_exp")
+        _req(O_exp, torch.uint8, "O_exp")
+        o_dtype = MOE_OUT_F16E
+    else:
+        _req(O, torch.float32, "O")
+        o_dtype = MOE_OUT_F32
     if shared is not None:
         _req(shared, torch.float32, "shared")
     T, k = topk_w.shape
     H = O.shape[1]
     if y is None:
         y = torch.empty((T, H), dtype=torch.bfloat16, device=O.device)
-    _check(load().moe_combine(_p(O), _p(inv_perm), _p(topk_w), _p(shared), T, k, H, _p(y), _stream(stream)))
+    _check(load().moe_combine(_p(O), o_dtype, _p(O_exp) if o_dtype == MOE_OUT_F16E else None, _p(inv_perm),
+                              _p(topk_w), _p(shared), T, k, H, _p(y), _stream(stream)))
     return y
 
 

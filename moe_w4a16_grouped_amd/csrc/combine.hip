@@ -4,17 +4,61 @@
 // outputs back.  Slots are summed in fp32 in ascending order (deterministic, no atomics), then the
 // shared expert's output is added if given (the Atlas page, section "KV Cache量化、MTP推测解码和调试
 // 工具链", lists a shared expert output beside the routed output), and y is rounded to bf16 once;
-// every element of y is written.
+// every element of y is written.  O is the down projection's output, fp32 or fp16 with a
+// power-of-two exponent per row and 16 columns (the layer's own launches use the latter).
 #include "launch.h"
 #include "moe_common.h"
 
 namespace moe {
 
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ O,
+// One slot row's 8 values at column block v as loaded: fp32 O (two 16-byte halves), or fp16 O
+// (one 16-byte load) and its exponent byte.
+struct RowRaw {
+  u32x4 a, b;
+  uint32_t ex;
+};
+
+template <bool O16>
+__device__ __forceinline__ RowRaw load_row(const void* O, const uint8_t* O_exp, int r, int H, int v) {
+  RowRaw x;
+  if (O16) {
+    x.a = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(O) + (size_t)r * H)[v];
+    x.b = u32x4{0u, 0u, 0u, 0u};
+    x.ex = O_exp[(size_t)r * (H / 16) + v / 2];
+  } else {
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const float*>(O) + (size_t)r * H) + 2 * v;
+    x.a = src[0];
+    x.b = src[1];
+    x.ex = 0;
+  }
+  return x;
+}
+
+// The 8 values in fp32: fp16 * 2^exp is exact in fp32.
+template <bool O16>
+__device__ __forceinline__ void row_values(const RowRaw& x, float (&o)[8]) {
+  if (O16) {
+    const float f = __uint_as_float((127u + x.ex) << 23);  // 2^ex, ex <= 113
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = f16_bits_to_f32(x.a[i] & 0xFFFFu) * f;
+      o[2 * i + 1] = f16_bits_to_f32(x.a[i] >> 16) * f;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[i] = __uint_as_float(x.a[i]);
+      o[4 + i] = __uint_as_float(x.b[i]);
+    }
+  }
+}
+
+template <bool O16>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ O, const uint8_t* __restrict__ O_exp,
                                                       const int32_t* __restrict__ inv_perm,
                                                       const float* __restrict__ w,
-                                                      const float* __restrict__ shared, int T, int k, int H,
-                                                      uint16_t* __restrict__ y) {
+                                                      const float* __restrict__ shared, int shared_o_row0, int T,
+                                                      int k, int H, uint16_t* __restrict__ y) {
   const int t = blockIdx.x;
   const int nvec = H / 8;
   for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
@@ -31,33 +75,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         r[j] = inv_perm[(size_t)t * k + s + j];
         ws[j] = w[(size_t)t * k + s + j];
       }
-      f32x4 a[8], b[8];
+      RowRaw x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = load_row<O16>(O, O_exp, r[j], H, v);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(O + (size_t)r[j] * H) + 2 * v;
-        a[j] = src[0];
-        b[j] = src[1];
+        float o[8];
+        row_values<O16>(x[j], o);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(ws[j], o[i], acc[i]);
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[i] = fmaf(ws[j], a[j][i], acc[i]);
-          acc[4 + i] = fmaf(ws[j], b[j][i], acc[4 + i]);
-        }
     }
     for (; s < k; ++s) {
       const int r = inv_perm[(size_t)t * k + s];
       const float ws = w[(size_t)t * k + s];
-      const f32x4* src = reinterpret_cast<const f32x4*>(O + (size_t)r * H) + 2 * v;
-      const f32x4 a = src[0], b = src[1];
+      const RowRaw x = load_row<O16>(O, O_exp, r, H, v);
+      float o[8];
+      row_values<O16>(x, o);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[i] = fmaf(ws, a[i], acc[i]);
-        acc[4 + i] = fmaf(ws, b[i], acc[4 + i]);
-      }
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(ws, o[i], acc[i]);
     }
-    if (shared) {
+    if (shared_o_row0 >= 0) {  // the shared expert's output is row shared_o_row0 + t of O
+      const RowRaw x = load_row<O16>(O, O_exp, shared_o_row0 + t, H, v);
+      float o[8];
+      row_values<O16>(x, o);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += o[i];
+    } else if (shared) {
       const f32x4* src = reinterpret_cast<const f32x4*>(shared + (size_t)t * H) + 2 * v;
       const f32x4 a = src[0], b = src[1];
 #pragma unroll
@@ -74,11 +118,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-hipError_t launch_combine(const float* O, const int32_t* inv_perm, const float* w, const float* shared, int T,
-                          int k, int H, uint16_t* y, hipStream_t stream) {
+hipError_t launch_combine(const void* O, const uint8_t* O_exp, const int32_t* inv_perm, const float* w,
+                          const float* shared, int shared_o_row0, int T, int k, int H, uint16_t* y,
+                          hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   const int threads = H / 8 >= 256 ? 256 : ((H / 8 + 63) / 64) * 64;
-  combine_kernel<<<T, threads, 0, stream>>>(O, inv_perm, w, shared, T, k, H, y);
+  if (O_exp)
+    combine_kernel<true><<<T, threads, 0, stream>>>(O, O_exp, inv_perm, w, shared, shared_o_row0, T, k, H, y);
+  else
+    combine_kernel<false><<<T, threads, 0, stream>>>(O, O_exp, inv_perm, w, shared, shared_o_row0, T, k, H, y);
   return hipGetLastError();
 }
 

@@ -106,15 +106,65 @@ __device__ __forceinline__ void column_of(const GemmArgs& p, int col0, int ni, i
   if (!valid) n = 0;
 }
 
-template <int EPI, bool OUT_F32, int MI, int NI>
+// Output kinds of the NONE epilogue (GemmArgs::out_f32): 0 bf16, 1 fp32, 2 fp16 with a power-of-two
+// exponent per row and 16-column block (kOutF16Exp).  With kind 2, element (r, n) is
+// fp16(C[r, n]) * 2^exp[r, n / 16]: the exponent is 0 unless the block's row holds a magnitude of at
+// least 2^15 (or a non-finite value), in which case the row segment is scaled by 2^-exp first so that
+// its largest finite magnitude lies below 2^15.  fp16 keeps 11 significant bits where bf16 keeps 8;
+// the exponent keeps any fp32 range representable.
+constexpr int kOutBf16 = 0, kOutF32 = 1, kOutF16Exp = 2;
+
+// One row of a 16 x 16 MFMA output block lives in the 16 lanes of a quarter (one lane per column):
+// the largest finite magnitude over those lanes.
+__device__ __forceinline__ float quarter_max_finite(float v) {
+  float m = (fabsf(v) <= 3.0e38f) ? fabsf(v) : 0.f;
+  m = fmaxf(m, __shfl_xor(m, 1));
+  m = fmaxf(m, __shfl_xor(m, 2));
+  m = fmaxf(m, __shfl_xor(m, 4));
+  m = fmaxf(m, __shfl_xor(m, 8));
+  return m;
+}
+
+template <int EPI, int OUT, int MI, int NI>
 __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x4 (&acc)[MI][NI], int row_base, int row0,
                                            int rows, int q, const int (&ncol)[NI], const bool (&nvalid)[NI]) {
   const int N = p.N;
+  bool scaled = false;  // kOutF16Exp: some row segment of this wave needs a nonzero exponent
+  if (EPI != MOE_EPI_SILU_MUL && OUT == kOutF16Exp) {
+    bool big = false;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) big |= !(fabsf(acc[mi][ni][r]) < 32768.f) && nvalid[ni];
+    scaled = __ballot(big) != 0ull;
+  }
+  const int l16 = threadIdx.x & 15;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = row_base + mi * 16 + q * 4 + r;
+      if (EPI != MOE_EPI_SILU_MUL && OUT == kOutF16Exp) {
+        // every lane takes part in the quarter reductions, whatever its row
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          float v = nvalid[ni] ? acc[mi][ni][r] : 0.f;
+          int ex = 0;
+          if (scaled) {
+            const float m = quarter_max_finite(v);
+            if (m >= 32768.f) ex = ((int)((__float_as_uint(m) >> 23) & 0xFF) - 127) - 14;
+            v *= __uint_as_float((uint32_t)(127 - ex) << 23);  // exact: 2^-ex, ex <= 113
+          }
+          if (row < rows && nvalid[ni]) {
+            const size_t orow = (size_t)(row0 + row);
+            static_cast<uint16_t*>(p.C)[orow * N + ncol[ni]] = f32_to_f16_bits(v);
+            if (l16 == 0) p.C_exp[orow * (size_t)((N + 15) / 16) + ncol[ni] / 16] = (uint8_t)ex;
+          }
+        }
+        continue;
+      }
       if (row >= rows) continue;
       const size_t orow = (size_t)(row0 + row);
       if (EPI == MOE_EPI_SILU_MUL) {
@@ -129,7 +179,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x4 (&acc)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
           if (!nvalid[ni]) continue;
-          if (OUT_F32) static_cast<float*>(p.C)[orow * N + ncol[ni]] = acc[mi][ni][r];
+          if (OUT == kOutF32) static_cast<float*>(p.C)[orow * N + ncol[ni]] = acc[mi][ni][r];
           else static_cast<uint16_t*>(p.C)[orow * N + ncol[ni]] = f32_to_bf16_bits(acc[mi][ni][r]);
         }
       }
@@ -320,7 +370,7 @@ constexpr int kLDA = kBK + 8;  // padded LDS activation row of the tiled kernel 
 // One BM x BN output tile (expert e, permuted rows [row0, row0 + rows), N block nb) of the tiled
 // kernel; p is the tile's view of the arguments and sRow already holds the activation row of each
 // tile row (padding rows repeat row 0); it is published by the barrier before the first K step.
-template <int BM, int BN, int WAVES_M, int PF, int EPI, bool OUT_F32, int LAYOUT>
+template <int BM, int BN, int WAVES_M, int PF, int EPI, int OUT_F32, int LAYOUT>
 __device__ __forceinline__ void tiled_tile(const GemmArgs& p, int e, int row0, int rows, int nb,
                                            uint16_t (&sA)[2][BM * kLDA], const int32_t (&sRow)[BM]) {
   constexpr int WAVES_N = 4 / WAVES_M;
@@ -442,7 +492,7 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& p, int e, int row0, i
 }
 
 // RNJ > 0: the launch runs the routing prologue (route_token over 64 * RNJ experts per lane group).
-template <int BM, int BN, int WAVES_M, int PF, int EPI, bool OUT_F32, int LAYOUT, int RNJ = 0>
+template <int BM, int BN, int WAVES_M, int PF, int EPI, int OUT_F32, int LAYOUT, int RNJ = 0>
 __global__ __launch_bounds__(256) void gemm_w4a16_tiled(GemmArgs p0) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kLDA];
   __shared__ int32_t sRow[BM];
@@ -478,7 +528,7 @@ __global__ __launch_bounds__(256) void gemm_w4a16_tiled(GemmArgs p0) {
 // (16-byte loads, rows gathered through a_row_of; padding rows repeat the tile's first row, which
 // the load coalescer merges), so the main loop has no LDS traffic and no barrier.  The KW partial
 // sums are reduced through LDS once per tile, in wave order.
-template <int BM, int BN, int PF, int EPI, bool OUT_F32, int LAYOUT, int KW = 4, int RNJ = 0>
+template <int BM, int BN, int PF, int EPI, int OUT_F32, int LAYOUT, int KW = 4, int RNJ = 0>
 __global__ __launch_bounds__(64 * KW) void gemm_w4a16_sk(GemmArgs p0) {
   constexpr int MI = BM / 16, NI = BN / 16;
   static_assert(MI >= 1 && MI <= 2 && NI >= 1, "tile shape");
@@ -644,7 +694,7 @@ constexpr int kMmBM = 128, kMmBN = 256;
 constexpr int kMmStage = kMmBM * 256 + (kMmBN / 16) * 1024 + (kMmBN / 16) * 128;  // A + codes + scales
 
 // One 128 x 256 output tile (tile list entry `tile`, N block `nb`) of the large-tile kernel.
-template <int EPI, bool OUT_F32, int NSTAGE>
+template <int EPI, int OUT_F32, int NSTAGE>
 __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, uint8_t (&smem)[NSTAGE * kMmStage],
                                         int32_t (&sRow)[kMmBM]) {
   constexpr int BM = kMmBM, BN = kMmBN, MI = 4, NI = 4;
@@ -798,7 +848,7 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, ui
   store_tile<EPI, OUT_F32, MI, NI>(p, acc, wm * 64, row0, rows, q, ncol, nvalid);
 }
 
-template <int EPI, bool OUT_F32, int NSTAGE>
+template <int EPI, int OUT_F32, int NSTAGE>
 __global__ __launch_bounds__(512) void gemm_w4a16_mm(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * kMmStage];
   __shared__ int32_t sRow[kMmBM];
@@ -827,7 +877,7 @@ static dim3 grid_of(const GemmArgs& a, int bn) {
 
 template <int BM, int BN, int WAVES_M, int PF>
 struct Tiled {
-  template <int EPI, bool F32, int LAYOUT, int RNJ = 0>
+  template <int EPI, int F32, int LAYOUT, int RNJ = 0>
   static hipError_t run(const GemmArgs& a, hipStream_t s) {
     gemm_w4a16_tiled<BM, BN, WAVES_M, PF, EPI, F32, LAYOUT, RNJ><<<grid_of(a, BN), 256, 0, s>>>(a);
     return hipGetLastError();
@@ -836,7 +886,7 @@ struct Tiled {
 
 template <int BM, int BN, int PF, int KW = 4>
 struct SplitK {
-  template <int EPI, bool F32, int LAYOUT, int RNJ = 0>
+  template <int EPI, int F32, int LAYOUT, int RNJ = 0>
   static hipError_t run(const GemmArgs& a, hipStream_t s) {
     gemm_w4a16_sk<BM, BN, PF, EPI, F32, LAYOUT, KW, RNJ><<<grid_of(a, BN), 64 * KW, 0, s>>>(a);
     return hipGetLastError();
@@ -850,7 +900,7 @@ struct SplitK {
 // against 10.4 / 19.7 us for 64-column blocks split 8 ways.
 constexpr int kSplitKMaxTiles = 32;
 
-template <class Cfg, int EPI, bool F32>
+template <class Cfg, int EPI, int F32>
 static hipError_t by_layout(const GemmArgs& a, hipStream_t s) {
   switch (layout_of(a)) {
     case kPacked: return Cfg::template run<EPI, F32, kPacked>(a, s);
@@ -878,12 +928,13 @@ static hipError_t routed(const GemmArgs& a, hipStream_t s) {
 
 template <class Cfg>
 static hipError_t by_variant(const GemmArgs& a, hipStream_t s) {
-  if (a.epilogue == MOE_EPI_SILU_MUL) return by_layout<Cfg, MOE_EPI_SILU_MUL, false>(a, s);
-  if (a.out_f32) return by_layout<Cfg, MOE_EPI_NONE, true>(a, s);
-  return by_layout<Cfg, MOE_EPI_NONE, false>(a, s);
+  if (a.epilogue == MOE_EPI_SILU_MUL) return by_layout<Cfg, MOE_EPI_SILU_MUL, kOutBf16>(a, s);
+  if (a.out_f32 == kOutF16Exp) return by_layout<Cfg, MOE_EPI_NONE, kOutF16Exp>(a, s);
+  if (a.out_f32 == kOutF32) return by_layout<Cfg, MOE_EPI_NONE, kOutF32>(a, s);
+  return by_layout<Cfg, MOE_EPI_NONE, kOutBf16>(a, s);
 }
 
-template <int EPI, bool F32>
+template <int EPI, int F32>
 static hipError_t launch_mm(const GemmArgs& a, hipStream_t s) {
   const int ncols = EPI == MOE_EPI_SILU_MUL ? a.N / 2 : a.N;
   const int bcols = EPI == MOE_EPI_SILU_MUL ? 128 : 256;
@@ -896,9 +947,10 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t strea
   if (a.max_tiles <= 0) return hipSuccess;
   // (packed SiLU*mul needs N % 32 == 0, checked by the caller: up rows start a 16-row block)
   if (block_m == 128 && a.packed) {
-    if (a.epilogue == MOE_EPI_SILU_MUL) return launch_mm<MOE_EPI_SILU_MUL, false>(a, stream);
-    if (a.out_f32) return launch_mm<MOE_EPI_NONE, true>(a, stream);
-    return launch_mm<MOE_EPI_NONE, false>(a, stream);
+    if (a.epilogue == MOE_EPI_SILU_MUL) return launch_mm<MOE_EPI_SILU_MUL, kOutBf16>(a, stream);
+    if (a.out_f32 == kOutF16Exp) return launch_mm<MOE_EPI_NONE, kOutF16Exp>(a, stream);
+    if (a.out_f32 == kOutF32) return launch_mm<MOE_EPI_NONE, kOutF32>(a, stream);
+    return launch_mm<MOE_EPI_NONE, kOutBf16>(a, stream);
   }
   switch (block_m) {
     case 16:

@@ -29,6 +29,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;  // v_cvt_f16_f32: round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
 // Eight E2M1 codes (one dword, element 0 in the low nibble) -> eight exact bf16 values.
 // The hardware FP4 converter is used with a unit scale, so every code lands exactly on its E2M1
 // value (0, ±0.5, ±1, ±1.5, ±2, ±3, ±4, ±6); the group scale is applied later in fp32.

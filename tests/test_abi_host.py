@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     assert lib.moe_status_string(0) == b"MOE_OK"
     for code, name in [(-1, b"MOE_ERR_INVALID_ARG"), (-2, b"MOE_ERR_UNSUPPORTED_SHAPE"), (-3, b"MOE_ERR_MISALIGNED"),
                        (-4, b"MOE_ERR_WORKSPACE"), (-5, b"MOE_ERR_HIP")]:
@@ -54,7 +54,7 @@ def test_pure_size_queries(lib):
     assert moe.moe_align_workspace_bytes(8192, 10, 512) == 20 * 4 * 512 * 4
     ws = moe.moe_ffn_workspace_bytes(800, 2048, 512, 256, 8)
     R = 800 * 8
-    assert ws >= R * 512 * 2 + R * 2048 * 4  # h (bf16) and the down output (fp32) at least
+    assert ws >= R * 512 * 2 + R * 2048 * 2 + R * 2048 // 16  # h (bf16), the down output (fp16) and its exponents
     assert moe.moe_ffn_workspace_bytes(4, 2048, 512, 8, 9) == 0    # k > E
 
 
@@ -70,7 +70,7 @@ def test_block_m_choice():
     # one workspace size serves both layouts: the tile list is sized for the smaller tile height
     R, E = 4096 * 2, 8
     ws = moe.moe_ffn_workspace_bytes(4096, 4096, 14336, E, 2)
-    assert ws >= R * 14336 * 2 + R * 4096 * 4 + moe.moe_max_tiles(4096, 2, E, 64) * 12
+    assert ws >= R * 14336 * 2 + R * 4096 * 2 + R * 4096 // 16 + moe.moe_max_tiles(4096, 2, E, 64) * 12
 
 
 FAKE = 1 << 20  # an aligned, never-dereferenced pointer value: validation fails before any launch
@@ -121,7 +121,7 @@ def test_grouped_gemm_rejects(lib):
         a = dict(args, **kw)
         return lib.moe_grouped_gemm_w4a16(a["A"], a["aro"], a["div"], a["Wq"], a["Ws"], a["lay"], a["E"], a["N"],
                                           a["K"], a["tiles"], a["mt"], a["nt"], a["bm"], a["epi"], a["C"], a["out"],
-                                          None)
+                                          a.get("cexp"), None)
 
     assert call(K=48) == -2            # K not a multiple of 32
     assert call(bm=24) == -2           # unsupported tile height
@@ -137,6 +137,9 @@ def test_grouped_gemm_rejects(lib):
     assert call(lay=1, N=200) == -2    # packed needs N % 16 == 0
     assert call(lay=1, N=80, epi=1) == -2  # packed SiLU*mul needs N % 32 == 0 (up rows start a block)
     assert call(lay=1, Ws=_ptr(FAKE + 2)) == -3  # packed scales need 8-byte alignment
+    assert call(out=3) == -1                     # fp16 with exponents needs its exponent array
+    assert call(out=3, epi=1, cexp=f) == -1      # ... and the plain epilogue
+    assert call(out=4) == -1                     # unknown output kind
 
 
 def test_prepack_rejects(lib):
@@ -151,9 +154,13 @@ def test_prepack_rejects(lib):
 
 def test_combine_and_forward_reject(lib):
     f = _ptr(FAKE)
-    assert lib.moe_combine(f, f, f, None, 4, 2, 12, f, None) == -2        # H % 8
-    assert lib.moe_combine(f, f, f, None, 0, 2, 16, f, None) == 0         # T == 0
-    assert lib.moe_combine(_ptr(FAKE + 4), f, f, None, 4, 2, 16, f, None) == -3
+    F32, F16E = moe.MOE_OUT_F32, moe.MOE_OUT_F16E
+    assert lib.moe_combine(f, F32, None, f, f, None, 4, 2, 12, f, None) == -2   # H % 8
+    assert lib.moe_combine(f, F16E, f, f, f, None, 4, 2, 24, f, None) == -2     # fp16 O: H % 16
+    assert lib.moe_combine(f, F32, None, f, f, None, 0, 2, 16, f, None) == 0    # T == 0
+    assert lib.moe_combine(_ptr(FAKE + 4), F32, None, f, f, None, 4, 2, 16, f, None) == -3
+    assert lib.moe_combine(f, F16E, None, f, f, None, 4, 2, 16, f, None) == -1  # fp16 O needs exponents
+    assert lib.moe_combine(f, 0, None, f, f, None, 4, 2, 16, f, None) == -1     # bf16 O is not accepted
     ws = moe.moe_ffn_workspace_bytes(16, 256, 128, 8, 2)
     fw = lambda **kw: lib.moe_ffn_forward(kw.get("x", f), f, kw.get("T", 16), kw.get("H", 256), kw.get("I", 128),
                                           kw.get("E", 8), kw.get("k", 2), f, f, f, f, kw.get("lay", 0), f, None,
@@ -375,7 +382,7 @@ def test_noalloc_entry_point_rejects_sizes_beyond_its_scratch(lib):
     """The entry point without allocation checks its fixed scratch size on the host, before any
     device call, so an oversized layer fails the same way with or without a GPU."""
     assert moe.moe_ffn_noalloc_scratch_bytes() == 64 << 20
-    # the 800-token, 256-expert layer fits; the 4096-token, 8-expert one (about 215 MB) does not
+    # the 800-token, 256-expert layer fits; the 4096-token, 8-expert one (about 305 MB) does not
     assert moe.moe_ffn_workspace_bytes(800, 2048, 512, 256, 8) <= moe.moe_ffn_noalloc_scratch_bytes()
     assert moe.moe_ffn_workspace_bytes(4096, 4096, 14336, 8, 2) > moe.moe_ffn_noalloc_scratch_bytes()
     P = _ptr(FAKE)

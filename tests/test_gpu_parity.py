@@ -227,8 +227,15 @@ def test_grouped_gemm_split_k_gate_up(I, H):
         np.testing.assert_array_equal(Cp.view(torch.int16).cpu().numpy(), C.view(torch.int16).cpu().numpy())
 
 
+def f16e_to_f64(C, Ce):
+    """fp16 values with per-(row, 16 columns) exponent bytes -> float64."""
+    v = C.float().cpu().numpy().astype(np.float64)
+    e = Ce.cpu().numpy().astype(np.int64)
+    return v * np.ldexp(1.0, np.repeat(e, 16, axis=1)[:, :v.shape[1]])
+
+
 @pytest.mark.parametrize("bm", [16, 64, 128])
-@pytest.mark.parametrize("out_dtype", [moe.MOE_OUT_F32, moe.MOE_OUT_BF16])
+@pytest.mark.parametrize("out_dtype", [moe.MOE_OUT_F32, moe.MOE_OUT_BF16, moe.MOE_OUT_F16E])
 @pytest.mark.parametrize("N,K", [(256, 128), (200, 160), (48, 1056)])
 def test_grouped_gemm_plain(bm, out_dtype, N, K):
     E, T, k = 6, 90, 2
@@ -246,13 +253,80 @@ def test_grouped_gemm_plain(bm, out_dtype, N, K):
     torch.cuda.synchronize()
     ra = oracle.align(rid, E, bm)
     ref = oracle.grouped_proj(A, None, 1, Wq, Ws, ra["offsets"])
-    got = C.cpu().numpy().astype(np.float64) if out_dtype == moe.MOE_OUT_F32 else gu.host_bf16_to_f64(C)
+    if out_dtype == moe.MOE_OUT_F16E:
+        C, Ce = C
+        assert np.all(Ce.cpu().numpy() == 0)  # magnitudes of order 1: no row segment is scaled
+        got = f16e_to_f64(C, Ce)
+    else:
+        got = C.cpu().numpy().astype(np.float64) if out_dtype == moe.MOE_OUT_F32 else gu.host_bf16_to_f64(C)
+    # bf16 x E2M1 products are exact in fp32; the fp32 summation takes at most (32 + K/32) roundings
+    # along any path, so |err| <= (64 + K/32) * 2^-24 * sum|terms|; an fp16 output adds one rounding
+    # (2^-11 relative, 2^-25 absolute below fp16's normal range).
+    ref_abs = oracle.grouped_proj(A & 0x7FFF, None, 1, Wq & 0x77, Ws, ra["offsets"])
+    acc_err = (64 + K / 32) * 2.0 ** -24 * ref_abs
     if out_dtype == moe.MOE_OUT_F32:
-        # bf16 x E2M1 products are exact in fp32; the only error is fp32 summation: at most
-        # (32 + K/32) roundings along any path, so |err| <= (64 + K/32) * 2^-24 * sum|terms|.
-        ref_abs = oracle.grouped_proj(A & 0x7FFF, None, 1, Wq & 0x77, Ws, ra["offsets"])
-        assert np.all(np.abs(got - ref) <= (64 + K / 32) * 2.0 ** -24 * ref_abs)
+        assert np.all(np.abs(got - ref) <= acc_err)
+    elif out_dtype == moe.MOE_OUT_F16E:
+        assert np.all(np.abs(got - ref) <= acc_err + 2.0 ** -11 * (np.abs(ref) + acc_err) + 2.0 ** -25)
     gu.assert_within_tolerance(got, ref, "plain")
+
+
+@pytest.mark.parametrize("bm,layout", [(32, 0), (64, 0), (16, 0), (128, 1)])
+def test_grouped_gemm_f16e_exponents(bm, layout):
+    """Outputs far beyond fp16's range: each row segment of 16 columns holding a magnitude >= 2^15
+    is stored scaled by 2^-exp (its largest magnitude then below 2^15) with exp in its byte; the
+    decoded values stay within the fp32 summation bound plus one fp16 rounding."""
+    E, T, k, N, K = 4, 70, 2, 256, 256
+    rng = np.random.default_rng(bm + 5)
+    logits = rng.standard_normal((T, E), dtype=np.float32)
+    rid, _ = oracle.route(logits, k)
+    R = T * k
+    A = rng.standard_normal((R, K), dtype=np.float32)
+    A[::3] *= 2.0 ** 20  # every third row: outputs around 2^22
+    A[1::7, :8] *= 2.0 ** 40  # a few rows with a huge first group: one segment far above the rest
+    A = mi.f32_to_bf16_bits(A)
+    Wq = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    Ws = mi.f32_to_bf16_bits(rng.uniform(0.005, 0.02, (E, N, K // 32)).astype(np.float32))
+    a = moe.moe_align(gu.dev(rid), E, bm)
+    d_wq, d_ws = gu.dev(Wq), gu.dev(Ws.view(np.int16))
+    if layout:
+        d_wq, d_ws = moe.moe_w4_prepack(d_wq, d_ws)
+    C, Ce = moe.moe_grouped_gemm_w4a16(gu.dev_bf16(A), None, 1, d_wq, d_ws, a["tiles"], a["max_tiles"],
+                                       a["num_tiles"], bm, moe.MOE_EPI_NONE, R, moe.MOE_OUT_F16E, weight_layout=layout)
+    torch.cuda.synchronize()
+    ra = oracle.align(rid, E, bm)
+    ref = oracle.grouped_proj(A, None, 1, Wq, Ws, ra["offsets"])
+    ref_abs = oracle.grouped_proj(A & 0x7FFF, None, 1, Wq & 0x77, Ws, ra["offsets"])
+    ce = Ce.cpu().numpy().astype(np.int64)
+    got = f16e_to_f64(C, Ce)
+    acc_err = (64 + K / 32) * 2.0 ** -24 * ref_abs
+    scale = np.ldexp(1.0, np.repeat(ce, 16, axis=1))
+    assert np.all(np.abs(got - ref) <= acc_err + 2.0 ** -11 * (np.abs(ref) + acc_err) + 2.0 ** -25 * scale)
+    # the exponent is 0 exactly where the segment's largest magnitude stays below 2^15
+    seg_max = np.abs(got).reshape(R, N // 16, 16).max(axis=2)  # (after one fp16 rounding)
+    assert np.all(seg_max[ce > 0] >= 2.0 ** 15 * (1 - 2.0 ** -10)) and np.all(seg_max[ce == 0] <= 2.0 ** 15)
+    assert np.all(np.abs(C.float().cpu().numpy()) <= 2.0 ** 15)
+    assert ce.max() >= 40 and (ce == 0).any()
+
+
+@pytest.mark.parametrize("k", [5, 8, 10, 16])
+def test_combine_f16e_matches_oracle(k):
+    """fp16 O with exponent bytes (the layer's down-projection output): each value is fp16 * 2^exp,
+    exact in fp32, so the bound is that of fp32 O."""
+    T, H = 29, 272
+    rng = np.random.default_rng(7 + k)
+    O16 = rng.standard_normal((T * k, H)).astype(np.float16)
+    ex = np.zeros((T * k, H // 16), np.uint8)
+    ex[::5] = rng.integers(0, 30, (len(ex[::5]), H // 16))
+    inv = rng.permutation(T * k).astype(np.int32)
+    w = rng.uniform(0, 1, (T, k)).astype(np.float32)
+    y = moe.moe_combine(gu.dev(O16), gu.dev(inv), gu.dev(w), O_exp=gu.dev(ex))
+    torch.cuda.synchronize()
+    O = O16.astype(np.float64) * np.ldexp(1.0, np.repeat(ex.astype(np.int64), 16, axis=1))
+    ref = oracle.combine(O, inv, w.astype(np.float64), T, k)
+    terms = oracle.combine(np.abs(O), inv, w.astype(np.float64), T, k)
+    got = gu.host_bf16_to_f64(y)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + (k + 2) * 2.0 ** -23 * terms)
 
 
 @pytest.mark.parametrize("k", [5, 8, 10, 16])
@@ -439,9 +513,9 @@ def _layer_from_entry_points(d, inp, packed):
     R = wl.T * wl.k
     h = moe.moe_grouped_gemm_w4a16(d.x, al["sorted_ids"], wl.k, q13, s13, al["tiles"], al["max_tiles"],
                                    al["num_tiles"], bm, moe.MOE_EPI_SILU_MUL, R, weight_layout=layout)
-    O = moe.moe_grouped_gemm_w4a16(h, None, 1, q2, s2, al["tiles"], al["max_tiles"], al["num_tiles"], bm,
-                                   moe.MOE_EPI_NONE, R, out_dtype=moe.MOE_OUT_F32, weight_layout=layout)
-    y = moe.moe_combine(O, al["inv_perm"], w)
+    O, Oe = moe.moe_grouped_gemm_w4a16(h, None, 1, q2, s2, al["tiles"], al["max_tiles"], al["num_tiles"], bm,
+                                       moe.MOE_EPI_NONE, R, out_dtype=moe.MOE_OUT_F16E, weight_layout=layout)
+    y = moe.moe_combine(O, al["inv_perm"], w, O_exp=Oe)
     torch.cuda.synchronize()
     return y
 
@@ -488,13 +562,19 @@ def test_grouped_gemm_packed_matches_canonical_bits(bm):
             (d.w13_q, d.w13_s, q13, s13, moe.MOE_EPI_SILU_MUL, d.x, a["sorted_ids"], wl.k, moe.MOE_OUT_BF16),
             (d.w2_q, d.w2_s, q2, s2, moe.MOE_EPI_NONE,
              gu.dev_bf16(mi.f32_to_bf16_bits(np.random.default_rng(2).standard_normal((R, wl.I), dtype=np.float32))),
-             None, 1, moe.MOE_OUT_F32)]:
+             None, 1, moe.MOE_OUT_F32),
+            (d.w2_q, d.w2_s, q2, s2, moe.MOE_EPI_NONE,
+             gu.dev_bf16(mi.f32_to_bf16_bits(np.random.default_rng(3).standard_normal((R, wl.I), dtype=np.float32))),
+             None, 1, moe.MOE_OUT_F16E)]:
         c1 = moe.moe_grouped_gemm_w4a16(A, aro, div, wq, ws, a["tiles"], a["max_tiles"], a["num_tiles"], bm, epi, R, od)
         c2 = moe.moe_grouped_gemm_w4a16(A, aro, div, pq, ps, a["tiles"], a["max_tiles"], a["num_tiles"], bm, epi, R, od,
                                         weight_layout=moe.MOE_LAYOUT_PACKED)
         torch.cuda.synchronize()
-        np.testing.assert_array_equal(c1.view(torch.int16 if od == moe.MOE_OUT_BF16 else torch.int32).cpu().numpy(),
-                                      c2.view(torch.int16 if od == moe.MOE_OUT_BF16 else torch.int32).cpu().numpy())
+        if od == moe.MOE_OUT_F16E:
+            np.testing.assert_array_equal(c1[1].cpu().numpy(), c2[1].cpu().numpy())
+            c1, c2 = c1[0], c2[0]
+        view = torch.int32 if od == moe.MOE_OUT_F32 else torch.int16
+        np.testing.assert_array_equal(c1.view(view).cpu().numpy(), c2.view(view).cpu().numpy())
 
 
 # The 128-row large-tile kernel (packed weights, block_m 128) against the canonical 64-row kernel: per
@@ -518,6 +598,7 @@ def test_large_tile_gemm_matches_canonical_bits(T, E, k, H, I, seed):
         projs.append((d.w13_q, d.w13_s, moe.MOE_EPI_SILU_MUL, d.x, "sorted", wl.k, moe.MOE_OUT_BF16))
     if wl.I % 128 == 0:
         projs.append((d.w2_q, d.w2_s, moe.MOE_EPI_NONE, h, None, 1, moe.MOE_OUT_F32))
+        projs.append((d.w2_q, d.w2_s, moe.MOE_EPI_NONE, h, None, 1, moe.MOE_OUT_F16E))
     assert projs
     for (wq, ws, epi, A, aro, div, od) in projs:
         _log(f"large tile T={T} E={E} k={k} H={H} I={I} epi={epi}")
@@ -528,7 +609,10 @@ def test_large_tile_gemm_matches_canonical_bits(T, E, k, H, I, seed):
                                          a128["max_tiles"], a128["num_tiles"], 128, epi, R, od,
                                          weight_layout=moe.MOE_LAYOUT_PACKED)
         torch.cuda.synchronize()
-        view = torch.int16 if od == moe.MOE_OUT_BF16 else torch.int32
+        if od == moe.MOE_OUT_F16E:
+            np.testing.assert_array_equal(out[1].cpu().numpy(), ref[1].cpu().numpy())
+            out, ref = out[0], ref[0]
+        view = torch.int32 if od == moe.MOE_OUT_F32 else torch.int16
         np.testing.assert_array_equal(out.view(view).cpu().numpy(), ref.view(view).cpu().numpy())
 
 
