@@ -825,8 +825,8 @@ def run_w4a16(args):
     wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
     bm = moe.moe_ffn_block_m(T, E, k, layout)
     h = torch.empty((R, I), dtype=torch.bfloat16, device="cuda")
-    O = torch.empty((R, H), dtype=torch.float16, device="cuda")  # the layer's fp16 down output + exponents
-    Oe = torch.empty((R, H // 16), dtype=torch.uint8, device="cuda")
+    O = torch.empty((R, H), dtype=torch.float16, device="cuda")  # the layer's fp16 down output + side values
+    Os = torch.empty((R, H // 8), dtype=torch.float32, device="cuda")
     names = ["route", "align", "gate_up", "down", "combine"]
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     al = None
@@ -842,9 +842,9 @@ def run_w4a16(args):
                                    al["num_tiles"], bm, moe.MOE_EPI_SILU_MUL, R, C=h, weight_layout=layout)
         if e: e[3].record()
         moe.moe_grouped_gemm_w4a16(h, None, 1, q2, s2, al["tiles"], al["max_tiles"], al["num_tiles"], bm,
-                                   moe.MOE_EPI_NONE, R, moe.MOE_OUT_F16E, C=O, C_exp=Oe, weight_layout=layout)
+                                   moe.MOE_EPI_NONE, R, moe.MOE_OUT_F16E, C=O, C_side=Os, weight_layout=layout)
         if e: e[4].record()
-        moe.moe_combine(O, al["inv_perm"], wts, y=y, O_exp=Oe)
+        moe.moe_combine(O, al["inv_perm"], wts, y=y, O_side=Os)
         if e: e[5].record()
     torch.cuda.synchronize()
     kern_us = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in evs]) * 1e3) for j, n in enumerate(names)}

@@ -53,7 +53,7 @@
  * Numerics: E2M1 codes are exact in bf16; each 32-element group is reduced by bf16 MFMA into an
  * fp32 partial that is multiplied by the group's scale in fp32; accumulation is fp32.  h (the
  * SiLU-mul output) is stored as bf16 (round to nearest even), the down-projection output as fp16
- * with a power-of-two exponent per row and 16 columns (MOE_OUT_F16E), and the combine sums the k
+ * with an in-band power-of-two exponent per row and 8 columns (MOE_OUT_F16E), and the combine sums the k
  * slots in fp32 in slot order before one rounding of y to bf16.
  */
 #ifndef MOE_W4A16_H
@@ -80,10 +80,13 @@ typedef int32_t moe_status_t;
 
 #define MOE_OUT_BF16 0
 #define MOE_OUT_F32 1
-/* fp16 with one power-of-two exponent byte per row and 16 columns: element (r, n) is
- * fp16(C[r, n]) * 2^C_exp[r, n/16].  The exponent is 0 unless that row segment holds a magnitude of
- * at least 2^15 or a non-finite value; then the segment is divided by 2^exp (exact) so that its
- * largest finite magnitude lies below 2^15.  The layer writes the down projection this way. */
+/* fp16 with an in-band power-of-two exponent per row and 8-column segment: a segment is 8 plain
+ * fp16 values (round to nearest even) unless it holds a magnitude of at least 2^15 or a non-finite
+ * value; then it is scaled by 2^-exp (exact; its largest finite magnitude lies below 2^15), its
+ * first element is replaced by a marker, the fp16 quiet NaN 0x7E00 | exp, and that element's scaled
+ * value is written to C_side[row, col / 8] (fp32).  Every value of a marked segment is then
+ * (fp16 or side value) * 2^exp.  No unmarked segment holds a NaN.  The layer writes the down
+ * projection this way: half the bytes of fp32, 3 more significant bits than bf16, any fp32 range. */
 #define MOE_OUT_F16E 3
 
 #define MOE_LAYOUT_CANONICAL 0 /* the weight format above */
@@ -179,9 +182,9 @@ moe_status_t moe_w4_prepack(const uint8_t* w_q, const uint16_t* w_s, int32_t E, 
  *              call with a larger capacity; both stay within the same error bound, and identical
  *              arguments always give identical bits.
  *   out_dtype  MOE_OUT_BF16 (round to nearest even), MOE_OUT_F32, or (NONE only) MOE_OUT_F16E:
- *              C fp16 [R_out, N] (round to nearest even) with C_exp uint8 [R_out, ceil(N/16)] (see
- *              MOE_OUT_F16E; C_exp is ignored for the other kinds and may be NULL).  SILU_MUL
- *              requires BF16.
+ *              C fp16 [R_out, N] with side values C_side fp32 [R_out, ceil(N/8)] (see
+ *              MOE_OUT_F16E; C_side is written only for marked segments, and is ignored for the
+ *              other kinds and may then be NULL).  SILU_MUL requires BF16.
  * Shapes: 1 <= E <= MOE_MAX_EXPERTS, N >= 1 (N even for SILU_MUL), K % 32 == 0, K >= 32.
  * Alignment: A, Wq, C 16 bytes; Ws 2 bytes.
  */
@@ -190,21 +193,22 @@ moe_status_t moe_grouped_gemm_w4a16(const uint16_t* A, const int32_t* a_row_of, 
                                     int32_t E, int32_t N,
                                     int32_t K, const int32_t* tiles, int32_t max_tiles,
                                     const int32_t* num_tiles, int32_t block_m, int32_t epilogue,
-                                    void* C, int32_t out_dtype, uint8_t* C_exp, void* stream);
+                                    void* C, int32_t out_dtype, float* C_side, void* stream);
 
 /*
  * Routing-weighted scatter-reduce (combine) [ATOM, 8.1]:
  *   y[t, c] = bf16( sum_{s=0}^{k-1} topk_w[t, s] * O[inv_perm[t*k + s], c]  (+ shared[t, c]) )
  * summed in fp32 in ascending slot order, then the shared term (if any) added, rounded once to bf16.
- *   O          expert outputs in permuted row order, [T*k, H]: o_dtype MOE_OUT_F32 (fp32, O_exp
- *              ignored) or MOE_OUT_F16E (fp16 with exponent bytes O_exp uint8 [T*k, H/16], the
- *              down projection's output kind in the layer; each value is fp16 * 2^exp, exact in fp32);
+ *   O          expert outputs in permuted row order, [T*k, H]: o_dtype MOE_OUT_F32 (fp32, O_side
+ *              ignored) or MOE_OUT_F16E (fp16 with in-band exponents and side values O_side fp32
+ *              [T*k, H/8], the down projection's output kind in the layer; each value decodes
+ *              exactly to fp32);
  *   inv_perm int32 [T*k]; topk_w fp32 [T, k]; shared fp32 [T, H] or NULL (the shared-expert output
  *   of moe_dense_ffn_w4a16, added with weight 1 [Atlas, KV Cache量化、MTP推测解码和调试工具链]);
  *   y bf16 [T, H] out.
- * Shapes: T >= 0, k >= 1, H % 8 == 0 (H % 16 == 0 for MOE_OUT_F16E).
+ * Shapes: T >= 0, k >= 1, H % 8 == 0.
  */
-moe_status_t moe_combine(const void* O, int32_t o_dtype, const uint8_t* O_exp, const int32_t* inv_perm,
+moe_status_t moe_combine(const void* O, int32_t o_dtype, const float* O_side, const int32_t* inv_perm,
                          const float* topk_w, const float* shared, int32_t T, int32_t k, int32_t H, uint16_t* y,
                          void* stream);
 

@@ -211,9 +211,9 @@ def moe_w4_prepack(w_q, w_s, packed_q=None, packed_s=None, stream=None):
 
 def moe_grouped_gemm_w4a16(A, a_row_of, a_row_div: int, Wq, Ws, tiles, max_tiles: int, num_tiles,
                            block_m: int, epilogue: int, out_rows: int, out_dtype: int = MOE_OUT_BF16,
-                           C=None, stream=None, weight_layout: int = MOE_LAYOUT_CANONICAL, C_exp=None):
+                           C=None, stream=None, weight_layout: int = MOE_LAYOUT_CANONICAL, C_side=None):
     """Grouped W4A16 GEMM over the tile list; returns C ([out_rows, N] or [out_rows, N/2]), or
-    (C fp16, C_exp uint8 [out_rows, ceil(N/16)]) for MOE_OUT_F16E."""
+    (C fp16, C_side fp32 [out_rows, ceil(N/8)]) for MOE_OUT_F16E."""
     _req(A, "16bit", "A")
     _req(Wq, torch.uint8, "Wq")
     E, N, K2 = Wq.shape
@@ -222,22 +222,22 @@ def moe_grouped_gemm_w4a16(A, a_row_of, a_row_div: int, Wq, Ws, tiles, max_tiles
     if C is None:
         dt = {MOE_OUT_F32: torch.float32, MOE_OUT_F16E: torch.float16}.get(out_dtype, torch.bfloat16)
         C = torch.empty((out_rows, ncols), dtype=dt, device=A.device)
-    if out_dtype == MOE_OUT_F16E and C_exp is None:
-        C_exp = torch.empty((out_rows, (ncols + 15) // 16), dtype=torch.uint8, device=A.device)
+    if out_dtype == MOE_OUT_F16E and C_side is None:
+        C_side = torch.empty((out_rows, (ncols + 7) // 8), dtype=torch.float32, device=A.device)
     _check(load().moe_grouped_gemm_w4a16(_p(A), _p(a_row_of), a_row_div, _p(Wq), _p(Ws), weight_layout, E, N, K,
                                          _p(tiles),
-                                         max_tiles, _p(num_tiles), block_m, epilogue, _p(C), out_dtype, _p(C_exp),
+                                         max_tiles, _p(num_tiles), block_m, epilogue, _p(C), out_dtype, _p(C_side),
                                          _stream(stream)))
-    return (C, C_exp) if out_dtype == MOE_OUT_F16E else C
+    return (C, C_side) if out_dtype == MOE_OUT_F16E else C
 
 
-def moe_combine(O, inv_perm, topk_w, y=None, stream=None, shared=None, O_exp=None):
-    """O fp32 [T*k, H], or fp16 [T*k, H] with exponent bytes O_exp [T*k, H/16] (MOE_OUT_F16E),
+def moe_combine(O, inv_perm, topk_w, y=None, stream=None, shared=None, O_side=None):
+    """O fp32 [T*k, H], or fp16 [T*k, H] with side values O_side fp32 [T*k, H/8] (MOE_OUT_F16E),
     inv_perm int32 [T*k], topk_w fp32 [T, k] (+ shared fp32 [T, H]) -> y bf16 [T, H]."""
     if O.dtype == torch.float16:
-        if O_exp is None:
-            raise ValueError("fp16 O needs its exponent bytes O_exp")
-        _req(O_exp, torch.uint8, "O_exp")
+        if O_side is None:
+            raise ValueError("fp16 O needs its side values O_side")
+        _req(O_side, torch.float32, "O_side")
         o_dtype = MOE_OUT_F16E
     else:
         _req(O, torch.float32, "O")
@@ -248,7 +248,7 @@ def moe_combine(O, inv_perm, topk_w, y=None, stream=None, shared=None, O_exp=Non
     H = O.shape[1]
     if y is None:
         y = torch.empty((T, H), dtype=torch.bfloat16, device=O.device)
-    _check(load().moe_combine(_p(O), o_dtype, _p(O_exp) if o_dtype == MOE_OUT_F16E else None, _p(inv_perm),
+    _check(load().moe_combine(_p(O), o_dtype, _p(O_side) if o_dtype == MOE_OUT_F16E else None, _p(inv_perm),
                               _p(topk_w), _p(shared), T, k, H, _p(y), _stream(stream)))
     return y
 

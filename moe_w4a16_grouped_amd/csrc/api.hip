@@ -66,7 +66,7 @@ int32_t pick_block_m(int64_t R, int64_t E, bool packed) {
 
 // Workspace carve-up for moe_ffn_forward (each region 256-byte aligned).
 struct FfnLayout {
-  size_t ids, w, counts, offsets, sorted, inv, tiles, ntiles, align_ws, h, o, oexp, total;
+  size_t ids, w, counts, offsets, sorted, inv, tiles, ntiles, align_ws, h, o, oside, total;
   int32_t block_m, max_tiles;
 };
 
@@ -94,8 +94,8 @@ FfnLayout ffn_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, bool
   L.ntiles = take(4);
   L.align_ws = take(moe::align_workspace_bytes((int)R, (int)E));
   L.h = take((size_t)(R + extra_rows) * I * 2);
-  L.o = take((size_t)(R + extra_rows) * H * 2);               // fp16 down output
-  L.oexp = take((size_t)(R + extra_rows) * ((H + 15) / 16));  // its exponent bytes
+  L.o = take((size_t)(R + extra_rows) * H * 2);                  // fp16 down output
+  L.oside = take((size_t)(R + extra_rows) * ((H + 7) / 8) * 4);  // its side values (scaled segments only)
   L.total = off;
   return L;
 }
@@ -191,7 +191,7 @@ moe_status_t run_ffn(const uint16_t* x, const float* router_logits, int32_t T, i
   int32_t* ntiles = reinterpret_cast<int32_t*>(ws + L.ntiles);
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
   uint16_t* o = reinterpret_cast<uint16_t*>(ws + L.o);
-  uint8_t* oexp = reinterpret_cast<uint8_t*>(ws + L.oexp);
+  float* oside = reinterpret_cast<float*>(ws + L.oside);
   const int R = T * k;
   const int packed = weight_layout == MOE_LAYOUT_PACKED;
   const int shared_tiles = sw.w13_q ? (T + L.block_m - 1) / L.block_m : 0;
@@ -223,13 +223,13 @@ moe_status_t run_ffn(const uint16_t* x, const float* router_logits, int32_t T, i
   }
   e = moe::launch_grouped_gemm(g1, L.block_m, s);
   if (e != hipSuccess) return hip_status(e, "gate_up launch");
-  // the down projection writes O as fp16 with per-(row, 16 columns) exponents (kind 2)
+  // the down projection writes O as fp16 with in-band per-(row, 8 columns) exponents (kind 2)
   moe::GemmArgs g2{h, nullptr, 1, w2_q, w2_s, H, I, tiles, ntiles, L.max_tiles + shared_tiles, 0, o, MOE_EPI_NONE, 2,
                    packed, sw.w2_q, sw.w2_s, T, R, 0};
-  g2.C_exp = oexp;
+  g2.C_side = oside;
   e = moe::launch_grouped_gemm(g2, L.block_m, s);
   if (e != hipSuccess) return hip_status(e, "down launch");
-  e = moe::launch_combine(o, oexp, inv, w, shared_out, sw.w13_q ? R : -1, T, k, H, y, s);
+  e = moe::launch_combine(o, oside, inv, w, shared_out, sw.w13_q ? R : -1, T, k, H, y, s);
   return hip_status(e, "combine launch");
 }
 
@@ -428,7 +428,7 @@ moe_status_t moe_grouped_gemm_w4a16(const uint16_t* A, const int32_t* a_row_of, 
                                     int32_t E, int32_t N,
                                     int32_t K, const int32_t* tiles, int32_t max_tiles,
                                     const int32_t* num_tiles, int32_t block_m, int32_t epilogue,
-                                    void* C, int32_t out_dtype, uint8_t* C_exp, void* stream) {
+                                    void* C, int32_t out_dtype, float* C_side, void* stream) {
   if (E < 1 || N < 1 || K < 1 || max_tiles < 0) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_w4a16: need E, N, K >= 1, max_tiles >= 0");
   if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E=%d exceeds %d", E, MOE_MAX_EXPERTS);
   if (K % 32 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "K=%d must be a multiple of 32", K);
@@ -439,8 +439,8 @@ moe_status_t moe_grouped_gemm_w4a16(const uint16_t* A, const int32_t* a_row_of, 
     return fail(MOE_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
   if (epilogue == MOE_EPI_SILU_MUL && (N % 2 != 0 || out_dtype != MOE_OUT_BF16))
     return fail(MOE_ERR_INVALID_ARG, "SILU_MUL needs an even N and bf16 output");
-  if (out_dtype == MOE_OUT_F16E && max_tiles > 0 && !C_exp)
-    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_w4a16: MOE_OUT_F16E needs C_exp");
+  if (out_dtype == MOE_OUT_F16E && max_tiles > 0 && !C_side)
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_w4a16: MOE_OUT_F16E needs C_side");
   if (a_row_of && a_row_div < 1) return fail(MOE_ERR_INVALID_ARG, "a_row_div must be >= 1");
   if (weight_layout != MOE_LAYOUT_CANONICAL && weight_layout != MOE_LAYOUT_PACKED)
     return fail(MOE_ERR_INVALID_ARG, "unknown weight_layout %d", weight_layout);
@@ -457,26 +457,26 @@ moe_status_t moe_grouped_gemm_w4a16(const uint16_t* A, const int32_t* a_row_of, 
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "max_tiles=%d too large", max_tiles);
   moe::GemmArgs a{A, a_row_of, a_row_div, Wq, Ws, N, K, tiles, num_tiles, max_tiles, 0, C, epilogue,
                   out_dtype == MOE_OUT_F16E ? 2 : (out_dtype == MOE_OUT_F32 ? 1 : 0), weight_layout == MOE_LAYOUT_PACKED};
-  a.C_exp = C_exp;
+  a.C_side = C_side;
   return hip_status(moe::launch_grouped_gemm(a, block_m, (hipStream_t)stream), "moe_grouped_gemm_w4a16 launch");
 }
 
-moe_status_t moe_combine(const void* O, int32_t o_dtype, const uint8_t* O_exp, const int32_t* inv_perm,
+moe_status_t moe_combine(const void* O, int32_t o_dtype, const float* O_side, const int32_t* inv_perm,
                          const float* topk_w, const float* shared, int32_t T, int32_t k, int32_t H, uint16_t* y,
                          void* stream) {
   if (T < 0 || k < 1 || H < 1) return fail(MOE_ERR_INVALID_ARG, "moe_combine: need T >= 0, k >= 1, H >= 1");
   if (o_dtype != MOE_OUT_F32 && o_dtype != MOE_OUT_F16E)
     return fail(MOE_ERR_INVALID_ARG, "moe_combine: o_dtype %d must be MOE_OUT_F32 or MOE_OUT_F16E", o_dtype);
-  if (H % 8 != 0 || (o_dtype == MOE_OUT_F16E && H % 16 != 0))
-    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_combine: H=%d must be a multiple of 8 (16 for fp16 O)", H);
+  if (H % 8 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_combine: H=%d must be a multiple of 8", H);
   if ((int64_t)T * k >= kMaxRows) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "T*k must be < 2^26");
   if (T == 0) return ok();
-  if (!O || !inv_perm || !topk_w || !y || (o_dtype == MOE_OUT_F16E && !O_exp))
+  if (!O || !inv_perm || !topk_w || !y || (o_dtype == MOE_OUT_F16E && !O_side))
     return fail(MOE_ERR_INVALID_ARG, "moe_combine: NULL pointer");
-  if (!aligned16(O) || !aligned16(y) || !aligned4(inv_perm) || !aligned4(topk_w) || (shared && !aligned16(shared)))
+  if (!aligned16(O) || !aligned16(y) || !aligned4(inv_perm) || !aligned4(topk_w) || (shared && !aligned16(shared)) ||
+      (O_side && !aligned4(O_side)))
     return fail(MOE_ERR_MISALIGNED, "moe_combine: O, shared and y need 16-byte alignment");
-  return hip_status(moe::launch_combine(O, o_dtype == MOE_OUT_F16E ? O_exp : nullptr, inv_perm, topk_w, shared, -1, T,
-                                        k, H, y, (hipStream_t)stream),
+  return hip_status(moe::launch_combine(O, o_dtype == MOE_OUT_F16E ? O_side : nullptr, inv_perm, topk_w, shared, -1,
+                                        T, k, H, y, (hipStream_t)stream),
                     "moe_combine launch");
 }
 

@@ -4,45 +4,50 @@
 // outputs back.  Slots are summed in fp32 in ascending order (deterministic, no atomics), then the
 // shared expert's output is added if given (the Atlas page, section "KV Cache量化、MTP推测解码和调试
 // 工具链", lists a shared expert output beside the routed output), and y is rounded to bf16 once;
-// every element of y is written.  O is the down projection's output, fp32 or fp16 with a
-// power-of-two exponent per row and 16 columns (the layer's own launches use the latter).
+// every element of y is written.  O is the down projection's output, fp32 or fp16 with an
+// in-band power-of-two exponent per row and 8 columns (the layer's own launches use the latter).
 #include "launch.h"
 #include "moe_common.h"
 
 namespace moe {
 
-// One slot row's 8 values at column block v as loaded: fp32 O (two 16-byte halves), or fp16 O
-// (one 16-byte load) and its exponent byte.
+// One slot row's 8 values at column block v as loaded: fp32 O (two 16-byte halves), or the fp16
+// segment (one 16-byte load).
 struct RowRaw {
   u32x4 a, b;
-  uint32_t ex;
 };
 
 template <bool O16>
-__device__ __forceinline__ RowRaw load_row(const void* O, const uint8_t* O_exp, int r, int H, int v) {
+__device__ __forceinline__ RowRaw load_row(const void* O, int r, int H, int v) {
   RowRaw x;
   if (O16) {
     x.a = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(O) + (size_t)r * H)[v];
     x.b = u32x4{0u, 0u, 0u, 0u};
-    x.ex = O_exp[(size_t)r * (H / 16) + v / 2];
   } else {
     const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const float*>(O) + (size_t)r * H) + 2 * v;
     x.a = src[0];
     x.b = src[1];
-    x.ex = 0;
   }
   return x;
 }
 
-// The 8 values in fp32: fp16 * 2^exp is exact in fp32.
+// The 8 values in fp32.  An fp16 segment whose first element is the marker (an fp16 NaN carrying the
+// segment's exponent in its low 7 bits) is scaled: every value is fp16 * 2^exp and the first one is
+// O_side[r, v] * 2^exp; both products are exact in fp32.  (No unmarked segment holds a NaN.)
 template <bool O16>
-__device__ __forceinline__ void row_values(const RowRaw& x, float (&o)[8]) {
+__device__ __forceinline__ void row_values(const RowRaw& x, const float* O_side, int r, int H, int v, float (&o)[8]) {
   if (O16) {
-    const float f = __uint_as_float((127u + x.ex) << 23);  // 2^ex, ex <= 113
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      o[2 * i] = f16_bits_to_f32(x.a[i] & 0xFFFFu) * f;
-      o[2 * i + 1] = f16_bits_to_f32(x.a[i] >> 16) * f;
+      o[2 * i] = f16_bits_to_f32(x.a[i] & 0xFFFFu);
+      o[2 * i + 1] = f16_bits_to_f32(x.a[i] >> 16);
+    }
+    const uint32_t first = x.a[0] & 0xFFFFu;
+    if ((first & 0x7E00u) == 0x7E00u) {
+      const float f = __uint_as_float((127u + (first & 0x7Fu)) << 23);  // 2^exp, exp <= 113
+      o[0] = O_side[(size_t)r * (H / 8) + v];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] *= f;
     }
   } else {
 #pragma unroll
@@ -54,7 +59,7 @@ __device__ __forceinline__ void row_values(const RowRaw& x, float (&o)[8]) {
 }
 
 template <bool O16>
-__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ O, const uint8_t* __restrict__ O_exp,
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ O, const float* __restrict__ O_side,
                                                       const int32_t* __restrict__ inv_perm,
                                                       const float* __restrict__ w,
                                                       const float* __restrict__ shared, int shared_o_row0, int T,
@@ -77,11 +82,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ O
       }
       RowRaw x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = load_row<O16>(O, O_exp, r[j], H, v);
+      for (int j = 0; j < 8; ++j) x[j] = load_row<O16>(O, r[j], H, v);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float o[8];
-        row_values<O16>(x[j], o);
+        row_values<O16>(x[j], O_side, r[j], H, v, o);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = fmaf(ws[j], o[i], acc[i]);
       }
@@ -89,16 +94,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ O
     for (; s < k; ++s) {
       const int r = inv_perm[(size_t)t * k + s];
       const float ws = w[(size_t)t * k + s];
-      const RowRaw x = load_row<O16>(O, O_exp, r, H, v);
+      const RowRaw x = load_row<O16>(O, r, H, v);
       float o[8];
-      row_values<O16>(x, o);
+      row_values<O16>(x, O_side, r, H, v, o);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = fmaf(ws, o[i], acc[i]);
     }
     if (shared_o_row0 >= 0) {  // the shared expert's output is row shared_o_row0 + t of O
-      const RowRaw x = load_row<O16>(O, O_exp, shared_o_row0 + t, H, v);
+      const RowRaw x = load_row<O16>(O, shared_o_row0 + t, H, v);
       float o[8];
-      row_values<O16>(x, o);
+      row_values<O16>(x, O_side, shared_o_row0 + t, H, v, o);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += o[i];
     } else if (shared) {
@@ -118,15 +123,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ O
   }
 }
 
-hipError_t launch_combine(const void* O, const uint8_t* O_exp, const int32_t* inv_perm, const float* w,
+hipError_t launch_combine(const void* O, const float* O_side, const int32_t* inv_perm, const float* w,
                           const float* shared, int shared_o_row0, int T, int k, int H, uint16_t* y,
                           hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   const int threads = H / 8 >= 256 ? 256 : ((H / 8 + 63) / 64) * 64;
-  if (O_exp)
-    combine_kernel<true><<<T, threads, 0, stream>>>(O, O_exp, inv_perm, w, shared, shared_o_row0, T, k, H, y);
+  if (O_side)
+    combine_kernel<true><<<T, threads, 0, stream>>>(O, O_side, inv_perm, w, shared, shared_o_row0, T, k, H, y);
   else
-    combine_kernel<false><<<T, threads, 0, stream>>>(O, O_exp, inv_perm, w, shared, shared_o_row0, T, k, H, y);
+    combine_kernel<false><<<T, threads, 0, stream>>>(O, O_side, inv_perm, w, shared, shared_o_row0, T, k, H, y);
   return hipGetLastError();
 }
 

@@ -106,22 +106,30 @@ __device__ __forceinline__ void column_of(const GemmArgs& p, int col0, int ni, i
   if (!valid) n = 0;
 }
 
-// Output kinds of the NONE epilogue (GemmArgs::out_f32): 0 bf16, 1 fp32, 2 fp16 with a power-of-two
-// exponent per row and 16-column block (kOutF16Exp).  With kind 2, element (r, n) is
-// fp16(C[r, n]) * 2^exp[r, n / 16]: the exponent is 0 unless the block's row holds a magnitude of at
-// least 2^15 (or a non-finite value), in which case the row segment is scaled by 2^-exp first so that
-// its largest finite magnitude lies below 2^15.  fp16 keeps 11 significant bits where bf16 keeps 8;
-// the exponent keeps any fp32 range representable.
+// Output kinds of the NONE epilogue (GemmArgs::out_f32): 0 bf16, 1 fp32, 2 fp16 (kOutF16Exp) with
+// an exponent per row and 8-column segment that is carried in band.  A segment is stored plainly
+// (8 fp16 values, exponent 0) unless it holds a magnitude of at least 2^15 or a non-finite value;
+// such a segment is scaled by 2^-exp (exact; its largest finite magnitude then lies below 2^15),
+// its first element is replaced by a marker (an fp16 NaN whose low 7 bits are exp) and that
+// element's scaled value goes to C_side[row, col / 8] in fp32.  fp16 keeps 11 significant bits
+// where bf16 keeps 8; the exponent keeps any fp32 range representable, and in the common case
+// nothing but the fp16 values is written.
 constexpr int kOutBf16 = 0, kOutF32 = 1, kOutF16Exp = 2;
+constexpr uint16_t kF16Marker = 0x7E00;  // quiet NaN; low 7 bits: the segment's exponent
 
-// One row of a 16 x 16 MFMA output block lives in the 16 lanes of a quarter (one lane per column):
-// the largest finite magnitude over those lanes.
-__device__ __forceinline__ float quarter_max_finite(float v) {
-  float m = (fabsf(v) <= 3.0e38f) ? fabsf(v) : 0.f;
+// The 8 columns of a segment live in 8 lanes of a quarter (one lane per column, l16 = 8j .. 8j+7):
+// the largest finite magnitude over them, and whether any is non-finite.
+__device__ __forceinline__ float seg8_max_finite(float v, bool& nonfinite) {
+  const bool nf = !(fabsf(v) <= 3.4e38f);
+  float m = nf ? 0.f : fabsf(v);
   m = fmaxf(m, __shfl_xor(m, 1));
   m = fmaxf(m, __shfl_xor(m, 2));
   m = fmaxf(m, __shfl_xor(m, 4));
-  m = fmaxf(m, __shfl_xor(m, 8));
+  int f = nf;
+  f |= __shfl_xor(f, 1);
+  f |= __shfl_xor(f, 2);
+  f |= __shfl_xor(f, 4);
+  nonfinite = f != 0;
   return m;
 }
 
@@ -129,7 +137,7 @@ template <int EPI, int OUT, int MI, int NI>
 __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x4 (&acc)[MI][NI], int row_base, int row0,
                                            int rows, int q, const int (&ncol)[NI], const bool (&nvalid)[NI]) {
   const int N = p.N;
-  bool scaled = false;  // kOutF16Exp: some row segment of this wave needs a nonzero exponent
+  bool scaled = false;  // kOutF16Exp: some segment of this wave needs an exponent or holds a non-finite value
   if (EPI != MOE_EPI_SILU_MUL && OUT == kOutF16Exp) {
     bool big = false;
 #pragma unroll
@@ -147,21 +155,26 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x4 (&acc)
     for (int r = 0; r < 4; ++r) {
       const int row = row_base + mi * 16 + q * 4 + r;
       if (EPI != MOE_EPI_SILU_MUL && OUT == kOutF16Exp) {
-        // every lane takes part in the quarter reductions, whatever its row
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
           float v = nvalid[ni] ? acc[mi][ni][r] : 0.f;
-          int ex = 0;
-          if (scaled) {
-            const float m = quarter_max_finite(v);
+          uint16_t bits;
+          if (!scaled) {
+            bits = f32_to_f16_bits(v);
+          } else {
+            // every lane takes part in the segment reductions, whatever its row
+            bool nonfinite;
+            const float m = seg8_max_finite(v, nonfinite);
+            int ex = 0;
             if (m >= 32768.f) ex = ((int)((__float_as_uint(m) >> 23) & 0xFF) - 127) - 14;
             v *= __uint_as_float((uint32_t)(127 - ex) << 23);  // exact: 2^-ex, ex <= 113
+            bits = f32_to_f16_bits(v);
+            if ((ex > 0 || nonfinite) && (l16 & 7) == 0) {
+              bits = (uint16_t)(kF16Marker | ex);
+              if (row < rows && nvalid[ni]) p.C_side[(size_t)(row0 + row) * (size_t)((N + 7) / 8) + ncol[ni] / 8] = v;
+            }
           }
-          if (row < rows && nvalid[ni]) {
-            const size_t orow = (size_t)(row0 + row);
-            static_cast<uint16_t*>(p.C)[orow * N + ncol[ni]] = f32_to_f16_bits(v);
-            if (l16 == 0) p.C_exp[orow * (size_t)((N + 15) / 16) + ncol[ni] / 16] = (uint8_t)ex;
-          }
+          if (row < rows && nvalid[ni]) static_cast<uint16_t*>(p.C)[(size_t)(row0 + row) * N + ncol[ni]] = bits;
         }
         continue;
       }

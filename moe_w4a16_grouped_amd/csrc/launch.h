@@ -50,7 +50,7 @@ struct GemmArgs {
   int dense_rows;          // dense mode: tile i covers rows [i * BM, min((i + 1) * BM, dense_rows)) of expert 0
   void* C;
   int epilogue;            // MOE_EPI_*
-  int out_f32;             // NONE epilogue: 0 bf16, 1 fp32, 2 fp16 with exponents (C_exp)
+  int out_f32;             // NONE epilogue: 0 bf16, 1 fp32, 2 fp16 with in-band exponents (C_side)
   int packed;              // weights in the prepacked kernel layout (prepack.hip)
   // Shared expert run in the same launch (NULL = none): one more expert with weights [N, K/2] and
   // [N, K/32] (same layout as Wq / Ws), applied to shared_rows rows whose output rows start at
@@ -74,8 +74,8 @@ struct GemmArgs {
   int32_t* route_num_tiles;
   int32_t* route_sorted;      // [T * k]
   int32_t* route_inv;         // [T * k]
-  // out_f32 == 2: one exponent byte per output row and 16-column block, [rows, ceil(N / 16)]
-  uint8_t* C_exp;
+  // out_f32 == 2: fp32 values of the marked elements, [rows, ceil(N / 8)] (see kOutF16Exp)
+  float* C_side;
 };
 // Batches the routing prologue serves: at most 16 tokens (so every expert fits one 16-row tile),
 // k <= 16, E <= 512.
@@ -152,10 +152,10 @@ hipError_t launch_f8_quant(const void* x, bool in_f32, long long rows, int K, ui
 hipError_t launch_prepack(const uint8_t* wq, const uint16_t* ws, int E, int N, int K, uint8_t* pq, uint16_t* ps,
                           hipStream_t stream);
 
-// O: fp32 [R, H] (O_exp NULL) or fp16 [R, H] with exponent bytes O_exp [R, H / 16] (value =
-// fp16 * 2^exp, the down projection's fp16 output).  Shared term: row shared_o_row0 + t of O when
+// O: fp32 [R, H] (O_side NULL) or the down projection's fp16 output [R, H] with its side values
+// O_side [R, H / 8] (MOE_OUT_F16E).  Shared term: row shared_o_row0 + t of O when
 // shared_o_row0 >= 0, else the fp32 rows `shared` (or none when NULL).
-hipError_t launch_combine(const void* O, const uint8_t* O_exp, const int32_t* inv_perm, const float* w,
+hipError_t launch_combine(const void* O, const float* O_side, const int32_t* inv_perm, const float* w,
                           const float* shared, int shared_o_row0, int T, int k, int H, uint16_t* y,
                           hipStream_t stream);
 

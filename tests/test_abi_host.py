@@ -54,7 +54,7 @@ def test_pure_size_queries(lib):
     assert moe.moe_align_workspace_bytes(8192, 10, 512) == 20 * 4 * 512 * 4
     ws = moe.moe_ffn_workspace_bytes(800, 2048, 512, 256, 8)
     R = 800 * 8
-    assert ws >= R * 512 * 2 + R * 2048 * 2 + R * 2048 // 16  # h (bf16), the down output (fp16) and its exponents
+    assert ws >= R * 512 * 2 + R * 2048 * 2 + R * 2048 // 8 * 4  # h (bf16), the down output (fp16), its side values
     assert moe.moe_ffn_workspace_bytes(4, 2048, 512, 8, 9) == 0    # k > E
 
 
@@ -70,7 +70,7 @@ def test_block_m_choice():
     # one workspace size serves both layouts: the tile list is sized for the smaller tile height
     R, E = 4096 * 2, 8
     ws = moe.moe_ffn_workspace_bytes(4096, 4096, 14336, E, 2)
-    assert ws >= R * 14336 * 2 + R * 4096 * 2 + R * 4096 // 16 + moe.moe_max_tiles(4096, 2, E, 64) * 12
+    assert ws >= R * 14336 * 2 + R * 4096 * 2 + R * 4096 // 8 * 4 + moe.moe_max_tiles(4096, 2, E, 64) * 12
 
 
 FAKE = 1 << 20  # an aligned, never-dereferenced pointer value: validation fails before any launch
@@ -137,7 +137,7 @@ def test_grouped_gemm_rejects(lib):
     assert call(lay=1, N=200) == -2    # packed needs N % 16 == 0
     assert call(lay=1, N=80, epi=1) == -2  # packed SiLU*mul needs N % 32 == 0 (up rows start a block)
     assert call(lay=1, Ws=_ptr(FAKE + 2)) == -3  # packed scales need 8-byte alignment
-    assert call(out=3) == -1                     # fp16 with exponents needs its exponent array
+    assert call(out=3) == -1                     # fp16 with in-band exponents needs its side array
     assert call(out=3, epi=1, cexp=f) == -1      # ... and the plain epilogue
     assert call(out=4) == -1                     # unknown output kind
 
@@ -156,10 +156,10 @@ def test_combine_and_forward_reject(lib):
     f = _ptr(FAKE)
     F32, F16E = moe.MOE_OUT_F32, moe.MOE_OUT_F16E
     assert lib.moe_combine(f, F32, None, f, f, None, 4, 2, 12, f, None) == -2   # H % 8
-    assert lib.moe_combine(f, F16E, f, f, f, None, 4, 2, 24, f, None) == -2     # fp16 O: H % 16
+    assert lib.moe_combine(f, F16E, f, f, f, None, 4, 2, 12, f, None) == -2     # fp16 O: H % 8 too
     assert lib.moe_combine(f, F32, None, f, f, None, 0, 2, 16, f, None) == 0    # T == 0
     assert lib.moe_combine(_ptr(FAKE + 4), F32, None, f, f, None, 4, 2, 16, f, None) == -3
-    assert lib.moe_combine(f, F16E, None, f, f, None, 4, 2, 16, f, None) == -1  # fp16 O needs exponents
+    assert lib.moe_combine(f, F16E, None, f, f, None, 4, 2, 16, f, None) == -1  # fp16 O needs its side values
     assert lib.moe_combine(f, 0, None, f, f, None, 4, 2, 16, f, None) == -1     # bf16 O is not accepted
     ws = moe.moe_ffn_workspace_bytes(16, 256, 128, 8, 2)
     fw = lambda **kw: lib.moe_ffn_forward(kw.get("x", f), f, kw.get("T", 16), kw.get("H", 256), kw.get("I", 128),

@@ -227,11 +227,22 @@ def test_grouped_gemm_split_k_gate_up(I, H):
         np.testing.assert_array_equal(Cp.view(torch.int16).cpu().numpy(), C.view(torch.int16).cpu().numpy())
 
 
-def f16e_to_f64(C, Ce):
-    """fp16 values with per-(row, 16 columns) exponent bytes -> float64."""
-    v = C.float().cpu().numpy().astype(np.float64)
-    e = Ce.cpu().numpy().astype(np.int64)
-    return v * np.ldexp(1.0, np.repeat(e, 16, axis=1)[:, :v.shape[1]])
+def f16e_decode(bits, side):
+    """fp16 values (uint16 bits [rows, N]) with in-band exponents and side values [rows, N/8] ->
+    (float64 values, exponent per 8-column segment).  A segment whose first element is the marker
+    (fp16 quiet NaN 0x7E00 | exp) is scaled by 2^exp and its first value is the side value."""
+    bits = np.asarray(bits, np.uint16)
+    rows, N = bits.shape
+    v = bits.view(np.float16).astype(np.float64).reshape(rows, N // 8, 8)
+    first = bits.reshape(rows, N // 8, 8)[:, :, 0]
+    marked = (first & 0x7E00) == 0x7E00
+    ex = np.where(marked, first & 0x7F, 0).astype(np.int64)
+    v[:, :, 0] = np.where(marked, side, v[:, :, 0])
+    return (v * np.ldexp(1.0, ex)[:, :, None]).reshape(rows, N), ex
+
+
+def f16e_to_f64(C, Cs):
+    return f16e_decode(C.view(torch.int16).cpu().numpy().view(np.uint16), Cs.cpu().numpy().astype(np.float64))
 
 
 @pytest.mark.parametrize("bm", [16, 64, 128])
@@ -254,9 +265,9 @@ def test_grouped_gemm_plain(bm, out_dtype, N, K):
     ra = oracle.align(rid, E, bm)
     ref = oracle.grouped_proj(A, None, 1, Wq, Ws, ra["offsets"])
     if out_dtype == moe.MOE_OUT_F16E:
-        C, Ce = C
-        assert np.all(Ce.cpu().numpy() == 0)  # magnitudes of order 1: no row segment is scaled
-        got = f16e_to_f64(C, Ce)
+        C, Cs = C
+        got, ex = f16e_to_f64(C, Cs)
+        assert np.all(ex == 0)  # magnitudes of order 1: no segment is scaled
     else:
         got = C.cpu().numpy().astype(np.float64) if out_dtype == moe.MOE_OUT_F32 else gu.host_bf16_to_f64(C)
     # bf16 x E2M1 products are exact in fp32; the fp32 summation takes at most (32 + K/32) roundings
@@ -273,9 +284,10 @@ def test_grouped_gemm_plain(bm, out_dtype, N, K):
 
 @pytest.mark.parametrize("bm,layout", [(32, 0), (64, 0), (16, 0), (128, 1)])
 def test_grouped_gemm_f16e_exponents(bm, layout):
-    """Outputs far beyond fp16's range: each row segment of 16 columns holding a magnitude >= 2^15
-    is stored scaled by 2^-exp (its largest magnitude then below 2^15) with exp in its byte; the
-    decoded values stay within the fp32 summation bound plus one fp16 rounding."""
+    """Outputs far beyond fp16's range: each 8-column row segment holding a magnitude >= 2^15 is
+    stored scaled by 2^-exp (its largest magnitude then below 2^15), marked in its first element,
+    whose value goes to the side array; decoded values stay within the fp32 summation bound plus one
+    fp16 rounding, and unmarked segments are plain fp16."""
     E, T, k, N, K = 4, 70, 2, 256, 256
     rng = np.random.default_rng(bm + 5)
     logits = rng.standard_normal((T, E), dtype=np.float32)
@@ -283,7 +295,7 @@ def test_grouped_gemm_f16e_exponents(bm, layout):
     R = T * k
     A = rng.standard_normal((R, K), dtype=np.float32)
     A[::3] *= 2.0 ** 20  # every third row: outputs around 2^22
-    A[1::7, :8] *= 2.0 ** 40  # a few rows with a huge first group: one segment far above the rest
+    A[1::7, :8] *= 2.0 ** 40  # a few rows with a huge first group: far above the rest
     A = mi.f32_to_bf16_bits(A)
     Wq = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
     Ws = mi.f32_to_bf16_bits(rng.uniform(0.005, 0.02, (E, N, K // 32)).astype(np.float32))
@@ -291,38 +303,41 @@ def test_grouped_gemm_f16e_exponents(bm, layout):
     d_wq, d_ws = gu.dev(Wq), gu.dev(Ws.view(np.int16))
     if layout:
         d_wq, d_ws = moe.moe_w4_prepack(d_wq, d_ws)
-    C, Ce = moe.moe_grouped_gemm_w4a16(gu.dev_bf16(A), None, 1, d_wq, d_ws, a["tiles"], a["max_tiles"],
+    C, Cs = moe.moe_grouped_gemm_w4a16(gu.dev_bf16(A), None, 1, d_wq, d_ws, a["tiles"], a["max_tiles"],
                                        a["num_tiles"], bm, moe.MOE_EPI_NONE, R, moe.MOE_OUT_F16E, weight_layout=layout)
     torch.cuda.synchronize()
     ra = oracle.align(rid, E, bm)
     ref = oracle.grouped_proj(A, None, 1, Wq, Ws, ra["offsets"])
     ref_abs = oracle.grouped_proj(A & 0x7FFF, None, 1, Wq & 0x77, Ws, ra["offsets"])
-    ce = Ce.cpu().numpy().astype(np.int64)
-    got = f16e_to_f64(C, Ce)
+    got, ex = f16e_to_f64(C, Cs)
     acc_err = (64 + K / 32) * 2.0 ** -24 * ref_abs
-    scale = np.ldexp(1.0, np.repeat(ce, 16, axis=1))
+    scale = np.repeat(np.ldexp(1.0, ex), 8, axis=1)
     assert np.all(np.abs(got - ref) <= acc_err + 2.0 ** -11 * (np.abs(ref) + acc_err) + 2.0 ** -25 * scale)
-    # the exponent is 0 exactly where the segment's largest magnitude stays below 2^15
-    seg_max = np.abs(got).reshape(R, N // 16, 16).max(axis=2)  # (after one fp16 rounding)
-    assert np.all(seg_max[ce > 0] >= 2.0 ** 15 * (1 - 2.0 ** -10)) and np.all(seg_max[ce == 0] <= 2.0 ** 15)
-    assert np.all(np.abs(C.float().cpu().numpy()) <= 2.0 ** 15)
-    assert ce.max() >= 40 and (ce == 0).any()
+    # a segment is marked exactly where its largest magnitude reaches 2^15
+    seg_max = np.abs(got).reshape(R, N // 8, 8).max(axis=2)  # (after one fp16 rounding)
+    assert np.all(seg_max[ex > 0] >= 2.0 ** 15 * (1 - 2.0 ** -10)) and np.all(seg_max[ex == 0] <= 2.0 ** 15)
+    assert ex.max() >= 40 and (ex == 0).any()
 
 
 @pytest.mark.parametrize("k", [5, 8, 10, 16])
 def test_combine_f16e_matches_oracle(k):
-    """fp16 O with exponent bytes (the layer's down-projection output): each value is fp16 * 2^exp,
-    exact in fp32, so the bound is that of fp32 O."""
+    """fp16 O with in-band exponents (the layer's down-projection output): every fifth row has its
+    segments marked with exponents 0..29 (side values in place of their first elements); each value
+    decodes exactly to fp32, so the bound is that of fp32 O."""
     T, H = 29, 272
     rng = np.random.default_rng(7 + k)
     O16 = rng.standard_normal((T * k, H)).astype(np.float16)
-    ex = np.zeros((T * k, H // 16), np.uint8)
-    ex[::5] = rng.integers(0, 30, (len(ex[::5]), H // 16))
+    bits = O16.view(np.uint16).copy()
+    side = rng.standard_normal((T * k, H // 8)).astype(np.float32)
+    ex = rng.integers(0, 30, (T * k, H // 8))
+    marked = np.zeros((T * k, H // 8), bool)
+    marked[::5] = True
+    bits.reshape(T * k, H // 8, 8)[:, :, 0] = np.where(marked, 0x7E00 | ex, bits.reshape(T * k, H // 8, 8)[:, :, 0])
     inv = rng.permutation(T * k).astype(np.int32)
     w = rng.uniform(0, 1, (T, k)).astype(np.float32)
-    y = moe.moe_combine(gu.dev(O16), gu.dev(inv), gu.dev(w), O_exp=gu.dev(ex))
+    y = moe.moe_combine(gu.dev(bits.view(np.int16)).view(torch.float16), gu.dev(inv), gu.dev(w), O_side=gu.dev(side))
     torch.cuda.synchronize()
-    O = O16.astype(np.float64) * np.ldexp(1.0, np.repeat(ex.astype(np.int64), 16, axis=1))
+    O, _ = f16e_decode(bits, side.astype(np.float64))
     ref = oracle.combine(O, inv, w.astype(np.float64), T, k)
     terms = oracle.combine(np.abs(O), inv, w.astype(np.float64), T, k)
     got = gu.host_bf16_to_f64(y)
@@ -513,9 +528,9 @@ def _layer_from_entry_points(d, inp, packed):
     R = wl.T * wl.k
     h = moe.moe_grouped_gemm_w4a16(d.x, al["sorted_ids"], wl.k, q13, s13, al["tiles"], al["max_tiles"],
                                    al["num_tiles"], bm, moe.MOE_EPI_SILU_MUL, R, weight_layout=layout)
-    O, Oe = moe.moe_grouped_gemm_w4a16(h, None, 1, q2, s2, al["tiles"], al["max_tiles"], al["num_tiles"], bm,
+    O, Os = moe.moe_grouped_gemm_w4a16(h, None, 1, q2, s2, al["tiles"], al["max_tiles"], al["num_tiles"], bm,
                                        moe.MOE_EPI_NONE, R, out_dtype=moe.MOE_OUT_F16E, weight_layout=layout)
-    y = moe.moe_combine(O, al["inv_perm"], w, O_exp=Oe)
+    y = moe.moe_combine(O, al["inv_perm"], w, O_side=Os)
     torch.cuda.synchronize()
     return y
 
@@ -570,8 +585,8 @@ def test_grouped_gemm_packed_matches_canonical_bits(bm):
         c2 = moe.moe_grouped_gemm_w4a16(A, aro, div, pq, ps, a["tiles"], a["max_tiles"], a["num_tiles"], bm, epi, R, od,
                                         weight_layout=moe.MOE_LAYOUT_PACKED)
         torch.cuda.synchronize()
-        if od == moe.MOE_OUT_F16E:
-            np.testing.assert_array_equal(c1[1].cpu().numpy(), c2[1].cpu().numpy())
+        if od == moe.MOE_OUT_F16E:  # no marked segment at these magnitudes: the side values are unused
+            assert np.all(f16e_to_f64(*c1)[1] == 0)
             c1, c2 = c1[0], c2[0]
         view = torch.int32 if od == moe.MOE_OUT_F32 else torch.int16
         np.testing.assert_array_equal(c1.view(view).cpu().numpy(), c2.view(view).cpu().numpy())
@@ -609,8 +624,8 @@ def test_large_tile_gemm_matches_canonical_bits(T, E, k, H, I, seed):
                                          a128["max_tiles"], a128["num_tiles"], 128, epi, R, od,
                                          weight_layout=moe.MOE_LAYOUT_PACKED)
         torch.cuda.synchronize()
-        if od == moe.MOE_OUT_F16E:
-            np.testing.assert_array_equal(out[1].cpu().numpy(), ref[1].cpu().numpy())
+        if od == moe.MOE_OUT_F16E:  # no marked segment at these magnitudes: the side values are unused
+            assert np.all(f16e_to_f64(*ref)[1] == 0)
             out, ref = out[0], ref[0]
         view = torch.int32 if od == moe.MOE_OUT_F32 else torch.int16
         np.testing.assert_array_equal(out.view(view).cpu().numpy(), ref.view(view).cpu().numpy())
