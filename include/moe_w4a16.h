@@ -47,14 +47,19 @@
  *   of scales [16 rows][4 groups].  It exists so that each wave-level load is one contiguous block
  *   (the ATOM page, 8.2, lists weight pre-rearrangement as part of a quantized format's contract).
  *   Requires N % 16 == 0 and K % 128 == 0; a gate_up tensor read with SILU_MUL also needs
- *   N % 32 == 0, so that its up rows (from N/2) start a block.  Results are bit-identical to the
- *   canonical layout.
+ *   N % 32 == 0, so that its up rows (from N/2) start a block.  A grouped GEMM gives the same bits
+ *   with either layout; the layer does too, except where the packed layout's 128-row tiles take the
+ *   exact fp16 path below (canonical weights never do), which agrees within the layer tolerance.
  *
  * Numerics: E2M1 codes are exact in bf16; each 32-element group is reduced by bf16 MFMA into an
  * fp32 partial that is multiplied by the group's scale in fp32; accumulation is fp32.  h (the
  * SiLU-mul output) is stored as bf16 (round to nearest even), the down-projection output as fp16
  * with an in-band power-of-two exponent per row and 8 columns (MOE_OUT_F16E), and the combine sums the k
- * slots in fp32 in slot order before one rounding of y to bf16.
+ * slots in fp32 in slot order before one rounding of y to bf16.  Layers whose experts average more
+ * than 256 rows with packed weights (128-row tiles) run the exact fp16 path instead: x in fp16 with a
+ * power-of-two exponent per row (moe_x_to_f16), weights formed exactly in fp16 as code * scale and
+ * reduced by fp16 MFMA with fp32 accumulation, and h in fp16 with exponents per row and 32 columns
+ * (moe_grouped_gemm_w4f16).
  */
 #ifndef MOE_W4A16_H
 #define MOE_W4A16_H
@@ -81,13 +86,22 @@ typedef int32_t moe_status_t;
 #define MOE_OUT_BF16 0
 #define MOE_OUT_F32 1
 /* fp16 with an in-band power-of-two exponent per row and 8-column segment: a segment is 8 plain
- * fp16 values (round to nearest even) unless it holds a magnitude of at least 2^15 or a non-finite
- * value; then it is scaled by 2^-exp (exact; its largest finite magnitude lies below 2^15), its
- * first element is replaced by a marker, the fp16 quiet NaN 0x7E00 | exp, and that element's scaled
- * value is written to C_side[row, col / 8] (fp32).  Every value of a marked segment is then
- * (fp16 or side value) * 2^exp.  No unmarked segment holds a NaN.  The layer writes the down
- * projection this way: half the bytes of fp32, 3 more significant bits than bf16, any fp32 range. */
+ * fp16 values (round to nearest even) when its largest finite magnitude m is 0 or in [2^-6, 2^15) and
+ * it holds no non-finite value; otherwise it is scaled by 2^-exp, exp = floor(log2 m) - 14 clamped to
+ * [-110, 113] (exact), its first element is replaced by a marker, the fp16 quiet NaN
+ * 0x7E00 | (exp + 256), and that element's scaled value is written to C_side[row, col / 8] (fp32).
+ * Every value of a marked segment is then (fp16 or side value) * 2^exp.  No unmarked segment holds a
+ * NaN.  The layer writes the down projection this way: half the bytes of fp32, 3 more significant
+ * bits than bf16, and fp32's range. */
 #define MOE_OUT_F16E 3
+/* SiLU*mul output of moe_grouped_gemm_w4f16: h as fp16 [R_out, N/2] (round to nearest even) with a
+ * signed exponent per row and block of 32 columns: row r's values in block j are fp16(h / 2^exp), exp =
+ * 0 unless the row's largest finite |h| m in that block is 2^15 or more, or below 2^-6 but not 0 (then
+ * exp = floor(log2 m) - 14 clamped to [-110, 113], which scales m into [2^14, 2^15) exactly).  C_aux
+ * uint8 [max_tiles, ceil(N/2/32)] flags, per tile and block, whether any row of the tile has a nonzero
+ * exponent there; C_aux2 int8 [R_out, ceil(N/2/32)] holds the exponents, written only for flagged
+ * blocks. */
+#define MOE_OUT_H16 4
 
 #define MOE_LAYOUT_CANONICAL 0 /* the weight format above */
 #define MOE_LAYOUT_PACKED 1    /* the same codes and scales re-laid out by moe_w4_prepack */
@@ -185,7 +199,8 @@ moe_status_t moe_w4_prepack(const uint8_t* w_q, const uint16_t* w_s, int32_t E, 
  *              C fp16 [R_out, N] with side values C_side fp32 [R_out, ceil(N/8)] (see
  *              MOE_OUT_F16E; C_side is written only for marked segments, and is ignored for the
  *              other kinds and may then be NULL).  SILU_MUL requires BF16.
- * Shapes: 1 <= E <= MOE_MAX_EXPERTS, N >= 1 (N even for SILU_MUL), K % 32 == 0, K >= 32.
+ * Shapes: 1 <= E <= MOE_MAX_EXPERTS, N >= 1 (N even for SILU_MUL), K % 32 == 0, K >= 32,
+ *         N*K/2 < 4 GiB (one expert's codes).
  * Alignment: A, Wq, C 16 bytes; Ws 2 bytes.
  */
 moe_status_t moe_grouped_gemm_w4a16(const uint16_t* A, const int32_t* a_row_of, int32_t a_row_div,
@@ -194,6 +209,44 @@ moe_status_t moe_grouped_gemm_w4a16(const uint16_t* A, const int32_t* a_row_of, 
                                     int32_t K, const int32_t* tiles, int32_t max_tiles,
                                     const int32_t* num_tiles, int32_t block_m, int32_t epilogue,
                                     void* C, int32_t out_dtype, float* C_side, void* stream);
+
+/*
+ * Activations for the exact fp16 path of the grouped GEMM (moe_grouped_gemm_w4f16):
+ *   x16[t, c] = fp16(x[t, c] * 2^-x_exp[t]) (round to nearest even), x_exp[t] = floor(log2 m) - 14
+ *   where m is row t's largest finite |x| (x_exp = 0 for an all-zero row; clamped to [-110, 113]).
+ * The row's largest magnitude lands in [2^14, 2^15): every value at most 2^31 below it is exact in
+ * fp16; non-finite values stay non-finite.
+ *   x bf16 [T, H]; x16 fp16 [T, H]; x_exp int32 [T].  Shapes: T >= 0, H % 8 == 0.
+ */
+moe_status_t moe_x_to_f16(const uint16_t* x, int32_t T, int32_t H, uint16_t* x16, int32_t* x_exp, void* stream);
+
+/*
+ * Grouped W4A16 GEMM, exact fp16 form [Atlas, 编译时内核选择和W4A16 Grouped GEMM: dequantization inside
+ * the matmul]: the same result as moe_grouped_gemm_w4a16 with activations given in fp16 with power-
+ * of-two exponents.  Each weight E2M1(code) * scale is formed in fp16, exact when the bf16 scale has
+ * an exponent in [-16, 12], so every product is exact and the fp32 MFMA accumulation carries the group
+ * scales with it.  A K step holding any other scale (zero, subnormal, non-finite, out of that range),
+ * or h blocks with exponents, takes a general form: the scale is split into an fp16-exact part and a
+ * power of two, and the fp32 accumulators are scaled by that power of two (exactly) around each group.
+ *   A          fp16 [*, K]: with a_row_of (gathered rows, e.g. x16 of moe_x_to_f16) activation row a
+ *              is A[a] * 2^a_row_exp[a] (a_row_exp NULL: exponents 0); with a_row_of NULL (h of the
+ *              previous SILU_MUL call, with its two exponent arrays as a_blk_flag and a_row_blk_exp)
+ *              row r's values in K columns [32j, 32j+32) are A * 2^a_row_blk_exp[r * ceil(K/32) + j]
+ *              when a_blk_flag[i * ceil(K/32) + j] is nonzero for r's tile i, else A (a_blk_flag
+ *              NULL: no exponents).
+ *   block_m    64, or 128 with MOE_LAYOUT_PACKED weights (the tile list of moe_align with it).
+ *   epilogue   MOE_EPI_SILU_MUL with out_dtype MOE_OUT_H16 (C fp16 [R_out, N/2], C_aux and C_aux2 the
+ *              exponent flags and exponents, see MOE_OUT_H16), or MOE_EPI_NONE with MOE_OUT_F32 (C
+ *              fp32) or MOE_OUT_F16E (C fp16, C_aux fp32 side values [R_out, ceil(N/8)]); C_aux2 is
+ *              used by SILU_MUL only.
+ * Other arguments, shapes and alignment as for moe_grouped_gemm_w4a16.
+ */
+moe_status_t moe_grouped_gemm_w4f16(const uint16_t* A, const int32_t* a_row_exp, const uint8_t* a_blk_flag,
+                                    const uint8_t* a_row_blk_exp, const int32_t* a_row_of, int32_t a_row_div,
+                                    const uint8_t* Wq, const uint16_t* Ws, int32_t weight_layout, int32_t E, int32_t N,
+                                    int32_t K, const int32_t* tiles, int32_t max_tiles, const int32_t* num_tiles,
+                                    int32_t block_m, int32_t epilogue, void* C, int32_t out_dtype, void* C_aux,
+                                    uint8_t* C_aux2, void* stream);
 
 /*
  * Routing-weighted scatter-reduce (combine) [ATOM, 8.1]:
@@ -260,7 +313,7 @@ size_t moe_ffn_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32
  *   topk_ids_out int32 [T, k], topk_w_out fp32 [T, k]: optional copies of the routing (NULL = skip).
  *   workspace: device scratch of at least moe_ffn_workspace_bytes(T, H, I, E, k) bytes.
  * Shapes: T >= 0 (T == 0 launches nothing), 1 <= k <= E <= MOE_MAX_EXPERTS, H % 32 == 0,
- *         I % 32 == 0, H >= 32, I >= 32, T*k < 2^26.
+ *         I % 32 == 0, H >= 32, I >= 32, T*k < 2^26, H*I < 4 GiB (one expert's gate_up codes).
  */
 moe_status_t moe_ffn_forward(const uint16_t* x, const float* router_logits, int32_t T, int32_t H,
                              int32_t I, int32_t E, int32_t k, const uint8_t* w13_q,

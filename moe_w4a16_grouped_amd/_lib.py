@@ -33,6 +33,7 @@ MOE_IN_BF16 = 0
 MOE_IN_F32 = 1
 MOE_OUT_F8 = 2
 MOE_OUT_F16E = 3
+MOE_OUT_H16 = 4
 
 _lib = None
 
@@ -63,6 +64,9 @@ def load() -> ctypes.CDLL:
         "moe_w4_prepack": ([P, P, I32, I32, I32, P, P, P], I32),
         "moe_grouped_gemm_w4a16": ([P, P, I32, P, P, I32, I32, I32, I32, P, I32, P, I32, I32, P, I32, P, P], I32),
         "moe_combine": ([P, I32, P, P, P, P, I32, I32, I32, P, P], I32),
+        "moe_x_to_f16": ([P, I32, I32, P, P, P], I32),
+        "moe_grouped_gemm_w4f16": ([P, P, P, P, P, I32, P, P, I32, I32, I32, I32, P, I32, P, I32, I32, P, I32, P, P, P],
+                                   I32),
         "moe_router_logits": ([P, P, I32, I32, I32, P, P], I32),
         "moe_dense_ffn_workspace_bytes": ([I32, I32, I32], SZ),
         "moe_dense_ffn_w4a16": ([P, I32, I32, I32, P, P, P, P, I32, P, P, SZ, P], I32),
@@ -111,7 +115,8 @@ EXPORTED = ("moe_abi_version", "moe_status_string", "moe_last_error", "moe_route
             "moe_ffn_mxfp4_workspace_bytes", "moe_ffn_forward_mxfp4", "moe_f8_quantize", "moe_grouped_gemm_f8",
             "moe_ffn_f8_block_m", "moe_ffn_f8_workspace_bytes", "moe_ffn_forward_f8", "moe_mx8_quantize",
             "moe_mx8_quantize_tiles", "moe_grouped_gemm_w4a8", "moe_ffn_w4a8_block_m", "moe_ffn_w4a8_workspace_bytes",
-            "moe_ffn_forward_w4a8", "moe_ffn_noalloc_scratch_bytes", "moe_ffn_forward_noalloc")
+            "moe_ffn_forward_w4a8", "moe_ffn_noalloc_scratch_bytes", "moe_ffn_forward_noalloc", "moe_x_to_f16",
+            "moe_grouped_gemm_w4f16")
 
 
 def _check(status: int):
@@ -229,6 +234,48 @@ def moe_grouped_gemm_w4a16(A, a_row_of, a_row_div: int, Wq, Ws, tiles, max_tiles
                                          max_tiles, _p(num_tiles), block_m, epilogue, _p(C), out_dtype, _p(C_side),
                                          _stream(stream)))
     return (C, C_side) if out_dtype == MOE_OUT_F16E else C
+
+
+def moe_x_to_f16(x, x16=None, x_exp=None, stream=None):
+    """bf16 x [T, H] -> (fp16 x16 [T, H], int32 row exponents [T]): x16 = fp16(x * 2^-x_exp)."""
+    _req(x, "16bit", "x")
+    T, H = x.shape
+    if x16 is None:
+        x16 = torch.empty((T, H), dtype=torch.float16, device=x.device)
+    if x_exp is None:
+        x_exp = torch.empty((T,), dtype=torch.int32, device=x.device)
+    _check(load().moe_x_to_f16(_p(x), T, H, _p(x16), _p(x_exp), _stream(stream)))
+    return x16, x_exp
+
+
+def moe_grouped_gemm_w4f16(A, a_row_exp, a_exps, a_row_of, a_row_div: int, Wq, Ws, tiles, max_tiles: int,
+                           num_tiles, block_m: int, epilogue: int, out_rows: int, out_dtype: int, C=None, C_aux=None,
+                           C_aux2=None, stream=None, weight_layout: int = MOE_LAYOUT_CANONICAL):
+    """Grouped GEMM of the exact fp16 path (fp16 activations with exponents).  a_exps: None or the
+    (flags, row exponents) pair a SILU_MUL call returned for h.  Returns (h fp16, (flags, row
+    exponents)) for SILU_MUL, (C fp16, side fp32) for MOE_OUT_F16E, or C fp32 for MOE_OUT_F32."""
+    _req(A, "16bit", "A")
+    _req(Wq, torch.uint8, "Wq")
+    E, N, K2 = Wq.shape
+    K = 2 * K2
+    ncols = N // 2 if epilogue == MOE_EPI_SILU_MUL else N
+    if C is None:
+        C = torch.empty((out_rows, ncols), dtype=torch.float32 if out_dtype == MOE_OUT_F32 else torch.float16,
+                        device=A.device)
+    if out_dtype == MOE_OUT_H16:
+        if C_aux is None:
+            C_aux = torch.empty((max(max_tiles, 1), (ncols + 31) // 32), dtype=torch.uint8, device=A.device)
+        if C_aux2 is None:
+            C_aux2 = torch.empty((out_rows, (ncols + 31) // 32), dtype=torch.uint8, device=A.device)
+    elif C_aux is None and out_dtype == MOE_OUT_F16E:
+        C_aux = torch.empty((out_rows, (ncols + 7) // 8), dtype=torch.float32, device=A.device)
+    bf, be = (None, None) if a_exps is None else a_exps
+    _check(load().moe_grouped_gemm_w4f16(_p(A), _p(a_row_exp), _p(bf), _p(be), _p(a_row_of), a_row_div, _p(Wq), _p(Ws),
+                                         weight_layout, E, N, K, _p(tiles), max_tiles, _p(num_tiles), block_m, epilogue,
+                                         _p(C), out_dtype, _p(C_aux), _p(C_aux2), _stream(stream)))
+    if out_dtype == MOE_OUT_F32:
+        return C
+    return (C, (C_aux, C_aux2)) if out_dtype == MOE_OUT_H16 else (C, C_aux)
 
 
 def moe_combine(O, inv_perm, topk_w, y=None, stream=None, shared=None, O_side=None):

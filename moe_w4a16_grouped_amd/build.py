@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(BUILD, "libmoe_w4a16.so")
-SOURCES = ["router.hip", "route.hip", "align.hip", "grouped_gemm.hip", "mx.hip", "f8.hip", "combine.hip", "prepack.hip", "api.hip"]
+SOURCES = ["router.hip", "route.hip", "align.hip", "grouped_gemm.hip", "mx.hip", "f8.hip", "combine.hip", "prepack.hip", "convert.hip", "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 instructions are disabled for every HIP object (hipcc -O3 would otherwise form them).
 # MFMA results are kept in ordinary VGPRs (the scale FMA reads every MFMA result; accumulation-

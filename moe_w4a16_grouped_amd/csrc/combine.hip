@@ -32,8 +32,8 @@ __device__ __forceinline__ RowRaw load_row(const void* O, int r, int H, int v) {
 }
 
 // The 8 values in fp32.  An fp16 segment whose first element is the marker (an fp16 NaN carrying the
-// segment's exponent in its low 7 bits) is scaled: every value is fp16 * 2^exp and the first one is
-// O_side[r, v] * 2^exp; both products are exact in fp32.  (No unmarked segment holds a NaN.)
+// segment's exponent + 256 in its low 9 bits) is scaled: every value is fp16 * 2^exp and the first one
+// is O_side[r, v] * 2^exp; both products are exact in fp32.  (No unmarked segment holds a NaN.)
 template <bool O16>
 __device__ __forceinline__ void row_values(const RowRaw& x, const float* O_side, int r, int H, int v, float (&o)[8]) {
   if (O16) {
@@ -44,7 +44,7 @@ __device__ __forceinline__ void row_values(const RowRaw& x, const float* O_side,
     }
     const uint32_t first = x.a[0] & 0xFFFFu;
     if ((first & 0x7E00u) == 0x7E00u) {
-      const float f = __uint_as_float((127u + (first & 0x7Fu)) << 23);  // 2^exp, exp <= 113
+      const float f = pow2f((int)(first & 0x1FFu) - 256);  // 2^exp, -110 <= exp <= 113
       o[0] = O_side[(size_t)r * (H / 8) + v];
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[i] *= f;

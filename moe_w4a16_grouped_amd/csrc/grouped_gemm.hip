@@ -33,22 +33,34 @@ constexpr int kBK = 128;  // K elements per step: 4 scale groups
 enum Layout { kCanonGeneric = 0, kCanonFull = 1, kPacked = 2 };
 
 // Weight-row block of one lane: canonical pointers or packed block base.
+struct WBase {
+  const uint8_t* q;   // the expert's codes (N x K/2 bytes in either layout)
+  const uint16_t* s;  // the expert's scales (N x K/32 in either layout)
+};
+// A lane's weight row as 32-bit offsets within its expert (the launcher checks that an expert's codes
+// stay below 4 GiB), so that a row costs two registers next to the wave-uniform expert base.
 struct WRow {
-  const uint8_t* q;   // canonical: row start (+ lane offset); packed: block (e, nb, ks=0) + lane * 16
-  const uint16_t* s;  // canonical: scale row start; packed: scale block (e, nb, ks=0) + (lane % 16) * 4
+  uint32_t q;  // canonical: row start (+ lane offset); packed: block (nb, ks=0) + lane * 16  (bytes)
+  uint32_t s;  // canonical: scale row start; packed: scale block (nb, ks=0) + (lane % 16) * 4 (elements)
 };
 
+__device__ __forceinline__ WBase wbase_of(const GemmArgs& p, int e) {
+  const size_t nk = (size_t)p.N * (size_t)p.K;
+  const size_t eu = (size_t)__builtin_amdgcn_readfirstlane(e);
+  return WBase{p.Wq + eu * (nk / 2), p.Ws + eu * (nk / kGroup)};
+}
+
 template <int LAYOUT>
-__device__ __forceinline__ WRow wrow_of(const GemmArgs& p, int e, int n, int q, int lane) {
-  const int N = p.N, K = p.K;
+__device__ __forceinline__ WRow wrow_of(const GemmArgs& p, int n, int q, int lane) {
+  const uint32_t K = (uint32_t)p.K;
   WRow w;
   if (LAYOUT == kPacked) {
-    const size_t blk = ((size_t)e * (N / 16) + n / 16) * (size_t)(K / kBK);
-    w.q = p.Wq + blk * 1024 + lane * 16;
-    w.s = p.Ws + blk * 64 + (lane & 15) * 4;
+    const uint32_t blk = (uint32_t)(n / 16) * (K / kBK);
+    w.q = blk * 1024u + (uint32_t)lane * 16u;
+    w.s = blk * 64u + (uint32_t)(lane & 15) * 4u;
   } else {
-    w.q = p.Wq + ((size_t)e * N + n) * (size_t)(K / 2) + (LAYOUT == kCanonFull ? q * 16 : 0);
-    w.s = p.Ws + ((size_t)e * N + n) * (size_t)(K / kGroup);
+    w.q = (uint32_t)n * (K / 2) + (LAYOUT == kCanonFull ? (uint32_t)q * 16u : 0u);
+    w.s = (uint32_t)n * (K / kGroup);
   }
   return w;
 }
@@ -56,22 +68,23 @@ __device__ __forceinline__ WRow wrow_of(const GemmArgs& p, int e, int n, int q, 
 // Load the codes and scales of K step ks (groups 4ks..4ks+3) for one lane.
 // sq: kCanonGeneric -> one bf16 per entry; otherwise [0], [1] = raw bf16 pairs.
 template <int LAYOUT>
-__device__ __forceinline__ void load_w(const WRow& w, int ks, int q, int kgroups, u32x4& b, uint32_t (&sq)[4]) {
+__device__ __forceinline__ void load_w(const WBase& wb, const WRow& w, int ks, int q, int kgroups, u32x4& b,
+                                       uint32_t (&sq)[4]) {
   if (LAYOUT == kPacked) {
-    b = *reinterpret_cast<const u32x4*>(w.q + (size_t)ks * 1024);
-    const u32x2 v = *reinterpret_cast<const u32x2*>(w.s + (size_t)ks * 64);
+    b = *reinterpret_cast<const u32x4*>(wb.q + (w.q + (uint32_t)ks * 1024u));
+    const u32x2 v = *reinterpret_cast<const u32x2*>(wb.s + (w.s + (uint32_t)ks * 64u));
     sq[0] = v[0];
     sq[1] = v[1];
   } else if (LAYOUT == kCanonFull) {
-    b = *reinterpret_cast<const u32x4*>(w.q + (size_t)ks * 64);
-    const u32x2 v = *reinterpret_cast<const u32x2*>(w.s + (size_t)ks * 4);
+    b = *reinterpret_cast<const u32x4*>(wb.q + (w.q + (uint32_t)ks * 64u));
+    const u32x2 v = *reinterpret_cast<const u32x2*>(wb.s + (w.s + (uint32_t)ks * 4u));
     sq[0] = v[0];
     sq[1] = v[1];
   } else {
     const int gq = min(ks * 4 + q, kgroups - 1);
-    b = *reinterpret_cast<const u32x4*>(w.q + (size_t)gq * 16);
+    b = *reinterpret_cast<const u32x4*>(wb.q + (w.q + (uint32_t)gq * 16u));
 #pragma unroll
-    for (int g = 0; g < 4; ++g) sq[g] = w.s[min(ks * 4 + g, kgroups - 1)];
+    for (int g = 0; g < 4; ++g) sq[g] = wb.s[w.s + (uint32_t)min(ks * 4 + g, kgroups - 1)];
   }
 }
 
@@ -85,6 +98,13 @@ template <int LAYOUT>
 __device__ __forceinline__ float scale_of(const uint32_t (&sq)[4], int g) {
   if (LAYOUT == kCanonGeneric) return bf16_bits_to_f32(sq[g]);
   return __uint_as_float((g & 1) ? (sq[g >> 1] & 0xFFFF0000u) : (sq[g >> 1] << 16));
+}
+
+// The bf16 bits of group g's scale (for the fp16 path's exactness test).
+template <int LAYOUT>
+__device__ __forceinline__ uint32_t scale_bits_of(const uint32_t (&sq)[4], int g) {
+  if (LAYOUT == kCanonGeneric) return sq[g] & 0xFFFFu;
+  return (g & 1) ? (sq[g >> 1] >> 16) : (sq[g >> 1] & 0xFFFFu);
 }
 
 // Column bookkeeping for one 16-column block of the output tile.  For SiLU*mul the first NI/2
@@ -108,14 +128,31 @@ __device__ __forceinline__ void column_of(const GemmArgs& p, int col0, int ni, i
 
 // Output kinds of the NONE epilogue (GemmArgs::out_f32): 0 bf16, 1 fp32, 2 fp16 (kOutF16Exp) with
 // an exponent per row and 8-column segment that is carried in band.  A segment is stored plainly
-// (8 fp16 values, exponent 0) unless it holds a magnitude of at least 2^15 or a non-finite value;
-// such a segment is scaled by 2^-exp (exact; its largest finite magnitude then lies below 2^15),
-// its first element is replaced by a marker (an fp16 NaN whose low 7 bits are exp) and that
-// element's scaled value goes to C_side[row, col / 8] in fp32.  fp16 keeps 11 significant bits
-// where bf16 keeps 8; the exponent keeps any fp32 range representable, and in the common case
-// nothing but the fp16 values is written.
+// (8 fp16 values, exponent 0) when its largest finite magnitude m is 0 or in [2^-6, 2^15) and it
+// holds no non-finite value; otherwise it is scaled by 2^-exp, exp = floor(log2 m) - 14 (exact; m then
+// lies in [2^14, 2^15)), its first element is replaced by a marker (an fp16 NaN whose low 9 bits are
+// exp + 256) and that element's scaled value goes to C_side[row, col / 8] in fp32.  fp16 keeps 11
+// significant bits where bf16 keeps 8; the exponent keeps any fp32 range representable (tiny segments
+// included), and in the common case nothing but the fp16 values is written.
 constexpr int kOutBf16 = 0, kOutF32 = 1, kOutF16Exp = 2;
-constexpr uint16_t kF16Marker = 0x7E00;  // quiet NaN; low 7 bits: the segment's exponent
+constexpr uint16_t kF16Marker = 0x7E00;  // quiet NaN; low 9 bits: the segment's exponent + 256
+constexpr float kF16Small = 0.015625f;   // 2^-6: smaller maxima are scaled up
+
+// Exponent of a row segment (or of a row's 32 columns of h) with largest finite magnitude m: 0 when m
+// is 0 or in [2^-6, 2^15), else floor(log2 m) - 14 clamped to [-110, 113].
+__device__ __forceinline__ int f16_seg_exponent(float m) {
+  if (m == 0.f || (m >= kF16Small && m < 32768.f)) return 0;
+  const int e = ilogbf(m) - 14;
+  return e < -110 ? -110 : (e > 113 ? 113 : e);
+}
+
+// Whether some aligned group of 8 lanes (a segment) has every bit of mask set.
+__device__ __forceinline__ bool any_full_octet(uint64_t m) {
+  m &= m >> 1;
+  m &= m >> 2;
+  m &= m >> 4;
+  return (m & 0x0101010101010101ull) != 0ull;
+}
 
 // The 8 columns of a segment live in 8 lanes of a quarter (one lane per column, l16 = 8j .. 8j+7):
 // the largest finite magnitude over them, and whether any is non-finite.
@@ -137,16 +174,22 @@ template <int EPI, int OUT, int MI, int NI>
 __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x4 (&acc)[MI][NI], int row_base, int row0,
                                            int rows, int q, const int (&ncol)[NI], const bool (&nvalid)[NI]) {
   const int N = p.N;
-  bool scaled = false;  // kOutF16Exp: some segment of this wave needs an exponent or holds a non-finite value
+  // kOutF16Exp: some segment of this wave may need an exponent (a magnitude of 2^15 or more, a
+  // non-finite value, or all eight below 2^-6)
+  bool scaled = false;
   if (EPI != MOE_EPI_SILU_MUL && OUT == kOutF16Exp) {
-    bool big = false;
+    bool big = false, tiny = false;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) big |= !(fabsf(acc[mi][ni][r]) < 32768.f) && nvalid[ni];
-    scaled = __ballot(big) != 0ull;
+        for (int r = 0; r < 4; ++r) {
+          const float a = nvalid[ni] ? fabsf(acc[mi][ni][r]) : 0.f;
+          big |= !(a < 32768.f);
+          tiny |= any_full_octet(__ballot(a < kF16Small));
+        }
+    scaled = __ballot(big) != 0ull || tiny;
   }
   const int l16 = threadIdx.x & 15;
 #pragma unroll
@@ -165,12 +208,11 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x4 (&acc)
             // every lane takes part in the segment reductions, whatever its row
             bool nonfinite;
             const float m = seg8_max_finite(v, nonfinite);
-            int ex = 0;
-            if (m >= 32768.f) ex = ((int)((__float_as_uint(m) >> 23) & 0xFF) - 127) - 14;
-            v *= __uint_as_float((uint32_t)(127 - ex) << 23);  // exact: 2^-ex, ex <= 113
+            const int ex = f16_seg_exponent(m);
+            v *= pow2f(-ex);  // exact
             bits = f32_to_f16_bits(v);
-            if ((ex > 0 || nonfinite) && (l16 & 7) == 0) {
-              bits = (uint16_t)(kF16Marker | ex);
+            if ((ex != 0 || nonfinite) && (l16 & 7) == 0) {
+              bits = (uint16_t)(kF16Marker | (ex + 256));
               if (row < rows && nvalid[ni]) p.C_side[(size_t)(row0 + row) * (size_t)((N + 7) / 8) + ncol[ni] / 8] = v;
             }
           }
@@ -197,6 +239,151 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x4 (&acc)
         }
       }
     }
+  }
+}
+
+// SiLU*mul output of the fp16 path (GemmArgs::out_f32 == kOutH16): h as fp16 with a signed exponent
+// per row and 32 columns (one wave's gate columns).  The gate and up row sums are first multiplied by
+// the row's power of two (gathered fp16 activations).  A row whose largest finite |h| in the block is
+// 2^15 or more, or below 2^-6 (but not 0), is divided there by 2^exp (f16_seg_exponent; exact
+// scaling into [2^14, 2^15)); other rows keep exp 0.
+// Per tile and block the flag c_blk_flag says whether any row of the block has a nonzero exponent; only
+// then are the block's row exponents written.  With WAVES_M > 1 the waves sharing a block (waves
+// wn, wn + 4, ...) combine their flags through sAny (one barrier; every wave calls this).
+constexpr int kOutH16 = 3;
+constexpr int kHBlock = 32;
+
+template <int MI, int NI, int WAVES_M>
+__device__ __forceinline__ void store_tile_h16(const GemmArgs& p, const f32x4 (&acc)[MI][NI], const float (&rowf)[MI][4],
+                                               int row_base, int row0, int rows, int q, const int (&ncol)[NI],
+                                               const bool (&nvalid)[NI], int tile, int col0_wave, int* sAny) {
+  static_assert(NI == 4, "a wave's gate columns form one 32-column block");
+  const int N2 = p.N / 2;
+  const int lane = threadIdx.x & 63, l16 = lane & 15;
+  const int blk = col0_wave / kHBlock;
+  float hv[MI][2][4];
+  int ex[MI][4];
+  bool any = false;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float m = 0.f;
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const float g = acc[mi][ni][r] * rowf[mi][r], u = acc[mi][ni + 2][r] * rowf[mi][r];
+        const float h = silu_f32(g) * u;
+        hv[mi][ni][r] = h;
+        if (nvalid[ni] && fabsf(h) <= 3.4e38f) m = fmaxf(m, fabsf(h));
+      }
+      // the row's 32 columns live in the 16 lanes of this quarter (two columns each)
+      m = fmaxf(m, __shfl_xor(m, 1));
+      m = fmaxf(m, __shfl_xor(m, 2));
+      m = fmaxf(m, __shfl_xor(m, 4));
+      m = fmaxf(m, __shfl_xor(m, 8));
+      ex[mi][r] = f16_seg_exponent(m);
+      any |= ex[mi][r] != 0 && row_base + mi * 16 + q * 4 + r < rows;
+    }
+  bool flagged = __ballot(any) != 0ull;
+  if constexpr (WAVES_M > 1) {
+    const int wave = threadIdx.x >> 6;
+    if (lane == 0) sAny[wave] = flagged;
+    __syncthreads();
+    flagged = false;
+#pragma unroll
+    for (int j = 0; j < WAVES_M; ++j) flagged |= sAny[(wave & 3) + 4 * j] != 0;
+  }
+  const bool blk_ok = blk * kHBlock < N2;
+  if (lane == 0 && blk_ok && (WAVES_M == 1 || (threadIdx.x >> 6) < 4))
+    p.c_blk_flag[(size_t)tile * p.c_blk_stride + blk] = flagged ? 1 : 0;
+  uint16_t* C = static_cast<uint16_t*>(p.C);
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = row_base + mi * 16 + q * 4 + r;
+      if (row >= rows) continue;
+      const float f = pow2f(-ex[mi][r]);
+      if (flagged && l16 == 0 && blk_ok)
+        p.c_row_blk_exp[(size_t)(row0 + row) * p.c_blk_stride + blk] = (uint8_t)(int8_t)ex[mi][r];
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        if (nvalid[ni]) C[(size_t)(row0 + row) * N2 + ncol[ni]] = f32_to_f16_bits(hv[mi][ni][r] * f);
+    }
+}
+
+// Whether any 32-column block of this tile's fp16 A (identity rows) carries row exponents, from the
+// flags a_blk_flag: computed by the whole workgroup, published through sFlag[wave] by the caller's
+// next barrier.
+__device__ __forceinline__ void tile_blk_exp_flag(const GemmArgs& p, int tile, int* sFlag) {
+  bool any = false;
+  if (p.a_f16 && p.a_blk_flag)
+    for (int i = threadIdx.x; i < p.a_blk_stride; i += blockDim.x) any |= p.a_blk_flag[(size_t)tile * p.a_blk_stride + i] != 0;
+  const uint64_t b = __ballot(any);
+  if ((threadIdx.x & 63) == 0) sFlag[threadIdx.x >> 6] = b != 0ull;
+}
+
+// Row factors 2^exp of gathered fp16 activation rows (a_row_exp, per activation row; 1 without it)
+// for this lane's output rows row_base + mi*16 + q*4 + r of the tile, read at the epilogue.
+template <int MI, int BM>
+__device__ __forceinline__ void gathered_row_factors(const GemmArgs& p, const int32_t (&sRow)[BM], int row_base, int q,
+                                                     float (&f)[MI][4]) {
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f[mi][r] = p.a_row_exp ? pow2f(p.a_row_exp[sRow[row_base + mi * 16 + q * 4 + r]]) : 1.f;
+}
+
+// Row factors 2^exp of block kb (32 columns of K) for this lane's output rows (base + mi*16 + q*4 + r
+// of the tile starting at row0; rows past `rows` read row 0's), 1 when the block is not flagged.
+// Whether any of the K step's four 32-column blocks of this tile's fp16 A carries row exponents.
+__device__ __forceinline__ bool step_blk_flagged(const GemmArgs& p, int tile, int s) {
+  bool f = false;
+#pragma unroll
+  for (int g = 0; g < kBK / kHBlock; ++g) {
+    const int kb = s * (kBK / kHBlock) + g;
+    if (kb < p.a_blk_stride) f |= p.a_blk_flag[(size_t)tile * p.a_blk_stride + kb] != 0;
+  }
+  return f;
+}
+
+// Row exponents of block kb for the four output rows q*4 .. q*4+3 of a 16-row block starting at tile
+// row rbase (rows past the tile repeat row 0); 0 for an unflagged block.
+__device__ __forceinline__ void blk_row_exps4(const GemmArgs& p, int tile, int kb, int rbase, int row0, int rows, int q,
+                                              int (&ex)[4]) {
+  const bool flagged = kb < p.a_blk_stride && p.a_blk_flag[(size_t)tile * p.a_blk_stride + kb] != 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    int row = rbase + q * 4 + r;
+    if (row >= rows) row = 0;
+    ex[r] = flagged ? (int)(int8_t)p.a_row_blk_exp[(size_t)(row0 + row) * p.a_blk_stride + kb] : 0;
+  }
+}
+
+// General form of one K group of the fp16 path.  The group's partial products are exact in fp16 only
+// at a common power of two per output element: 2^(rex[row] + d[col]) with rex the A row's block
+// exponent (identity rows with block exponents, else 0) and d the shift of the column's scale
+// (scale_f16_shift).  The accumulators are brought to that power before the group's MFMAs (sign -1)
+// and back after them (sign +1); both are exact power-of-two scalings (ldexp), so the group's
+// contribution is rounded once, in the MFMA's fp32 accumulation.  The exponents are re-derived on
+// each call rather than kept across the MFMAs, which keeps the fast form's registers free.
+// scale_at(ni) gives the group scale of column block ni, rex_at(mi, rex) the row exponents of the
+// lane's four rows of 16-row block mi.
+template <int MI, int NI, class ScaleAt, class RexAt>
+__device__ __forceinline__ void general_rescale(f32x4 (&acc)[MI][NI], ScaleAt scale_at, RexAt rex_at, int sign) {
+  // (a compiler-only memory barrier: the exponents are derived again rather than carried over)
+  asm volatile("" ::: "memory");
+  int d[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) d[ni] = sign * scale_f16_shift(scale_at(ni));
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    int rex[4];
+    rex_at(mi, rex);
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[mi][ni][r] = ldexpf(acc[mi][ni][r], sign * rex[r] + d[ni]);
   }
 }
 
@@ -383,8 +570,12 @@ constexpr int kLDA = kBK + 8;  // padded LDS activation row of the tiled kernel 
 // One BM x BN output tile (expert e, permuted rows [row0, row0 + rows), N block nb) of the tiled
 // kernel; p is the tile's view of the arguments and sRow already holds the activation row of each
 // tile row (padding rows repeat row 0); it is published by the barrier before the first K step.
-template <int BM, int BN, int WAVES_M, int PF, int EPI, int OUT_F32, int LAYOUT>
-__device__ __forceinline__ void tiled_tile(const GemmArgs& p, int e, int row0, int rows, int nb,
+// F16: the exact fp16 path (GemmArgs::a_f16): fp16 activations, weights dequantized to fp16 as
+// code * scale (exact when the step's scales pass scales_f16_ok, checked per wave and K step), one
+// MFMA per group accumulating in place.  A step whose scales fail the test, or whose A blocks carry
+// row exponents, takes the general form (general_rescale around the same MFMAs).
+template <int BM, int BN, int WAVES_M, int PF, int EPI, int OUT_F32, int LAYOUT, bool F16 = false>
+__device__ __forceinline__ void tiled_tile(const GemmArgs& p, int tile, int e, int row0, int rows, int nb,
                                            uint16_t (&sA)[2][BM * kLDA], const int32_t (&sRow)[BM]) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -403,28 +594,33 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& p, int e, int row0, i
   const int kgroups = K / kGroup;
   const int nks = (K + kBK - 1) / kBK;
 
+  const WBase wb = wbase_of(p, e);
   WRow wr[NI];
-  int ncol[NI];
-  bool nvalid[NI];
   const int col0 = EPI == MOE_EPI_SILU_MUL ? nb * (BN / 2) + wn * (WN / 2) : nb * BN + wn * WN;
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) {
-    int n;
-    column_of<EPI, NI>(p, col0, ni, l16, n, ncol[ni], nvalid[ni]);
-    wr[ni] = wrow_of<LAYOUT>(p, e, n, q, lane);
+    int n, nc;
+    bool nv;
+    column_of<EPI, NI>(p, col0, ni, l16, n, nc, nv);
+    wr[ni] = wrow_of<LAYOUT>(p, n, q, lane);
   }
+  __shared__ int sFlag[4];
+  // row exponents of the K step's four A blocks (tiles whose A blocks carry exponents), per LDS buffer
+  __shared__ int8_t sRex[F16 ? 2 : 1][F16 ? BM * 4 : 1];
+  if (F16) tile_blk_exp_flag(p, tile, sFlag);
   __syncthreads();
+  // (gathered activations carry row exponents only: the block form is for identity rows, never SiLU*mul)
+  // (read through readfirstlane: the branches on it are uniform, which keeps them out of exec masking)
+  const bool hblk = F16 && EPI != MOE_EPI_SILU_MUL &&
+                    __builtin_amdgcn_readfirstlane(sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3]) != 0;
 
+  // thread tid stages chunk column acol of rows tid / 16 + 16 i (256 threads cover 16 rows of 16 chunks)
+  static_assert(kBK / 8 == 16, "16 chunks per activation row of a K step");
+  const int acol = (tid % 16) * 8;
+  const int alds0 = (tid / 16) * LDA + acol;
   const uint16_t* arow[ACH];
-  int acol[ACH], alds[ACH];
 #pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    const int c = tid + 256 * i;
-    const int row = c / (kBK / 8);
-    acol[i] = (c % (kBK / 8)) * 8;
-    alds[i] = row * LDA + acol[i];
-    arow[i] = p.A + (size_t)sRow[row] * K;
-  }
+  for (int i = 0; i < ACH; ++i) arow[i] = p.A + (size_t)sRow[tid / 16 + 16 * i] * K;
 
   f32x4 acc[MI][NI];
 #pragma unroll
@@ -440,32 +636,86 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& p, int e, int row0, i
     s = min(s, nks - 1);  // prefetches past the end re-read the last step (never used)
 #pragma unroll
     for (int i = 0; i < ACH; ++i)
-      areg[u][i] = *reinterpret_cast<const u32x4*>(arow[i] + min(s * kBK + acol[i], K - 8));
+      areg[u][i] = *reinterpret_cast<const u32x4*>(arow[i] + min(s * kBK + acol, K - 8));
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) load_w<LAYOUT>(wr[ni], s, q, kgroups, breg[u][ni], sreg[u][ni]);
+    for (int ni = 0; ni < NI; ++ni) load_w<LAYOUT>(wb, wr[ni], s, q, kgroups, breg[u][ni], sreg[u][ni]);
   };
 
-  auto compute_step = [&](const uint16_t* a_lds, int u) {
+  auto compute_step = [&](const uint16_t* a_lds, int u, int s) {
     u32x4 bt[NI];
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) bt[ni] = b_operands<LAYOUT>(breg[u][ni]);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x8 bf[NI];
-      float sc[NI];
+    if constexpr (F16) {
+      // the step's scales as bf16 pairs: sd[2 ni + h] holds groups 2h (low half) and 2h + 1
+      uint32_t sd[2 * NI];
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
-        bf[ni] = e2m1x8_to_bf16(bt[ni][g]);
-        sc[ni] = scale_of<LAYOUT>(sreg[u][ni], g);
+        sd[2 * ni] = scale_bits_of<LAYOUT>(sreg[u][ni], 0) | (scale_bits_of<LAYOUT>(sreg[u][ni], 1) << 16);
+        sd[2 * ni + 1] = scale_bits_of<LAYOUT>(sreg[u][ni], 2) | (scale_bits_of<LAYOUT>(sreg[u][ni], 3) << 16);
       }
+      const bool general = __builtin_amdgcn_readfirstlane(
+                               __ballot(!scales_f16_ok(sd)) != 0ull || (hblk && step_blk_flagged(p, tile, s))) != 0;
+      // one pass in the fast form, one pass per group in the general form (as in mm_tile)
+      const int npass = general ? 4 : 1;
+      for (int pass = 0; pass < npass; ++pass) {
+        uint32_t sw[2 * NI];
+        auto sc_p = [&](int ni) {
+          const uint32_t d = sd[2 * ni + (pass >> 1)];
+          return __uint_as_float((pass & 1) ? (d & 0xFFFF0000u) : (d << 16));
+        };
+        auto rex_p = [&](int mi, int (&rex)[4]) {
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const bf16x8 af =
-            *reinterpret_cast<const bf16x8*>(&a_lds[(wm * WM + mi * 16 + l16) * LDA + g * 32 + q * 8]);
+          for (int r = 0; r < 4; ++r) rex[r] = hblk ? (int)sRex[s & 1][(wm * WM + mi * 16 + q * 4 + r) * 4 + pass] : 0;
+        };
+        if (general) {
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) {
+            const uint32_t m = scale_f16_mantissa_bits(sc_p(ni)) << (16 * (pass & 1));
+            sw[2 * ni] = (pass >> 1) == 0 ? m : 0u;
+            sw[2 * ni + 1] = (pass >> 1) == 1 ? m : 0u;
+          }
+          general_rescale<MI, NI>(acc, sc_p, rex_p, -1);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 2 * NI; ++i) sw[i] = sd[i];
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f16x8 bf[NI];
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) {
+            const uint32_t d = sw[2 * ni + (g >> 1)];
+            bf[ni] = e2m1x8_to_f16(bt[ni][g], (_Float16)__uint_as_float((g & 1) ? (d & 0xFFFF0000u) : (d << 16)));
+          }
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi) {
+            const f16x8 af =
+                *reinterpret_cast<const f16x8*>(&a_lds[(wm * WM + mi * 16 + l16) * LDA + g * 32 + q * 8]);
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma16x16x32_f16(af, bf[ni], acc[mi][ni]);
+          }
+        }
+        if (general) general_rescale<MI, NI>(acc, sc_p, rex_p, 1);
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x8 bf[NI];
+        float sc[NI];
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
-          const f32x4 part = mfma16x16x32(af, bf[ni], f32x4{0.f, 0.f, 0.f, 0.f});
-          acc[mi][ni] += sc[ni] * part;
+          bf[ni] = e2m1x8_to_bf16(bt[ni][g]);
+          sc[ni] = scale_of<LAYOUT>(sreg[u][ni], g);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          const bf16x8 af =
+              *reinterpret_cast<const bf16x8*>(&a_lds[(wm * WM + mi * 16 + l16) * LDA + g * 32 + q * 8]);
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) {
+            const f32x4 part = mfma16x16x32(af, bf[ni], f32x4{0.f, 0.f, 0.f, 0.f});
+            acc[mi][ni] += sc[ni] * part;
+          }
         }
       }
     }
@@ -482,12 +732,22 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& p, int e, int row0, i
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
       u32x4 v = areg[u][i];
-      if (LAYOUT == kCanonGeneric && s * kBK + acol[i] >= K) v = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&a_lds[alds[i]]) = v;
+      if (LAYOUT == kCanonGeneric && s * kBK + acol >= K) v = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&a_lds[alds0 + 16 * i * LDA]) = v;
+    }
+    if constexpr (F16 && EPI != MOE_EPI_SILU_MUL) {
+      if (hblk) {
+        // thread i < BM * 4: row i / 4 of the tile, block 4 s + i % 4 (rows past the tile read row 0)
+        for (int i = tid; i < BM * 4; i += 256) {
+          const int row = i / 4 < rows ? i / 4 : 0, kb = s * (kBK / kHBlock) + i % 4;
+          const bool f = kb < p.a_blk_stride && p.a_blk_flag[(size_t)tile * p.a_blk_stride + kb] != 0;
+          sRex[s & 1][i] = f ? (int8_t)p.a_row_blk_exp[(size_t)(row0 + row) * p.a_blk_stride + kb] : (int8_t)0;
+        }
+      }
     }
     __syncthreads();
     if (prefetch) load_step(s + PF, (u + PF) % NS);
-    compute_step(a_lds, u);
+    compute_step(a_lds, u, s);
   };
 
 #pragma unroll
@@ -501,12 +761,28 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& p, int e, int row0, i
   for (int u = 0; u < NS - 1; ++u)
     if (s0 + u < nks) step(s0 + u, u, false);
 
-  store_tile<EPI, OUT_F32, MI, NI>(p, acc, wm * WM, row0, rows, q, ncol, nvalid);
+  int ncol[NI];
+  bool nvalid[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    int n;
+    column_of<EPI, NI>(p, col0, ni, l16, n, ncol[ni], nvalid[ni]);
+  }
+  if constexpr (F16 && EPI == MOE_EPI_SILU_MUL) {
+    static_assert(WAVES_M == 1, "one wave per 32-column block of h");
+    float rowf[MI][4];
+    gathered_row_factors<MI>(p, sRow, wm * WM, q, rowf);
+    store_tile_h16<MI, NI, 1>(p, acc, rowf, wm * WM, row0, rows, q, ncol, nvalid, tile, col0, nullptr);
+  } else {
+    store_tile<EPI, OUT_F32, MI, NI>(p, acc, wm * WM, row0, rows, q, ncol, nvalid);
+  }
 }
 
 // RNJ > 0: the launch runs the routing prologue (route_token over 64 * RNJ experts per lane group).
-template <int BM, int BN, int WAVES_M, int PF, int EPI, int OUT_F32, int LAYOUT, int RNJ = 0>
-__global__ __launch_bounds__(256) void gemm_w4a16_tiled(GemmArgs p0) {
+// The fp16 path with packed weights (fp16 h or fp16 O) is held to two workgroups per CU (its register need
+// is just above that budget otherwise, which would halve the CU's waves).
+template <int BM, int BN, int WAVES_M, int PF, int EPI, int OUT_F32, int LAYOUT, int RNJ = 0, bool F16 = false>
+__global__ __launch_bounds__(256, (F16 && LAYOUT == kPacked && OUT_F32 != kOutF32) ? 2 : 1) void gemm_w4a16_tiled(GemmArgs p0) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kLDA];
   __shared__ int32_t sRow[BM];
   const int nbn = EPI == MOE_EPI_SILU_MUL ? (p0.N / 2 + BN / 2 - 1) / (BN / 2) : (p0.N + BN - 1) / BN;
@@ -530,7 +806,7 @@ __global__ __launch_bounds__(256) void gemm_w4a16_tiled(GemmArgs p0) {
     p = tile_view(p0, tile, BM, e, row0, rows);
     for (int i = threadIdx.x; i < BM; i += 256) sRow[i] = a_row(p, row0 + (i < rows ? i : 0));
   }
-  tiled_tile<BM, BN, WAVES_M, PF, EPI, OUT_F32, LAYOUT>(p, e, row0, rows, nb, sA, sRow);
+  tiled_tile<BM, BN, WAVES_M, PF, EPI, OUT_F32, LAYOUT, F16>(p, tile, e, row0, rows, nb, sA, sRow);
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -589,6 +865,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a16_sk(GemmArgs p0) {
   const uint16_t* arow[MI];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) arow[mi] = p.A + (size_t)arow_of[mi] * K + q * 8;
+  const WBase wb = wbase_of(p, e);
   WRow wr[NI];
   int ncol[NI];
   bool nvalid[NI];
@@ -597,7 +874,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a16_sk(GemmArgs p0) {
   for (int ni = 0; ni < NI; ++ni) {
     int n;
     column_of<EPI, NI>(p, col0, ni, l16, n, ncol[ni], nvalid[ni]);
-    wr[ni] = wrow_of<LAYOUT>(p, e, n, q, lane);
+    wr[ni] = wrow_of<LAYOUT>(p, n, q, lane);
   }
 
   f32x4 acc[MI][NI];
@@ -613,7 +890,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a16_sk(GemmArgs p0) {
   auto load_step = [&](int s, int u) {
     s = min(s, s_end - 1);  // prefetches past this wave's range re-read its last step (unused)
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) load_w<LAYOUT>(wr[ni], s, q, kgroups, breg[u][ni], sreg[u][ni]);
+    for (int ni = 0; ni < NI; ++ni) load_w<LAYOUT>(wb, wr[ni], s, q, kgroups, breg[u][ni], sreg[u][ni]);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -704,15 +981,22 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a16_sk(GemmArgs p0) {
 // blocks the XCDs take contiguous shares of the tile list instead, so that none idles.
 
 constexpr int kMmBM = 128, kMmBN = 256;
-constexpr int kMmStage = kMmBM * 256 + (kMmBN / 16) * 1024 + (kMmBN / 16) * 128;  // A + codes + scales
+constexpr int kMmStage = kMmBM * 256 + (kMmBN / 16) * 1024;  // A + codes of one K step
+// Scales travel one K step ahead of A and codes, in a ring of their own (4 slots: the step computed,
+// the next one, whose scales the fp16 path tests meanwhile, and two in flight).
+constexpr int kMmScaleSlot = (kMmBN / 16) * 128, kMmScaleSlots = 4;
+template <int NSTAGE>
+constexpr int mm_lds_bytes() { return NSTAGE * kMmStage + kMmScaleSlots * kMmScaleSlot; }
 
 // One 128 x 256 output tile (tile list entry `tile`, N block `nb`) of the large-tile kernel.
-template <int EPI, int OUT_F32, int NSTAGE>
-__device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, uint8_t (&smem)[NSTAGE * kMmStage],
+// F16: the exact fp16 path as in tiled_tile (fp16 activations in the same LDS layout, weights
+// dequantized to fp16 as code * scale, one MFMA per group accumulating in place, the general form for
+// steps whose scales fail the exactness test or whose A blocks carry row exponents).
+template <int EPI, int OUT_F32, int NSTAGE, bool F16 = false>
+__device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, uint8_t (&smem)[mm_lds_bytes<NSTAGE>()],
                                         int32_t (&sRow)[kMmBM]) {
   constexpr int BM = kMmBM, BN = kMmBN, MI = 4, NI = 4;
   constexpr int A_BYTES = BM * 256;          // 128 rows x 128 K x bf16
-  constexpr int B_BYTES = (BN / 16) * 1024;  // 16 packed code blocks
   constexpr int STAGE = kMmStage;
   int e, row0, rows;
   const GemmArgs p = tile_view(p0, tile, BM, e, row0, rows);
@@ -728,7 +1012,13 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, ui
     const int r = row0 + (i < rows ? i : 0);
     sRow[i] = a_row(p, r);
   }
+  __shared__ int sFlag[8];
+  if (F16) tile_blk_exp_flag(p, tile, sFlag);
   __syncthreads();
+  int any_flag = 0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) any_flag |= sFlag[w];
+  const bool hblk = F16 && EPI != MOE_EPI_SILU_MUL && __builtin_amdgcn_readfirstlane(any_flag) != 0;
 
   // global sources of this wave's direct loads
   const uint16_t* a_src[4];  // activation instructions i = 4*wave + t: rows 4i .. 4i+3
@@ -758,20 +1048,40 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, ui
   const uint8_t* s_src = reinterpret_cast<const uint8_t*>(p.Ws) +
                          ((size_t)e * NB16 + block_row(8 * (wave & 1) + (lane >> 3))) * (size_t)nks * 128 + (lane & 7) * 16;
 
+  // LDS blocks of this wave's 4 column blocks
+  int blk[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+    blk[ni] = EPI == MOE_EPI_SILU_MUL ? (ni < 2 ? 2 * wn + ni : 8 + 2 * wn + (ni - 2)) : 4 * wn + ni;
+
+  uint8_t* const sring = smem + NSTAGE * STAGE;
+  auto issue_scales = [&](int ks) {
+    if (wave < 2) g2lds16(s_src + (size_t)ks * 128, sring + (ks % kMmScaleSlots) * kMmScaleSlot + wave * 1024);
+  };
+  // A and codes of step ks into stage `stage`, and the scales of step ks + 1
   auto issue = [&](int ks, int stage) {
     uint8_t* st = smem + stage * STAGE;
 #pragma unroll
     for (int t = 0; t < 4; ++t) g2lds16(a_src[t] + (size_t)ks * kBK, st + (4 * wave + t) * 1024);
 #pragma unroll
     for (int t = 0; t < 2; ++t) g2lds16(b_src[t] + (size_t)ks * 1024, st + A_BYTES + (2 * wave + t) * 1024);
-    if (wave < 2) g2lds16(s_src + (size_t)ks * 128, st + A_BYTES + B_BYTES + wave * 1024);
+    if (ks + 1 < nks) issue_scales(ks + 1);
   };
-
-  // LDS blocks of this wave's 4 column blocks
-  int blk[NI];
+  auto scales_of = [&](int s, int ni) -> u32x2 {
+    return *reinterpret_cast<const u32x2*>(sring + (s % kMmScaleSlots) * kMmScaleSlot + blk[ni] * 128 + l16 * 8);
+  };
+  // fp16 path: whether step s, with this wave's scales sc, takes the general form (scales outside
+  // fp16's exact range, or A blocks with row exponents), wave-uniform
+  auto general_of = [&](int s, const u32x2 (&sc)[NI]) -> bool {
+    uint32_t sd[2 * NI];
 #pragma unroll
-  for (int ni = 0; ni < NI; ++ni)
-    blk[ni] = EPI == MOE_EPI_SILU_MUL ? (ni < 2 ? 2 * wn + ni : 8 + 2 * wn + (ni - 2)) : 4 * wn + ni;
+    for (int ni = 0; ni < NI; ++ni) {
+      sd[2 * ni] = sc[ni][0];
+      sd[2 * ni + 1] = sc[ni][1];
+    }
+    return __builtin_amdgcn_readfirstlane(__ballot(!scales_f16_ok(sd)) != 0ull ||
+                                          (hblk && step_blk_flagged(p, tile, s))) != 0;
+  };
 
   f32x4 acc[MI][NI];
 #pragma unroll
@@ -793,14 +1103,74 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, ui
     pend[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto compute = [&](int stage) {
+  // sc: this wave's scales of step s (the fp16 path reads them one step ahead)
+  auto compute = [&](int stage, int s, bool general, const u32x2 (&sc)[NI]) {
     const uint8_t* st = smem + stage * STAGE;
     u32x4 braw[NI];
     u32x2 sraw[NI];
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       braw[ni] = *reinterpret_cast<const u32x4*>(st + A_BYTES + blk[ni] * 1024 + lane * 16);
-      sraw[ni] = *reinterpret_cast<const u32x2*>(st + A_BYTES + B_BYTES + blk[ni] * 128 + l16 * 8);
+      sraw[ni] = F16 ? sc[ni] : scales_of(s, ni);
+    }
+    if constexpr (F16) {
+      uint32_t sd[2 * NI];
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        sd[2 * ni] = sraw[ni][0];
+        sd[2 * ni + 1] = sraw[ni][1];
+      }
+      // One pass over the step's four groups in the fast form; in the general form one pass per group
+      // (the other groups' scales zeroed), with the accumulators rescaled around the pass.  The MFMA
+      // sequence is the same straight-line block either way.
+      const int npass = general ? 4 : 1;
+      for (int pass = 0; pass < npass; ++pass) {
+        uint32_t sw[2 * NI];
+        auto sc_p = [&](int ni) {
+          const uint32_t d = sd[2 * ni + (pass >> 1)];
+          return __uint_as_float((pass & 1) ? (d & 0xFFFF0000u) : (d << 16));
+        };
+        auto rex_p = [&](int mi, int (&rex)[4]) {
+          if (hblk) {
+            blk_row_exps4(p, tile, s * (kBK / kHBlock) + pass, wm * 64 + mi * 16, row0, rows, q, rex);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rex[r] = 0;
+          }
+        };
+        if (general) {
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) {
+            const uint32_t m = scale_f16_mantissa_bits(sc_p(ni)) << (16 * (pass & 1));
+            sw[2 * ni] = (pass >> 1) == 0 ? m : 0u;
+            sw[2 * ni + 1] = (pass >> 1) == 1 ? m : 0u;
+          }
+          general_rescale<MI, NI>(acc, sc_p, rex_p, -1);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 2 * NI; ++i) sw[i] = sd[i];
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f16x8 af[MI], bf[NI];
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi) {
+            const int r = wm * 64 + mi * 16 + l16;  // r % 16 == l16
+            af[mi] = *reinterpret_cast<const f16x8*>(st + r * 256 + (((g * 4 + q) ^ l16) * 16));
+          }
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) {
+            const uint32_t d = sw[2 * ni + (g >> 1)];
+            bf[ni] = e2m1x8_to_f16(braw[ni][g], (_Float16)__uint_as_float((g & 1) ? (d & 0xFFFF0000u) : (d << 16)));
+          }
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma16x16x32_f16(af[mi], bf[ni], acc[mi][ni]);
+        }
+        if (general) general_rescale<MI, NI>(acc, sc_p, rex_p, 1);
+      }
+      return;
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -835,17 +1205,37 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, ui
     }
   };
 
-  // Per-step direct loads of each wave: 6 (waves 2..7) or 7 (waves 0, 1).  Step s lives in stage
-  // s % NSTAGE.  The waits are explicit: a stage is read after this wave's loads for it have landed
-  // (at most the next step's loads still in flight) and after the barrier that publishes everyone's.
+  // Per-step direct loads of each wave: 6 (waves 2..7) or at most 7 (waves 0, 1).  Step s lives in
+  // stage s % NSTAGE, its scales in slot s % 4, loaded with the previous step.  The waits are explicit:
+  // a stage is read after this wave's loads for it (and for the next step's scales) have landed (at
+  // most the next step's loads still in flight) and after the barrier that publishes everyone's.
+  issue_scales(0);
   issue(0, 0);
   if (nks > 1) issue(1, 1);
+  // fp16 path: the next step's scales are read into registers before this step's MFMAs and tested
+  // behind them, so neither the LDS read nor the test delays the MFMAs
+  bool general = false;
+  u32x2 snext[NI];
   for (int s = 0; s < nks; ++s) {
     if (s + 1 < nks) wait_vmcnt<6>();
     else wait_vmcnt<0>();
     __syncthreads();
     if (s + 2 < nks) issue(s + 2, (s + 2) % NSTAGE);
-    compute(s % NSTAGE);
+    u32x2 scur[NI];
+    if constexpr (F16) {
+      if (s == 0) {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) snext[ni] = scales_of(0, ni);
+        general = general_of(0, snext);
+      }
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        scur[ni] = snext[ni];
+        if (s + 1 < nks) snext[ni] = scales_of(s + 1, ni);
+      }
+    }
+    compute(s % NSTAGE, s, general, scur);
+    if (F16) general = s + 1 < nks && general_of(s + 1, snext);
   }
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) acc[MI - 1][ni] += psc[ni] * pend[ni];
@@ -858,19 +1248,25 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, ui
     int n;
     column_of<EPI, NI>(p, col0, ni, l16, n, ncol[ni], nvalid[ni]);
   }
-  store_tile<EPI, OUT_F32, MI, NI>(p, acc, wm * 64, row0, rows, q, ncol, nvalid);
+  if constexpr (F16 && EPI == MOE_EPI_SILU_MUL) {
+    float rowf[MI][4];
+    gathered_row_factors<MI>(p, sRow, wm * 64, q, rowf);
+    store_tile_h16<MI, NI, 2>(p, acc, rowf, wm * 64, row0, rows, q, ncol, nvalid, tile, col0, sFlag);
+  } else {
+    store_tile<EPI, OUT_F32, MI, NI>(p, acc, wm * 64, row0, rows, q, ncol, nvalid);
+  }
 }
 
-template <int EPI, int OUT_F32, int NSTAGE>
+template <int EPI, int OUT_F32, int NSTAGE, bool F16 = false>
 __global__ __launch_bounds__(512) void gemm_w4a16_mm(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * kMmStage];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[mm_lds_bytes<NSTAGE>()];
   __shared__ int32_t sRow[kMmBM];
   const int ncols = EPI == MOE_EPI_SILU_MUL ? p.N / 2 : p.N;
   const int bcols = EPI == MOE_EPI_SILU_MUL ? kMmBN / 2 : kMmBN;
   const int nbn = (ncols + bcols - 1) / bcols;
   int tile, nb;
   if (!mm_work(linear_block(), nbn, tile_count(p, kMmBM), tile, nb)) return;
-  mm_tile<EPI, OUT_F32, NSTAGE>(p, tile, nb, smem, sRow);
+  mm_tile<EPI, OUT_F32, NSTAGE, F16>(p, tile, nb, smem, sRow);
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -890,9 +1286,9 @@ static dim3 grid_of(const GemmArgs& a, int bn) {
 
 template <int BM, int BN, int WAVES_M, int PF>
 struct Tiled {
-  template <int EPI, int F32, int LAYOUT, int RNJ = 0>
+  template <int EPI, int F32, int LAYOUT, int RNJ = 0, bool F16 = false>
   static hipError_t run(const GemmArgs& a, hipStream_t s) {
-    gemm_w4a16_tiled<BM, BN, WAVES_M, PF, EPI, F32, LAYOUT, RNJ><<<grid_of(a, BN), 256, 0, s>>>(a);
+    gemm_w4a16_tiled<BM, BN, WAVES_M, PF, EPI, F32, LAYOUT, RNJ, F16><<<grid_of(a, BN), 256, 0, s>>>(a);
     return hipGetLastError();
   }
 };
@@ -939,6 +1335,23 @@ static hipError_t routed(const GemmArgs& a, hipStream_t s) {
   }
 }
 
+// The fp16 path (a.a_f16) of a tiled configuration: SiLU*mul writes fp16 h with block exponents.
+template <class Cfg, int EPI, int F32>
+static hipError_t by_layout_f16(const GemmArgs& a, hipStream_t s) {
+  switch (layout_of(a)) {
+    case kPacked: return Cfg::template run<EPI, F32, kPacked, 0, true>(a, s);
+    case kCanonFull: return Cfg::template run<EPI, F32, kCanonFull, 0, true>(a, s);
+    default: return Cfg::template run<EPI, F32, kCanonGeneric, 0, true>(a, s);
+  }
+}
+
+template <class Cfg>
+static hipError_t by_variant_f16(const GemmArgs& a, hipStream_t s) {
+  if (a.epilogue == MOE_EPI_SILU_MUL) return by_layout_f16<Cfg, MOE_EPI_SILU_MUL, kOutH16>(a, s);
+  if (a.out_f32 == kOutF16Exp) return by_layout_f16<Cfg, MOE_EPI_NONE, kOutF16Exp>(a, s);
+  return by_layout_f16<Cfg, MOE_EPI_NONE, kOutF32>(a, s);
+}
+
 template <class Cfg>
 static hipError_t by_variant(const GemmArgs& a, hipStream_t s) {
   if (a.epilogue == MOE_EPI_SILU_MUL) return by_layout<Cfg, MOE_EPI_SILU_MUL, kOutBf16>(a, s);
@@ -947,17 +1360,28 @@ static hipError_t by_variant(const GemmArgs& a, hipStream_t s) {
   return by_layout<Cfg, MOE_EPI_NONE, kOutBf16>(a, s);
 }
 
-template <int EPI, int F32>
+template <int EPI, int F32, bool F16 = false>
 static hipError_t launch_mm(const GemmArgs& a, hipStream_t s) {
   const int ncols = EPI == MOE_EPI_SILU_MUL ? a.N / 2 : a.N;
   const int bcols = EPI == MOE_EPI_SILU_MUL ? 128 : 256;
   const int nbn = (ncols + bcols - 1) / bcols;
-  gemm_w4a16_mm<EPI, F32, 3><<<mm_grid(nbn, a.max_tiles), 512, 0, s>>>(a);
+  gemm_w4a16_mm<EPI, F32, 3, F16><<<mm_grid(nbn, a.max_tiles), 512, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t stream) {
   if (a.max_tiles <= 0) return hipSuccess;
+  // weight rows are addressed by 32-bit offsets within an expert (WRow)
+  if ((size_t)a.N * (size_t)a.K / 2 > 0xFFFFF000ull) return hipErrorInvalidValue;
+  if (a.a_f16) {
+    // the exact fp16 path: 128-row tiles (packed weights) or 64-row tiles (checked by the caller)
+    if (block_m == 128) {
+      if (a.epilogue == MOE_EPI_SILU_MUL) return launch_mm<MOE_EPI_SILU_MUL, kOutH16, true>(a, stream);
+      if (a.out_f32 == kOutF16Exp) return launch_mm<MOE_EPI_NONE, kOutF16Exp, true>(a, stream);
+      return launch_mm<MOE_EPI_NONE, kOutF32, true>(a, stream);
+    }
+    return by_variant_f16<Tiled<64, 256, 1, 1>>(a, stream);
+  }
   // (packed SiLU*mul needs N % 32 == 0, checked by the caller: up rows start a 16-row block)
   if (block_m == 128 && a.packed) {
     if (a.epilogue == MOE_EPI_SILU_MUL) return launch_mm<MOE_EPI_SILU_MUL, kOutBf16>(a, stream);

@@ -76,6 +76,24 @@ struct GemmArgs {
   int32_t* route_inv;         // [T * k]
   // out_f32 == 2: fp32 values of the marked elements, [rows, ceil(N / 8)] (see kOutF16Exp)
   float* C_side;
+  // The exact fp16 path (64- and 128-row tile kernels; a_f16 != 0): A holds fp16 values.
+  //  * Gathered rows (a_row_of set, or the shared expert's token rows): activation row a is
+  //    A[a] * 2^a_row_exp[a] (launch_x_to_f16); the row sums are multiplied by that power of two.
+  //  * Identity rows (h), in blocks of 32 columns of K: a_blk_flag[tile * a_blk_stride + kk / 32]
+  //    says whether any row of the tile carries an exponent in that block; if so, row r's values
+  //    there are A * 2^a_row_blk_exp[r * a_blk_stride + kk / 32].
+  //  * SILU_MUL output (out_f32 == 3): h as fp16 [rows, N/2]; per row and 32 columns the values are
+  //    divided by 2^exp first, exp = 0 unless the row's largest finite |h| there reached 2^15; the
+  //    flags c_blk_flag [tiles, c_blk_stride] are always written, the exponents c_row_blk_exp
+  //    [rows, c_blk_stride] only for flagged blocks.
+  int a_f16;
+  const int32_t* a_row_exp;
+  const uint8_t* a_blk_flag;
+  const uint8_t* a_row_blk_exp;
+  int a_blk_stride;
+  uint8_t* c_blk_flag;
+  uint8_t* c_row_blk_exp;
+  int c_blk_stride;
 };
 // Batches the routing prologue serves: at most 16 tokens (so every expert fits one 16-row tile),
 // k <= 16, E <= 512.
@@ -84,6 +102,8 @@ inline bool route_prologue_fits(int T, int E, int k) {
   return T >= 1 && T <= kRouteMaxT && k <= kRouteMaxK && E <= kAlignSingleMaxE;
 }
 hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t stream);
+// bf16 x [T, H] -> fp16 x16 [T, H] and row exponents xexp [T]: x16 = fp16(x * 2^-xexp) (convert.hip).
+hipError_t launch_x_to_f16(const uint16_t* x, int T, int H, uint16_t* x16, int32_t* xexp, hipStream_t stream);
 
 // MXFP4 (W4A4) grouped GEMM: activations and weights as E2M1 codes with E8M0 scale bytes per 32 K.
 struct MxGemmArgs {

@@ -52,6 +52,66 @@ __device__ __forceinline__ bf16x8 e2m1x8_to_bf16(uint32_t w) {
   return r;
 }
 
+// ---- fp16 operands (the exact fp16 path of the 64- and 128-row tile kernels) ---------------------
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// A bf16 group scale whose products with every E2M1 value are exact in fp16 has an exponent in
+// [-16, 12] (then the scale is exact in fp16, 6 * scale stays below fp16's largest finite value and
+// 0.5 * scale keeps its lowest bit at or above 2^-24).  For a positive scale that is the bit range
+// [0x3780, 0x4600).  Whether all scales of the given dwords (two bf16 scales each) pass: the bits
+// minus 0x3780 as unsigned 16-bit lanes, largest below 0x0E80.  Zero, negative, subnormal and
+// non-finite scales fail (the general form handles them).
+template <int N>
+__device__ __forceinline__ bool scales_f16_ok(const uint32_t (&v)[N]) {
+  u16x2 worst = u16x2{0, 0};
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    worst = __builtin_elementwise_max(worst, __builtin_bit_cast(u16x2, v[i]) - u16x2{0x3780, 0x3780});
+  return worst[0] < 0x0E80 && worst[1] < 0x0E80;
+}
+
+// The general form's split of a scale into m * 2^d with m's exponent in [-16, 12] (so code * m is
+// exact in fp16); d = 0 for scales already in range and for zero and non-finite scales.
+__device__ __forceinline__ int scale_f16_shift(float sc) {
+  const int e = __builtin_amdgcn_frexp_expf(sc) - 1;  // |sc| in [2^e, 2^(e+1)); 0 -> -1, inf/nan -> -1
+  return e > 12 ? e - 12 : (e < -16 ? e + 16 : 0);
+}
+
+// bf16 bits of m = sc * 2^-scale_f16_shift(sc) (exact: m keeps sc's eight significant bits).
+__device__ __forceinline__ uint32_t scale_f16_mantissa_bits(float sc) {
+  return __float_as_uint(ldexpf(sc, -scale_f16_shift(sc))) >> 16;
+}
+
+// Eight E2M1 codes -> eight fp16 values code * scale: the hardware converter at unit scale gives the
+// exact E2M1 values (it applies only the exponent of a scale operand, so the scale is not given to
+// it), then one packed fp16 multiply by the scale per pair, exact for scales with an exponent in
+// [-16, 12].
+__device__ __forceinline__ f16x8 e2m1x8_to_f16(uint32_t w, _Float16 sc) {
+  f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+  f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+  f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+  f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  const f16x2 s2 = f16x2{sc, sc};
+  p0 *= s2;
+  p1 *= s2;
+  p2 *= s2;
+  p3 *= s2;
+  f16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 2^e as fp32 for -126 <= e <= 127 (exact).
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
+
 // 4x4 transpose of dwords across the four 16-lane quarters of a wave.
 // Before: quarter q, register j holds dword j of K-group q (one 16-byte load per lane).
 // After:  register g, quarter q holds dword q of K-group g, which is the B-operand layout of
