@@ -980,59 +980,91 @@ __global__ __launch_bounds__(64 * KW) void gemm_w4a16_sk(GemmArgs p0) {
 // activations are fetched into that XCD's L2 once and reused by all of its N blocks; with fewer N
 // blocks the XCDs take contiguous shares of the tile list instead, so that none idles.
 
-constexpr int kMmBM = 128, kMmBN = 256;
-constexpr int kMmStage = kMmBM * 256 + (kMmBN / 16) * 1024;  // A + codes of one K step
-// Scales travel one K step ahead of A and codes, in a ring of their own (4 slots: the step computed,
-// the next one, whose scales the fp16 path tests meanwhile, and two in flight).
-constexpr int kMmScaleSlot = (kMmBN / 16) * 128, kMmScaleSlots = 4;
-template <int NSTAGE>
-constexpr int mm_lds_bytes() { return NSTAGE * kMmStage + kMmScaleSlots * kMmScaleSlot; }
+// Shape of a direct-load tile kernel: BM x BN output tile per workgroup of WAVES_M x WAVES_N waves,
+// NSTAGE LDS stages of activations and codes.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int NSTAGE_>
+struct MmCfg {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NSTAGE = NSTAGE_;
+  static constexpr int NW = WAVES_M * WAVES_N, THREADS = 64 * NW;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, MI = WM / 16, NI = WN / 16;
+  static constexpr int CB = BN / 16;      // 16-row code blocks per stage
+  static constexpr int AI = BM / 4 / NW;  // activation loads per wave and step (4 rows of 256 bytes each)
+  static constexpr int BI = CB / NW;      // code block loads per wave and step
+  static constexpr int SI = CB / 8;       // scale loads per step (1 KiB each, waves 0 .. SI-1)
+  static constexpr int A_BYTES = BM * 256, STAGE = A_BYTES + CB * 1024;
+  // Scales travel one K step ahead of activations and codes, in a ring of their own: at step s the
+  // slots of steps s (computed), s + 1 (tested meanwhile by the fp16 path, or in flight) up to
+  // s + NSTAGE (issued at step s) are live, NSTAGE + 1 slots.
+  static constexpr int SCALE_SLOT = CB * 128, SCALE_SLOTS = NSTAGE + 1;
+  static constexpr int LDS = NSTAGE * STAGE + SCALE_SLOTS * SCALE_SLOT;
+  static_assert(MI >= 1 && NI >= 2 && NI % 2 == 0 && AI >= 1 && BI >= 1 && SI >= 1 && SI <= NW, "tile shape");
+  static_assert(AI * NW * 4 == BM && BI * NW == CB && SI * 8 == CB, "loads cover the stage");
+  static_assert(NSTAGE >= 3 && NSTAGE <= 5, "stages");
+};
+// 128 x 256 tiles, 8 waves, for MFMA-bound shapes.  (32 x 128 tiles in this form, 4 waves with 3 or 4
+// stages, were measured on MI355X at 800 tokens over 256 experts: gate_up 90.2 / 95.5 us against
+// 87.7 us for the register-staged tiled kernel.)
+using MmLarge = MmCfg<128, 256, 2, 4, 3>;
 
-// One 128 x 256 output tile (tile list entry `tile`, N block `nb`) of the large-tile kernel.
+// s_waitcnt for `later` K steps' loads still in flight (at most MAXL), X loads per step.
+template <int X, int MAXL>
+__device__ __forceinline__ void wait_steps(int later) {
+  if constexpr (MAXL == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (later >= MAXL) wait_vmcnt<X * MAXL>();
+    else wait_steps<X, MAXL - 1>(later);
+  }
+}
+
+// One BM x BN output tile (tile list entry `tile`, N block `nb`) of a direct-load tile kernel.
 // F16: the exact fp16 path as in tiled_tile (fp16 activations in the same LDS layout, weights
 // dequantized to fp16 as code * scale, one MFMA per group accumulating in place, the general form for
 // steps whose scales fail the exactness test or whose A blocks carry row exponents).
-template <int EPI, int OUT_F32, int NSTAGE, bool F16 = false>
-__device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, uint8_t (&smem)[mm_lds_bytes<NSTAGE>()],
-                                        int32_t (&sRow)[kMmBM]) {
-  constexpr int BM = kMmBM, BN = kMmBN, MI = 4, NI = 4;
-  constexpr int A_BYTES = BM * 256;          // 128 rows x 128 K x bf16
-  constexpr int STAGE = kMmStage;
+template <class Cfg, int EPI, int OUT_F32, bool F16 = false>
+__device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, uint8_t (&smem)[Cfg::LDS],
+                                        int32_t (&sRow)[Cfg::BM]) {
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, MI = Cfg::MI, NI = Cfg::NI, NW = Cfg::NW, NSTAGE = Cfg::NSTAGE;
+  constexpr int WM = Cfg::WM, WN = Cfg::WN, CB = Cfg::CB, AI = Cfg::AI, BI = Cfg::BI, SI = Cfg::SI;
+  constexpr int A_BYTES = Cfg::A_BYTES, STAGE = Cfg::STAGE;
+  static_assert(!F16 || (NI == 4 && Cfg::WAVES_M == 2), "the fp16 path's h blocks: one wave's 32 gate columns");
   int e, row0, rows;
   const GemmArgs p = tile_view(p0, tile, BM, e, row0, rows);
   const int N = p.N, K = p.K;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
   const int l16 = lane & 15, q = lane >> 4;
   const int nks = K / kBK;
   const int NB16 = N / 16;
 
-  for (int i = tid; i < BM; i += 512) {
+  for (int i = tid; i < BM; i += Cfg::THREADS) {
     const int r = row0 + (i < rows ? i : 0);
     sRow[i] = a_row(p, r);
   }
-  __shared__ int sFlag[8];
+  __shared__ int sFlag[NW];
   if (F16) tile_blk_exp_flag(p, tile, sFlag);
   __syncthreads();
   int any_flag = 0;
+  if constexpr (F16) {
 #pragma unroll
-  for (int w = 0; w < 8; ++w) any_flag |= sFlag[w];
+    for (int w = 0; w < NW; ++w) any_flag |= sFlag[w];
+  }
   const bool hblk = F16 && EPI != MOE_EPI_SILU_MUL && __builtin_amdgcn_readfirstlane(any_flag) != 0;
 
   // global sources of this wave's direct loads
-  const uint16_t* a_src[4];  // activation instructions i = 4*wave + t: rows 4i .. 4i+3
+  const uint16_t* a_src[AI];  // activation instructions i = AI*wave + t: rows 4i .. 4i+3
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int r = 4 * (4 * wave + t) + (lane >> 4);
+  for (int t = 0; t < AI; ++t) {
+    const int r = 4 * (AI * wave + t) + (lane >> 4);
     const int c = (lane & 15) ^ (r & 15);
     a_src[t] = p.A + (size_t)sRow[r] * K + c * 8;
   }
   auto block_row = [&](int blk) -> int {  // packed row-block index of LDS block blk (clamped)
     int rb, first;
     if (EPI == MOE_EPI_SILU_MUL) {
-      first = nb * (BN / 2) + (blk & 7) * 16;
-      rb = (blk < 8 ? first : N / 2 + first) / 16;
+      first = nb * (BN / 2) + (blk % (CB / 2)) * 16;
+      rb = (blk < CB / 2 ? first : N / 2 + first) / 16;
       if (first >= N / 2) rb = 0;
     } else {
       first = nb * BN + blk * 16;
@@ -1041,34 +1073,37 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, ui
     }
     return rb;
   };
-  const uint8_t* b_src[2];
+  const uint8_t* b_src[BI];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-    b_src[t] = p.Wq + ((size_t)e * NB16 + block_row(2 * wave + t)) * (size_t)nks * 1024 + lane * 16;
+  for (int t = 0; t < BI; ++t)
+    b_src[t] = p.Wq + ((size_t)e * NB16 + block_row(BI * wave + t)) * (size_t)nks * 1024 + lane * 16;
   const uint8_t* s_src = reinterpret_cast<const uint8_t*>(p.Ws) +
-                         ((size_t)e * NB16 + block_row(8 * (wave & 1) + (lane >> 3))) * (size_t)nks * 128 + (lane & 7) * 16;
+                         ((size_t)e * NB16 + block_row(8 * (wave % SI) + (lane >> 3))) * (size_t)nks * 128 +
+                         (lane & 7) * 16;
 
-  // LDS blocks of this wave's 4 column blocks
+  // LDS blocks of this wave's column blocks (SiLU*mul: NI/2 gate blocks, then the matching up blocks)
   int blk[NI];
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni)
-    blk[ni] = EPI == MOE_EPI_SILU_MUL ? (ni < 2 ? 2 * wn + ni : 8 + 2 * wn + (ni - 2)) : 4 * wn + ni;
+    blk[ni] = EPI == MOE_EPI_SILU_MUL ? (ni < NI / 2 ? wn * (NI / 2) + ni : CB / 2 + wn * (NI / 2) + (ni - NI / 2))
+                                      : wn * NI + ni;
 
   uint8_t* const sring = smem + NSTAGE * STAGE;
   auto issue_scales = [&](int ks) {
-    if (wave < 2) g2lds16(s_src + (size_t)ks * 128, sring + (ks % kMmScaleSlots) * kMmScaleSlot + wave * 1024);
+    if (wave < SI)
+      g2lds16(s_src + (size_t)ks * 128, sring + (ks % Cfg::SCALE_SLOTS) * Cfg::SCALE_SLOT + wave * 1024);
   };
   // A and codes of step ks into stage `stage`, and the scales of step ks + 1
   auto issue = [&](int ks, int stage) {
     uint8_t* st = smem + stage * STAGE;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) g2lds16(a_src[t] + (size_t)ks * kBK, st + (4 * wave + t) * 1024);
+    for (int t = 0; t < AI; ++t) g2lds16(a_src[t] + (size_t)ks * kBK, st + (AI * wave + t) * 1024);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) g2lds16(b_src[t] + (size_t)ks * 1024, st + A_BYTES + (2 * wave + t) * 1024);
+    for (int t = 0; t < BI; ++t) g2lds16(b_src[t] + (size_t)ks * 1024, st + A_BYTES + (BI * wave + t) * 1024);
     if (ks + 1 < nks) issue_scales(ks + 1);
   };
   auto scales_of = [&](int s, int ni) -> u32x2 {
-    return *reinterpret_cast<const u32x2*>(sring + (s % kMmScaleSlots) * kMmScaleSlot + blk[ni] * 128 + l16 * 8);
+    return *reinterpret_cast<const u32x2*>(sring + (s % Cfg::SCALE_SLOTS) * Cfg::SCALE_SLOT + blk[ni] * 128 + l16 * 8);
   };
   // fp16 path: whether step s, with this wave's scales sc, takes the general form (scales outside
   // fp16's exact range, or A blocks with row exponents), wave-uniform
@@ -1132,7 +1167,7 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, ui
         };
         auto rex_p = [&](int mi, int (&rex)[4]) {
           if (hblk) {
-            blk_row_exps4(p, tile, s * (kBK / kHBlock) + pass, wm * 64 + mi * 16, row0, rows, q, rex);
+            blk_row_exps4(p, tile, s * (kBK / kHBlock) + pass, wm * WM + mi * 16, row0, rows, q, rex);
           } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) rex[r] = 0;
@@ -1155,7 +1190,7 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, ui
           f16x8 af[MI], bf[NI];
 #pragma unroll
           for (int mi = 0; mi < MI; ++mi) {
-            const int r = wm * 64 + mi * 16 + l16;  // r % 16 == l16
+            const int r = wm * WM + mi * 16 + l16;  // r % 16 == l16
             af[mi] = *reinterpret_cast<const f16x8*>(st + r * 256 + (((g * 4 + q) ^ l16) * 16));
           }
 #pragma unroll
@@ -1178,7 +1213,7 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, ui
       float sc[NI];
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
-        const int r = wm * 64 + mi * 16 + l16;  // r % 16 == l16
+        const int r = wm * WM + mi * 16 + l16;  // r % 16 == l16
         af[mi] = *reinterpret_cast<const bf16x8*>(st + r * 256 + (((g * 4 + q) ^ l16) * 16));
       }
 #pragma unroll
@@ -1205,22 +1240,23 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, ui
     }
   };
 
-  // Per-step direct loads of each wave: 6 (waves 2..7) or at most 7 (waves 0, 1).  Step s lives in
-  // stage s % NSTAGE, its scales in slot s % 4, loaded with the previous step.  The waits are explicit:
-  // a stage is read after this wave's loads for it (and for the next step's scales) have landed (at
-  // most the next step's loads still in flight) and after the barrier that publishes everyone's.
+  // Per-step direct loads of each wave: AI + BI, one more for the waves that load scales.  Step s
+  // lives in stage s % NSTAGE, its scales in slot s % 4, loaded with the previous step; steps
+  // s+1 .. s+NSTAGE-2 are in flight while step s is computed.  The waits are explicit: a stage is read
+  // after this wave's loads for it (and for the next step's scales) have landed (only later steps'
+  // loads still in flight) and after the barrier that publishes everyone's.
   issue_scales(0);
-  issue(0, 0);
-  if (nks > 1) issue(1, 1);
+#pragma unroll
+  for (int u = 0; u < NSTAGE - 1; ++u)
+    if (u < nks) issue(u, u);
   // fp16 path: the next step's scales are read into registers before this step's MFMAs and tested
   // behind them, so neither the LDS read nor the test delays the MFMAs
   bool general = false;
   u32x2 snext[NI];
   for (int s = 0; s < nks; ++s) {
-    if (s + 1 < nks) wait_vmcnt<6>();
-    else wait_vmcnt<0>();
+    wait_steps<AI + BI, NSTAGE - 2>(min(NSTAGE - 2, nks - 1 - s));
     __syncthreads();
-    if (s + 2 < nks) issue(s + 2, (s + 2) % NSTAGE);
+    if (s + NSTAGE - 1 < nks) issue(s + NSTAGE - 1, (s + NSTAGE - 1) % NSTAGE);
     u32x2 scur[NI];
     if constexpr (F16) {
       if (s == 0) {
@@ -1242,7 +1278,7 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, ui
 
   int ncol[NI];
   bool nvalid[NI];
-  const int col0 = EPI == MOE_EPI_SILU_MUL ? nb * (BN / 2) + wn * 32 : nb * BN + wn * 64;
+  const int col0 = EPI == MOE_EPI_SILU_MUL ? nb * (BN / 2) + wn * (WN / 2) : nb * BN + wn * WN;
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) {
     int n;
@@ -1250,23 +1286,23 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, ui
   }
   if constexpr (F16 && EPI == MOE_EPI_SILU_MUL) {
     float rowf[MI][4];
-    gathered_row_factors<MI>(p, sRow, wm * 64, q, rowf);
-    store_tile_h16<MI, NI, 2>(p, acc, rowf, wm * 64, row0, rows, q, ncol, nvalid, tile, col0, sFlag);
+    gathered_row_factors<MI>(p, sRow, wm * WM, q, rowf);
+    store_tile_h16<MI, NI, Cfg::WAVES_M>(p, acc, rowf, wm * WM, row0, rows, q, ncol, nvalid, tile, col0, sFlag);
   } else {
-    store_tile<EPI, OUT_F32, MI, NI>(p, acc, wm * 64, row0, rows, q, ncol, nvalid);
+    store_tile<EPI, OUT_F32, MI, NI>(p, acc, wm * WM, row0, rows, q, ncol, nvalid);
   }
 }
 
-template <int EPI, int OUT_F32, int NSTAGE, bool F16 = false>
-__global__ __launch_bounds__(512) void gemm_w4a16_mm(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[mm_lds_bytes<NSTAGE>()];
-  __shared__ int32_t sRow[kMmBM];
+template <class Cfg, int EPI, int OUT_F32, bool F16 = false>
+__global__ __launch_bounds__(Cfg::THREADS) void gemm_w4a16_mm(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::LDS];
+  __shared__ int32_t sRow[Cfg::BM];
   const int ncols = EPI == MOE_EPI_SILU_MUL ? p.N / 2 : p.N;
-  const int bcols = EPI == MOE_EPI_SILU_MUL ? kMmBN / 2 : kMmBN;
+  const int bcols = EPI == MOE_EPI_SILU_MUL ? Cfg::BN / 2 : Cfg::BN;
   const int nbn = (ncols + bcols - 1) / bcols;
   int tile, nb;
-  if (!mm_work(linear_block(), nbn, tile_count(p, kMmBM), tile, nb)) return;
-  mm_tile<EPI, OUT_F32, NSTAGE, F16>(p, tile, nb, smem, sRow);
+  if (!mm_work(linear_block(), nbn, tile_count(p, Cfg::BM), tile, nb)) return;
+  mm_tile<Cfg, EPI, OUT_F32, F16>(p, tile, nb, smem, sRow);
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -1360,12 +1396,12 @@ static hipError_t by_variant(const GemmArgs& a, hipStream_t s) {
   return by_layout<Cfg, MOE_EPI_NONE, kOutBf16>(a, s);
 }
 
-template <int EPI, int F32, bool F16 = false>
+template <class Cfg, int EPI, int F32, bool F16 = false>
 static hipError_t launch_mm(const GemmArgs& a, hipStream_t s) {
   const int ncols = EPI == MOE_EPI_SILU_MUL ? a.N / 2 : a.N;
-  const int bcols = EPI == MOE_EPI_SILU_MUL ? 128 : 256;
+  const int bcols = EPI == MOE_EPI_SILU_MUL ? Cfg::BN / 2 : Cfg::BN;
   const int nbn = (ncols + bcols - 1) / bcols;
-  gemm_w4a16_mm<EPI, F32, 3, F16><<<mm_grid(nbn, a.max_tiles), 512, 0, s>>>(a);
+  gemm_w4a16_mm<Cfg, EPI, F32, F16><<<mm_grid(nbn, a.max_tiles), Cfg::THREADS, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -1376,18 +1412,18 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t strea
   if (a.a_f16) {
     // the exact fp16 path: 128-row tiles (packed weights) or 64-row tiles (checked by the caller)
     if (block_m == 128) {
-      if (a.epilogue == MOE_EPI_SILU_MUL) return launch_mm<MOE_EPI_SILU_MUL, kOutH16, true>(a, stream);
-      if (a.out_f32 == kOutF16Exp) return launch_mm<MOE_EPI_NONE, kOutF16Exp, true>(a, stream);
-      return launch_mm<MOE_EPI_NONE, kOutF32, true>(a, stream);
+      if (a.epilogue == MOE_EPI_SILU_MUL) return launch_mm<MmLarge, MOE_EPI_SILU_MUL, kOutH16, true>(a, stream);
+      if (a.out_f32 == kOutF16Exp) return launch_mm<MmLarge, MOE_EPI_NONE, kOutF16Exp, true>(a, stream);
+      return launch_mm<MmLarge, MOE_EPI_NONE, kOutF32, true>(a, stream);
     }
     return by_variant_f16<Tiled<64, 256, 1, 1>>(a, stream);
   }
   // (packed SiLU*mul needs N % 32 == 0, checked by the caller: up rows start a 16-row block)
   if (block_m == 128 && a.packed) {
-    if (a.epilogue == MOE_EPI_SILU_MUL) return launch_mm<MOE_EPI_SILU_MUL, kOutBf16>(a, stream);
-    if (a.out_f32 == kOutF16Exp) return launch_mm<MOE_EPI_NONE, kOutF16Exp>(a, stream);
-    if (a.out_f32 == kOutF32) return launch_mm<MOE_EPI_NONE, kOutF32>(a, stream);
-    return launch_mm<MOE_EPI_NONE, kOutBf16>(a, stream);
+    if (a.epilogue == MOE_EPI_SILU_MUL) return launch_mm<MmLarge, MOE_EPI_SILU_MUL, kOutBf16>(a, stream);
+    if (a.out_f32 == kOutF16Exp) return launch_mm<MmLarge, MOE_EPI_NONE, kOutF16Exp>(a, stream);
+    if (a.out_f32 == kOutF32) return launch_mm<MmLarge, MOE_EPI_NONE, kOutF32>(a, stream);
+    return launch_mm<MmLarge, MOE_EPI_NONE, kOutBf16>(a, stream);
   }
   switch (block_m) {
     case 16:
