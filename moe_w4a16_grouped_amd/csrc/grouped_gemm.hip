@@ -1038,28 +1038,6 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, ui
   const int nks = K / kBK;
   const int NB16 = N / 16;
 
-  for (int i = tid; i < BM; i += Cfg::THREADS) {
-    const int r = row0 + (i < rows ? i : 0);
-    sRow[i] = a_row(p, r);
-  }
-  __shared__ int sFlag[NW];
-  if (F16) tile_blk_exp_flag(p, tile, sFlag);
-  __syncthreads();
-  int any_flag = 0;
-  if constexpr (F16) {
-#pragma unroll
-    for (int w = 0; w < NW; ++w) any_flag |= sFlag[w];
-  }
-  const bool hblk = F16 && EPI != MOE_EPI_SILU_MUL && __builtin_amdgcn_readfirstlane(any_flag) != 0;
-
-  // global sources of this wave's direct loads
-  const uint16_t* a_src[AI];  // activation instructions i = AI*wave + t: rows 4i .. 4i+3
-#pragma unroll
-  for (int t = 0; t < AI; ++t) {
-    const int r = 4 * (AI * wave + t) + (lane >> 4);
-    const int c = (lane & 15) ^ (r & 15);
-    a_src[t] = p.A + (size_t)sRow[r] * K + c * 8;
-  }
   auto block_row = [&](int blk) -> int {  // packed row-block index of LDS block blk (clamped)
     int rb, first;
     if (EPI == MOE_EPI_SILU_MUL) {
@@ -1073,6 +1051,64 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, ui
     }
     return rb;
   };
+
+  // fp16 path: the tile's scales over the whole of K are tested once, here (CB row blocks of nks * 128
+  // contiguous bytes each); their loads overlap those of the permutation below
+  constexpr int kScanUnroll = 8;
+  bool scales_ok = true;
+  if constexpr (F16) {
+    const int per_blk = nks * 8;  // 16-byte chunks of one row block's scales
+    const int total = CB * per_blk;
+    const uint8_t* ws = reinterpret_cast<const uint8_t*>(p.Ws);
+    for (int i0 = tid; i0 < total; i0 += kScanUnroll * Cfg::THREADS) {
+      u32x4 v[kScanUnroll];
+#pragma unroll
+      for (int u = 0; u < kScanUnroll; ++u) {
+        const int i = min(i0 + u * Cfg::THREADS, total - 1);
+        const int b = i / per_blk;
+        v[u] = *reinterpret_cast<const u32x4*>(ws + ((size_t)e * NB16 + block_row(b)) * (size_t)nks * 128 +
+                                               (size_t)(i - b * per_blk) * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < kScanUnroll; ++u) {
+        const uint32_t d[4] = {v[u][0], v[u][1], v[u][2], v[u][3]};
+        scales_ok &= scales_f16_ok(d);
+      }
+    }
+  }
+  for (int i = tid; i < BM; i += Cfg::THREADS) {
+    const int r = row0 + (i < rows ? i : 0);
+    sRow[i] = a_row(p, r);
+  }
+  __shared__ int sFlag[NW];
+  __shared__ int sGen[NW];
+  if constexpr (F16) {
+    tile_blk_exp_flag(p, tile, sFlag);
+    const uint64_t bad = __ballot(!scales_ok);
+    if (lane == 0) sGen[wave] = bad != 0ull;
+  }
+  __syncthreads();
+  int any_flag = 0, any_bad = 0;
+  if constexpr (F16) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      any_flag |= sFlag[w];
+      any_bad |= sGen[w];
+    }
+  }
+  const bool hblk = F16 && EPI != MOE_EPI_SILU_MUL && __builtin_amdgcn_readfirstlane(any_flag) != 0;
+  // every K step of the tile takes the general form when one scale of the tile fails the test or an
+  // A block carries row exponents (wave-uniform)
+  const bool general = F16 && (hblk || __builtin_amdgcn_readfirstlane(any_bad) != 0);
+
+  // global sources of this wave's direct loads
+  const uint16_t* a_src[AI];  // activation instructions i = AI*wave + t: rows 4i .. 4i+3
+#pragma unroll
+  for (int t = 0; t < AI; ++t) {
+    const int r = 4 * (AI * wave + t) + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    a_src[t] = p.A + (size_t)sRow[r] * K + c * 8;
+  }
   const uint8_t* b_src[BI];
 #pragma unroll
   for (int t = 0; t < BI; ++t)
@@ -1105,19 +1141,6 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, ui
   auto scales_of = [&](int s, int ni) -> u32x2 {
     return *reinterpret_cast<const u32x2*>(sring + (s % Cfg::SCALE_SLOTS) * Cfg::SCALE_SLOT + blk[ni] * 128 + l16 * 8);
   };
-  // fp16 path: whether step s, with this wave's scales sc, takes the general form (scales outside
-  // fp16's exact range, or A blocks with row exponents), wave-uniform
-  auto general_of = [&](int s, const u32x2 (&sc)[NI]) -> bool {
-    uint32_t sd[2 * NI];
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-      sd[2 * ni] = sc[ni][0];
-      sd[2 * ni + 1] = sc[ni][1];
-    }
-    return __builtin_amdgcn_readfirstlane(__ballot(!scales_f16_ok(sd)) != 0ull ||
-                                          (hblk && step_blk_flagged(p, tile, s))) != 0;
-  };
-
   f32x4 acc[MI][NI];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
@@ -1138,15 +1161,14 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, ui
     pend[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // sc: this wave's scales of step s (the fp16 path reads them one step ahead)
-  auto compute = [&](int stage, int s, bool general, const u32x2 (&sc)[NI]) {
+  auto compute = [&](int stage, int s) {
     const uint8_t* st = smem + stage * STAGE;
     u32x4 braw[NI];
     u32x2 sraw[NI];
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       braw[ni] = *reinterpret_cast<const u32x4*>(st + A_BYTES + blk[ni] * 1024 + lane * 16);
-      sraw[ni] = F16 ? sc[ni] : scales_of(s, ni);
+      sraw[ni] = scales_of(s, ni);
     }
     if constexpr (F16) {
       uint32_t sd[2 * NI];
@@ -1249,29 +1271,11 @@ __device__ __forceinline__ void mm_tile(const GemmArgs& p0, int tile, int nb, ui
 #pragma unroll
   for (int u = 0; u < NSTAGE - 1; ++u)
     if (u < nks) issue(u, u);
-  // fp16 path: the next step's scales are read into registers before this step's MFMAs and tested
-  // behind them, so neither the LDS read nor the test delays the MFMAs
-  bool general = false;
-  u32x2 snext[NI];
   for (int s = 0; s < nks; ++s) {
     wait_steps<AI + BI, NSTAGE - 2>(min(NSTAGE - 2, nks - 1 - s));
     __syncthreads();
     if (s + NSTAGE - 1 < nks) issue(s + NSTAGE - 1, (s + NSTAGE - 1) % NSTAGE);
-    u32x2 scur[NI];
-    if constexpr (F16) {
-      if (s == 0) {
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) snext[ni] = scales_of(0, ni);
-        general = general_of(0, snext);
-      }
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        scur[ni] = snext[ni];
-        if (s + 1 < nks) snext[ni] = scales_of(s + 1, ni);
-      }
-    }
-    compute(s % NSTAGE, s, general, scur);
-    if (F16) general = s + 1 < nks && general_of(s + 1, snext);
+    compute(s % NSTAGE, s);
   }
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) acc[MI - 1][ni] += psc[ni] * pend[ni];
