@@ -30,7 +30,7 @@ import torch
 import moe_inputs as mi
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 (and fp16) MFMA
 MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense fp4 MFMA
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 RIDGE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
@@ -824,28 +824,52 @@ def run_w4a16(args):
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
     bm = moe.moe_ffn_block_m(T, E, k, layout)
-    h = torch.empty((R, I), dtype=torch.bfloat16, device="cuda")
+    # the layer runs its 128-row tiles (packed weights) on the exact fp16 path: x to fp16 first
+    f16 = bm == 128 and layout == moe.MOE_LAYOUT_PACKED
+    h = torch.empty((R, I), dtype=torch.float16 if f16 else torch.bfloat16, device="cuda")
     O = torch.empty((R, H), dtype=torch.float16, device="cuda")  # the layer's fp16 down output + side values
     Os = torch.empty((R, H // 8), dtype=torch.float32, device="cuda")
-    names = ["route", "align", "gate_up", "down", "combine"]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    if f16:
+        x16 = torch.empty((T, H), dtype=torch.float16, device="cuda")
+        xe = torch.empty((T,), dtype=torch.int32, device="cuda")
+        hfl = torch.empty((max(moe.moe_max_tiles(T, k, E, bm), 1), (I + 31) // 32), dtype=torch.uint8, device="cuda")
+        hex_ = torch.empty((R, (I + 31) // 32), dtype=torch.uint8, device="cuda")
+    names = ["route", "align"] + (["x_to_f16"] if f16 else []) + ["gate_up", "down", "combine"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     al = None
     for i in range(args.warmup + args.steps):
         q13, s13, q2, s2 = copies[i % L]
         e = evs[i - args.warmup] if i >= args.warmup else None
-        if e: e[0].record()
+        j = 0
+
+        def mark():
+            nonlocal j
+            if e: e[j].record()
+            j += 1
+        mark()
         moe.moe_route_topk(logits, k, ids, wts)
-        if e: e[1].record()
+        mark()
         al = moe.moe_align(ids, E, bm)
-        if e: e[2].record()
-        moe.moe_grouped_gemm_w4a16(x, al["sorted_ids"], k, q13, s13, al["tiles"], al["max_tiles"],
-                                   al["num_tiles"], bm, moe.MOE_EPI_SILU_MUL, R, C=h, weight_layout=layout)
-        if e: e[3].record()
-        moe.moe_grouped_gemm_w4a16(h, None, 1, q2, s2, al["tiles"], al["max_tiles"], al["num_tiles"], bm,
-                                   moe.MOE_EPI_NONE, R, moe.MOE_OUT_F16E, C=O, C_side=Os, weight_layout=layout)
-        if e: e[4].record()
+        mark()
+        if f16:
+            moe.moe_x_to_f16(x, x16=x16, x_exp=xe)
+            mark()
+            moe.moe_grouped_gemm_w4f16(x16, xe, None, al["sorted_ids"], k, q13, s13, al["tiles"], al["max_tiles"],
+                                       al["num_tiles"], bm, moe.MOE_EPI_SILU_MUL, R, moe.MOE_OUT_H16, C=h,
+                                       C_aux=hfl, C_aux2=hex_, weight_layout=layout)
+            mark()
+            moe.moe_grouped_gemm_w4f16(h, None, (hfl, hex_), None, 1, q2, s2, al["tiles"], al["max_tiles"],
+                                       al["num_tiles"], bm, moe.MOE_EPI_NONE, R, moe.MOE_OUT_F16E, C=O, C_aux=Os,
+                                       weight_layout=layout)
+        else:
+            moe.moe_grouped_gemm_w4a16(x, al["sorted_ids"], k, q13, s13, al["tiles"], al["max_tiles"],
+                                       al["num_tiles"], bm, moe.MOE_EPI_SILU_MUL, R, C=h, weight_layout=layout)
+            mark()
+            moe.moe_grouped_gemm_w4a16(h, None, 1, q2, s2, al["tiles"], al["max_tiles"], al["num_tiles"], bm,
+                                       moe.MOE_EPI_NONE, R, moe.MOE_OUT_F16E, C=O, C_side=Os, weight_layout=layout)
+        mark()
         moe.moe_combine(O, al["inv_perm"], wts, y=y, O_side=Os)
-        if e: e[5].record()
+        mark()
     torch.cuda.synchronize()
     kern_us = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in evs]) * 1e3) for j, n in enumerate(names)}
     touched = int((al["counts"] > 0).sum().item())
@@ -894,7 +918,7 @@ def run_w4a16(args):
                    "mean_us": round(mean_ms * 1e3, 2),
                    "graph_median_us": None if graph_med is None else round(graph_med * 1e3, 2)},
         "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
-        "roofline": {"kernel": ("gemm_w4a16_mm" if bm == 128 and layout == moe.MOE_LAYOUT_PACKED else "gemm_w4a16_tiled")
+        "roofline": {"kernel": ("gemm_w4a16_mm, exact fp16 path" if f16 else "gemm_w4a16_tiled")
                                + " (gate_up + SiLU*mul)", "bound": bound, "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(wl.name) if args.layout == "packed" else None,
