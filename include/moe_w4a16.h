@@ -334,7 +334,7 @@ size_t moe_ffn_noalloc_scratch_bytes(void);
  * kernels moe_ffn_forward launches, so its outputs are bit-identical to moe_ffn_forward's.
  *   - Limit: sizes whose moe_ffn_workspace_bytes exceeds MOE_NOALLOC_SCRATCH_BYTES are rejected with
  *     MOE_ERR_WORKSPACE before anything touches the device (the 800-token, 256-expert, H = 2048,
- *     I = 512 layer needs about 59 MB; every decode batch of a few hundred tokens fits).
+ *     I = 512 layer needs about 39 MB; every decode batch of a few hundred tokens fits).
  *   - Each GPU holds its own copy of the array from the first call on that device (the calling
  *     thread's current device, which `stream` must belong to) until the process ends.
  *   - All calls on one GPU share that GPU's array: calls that overlap in time on one GPU (two streams,
