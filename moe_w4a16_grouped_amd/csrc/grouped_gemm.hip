@@ -16,7 +16,10 @@
 //    converted to exact bf16 (hardware FP4 converter, unit scale); the MFMA produces the group's
 //    fp32 partial, which is multiplied by the bf16 group scale and added to the fp32 accumulator.
 //    (Rounding code*scale to bf16 instead would not keep the layer inside its error bound.)
-//  * Weights go HBM -> registers.  Canonical layout: one 16-byte load per lane per 4 groups (row n,
+//  * The exact fp16 form (F16, activations in fp16 with power-of-two exponents): code*scale is
+//    formed in fp16, exact for scales with an exponent in [-16, 12], and v_mfma_f32_16x16x32_f16
+//    accumulates every group in place, with no fp32 scale work per group.
+//  * Weights go HBM -> registers (tiled kernels) or LDS (the direct-load kernel).  Canonical layout: one 16-byte load per lane per 4 groups (row n,
 //    group q of the K step) followed by a 4x4 cross-quarter transpose (permlane32/16 swaps) into
 //    MFMA B-operand order.  Packed layout (prepack.hip): the same registers come from one linear
 //    1 KB load per wave, and the 16 rows x 4 group scales from one 128-byte load.
