@@ -15,7 +15,8 @@
 //  * v_mfma_f32_16x16x32_bf16: one MFMA spans exactly one 32-element scale group.  Codes are
 //    converted to exact bf16 (hardware FP4 converter, unit scale); the MFMA produces the group's
 //    fp32 partial, which is multiplied by the bf16 group scale and added to the fp32 accumulator.
-//    (Rounding code*scale to bf16 instead would not keep the layer inside its error bound.)
+//    (Rounding code*scale to bf16 instead would not keep the layer inside its error bound.)  That
+//    scale FMA is issued a few MFMAs after its partial's MFMA, so it never waits on the matrix core.
 //  * The exact fp16 form (F16, activations in fp16 with power-of-two exponents): code*scale is
 //    formed in fp16, exact for scales with an exponent in [-16, 12], and v_mfma_f32_16x16x32_f16
 //    accumulates every group in place, with no fp32 scale work per group.
@@ -630,6 +631,15 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& p, int tile, int e, i
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // bf16 form: the partial waiting for its scale, and the scale of a partial of the previous group
+  // (the pipeline starts with zero partials and scales: 0 * 0 added to a zero accumulator)
+  f32x4 pend[NI];
+  float psc[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    pend[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+    psc[ni] = 0.f;
+  }
 
   u32x4 areg[NS][ACH];
   u32x4 breg[NS][NI];
@@ -701,6 +711,9 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& p, int tile, int e, i
         if (general) general_rescale<MI, NI>(acc, sc_p, rex_p, 1);
       }
     } else {
+      // the partial of MFMA (mi, ni) is scaled into its accumulator NI MFMAs later (pend, psc: as in
+      // mm_tile), so no FMA waits on the MFMA just issued; each accumulator still takes its groups in
+      // K order
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         bf16x8 bf[NI];
@@ -717,9 +730,13 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& p, int tile, int e, i
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni) {
             const f32x4 part = mfma16x16x32(af, bf[ni], f32x4{0.f, 0.f, 0.f, 0.f});
-            acc[mi][ni] += sc[ni] * part;
+            if (mi == 0) acc[MI - 1][ni] += psc[ni] * pend[ni];
+            else acc[mi - 1][ni] += sc[ni] * pend[ni];
+            pend[ni] = part;
           }
         }
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) psc[ni] = sc[ni];
       }
     }
   };
@@ -763,6 +780,10 @@ __device__ __forceinline__ void tiled_tile(const GemmArgs& p, int tile, int e, i
 #pragma unroll
   for (int u = 0; u < NS - 1; ++u)
     if (s0 + u < nks) step(s0 + u, u, false);
+  if constexpr (!F16) {
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) acc[MI - 1][ni] += psc[ni] * pend[ni];
+  }
 
   int ncol[NI];
   bool nvalid[NI];
