@@ -6,8 +6,11 @@ GEMM -> combine) over one batch of seeded synthetic inputs already resident in H
 workload is the 800-token / 256-expert prefill shape (top-8, hidden 2048, intermediate 512, E2M1
 group-32 bf16 scales).  Weights are rotated over L distinct copies (L * bytes of the experts the
 routing touches >= 1 GiB) so that no step finds its weights in L2 or the Infinity Cache.  The K
-timed steps run as eager launches with a HIP event between consecutive steps; `value` is the median
-per-step time (p10, p90, the mean and a median from one-layer HIP graphs are under `timing`).  The
+timed steps run as eager launches with a HIP event between consecutive steps, after a warm-up that
+brings clocks and caches to their steady state (by default at least 0.25 s of steps); the events are
+created without the system-scope fence that torch's events add at every record (an L2 write-back and
+invalidate that slows the next step).  `value` is the median per-step time (p10, p90, the mean and a
+median from one-layer HIP graphs are under `timing`).  The
 dominant kernel's roofline uses its mean HIP-event launch time from a per-kernel pass.  `workloads`
 times the decode, 4096-token and skewed shapes the same way (timing only); `block` adds the whole MoE
 block around the layer (router gate GEMM, shared expert); `cpu_baseline` times the CPU oracle on the
@@ -40,6 +43,97 @@ METRIC = "MoE layer µs, TFLOP/s and weight GB/s (% roofline) at 800 tok/256 exp
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+WARMUP_SECONDS = 0.25  # default warm-up before each timed region: at least this long, and >= 10 steps
+
+_hip_rt = None
+
+
+def hip_runtime():
+    """The HIP runtime that torch has loaded (the same instance, so that torch's streams are valid)."""
+    global _hip_rt
+    if _hip_rt is None:
+        import ctypes
+
+        path = "libamdhip64.so.7"
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        rt = ctypes.CDLL(path)
+        rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _hip_rt = rt
+    return _hip_rt
+
+
+class TimingEvent:
+    """A HIP timing event created with hipEventDisableSystemFence, used like torch.cuda.Event
+    (record(), elapsed_time() in ms, read after a device synchronisation).  torch's timing events
+    release to system scope when recorded, which writes back and invalidates the L2 caches and delays
+    the work that follows (measured on MI355X: about 2 us per record between 800-token layers, 1.6 us
+    between 1-token layers); these time the work between them without adding that."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+
+        self._ct = ctypes
+        self.h = ctypes.c_void_p()
+        rc = hip_runtime().hipEventCreateWithFlags(ctypes.byref(self.h), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed (status {rc})")
+
+    def record(self, stream=None):
+        s = (stream or torch.cuda.current_stream()).cuda_stream
+        rc = hip_runtime().hipEventRecord(self.h, self._ct.c_void_p(s))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed (status {rc})")
+
+    def elapsed_time(self, end: "TimingEvent") -> float:
+        ms = self._ct.c_float()
+        rc = hip_runtime().hipEventElapsedTime(self._ct.byref(ms), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed (status {rc})")
+        return ms.value
+
+    def __del__(self):
+        try:
+            if self.h:
+                _hip_rt.hipEventDestroy(self.h)
+        except Exception:
+            pass
+
+
+def warm_up(step, W: int) -> int:
+    """Untimed steps before a timed region: W of them, or by default (W < 0) at least 10 and as many as
+    fill WARMUP_SECONDS of wall time, so that clocks and caches are in their steady state (measured on
+    MI355X: the first ~200 800-token layers after an idle period run up to 12 % slower).  Returns the
+    count."""
+    n = 0
+    t0 = time.perf_counter()
+    while (n < W) if W >= 0 else (n < 10 or time.perf_counter() - t0 < WARMUP_SECONDS):
+        step(n)
+        n += 1
+        if W < 0 and n % 10 == 0:
+            torch.cuda.synchronize()  # keep the wall clock on the GPU's work, not the launch queue
+    torch.cuda.synchronize()
+    return n
+
+
+def warm_text(args) -> str:
+    return str(args.warmup) if args.warmup >= 0 else f">= {WARMUP_SECONDS} s"
+
+
+def warmup_count(W: int, step_ms: float) -> int:
+    """Untimed steps before a further timed pass over steps of about step_ms: W, or by default enough
+    to fill WARMUP_SECONDS (at least 10)."""
+    return W if W >= 0 else max(10, math.ceil(WARMUP_SECONDS * 1e3 / max(step_ms, 1e-3)))
 
 
 def dev_bf16(bits):
@@ -94,7 +188,7 @@ def calibrate():
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0, ev1 = TimingEvent(), TimingEvent()
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
@@ -154,10 +248,11 @@ def time_block(moe, wl, inp, x, copies, layout, args):
     lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
     so = torch.empty((T, H), dtype=torch.float32, device="cuda")
     dws = torch.empty(max(moe.moe_dense_ffn_workspace_bytes(T, H, Is), 256), dtype=torch.uint8, device="cuda")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.warmup + args.steps):
+    evs = [[TimingEvent() for _ in range(3)] for _ in range(args.steps)]
+    nw = warmup_count(args.warmup, eager_ms)
+    for i in range(nw + args.steps):
         wr, sh = extra[i % L]
-        e = evs[i - args.warmup] if i >= args.warmup else None
+        e = evs[i - nw] if i >= nw else None
         if e: e[0].record()
         moe.moe_router_logits(x, wr, logits=lg)
         if e: e[1].record()
@@ -179,10 +274,11 @@ def time_block(moe, wl, inp, x, copies, layout, args):
 
 
 def time_steps(step, L, args):
-    """K steps: the median per-step eager time, and the median from one-layer HIP graphs (ms)."""
-    eager_ms = pctl(per_step_times(step, args.steps, args.warmup)[0])[0]
+    """K steps: the median per-step eager time, the median from one-layer HIP graphs (ms) and the
+    eager warm-up step count."""
+    per, _, nw = per_step_times(step, args.steps, args.warmup)
     graph_ms = None if args.no_graph else pctl(per_step_graph_times(step, L, args.steps, args.warmup))[0]
-    return eager_ms, graph_ms
+    return pctl(per)[0], graph_ms, nw
 
 
 def cpu_baseline_mx(inp, target_s: float, fn=None):
@@ -232,13 +328,13 @@ def run_mxfp4(args):
         torch.cuda.synchronize()
     y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(moe.moe_ffn_mxfp4_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device="cuda")
-    log(f"bench: {L} weight copies ({touched} of {E} experts touched); warmup {args.warmup}, steps {args.steps}")
+    log(f"bench: {L} weight copies ({touched} of {E} experts touched); warmup {warm_text(args)}, steps {args.steps}")
 
     def step(i):
         q13, e13, q2, e2 = copies[i % L]
         moe.moe_ffn_forward_mxfp4(x, logits, q13, e13, q2, e2, k, y=y, workspace=ws, weight_layout=layout)
 
-    eager_ms, graph_ms = time_steps(step, L, args)
+    eager_ms, graph_ms, nwarm = time_steps(step, L, args)
     ms = eager_ms  # the value: median per-step eager time
     log(f"bench: MXFP4 layer eager {eager_ms * 1e3:.1f} us, graph {graph_ms * 1e3 if graph_ms else 0:.1f} us")
 
@@ -255,11 +351,12 @@ def run_mxfp4(args):
     hs = torch.empty((rows_cap, I // 32), dtype=torch.uint8, device="cuda")
     O = torch.empty((R, H), dtype=torch.float32, device="cuda")
     names = ["route", "align", "quant_x", "gate_up", "down", "combine"]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(7)] for _ in range(args.steps)]
     al = None
-    for i in range(args.warmup + args.steps):
+    nw = warmup_count(args.warmup, eager_ms)
+    for i in range(nw + args.steps):
         q13, e13, q2, e2 = copies[i % L]
-        e = evs[i - args.warmup] if i >= args.warmup else None
+        e = evs[i - nw] if i >= nw else None
         if e: e[0].record()
         moe.moe_route_topk(logits, k, ids, wts)
         if e: e[1].record()
@@ -301,7 +398,7 @@ def run_mxfp4(args):
         "unit": "us/layer",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": nwarm,
         "ms_per_step": round(ms, 5),
         "higher_is_better": False,
         "scaling": "weak",
@@ -314,7 +411,7 @@ def run_mxfp4(args):
                    "weight_layout": args.layout},
         "tflops": round(flops / (us * 1e-6) / 1e12, 3),
         "weight_gbps": round(weight_bytes / (us * 1e-6) / 1e9, 1),
-        "timing": {"method": "median of per-step eager times (HIP event between consecutive steps)",
+        "timing": {"method": "median of per-step eager times (HIP event without system-scope fence between consecutive steps, after a warm-up of >= 0.25 s)",
                    "eager_us": round(eager_ms * 1e3, 2),
                    "graph_median_us": None if graph_ms is None else round(graph_ms * 1e3, 2)},
         "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
@@ -352,13 +449,13 @@ def run_w4a8(args):
         torch.cuda.synchronize()
     y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(moe.moe_ffn_w4a8_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device="cuda")
-    log(f"bench: {L} weight copies ({touched} of {E} experts touched); warmup {args.warmup}, steps {args.steps}")
+    log(f"bench: {L} weight copies ({touched} of {E} experts touched); warmup {warm_text(args)}, steps {args.steps}")
 
     def step(i):
         q13, e13, q2, e2 = copies[i % L]
         moe.moe_ffn_forward_w4a8(x, logits, q13, e13, q2, e2, k, y=y, workspace=ws, weight_layout=layout)
 
-    eager_ms, graph_ms = time_steps(step, L, args)
+    eager_ms, graph_ms, nwarm = time_steps(step, L, args)
     ms = eager_ms  # the value: median per-step eager time
     log(f"bench: W4A8 layer eager {eager_ms * 1e3:.1f} us, graph {graph_ms * 1e3 if graph_ms else 0:.1f} us")
 
@@ -375,10 +472,11 @@ def run_w4a8(args):
     hs = torch.empty((rows_cap, I // 32), dtype=torch.uint8, device="cuda")
     O = torch.empty((R, H), dtype=torch.float32, device="cuda")
     names = ["route", "align", "quant_x", "gate_up", "down", "combine"]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
-    for i in range(args.warmup + args.steps):
+    evs = [[TimingEvent() for _ in range(7)] for _ in range(args.steps)]
+    nw = warmup_count(args.warmup, eager_ms)
+    for i in range(nw + args.steps):
         q13, e13, q2, e2 = copies[i % L]
-        e = evs[i - args.warmup] if i >= args.warmup else None
+        e = evs[i - nw] if i >= nw else None
         if e: e[0].record()
         moe.moe_route_topk(logits, k, ids, wts)
         if e: e[1].record()
@@ -422,7 +520,7 @@ def run_w4a8(args):
         "unit": "us/layer",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": nwarm,
         "ms_per_step": round(ms, 5),
         "higher_is_better": False,
         "scaling": "weak",
@@ -435,7 +533,7 @@ def run_w4a8(args):
                    "weight_layout": args.layout},
         "tflops": round(flops / (us * 1e-6) / 1e12, 3),
         "weight_gbps": round(weight_bytes / (us * 1e-6) / 1e9, 1),
-        "timing": {"method": "median of per-step eager times (HIP event between consecutive steps)",
+        "timing": {"method": "median of per-step eager times (HIP event without system-scope fence between consecutive steps, after a warm-up of >= 0.25 s)",
                    "eager_us": round(eager_ms * 1e3, 2),
                    "graph_median_us": None if graph_ms is None else round(graph_ms * 1e3, 2)},
         "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
@@ -471,13 +569,13 @@ def run_f8(args):
     copies = [w0] + [tuple(t.clone() for t in w0) for _ in range(L - 1)]
     y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(moe.moe_ffn_f8_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device="cuda")
-    log(f"bench: {L} weight copies ({touched} of {E} experts touched); warmup {args.warmup}, steps {args.steps}")
+    log(f"bench: {L} weight copies ({touched} of {E} experts touched); warmup {warm_text(args)}, steps {args.steps}")
 
     def step(i):
         q13, s13, q2, s2 = copies[i % L]
         moe.moe_ffn_forward_f8(x, logits, q13, s13, q2, s2, k, y=y, workspace=ws)
 
-    eager_ms, graph_ms = time_steps(step, L, args)
+    eager_ms, graph_ms, nwarm = time_steps(step, L, args)
     ms = eager_ms  # the value: median per-step eager time
     log(f"bench: FP8 layer eager {eager_ms * 1e3:.1f} us, graph {graph_ms * 1e3 if graph_ms else 0:.1f} us")
 
@@ -493,10 +591,11 @@ def run_f8(args):
     hs = torch.empty((R, I // 128), dtype=torch.float32, device="cuda")
     O = torch.empty((R, H), dtype=torch.float32, device="cuda")
     names = ["route", "align", "quant_x", "gate_up", "quant_h", "down", "combine"]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    for i in range(args.warmup + args.steps):
+    evs = [[TimingEvent() for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    nw = warmup_count(args.warmup, eager_ms)
+    for i in range(nw + args.steps):
         q13, s13, q2, s2 = copies[i % L]
-        e = evs[i - args.warmup] if i >= args.warmup else None
+        e = evs[i - nw] if i >= nw else None
         if e: e[0].record()
         moe.moe_route_topk(logits, k, ids, wts)
         if e: e[1].record()
@@ -541,7 +640,7 @@ def run_f8(args):
         "unit": "us/layer",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": nwarm,
         "ms_per_step": round(ms, 5),
         "higher_is_better": False,
         "scaling": "weak",
@@ -554,7 +653,7 @@ def run_f8(args):
                    "hidden": H, "intermediate": I, "weight_copies": L, "touched_experts": touched},
         "tflops": round(flops / (us * 1e-6) / 1e12, 3),
         "weight_gbps": round(weight_bytes / (us * 1e-6) / 1e9, 1),
-        "timing": {"method": "median of per-step eager times (HIP event between consecutive steps)",
+        "timing": {"method": "median of per-step eager times (HIP event without system-scope fence between consecutive steps, after a warm-up of >= 0.25 s)",
                    "eager_us": round(eager_ms * 1e3, 2),
                    "graph_median_us": None if graph_ms is None else round(graph_ms * 1e3, 2)},
         "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
@@ -643,21 +742,19 @@ def pctl(xs):
 
 
 def per_step_times(step, K: int, W: int):
-    """W untimed steps, then K steps with a HIP event between consecutive steps on the stream the
-    layer runs on (torch's current stream), bracketed by device synchronisation.  Returns the K
-    per-step durations (ms) and the host wall time of the K steps (s)."""
-    for i in range(W):
-        step(i)
-    torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    """The warm-up (warm_up), then K steps with a HIP event between consecutive steps on the stream
+    the layer runs on (torch's current stream), bracketed by device synchronisation.  Returns the K
+    per-step durations (ms), the host wall time of the K steps (s) and the warm-up step count."""
+    nw = warm_up(step, W)
+    evs = [TimingEvent() for _ in range(K + 1)]
     t0 = time.perf_counter()
     evs[0].record()
     for i in range(K):
-        step(i)
+        step(nw + i)
         evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return [evs[i].elapsed_time(evs[i + 1]) for i in range(K)], wall
+    return [evs[i].elapsed_time(evs[i + 1]) for i in range(K)], wall, nw
 
 
 def per_step_graph_times(step, L: int, K: int, W: int):
@@ -676,13 +773,11 @@ def per_step_graph_times(step, L: int, K: int, W: int):
         with torch.cuda.graph(g):
             step(i)
         graphs.append(g)
-    for i in range(W):
-        graphs[i % L].replay()
-    torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    nw = warm_up(lambda i: graphs[i % L].replay(), W)
+    evs = [TimingEvent() for _ in range(K + 1)]
     evs[0].record()
     for i in range(K):
-        graphs[i % L].replay()
+        graphs[(nw + i) % L].replay()
         evs[i + 1].record()
     torch.cuda.synchronize()
     return [evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
@@ -693,7 +788,7 @@ def measured_hbm(n_bytes: int = 1 << 30):
     second) and a read-only reduction of n_bytes."""
     src = torch.ones(n_bytes // 2, dtype=torch.bfloat16, device="cuda")
     dst = torch.empty_like(src)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0, ev1 = TimingEvent(), TimingEvent()
     out = {}
     for _ in range(3):
         dst.copy_(src)
@@ -767,7 +862,7 @@ def time_workloads(moe, names, layout, args):
             q13, s13, q2, s2 = copies[i % L]
             moe.moe_ffn_forward(x, logits, q13, s13, q2, s2, wl.k, y=y, workspace=ws, weight_layout=lay)
 
-        per, _ = per_step_times(step, K, args.warmup)
+        per, _, _ = per_step_times(step, K, args.warmup)
         med, p10, p90 = pctl(per)
         gmed = None
         if not args.no_graph:
@@ -801,14 +896,14 @@ def run_w4a16(args):
     y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(moe.moe_ffn_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device="cuda")
     log(f"bench: {L} weight copies of {wbytes_all / 1e6:.1f} MB ({touched0} of {E} experts touched); "
-        f"warmup {args.warmup}, timed steps {args.steps}")
+        f"warmup {warm_text(args)}, timed steps {args.steps}")
 
     def step(i):
         q13, s13, q2, s2 = copies[i % L]
         moe.moe_ffn_forward(x, logits, q13, s13, q2, s2, k, y=y, workspace=ws, weight_layout=layout)
 
     # The timed region: K eager steps, a HIP event between consecutive steps; value = the median.
-    per, wall = per_step_times(step, args.steps, args.warmup)
+    per, wall, nwarm = per_step_times(step, args.steps, args.warmup)
     med, p10, p90 = pctl(per)
     mean_ms = float(np.sum(per)) / args.steps
     log(f"bench: whole layer median {med * 1e3:.1f} us/step (p10 {p10 * 1e3:.1f}, p90 {p90 * 1e3:.1f}, "
@@ -835,11 +930,12 @@ def run_w4a16(args):
         hfl = torch.empty((max(moe.moe_max_tiles(T, k, E, bm), 1), (I + 31) // 32), dtype=torch.uint8, device="cuda")
         hex_ = torch.empty((R, (I + 31) // 32), dtype=torch.uint8, device="cuda")
     names = ["route", "align"] + (["x_to_f16"] if f16 else []) + ["gate_up", "down", "combine"]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(len(names) + 1)] for _ in range(args.steps)]
     al = None
-    for i in range(args.warmup + args.steps):
+    nw = warmup_count(args.warmup, med)
+    for i in range(nw + args.steps):
         q13, s13, q2, s2 = copies[i % L]
-        e = evs[i - args.warmup] if i >= args.warmup else None
+        e = evs[i - nw] if i >= nw else None
         j = 0
 
         def mark():
@@ -896,7 +992,7 @@ def run_w4a16(args):
         "unit": "us/layer",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": nwarm,
         "ms_per_step": round(med, 5),
         "higher_is_better": False,
         "scaling": "weak",
@@ -913,7 +1009,7 @@ def run_w4a16(args):
         "layer_gbps": round(layer_bytes / (us * 1e-6) / 1e9, 1),
         "layer_roofline": {"bound": layer_bound, "algorithmic_bytes": layer_bytes, "algorithmic_flops": flops,
                            "roofline_us": round(t_min * 1e6, 2), "frac": round(t_min / (us * 1e-6), 4)},
-        "timing": {"method": "median of per-step eager times (HIP event between consecutive steps)",
+        "timing": {"method": "median of per-step eager times (HIP event without system-scope fence between consecutive steps, after a warm-up of >= 0.25 s)",
                    "median_us": round(us, 2), "p10_us": round(p10 * 1e3, 2), "p90_us": round(p90 * 1e3, 2),
                    "mean_us": round(mean_ms * 1e3, 2),
                    "graph_median_us": None if graph_med is None else round(graph_med * 1e3, 2)},
@@ -949,7 +1045,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=-1,
+                    help="untimed steps before each timed region (default: at least 10, filling "
+                         f"{WARMUP_SECONDS} s)")
     ap.add_argument("--workload", default="pre800", choices=sorted(mi.WORKLOADS))
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = enough for 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
