@@ -1012,6 +1012,8 @@ def run_w4a16(args):
         "timing": {"method": "median of per-step eager times (HIP event without system-scope fence between consecutive steps, after a warm-up of >= 0.25 s)",
                    "median_us": round(us, 2), "p10_us": round(p10 * 1e3, 2), "p90_us": round(p90 * 1e3, 2),
                    "mean_us": round(mean_ms * 1e3, 2),
+                   # host clock around the K timed steps (launches to the final synchronisation) / K
+                   "host_wall_us_per_step": round(wall / args.steps * 1e6, 2),
                    "graph_median_us": None if graph_med is None else round(graph_med * 1e3, 2)},
         "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
         "roofline": {"kernel": ("gemm_w4a16_mm, exact fp16 path" if f16 else "gemm_w4a16_tiled")
