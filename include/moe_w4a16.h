@@ -314,6 +314,12 @@ size_t moe_ffn_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32
  *   workspace: device scratch of at least moe_ffn_workspace_bytes(T, H, I, E, k) bytes.
  * Shapes: T >= 0 (T == 0 launches nothing), 1 <= k <= E <= MOE_MAX_EXPERTS, H % 32 == 0,
  *         I % 32 == 0, H >= 32, I >= 32, T*k < 2^26, H*I < 4 GiB (one expert's gate_up codes).
+ * Diagnostics: with MOE_DUMP=1 in the environment (read on every call), the call then synchronises
+ *   `stream` and prints one line to stderr: shape, tile height and count, rows per expert (least,
+ *   most, experts without rows), most tiles of one expert, the ten largest logits of token 0 and
+ *   the L2 norms of x and y [Atlas, KV Cache量化、MTP推测解码和调试工具链: per-layer expert-id dump].
+ *   Results are unchanged; nothing is printed for a stream under graph capture; a failing copy
+ *   returns MOE_ERR_HIP.  moe_ffn_block_forward does the same; moe_ffn_forward_noalloc never dumps.
  */
 moe_status_t moe_ffn_forward(const uint16_t* x, const float* router_logits, int32_t T, int32_t H,
                              int32_t I, int32_t E, int32_t k, const uint8_t* w13_q,

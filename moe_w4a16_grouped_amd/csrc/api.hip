@@ -7,7 +7,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
+#include <vector>
 
 #include "launch.h"
 #include "moe_w4a16.h"
@@ -280,6 +282,75 @@ moe_status_t run_ffn(const uint16_t* x, const float* router_logits, int32_t T, i
   if (e != hipSuccess) return hip_status(e, "down launch");
   e = moe::launch_combine(o, oside, inv, w, shared_out, sw.w13_q ? R : -1, T, k, H, y, s);
   return hip_status(e, "combine launch");
+}
+
+// MOE_DUMP=1 in the environment: after a layer call's launches, synchronise its stream and print one
+// line of diagnostics to stderr, in the spirit of the Atlas page's per-layer dump of expert ids
+// ("告别Python堆栈：Atlas用纯Rust重写LLM推理，在GB10上跑赢vLLM", section "KV Cache量化、MTP推测解码和调试工具链"):
+// the shape, the tile height and tile count, the rows per expert (least, most, experts without
+// rows), the most tiles of one expert, the ten largest router logits of token 0 (expert:value) and
+// the L2 norms of x and y.  It only reads device memory, so results are unchanged; it is skipped on
+// a stream under graph capture.  Read on every call (getenv), off unless the value is exactly "1".
+bool dump_enabled() {
+  const char* v = getenv("MOE_DUMP");
+  return v && v[0] == '1' && v[1] == '\0';
+}
+
+moe_status_t dump_layer(const uint16_t* x, const float* logits, const int32_t* ids, const int32_t* ntiles,
+                        const uint16_t* y, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t block_m,
+                        hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return ok();
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e, "MOE_DUMP synchronize");
+  const size_t R = (size_t)T * k, n = (size_t)T * H;
+  std::vector<int32_t> hid(R);
+  std::vector<float> hl(E);
+  std::vector<uint16_t> hx(n), hy(n);
+  int32_t nt = 0;
+  if ((e = hipMemcpy(hid.data(), ids, R * sizeof(int32_t), hipMemcpyDeviceToHost)) != hipSuccess ||
+      (e = hipMemcpy(hl.data(), logits, E * sizeof(float), hipMemcpyDeviceToHost)) != hipSuccess ||
+      (e = hipMemcpy(&nt, ntiles, sizeof(int32_t), hipMemcpyDeviceToHost)) != hipSuccess ||
+      (e = hipMemcpy(hx.data(), x, n * sizeof(uint16_t), hipMemcpyDeviceToHost)) != hipSuccess ||
+      (e = hipMemcpy(hy.data(), y, n * sizeof(uint16_t), hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_status(e, "MOE_DUMP copy");
+  std::vector<int64_t> cnt(E, 0);
+  for (int32_t id : hid)
+    if (id >= 0 && id < E) ++cnt[id];
+  int64_t cmin = cnt[0], cmax = cnt[0], tiles_max = 0;
+  int empty = 0;
+  for (int64_t c : cnt) {
+    cmin = std::min(cmin, c);
+    cmax = std::max(cmax, c);
+    empty += c == 0;
+    tiles_max = std::max(tiles_max, (c + block_m - 1) / block_m);
+  }
+  std::vector<int> order(E);
+  for (int i = 0; i < E; ++i) order[i] = i;
+  const int top = std::min(E, 10);
+  std::partial_sort(order.begin(), order.begin() + top, order.end(),
+                    [&](int a, int b) { return hl[a] > hl[b] || (hl[a] == hl[b] && a < b); });
+  auto norm = [](const std::vector<uint16_t>& v) {
+    double acc = 0.0;
+    for (uint16_t b : v) {
+      uint32_t u = (uint32_t)b << 16;
+      float f;
+      memcpy(&f, &u, 4);
+      acc += (double)f * f;
+    }
+    return std::sqrt(acc);
+  };
+  char buf[512];
+  int len = 0;
+  for (int i = 0; i < top && len < (int)sizeof(buf) - 32; ++i)
+    len += snprintf(buf + len, sizeof(buf) - len, "%s%d:%.6g", i ? " " : "", order[i], hl[order[i]]);
+  fprintf(stderr,
+          "moe_dump: T=%d H=%d I=%d E=%d k=%d block_m=%d tiles=%d rows_per_expert min=%lld max=%lld empty=%d "
+          "max_tiles_per_expert=%lld logits0_top=[%s] x_norm=%.9g y_norm=%.9g\n",
+          T, H, I, E, k, block_m, nt, (long long)cmin, (long long)cmax, empty, (long long)tiles_max, buf, norm(hx),
+          norm(hy));
+  fflush(stderr);
+  return ok();
 }
 
 // Scratch of the layer entry point that allocates nothing: a static device array of fixed size.
@@ -638,8 +709,13 @@ moe_status_t moe_ffn_forward(const uint16_t* x, const float* router_logits, int3
   const FfnLayout L = ffn_layout(T, H, I, E, k, weight_layout == MOE_LAYOUT_PACKED);
   if (workspace_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "moe_ffn_forward: workspace %zu B < required %zu B", workspace_bytes, L.total);
-  return run_ffn(x, router_logits, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, weight_layout, y, topk_ids_out,
-                 topk_w_out, static_cast<char*>(workspace), L, SharedW{}, nullptr, (hipStream_t)stream);
+  char* ws = static_cast<char*>(workspace);
+  if (moe_status_t st = run_ffn(x, router_logits, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, weight_layout, y,
+                                topk_ids_out, topk_w_out, ws, L, SharedW{}, nullptr, (hipStream_t)stream))
+    return st;
+  if (!dump_enabled()) return ok();
+  return dump_layer(x, router_logits, topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids),
+                    reinterpret_cast<int32_t*>(ws + L.ntiles), y, T, H, I, E, k, L.block_m, (hipStream_t)stream);
 }
 
 size_t moe_ffn_noalloc_scratch_bytes(void) { return scratch_capacity(); }
@@ -750,8 +826,12 @@ moe_status_t moe_ffn_block_forward(const uint16_t* x, const uint16_t* w_router, 
     e = run_dense_ffn(x, T, H, Is, w13s_q, w13s_s, w2s_q, w2s_s, weight_layout, hs, shared_out, s);
     if (e != hipSuccess) return hip_status(e, "shared expert launch");
   }
-  return run_ffn(x, logits, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, weight_layout, y, topk_ids_out, topk_w_out, ws,
-                 L, sw, shared_out, s);
+  if (moe_status_t st = run_ffn(x, logits, T, H, I, E, k, w13_q, w13_s, w2_q, w2_s, weight_layout, y, topk_ids_out,
+                                topk_w_out, ws, L, sw, shared_out, s))
+    return st;
+  if (!dump_enabled()) return ok();
+  return dump_layer(x, logits, topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids),
+                    reinterpret_cast<int32_t*>(ws + L.ntiles), y, T, H, I, E, k, L.block_m, s);
 }
 
 // ---- MXFP4 (W4A4) variant -------------------------------------------------------------------------
