@@ -1491,8 +1491,12 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t strea
       // CU, against 256 VGPRs and two for 64 x 256): measured on MI355X, 8192 tokens over 512 experts
       // top-10 (K = 512) 291 against 307 us, and 4096 tokens over 8 experts top-2 with canonical
       // weights (K = 14336) 1423-1427 against 1887-1892 us.  gate_up keeps 256-column blocks (8192
-      // tokens: 379-386 against 410-412 us with 128-column blocks).
+      // tokens: 379-386 against 410-412 us with 128-column blocks) when the weights are packed; with
+      // canonical weights (whose loads take a cross-lane transpose) 128-column blocks two steps ahead
+      // are faster there too: 8192 skewed tokens 474-487 against 585 us, 4096 tokens 3144-3151
+      // against 3387-3463 us.
       if (a.epilogue != MOE_EPI_SILU_MUL) return by_variant_none<Tiled<64, 128, 1, 2>>(a, stream);
+      if (!a.packed) return by_variant<Tiled<64, 128, 1, 2>>(a, stream);
       return by_variant<Tiled<64, 256, 1, 1>>(a, stream);
     default: return by_variant<Tiled<128, 128, 2, 1>>(a, stream);
   }
