@@ -1483,9 +1483,14 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, int block_m, hipStream_t strea
     case 32:
       // 800 tokens, 256 experts top-8 (H 2048, I 512), four runs on one MI355X: gate_up 70.4-71.2 us one
       // K step ahead against 72.1-73.1 us two steps ahead; down 47.2-48.1 us two steps ahead against
-      // 47.9-48.9 us one step ahead
-      if (a.epilogue == MOE_EPI_SILU_MUL) return by_variant<Tiled<32, 128, 1, 1>>(a, stream);
-      return by_variant<Tiled<32, 128, 1, 2>>(a, stream);
+      // 47.9-48.9 us one step ahead.  With canonical weights the other way round: the layer took
+      // 173.2-174.1 against 176.6-177.4 us.
+      if (a.epilogue == MOE_EPI_SILU_MUL) {
+        if (!a.packed) return by_variant<Tiled<32, 128, 1, 2>>(a, stream);
+        return by_variant<Tiled<32, 128, 1, 1>>(a, stream);
+      }
+      if (!a.packed) return by_variant_none<Tiled<32, 128, 1, 1>>(a, stream);
+      return by_variant_none<Tiled<32, 128, 1, 2>>(a, stream);
     case 64:
       // The down projection in 128-column blocks two K steps ahead (164-168 VGPRs, three workgroups per
       // CU, against 256 VGPRs and two for 64 x 256): measured on MI355X, 8192 tokens over 512 experts
