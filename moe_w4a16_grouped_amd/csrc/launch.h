@@ -131,6 +131,9 @@ struct MxGemmArgs {
   // 2048 code bytes and 64 scale bytes, see mx8_quant_tiles_kernel); a SILU_MUL output is MXFP8 h in the
   // same arrangement (row-major codes [rows, N/2], scale bytes [rows, N/64]).
   int act_e4m3;
+  // out_f32 == 2 (fp16 C with in-band exponents, kOutF16Exp; E2M1 activations only): fp32 values of
+  // the marked elements, [rows, ceil(N / 8)]
+  float* C_side;
 };
 hipError_t launch_grouped_gemm_mx(const MxGemmArgs& a, int block_m, hipStream_t stream);
 hipError_t launch_mx_quant(const uint16_t* x, long long rows, int K, uint8_t* q, uint8_t* s, hipStream_t stream);

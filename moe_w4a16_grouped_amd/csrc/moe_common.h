@@ -148,6 +148,107 @@ __device__ __forceinline__ void g2lds16(const void* g, void* lds_wave_base) {
 }
 
 
+// Output kinds of the NONE epilogue (GemmArgs::out_f32): 0 bf16, 1 fp32, 2 fp16 (kOutF16Exp) with
+// an exponent per row and 8-column segment that is carried in band.  A segment is stored plainly
+// (8 fp16 values, exponent 0) when its largest finite magnitude m is 0 or in [2^-6, 2^15) and it
+// holds no non-finite value; otherwise it is scaled by 2^-exp, exp = floor(log2 m) - 14 (exact; m then
+// lies in [2^14, 2^15)), its first element is replaced by a marker (an fp16 NaN whose low 9 bits are
+// exp + 256) and that element's scaled value goes to C_side[row, col / 8] in fp32.  fp16 keeps 11
+// significant bits where bf16 keeps 8; the exponent keeps any fp32 range representable (tiny segments
+// included), and in the common case nothing but the fp16 values is written.
+constexpr int kOutBf16 = 0, kOutF32 = 1, kOutF16Exp = 2;
+constexpr uint16_t kF16Marker = 0x7E00;  // quiet NaN; low 9 bits: the segment's exponent + 256
+constexpr float kF16Small = 0.015625f;   // 2^-6: smaller maxima are scaled up
+
+// Exponent of a row segment (or of a row's 32 columns of h) with largest finite magnitude m: 0 when m
+// is 0 or in [2^-6, 2^15), else floor(log2 m) - 14 clamped to [-110, 113].
+__device__ __forceinline__ int f16_seg_exponent(float m) {
+  if (m == 0.f || (m >= kF16Small && m < 32768.f)) return 0;
+  const int e = ilogbf(m) - 14;
+  return e < -110 ? -110 : (e > 113 ? 113 : e);
+}
+
+// Whether some aligned group of 8 lanes (a segment) has every bit of mask set.
+__device__ __forceinline__ bool any_full_octet(uint64_t m) {
+  m &= m >> 1;
+  m &= m >> 2;
+  m &= m >> 4;
+  return (m & 0x0101010101010101ull) != 0ull;
+}
+
+// The 8 columns of a segment live in 8 lanes of a quarter (one lane per column, l16 = 8j .. 8j+7):
+// the largest finite magnitude over them, and whether any is non-finite.
+__device__ __forceinline__ float seg8_max_finite(float v, bool& nonfinite) {
+  const bool nf = !(fabsf(v) <= 3.4e38f);
+  float m = nf ? 0.f : fabsf(v);
+  m = fmaxf(m, __shfl_xor(m, 1));
+  m = fmaxf(m, __shfl_xor(m, 2));
+  m = fmaxf(m, __shfl_xor(m, 4));
+  int f = nf;
+  f |= __shfl_xor(f, 1);
+  f |= __shfl_xor(f, 2);
+  f |= __shfl_xor(f, 4);
+  nonfinite = f != 0;
+  return m;
+}
+
+// A wave's MI x NI blocks of 16 x 16 fp32 results stored as kOutF16Exp: lane (q, l16) holds rows
+// row_base + mi*16 + q*4 + r (r < 4) of the tile starting at row0, at columns ncol[ni] (l16 the column
+// within the block, so an 8-column segment is 8 lanes of a quarter).  C fp16 [rows, N], C_side fp32
+// [rows, ceil(N / 8)]; rows at or past `rows` and columns with nvalid false are not written.  When no
+// segment of the wave needs an exponent (the common case) each value is just rounded to fp16.
+// PAD_ROWS: the tile's padding rows may hold anything (zeros, stale data) and are left out of that
+// test; without it they are taken to be copies of a real row, whose values are representative.
+template <int MI, int NI, bool PAD_ROWS>
+__device__ __forceinline__ void store_f16e(uint16_t* C, float* C_side, int N, const f32x4 (&acc)[MI][NI], int row_base,
+                                           int row0, int rows, int q, const int (&ncol)[NI], const bool (&nvalid)[NI]) {
+  // some segment of this wave may need an exponent (a magnitude of 2^15 or more, a non-finite value,
+  // or all eight below 2^-6; an invalid column counts as below).  With PAD_ROWS a padding row's
+  // segments count as neither.
+  bool big = false, tiny = false;
+  const int row_lim = rows - row_base - q * 4;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool live = !PAD_ROWS || mi * 16 + r < row_lim;
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const float a = !live ? 1.f : (nvalid[ni] ? fabsf(acc[mi][ni][r]) : 0.f);
+        big |= !(a < 32768.f);
+        tiny |= any_full_octet(__ballot(a < kF16Small));
+      }
+    }
+  const bool scaled = __ballot(big) != 0ull || tiny;
+  const int l16 = threadIdx.x & 15;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = row_base + mi * 16 + q * 4 + r;
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        float v = nvalid[ni] ? acc[mi][ni][r] : 0.f;
+        uint16_t bits;
+        if (!scaled) {
+          bits = f32_to_f16_bits(v);
+        } else {
+          // every lane takes part in the segment reductions, whatever its row
+          bool nonfinite;
+          const float m = seg8_max_finite(v, nonfinite);
+          const int ex = f16_seg_exponent(m);
+          v *= pow2f(-ex);  // exact
+          bits = f32_to_f16_bits(v);
+          if ((ex != 0 || nonfinite) && (l16 & 7) == 0) {
+            bits = (uint16_t)(kF16Marker | (ex + 256));
+            if (row < rows && nvalid[ni]) C_side[(size_t)(row0 + row) * (size_t)((N + 7) / 8) + ncol[ni] / 8] = v;
+          }
+        }
+        if (row < rows && nvalid[ni]) C[(size_t)(row0 + row) * N + ncol[ni]] = bits;
+      }
+    }
+}
+
 // Launch grids are 2-D: x holds at most kGridX workgroups (a multiple of 8, so with linear index
 // b = y * gridDim.x + x, b % 8 still names the XCD) and y as many rows as the work list needs.
 constexpr unsigned kGridX = 8u << 16;

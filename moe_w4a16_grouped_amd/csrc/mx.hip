@@ -318,7 +318,7 @@ hipError_t launch_mx_prepack(const uint8_t* wq, const uint8_t* we, int E, int N,
 // layout above; MODE 2: the tile-blocked MXFP8 layout, two contiguous 1 KB loads per wave), the
 // instruction's A format E4M3, and h quantized to MXFP8 (row-major: codes [rows, N/2], scale bytes
 // [rows, N/64]; MODE 2: tile-blocked).
-template <int BM, int BN, int KW, int PF, int EPI, bool OUT_F32, int MODE, int AF = 4>
+template <int BM, int BN, int KW, int PF, int EPI, int OUT, int MODE, int AF = 4>
 __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
   constexpr bool ATB = MODE == 2, WPK = MODE >= 1;  // tile-blocked activations, packed weights
   constexpr bool A8 = AF == 0;                       // E4M3 activations
@@ -565,6 +565,10 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
     }
   } else {
     if (!owner) return;
+    if constexpr (OUT == kOutF16Exp) {
+      store_f16e<MI, NI, true>(static_cast<uint16_t*>(p.C), p.C_side, N, acc, 0, row0, rows, q, ncol, nvalid);
+      return;
+    }
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -575,7 +579,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(MxGemmArgs p) {
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
           if (!nvalid[ni]) continue;
-          if (OUT_F32) static_cast<float*>(p.C)[orow * N + ncol[ni]] = acc[mi][ni][r];
+          if (OUT == kOutF32) static_cast<float*>(p.C)[orow * N + ncol[ni]] = acc[mi][ni][r];
           else static_cast<uint16_t*>(p.C)[orow * N + ncol[ni]] = f32_to_bf16_bits(acc[mi][ni][r]);
         }
       }
@@ -627,7 +631,7 @@ __device__ __forceinline__ void wait_vmcnt_upto8(int n) {
 
 // AF = 0 (W4A8): E4M3 activations, 128-byte code rows per K step copied by two direct loads per wave
 // and read in the 8-bit operand layout (two 16-byte halves per lane); h leaves as MXFP8.
-template <int EPI, bool OUT_F32, int MODE, int NSTAGE, int AF = 4>
+template <int EPI, int OUT, int MODE, int NSTAGE, int AF = 4>
 __global__ __launch_bounds__(512) void gemm_mx_mm(MxGemmArgs p) {
   constexpr int MI = 4, NI = 4;
   constexpr bool WPK = MODE == 1;
@@ -832,6 +836,22 @@ __global__ __launch_bounds__(512) void gemm_mx_mm(MxGemmArgs p) {
       }
     }
   } else {
+    if constexpr (OUT == kOutF16Exp) {
+      int ncol[NI];
+      bool nvalid[NI];
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        ncol[ni] = nb * kMxMmBN + wn * 64 + ni * 16 + l16;
+        nvalid[ni] = ncol[ni] < N;
+      }
+      // one 16-row block at a time keeps the wave within 128 VGPRs (4 waves per SIMD)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        store_f16e<1, NI, true>(static_cast<uint16_t*>(p.C), p.C_side, N,
+                                reinterpret_cast<const f32x4(&)[1][NI]>(acc[mi]), wm * 64 + mi * 16, row0, rows, q,
+                                ncol, nvalid);
+      return;
+    }
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -843,7 +863,7 @@ __global__ __launch_bounds__(512) void gemm_mx_mm(MxGemmArgs p) {
         for (int ni = 0; ni < NI; ++ni) {
           const int n = nb * kMxMmBN + wn * 64 + ni * 16 + l16;
           if (n >= N) continue;
-          if (OUT_F32) static_cast<float*>(p.C)[orow * N + n] = acc[mi][ni][rr];
+          if (OUT == kOutF32) static_cast<float*>(p.C)[orow * N + n] = acc[mi][ni][rr];
           else static_cast<uint16_t*>(p.C)[orow * N + n] = f32_to_bf16_bits(acc[mi][ni][rr]);
         }
       }
@@ -856,18 +876,22 @@ static hipError_t launch_mx_mm(const MxGemmArgs& a, hipStream_t s) {
   const int bcols = a.epilogue == MOE_EPI_SILU_MUL ? kMxMmBN / 2 : kMxMmBN;
   const int nbn = (ncols + bcols - 1) / bcols;
   const dim3 grid = mm_grid(nbn, a.max_tiles);
-  if (a.epilogue == MOE_EPI_SILU_MUL) gemm_mx_mm<MOE_EPI_SILU_MUL, false, MODE, 3, AF><<<grid, 512, 0, s>>>(a);
-  else if (a.out_f32) gemm_mx_mm<MOE_EPI_NONE, true, MODE, 3, AF><<<grid, 512, 0, s>>>(a);
-  else gemm_mx_mm<MOE_EPI_NONE, false, MODE, 3, AF><<<grid, 512, 0, s>>>(a);
+  if (a.epilogue == MOE_EPI_SILU_MUL) gemm_mx_mm<MOE_EPI_SILU_MUL, kOutBf16, MODE, 3, AF><<<grid, 512, 0, s>>>(a);
+  else if (AF == 4 && a.out_f32 == kOutF16Exp)
+    gemm_mx_mm<MOE_EPI_NONE, AF == 4 ? kOutF16Exp : kOutF32, MODE, 3, AF><<<grid, 512, 0, s>>>(a);
+  else if (a.out_f32) gemm_mx_mm<MOE_EPI_NONE, kOutF32, MODE, 3, AF><<<grid, 512, 0, s>>>(a);
+  else gemm_mx_mm<MOE_EPI_NONE, kOutBf16, MODE, 3, AF><<<grid, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <int BM, int BN, int KW, int PF, int MODE, int AF = 4>
 static void launch_mx_mode(const MxGemmArgs& a, dim3 grid, hipStream_t s) {
   if (a.epilogue == MOE_EPI_SILU_MUL)
-    gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_SILU_MUL, false, MODE, AF><<<grid, 256, 0, s>>>(a);
-  else if (a.out_f32) gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, true, MODE, AF><<<grid, 256, 0, s>>>(a);
-  else gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, false, MODE, AF><<<grid, 256, 0, s>>>(a);
+    gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_SILU_MUL, kOutBf16, MODE, AF><<<grid, 256, 0, s>>>(a);
+  else if (AF == 4 && a.out_f32 == kOutF16Exp)
+    gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, AF == 4 ? kOutF16Exp : kOutF32, MODE, AF><<<grid, 256, 0, s>>>(a);
+  else if (a.out_f32) gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, kOutF32, MODE, AF><<<grid, 256, 0, s>>>(a);
+  else gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, kOutBf16, MODE, AF><<<grid, 256, 0, s>>>(a);
 }
 
 template <int BM, int BN, int KW, int PF>
@@ -896,6 +920,8 @@ constexpr int kMxSplitKMaxTiles = 32;
 
 hipError_t launch_grouped_gemm_mx(const MxGemmArgs& a, int block_m, hipStream_t stream) {
   if (a.max_tiles <= 0) return hipSuccess;
+  // fp16 output with in-band exponents is built for E2M1 activations only
+  if (a.out_f32 == kOutF16Exp && (a.act_e4m3 || a.epilogue != MOE_EPI_NONE || !a.C_side)) return hipErrorInvalidValue;
   if (block_m == 128) {
     if (a.act_e4m3) return a.mode == 1 ? launch_mx_mm<1, 0>(a, stream) : launch_mx_mm<0, 0>(a, stream);
     return a.mode == 1 ? launch_mx_mm<1>(a, stream) : launch_mx_mm<0>(a, stream);

@@ -251,6 +251,36 @@ def test_ffn_forward_mxfp4_edges(wl):
     gu.assert_within_tolerance(gu.host_bf16_to_f64(y), oracle.moe_ffn_mx(inp), wl.name)
 
 
+@pytest.mark.parametrize("layout", [moe.MOE_LAYOUT_CANONICAL, moe.MOE_LAYOUT_PACKED])
+@pytest.mark.parametrize("wl,bm", [
+    (mi.custom("mx_o16_small_tiles", 64, 32, 8, 256, 128, seed=21), 16),
+    (mi.custom("mx_o16_large_tiles", 1024, 8, 2, 256, 128, seed=22), 128),
+])
+def test_ffn_forward_mxfp4_fp16_o_extreme_rows(wl, bm, layout):
+    """From 256 rows the layer keeps the down projection's output as fp16 with per-(row, 8 columns)
+    exponents.  Tokens scaled by 2^40 (outputs near 2^80, far past fp16's range) and by 2^-30 (outputs
+    near 2^-60, below its normal range) take the exponent path in both the register-tile and the
+    128-row kernels; each class of rows is held to the layer's tolerance on its own, so an error in
+    the small rows is not hidden by the large ones.  The scalings are powers of two, so x stays
+    exact in bf16."""
+    inp = mi.make_mx_inputs(wl)
+    assert wl.T * wl.k >= 256
+    assert moe.moe_ffn_mxfp4_block_m(wl.T, wl.H, wl.I, wl.E, wl.k) == bm
+    x = mi.bf16_bits_to_f32(inp.x)
+    x[0::3] *= np.float32(2.0 ** 40)
+    x[1::3] *= np.float32(2.0 ** -30)
+    inp.x = mi.f32_to_bf16_bits(x)
+    assert np.array_equal(mi.bf16_bits_to_f32(inp.x), x)
+    _log(f"mxfp4 layer {wl.name} (fp16 O, extreme rows, layout {layout})")
+    d = MXDevice(inp)
+    y, ids = _forward(d, wl, layout)
+    np.testing.assert_array_equal(ids.cpu().numpy(), oracle.route(inp.logits, wl.k)[0])
+    yh, ref = gu.host_bf16_to_f64(y), oracle.moe_ffn_mx(inp)
+    assert np.abs(ref[0::3]).max() > 2.0 ** 60 and 0 < np.abs(ref[1::3]).max() < 2.0 ** -40
+    for c, label in enumerate(["x 2^40", "x 2^-30", "unscaled"]):
+        gu.assert_within_tolerance(yh[c::3], ref[c::3], f"{wl.name} {label}")
+
+
 def test_ffn_forward_mxfp4_deterministic_and_empty():
     wl = mi.custom("mx_det", 200, 32, 4, 512, 256, seed=13)
     d = MXDevice(mi.make_mx_inputs(wl))
