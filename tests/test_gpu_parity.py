@@ -489,6 +489,44 @@ def test_token_permutation_equivariant():
 
 
 # ---------------------------------------------------------------------------------------------------
+# decode batches (at most 16 routed rows in 16-row tiles, the split-K kernels), every token checked
+
+DC_CASES = [
+    mi.custom("dc_t1_k16", 1, 64, 16, 256, 128, seed=51),    # 16 tiles of one row: two rounds of 8 slots
+    mi.custom("dc_t16_k1", 16, 32, 1, 256, 128, seed=52),    # 16 tokens, up to 16 tiles
+    mi.custom("dc_t2_k8", 2, 128, 8, 512, 256, seed=53),     # K = 256: both K halves of a tile busy
+    mi.custom("dc_t4_e2", 4, 2, 2, 128, 128, seed=54),       # two tiles of 4 rows each
+    mi.custom("dc_t3_tail", 3, 8, 4, 160, 96, seed=55),      # I = 96: the canonical form's K tail
+    mi.custom("dc_t5_k3", 5, 16, 3, 256, 128, seed=56),      # 15 rows
+]
+
+
+@pytest.mark.parametrize("layout", [moe.MOE_LAYOUT_CANONICAL, moe.MOE_LAYOUT_PACKED])
+@pytest.mark.parametrize("wl", DC_CASES, ids=lambda w: w.name)
+def test_decode_batch_matches_oracle(wl, layout):
+    """Every token against the oracle, the routing bit-exact, and two calls bit-identical."""
+    assert wl.T * wl.k <= 16 and moe.moe_ffn_block_m(wl.T, wl.E, wl.k, layout) == 16
+    if layout == moe.MOE_LAYOUT_PACKED and wl.I % 128:
+        pytest.skip("packed weights need K % 128 == 0")
+    inp = mi.make_inputs(wl)
+    d = gu.DeviceInputs(inp)
+    wts = _packed(d) if layout == moe.MOE_LAYOUT_PACKED else (d.w13_q, d.w13_s, d.w2_q, d.w2_s)
+    _log(f"decode down+combine {wl.name} layout {layout}")
+    outs = []
+    for _ in range(2):
+        y = torch.full((wl.T, wl.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+        ids = torch.full((wl.T, wl.k), -7, dtype=torch.int32, device="cuda")
+        ws = torch.full((max(moe.moe_ffn_workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.k), 256),), 0xFF,
+                        dtype=torch.uint8, device="cuda")
+        moe.moe_ffn_forward(d.x, d.logits, *wts, wl.k, y=y, topk_ids_out=ids, workspace=ws, weight_layout=layout)
+        torch.cuda.synchronize()
+        outs.append((y, ids))
+    np.testing.assert_array_equal(_bits(outs[0][0]), _bits(outs[1][0]))
+    np.testing.assert_array_equal(outs[0][1].cpu().numpy(), oracle.route(inp.logits, wl.k)[0])
+    gu.assert_within_tolerance(gu.host_bf16_to_f64(outs[0][0]), oracle.moe_ffn(inp), wl.name)
+
+
+# ---------------------------------------------------------------------------------------------------
 # packed weight layout: same values re-laid out; results must be bit-identical to the canonical path
 
 def _packed(d):
