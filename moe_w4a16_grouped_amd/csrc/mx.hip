@@ -166,6 +166,26 @@ hipError_t launch_mx_quant(const uint16_t* x, long long rows, int K, uint8_t* q,
 //    gate_up epilogue, read by the grouped GEMM with no gather.
 __device__ __forceinline__ size_t mx_block(long long group, int s, int nks) { return (size_t)group * nks + s; }
 
+// Tile, row and 32-K block of this thread of a tile-list quantization launch (one thread per
+// (tile, row, block), 256 per workgroup); false past the end.  Below 2^31 threads the index
+// arithmetic is 32-bit (the 64-bit divisions would otherwise precede every load).
+__device__ __forceinline__ bool quant_tile_index(long long total, int kb, int bm, int& t, int& i, int& b) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return false;
+  if (total < (1LL << 31)) {
+    const uint32_t id = (uint32_t)idx, rest = id / (uint32_t)kb;
+    b = (int)(id - rest * (uint32_t)kb);
+    t = (int)(rest / (uint32_t)bm);
+    i = (int)(rest - (uint32_t)t * (uint32_t)bm);
+  } else {
+    const long long rest = idx / kb;
+    b = (int)(idx - rest * kb);
+    t = (int)(rest / bm);
+    i = (int)(rest - (long long)t * bm);
+  }
+  return true;
+}
+
 // x rows of a tile list quantized into the tile-blocked layout: one thread per (tile, row, 32-K
 // block); tiles past num_tiles and padding rows are not written (the GEMM never stores them).
 __global__ __launch_bounds__(256) void mx_quant_tiles_kernel(const uint16_t* __restrict__ x, int K,
@@ -174,15 +194,15 @@ __global__ __launch_bounds__(256) void mx_quant_tiles_kernel(const uint16_t* __r
                                                              const int32_t* __restrict__ num_tiles, int bm,
                                                              long long total, uint8_t* __restrict__ q,
                                                              uint8_t* __restrict__ s) {
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= total) return;
   const int kb = K / 32;
-  const int b = (int)(idx % kb);
-  const long long rest = idx / kb;
-  const int i = (int)(rest % bm);
-  const int t = (int)(rest / bm);
-  if (t >= *num_tiles || i >= tiles[3 * t + 2]) return;
-  const int r = tiles[3 * t + 1] + i;
+  int t, i, b;
+  if (!quant_tile_index(total, kb, bm, t, i, b)) return;
+  // the tile count and the tile's entry in one round trip (t < max_tiles: the entry is in bounds;
+  // past num_tiles it is not used): one condition over all three, without short-circuit, so that
+  // the loads are issued together
+  const int nt = *num_tiles, row0 = tiles[3 * t + 1], rows = tiles[3 * t + 2];
+  if ((t >= nt) | (i >= rows) | (row0 < 0)) return;
+  const int r = row0 + i;
   const int src = a_row_of ? a_row_of[r] / a_row_div : r;
   const u32x4* in = reinterpret_cast<const u32x4*>(x + (size_t)src * K + 32 * b);
   float v[32];
@@ -233,15 +253,15 @@ __global__ __launch_bounds__(256) void mx8_quant_tiles_kernel(const uint16_t* __
                                                               const int32_t* __restrict__ num_tiles, int bm,
                                                               long long total, uint8_t* __restrict__ q,
                                                               uint8_t* __restrict__ s) {
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= total) return;
   const int kb = K / 32;
-  const int b = (int)(idx % kb);
-  const long long rest = idx / kb;
-  const int i = (int)(rest % bm);
-  const int t = (int)(rest / bm);
-  if (t >= *num_tiles || i >= tiles[3 * t + 2]) return;
-  const int r = tiles[3 * t + 1] + i;
+  int t, i, b;
+  if (!quant_tile_index(total, kb, bm, t, i, b)) return;
+  // the tile count and the tile's entry in one round trip (t < max_tiles: the entry is in bounds;
+  // past num_tiles it is not used): one condition over all three, without short-circuit, so that
+  // the loads are issued together
+  const int nt = *num_tiles, row0 = tiles[3 * t + 1], rows = tiles[3 * t + 2];
+  if ((t >= nt) | (i >= rows) | (row0 < 0)) return;
+  const int r = row0 + i;
   const int src = a_row_of ? a_row_of[r] / a_row_div : r;
   const u32x4* in = reinterpret_cast<const u32x4*>(x + (size_t)src * K + 32 * b);
   float v[32];
