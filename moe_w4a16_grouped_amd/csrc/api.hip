@@ -1018,10 +1018,15 @@ namespace {
 
 // Workspace of the W4A8 layer: the routing regions of ffn_layout (canonical tile heights), then x
 // quantized (codes [T, H], scale bytes [T, H/32]), h quantized (codes [R, I], scale bytes [R, I/32])
-// and O fp32 [R, H].
+// and O: fp32 [R, H], or (o16) fp16 with in-band exponents [R, H] and its side values fp32
+// [R, ceil(H/8)].
 struct W4a8Layout {
   FfnLayout L;
-  size_t xq, xs, hq, hs, o, total;
+  // O as fp16 with in-band exponents from 16384 rows on.  Measured on MI355X in alternated A/B runs:
+  // 8192 skewed tokens over 512 experts top-10 651 -> 590 us; 800 tokens equal; 32 and 64 tokens
+  // +0.3 us and 4096 tokens over 8 experts top-2 +0.3-0.7 % with fp16 O, so those keep fp32.
+  bool o16;
+  size_t xq, xs, hq, hs, o, oside, total;
 };
 
 // Tile heights as the MXFP4 layer: experts averaging more than 128 rows (H, I multiples of 128) take the
@@ -1041,7 +1046,9 @@ W4a8Layout w4a8_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   M.xs = take((size_t)xr * H / 32);
   M.hq = take((size_t)hr * I);
   M.hs = take((size_t)hr * I / 32);
-  M.o = take((size_t)R * H * 4);
+  M.o16 = R >= 16384;
+  M.o = take((size_t)R * H * (M.o16 ? 2 : 4));
+  M.oside = M.o16 ? take((size_t)R * ((H + 7) / 8) * 4) : 0;
   M.total = off;
   return M;
 }
@@ -1169,7 +1176,8 @@ moe_status_t moe_ffn_forward_w4a8(const uint16_t* x, const float* router_logits,
   uint8_t* xs = reinterpret_cast<uint8_t*>(ws + M.xs);
   uint8_t* hq = reinterpret_cast<uint8_t*>(ws + M.hq);
   uint8_t* hs = reinterpret_cast<uint8_t*>(ws + M.hs);
-  float* o = reinterpret_cast<float*>(ws + M.o);
+  void* o = ws + M.o;
+  float* oside = M.o16 ? reinterpret_cast<float*>(ws + M.oside) : nullptr;
   const int R = T * k;
   hipError_t e;
   if (moe::route_align_fused_fits(T, E, k)) {
@@ -1196,11 +1204,13 @@ moe_status_t moe_ffn_forward_w4a8(const uint16_t* x, const float* router_logits,
                      MOE_EPI_SILU_MUL, 0, mode, 1};
   e = moe::launch_grouped_gemm_mx(g1, L.block_m, s);
   if (e != hipSuccess) return hip_status(e, "gate_up launch");
-  moe::MxGemmArgs g2{hq, hs, nullptr, 1, w2_q, w2_e, H, I, tiles, ntiles, L.max_tiles, o, nullptr, MOE_EPI_NONE, 1,
-                     mode, 1};
+  // O fp32, or fp16 with in-band per-(row, 8 columns) exponents (kind 2)
+  moe::MxGemmArgs g2{hq, hs, nullptr, 1, w2_q, w2_e, H, I, tiles, ntiles, L.max_tiles, o, nullptr, MOE_EPI_NONE,
+                     M.o16 ? 2 : 1, mode, 1};
+  g2.C_side = oside;
   e = moe::launch_grouped_gemm_mx(g2, L.block_m, s);
   if (e != hipSuccess) return hip_status(e, "down launch");
-  return hip_status(moe::launch_combine(o, nullptr, inv, w, nullptr, -1, T, k, H, y, s), "combine launch");
+  return hip_status(moe::launch_combine(o, oside, inv, w, nullptr, -1, T, k, H, y, s), "combine launch");
 }
 
 // ---- FP8 (W8A8, per-1x128) variant ------------------------------------------------------------------

@@ -897,8 +897,7 @@ static hipError_t launch_mx_mm(const MxGemmArgs& a, hipStream_t s) {
   const int nbn = (ncols + bcols - 1) / bcols;
   const dim3 grid = mm_grid(nbn, a.max_tiles);
   if (a.epilogue == MOE_EPI_SILU_MUL) gemm_mx_mm<MOE_EPI_SILU_MUL, kOutBf16, MODE, 3, AF><<<grid, 512, 0, s>>>(a);
-  else if (AF == 4 && a.out_f32 == kOutF16Exp)
-    gemm_mx_mm<MOE_EPI_NONE, AF == 4 ? kOutF16Exp : kOutF32, MODE, 3, AF><<<grid, 512, 0, s>>>(a);
+  else if (a.out_f32 == kOutF16Exp) gemm_mx_mm<MOE_EPI_NONE, kOutF16Exp, MODE, 3, AF><<<grid, 512, 0, s>>>(a);
   else if (a.out_f32) gemm_mx_mm<MOE_EPI_NONE, kOutF32, MODE, 3, AF><<<grid, 512, 0, s>>>(a);
   else gemm_mx_mm<MOE_EPI_NONE, kOutBf16, MODE, 3, AF><<<grid, 512, 0, s>>>(a);
   return hipGetLastError();
@@ -908,8 +907,8 @@ template <int BM, int BN, int KW, int PF, int MODE, int AF = 4>
 static void launch_mx_mode(const MxGemmArgs& a, dim3 grid, hipStream_t s) {
   if (a.epilogue == MOE_EPI_SILU_MUL)
     gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_SILU_MUL, kOutBf16, MODE, AF><<<grid, 256, 0, s>>>(a);
-  else if (AF == 4 && a.out_f32 == kOutF16Exp)
-    gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, AF == 4 ? kOutF16Exp : kOutF32, MODE, AF><<<grid, 256, 0, s>>>(a);
+  else if (a.out_f32 == kOutF16Exp)
+    gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, kOutF16Exp, MODE, AF><<<grid, 256, 0, s>>>(a);
   else if (a.out_f32) gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, kOutF32, MODE, AF><<<grid, 256, 0, s>>>(a);
   else gemm_mx_kernel<BM, BN, KW, PF, MOE_EPI_NONE, kOutBf16, MODE, AF><<<grid, 256, 0, s>>>(a);
 }
@@ -940,8 +939,8 @@ constexpr int kMxSplitKMaxTiles = 32;
 
 hipError_t launch_grouped_gemm_mx(const MxGemmArgs& a, int block_m, hipStream_t stream) {
   if (a.max_tiles <= 0) return hipSuccess;
-  // fp16 output with in-band exponents is built for E2M1 activations only
-  if (a.out_f32 == kOutF16Exp && (a.act_e4m3 || a.epilogue != MOE_EPI_NONE || !a.C_side)) return hipErrorInvalidValue;
+  // fp16 output with in-band exponents: NONE epilogue, with its side array
+  if (a.out_f32 == kOutF16Exp && (a.epilogue != MOE_EPI_NONE || !a.C_side)) return hipErrorInvalidValue;
   if (block_m == 128) {
     if (a.act_e4m3) return a.mode == 1 ? launch_mx_mm<1, 0>(a, stream) : launch_mx_mm<0, 0>(a, stream);
     return a.mode == 1 ? launch_mx_mm<1>(a, stream) : launch_mx_mm<0>(a, stream);

@@ -409,6 +409,49 @@ def test_ffn_forward_w4a8_matches_oracle(name, nsample):
     _log(f"  {name}: {r}")
 
 
+@pytest.mark.parametrize("layout", [moe.MOE_LAYOUT_CANONICAL, moe.MOE_LAYOUT_PACKED])
+@pytest.mark.parametrize("E,bm", [(128, 64), (8, 128)])
+def test_ffn_forward_w4a8_fp16_o_matches_fp32_o(E, bm, layout):
+    """From 16384 rows the layer keeps the down projection's output as fp16 with per-(row, 8 columns)
+    exponents; below, as fp32.  The first 1024 of 2048 tokens (k = 8: 16384 rows, fp16 O) are run
+    again on their own (8192 rows, fp32 O) with the same tile height, so that only O's format
+    differs (every other step is per row).  Tokens scaled by 2^40 (outputs near 2^80) and by 2^-30
+    (outputs near 2^-60) take the exponent path.  Per element the two results may differ by what one
+    fp16 rounding of each O value (2^-11 relative) can move y, which can flip y's bf16 rounding by one
+    step (2^-7 relative), plus 2^-8 of the class's rms for sums that cancel."""
+    T, k, H, I = 2048, 8, 256, 128
+    wl = mi.custom(f"w8_o16_e{E}", T, E, k, H, I, seed=23 + E)
+    half = mi.custom(f"w8_o32_e{E}", T // 2, E, k, H, I, seed=23 + E)
+    assert moe.moe_ffn_w4a8_block_m(T, H, I, E, k) == bm == moe.moe_ffn_w4a8_block_m(T // 2, H, I, E, k)
+    inp = mi.make_mx_inputs(wl)
+    x = mi.bf16_bits_to_f32(inp.x)
+    x[0::3] *= np.float32(2.0 ** 40)
+    x[1::3] *= np.float32(2.0 ** -30)
+    inp.x = mi.f32_to_bf16_bits(x)
+    assert np.array_equal(mi.bf16_bits_to_f32(inp.x), x)
+    inp_half = mi.MXInputs(half, inp.x[:T // 2].copy(), inp.logits[:T // 2].copy(), inp.w13_q, inp.w13_e,
+                           inp.w2_q, inp.w2_e)
+    _log(f"w4a8 fp16 O against fp32 O: E={E} bm={bm} layout {layout}")
+    d = MXDevice(inp)
+    d_half = MXDevice(inp_half)
+    d_half._packed = d.packed() if layout == moe.MOE_LAYOUT_PACKED else None
+    y16, ids16 = _forward(d, wl, layout)
+    y32, ids32 = _forward(d_half, half, layout)
+    np.testing.assert_array_equal(ids16.cpu().numpy()[:T // 2], ids32.cpu().numpy())
+    a = gu.host_bf16_to_f64(y16)[:T // 2]
+    b = gu.host_bf16_to_f64(y32)
+    assert np.all(np.isfinite(a)) and np.all(np.isfinite(b))
+    for c, label in enumerate(["x 2^40", "x 2^-30", "unscaled"]):
+        ac, bc = a[c::3], b[c::3]
+        rms = float(np.sqrt(np.mean(bc * bc)))
+        assert rms > 0
+        bound = 2.0 ** -7 * np.maximum(np.abs(ac), np.abs(bc)) + 2.0 ** -8 * rms
+        worst = float(np.max(np.abs(ac - bc) - bound))
+        assert worst <= 0, f"{label}: worst excess {worst / rms:.3e} rms"
+    # the classes are where they were put: far above and far below fp16's range
+    assert np.abs(b[0::3]).max() > 2.0 ** 60 and 0 < np.abs(b[1::3]).max() < 2.0 ** -40
+
+
 @pytest.mark.parametrize("wl", [
     mi.custom("w8_one_expert", 3, 1, 1, 256, 128, seed=5),
     mi.custom("w8_ragged", 37, 16, 4, 160, 96, seed=6),
