@@ -432,10 +432,12 @@ MxLayout mx_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
 
 // Workspace of the FP8 layer: the routing regions of ffn_layout (canonical tile heights), then
 // x quantized (codes [T, H], scales [T, H/128]), h in fp32 [R, I], h quantized (codes [R, I],
-// scales [R, I/128]) and O fp32 [R, H].
+// scales [R, I/128]) and O: fp32 [R, H], or (o16) fp16 with in-band exponents [R, H] and its side
+// values fp32 [R, ceil(H/8)].
 struct F8Layout {
   FfnLayout L;
-  size_t xq, xs, hf, hq, hs, o, total;
+  bool o16;  // O as fp16 with in-band exponents: 128-row tiles and at least 16384 rows
+  size_t xq, xs, hf, hq, hs, o, oside, total;
 };
 
 // Row-tile height of the FP8 layer: as the canonical W4A16 choice, but experts averaging more than
@@ -460,7 +462,9 @@ F8Layout f8_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   M.hf = take((size_t)R * I * 4);
   M.hq = take((size_t)R * I);
   M.hs = take((size_t)R * (I / 128) * 4);
-  M.o = take((size_t)R * H * 4);
+  M.o16 = M.L.block_m == 128 && R >= 16384;
+  M.o = take((size_t)R * H * (M.o16 ? 2 : 4));
+  M.oside = M.o16 ? take((size_t)R * ((H + 7) / 8) * 4) : 0;
   M.total = off;
   return M;
 }
@@ -1306,7 +1310,8 @@ moe_status_t moe_ffn_forward_f8(const uint16_t* x, const float* router_logits, i
   float* hf = reinterpret_cast<float*>(ws + M.hf);
   uint8_t* hq = reinterpret_cast<uint8_t*>(ws + M.hq);
   float* hs = reinterpret_cast<float*>(ws + M.hs);
-  float* o = reinterpret_cast<float*>(ws + M.o);
+  void* o = ws + M.o;
+  float* oside = M.o16 ? reinterpret_cast<float*>(ws + M.oside) : nullptr;
   const int R = T * k;
   hipError_t e;
   if (moe::route_align_fused_fits(T, E, k)) {
@@ -1333,10 +1338,13 @@ moe_status_t moe_ffn_forward_f8(const uint16_t* x, const float* router_logits, i
     e = moe::launch_f8_quant(hf, true, R, I, hq, hs, s);
     if (e != hipSuccess) return hip_status(e, "h quantization launch");
   }
-  moe::F8GemmArgs g2{hq, hs, nullptr, 1, w2_q, w2_s, H, I, tiles, ntiles, L.max_tiles, o, MOE_EPI_NONE, 1};
+  // O fp32, or fp16 with in-band per-(row, 8 columns) exponents (kind 3 of the FP8 GEMM)
+  moe::F8GemmArgs g2{hq, hs, nullptr, 1, w2_q, w2_s, H, I, tiles, ntiles, L.max_tiles, o, MOE_EPI_NONE,
+                     M.o16 ? 3 : 1};
+  g2.C_side = oside;
   e = moe::launch_grouped_gemm_f8(g2, L.block_m, s);
   if (e != hipSuccess) return hip_status(e, "down launch");
-  return hip_status(moe::launch_combine(o, nullptr, inv, w, nullptr, -1, T, k, H, y, s), "combine launch");
+  return hip_status(moe::launch_combine(o, oside, inv, w, nullptr, -1, T, k, H, y, s), "combine launch");
 }
 
 }  // extern "C"

@@ -315,6 +315,25 @@ __device__ __forceinline__ void g2lds4(const void* g, void* lds_wave_base) {
 
 __device__ __forceinline__ int f8_swz(int row) { return (row >> 1) & 7; }
 
+// The NONE epilogue of gemm_f8_mm with fp16 output and in-band exponents (OUT 3), one 16-row block at a
+// time (fewer live registers); padding rows are left out of the exponent test.
+template <int MI, int NI>
+__device__ __forceinline__ void f8_mm_store_f16e(const F8GemmArgs& p, const f32x4 (&acc)[MI][NI], int nb, int wm,
+                                                 int wn, int row0, int rows, int q, int l16) {
+  int ncol[NI];
+  bool nvalid[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    ncol[ni] = nb * kF8MmBN + wn * 64 + ni * 16 + l16;
+    nvalid[ni] = ncol[ni] < p.N;
+  }
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+    store_f16e<1, NI, true>(static_cast<uint16_t*>(p.C), p.C_side, p.N,
+                            reinterpret_cast<const f32x4(&)[1][NI]>(acc[mi]), wm * 64 + mi * 16, row0, rows, q, ncol,
+                            nvalid);
+}
+
 template <int EPI, int OUT, int NSTAGE>
 __global__ __launch_bounds__(512) void gemm_f8_mm(F8GemmArgs p) {
   constexpr int MI = 4, NI = 4;
@@ -487,6 +506,10 @@ __global__ __launch_bounds__(512) void gemm_f8_mm(F8GemmArgs p) {
     }
     return;
   }
+  if constexpr (EPI == MOE_EPI_NONE && OUT == 3) {
+    f8_mm_store_f16e<MI, NI>(p, acc, nb, wm, wn, row0, rows, q, l16);
+    return;
+  }
 
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
@@ -513,6 +536,7 @@ __global__ __launch_bounds__(512) void gemm_f8_mm(F8GemmArgs p) {
       }
     }
 }
+
 
 template <int EPI, int OUT>
 static hipError_t launch_f8_mm(const F8GemmArgs& a, hipStream_t s) {
@@ -543,9 +567,11 @@ hipError_t launch_grouped_gemm_f8(const F8GemmArgs& a, int block_m, hipStream_t 
   if (block_m == 128) {
     if (a.epilogue == MOE_EPI_SILU_MUL)
       return a.out_f32 == 2 ? launch_f8_mm<MOE_EPI_SILU_MUL, 2>(a, stream) : launch_f8_mm<MOE_EPI_SILU_MUL, 1>(a, stream);
+    if (a.out_f32 == 3) return a.C_side ? launch_f8_mm<MOE_EPI_NONE, 3>(a, stream) : hipErrorInvalidValue;
     if (a.out_f32) return launch_f8_mm<MOE_EPI_NONE, 1>(a, stream);
     return launch_f8_mm<MOE_EPI_NONE, 0>(a, stream);
   }
+  if (a.out_f32 == 3) return hipErrorInvalidValue;  // fp16 output with exponents: 128-row tiles only
   // Configurations from sweeps on MI355X (HIP events, weights streamed from HBM): with 128 experts
   // top-8 at 8 and 64 tokens, gate_up takes 36 / 86 us with <16,64,KW2> against 43 / 90 us for
   // <16,128,KW1>, down 21 / 44 us with <16,256,KW2> against 21 / 52 us; at 800 tokens and 256

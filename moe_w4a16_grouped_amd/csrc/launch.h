@@ -164,8 +164,10 @@ struct F8GemmArgs {
   int max_tiles;
   void* C;                  // NONE: fp32 or bf16 [rows, N]; SILU_MUL: fp32 h [rows, N/2] or h codes
   int epilogue;             // MOE_EPI_*
-  int out_f32;              // 0 bf16, 1 fp32, 2 (SILU_MUL, 128-row tiles) h quantized per 1x128
+  int out_f32;              // 0 bf16, 1 fp32, 2 (SILU_MUL, 128-row tiles) h quantized per 1x128,
+                            // 3 (NONE, 128-row tiles) fp16 with in-band exponents (kOutF16Exp's format)
   float* Cs;                // out_f32 == 2: h scales [rows, N/256]
+  float* C_side;            // out_f32 == 3: fp32 values of the marked elements, [rows, ceil(N / 8)]
 };
 hipError_t launch_grouped_gemm_f8(const F8GemmArgs& a, int block_m, hipStream_t stream);
 // x (bf16, or fp32 when in_f32) [rows, K] -> codes [rows, K] and scales [rows, K/128].

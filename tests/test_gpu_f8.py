@@ -411,6 +411,44 @@ def test_ffn_forward_f8_edges(wl):
     _assert_layer(gu.host_bf16_to_f64(y), inp, np.arange(wl.T), wl.name)
 
 
+@pytest.mark.parametrize("E", [8, 32])
+def test_ffn_forward_f8_fp16_o_matches_fp32_o(E):
+    """With 128-row tiles and from 16384 rows the layer keeps the down projection's output as fp16
+    with per-(row, 8 columns) exponents; below, as fp32.  The first 1024 of 2048 tokens (k = 8:
+    16384 rows, fp16 O) are run again on their own (8192 rows, fp32 O) with the same tile height, so
+    that only O's format differs (every other step is per row).  Tokens scaled by 2^40 (outputs near
+    2^80) and by 2^-30 (outputs near 2^-60) take the exponent path.  Per element the two results may
+    differ by what one fp16 rounding of each O value (2^-11 relative) can move y, which can flip y's
+    bf16 rounding by one step (2^-7 relative), plus 2^-8 of the class's rms for sums that cancel."""
+    T, k, H, I = 2048, 8, 256, 256
+    wl = mi.custom(f"f8_o16_e{E}", T, E, k, H, I, seed=31 + E)
+    half = mi.custom(f"f8_o32_e{E}", T // 2, E, k, H, I, seed=31 + E)
+    assert moe.moe_ffn_f8_block_m(T, E, k) == 128 == moe.moe_ffn_f8_block_m(T // 2, E, k)
+    inp = mi.make_f8_inputs(wl)
+    x = mi.bf16_bits_to_f32(inp.x)
+    x[0::3] *= np.float32(2.0 ** 40)
+    x[1::3] *= np.float32(2.0 ** -30)
+    inp.x = mi.f32_to_bf16_bits(x)
+    assert np.array_equal(mi.bf16_bits_to_f32(inp.x), x)
+    inp_half = mi.F8Inputs(half, inp.x[:T // 2].copy(), inp.logits[:T // 2].copy(), inp.w13_q, inp.w13_s,
+                           inp.w2_q, inp.w2_s)
+    _log(f"fp8 fp16 O against fp32 O: E={E}")
+    y16, ids16 = _forward(F8Device(inp), wl)
+    y32, ids32 = _forward(F8Device(inp_half), half)
+    np.testing.assert_array_equal(ids16.cpu().numpy()[:T // 2], ids32.cpu().numpy())
+    a = gu.host_bf16_to_f64(y16)[:T // 2]
+    b = gu.host_bf16_to_f64(y32)
+    assert np.all(np.isfinite(a)) and np.all(np.isfinite(b))
+    for c, label in enumerate(["x 2^40", "x 2^-30", "unscaled"]):
+        ac, bc = a[c::3], b[c::3]
+        rms = float(np.sqrt(np.mean(bc * bc)))
+        assert rms > 0
+        bound = 2.0 ** -7 * np.maximum(np.abs(ac), np.abs(bc)) + 2.0 ** -8 * rms
+        worst = float(np.max(np.abs(ac - bc) - bound))
+        assert worst <= 0, f"{label}: worst excess {worst / rms:.3e} rms"
+    assert np.abs(b[0::3]).max() > 2.0 ** 60 and 0 < np.abs(b[1::3]).max() < 2.0 ** -40
+
+
 def test_ffn_forward_f8_deterministic_and_empty():
     wl = mi.custom("f8_det", 200, 32, 4, 512, 256, seed=13)
     d = F8Device(mi.make_f8_inputs(wl))
