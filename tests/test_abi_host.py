@@ -378,6 +378,23 @@ def test_w4a8_entry_points_reject(lib):
     assert fw(T=0) == 0
 
 
+@pytest.mark.parametrize("variant,T,E,k,H,I", [
+    ("mxfp4", 32, 8, 8, 256, 128),     # 256 rows
+    ("w4a8", 2048, 8, 8, 256, 128),    # 16384 rows
+    ("f8", 2048, 8, 8, 256, 256),      # 16384 rows, 128-row tiles
+])
+def test_variant_layers_switch_to_fp16_o_at_their_row_threshold(variant, T, E, k, H, I):
+    """From a row threshold a variant layer keeps the down projection's output as fp16 with in-band
+    exponents (R*H*2 bytes plus R*H/8 fp32 side values) instead of fp32 (R*H*4): the workspace
+    shrinks by about R*H*1.5 bytes between T - 1 and T tokens although everything else grows."""
+    ws = {"mxfp4": moe.moe_ffn_mxfp4_workspace_bytes, "w4a8": moe.moe_ffn_w4a8_workspace_bytes,
+          "f8": moe.moe_ffn_f8_workspace_bytes}[variant]
+    below, at = ws(T - 1, H, I, E, k), ws(T, H, I, E, k)
+    R = T * k
+    assert 0 < at and below - at > R * H  # the O saving (R*H*1.5) outweighs one token's other growth
+    assert ws(T + 1, H, I, E, k) > at      # and it keeps growing above
+
+
 def test_noalloc_entry_point_rejects_sizes_beyond_its_scratch(lib):
     """The entry point without allocation checks its fixed scratch size on the host, before any
     device call, so an oversized layer fails the same way with or without a GPU."""
