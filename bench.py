@@ -415,6 +415,7 @@ def run_mxfp4(args):
                    "eager_us": round(eager_ms * 1e3, 2),
                    "graph_median_us": None if graph_ms is None else round(graph_ms * 1e3, 2)},
         "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
+        "kernels_note": "per-kernel pass through the stand-alone entry points, whose down projection writes fp32 O for the combine; the layer keeps O as fp16 with in-band exponents (MXFP4 layer: from 256 rows)",
         "roofline": {"kernel": "gemm_mx_kernel (gate_up + SiLU*mul + h quantization)", "bound": bound,
                      "achieved": round(achieved, 2), "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": None, "algorithmic_bytes": gu_bytes, "algorithmic_flops": gu_flops},
@@ -537,6 +538,7 @@ def run_w4a8(args):
                    "eager_us": round(eager_ms * 1e3, 2),
                    "graph_median_us": None if graph_ms is None else round(graph_ms * 1e3, 2)},
         "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
+        "kernels_note": "per-kernel pass through the stand-alone entry points, whose down projection writes fp32 O for the combine; the layer keeps O as fp16 with in-band exponents (W4A8 layer: from 16384 rows)",
         "roofline": {"kernel": "gemm_mx_kernel, E4M3 activations (gate_up + SiLU*mul + h quantization)", "bound": bound,
                      "achieved": round(achieved, 2), "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": None, "algorithmic_bytes": gu_bytes, "algorithmic_flops": gu_flops},
@@ -657,6 +659,7 @@ def run_f8(args):
                    "eager_us": round(eager_ms * 1e3, 2),
                    "graph_median_us": None if graph_ms is None else round(graph_ms * 1e3, 2)},
         "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
+        "kernels_note": "per-kernel pass through the stand-alone entry points, whose down projection writes fp32 O for the combine; the layer keeps O as fp16 with in-band exponents (FP8 layer: with 128-row tiles from 16384 rows)",
         "roofline": {"kernel": ("gemm_f8_mm (gate_up + SiLU*mul + h quantization)" if fused_h
                                 else "gemm_f8_kernel (gate_up + SiLU*mul, fp32 h)"), "bound": bound,
                      "achieved": round(achieved, 2), "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
