@@ -168,12 +168,14 @@ __device__ __forceinline__ int f16_seg_exponent(float m) {
   return e < -110 ? -110 : (e > 113 ? 113 : e);
 }
 
-// Whether some aligned group of 8 lanes (a segment) has every bit of mask set.
-__device__ __forceinline__ bool any_full_octet(uint64_t m) {
-  m &= m >> 1;
-  m &= m >> 2;
-  m &= m >> 4;
-  return (m & 0x0101010101010101ull) != 0ull;
+// OR of v over the 8 lanes of each aligned group of 8 (a segment), by DPP lane moves within a row of
+// 16: quad_perm [1,0,3,2], quad_perm [2,3,0,1], then row_half_mirror (lane i of a half-row takes
+// lane 7 - i), after which every lane holds its segment's OR.
+__device__ __forceinline__ uint32_t seg8_or(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true);
+  return v;
 }
 
 // The 8 columns of a segment live in 8 lanes of a quarter (one lane per column, l16 = 8j .. 8j+7):
@@ -204,8 +206,13 @@ __device__ __forceinline__ void store_f16e(uint16_t* C, float* C_side, int N, co
                                            int row0, int rows, int q, const int (&ncol)[NI], const bool (&nvalid)[NI]) {
   // some segment of this wave may need an exponent (a magnitude of 2^15 or more, a non-finite value,
   // or all eight below 2^-6; an invalid column counts as below).  With PAD_ROWS a padding row's
-  // segments count as neither.
-  bool big = false, tiny = false;
+  // segments count as neither.  Bit j of `keep` says that value j of this lane is not below 2^-6;
+  // OR-ed over the 8 lanes of each segment (lanes differing in their three low bits), a clear bit
+  // marks a segment whose values are all below.
+  constexpr int NV = MI * NI * 4;
+  static_assert(NV <= 64, "a lane holds at most 64 values");
+  bool big = false;
+  uint32_t keep_lo = 0u, keep_hi = 0u;
   const int row_lim = rows - row_base - q * 4;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
@@ -214,12 +221,37 @@ __device__ __forceinline__ void store_f16e(uint16_t* C, float* C_side, int N, co
       const bool live = !PAD_ROWS || mi * 16 + r < row_lim;
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
+        const int j = (mi * 4 + r) * NI + ni;
         const float a = !live ? 1.f : (nvalid[ni] ? fabsf(acc[mi][ni][r]) : 0.f);
         big |= !(a < 32768.f);
-        tiny |= any_full_octet(__ballot(a < kF16Small));
+        const uint32_t bit = a < kF16Small ? 0u : 1u;
+        if (j < 32) keep_lo |= bit << j;
+        else keep_hi |= bit << (j - 32);
       }
     }
-  const bool scaled = __ballot(big) != 0ull || tiny;
+  // the OR over a segment's 8 lanes by row-local lane moves: swap neighbours, swap pairs, then
+  // mirror each half-row of 8 (lane i <-> 7 - i)
+  keep_lo = seg8_or(keep_lo);
+  if constexpr (NV > 32) keep_hi = seg8_or(keep_hi);
+  constexpr uint32_t kFullLo = NV >= 32 ? 0xFFFFFFFFu : ((1u << NV) - 1u);
+  constexpr uint32_t kFullHi = NV >= 64 ? 0xFFFFFFFFu : (NV > 32 ? ((1u << (NV - 32)) - 1u) : 0u);
+  const bool tiny_here = keep_lo != kFullLo || keep_hi != kFullHi;
+  const bool scaled = __ballot(big || tiny_here) != 0ull;
+  if (!scaled) {
+    // the common case: every value just rounded to fp16, row by row
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row_base + mi * 16 + q * 4 + r;
+        if (row >= rows) continue;
+        uint16_t* crow = C + (size_t)(row0 + row) * N;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          if (nvalid[ni]) crow[ncol[ni]] = f32_to_f16_bits(acc[mi][ni][r]);
+      }
+    return;
+  }
   const int l16 = threadIdx.x & 15;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
@@ -229,20 +261,15 @@ __device__ __forceinline__ void store_f16e(uint16_t* C, float* C_side, int N, co
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         float v = nvalid[ni] ? acc[mi][ni][r] : 0.f;
-        uint16_t bits;
-        if (!scaled) {
-          bits = f32_to_f16_bits(v);
-        } else {
-          // every lane takes part in the segment reductions, whatever its row
-          bool nonfinite;
-          const float m = seg8_max_finite(v, nonfinite);
-          const int ex = f16_seg_exponent(m);
-          v *= pow2f(-ex);  // exact
-          bits = f32_to_f16_bits(v);
-          if ((ex != 0 || nonfinite) && (l16 & 7) == 0) {
-            bits = (uint16_t)(kF16Marker | (ex + 256));
-            if (row < rows && nvalid[ni]) C_side[(size_t)(row0 + row) * (size_t)((N + 7) / 8) + ncol[ni] / 8] = v;
-          }
+        // every lane takes part in the segment reductions, whatever its row
+        bool nonfinite;
+        const float m = seg8_max_finite(v, nonfinite);
+        const int ex = f16_seg_exponent(m);
+        v *= pow2f(-ex);  // exact
+        uint16_t bits = f32_to_f16_bits(v);
+        if ((ex != 0 || nonfinite) && (l16 & 7) == 0) {
+          bits = (uint16_t)(kF16Marker | (ex + 256));
+          if (row < rows && nvalid[ni]) C_side[(size_t)(row0 + row) * (size_t)((N + 7) / 8) + ncol[ni] / 8] = v;
         }
         if (row < rows && nvalid[ni]) C[(size_t)(row0 + row) * N + ncol[ni]] = bits;
       }
