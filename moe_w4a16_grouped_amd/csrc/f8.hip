@@ -26,20 +26,6 @@ typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 constexpr int kF8Block = 128;   // K elements per scale (and per K step)
 constexpr float kE4M3Max = 448.0f;
 
-// Inclusive max over the 16 lanes of a DPP row (rotations by 8, 4, 2, 1 within the row).
-template <int CTRL>
-__device__ __forceinline__ float dpp_max(float v) {
-  const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false);
-  return fmaxf(v, __int_as_float(o));
-}
-__device__ __forceinline__ float row16_max(float v) {
-  v = dpp_max<0x128>(v);  // row_ror:8
-  v = dpp_max<0x124>(v);  // row_ror:4
-  v = dpp_max<0x122>(v);  // row_ror:2
-  v = dpp_max<0x121>(v);  // row_ror:1
-  return v;
-}
-
 // Four E4M3 codes of v[j] / s, j < 4 (correctly rounded fp32 quotient, clamped to +-448, then the
 // hardware conversion: round to nearest even).
 __device__ __forceinline__ uint32_t f8_encode4(const float* v, float s) {

@@ -200,10 +200,7 @@ __device__ __forceinline__ void store_tile_h16(const GemmArgs& p, const f32x4 (&
         if (nvalid[ni] && fabsf(h) <= 3.4e38f) m = fmaxf(m, fabsf(h));
       }
       // the row's 32 columns live in the 16 lanes of this quarter (two columns each)
-      m = fmaxf(m, __shfl_xor(m, 1));
-      m = fmaxf(m, __shfl_xor(m, 2));
-      m = fmaxf(m, __shfl_xor(m, 4));
-      m = fmaxf(m, __shfl_xor(m, 8));
+      m = row16_max(m);
       ex[mi][r] = f16_seg_exponent(m);
       any |= ex[mi][r] != 0 && row_base + mi * 16 + q * 4 + r < rows;
     }

@@ -178,18 +178,27 @@ __device__ __forceinline__ uint32_t seg8_or(uint32_t v) {
   return v;
 }
 
+// Largest value of m over each row of 16 lanes (a quarter of the wave), by DPP lane moves: the
+// two quad swaps and the half-row mirror of seg8_or, then row_mirror (lane i <-> 15 - i).  (fmaxf
+// ignores a NaN operand, so the order of the moves does not change the result.)
+__device__ __forceinline__ float row16_max(float m) {
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, true)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x141, 0xF, 0xF, true)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x140, 0xF, 0xF, true)));
+  return m;
+}
+
 // The 8 columns of a segment live in 8 lanes of a quarter (one lane per column, l16 = 8j .. 8j+7):
 // the largest finite magnitude over them, and whether any is non-finite.
 __device__ __forceinline__ float seg8_max_finite(float v, bool& nonfinite) {
   const bool nf = !(fabsf(v) <= 3.4e38f);
   float m = nf ? 0.f : fabsf(v);
-  m = fmaxf(m, __shfl_xor(m, 1));
-  m = fmaxf(m, __shfl_xor(m, 2));
-  m = fmaxf(m, __shfl_xor(m, 4));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, true)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x141, 0xF, 0xF, true)));
   int f = nf;
-  f |= __shfl_xor(f, 1);
-  f |= __shfl_xor(f, 2);
-  f |= __shfl_xor(f, 4);
+  f = (int)seg8_or((uint32_t)f);
   nonfinite = f != 0;
   return m;
 }
@@ -233,8 +242,8 @@ __device__ __forceinline__ void store_f16e(uint16_t* C, float* C_side, int N, co
   // mirror each half-row of 8 (lane i <-> 7 - i)
   keep_lo = seg8_or(keep_lo);
   if constexpr (NV > 32) keep_hi = seg8_or(keep_hi);
-  constexpr uint32_t kFullLo = NV >= 32 ? 0xFFFFFFFFu : ((1u << NV) - 1u);
-  constexpr uint32_t kFullHi = NV >= 64 ? 0xFFFFFFFFu : (NV > 32 ? ((1u << (NV - 32)) - 1u) : 0u);
+  constexpr uint32_t kFullLo = NV >= 32 ? 0xFFFFFFFFu : ((1u << (NV & 31)) - 1u);
+  constexpr uint32_t kFullHi = NV >= 64 ? 0xFFFFFFFFu : (NV > 32 ? ((1u << ((NV - 32) & 31)) - 1u) : 0u);
   const bool tiny_here = keep_lo != kFullLo || keep_hi != kFullHi;
   const bool scaled = __ballot(big || tiny_here) != 0ull;
   if (!scaled) {
